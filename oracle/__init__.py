@@ -1,0 +1,232 @@
+"""CPU oracle for one MoE-layer forward pass -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and ``bench.py``'s cpu_baseline
+leg may import this package.  The product path (the HIP library and its
+binding) never does.  The arithmetic lives in ``moe_oracle.c`` (plain C,
+double precision), which shares no code with the HIP library; this module
+only marshals numpy arrays into it.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "moe_oracle.c")
+_LIB = os.path.join(_HERE, "libmoe_oracle.so")
+
+F32, BF16, I8 = 0, 1, 2
+RELU, SWIGLU = 0, 1
+MAX_E = 64
+_DT = {"f32": F32, "bf16": BF16, "i8": I8}
+_KIND = {"relu": RELU, "swiglu": SWIGLU}
+
+
+def build() -> str:
+    """Compile the oracle with gcc (always recompiles)."""
+    tmp = _LIB + ".tmp"
+    subprocess.run(
+        ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-I", _HERE, "-o", tmp, _SRC, "-lm"],
+        check=True,
+    )
+    os.replace(tmp, _LIB)
+    return _LIB
+
+
+class _Experts(ctypes.Structure):
+    _fields_ = [
+        ("m", ctypes.c_int), ("p", ctypes.c_int), ("E", ctypes.c_int),
+        ("kind", ctypes.c_int), ("w_dtype", ctypes.c_int),
+        ("w1", ctypes.c_void_p), ("w3", ctypes.c_void_p), ("w2", ctypes.c_void_p),
+        ("s1", ctypes.c_void_p), ("s3", ctypes.c_void_p), ("s2", ctypes.c_void_p),
+    ]
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build()
+        L = ctypes.CDLL(_LIB)
+        vp, i32 = ctypes.c_void_p, ctypes.c_int
+        P = ctypes.POINTER(_Experts)
+        L.orc_router_logits.argtypes = [vp, i32, vp, vp, i32, i32, i32, vp]
+        L.orc_topk.argtypes = [vp, i32, i32, i32, vp, vp]
+        L.orc_dispatch.argtypes = [vp, i32, i32, i32, vp, vp, vp, vp]
+        L.orc_expert_apply.argtypes = [P, i32, vp, vp, vp]
+        L.orc_expert_rows.argtypes = [P, vp, i32, i32, i32, vp, vp, vp, i32, vp, vp]
+        L.orc_combine.argtypes = [vp, vp, vp, vp, i32, i32, i32, vp]
+        L.orc_forward_tokens.argtypes = [P, vp, i32, vp, vp, vp, i32, i32, vp, i32, vp, vp, vp, vp]
+        L.orc_dense_masked.argtypes = [P, vp, i32, vp, vp, i32, i32, vp]
+        for f in ("orc_router_logits", "orc_topk", "orc_dispatch", "orc_expert_apply", "orc_expert_rows",
+                  "orc_combine", "orc_forward_tokens", "orc_dense_masked"):
+            getattr(L, f).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data
+
+
+def _c(a, dtype=None):
+    if a is None:
+        return None
+    a = np.ascontiguousarray(a if dtype is None else a.astype(dtype, copy=False))
+    return a
+
+
+def _check(rc, what):
+    if rc != 0:
+        raise ValueError(f"oracle {what} rejected its arguments (rc={rc})")
+
+
+def _xdt(x):
+    return BF16 if x.dtype == np.uint16 else F32
+
+
+class Experts:
+    """Expert weights of one layer in canonical layout (see synth)."""
+
+    def __init__(self, kind, w1, w2, w3=None, s1=None, s2=None, s3=None):
+        self.kind = kind
+        self.w1, self.w2, self.w3 = _c(w1), _c(w2), _c(w3)
+        self.s1, self.s2, self.s3 = _c(s1, np.float32), _c(s2, np.float32), _c(s3, np.float32)
+        E, m, p = self.w1.shape
+        assert self.w2.shape == (E, p, m)
+        if self.w1.dtype == np.float32:
+            dt = F32
+        elif self.w1.dtype == np.uint16:
+            dt = BF16
+        elif self.w1.dtype == np.int8:
+            dt = I8
+        else:
+            raise TypeError(self.w1.dtype)
+        self.E, self.m, self.p, self.w_dtype = E, m, p, dt
+        self._s = _Experts(m, p, E, _KIND[kind], dt, _ptr(self.w1), _ptr(self.w3), _ptr(self.w2),
+                           _ptr(self.s1), _ptr(self.s3), _ptr(self.s2))
+
+    @classmethod
+    def from_layer(cls, layer):
+        sp = layer["spec"]
+        return cls(sp.kind, layer["w1"], layer["w2"], layer["w3"], layer["s1"], layer["s2"], layer["s3"])
+
+    def param_bytes(self) -> int:
+        """Bytes of one expert's weight matrices as stored."""
+        nmat = 3 if self.kind == "swiglu" else 2
+        return nmat * self.m * self.p * self.w1.itemsize
+
+
+def router_logits(x, wg, bias=None):
+    x = _c(x)
+    wg = _c(wg, np.float32)
+    bias = _c(bias, np.float32)
+    T, m = x.shape
+    E = wg.shape[1]
+    out = np.empty((T, E), np.float32)
+    _check(lib().orc_router_logits(_ptr(x), _xdt(x), _ptr(wg), _ptr(bias), T, m, E, _ptr(out)), "router")
+    return out
+
+
+def topk(logits, k):
+    logits = _c(logits, np.float32)
+    T, E = logits.shape
+    idx = np.empty((T, k), np.int32)
+    w = np.empty((T, k), np.float32)
+    _check(lib().orc_topk(_ptr(logits), T, E, k, _ptr(idx), _ptr(w)), "topk")
+    return idx, w
+
+
+def dispatch(idx, E):
+    idx = _c(idx, np.int32)
+    T, k = idx.shape
+    counts = np.empty(E, np.int32)
+    offsets = np.empty(E + 1, np.int32)
+    perm = np.empty(T * k, np.int32)
+    inv = np.empty(T * k, np.int32)
+    _check(lib().orc_dispatch(_ptr(idx), T, E, k, _ptr(counts), _ptr(offsets), _ptr(perm), _ptr(inv)), "dispatch")
+    return counts, offsets, perm, inv
+
+
+def expert_apply(X: Experts, e, xrow):
+    """One expert on one activation row (float64); returns (o, ops[3])."""
+    xrow = _c(xrow, np.float64)
+    o = np.empty(X.m, np.float64)
+    ops = np.zeros(3, np.uint64)
+    _check(lib().orc_expert_apply(ctypes.byref(X._s), e, _ptr(xrow), _ptr(o), _ptr(ops)), "expert_apply")
+    return o, ops
+
+
+def expert_rows(X: Experts, x, k, perm, offsets, rows=None):
+    """Unweighted expert outputs for permuted rows (all T*k when rows is None)."""
+    x = _c(x)
+    perm = _c(perm, np.int32)
+    offsets = _c(offsets, np.int32)
+    rows = _c(rows, np.int32)
+    T = x.shape[0]
+    n = T * k if rows is None else len(rows)
+    out = np.empty((n, X.m), np.float64)
+    ops = np.zeros(3, np.uint64)
+    _check(lib().orc_expert_rows(ctypes.byref(X._s), _ptr(x), _xdt(x), T, k, _ptr(perm), _ptr(offsets),
+                                 _ptr(rows), n, _ptr(out), _ptr(ops)), "expert_rows")
+    return out, ops
+
+
+def combine(y_perm, inv_perm, idx, w):
+    y_perm = _c(y_perm, np.float64)
+    inv_perm = _c(inv_perm, np.int32)
+    idx = _c(idx, np.int32)
+    w = _c(w, np.float32)
+    T, k = idx.shape
+    m = y_perm.shape[1]
+    y = np.empty((T, m), np.float64)
+    _check(lib().orc_combine(_ptr(y_perm), _ptr(inv_perm), _ptr(idx), _ptr(w), T, m, k, _ptr(y)), "combine")
+    return y
+
+
+def forward_tokens(X: Experts, x, wg, bias, k, tokens, logits=None):
+    """End-to-end output rows for the given tokens; returns (y, idx, w, ops)."""
+    x = _c(x)
+    wg = _c(wg, np.float32)
+    bias = _c(bias, np.float32)
+    logits = _c(logits, np.float32)
+    tokens = _c(np.asarray(tokens), np.int32)
+    T = x.shape[0]
+    n = len(tokens)
+    y = np.empty((n, X.m), np.float64)
+    idx = np.empty((n, k), np.int32)
+    w = np.empty((n, k), np.float32)
+    ops = np.zeros(3, np.uint64)
+    _check(lib().orc_forward_tokens(ctypes.byref(X._s), _ptr(x), _xdt(x), _ptr(wg), _ptr(bias), _ptr(logits),
+                                    T, k, _ptr(tokens), n, _ptr(y), _ptr(idx), _ptr(w), _ptr(ops)),
+           "forward_tokens")
+    return y, idx, w, ops
+
+
+def dense_masked(X: Experts, x, idx, w):
+    x = _c(x)
+    idx = _c(idx, np.int32)
+    w = _c(w, np.float32)
+    T, k = idx.shape
+    y = np.empty((T, X.m), np.float64)
+    _check(lib().orc_dense_masked(ctypes.byref(X._s), _ptr(x), _xdt(x), _ptr(idx), _ptr(w), T, k, _ptr(y)),
+           "dense_masked")
+    return y
+
+
+def layer_forward(X: Experts, x, wg, bias, k, logits=None):
+    """Whole layer through the routed path: returns a dict of every stage."""
+    if logits is None:
+        logits = router_logits(x, wg, bias)
+    idx, w = topk(logits, k)
+    counts, offsets, perm, inv = dispatch(idx, X.E)
+    y_perm, ops = expert_rows(X, x, k, perm, offsets)
+    y = combine(y_perm, inv, idx, w)
+    return dict(logits=logits, idx=idx, w=w, counts=counts, offsets=offsets, perm=perm, inv_perm=inv,
+                y_perm=y_perm, y=y, ops=ops)

@@ -1,0 +1,371 @@
+/*
+ * CPU oracle for one MoE-layer forward pass.  TEST INFRASTRUCTURE ONLY:
+ * it is used by tests/, by __graft_entry__.smoke() and by bench.py's
+ * cpu_baseline leg, never by the product path.  It shares no code with the
+ * HIP library.
+ *
+ * It is the plain definition, written slowly and in double precision:
+ *
+ *  - router: logits[t][e] = fp32( sum_i x[t][i] * Wg[i][e]  (+ b[e]) )
+ *    (a router maps every token to its experts: HARMOEny article,
+ *    yejing.asia, section 3.3 step one; the gating network runs on the GPU:
+ *    GPU-cache article, coreui.cn, section 3.1).
+ *  - top-k: experts ranked by (logit descending, expert index ascending),
+ *    NaN below every number, +0 == -0; the k first are taken, slot 0 first.
+ *  - gate weights: softmax over the k selected logits,
+ *    w_j = exp(l_j - l_0) / sum_{i<k} exp(l_i - l_0), in double, stored fp32.
+ *    (Equal in exact arithmetic to a softmax over all E renormalised over the
+ *    selected k.)
+ *  - dispatch: counts, exclusive offsets and the stable counting-sort
+ *    permutation of assignment ids a = t*k + j by expert (HARMOEny article,
+ *    section 3.3 step four: tokens are sent to their experts).
+ *  - expert: the two-layer MLP x*W1*W2 with W1 m x p and W2 p x m (HARMOEny
+ *    article, section 3.2 "expert prefetch"), with ReLU between the two
+ *    matrices, or its SwiGLU form h = SiLU(x*W1) * (x*W3), o = h*W2.  int8
+ *    weights stand for q[i][n] * s[n] (per output channel n).  Every dot
+ *    product of length n is a0*b0 followed by n-1 multiply-adds, and an
+ *    operation counter records each multiply and each add.
+ *  - combine: y[t] = sum over the token's selections, in ascending expert
+ *    index, of w * o  (HARMOEny article, section 3.3 step six: finished
+ *    tokens are collected).
+ *
+ * Return codes: 0 on success, -1 on a bad argument.
+ */
+#include "moe_oracle.h"
+
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* ---- element access ----------------------------------------------------- */
+
+static double bf16_bits_to_double(uint16_t b) {
+  uint32_t u = (uint32_t)b << 16;
+  float f;
+  memcpy(&f, &u, 4);
+  return (double)f;
+}
+
+/* Activation element i of a fp32 or bf16 array. */
+static double act_at(const void* x, int dtype, int64_t i) {
+  if (dtype == ORC_F32) return (double)((const float*)x)[i];
+  return bf16_bits_to_double(((const uint16_t*)x)[i]);
+}
+
+/* Weight element i of expert matrix storage; for int8 the per-output-channel
+ * scale of column n multiplies the integer. */
+static double w_at(const void* w, const float* s, int dtype, int64_t i, int64_t scale_i) {
+  switch (dtype) {
+    case ORC_F32: return (double)((const float*)w)[i];
+    case ORC_BF16: return bf16_bits_to_double(((const uint16_t*)w)[i]);
+    default: return (double)((const int8_t*)w)[i] * (double)s[scale_i];
+  }
+}
+
+/* ---- router ------------------------------------------------------------- */
+
+int orc_router_logits(const void* x, int x_dtype, const float* wg, const float* bias, int T, int m, int E,
+                      float* logits) {
+  if (T < 0 || m < 1 || E < 1 || (T > 0 && (!x || !wg || !logits))) return -1;
+  if (x_dtype != ORC_F32 && x_dtype != ORC_BF16) return -1;
+  for (int t = 0; t < T; ++t) {
+    for (int e = 0; e < E; ++e) {
+      double s = act_at(x, x_dtype, (int64_t)t * m) * (double)wg[e];
+      for (int i = 1; i < m; ++i) s += act_at(x, x_dtype, (int64_t)t * m + i) * (double)wg[(int64_t)i * E + e];
+      if (bias) s += (double)bias[e];
+      logits[(int64_t)t * E + e] = (float)s;
+    }
+  }
+  return 0;
+}
+
+/* ---- top-k and gate weights --------------------------------------------- */
+
+/* 1 if expert a (logit va) ranks before expert b (logit vb). */
+static int ranks_before(float va, int a, float vb, int b) {
+  const int na = isnan(va), nb = isnan(vb);
+  if (na || nb) {
+    if (na && nb) return a < b;
+    return nb; /* a number ranks before NaN */
+  }
+  if (va > vb) return 1;
+  if (va < vb) return 0;
+  return a < b; /* equal values (including +0 and -0): lower index first */
+}
+
+int orc_topk(const float* logits, int T, int E, int k, int32_t* idx, float* w) {
+  if (T < 0 || E < 1 || E > ORC_MAX_E || k < 1 || k > E) return -1;
+  int order[ORC_MAX_E];
+  for (int t = 0; t < T; ++t) {
+    const float* l = logits + (int64_t)t * E;
+    /* stable insertion sort of 0..E-1 by the ranking */
+    for (int e = 0; e < E; ++e) {
+      int j = e;
+      while (j > 0 && ranks_before(l[e], e, l[order[j - 1]], order[j - 1])) {
+        order[j] = order[j - 1];
+        --j;
+      }
+      order[j] = e;
+    }
+    const double l0 = (double)l[order[0]];
+    double denom = 0.0;
+    for (int j = 0; j < k; ++j) denom += exp((double)l[order[j]] - l0);
+    for (int j = 0; j < k; ++j) {
+      idx[(int64_t)t * k + j] = order[j];
+      w[(int64_t)t * k + j] = (float)(exp((double)l[order[j]] - l0) / denom);
+    }
+  }
+  return 0;
+}
+
+/* ---- dispatch ----------------------------------------------------------- */
+
+int orc_dispatch(const int32_t* idx, int T, int E, int k, int32_t* counts, int32_t* offsets, int32_t* perm,
+                 int32_t* inv_perm) {
+  if (T < 0 || E < 1 || k < 1) return -1;
+  const int64_t n = (int64_t)T * k;
+  for (int64_t a = 0; a < n; ++a)
+    if (idx[a] < 0 || idx[a] >= E) return -1;
+  for (int e = 0; e < E; ++e) counts[e] = 0;
+  for (int64_t a = 0; a < n; ++a) counts[idx[a]] += 1;
+  offsets[0] = 0;
+  for (int e = 0; e < E; ++e) offsets[e + 1] = offsets[e] + counts[e];
+  int32_t* cursor = (int32_t*)calloc((size_t)E, sizeof(int32_t));
+  if (!cursor) return -1;
+  for (int64_t a = 0; a < n; ++a) {
+    const int e = idx[a];
+    perm[offsets[e] + cursor[e]] = (int32_t)a;
+    cursor[e] += 1;
+  }
+  free(cursor);
+  for (int64_t r = 0; r < n; ++r) inv_perm[perm[r]] = (int32_t)r;
+  return 0;
+}
+
+/* ---- one expert on one activation row ----------------------------------- */
+
+static double silu(double z) { return z / (1.0 + exp(-z)); }
+
+/* x[m] (double) -> o[m] (double) through expert e.  Scratch: g[p], u[p].
+ * ops[0] += multiplies+adds of the dot products, ops[1] += activation
+ * evaluations (ReLU or SiLU), ops[2] += the SwiGLU elementwise products. */
+static void expert_row(const orc_experts* X, int e, const double* x, double* g, double* u, double* o,
+                       uint64_t ops[3]) {
+  const int m = X->m, p = X->p;
+  const int64_t in_base = (int64_t)e * m * p;  /* [E][m][p] */
+  const int64_t out_base = (int64_t)e * p * m; /* [E][p][m] */
+  const int64_t s_in = (int64_t)e * p, s_out = (int64_t)e * m;
+  const int swiglu = (X->kind == ORC_SWIGLU);
+
+  /* g = x*W1 (and u = x*W3): every g[n] is the length-m dot product in
+   * increasing i, started with the i = 0 product. */
+  for (int n = 0; n < p; ++n) {
+    g[n] = x[0] * w_at(X->w1, X->s1, X->w_dtype, in_base + n, s_in + n);
+    if (swiglu) u[n] = x[0] * w_at(X->w3, X->s3, X->w_dtype, in_base + n, s_in + n);
+  }
+  for (int i = 1; i < m; ++i) {
+    const int64_t row = in_base + (int64_t)i * p;
+    for (int n = 0; n < p; ++n) {
+      g[n] += x[i] * w_at(X->w1, X->s1, X->w_dtype, row + n, s_in + n);
+      if (swiglu) u[n] += x[i] * w_at(X->w3, X->s3, X->w_dtype, row + n, s_in + n);
+    }
+  }
+  const uint64_t dots_in = (uint64_t)p * (uint64_t)(2 * (int64_t)m - 1);
+  ops[0] += swiglu ? 2 * dots_in : dots_in;
+
+  /* h overwrites g, kept in double (not rounded) */
+  for (int n = 0; n < p; ++n) g[n] = swiglu ? silu(g[n]) * u[n] : (g[n] > 0.0 ? g[n] : 0.0);
+  ops[1] += (uint64_t)p;
+  if (swiglu) ops[2] += (uint64_t)p;
+
+  /* o = h*W2 */
+  for (int j = 0; j < m; ++j) o[j] = g[0] * w_at(X->w2, X->s2, X->w_dtype, out_base + j, s_out + j);
+  for (int n = 1; n < p; ++n) {
+    const int64_t row = out_base + (int64_t)n * m;
+    for (int j = 0; j < m; ++j) o[j] += g[n] * w_at(X->w2, X->s2, X->w_dtype, row + j, s_out + j);
+  }
+  ops[0] += (uint64_t)m * (uint64_t)(2 * (int64_t)p - 1);
+}
+
+static int check_experts(const orc_experts* X) {
+  if (!X || X->m < 1 || X->p < 1 || X->E < 1 || !X->w1 || !X->w2) return -1;
+  if (X->kind != ORC_RELU && X->kind != ORC_SWIGLU) return -1;
+  if (X->kind == ORC_SWIGLU && !X->w3) return -1;
+  if (X->w_dtype == ORC_I8 && (!X->s1 || !X->s2 || (X->kind == ORC_SWIGLU && !X->s3))) return -1;
+  if (X->w_dtype != ORC_F32 && X->w_dtype != ORC_BF16 && X->w_dtype != ORC_I8) return -1;
+  return 0;
+}
+
+int orc_expert_apply(const orc_experts* X, int e, const double* x, double* o, uint64_t* ops3) {
+  if (check_experts(X) || e < 0 || e >= X->E) return -1;
+  double* g = (double*)malloc(sizeof(double) * (size_t)X->p);
+  double* u = (double*)malloc(sizeof(double) * (size_t)X->p);
+  if (!g || !u) { free(g); free(u); return -1; }
+  uint64_t ops[3] = {0, 0, 0};
+  expert_row(X, e, x, g, u, o, ops);
+  if (ops3) { ops3[0] += ops[0]; ops3[1] += ops[1]; ops3[2] += ops[2]; }
+  free(g);
+  free(u);
+  return 0;
+}
+
+/* Permuted expert rows: out[i] = FFN_{e}(x[perm[r]/k]) for r = rows[i], with
+ * e the expert whose offsets segment holds r.  rows == NULL means all
+ * T*k rows in order. */
+int orc_expert_rows(const orc_experts* X, const void* x, int x_dtype, int T, int k, const int32_t* perm,
+                    const int32_t* offsets, const int32_t* rows, int nrows, double* out, uint64_t* ops3) {
+  if (check_experts(X) || T < 0 || k < 1 || (x_dtype != ORC_F32 && x_dtype != ORC_BF16)) return -1;
+  const int m = X->m, p = X->p, E = X->E;
+  const int64_t n_all = (int64_t)T * k;
+  if (!rows) nrows = (int)n_all;
+  int bad = 0;
+  uint64_t o0 = 0, o1 = 0, o2 = 0;
+#pragma omp parallel reduction(+ : o0, o1, o2) reduction(| : bad)
+  {
+    double* g = (double*)malloc(sizeof(double) * (size_t)p);
+    double* u = (double*)malloc(sizeof(double) * (size_t)p);
+    double* xr = (double*)malloc(sizeof(double) * (size_t)m);
+    if (!g || !u || !xr) bad = 1;
+#pragma omp for schedule(dynamic, 1)
+    for (int i = 0; i < nrows; ++i) {
+      if (bad) continue;
+      const int64_t r = rows ? rows[i] : i;
+      if (r < 0 || r >= n_all) { bad = 1; continue; }
+      int e = 0;
+      while (e < E && !(offsets[e] <= r && r < offsets[e + 1])) ++e;
+      if (e == E) { bad = 1; continue; }
+      const int64_t t = perm[r] / k;
+      for (int c = 0; c < m; ++c) xr[c] = act_at(x, x_dtype, t * m + c);
+      uint64_t ops[3] = {0, 0, 0};
+      expert_row(X, e, xr, g, u, out + (int64_t)i * m, ops);
+      o0 += ops[0]; o1 += ops[1]; o2 += ops[2];
+    }
+    free(g); free(u); free(xr);
+  }
+  if (ops3) { ops3[0] += o0; ops3[1] += o1; ops3[2] += o2; }
+  return bad ? -1 : 0;
+}
+
+/* ---- combine ------------------------------------------------------------ */
+
+/* Selections of token t in ascending expert index (ties keep slot order). */
+static void ascending_slots(const int32_t* idx_t, int k, int* slot) {
+  for (int j = 0; j < k; ++j) {
+    int i = j;
+    while (i > 0 && idx_t[slot[i - 1]] > idx_t[j]) { slot[i] = slot[i - 1]; --i; }
+    slot[i] = j;
+  }
+}
+
+int orc_combine(const double* y_perm, const int32_t* inv_perm, const int32_t* idx, const float* w, int T, int m,
+                int k, double* y) {
+  if (T < 0 || m < 1 || k < 1 || k > ORC_MAX_E) return -1;
+  int slot[ORC_MAX_E];
+  for (int t = 0; t < T; ++t) {
+    ascending_slots(idx + (int64_t)t * k, k, slot);
+    double* yt = y + (int64_t)t * m;
+    for (int c = 0; c < m; ++c) yt[c] = 0.0;
+    for (int s = 0; s < k; ++s) {
+      const int j = slot[s];
+      const double wj = (double)w[(int64_t)t * k + j];
+      const double* o = y_perm + (int64_t)inv_perm[(int64_t)t * k + j] * m;
+      for (int c = 0; c < m; ++c) yt[c] += wj * o[c];
+    }
+  }
+  return 0;
+}
+
+/* ---- end to end on selected tokens -------------------------------------- */
+
+/*
+ * y[i] for token tokens[i], straight from the definition: its logits (or the
+ * given fp32 logits when logits_in != NULL), its top-k and gate weights, its
+ * k expert outputs and their weighted sum in ascending expert index.  The
+ * token's selections and weights are written to idx_out/w_out when given.
+ */
+int orc_forward_tokens(const orc_experts* X, const void* x, int x_dtype, const float* wg, const float* bias,
+                       const float* logits_in, int T, int k, const int32_t* tokens, int ntok, double* y,
+                       int32_t* idx_out, float* w_out, uint64_t* ops3) {
+  if (check_experts(X) || T < 0 || k < 1 || k > X->E || X->E > ORC_MAX_E) return -1;
+  const int m = X->m, p = X->p, E = X->E;
+  int bad = 0;
+  uint64_t o0 = 0, o1 = 0, o2 = 0;
+#pragma omp parallel reduction(+ : o0, o1, o2) reduction(| : bad)
+  {
+    double* g = (double*)malloc(sizeof(double) * (size_t)p);
+    double* u = (double*)malloc(sizeof(double) * (size_t)p);
+    double* xr = (double*)malloc(sizeof(double) * (size_t)m);
+    double* o = (double*)malloc(sizeof(double) * (size_t)m);
+    if (!g || !u || !xr || !o) bad = 1;
+#pragma omp for schedule(dynamic, 1)
+    for (int i = 0; i < ntok; ++i) {
+      if (bad) continue;
+      const int t = tokens[i];
+      if (t < 0 || t >= T) { bad = 1; continue; }
+      float lg[ORC_MAX_E];
+      int32_t sel[ORC_MAX_E];
+      float wt[ORC_MAX_E];
+      if (logits_in) {
+        for (int e = 0; e < E; ++e) lg[e] = logits_in[(int64_t)t * E + e];
+      } else {
+        orc_router_logits((const char*)x + (int64_t)t * m * (x_dtype == ORC_F32 ? 4 : 2), x_dtype, wg, bias, 1, m,
+                          E, lg);
+      }
+      orc_topk(lg, 1, E, k, sel, wt);
+      for (int c = 0; c < m; ++c) xr[c] = act_at(x, x_dtype, (int64_t)t * m + c);
+      int slot[ORC_MAX_E];
+      ascending_slots(sel, k, slot);
+      double* yt = y + (int64_t)i * m;
+      for (int c = 0; c < m; ++c) yt[c] = 0.0;
+      uint64_t ops[3] = {0, 0, 0};
+      for (int s = 0; s < k; ++s) {
+        const int j = slot[s];
+        expert_row(X, sel[j], xr, g, u, o, ops);
+        for (int c = 0; c < m; ++c) yt[c] += (double)wt[j] * o[c];
+      }
+      o0 += ops[0]; o1 += ops[1]; o2 += ops[2];
+      if (idx_out)
+        for (int j = 0; j < k; ++j) idx_out[(int64_t)i * k + j] = sel[j];
+      if (w_out)
+        for (int j = 0; j < k; ++j) w_out[(int64_t)i * k + j] = wt[j];
+    }
+    free(g); free(u); free(xr); free(o);
+  }
+  if (ops3) { ops3[0] += o0; ops3[1] += o1; ops3[2] += o2; }
+  return bad ? -1 : 0;
+}
+
+/* ---- dense brute force (tiny inputs) ------------------------------------ */
+
+/*
+ * y[t] = sum_{e=0}^{E-1} G[t][e] * FFN_e(x_t), with G[t][e] = w[t][j] where
+ * idx[t][j] == e and 0 otherwise: every expert runs on every token and the
+ * gates mask the sum.  Equal to the routed result when the routed sum runs in
+ * ascending expert index.
+ */
+int orc_dense_masked(const orc_experts* X, const void* x, int x_dtype, const int32_t* idx, const float* w, int T,
+                     int k, double* y) {
+  if (check_experts(X) || T < 0 || k < 1 || k > X->E) return -1;
+  const int m = X->m, p = X->p, E = X->E;
+  double* g = (double*)malloc(sizeof(double) * (size_t)p);
+  double* u = (double*)malloc(sizeof(double) * (size_t)p);
+  double* xr = (double*)malloc(sizeof(double) * (size_t)m);
+  double* o = (double*)malloc(sizeof(double) * (size_t)m);
+  if (!g || !u || !xr || !o) { free(g); free(u); free(xr); free(o); return -1; }
+  uint64_t ops[3] = {0, 0, 0};
+  for (int t = 0; t < T; ++t) {
+    for (int c = 0; c < m; ++c) xr[c] = act_at(x, x_dtype, (int64_t)t * m + c);
+    double* yt = y + (int64_t)t * m;
+    for (int c = 0; c < m; ++c) yt[c] = 0.0;
+    for (int e = 0; e < E; ++e) {
+      double gate = 0.0;
+      for (int j = 0; j < k; ++j)
+        if (idx[(int64_t)t * k + j] == e) gate = (double)w[(int64_t)t * k + j];
+      expert_row(X, e, xr, g, u, o, ops);
+      for (int c = 0; c < m; ++c) yt[c] += gate * o[c];
+    }
+  }
+  free(g); free(u); free(xr); free(o);
+  return 0;
+}

@@ -1,0 +1,42 @@
+/*
+ * CPU oracle for one MoE-layer forward pass -- TEST INFRASTRUCTURE ONLY.
+ * Only tests/, __graft_entry__.smoke() and bench.py's cpu_baseline leg may
+ * load it.  It shares no code, header or constant with the HIP library.
+ * Definitions and citations: moe_oracle.c.
+ */
+#ifndef MOE_ORACLE_H
+#define MOE_ORACLE_H
+
+#include <stdint.h>
+
+#define ORC_MAX_E 64
+
+enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_I8 = 2 };
+enum { ORC_RELU = 0, ORC_SWIGLU = 1 };
+
+/* Expert weights in canonical row-major layout:
+ * w1 (ReLU MLP W1, or SwiGLU gate) [E][m][p], w3 (SwiGLU up) [E][m][p],
+ * w2 (second / down) [E][p][m]; int8 scales s1, s3 [E][p], s2 [E][m]. */
+typedef struct {
+  int m, p, E, kind, w_dtype;
+  const void *w1, *w3, *w2;
+  const float *s1, *s3, *s2;
+} orc_experts;
+
+int orc_router_logits(const void* x, int x_dtype, const float* wg, const float* bias, int T, int m, int E,
+                      float* logits);
+int orc_topk(const float* logits, int T, int E, int k, int32_t* idx, float* w);
+int orc_dispatch(const int32_t* idx, int T, int E, int k, int32_t* counts, int32_t* offsets, int32_t* perm,
+                 int32_t* inv_perm);
+int orc_expert_apply(const orc_experts* X, int e, const double* x, double* o, uint64_t* ops3);
+int orc_expert_rows(const orc_experts* X, const void* x, int x_dtype, int T, int k, const int32_t* perm,
+                    const int32_t* offsets, const int32_t* rows, int nrows, double* out, uint64_t* ops3);
+int orc_combine(const double* y_perm, const int32_t* inv_perm, const int32_t* idx, const float* w, int T, int m,
+                int k, double* y);
+int orc_forward_tokens(const orc_experts* X, const void* x, int x_dtype, const float* wg, const float* bias,
+                       const float* logits_in, int T, int k, const int32_t* tokens, int ntok, double* y,
+                       int32_t* idx_out, float* w_out, uint64_t* ops3);
+int orc_dense_masked(const orc_experts* X, const void* x, int x_dtype, const int32_t* idx, const float* w, int T,
+                     int k, double* y);
+
+#endif
