@@ -1,0 +1,206 @@
+/*
+ * moe_gemv.h -- C ABI of a mixture-of-experts layer forward pass for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * Problem statement.  An MoE layer replaces a transformer block's FFN with a
+ * router and E experts; the router sends each of the T tokens (hidden size m)
+ * to its top-k experts, each expert is a two-layer MLP with W1 of m x p and
+ * W2 of p x m, and the experts' outputs are gathered back to their tokens
+ * (HARMOEny article, yejing.asia/?p=12: section 1 for the router + expert
+ * structure, section 3.2 "expert prefetch" for the expert x*W1*W2 with W1
+ * m x p and W2 p x m, section 3.3 for route -> dispatch -> expert compute ->
+ * gather).  The expert comes in two forms: the ReLU MLP relu(x W1) W2 and the
+ * SwiGLU form (SiLU(x W1) * (x W3)) W2, whose W3 is a second m x p matrix.
+ *
+ * Conventions shared by every entry point:
+ *  - Tensor pointers are DEVICE pointers owned by the caller, row-major and
+ *    16-byte aligned.  bf16 tensors hold raw bfloat16 bit patterns.
+ *  - `stream` is a hipStream_t (NULL = the null stream).  Every call except
+ *    moe_weights_create/moe_weights_destroy/moe_profile_end only enqueues work
+ *    on that stream and returns without synchronising.
+ *  - Every call returns a moe_status.  Arguments are validated before
+ *    anything is enqueued: a non-OK status means nothing was launched.
+ *    moe_last_error() gives a message for the calling thread's last failure.
+ *  - The library keeps no caller pointer after a call returns.  The only
+ *    memory it owns is the packed weight store inside a moe_weights.
+ *  - Calls are reentrant.  One moe_weights may serve several streams at once
+ *    if every in-flight call has its own workspace.
+ *  - Shape limits: 1 <= E <= 64, 1 <= k <= E, m and p positive multiples of
+ *    64, T*k < 2^31.  T == 0 is a successful no-op.
+ *  - Supported (activation / weight / expert) combinations: F32/F32/RELU,
+ *    F32/F32/SWIGLU, BF16/BF16/RELU, BF16/BF16/SWIGLU, BF16/I8/SWIGLU,
+ *    BF16/I8/RELU.  Anything else returns MOE_ERR_UNSUPPORTED.
+ */
+#ifndef MOE_GEMV_H
+#define MOE_GEMV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1, /* NULL required pointer, bad size, k > E, shape mismatch, misalignment */
+  MOE_ERR_UNSUPPORTED = 2, /* valid but outside the limits above */
+  MOE_ERR_WORKSPACE = 3,   /* workspace missing or smaller than moe_workspace_size() */
+  MOE_ERR_HIP = 4,         /* a HIP runtime call or kernel launch failed */
+  MOE_ERR_OOM = 5          /* device allocation failed */
+} moe_status;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_I8 = 2 } moe_dtype;
+typedef enum { MOE_MLP_RELU = 0, MOE_SWIGLU = 1 } moe_ffn_kind;
+
+#define MOE_MAX_EXPERTS 64
+/* moe_route_topk flag: skip the router product and read fp32 logits from `logits`. */
+#define MOE_ROUTE_LOGITS_IN 1u
+
+/* Opaque, library-owned expert weights in the packed device layout. */
+typedef struct moe_weights moe_weights;
+
+/* Message describing the calling thread's most recent failure ("" if none). */
+const char* moe_last_error(void);
+
+/* ABI version of this header (bumped on incompatible changes). */
+int moe_abi_version(void);
+
+/*
+ * moe_weights_create -- take a layer's expert weights and re-lay them out
+ * once, at initialisation, so that the forward pass streams every weight
+ * byte in full 128-byte lines (the DeepSpeed-Inference summary,
+ * datalearner.com, section 3 "SBI-GeMM", part 3: weights transposed at
+ * initialisation so each thread reads consecutive input-dimension
+ * elements of one output column).
+ *
+ *  m, p, E       hidden size, expert inner size, number of experts.
+ *  kind          MOE_MLP_RELU (w1 = W1, w2 = W2, w_up must be NULL) or
+ *                MOE_SWIGLU (w1 = gate W1, w_up = up W3, w2 = down W2).
+ *  w_dtype       MOE_F32, MOE_BF16 or MOE_I8.
+ *  w1, w_up      device [E][m][p] in w_dtype.
+ *  w2            device [E][p][m] in w_dtype.
+ *  s1, s_up      MOE_I8 only: device fp32 [E][p] per-output-channel scales
+ *                of w1 and w_up (the weight is q * s); NULL otherwise.
+ *  s2            MOE_I8 only: device fp32 [E][m] scales of w2; NULL otherwise.
+ *  stream        packing runs on this stream; the call synchronises it
+ *                before returning, so the inputs may be freed afterwards.
+ *  out           receives the handle; release it with moe_weights_destroy.
+ * Errors: INVALID_ARG, UNSUPPORTED, OOM, HIP.  On error *out is NULL.
+ */
+int moe_weights_create(int m, int p, int E, int kind, int w_dtype, const void* w1, const void* w_up,
+                       const void* w2, const float* s1, const float* s_up, const float* s2, void* stream,
+                       moe_weights** out);
+
+/* Free a handle from moe_weights_create (NULL is accepted).  Synchronises the device. */
+int moe_weights_destroy(moe_weights* w);
+
+/* Bytes of device workspace moe_layer_forward / moe_expert_ffn need for T tokens at top-k. */
+int moe_workspace_size(const moe_weights* w, int T, int k, size_t* bytes);
+
+/*
+ * moe_route_topk -- router product, top-k and gate weights for T tokens.
+ * The gating network runs on the GPU and maps every token to its experts
+ * (GPU-cache article, coreui.cn, section 3.1; HARMOEny article, section 3.3
+ * step one).
+ *   logits[t][e] = sum_i x[t][i] * w_router[i][e] (+ b_router[e]), fp32.
+ *   Experts are ranked by (logit descending, expert index ascending); NaN
+ *   ranks below every number and +0 equals -0.  topk_idx[t][j] is the j-th
+ *   ranked expert, and topk_w[t][j] = exp(l_j - l_0) / sum_{i<k} exp(l_i - l_0)
+ *   (softmax over the selected k).
+ *
+ *  x          device [T][m], x_dtype MOE_F32 or MOE_BF16 (ignored with LOGITS_IN).
+ *  w_router   device fp32 [m][E] (ignored with LOGITS_IN).
+ *  b_router   device fp32 [E] or NULL.
+ *  flags      0 or MOE_ROUTE_LOGITS_IN (read logits instead of computing them).
+ *  logits     device fp32 [T][E]: output (may be NULL) or, with LOGITS_IN, input.
+ *  topk_idx   device int32 [T][k] output.   topk_w  device fp32 [T][k] output.
+ * Errors: INVALID_ARG, UNSUPPORTED, HIP.
+ */
+int moe_route_topk(const void* x, int x_dtype, const float* w_router, const float* b_router, int T, int m, int E,
+                   int k, unsigned flags, float* logits, int32_t* topk_idx, float* topk_w, void* stream);
+
+/*
+ * moe_dispatch -- group the T*k assignments (a = t*k + j) by expert: the
+ * single-GPU form of sending tokens to their experts (HARMOEny article,
+ * section 3.3 step four).
+ *   counts[e]  = number of assignments to expert e;
+ *   offsets    = exclusive prefix sum of counts, offsets[E] = T*k;
+ *   perm[r]    = assignment id at permuted row r: expert-major, and within
+ *                an expert in increasing assignment id (stable);
+ *   inv_perm[a]= the row r with perm[r] = a.
+ *  topk_idx   device int32 [T*k] input; an id outside [0, E) is clamped into
+ *             range (the result stays a valid permutation, its grouping is
+ *             then meaningless).
+ *  counts [E], offsets [E+1], perm [T*k], inv_perm [T*k]: device int32 outputs.
+ * Errors: INVALID_ARG, UNSUPPORTED, HIP.
+ */
+int moe_dispatch(const int32_t* topk_idx, int T, int E, int k, int32_t* counts, int32_t* offsets, int32_t* perm,
+                 int32_t* inv_perm, void* stream);
+
+/*
+ * moe_expert_ffn -- every expert on its rows: for each permuted row r of
+ * expert e (offsets[e] <= r < offsets[e+1]) with token t = perm[r] / k,
+ *   y_perm[r] = relu(x_t W1_e) W2_e              (MOE_MLP_RELU)
+ *   y_perm[r] = (SiLU(x_t W1_e) * (x_t W3_e)) W2_e  (MOE_SWIGLU)
+ * unweighted, fp32 (HARMOEny article, section 3.2: the expert is x*W1*W2).
+ * For bf16/int8 weights the hidden activation is rounded to bf16 between the
+ * two projections; accumulation is fp32.
+ *  w          handle from moe_weights_create (m, p, E must match).
+ *  x          device [T][m] in x_dtype.
+ *  perm, offsets   from moe_dispatch (device int32).
+ *  y_perm     device fp32 [T*k][m] output.
+ *  workspace  device, >= moe_workspace_size(w, T, k) bytes, 256-byte aligned.
+ * Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE, HIP.
+ */
+int moe_expert_ffn(const moe_weights* w, const void* x, int x_dtype, int T, int m, int p, int E, int k,
+                   const int32_t* perm, const int32_t* offsets, float* y_perm, void* workspace, size_t ws_bytes,
+                   void* stream);
+
+/*
+ * moe_combine -- gather the expert outputs back to their tokens, weighted
+ * (HARMOEny article, section 3.3 step six; GPU-cache article, section 3.1):
+ *   y[t] = sum_{j<k} topk_w[t][j] * y_perm[inv_perm[t*k + j]]   (fp32 sum)
+ *  y_perm     device fp32 [T*k][m];  inv_perm  device int32 [T*k];
+ *  topk_w     device fp32 [T][k];    y  device [T][m] in y_dtype (F32 or BF16).
+ * Errors: INVALID_ARG, UNSUPPORTED, HIP.
+ */
+int moe_combine(const float* y_perm, const int32_t* inv_perm, const float* topk_w, int T, int m, int k, void* y,
+                int y_dtype, void* stream);
+
+/*
+ * moe_layer_forward -- the whole layer: route + top-k, dispatch, experts and
+ * the weighted combine, fused where possible and all on `stream`, with no
+ * host synchronisation.
+ *  w_router, b_router, x, x_dtype   as in moe_route_topk.
+ *  y          device [T][m] output in y_dtype (F32 or BF16).
+ *  workspace  device, >= moe_workspace_size(w, T, k) bytes, 256-byte aligned.
+ *  dbg_*      optional device outputs of the intermediate stages (each may be
+ *             NULL): topk_idx [T][k], topk_w [T][k], logits [T][E],
+ *             counts [E], offsets [E+1], perm [T*k].
+ * Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE, HIP.
+ */
+int moe_layer_forward(const moe_weights* w, const float* w_router, const float* b_router, const void* x, int x_dtype,
+                      int T, int m, int p, int E, int k, void* y, int y_dtype, void* workspace, size_t ws_bytes,
+                      int32_t* dbg_topk_idx, float* dbg_topk_w, float* dbg_logits, int32_t* dbg_counts,
+                      int32_t* dbg_offsets, int32_t* dbg_perm, void* stream);
+
+/*
+ * Measurement aid (not part of the layer).  Between moe_profile_begin and
+ * moe_profile_end every kernel the library launches is bracketed by HIP
+ * events on its own stream.  moe_profile_end waits for the last event and
+ * folds the durations into per-kernel totals readable with
+ * moe_profile_query(name, &total_ms, &launches).  Process-global, not
+ * thread-safe; max_launches bounds the events recorded (later launches are
+ * not timed).  Kernel names: "route_topk", "dispatch", "ffn_up", "ffn_down",
+ * "ffn_f32_up", "ffn_f32_down", "combine", "finalize", "fill".
+ */
+int moe_profile_begin(int max_launches);
+int moe_profile_end(void);
+int moe_profile_query(const char* kernel, double* total_ms, int* launches);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_GEMV_H */

@@ -1,0 +1,162 @@
+"""Python binding of libmoe_gemv.so (include/moe_gemv.h): argument marshalling only.
+
+Every function has the C name and argument order.  Tensor arguments are
+torch tensors on the GPU (or None for an optional pointer); they are passed
+as raw device pointers.  ``stream`` defaults to torch's current stream.  A
+non-zero status raises :class:`MoeError` carrying ``moe_last_error()``.
+
+All computation happens in the HIP library: there is no Python or CPU
+fallback, and importing the binding fails loudly when the library is absent.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe_gemv.so")
+
+MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP, MOE_ERR_OOM = range(6)
+MOE_F32, MOE_BF16, MOE_I8 = 0, 1, 2
+MOE_MLP_RELU, MOE_SWIGLU = 0, 1
+MOE_ROUTE_LOGITS_IN = 1
+MOE_MAX_EXPERTS = 64
+
+STATUS_NAMES = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARG", 2: "MOE_ERR_UNSUPPORTED", 3: "MOE_ERR_WORKSPACE",
+                4: "MOE_ERR_HIP", 5: "MOE_ERR_OOM"}
+
+
+class MoeError(RuntimeError):
+    def __init__(self, fn: str, status: int, message: str):
+        super().__init__(f"{fn}: {STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+        self.message = message
+
+
+_lib = None
+
+_vp, _i32, _u32, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_uint, ctypes.c_size_t
+_SIGS = {
+    "moe_last_error": ([], ctypes.c_char_p),
+    "moe_abi_version": ([], _i32),
+    "moe_weights_create": ([_i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                            ctypes.POINTER(_vp)], _i32),
+    "moe_weights_destroy": ([_vp], _i32),
+    "moe_workspace_size": ([_vp, _i32, _i32, ctypes.POINTER(_sz)], _i32),
+    "moe_route_topk": ([_vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32, _u32, _vp, _vp, _vp, _vp], _i32),
+    "moe_dispatch": ([_vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp], _i32),
+    "moe_expert_ffn": ([_vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _sz, _vp], _i32),
+    "moe_combine": ([_vp, _vp, _vp, _i32, _i32, _i32, _vp, _i32, _vp], _i32),
+    "moe_layer_forward": ([_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _i32, _vp, _sz,
+                           _vp, _vp, _vp, _vp, _vp, _vp, _vp], _i32),
+    "moe_profile_begin": ([_i32], _i32),
+    "moe_profile_end": ([], _i32),
+    "moe_profile_query": ([ctypes.c_char_p, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_i32)], _i32),
+}
+
+
+def lib():
+    """Load libmoe_gemv.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                              "(or python mixture_experts_layer_gemv_amd/build.py)")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (args, res) in _SIGS.items():
+            f = getattr(L, name)
+            f.argtypes = args
+            f.restype = res
+        _lib = L
+    return _lib
+
+
+def _p(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _s(stream):
+    if stream is None:
+        import torch
+
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(fn, rc):
+    if rc != MOE_OK:
+        raise MoeError(fn, rc, lib().moe_last_error().decode())
+
+
+def moe_last_error() -> str:
+    return lib().moe_last_error().decode()
+
+
+def moe_abi_version() -> int:
+    return lib().moe_abi_version()
+
+
+def moe_weights_create(m, p, E, kind, w_dtype, w1, w_up, w2, s1=None, s_up=None, s2=None, stream=None):
+    h = _vp()
+    _check("moe_weights_create", lib().moe_weights_create(m, p, E, kind, w_dtype, _p(w1), _p(w_up), _p(w2), _p(s1),
+                                                          _p(s_up), _p(s2), _s(stream), ctypes.byref(h)))
+    return h
+
+
+def moe_weights_destroy(w):
+    _check("moe_weights_destroy", lib().moe_weights_destroy(w))
+
+
+def moe_workspace_size(w, T, k) -> int:
+    n = _sz()
+    _check("moe_workspace_size", lib().moe_workspace_size(w, T, k, ctypes.byref(n)))
+    return n.value
+
+
+def moe_route_topk(x, x_dtype, w_router, b_router, T, m, E, k, flags, logits, topk_idx, topk_w, stream=None):
+    _check("moe_route_topk", lib().moe_route_topk(_p(x), x_dtype, _p(w_router), _p(b_router), T, m, E, k, flags,
+                                                  _p(logits), _p(topk_idx), _p(topk_w), _s(stream)))
+
+
+def moe_dispatch(topk_idx, T, E, k, counts, offsets, perm, inv_perm, stream=None):
+    _check("moe_dispatch", lib().moe_dispatch(_p(topk_idx), T, E, k, _p(counts), _p(offsets), _p(perm),
+                                              _p(inv_perm), _s(stream)))
+
+
+def moe_expert_ffn(w, x, x_dtype, T, m, p, E, k, perm, offsets, y_perm, workspace, ws_bytes, stream=None):
+    _check("moe_expert_ffn", lib().moe_expert_ffn(w, _p(x), x_dtype, T, m, p, E, k, _p(perm), _p(offsets),
+                                                  _p(y_perm), _p(workspace), ws_bytes, _s(stream)))
+
+
+def moe_combine(y_perm, inv_perm, topk_w, T, m, k, y, y_dtype, stream=None):
+    _check("moe_combine", lib().moe_combine(_p(y_perm), _p(inv_perm), _p(topk_w), T, m, k, _p(y), y_dtype,
+                                            _s(stream)))
+
+
+def moe_layer_forward(w, w_router, b_router, x, x_dtype, T, m, p, E, k, y, y_dtype, workspace, ws_bytes,
+                      dbg_topk_idx=None, dbg_topk_w=None, dbg_logits=None, dbg_counts=None, dbg_offsets=None,
+                      dbg_perm=None, stream=None):
+    _check("moe_layer_forward", lib().moe_layer_forward(
+        w, _p(w_router), _p(b_router), _p(x), x_dtype, T, m, p, E, k, _p(y), y_dtype, _p(workspace), ws_bytes,
+        _p(dbg_topk_idx), _p(dbg_topk_w), _p(dbg_logits), _p(dbg_counts), _p(dbg_offsets), _p(dbg_perm),
+        _s(stream)))
+
+
+def moe_profile_begin(max_launches: int):
+    _check("moe_profile_begin", lib().moe_profile_begin(max_launches))
+
+
+def moe_profile_end():
+    _check("moe_profile_end", lib().moe_profile_end())
+
+
+def moe_profile_query(kernel: str):
+    ms, n = ctypes.c_double(), _i32()
+    _check("moe_profile_query", lib().moe_profile_query(kernel.encode(), ctypes.byref(ms), ctypes.byref(n)))
+    return ms.value, n.value

@@ -1,0 +1,469 @@
+// C ABI of the MoE-layer forward pass (declared in include/moe_gemv.h):
+// argument validation, the packed weight store, workspace carving and the
+// launch sequence.  Nothing here computes; every step of the layer runs in
+// the gfx950 kernels.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <map>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "moe_gemv.h"
+#include "moe_kernels.hpp"
+
+struct moe_weights {
+  int m = 0, p = 0, E = 0, kind = 0, w_dtype = 0;
+  void* buf = nullptr;
+  size_t bytes = 0;
+  void* up = nullptr;    // packed gate(+up) [E][p/16][U][G] (bf16/i8), or fp32 w1 [E][m][p]
+  void* up3 = nullptr;   // fp32 SwiGLU only: w3 [E][m][p]
+  void* down = nullptr;  // packed down [E][m/16][U][1] (bf16/i8), or fp32 w2 [E][p][m]
+  float* s_gate = nullptr;
+  float* s_up = nullptr;
+  float* s_down = nullptr;
+};
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int ok() {
+  g_err.clear();
+  return MOE_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+size_t align256(size_t n) { return (n + 255) & ~size_t(255); }
+hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+#define MOE_TRY_HIP(expr)                                                                       \
+  do {                                                                                          \
+    hipError_t e_ = (expr);                                                                     \
+    if (e_ != hipSuccess) return fail(MOE_ERR_HIP, "%s failed: %s", #expr, hipGetErrorString(e_)); \
+  } while (0)
+
+// ---- kernel timing (measurement aid) ------------------------------------------
+
+struct Prof {
+  std::mutex mu;
+  bool on = false;
+  int max = 0, n = 0;
+  std::vector<hipEvent_t> ev;
+  std::vector<const char*> name;
+  std::map<std::string, std::pair<double, int>> total;
+};
+Prof g_prof;
+
+template <class F>
+hipError_t run(const char* name, hipStream_t s, F&& launch) {
+  if (g_prof.on && g_prof.n < g_prof.max) {
+    const int i = g_prof.n++;
+    g_prof.name[i] = name;
+    (void)hipEventRecord(g_prof.ev[2 * i], s);
+    const hipError_t e = launch();
+    (void)hipEventRecord(g_prof.ev[2 * i + 1], s);
+    return e;
+  }
+  return launch();
+}
+
+// ---- shape / dtype rules ---------------------------------------------------------
+
+int check_shape(int T, int m, int p, int E, int k) {
+  if (T < 0) return fail(MOE_ERR_INVALID_ARG, "T=%d must be >= 0", T);
+  if (m <= 0 || p <= 0) return fail(MOE_ERR_INVALID_ARG, "m=%d and p=%d must be positive", m, p);
+  if (E < 1) return fail(MOE_ERR_INVALID_ARG, "E=%d must be >= 1", E);
+  if (k < 1 || k > E) return fail(MOE_ERR_INVALID_ARG, "k=%d must be in [1, E=%d]", k, E);
+  if (E > MOE_MAX_EXPERTS) return fail(MOE_ERR_UNSUPPORTED, "E=%d exceeds %d", E, MOE_MAX_EXPERTS);
+  if (m % 64 || p % 64) return fail(MOE_ERR_UNSUPPORTED, "m=%d and p=%d must be multiples of 64", m, p);
+  if ((long long)T * k > 0x7FFFFFFFLL) return fail(MOE_ERR_UNSUPPORTED, "T*k exceeds 2^31-1");
+  return MOE_OK;
+}
+
+bool valid_dtype(int d) { return d == MOE_F32 || d == MOE_BF16 || d == MOE_I8; }
+
+int check_combo(int x_dtype, int w_dtype) {
+  if (x_dtype != MOE_F32 && x_dtype != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "x dtype %d unsupported", x_dtype);
+  if (w_dtype == MOE_F32 && x_dtype != MOE_F32)
+    return fail(MOE_ERR_UNSUPPORTED, "fp32 weights need fp32 activations");
+  if (w_dtype != MOE_F32 && x_dtype != MOE_BF16)
+    return fail(MOE_ERR_UNSUPPORTED, "bf16/int8 weights need bf16 activations");
+  return MOE_OK;
+}
+
+// Workspace carving, in the order listed.
+struct Ws {
+  size_t logits, idx, w, counts, offsets, perm, inv, h, yacc, total;
+};
+
+Ws ws_layout(const moe_weights* W, int T, int k) {
+  Ws L{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += align256(bytes);
+    return o;
+  };
+  const size_t n = (size_t)T * k;
+  L.logits = take((size_t)T * W->E * 4);
+  L.idx = take(n * 4);
+  L.w = take(n * 4);
+  L.counts = take((size_t)W->E * 4);
+  L.offsets = take((size_t)(W->E + 1) * 4);
+  L.perm = take(n * 4);
+  L.inv = take(n * 4);
+  L.h = take(n * (size_t)W->p * (W->w_dtype == MOE_F32 ? 4 : 2));
+  L.yacc = take((size_t)T * W->m * 4);
+  L.total = off;
+  return L;
+}
+
+int skinny_mt(int T, int k, int E) {
+  const long long avg = ((long long)T * k + E - 1) / E;
+  return avg <= 12 ? 1 : (avg <= 24 ? 2 : 4);
+}
+
+// Both projections of the expert FFN.  h: hidden buffer; down_out: y_acc
+// (weighted, accumulate) or y_perm (rows), selected by `combine`.
+int run_ffn(const moe_weights* W, const void* x, int T, int k, const int32_t* perm, const int32_t* offsets,
+            const float* topk_w, void* h, float* down_out, bool combine, hipStream_t s) {
+  const int m = W->m, p = W->p, E = W->E;
+  const bool swiglu = W->kind == MOE_SWIGLU;
+  if (W->w_dtype == MOE_F32) {
+    moe::F32Args a{};
+    a.perm = perm;
+    a.offsets = offsets;
+    a.topk = k;
+    a.E = E;
+    a.W = E + (int)((long long)T * k / 16);
+    a.topk_w = topk_w;
+    // up: x [T][m] -> H [T*k][p]
+    a.w1 = static_cast<const float*>(W->up);
+    a.w3 = swiglu ? static_cast<const float*>(W->up3) : nullptr;
+    a.act = static_cast<const float*>(x);
+    a.out = static_cast<float*>(h);
+    a.K = m;
+    a.N = p;
+    a.gather = 1;
+    a.epi = swiglu ? moe::EPI_UP_SWIGLU : moe::EPI_UP_RELU;
+    MOE_TRY_HIP(run("ffn_f32_up", s, [&] { return moe::launch_ffn_f32(a, s); }));
+    // down: H -> y
+    a.w1 = static_cast<const float*>(W->down);
+    a.w3 = nullptr;
+    a.act = static_cast<const float*>(h);
+    a.out = down_out;
+    a.K = p;
+    a.N = m;
+    a.gather = 0;
+    a.epi = combine ? moe::EPI_DOWN_ACC : moe::EPI_DOWN_ROWS;
+    MOE_TRY_HIP(run("ffn_f32_down", s, [&] { return moe::launch_ffn_f32(a, s); }));
+    return MOE_OK;
+  }
+  const bool i8 = W->w_dtype == MOE_I8;
+  const int mt = skinny_mt(T, k, E);
+  const int R = moe::skinny_rows(mt);
+  moe::SkinnyArgs a{};
+  a.perm = perm;
+  a.offsets = offsets;
+  a.topk = k;
+  a.E = E;
+  a.W = E + (int)((long long)T * k / R);
+  a.topk_w = topk_w;
+  if ((long long)(p / 16) * a.W >= 0x7FFFFFF0LL || (long long)(m / 16) * a.W >= 0x7FFFFFF0LL)
+    return fail(MOE_ERR_UNSUPPORTED, "too many work items for one launch (T*k=%lld)", (long long)T * k);
+  a.w = W->up;
+  a.scale0 = W->s_gate;
+  a.scale1 = W->s_up;
+  a.act = static_cast<const uint16_t*>(x);
+  a.h_out = static_cast<uint16_t*>(h);
+  a.K = m;
+  a.N = p;
+  a.gather = 1;
+  const int up_epi = swiglu ? moe::EPI_UP_SWIGLU : moe::EPI_UP_RELU;
+  MOE_TRY_HIP(run("ffn_up", s, [&] { return moe::launch_ffn_skinny(a, up_epi, i8, mt, s); }));
+  a.w = W->down;
+  a.scale0 = W->s_down;
+  a.scale1 = nullptr;
+  a.act = static_cast<const uint16_t*>(h);
+  a.h_out = nullptr;
+  a.f_out = down_out;
+  a.K = p;
+  a.N = m;
+  a.gather = 0;
+  const int dn_epi = combine ? moe::EPI_DOWN_ACC : moe::EPI_DOWN_ROWS;
+  MOE_TRY_HIP(run("ffn_down", s, [&] { return moe::launch_ffn_skinny(a, dn_epi, i8, mt, s); }));
+  return MOE_OK;
+}
+
+int check_weights_match(const moe_weights* w, int m, int p, int E) {
+  if (!w) return fail(MOE_ERR_INVALID_ARG, "weights handle is NULL");
+  if (w->m != m || w->p != p || w->E != E)
+    return fail(MOE_ERR_INVALID_ARG, "shape (m=%d,p=%d,E=%d) does not match the weights (m=%d,p=%d,E=%d)", m, p, E,
+                w->m, w->p, w->E);
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_last_error(void) { return g_err.c_str(); }
+
+int moe_abi_version(void) { return 1; }
+
+int moe_weights_create(int m, int p, int E, int kind, int w_dtype, const void* w1, const void* w_up, const void* w2,
+                       const float* s1, const float* s_up, const float* s2, void* stream, moe_weights** out) {
+  if (!out) return fail(MOE_ERR_INVALID_ARG, "out is NULL");
+  *out = nullptr;
+  if (int rc = check_shape(1, m, p, E, 1)) return rc;
+  if (kind != MOE_MLP_RELU && kind != MOE_SWIGLU) return fail(MOE_ERR_INVALID_ARG, "unknown expert kind %d", kind);
+  if (!valid_dtype(w_dtype)) return fail(MOE_ERR_UNSUPPORTED, "weight dtype %d unsupported", w_dtype);
+  const bool swiglu = kind == MOE_SWIGLU;
+  if (!w1 || !w2 || (swiglu && !w_up)) return fail(MOE_ERR_INVALID_ARG, "required weight pointer is NULL");
+  if (!swiglu && w_up) return fail(MOE_ERR_INVALID_ARG, "w_up must be NULL for the ReLU MLP");
+  const bool i8 = w_dtype == MOE_I8;
+  if (i8 && (!s1 || !s2 || (swiglu && !s_up))) return fail(MOE_ERR_INVALID_ARG, "int8 weights need their scales");
+  if (!i8 && (s1 || s2 || s_up)) return fail(MOE_ERR_INVALID_ARG, "scales are only for int8 weights");
+  if (!aligned16(w1) || !aligned16(w2) || (w_up && !aligned16(w_up)) || (s1 && !aligned16(s1)) ||
+      (s2 && !aligned16(s2)) || (s_up && !aligned16(s_up)))
+    return fail(MOE_ERR_INVALID_ARG, "weight pointers must be 16-byte aligned");
+
+  const hipStream_t s = as_stream(stream);
+  const int G = swiglu ? 2 : 1;
+  size_t up_b, up3_b = 0, dn_b, sc_b = 0;
+  if (w_dtype == MOE_F32) {
+    up_b = (size_t)E * m * p * 4;
+    up3_b = swiglu ? up_b : 0;
+    dn_b = (size_t)E * p * m * 4;
+  } else {
+    up_b = moe::packed_bytes(E, m, p, G, i8);
+    dn_b = moe::packed_bytes(E, p, m, 1, i8);
+    if (i8) sc_b = align256((size_t)E * p * 4) * (swiglu ? 2 : 1) + align256((size_t)E * m * 4);
+  }
+  const size_t total = align256(up_b) + align256(up3_b) + align256(dn_b) + sc_b;
+  moe_weights* W = new (std::nothrow) moe_weights;
+  if (!W) return fail(MOE_ERR_OOM, "host allocation failed");
+  W->m = m;
+  W->p = p;
+  W->E = E;
+  W->kind = kind;
+  W->w_dtype = w_dtype;
+  W->bytes = total;
+  if (hipMalloc(&W->buf, total) != hipSuccess) {
+    delete W;
+    (void)hipGetLastError();
+    return fail(MOE_ERR_OOM, "hipMalloc of %zu bytes for the packed weights failed", total);
+  }
+  char* base = static_cast<char*>(W->buf);
+  size_t off = 0;
+  auto carve = [&](size_t b) {
+    void* q = b ? base + off : nullptr;
+    off += align256(b);
+    return q;
+  };
+  W->up = carve(up_b);
+  W->up3 = carve(up3_b);
+  W->down = carve(dn_b);
+  hipError_t e = hipSuccess;
+  if (w_dtype == MOE_F32) {
+    e = hipMemcpyAsync(W->up, w1, up_b, hipMemcpyDeviceToDevice, s);
+    if (e == hipSuccess && swiglu) e = hipMemcpyAsync(W->up3, w_up, up3_b, hipMemcpyDeviceToDevice, s);
+    if (e == hipSuccess) e = hipMemcpyAsync(W->down, w2, dn_b, hipMemcpyDeviceToDevice, s);
+  } else if (i8) {
+    W->s_gate = static_cast<float*>(carve((size_t)E * p * 4));
+    if (swiglu) W->s_up = static_cast<float*>(carve((size_t)E * p * 4));
+    W->s_down = static_cast<float*>(carve((size_t)E * m * 4));
+    e = moe::launch_pack_i8(static_cast<const int8_t*>(w1), W->up, E, m, p, G, 0, s);
+    if (e == hipSuccess && swiglu) e = moe::launch_pack_i8(static_cast<const int8_t*>(w_up), W->up, E, m, p, G, 1, s);
+    if (e == hipSuccess) e = moe::launch_pack_i8(static_cast<const int8_t*>(w2), W->down, E, p, m, 1, 0, s);
+    if (e == hipSuccess) e = hipMemcpyAsync(W->s_gate, s1, (size_t)E * p * 4, hipMemcpyDeviceToDevice, s);
+    if (e == hipSuccess && swiglu) e = hipMemcpyAsync(W->s_up, s_up, (size_t)E * p * 4, hipMemcpyDeviceToDevice, s);
+    if (e == hipSuccess) e = hipMemcpyAsync(W->s_down, s2, (size_t)E * m * 4, hipMemcpyDeviceToDevice, s);
+  } else {
+    e = moe::launch_pack_bf16(static_cast<const uint16_t*>(w1), W->up, E, m, p, G, 0, s);
+    if (e == hipSuccess && swiglu) e = moe::launch_pack_bf16(static_cast<const uint16_t*>(w_up), W->up, E, m, p, G, 1, s);
+    if (e == hipSuccess) e = moe::launch_pack_bf16(static_cast<const uint16_t*>(w2), W->down, E, p, m, 1, 0, s);
+  }
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) {
+    (void)hipFree(W->buf);
+    delete W;
+    return fail(MOE_ERR_HIP, "packing the weights failed: %s", hipGetErrorString(e));
+  }
+  *out = W;
+  return ok();
+}
+
+int moe_weights_destroy(moe_weights* w) {
+  if (!w) return ok();
+  const hipError_t e = hipFree(w->buf);
+  delete w;
+  if (e != hipSuccess) return fail(MOE_ERR_HIP, "hipFree failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int moe_workspace_size(const moe_weights* w, int T, int k, size_t* bytes) {
+  if (!w || !bytes) return fail(MOE_ERR_INVALID_ARG, "NULL argument");
+  if (int rc = check_shape(T, w->m, w->p, w->E, k)) return rc;
+  *bytes = ws_layout(w, T, k).total;
+  return ok();
+}
+
+int moe_route_topk(const void* x, int x_dtype, const float* w_router, const float* b_router, int T, int m, int E,
+                   int k, unsigned flags, float* logits, int32_t* topk_idx, float* topk_w, void* stream) {
+  if (int rc = check_shape(T, m, 64, E, k)) return rc;
+  const bool lin = (flags & MOE_ROUTE_LOGITS_IN) != 0;
+  if (flags & ~MOE_ROUTE_LOGITS_IN) return fail(MOE_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
+  if (!lin && x_dtype != MOE_F32 && x_dtype != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "x dtype %d", x_dtype);
+  if (T == 0) return ok();
+  if (!topk_idx || !topk_w) return fail(MOE_ERR_INVALID_ARG, "topk_idx/topk_w are NULL");
+  if (lin && !logits) return fail(MOE_ERR_INVALID_ARG, "MOE_ROUTE_LOGITS_IN needs logits");
+  if (!lin && (!x || !w_router)) return fail(MOE_ERR_INVALID_ARG, "x/w_router are NULL");
+  if (!lin && (!aligned16(x))) return fail(MOE_ERR_INVALID_ARG, "x must be 16-byte aligned");
+  const hipStream_t s = as_stream(stream);
+  MOE_TRY_HIP(run("route_topk", s, [&] {
+    return moe::launch_route_topk(x, x_dtype == MOE_BF16, w_router, b_router, T, m, E, k, lin, logits, topk_idx,
+                                  topk_w, s);
+  }));
+  return ok();
+}
+
+int moe_dispatch(const int32_t* topk_idx, int T, int E, int k, int32_t* counts, int32_t* offsets, int32_t* perm,
+                 int32_t* inv_perm, void* stream) {
+  if (int rc = check_shape(T, 64, 64, E, k)) return rc;
+  if (!counts || !offsets) return fail(MOE_ERR_INVALID_ARG, "counts/offsets are NULL");
+  if (T > 0 && (!topk_idx || !perm || !inv_perm)) return fail(MOE_ERR_INVALID_ARG, "NULL argument");
+  const hipStream_t s = as_stream(stream);
+  MOE_TRY_HIP(run("dispatch", s, [&] {
+    return moe::launch_dispatch(topk_idx, T * k, E, counts, offsets, perm, inv_perm, s);
+  }));
+  return ok();
+}
+
+int moe_expert_ffn(const moe_weights* w, const void* x, int x_dtype, int T, int m, int p, int E, int k,
+                   const int32_t* perm, const int32_t* offsets, float* y_perm, void* workspace, size_t ws_bytes,
+                   void* stream) {
+  if (int rc = check_weights_match(w, m, p, E)) return rc;
+  if (int rc = check_shape(T, m, p, E, k)) return rc;
+  if (int rc = check_combo(x_dtype, w->w_dtype)) return rc;
+  if (T == 0) return ok();
+  if (!x || !perm || !offsets || !y_perm) return fail(MOE_ERR_INVALID_ARG, "NULL argument");
+  if (!aligned16(x) || !aligned16(y_perm)) return fail(MOE_ERR_INVALID_ARG, "x/y_perm must be 16-byte aligned");
+  const Ws L = ws_layout(w, T, k);
+  if (!workspace || ws_bytes < L.total)
+    return fail(MOE_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", L.total, workspace ? ws_bytes : 0);
+  if (reinterpret_cast<uintptr_t>(workspace) & 255u) return fail(MOE_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  char* ws = static_cast<char*>(workspace);
+  if (int rc = run_ffn(w, x, T, k, perm, offsets, nullptr, ws + L.h, y_perm, false, as_stream(stream))) return rc;
+  return ok();
+}
+
+int moe_combine(const float* y_perm, const int32_t* inv_perm, const float* topk_w, int T, int m, int k, void* y,
+                int y_dtype, void* stream) {
+  if (T < 0 || m <= 0 || k < 1) return fail(MOE_ERR_INVALID_ARG, "bad sizes T=%d m=%d k=%d", T, m, k);
+  if (m % 64) return fail(MOE_ERR_UNSUPPORTED, "m=%d must be a multiple of 64", m);
+  if (y_dtype != MOE_F32 && y_dtype != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "y dtype %d", y_dtype);
+  if (k > MOE_MAX_EXPERTS) return fail(MOE_ERR_UNSUPPORTED, "k=%d too large", k);
+  if (T == 0) return ok();
+  if (!y_perm || !inv_perm || !topk_w || !y) return fail(MOE_ERR_INVALID_ARG, "NULL argument");
+  if (!aligned16(y_perm) || !aligned16(y)) return fail(MOE_ERR_INVALID_ARG, "y_perm/y must be 16-byte aligned");
+  const hipStream_t s = as_stream(stream);
+  MOE_TRY_HIP(run("combine", s, [&] {
+    return moe::launch_combine(y_perm, inv_perm, topk_w, T, m, k, y, y_dtype == MOE_BF16, s);
+  }));
+  return ok();
+}
+
+int moe_layer_forward(const moe_weights* w, const float* w_router, const float* b_router, const void* x, int x_dtype,
+                      int T, int m, int p, int E, int k, void* y, int y_dtype, void* workspace, size_t ws_bytes,
+                      int32_t* dbg_topk_idx, float* dbg_topk_w, float* dbg_logits, int32_t* dbg_counts,
+                      int32_t* dbg_offsets, int32_t* dbg_perm, void* stream) {
+  if (int rc = check_weights_match(w, m, p, E)) return rc;
+  if (int rc = check_shape(T, m, p, E, k)) return rc;
+  if (int rc = check_combo(x_dtype, w->w_dtype)) return rc;
+  if (y_dtype != MOE_F32 && y_dtype != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "y dtype %d", y_dtype);
+  if (T == 0) return ok();
+  if (!w_router || !x || !y) return fail(MOE_ERR_INVALID_ARG, "NULL argument");
+  if (!aligned16(x) || !aligned16(y)) return fail(MOE_ERR_INVALID_ARG, "x/y must be 16-byte aligned");
+  const Ws L = ws_layout(w, T, k);
+  if (!workspace || ws_bytes < L.total)
+    return fail(MOE_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", L.total, workspace ? ws_bytes : 0);
+  if (reinterpret_cast<uintptr_t>(workspace) & 255u) return fail(MOE_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  char* ws = static_cast<char*>(workspace);
+  const hipStream_t s = as_stream(stream);
+  float* logits = dbg_logits ? dbg_logits : reinterpret_cast<float*>(ws + L.logits);
+  int32_t* idx = dbg_topk_idx ? dbg_topk_idx : reinterpret_cast<int32_t*>(ws + L.idx);
+  float* tw = dbg_topk_w ? dbg_topk_w : reinterpret_cast<float*>(ws + L.w);
+  int32_t* counts = dbg_counts ? dbg_counts : reinterpret_cast<int32_t*>(ws + L.counts);
+  int32_t* offsets = dbg_offsets ? dbg_offsets : reinterpret_cast<int32_t*>(ws + L.offsets);
+  int32_t* perm = dbg_perm ? dbg_perm : reinterpret_cast<int32_t*>(ws + L.perm);
+  int32_t* inv = reinterpret_cast<int32_t*>(ws + L.inv);
+  float* yacc = y_dtype == MOE_F32 ? static_cast<float*>(y) : reinterpret_cast<float*>(ws + L.yacc);
+  const size_t ny = (size_t)T * m;
+
+  MOE_TRY_HIP(run("fill", s, [&] { return moe::launch_fill_zero(yacc, ny, s); }));
+  MOE_TRY_HIP(run("route_topk", s, [&] {
+    return moe::launch_route_topk(x, x_dtype == MOE_BF16, w_router, b_router, T, m, E, k, false, logits, idx, tw, s);
+  }));
+  MOE_TRY_HIP(run("dispatch", s, [&] { return moe::launch_dispatch(idx, T * k, E, counts, offsets, perm, inv, s); }));
+  if (int rc = run_ffn(w, x, T, k, perm, offsets, tw, ws + L.h, yacc, true, s)) return rc;
+  if (y_dtype == MOE_BF16)
+    MOE_TRY_HIP(run("finalize", s, [&] { return moe::launch_f32_to_bf16(yacc, static_cast<uint16_t*>(y), ny, s); }));
+  return ok();
+}
+
+int moe_profile_begin(int max_launches) {
+  std::lock_guard<std::mutex> lk(g_prof.mu);
+  if (max_launches < 1 || max_launches > (1 << 20)) return fail(MOE_ERR_INVALID_ARG, "max_launches out of range");
+  for (hipEvent_t e : g_prof.ev) (void)hipEventDestroy(e);
+  g_prof.ev.assign(2 * (size_t)max_launches, nullptr);
+  for (auto& e : g_prof.ev) MOE_TRY_HIP(hipEventCreate(&e));
+  g_prof.name.assign(max_launches, nullptr);
+  g_prof.total.clear();
+  g_prof.max = max_launches;
+  g_prof.n = 0;
+  g_prof.on = true;
+  return ok();
+}
+
+int moe_profile_end(void) {
+  std::lock_guard<std::mutex> lk(g_prof.mu);
+  if (!g_prof.on) return fail(MOE_ERR_INVALID_ARG, "profiling was not started");
+  g_prof.on = false;
+  for (int i = 0; i < g_prof.n; ++i) {
+    MOE_TRY_HIP(hipEventSynchronize(g_prof.ev[2 * i + 1]));
+    float ms = 0.0f;
+    MOE_TRY_HIP(hipEventElapsedTime(&ms, g_prof.ev[2 * i], g_prof.ev[2 * i + 1]));
+    auto& t = g_prof.total[g_prof.name[i]];
+    t.first += ms;
+    t.second += 1;
+  }
+  for (hipEvent_t e : g_prof.ev) (void)hipEventDestroy(e);
+  g_prof.ev.clear();
+  g_prof.n = 0;
+  return ok();
+}
+
+int moe_profile_query(const char* kernel, double* total_ms, int* launches) {
+  if (!kernel || !total_ms || !launches) return fail(MOE_ERR_INVALID_ARG, "NULL argument");
+  std::lock_guard<std::mutex> lk(g_prof.mu);
+  auto it = g_prof.total.find(kernel);
+  *total_ms = it == g_prof.total.end() ? 0.0 : it->second.first;
+  *launches = it == g_prof.total.end() ? 0 : it->second.second;
+  return ok();
+}
+
+}  // extern "C"

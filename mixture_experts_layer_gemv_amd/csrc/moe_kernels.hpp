@@ -1,0 +1,111 @@
+// Internal interface between the C ABI layer (moe_api.cpp) and the gfx950
+// kernels.  Every launch_* function only enqueues on the given stream and
+// returns the launch status; shape checks happen in moe_api.cpp.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+// ---- device helpers ------------------------------------------------------
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float floatx4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// fp32 -> bf16 bits, round to nearest even, NaN kept quiet.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu)) return (uint16_t)((u >> 16) | 0x0040u);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// ---- packed weight layout -------------------------------------------------
+//
+// A projection W[e][K][N] (K = reduction dim, N = output dim) is stored as
+// 1 KiB blocks, one per (expert, 16-column tile nb, K unit u, stream g):
+//   block index ((e * NB + nb) * U + u) * G + g,   NB = N / 16
+// Inside a block, lane l (0..63) owns 16 contiguous bytes holding column
+// n = nb*16 + (l & 15):
+//   bf16 (U = K/32): element j (0..7) is k = u*32 + 8*(l >> 4) + j
+//   int8 (U = K/64): byte j (0..15) is  k = u*64 + 32*(j >> 3) + 8*(l >> 4) + (j & 7)
+// which is the B-operand order of v_mfma_f32_16x16x32_bf16.  A wave loading
+// one unit reads 1 KiB of contiguous memory: eight full 128-byte lines.
+// G = 2 interleaves the SwiGLU gate (g = 0) and up (g = 1) matrices so one
+// stream of a column tile carries both.
+
+constexpr int kUnitBytes = 1024;
+
+inline size_t packed_bytes(int E, int K, int N, int G, bool i8) {
+  const size_t units = (size_t)K / (i8 ? 64 : 32);
+  return (size_t)E * (size_t)(N / 16) * units * (size_t)G * kUnitBytes;
+}
+
+hipError_t launch_pack_bf16(const uint16_t* src, void* dst, int E, int K, int N, int G, int g, hipStream_t s);
+hipError_t launch_pack_i8(const int8_t* src, void* dst, int E, int K, int N, int G, int g, hipStream_t s);
+
+// ---- routing ---------------------------------------------------------------
+
+hipError_t launch_route_topk(const void* x, bool x_bf16, const float* wg, const float* bias, int T, int m, int E,
+                             int k, bool logits_in, float* logits, int32_t* idx, float* w, hipStream_t s);
+
+hipError_t launch_dispatch(const int32_t* idx, int n, int E, int32_t* counts, int32_t* offsets, int32_t* perm,
+                           int32_t* inv_perm, hipStream_t s);
+
+// ---- expert FFN, skinny (decode-sized) path ----------------------------------
+
+enum SkinnyEpilogue {
+  EPI_UP_SWIGLU = 0,  // H = bf16(SiLU(g) * u), two streams
+  EPI_UP_RELU = 1,    // H = bf16(max(g, 0)),  one stream
+  EPI_DOWN_ACC = 2,   // y_acc[t] += w * o  (fp32 atomics)
+  EPI_DOWN_ROWS = 3,  // y_perm[r] = o     (fp32 rows)
+};
+
+struct SkinnyArgs {
+  const void* w;          // packed weights of this projection
+  const float* scale0;    // int8: per-column scales of stream 0 [E][N]
+  const float* scale1;    // int8: per-column scales of stream 1 [E][N]
+  const uint16_t* act;    // bf16 activations: x [T][K] (gather) or H [T*k][K]
+  const int32_t* perm;    // [T*k]
+  const int32_t* offsets; // [E+1]
+  const float* topk_w;    // [T*k] (EPI_DOWN_ACC)
+  uint16_t* h_out;        // [T*k][N] bf16 (up epilogues)
+  float* f_out;           // y_acc [T][N] or y_perm [T*k][N]
+  int K, N, E, topk;
+  int gather;             // 1: activation row = perm[r] / topk, 0: row r
+  int W;                  // upper bound on (expert, row-chunk) pairs
+};
+
+// Rows per work item for a given M-tile count (16 rows per tile).
+inline int skinny_rows(int mt) { return 16 * mt; }
+
+hipError_t launch_ffn_skinny(const SkinnyArgs& a, int epi, bool i8, int mt, hipStream_t s);
+
+// ---- expert FFN, fp32 path ----------------------------------------------------
+
+struct F32Args {
+  const float* w1;   // [E][K][N]
+  const float* w3;   // [E][K][N] or null (ReLU)
+  const float* act;  // x [T][K] (gather) or H [T*k][K]
+  const int32_t* perm;
+  const int32_t* offsets;
+  const float* topk_w;
+  float* out;        // H [T*k][N], y_acc [T][N] or y_perm [T*k][N]
+  int K, N, E, topk, gather, W;
+  int epi;           // EPI_UP_SWIGLU / EPI_UP_RELU / EPI_DOWN_ACC / EPI_DOWN_ROWS
+};
+
+hipError_t launch_ffn_f32(const F32Args& a, hipStream_t s);
+
+// ---- combine / elementwise ------------------------------------------------------
+
+hipError_t launch_combine(const float* y_perm, const int32_t* inv_perm, const float* topk_w, int T, int m, int k,
+                          void* y, bool y_bf16, hipStream_t s);
+hipError_t launch_fill_zero(float* p, size_t n, hipStream_t s);
+hipError_t launch_f32_to_bf16(const float* src, uint16_t* dst, size_t n, hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,230 @@
+// Supporting kernels: init-time weight packing, the fp32 expert FFN, the
+// standalone weighted combine and small elementwise passes.
+#include "moe_kernels.hpp"
+
+namespace moe {
+namespace {
+
+// ---- packing (run once in moe_weights_create) ------------------------------
+
+// One thread writes one lane's 16 bytes of one 1 KiB block (layout described
+// in moe_kernels.hpp).  Reads are strided; this runs once per layer.
+__global__ __launch_bounds__(256) void k_pack_bf16(const uint16_t* __restrict__ src, uint4* __restrict__ dst, int E,
+                                                   int K, int N, int G, int g) {
+  const int NB = N / 16, U = K / 32;
+  const size_t total = (size_t)E * NB * U * 64;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (size_t)gridDim.x * blockDim.x) {
+    const int lane = (int)(i & 63);
+    size_t rest = i >> 6;
+    const int u = (int)(rest % U);
+    rest /= U;
+    const int nb = (int)(rest % NB);
+    const int e = (int)(rest / NB);
+    const int n = nb * 16 + (lane & 15);
+    const int k0 = u * 32 + 8 * (lane >> 4);
+    const uint16_t* s = src + ((size_t)e * K + k0) * N + n;
+    uint32_t d[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) d[j] = (uint32_t)s[(size_t)(2 * j) * N] | ((uint32_t)s[(size_t)(2 * j + 1) * N] << 16);
+    dst[((((size_t)e * NB + nb) * U + u) * G + g) * 64 + lane] = make_uint4(d[0], d[1], d[2], d[3]);
+  }
+}
+
+__global__ __launch_bounds__(256) void k_pack_i8(const int8_t* __restrict__ src, uint4* __restrict__ dst, int E,
+                                                 int K, int N, int G, int g) {
+  const int NB = N / 16, U = K / 64;
+  const size_t total = (size_t)E * NB * U * 64;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (size_t)gridDim.x * blockDim.x) {
+    const int lane = (int)(i & 63);
+    size_t rest = i >> 6;
+    const int u = (int)(rest % U);
+    rest /= U;
+    const int nb = (int)(rest % NB);
+    const int e = (int)(rest / NB);
+    const int n = nb * 16 + (lane & 15);
+    uint32_t d[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int kk = u * 64 + 32 * (j >> 3) + 8 * (lane >> 4) + (j & 7);
+      const uint32_t byte = (uint8_t)src[((size_t)e * K + kk) * N + n];
+      d[j >> 2] |= byte << (8 * (j & 3));
+    }
+    dst[((((size_t)e * NB + nb) * U + u) * G + g) * 64 + lane] = make_uint4(d[0], d[1], d[2], d[3]);
+  }
+}
+
+// ---- fp32 expert FFN ------------------------------------------------------------
+//
+// True fp32 arithmetic (one fused multiply-add per term, in increasing k) for
+// fp32 layers.  Block = (expert, 16-row chunk) x 256 output columns; each
+// thread owns one column and up to 16 rows.
+
+__device__ __forceinline__ float silu_f(float z) { return z / (1.0f + expf(-z)); }
+
+template <int EPI>
+__global__ __launch_bounds__(256) void k_ffn_f32(const F32Args A) {
+  constexpr int R = 16;
+  int e = -1, chunk = 0;
+  {
+    int rem = blockIdx.x;
+    for (int i = 0; i < A.E; ++i) {
+      const int c = A.offsets[i + 1] - A.offsets[i];
+      const int nch = (c + R - 1) / R;
+      if (rem < nch) {
+        e = i;
+        chunk = rem;
+        break;
+      }
+      rem -= nch;
+    }
+  }
+  if (e < 0) return;
+  const int n = blockIdx.y * 256 + threadIdx.x;
+  if (n >= A.N) return;
+  const int row0 = A.offsets[e] + chunk * R;
+  const int nrows = min(R, A.offsets[e + 1] - row0);
+  const float* src[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    int s = 0;
+    if (r < nrows) s = A.gather ? A.perm[row0 + r] / A.topk : row0 + r;
+    src[r] = A.act + (size_t)s * A.K;
+  }
+  constexpr bool GATED = EPI == EPI_UP_SWIGLU;
+  float acc1[R], acc3[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) acc1[r] = acc3[r] = 0.0f;
+  const float* w1 = A.w1 + (size_t)e * A.K * A.N + n;
+  const float* w3 = GATED ? A.w3 + (size_t)e * A.K * A.N + n : nullptr;
+  for (int kk = 0; kk < A.K; ++kk) {
+    const float a1 = w1[(size_t)kk * A.N];
+    const float a3 = GATED ? w3[(size_t)kk * A.N] : 0.0f;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      if (r < nrows) {
+        const float xv = src[r][kk];
+        acc1[r] = fmaf(xv, a1, acc1[r]);
+        if (GATED) acc3[r] = fmaf(xv, a3, acc3[r]);
+      }
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    if (r >= nrows) continue;
+    const int row = row0 + r;
+    if constexpr (EPI == EPI_UP_SWIGLU) {
+      A.out[(size_t)row * A.N + n] = silu_f(acc1[r]) * acc3[r];
+    } else if constexpr (EPI == EPI_UP_RELU) {
+      A.out[(size_t)row * A.N + n] = acc1[r] > 0.0f ? acc1[r] : 0.0f;
+    } else if constexpr (EPI == EPI_DOWN_ACC) {
+      const int a = A.perm[row];
+      unsafeAtomicAdd(A.out + (size_t)(a / A.topk) * A.N + n, A.topk_w[a] * acc1[r]);
+    } else {
+      A.out[(size_t)row * A.N + n] = acc1[r];
+    }
+  }
+}
+
+// ---- combine and elementwise ----------------------------------------------------
+
+// y[t][c] = sum_{j<k} w[t][j] * y_perm[inv_perm[t*k+j]][c], four columns per thread.
+template <bool BF16>
+__global__ __launch_bounds__(256) void k_combine(const float* __restrict__ y_perm, const int32_t* __restrict__ inv,
+                                                 const float* __restrict__ w, int T, int m, int k, void* __restrict__ y) {
+  const size_t q = (size_t)blockIdx.x * blockDim.x + threadIdx.x;  // float4 index
+  const size_t per_row = (size_t)m / 4;
+  if (q >= (size_t)T * per_row) return;
+  const int t = (int)(q / per_row);
+  const int c = (int)(q - (size_t)t * per_row) * 4;
+  float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int j = 0; j < k; ++j) {
+    const float wj = w[(size_t)t * k + j];
+    const float4 v = *reinterpret_cast<const float4*>(y_perm + (size_t)inv[(size_t)t * k + j] * m + c);
+    s.x = fmaf(wj, v.x, s.x);
+    s.y = fmaf(wj, v.y, s.y);
+    s.z = fmaf(wj, v.z, s.z);
+    s.w = fmaf(wj, v.w, s.w);
+  }
+  if (BF16) {
+    uint16_t* o = static_cast<uint16_t*>(y) + (size_t)t * m + c;
+    const uint2 pk = make_uint2((uint32_t)f32_to_bf16(s.x) | ((uint32_t)f32_to_bf16(s.y) << 16),
+                                (uint32_t)f32_to_bf16(s.z) | ((uint32_t)f32_to_bf16(s.w) << 16));
+    *reinterpret_cast<uint2*>(o) = pk;
+  } else {
+    *reinterpret_cast<float4*>(static_cast<float*>(y) + (size_t)t * m + c) = s;
+  }
+}
+
+__global__ __launch_bounds__(256) void k_fill_zero(float* __restrict__ p, size_t n) {
+  const size_t n4 = n / 4;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += (size_t)gridDim.x * blockDim.x)
+    reinterpret_cast<float4*>(p)[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+  const size_t tail = n4 * 4 + (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (tail < n) p[tail] = 0.0f;
+}
+
+__global__ __launch_bounds__(256) void k_f32_to_bf16(const float* __restrict__ src, uint16_t* __restrict__ dst,
+                                                     size_t n) {
+  const size_t n4 = n / 4;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += (size_t)gridDim.x * blockDim.x) {
+    const float4 v = reinterpret_cast<const float4*>(src)[i];
+    reinterpret_cast<uint2*>(dst)[i] = make_uint2((uint32_t)f32_to_bf16(v.x) | ((uint32_t)f32_to_bf16(v.y) << 16),
+                                                  (uint32_t)f32_to_bf16(v.z) | ((uint32_t)f32_to_bf16(v.w) << 16));
+  }
+  const size_t tail = n4 * 4 + (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (tail < n) dst[tail] = f32_to_bf16(src[tail]);
+}
+
+unsigned grid_for(size_t work, unsigned cap = 65536u) {
+  size_t b = (work + 255) / 256;
+  if (b < 1) b = 1;
+  return (unsigned)(b < cap ? b : cap);
+}
+
+}  // namespace
+
+hipError_t launch_pack_bf16(const uint16_t* src, void* dst, int E, int K, int N, int G, int g, hipStream_t s) {
+  const size_t total = (size_t)E * (N / 16) * (K / 32) * 64;
+  k_pack_bf16<<<grid_for(total, 1u << 20), 256, 0, s>>>(src, static_cast<uint4*>(dst), E, K, N, G, g);
+  return hipGetLastError();
+}
+
+hipError_t launch_pack_i8(const int8_t* src, void* dst, int E, int K, int N, int G, int g, hipStream_t s) {
+  const size_t total = (size_t)E * (N / 16) * (K / 64) * 64;
+  k_pack_i8<<<grid_for(total, 1u << 20), 256, 0, s>>>(src, static_cast<uint4*>(dst), E, K, N, G, g);
+  return hipGetLastError();
+}
+
+hipError_t launch_ffn_f32(const F32Args& a, hipStream_t s) {
+  const dim3 grid((unsigned)a.W, (unsigned)((a.N + 255) / 256)), block(256);
+  switch (a.epi) {
+    case EPI_UP_SWIGLU: k_ffn_f32<EPI_UP_SWIGLU><<<grid, block, 0, s>>>(a); break;
+    case EPI_UP_RELU: k_ffn_f32<EPI_UP_RELU><<<grid, block, 0, s>>>(a); break;
+    case EPI_DOWN_ACC: k_ffn_f32<EPI_DOWN_ACC><<<grid, block, 0, s>>>(a); break;
+    default: k_ffn_f32<EPI_DOWN_ROWS><<<grid, block, 0, s>>>(a); break;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_combine(const float* y_perm, const int32_t* inv_perm, const float* topk_w, int T, int m, int k,
+                          void* y, bool y_bf16, hipStream_t s) {
+  const size_t work = (size_t)T * (m / 4);
+  const unsigned grid = (unsigned)((work + 255) / 256);
+  if (y_bf16)
+    k_combine<true><<<grid, 256, 0, s>>>(y_perm, inv_perm, topk_w, T, m, k, y);
+  else
+    k_combine<false><<<grid, 256, 0, s>>>(y_perm, inv_perm, topk_w, T, m, k, y);
+  return hipGetLastError();
+}
+
+hipError_t launch_fill_zero(float* p, size_t n, hipStream_t s) {
+  k_fill_zero<<<grid_for(n / 4 + 1, 8192u), 256, 0, s>>>(p, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_f32_to_bf16(const float* src, uint16_t* dst, size_t n, hipStream_t s) {
+  k_f32_to_bf16<<<grid_for(n / 4 + 1, 8192u), 256, 0, s>>>(src, dst, n);
+  return hipGetLastError();
+}
+
+}  // namespace moe

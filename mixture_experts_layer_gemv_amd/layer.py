@@ -1,0 +1,93 @@
+"""Device plumbing around the C ABI: upload a layer's tensors with torch, own
+the packed weights and a workspace, call moe_layer_forward.
+
+No arithmetic happens here; torch only provides device memory and streams.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from . import (MOE_BF16, MOE_F32, MOE_I8, MOE_MLP_RELU, MOE_SWIGLU, moe_layer_forward, moe_weights_create,
+               moe_weights_destroy, moe_workspace_size)
+
+DTYPE_CODE = {"f32": MOE_F32, "bf16": MOE_BF16, "i8": MOE_I8}
+KIND_CODE = {"relu": MOE_MLP_RELU, "swiglu": MOE_SWIGLU}
+
+
+def to_device(a, device="cuda"):
+    """numpy -> torch on the device; uint16 arrays are bf16 bit patterns."""
+    if a is None:
+        return None
+    if a.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(device).view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(a)).to(device)
+
+
+class MoELayer:
+    """One MoE layer resident on the GPU, built from a synthetic layer dict."""
+
+    def __init__(self, layer: dict, device="cuda", stream=None):
+        sp = layer["spec"]
+        self.spec = sp
+        self.device = device
+        self.T, self.m, self.p, self.E, self.k = sp.T, sp.m, sp.p, sp.E, sp.k
+        self.x_dtype = DTYPE_CODE[sp.x_dtype]
+        self.y_dtype = self.x_dtype
+        self.x = to_device(layer["x"], device) if layer.get("x") is not None else None
+        self.wg = to_device(layer["wg"], device)
+        self.bias = to_device(layer["bias"], device)
+        w1, w3, w2 = (to_device(layer[k], device) for k in ("w1", "w3", "w2"))
+        s1, s3, s2 = (to_device(layer[k], device) for k in ("s1", "s3", "s2"))
+        self.handle = moe_weights_create(self.m, self.p, self.E, KIND_CODE[sp.kind], DTYPE_CODE[sp.w_dtype],
+                                         w1, w3, w2, s1, s3, s2, stream=stream)
+        del w1, w3, w2, s1, s3, s2
+        self._ws = None
+        self._ws_T = -1
+        self.ensure_workspace(self.T)
+
+    def ensure_workspace(self, T):
+        if T > self._ws_T:
+            self.ws_bytes = moe_workspace_size(self.handle, T, self.k)
+            self._ws = torch.empty(max(self.ws_bytes, 256), dtype=torch.uint8, device=self.device)
+            self._ws_T = T
+        return self._ws
+
+    def new_output(self, T=None):
+        T = self.T if T is None else T
+        dt = torch.float32 if self.y_dtype == MOE_F32 else torch.bfloat16
+        return torch.empty((T, self.m), dtype=dt, device=self.device)
+
+    def forward(self, x=None, y=None, T=None, dbg=None, stream=None):
+        x = self.x if x is None else x
+        T = x.shape[0] if T is None else T
+        y = self.new_output(T) if y is None else y
+        ws = self.ensure_workspace(T)
+        dbg = dbg or {}
+        moe_layer_forward(self.handle, self.wg, self.bias, x, self.x_dtype, T, self.m, self.p, self.E, self.k, y,
+                          self.y_dtype, ws, self.ws_bytes, dbg.get("topk_idx"), dbg.get("topk_w"),
+                          dbg.get("logits"), dbg.get("counts"), dbg.get("offsets"), dbg.get("perm"), stream=stream)
+        return y
+
+    def debug_buffers(self, T=None):
+        T = self.T if T is None else T
+        d = self.device
+        return {
+            "topk_idx": torch.empty((T, self.k), dtype=torch.int32, device=d),
+            "topk_w": torch.empty((T, self.k), dtype=torch.float32, device=d),
+            "logits": torch.empty((T, self.E), dtype=torch.float32, device=d),
+            "counts": torch.empty(self.E, dtype=torch.int32, device=d),
+            "offsets": torch.empty(self.E + 1, dtype=torch.int32, device=d),
+            "perm": torch.empty(T * self.k, dtype=torch.int32, device=d),
+        }
+
+    def close(self):
+        if self.handle is not None:
+            moe_weights_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -64,11 +64,18 @@ def lib():
         L.orc_combine.argtypes = [vp, vp, vp, vp, i32, i32, i32, vp]
         L.orc_forward_tokens.argtypes = [P, vp, i32, vp, vp, vp, i32, i32, vp, i32, vp, vp, vp, vp]
         L.orc_dense_masked.argtypes = [P, vp, i32, vp, vp, i32, i32, vp]
+        L.orc_max_threads.argtypes = []
+        L.orc_max_threads.restype = ctypes.c_int
         for f in ("orc_router_logits", "orc_topk", "orc_dispatch", "orc_expert_apply", "orc_expert_rows",
                   "orc_combine", "orc_forward_tokens", "orc_dense_masked"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
+
+
+def max_threads() -> int:
+    """OpenMP threads the oracle's parallel loops use."""
+    return int(lib().orc_max_threads())
 
 
 def _ptr(a):

@@ -37,6 +37,9 @@
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
 
 /* ---- element access ----------------------------------------------------- */
 
@@ -159,33 +162,58 @@ static void expert_row(const orc_experts* X, int e, const double* x, double* g, 
   const int swiglu = (X->kind == ORC_SWIGLU);
 
   /* g = x*W1 (and u = x*W3): every g[n] is the length-m dot product in
-   * increasing i, started with the i = 0 product. */
+   * increasing i, started with the i = 0 product.  The counters tick once
+   * per multiply and once per add actually performed. */
+  uint64_t mul = 0, add = 0, act = 0, prod = 0;
   for (int n = 0; n < p; ++n) {
     g[n] = x[0] * w_at(X->w1, X->s1, X->w_dtype, in_base + n, s_in + n);
-    if (swiglu) u[n] = x[0] * w_at(X->w3, X->s3, X->w_dtype, in_base + n, s_in + n);
+    mul += 1;
+    if (swiglu) {
+      u[n] = x[0] * w_at(X->w3, X->s3, X->w_dtype, in_base + n, s_in + n);
+      mul += 1;
+    }
   }
   for (int i = 1; i < m; ++i) {
     const int64_t row = in_base + (int64_t)i * p;
     for (int n = 0; n < p; ++n) {
       g[n] += x[i] * w_at(X->w1, X->s1, X->w_dtype, row + n, s_in + n);
-      if (swiglu) u[n] += x[i] * w_at(X->w3, X->s3, X->w_dtype, row + n, s_in + n);
+      mul += 1;
+      add += 1;
+      if (swiglu) {
+        u[n] += x[i] * w_at(X->w3, X->s3, X->w_dtype, row + n, s_in + n);
+        mul += 1;
+        add += 1;
+      }
     }
   }
-  const uint64_t dots_in = (uint64_t)p * (uint64_t)(2 * (int64_t)m - 1);
-  ops[0] += swiglu ? 2 * dots_in : dots_in;
 
   /* h overwrites g, kept in double (not rounded) */
-  for (int n = 0; n < p; ++n) g[n] = swiglu ? silu(g[n]) * u[n] : (g[n] > 0.0 ? g[n] : 0.0);
-  ops[1] += (uint64_t)p;
-  if (swiglu) ops[2] += (uint64_t)p;
+  for (int n = 0; n < p; ++n) {
+    if (swiglu) {
+      g[n] = silu(g[n]) * u[n];
+      prod += 1;
+    } else {
+      g[n] = g[n] > 0.0 ? g[n] : 0.0;
+    }
+    act += 1;
+  }
 
   /* o = h*W2 */
-  for (int j = 0; j < m; ++j) o[j] = g[0] * w_at(X->w2, X->s2, X->w_dtype, out_base + j, s_out + j);
+  for (int j = 0; j < m; ++j) {
+    o[j] = g[0] * w_at(X->w2, X->s2, X->w_dtype, out_base + j, s_out + j);
+    mul += 1;
+  }
   for (int n = 1; n < p; ++n) {
     const int64_t row = out_base + (int64_t)n * m;
-    for (int j = 0; j < m; ++j) o[j] += g[n] * w_at(X->w2, X->s2, X->w_dtype, row + j, s_out + j);
+    for (int j = 0; j < m; ++j) {
+      o[j] += g[n] * w_at(X->w2, X->s2, X->w_dtype, row + j, s_out + j);
+      mul += 1;
+      add += 1;
+    }
   }
-  ops[0] += (uint64_t)m * (uint64_t)(2 * (int64_t)p - 1);
+  ops[0] += mul + add;
+  ops[1] += act;
+  ops[2] += prod;
 }
 
 static int check_experts(const orc_experts* X) {
@@ -368,4 +396,13 @@ int orc_dense_masked(const orc_experts* X, const void* x, int x_dtype, const int
   }
   free(g); free(u); free(xr); free(o);
   return 0;
+}
+
+/* Threads the parallel loops above use (1 without OpenMP). */
+int orc_max_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
 }

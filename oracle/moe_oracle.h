@@ -39,4 +39,6 @@ int orc_forward_tokens(const orc_experts* X, const void* x, int x_dtype, const f
 int orc_dense_masked(const orc_experts* X, const void* x, int x_dtype, const int32_t* idx, const float* w, int T,
                      int k, double* y);
 
+int orc_max_threads(void);
+
 #endif

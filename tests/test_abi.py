@@ -1,0 +1,127 @@
+"""The C ABI library loads, exports what include/moe_gemv.h declares, and
+rejects bad arguments before touching the GPU (no compute calls here)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_gemv.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\**(moe_\w+)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import mixture_experts_layer_gemv_amd as M
+
+    if not os.path.exists(M.LIB_PATH):
+        pytest.fail("libmoe_gemv.so is not built (run __graft_entry__.build())")
+    return M
+
+
+def test_header_declares_the_boundary():
+    names = _declared()
+    for fn in ["moe_route_topk", "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_layer_forward",
+               "moe_weights_create", "moe_weights_destroy", "moe_workspace_size", "moe_last_error"]:
+        assert fn in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", lib.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    exported = set(re.findall(r"\sT\s+(moe_\w+)$", out, flags=re.M))
+    missing = [n for n in _declared() if n not in exported]
+    assert not missing, missing
+    L = lib.lib()
+    for n in _declared():
+        assert hasattr(L, n)
+    assert lib.moe_abi_version() == 1
+
+
+def test_binding_names_match_header(lib):
+    for n in _declared():
+        assert callable(getattr(lib, n)), n
+
+
+FAKE = 0x7F0000000000  # never dereferenced: every case below fails validation first
+
+
+def _rc(fn, *args):
+    return fn(*args)
+
+
+def test_weights_create_validation(lib):
+    L = lib.lib()
+    out = ctypes.c_void_p()
+    Z = None
+    # out == NULL
+    assert L.moe_weights_create(64, 64, 8, 1, 1, FAKE, FAKE, FAKE, Z, Z, Z, Z, None) == lib.MOE_ERR_INVALID_ARG
+    cases = [
+        ((64, 64, 65, 1, 1, FAKE, FAKE, FAKE, Z, Z, Z), lib.MOE_ERR_UNSUPPORTED),  # E > 64
+        ((64, 64, 0, 1, 1, FAKE, FAKE, FAKE, Z, Z, Z), lib.MOE_ERR_INVALID_ARG),  # E < 1
+        ((100, 64, 8, 1, 1, FAKE, FAKE, FAKE, Z, Z, Z), lib.MOE_ERR_UNSUPPORTED),  # m % 64
+        ((64, 96, 8, 1, 1, FAKE, FAKE, FAKE, Z, Z, Z), lib.MOE_ERR_UNSUPPORTED),  # p % 64
+        ((64, 64, 8, 1, 7, FAKE, FAKE, FAKE, Z, Z, Z), lib.MOE_ERR_UNSUPPORTED),  # dtype
+        ((64, 64, 8, 5, 1, FAKE, FAKE, FAKE, Z, Z, Z), lib.MOE_ERR_INVALID_ARG),  # kind
+        ((64, 64, 8, 1, 1, FAKE, Z, FAKE, Z, Z, Z), lib.MOE_ERR_INVALID_ARG),  # SwiGLU without w_up
+        ((64, 64, 8, 0, 1, FAKE, FAKE, FAKE, Z, Z, Z), lib.MOE_ERR_INVALID_ARG),  # ReLU with w_up
+        ((64, 64, 8, 1, 2, FAKE, FAKE, FAKE, Z, Z, Z), lib.MOE_ERR_INVALID_ARG),  # int8 without scales
+        ((64, 64, 8, 1, 1, FAKE, FAKE, FAKE, FAKE, Z, Z), lib.MOE_ERR_INVALID_ARG),  # scales for bf16
+        ((64, 64, 8, 1, 1, FAKE + 2, FAKE, FAKE, Z, Z, Z), lib.MOE_ERR_INVALID_ARG),  # misaligned
+    ]
+    for args, want in cases:
+        rc = L.moe_weights_create(*args, None, ctypes.byref(out))
+        assert rc == want, (args, rc, lib.moe_last_error())
+        assert out.value is None
+        assert lib.moe_last_error() != ""
+
+
+def test_stage_validation_without_gpu(lib):
+    L = lib.lib()
+    Z = None
+    # route: k > E, E > 64, bad flags, NULL outputs, misaligned x
+    assert L.moe_route_topk(FAKE, 1, FAKE, Z, 4, 64, 8, 9, 0, Z, FAKE, FAKE, Z) == lib.MOE_ERR_INVALID_ARG
+    assert L.moe_route_topk(FAKE, 1, FAKE, Z, 4, 64, 65, 2, 0, Z, FAKE, FAKE, Z) == lib.MOE_ERR_UNSUPPORTED
+    assert L.moe_route_topk(FAKE, 1, FAKE, Z, 4, 64, 8, 2, 4, Z, FAKE, FAKE, Z) == lib.MOE_ERR_INVALID_ARG
+    assert L.moe_route_topk(FAKE, 1, FAKE, Z, 4, 64, 8, 2, 0, Z, Z, FAKE, Z) == lib.MOE_ERR_INVALID_ARG
+    assert L.moe_route_topk(FAKE, 2, FAKE, Z, 4, 64, 8, 2, 0, Z, FAKE, FAKE, Z) == lib.MOE_ERR_UNSUPPORTED
+    assert L.moe_route_topk(FAKE + 8, 1, FAKE, Z, 4, 64, 8, 2, 0, Z, FAKE, FAKE, Z) == lib.MOE_ERR_INVALID_ARG
+    assert L.moe_route_topk(Z, 1, Z, Z, 4, 64, 8, 2, 1, Z, FAKE, FAKE, Z) == lib.MOE_ERR_INVALID_ARG  # LOGITS_IN
+    assert L.moe_route_topk(FAKE, 1, FAKE, Z, -1, 64, 8, 2, 0, Z, FAKE, FAKE, Z) == lib.MOE_ERR_INVALID_ARG
+    assert L.moe_route_topk(FAKE, 1, FAKE, Z, 0, 64, 8, 2, 0, Z, FAKE, FAKE, Z) == lib.MOE_OK  # T = 0: no-op
+    # dispatch
+    assert L.moe_dispatch(FAKE, 4, 8, 0, FAKE, FAKE, FAKE, FAKE, Z) == lib.MOE_ERR_INVALID_ARG
+    assert L.moe_dispatch(FAKE, 4, 8, 2, Z, FAKE, FAKE, FAKE, Z) == lib.MOE_ERR_INVALID_ARG
+    assert L.moe_dispatch(FAKE, 2**30, 8, 4, FAKE, FAKE, FAKE, FAKE, Z) == lib.MOE_ERR_UNSUPPORTED
+    # combine
+    assert L.moe_combine(FAKE, FAKE, FAKE, 4, 96, 2, FAKE, 1, Z) == lib.MOE_ERR_UNSUPPORTED
+    assert L.moe_combine(FAKE, FAKE, FAKE, 4, 64, 2, FAKE, 2, Z) == lib.MOE_ERR_UNSUPPORTED
+    assert L.moe_combine(Z, FAKE, FAKE, 4, 64, 2, FAKE, 1, Z) == lib.MOE_ERR_INVALID_ARG
+    assert L.moe_combine(FAKE, FAKE, FAKE, 0, 64, 2, FAKE, 1, Z) == lib.MOE_OK
+    # handle-based calls with a NULL handle
+    assert L.moe_expert_ffn(Z, FAKE, 1, 4, 64, 64, 8, 2, FAKE, FAKE, FAKE, FAKE, 1 << 20, Z) == lib.MOE_ERR_INVALID_ARG
+    assert L.moe_layer_forward(Z, FAKE, Z, FAKE, 1, 4, 64, 64, 8, 2, FAKE, 1, FAKE, 1 << 20,
+                               Z, Z, Z, Z, Z, Z, Z) == lib.MOE_ERR_INVALID_ARG
+    n = ctypes.c_size_t()
+    assert L.moe_workspace_size(Z, 4, 2, ctypes.byref(n)) == lib.MOE_ERR_INVALID_ARG
+    assert L.moe_weights_destroy(Z) == lib.MOE_OK
+
+
+def test_profile_query_is_host_only(lib):
+    ms, n = lib.moe_profile_query("ffn_up")
+    assert (ms, n) == (0.0, 0)
+    with pytest.raises(lib.MoeError):
+        lib.moe_profile_end()  # never started
+
+
+def test_binding_raises_with_message(lib):
+    with pytest.raises(lib.MoeError) as ei:
+        lib.moe_combine(FAKE, FAKE, FAKE, 4, 96, 2, FAKE, 1, stream=0)
+    assert ei.value.status == lib.MOE_ERR_UNSUPPORTED and "multiple of 64" in ei.value.message
