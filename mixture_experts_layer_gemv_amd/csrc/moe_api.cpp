@@ -6,6 +6,7 @@
 
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <map>
 #include <mutex>
 #include <string>
@@ -136,25 +137,49 @@ int skinny_mt(int T, int k, int E) {
   return avg <= 12 ? 1 : (avg <= 24 ? 2 : 4);
 }
 
-// Both projections of the expert FFN.  h: hidden buffer; down_out: y_acc
-// (weighted, accumulate) or y_perm (rows), selected by `combine`.
-int run_ffn(const moe_weights* W, const void* x, int T, int k, const int32_t* perm, const int32_t* offsets,
-            const float* topk_w, void* h, float* down_out, bool combine, hipStream_t s) {
-  const int m = W->m, p = W->p, E = W->E;
+int env_int(const char* name, int dflt) {
+  const char* v = getenv(name);
+  return v && *v ? atoi(v) : dflt;
+}
+
+// Reduction slices per down-projection work item: enough work items that
+// every CU keeps several in flight and the last round is short.
+int down_ksplit(long long items) {
+  const int forced = env_int("MOE_DOWN_KSPLIT", 0);
+  if (forced > 0) return forced;
+  if (items >= 8192) return 1;
+  if (items >= 4096) return 2;
+  return 4;
+}
+
+// Inputs and outputs of the two FFN projections.
+struct FfnIo {
+  const void* x;
+  int T, k;
+  const int32_t* topk_idx;  // non-null: the up projection derives the dispatch
+  int32_t *counts, *offsets, *perm, *inv;
+  const float* topk_w;
+  void* h;                  // hidden activations [T*k][p]
+  float* down_out;          // y_acc [T][m] (combine) or y_perm [T*k][m]
+  bool combine;
+};
+
+int run_ffn(const moe_weights* W, const FfnIo& io, hipStream_t s) {
+  const int m = W->m, p = W->p, E = W->E, T = io.T, k = io.k;
   const bool swiglu = W->kind == MOE_SWIGLU;
   if (W->w_dtype == MOE_F32) {
     moe::F32Args a{};
-    a.perm = perm;
-    a.offsets = offsets;
+    a.perm = io.perm;
+    a.offsets = io.offsets;
     a.topk = k;
     a.E = E;
     a.W = E + (int)((long long)T * k / 16);
-    a.topk_w = topk_w;
+    a.topk_w = io.topk_w;
     // up: x [T][m] -> H [T*k][p]
     a.w1 = static_cast<const float*>(W->up);
     a.w3 = swiglu ? static_cast<const float*>(W->up3) : nullptr;
-    a.act = static_cast<const float*>(x);
-    a.out = static_cast<float*>(h);
+    a.act = static_cast<const float*>(io.x);
+    a.out = static_cast<float*>(io.h);
     a.K = m;
     a.N = p;
     a.gather = 1;
@@ -163,47 +188,63 @@ int run_ffn(const moe_weights* W, const void* x, int T, int k, const int32_t* pe
     // down: H -> y
     a.w1 = static_cast<const float*>(W->down);
     a.w3 = nullptr;
-    a.act = static_cast<const float*>(h);
-    a.out = down_out;
+    a.act = static_cast<const float*>(io.h);
+    a.out = io.down_out;
     a.K = p;
     a.N = m;
     a.gather = 0;
-    a.epi = combine ? moe::EPI_DOWN_ACC : moe::EPI_DOWN_ROWS;
+    a.epi = io.combine ? moe::EPI_DOWN_ACC : moe::EPI_DOWN_ROWS;
     MOE_TRY_HIP(run("ffn_f32_down", s, [&] { return moe::launch_ffn_f32(a, s); }));
     return MOE_OK;
   }
   const bool i8 = W->w_dtype == MOE_I8;
-  const int mt = skinny_mt(T, k, E);
+  const long long avg = ((long long)T * k + E - 1) / E;
+  int mt = env_int("MOE_SKINNY_MT", avg <= 12 ? 1 : (avg <= 24 ? 2 : 4));
+  mt = mt <= 1 ? 1 : (mt == 2 ? 2 : 4);
   const int R = moe::skinny_rows(mt);
   moe::SkinnyArgs a{};
-  a.perm = perm;
-  a.offsets = offsets;
+  a.perm = io.perm;
+  a.offsets = io.offsets;
   a.topk = k;
+  a.T = T;
   a.E = E;
   a.W = E + (int)((long long)T * k / R);
-  a.topk_w = topk_w;
-  if ((long long)(p / 16) * a.W >= 0x7FFFFFF0LL || (long long)(m / 16) * a.W >= 0x7FFFFFF0LL)
+  a.topk_w = io.topk_w;
+  a.ksplit = 1;
+  if ((long long)(p / 16) * a.W * 4 >= 0x7FFFFFF0LL || (long long)(m / 16) * a.W * 4 >= 0x7FFFFFF0LL)
     return fail(MOE_ERR_UNSUPPORTED, "too many work items for one launch (T*k=%lld)", (long long)T * k);
+  // up: gate (+up) projection with the activation epilogue, x -> H
   a.w = W->up;
   a.scale0 = W->s_gate;
   a.scale1 = W->s_up;
-  a.act = static_cast<const uint16_t*>(x);
-  a.h_out = static_cast<uint16_t*>(h);
+  a.act = static_cast<const uint16_t*>(io.x);
+  a.h_out = static_cast<uint16_t*>(io.h);
   a.K = m;
   a.N = p;
   a.gather = 1;
+  if (io.topk_idx) {
+    a.topk_idx = io.topk_idx;
+    a.d_counts = io.counts;
+    a.d_offsets = io.offsets;
+    a.d_perm = io.perm;
+    a.d_inv = io.inv;
+  }
   const int up_epi = swiglu ? moe::EPI_UP_SWIGLU : moe::EPI_UP_RELU;
   MOE_TRY_HIP(run("ffn_up", s, [&] { return moe::launch_ffn_skinny(a, up_epi, i8, mt, s); }));
+  // down: H -> weighted combine (or unweighted rows)
+  a.topk_idx = nullptr;
+  a.d_counts = a.d_offsets = a.d_perm = a.d_inv = nullptr;
   a.w = W->down;
   a.scale0 = W->s_down;
   a.scale1 = nullptr;
-  a.act = static_cast<const uint16_t*>(h);
+  a.act = static_cast<const uint16_t*>(io.h);
   a.h_out = nullptr;
-  a.f_out = down_out;
+  a.f_out = io.down_out;
   a.K = p;
   a.N = m;
   a.gather = 0;
-  const int dn_epi = combine ? moe::EPI_DOWN_ACC : moe::EPI_DOWN_ROWS;
+  if (io.combine) a.ksplit = down_ksplit((long long)(m / 16) * a.W);
+  const int dn_epi = io.combine ? moe::EPI_DOWN_ACC : moe::EPI_DOWN_ROWS;
   MOE_TRY_HIP(run("ffn_down", s, [&] { return moe::launch_ffn_skinny(a, dn_epi, i8, mt, s); }));
   return MOE_OK;
 }
@@ -336,7 +377,7 @@ int moe_route_topk(const void* x, int x_dtype, const float* w_router, const floa
   const hipStream_t s = as_stream(stream);
   MOE_TRY_HIP(run("route_topk", s, [&] {
     return moe::launch_route_topk(x, x_dtype == MOE_BF16, w_router, b_router, T, m, E, k, lin, logits, topk_idx,
-                                  topk_w, s);
+                                  topk_w, nullptr, 0, s);
   }));
   return ok();
 }
@@ -367,7 +408,16 @@ int moe_expert_ffn(const moe_weights* w, const void* x, int x_dtype, int T, int 
     return fail(MOE_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", L.total, workspace ? ws_bytes : 0);
   if (reinterpret_cast<uintptr_t>(workspace) & 255u) return fail(MOE_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
   char* ws = static_cast<char*>(workspace);
-  if (int rc = run_ffn(w, x, T, k, perm, offsets, nullptr, ws + L.h, y_perm, false, as_stream(stream))) return rc;
+  FfnIo io{};
+  io.x = x;
+  io.T = T;
+  io.k = k;
+  io.perm = const_cast<int32_t*>(perm);
+  io.offsets = const_cast<int32_t*>(offsets);
+  io.h = ws + L.h;
+  io.down_out = y_perm;
+  io.combine = false;
+  if (int rc = run_ffn(w, io, as_stream(stream))) return rc;
   return ok();
 }
 
@@ -411,16 +461,34 @@ int moe_layer_forward(const moe_weights* w, const float* w_router, const float* 
   int32_t* offsets = dbg_offsets ? dbg_offsets : reinterpret_cast<int32_t*>(ws + L.offsets);
   int32_t* perm = dbg_perm ? dbg_perm : reinterpret_cast<int32_t*>(ws + L.perm);
   int32_t* inv = reinterpret_cast<int32_t*>(ws + L.inv);
-  float* yacc = y_dtype == MOE_F32 ? static_cast<float*>(y) : reinterpret_cast<float*>(ws + L.yacc);
+  const bool y_bf16 = y_dtype == MOE_BF16;
+  float* yacc = y_bf16 ? reinterpret_cast<float*>(ws + L.yacc) : static_cast<float*>(y);
   const size_t ny = (size_t)T * m;
+  // decode-sized layers on the MFMA path: the up projection derives the
+  // dispatch itself
+  const bool fused = w->w_dtype != MOE_F32 && (long long)T * k <= moe::kFusedDispatchMax;
 
-  MOE_TRY_HIP(run("fill", s, [&] { return moe::launch_fill_zero(yacc, ny, s); }));
   MOE_TRY_HIP(run("route_topk", s, [&] {
-    return moe::launch_route_topk(x, x_dtype == MOE_BF16, w_router, b_router, T, m, E, k, false, logits, idx, tw, s);
+    return moe::launch_route_topk(x, x_dtype == MOE_BF16, w_router, b_router, T, m, E, k, false, logits, idx, tw,
+                                  yacc, m, s);
   }));
-  MOE_TRY_HIP(run("dispatch", s, [&] { return moe::launch_dispatch(idx, T * k, E, counts, offsets, perm, inv, s); }));
-  if (int rc = run_ffn(w, x, T, k, perm, offsets, tw, ws + L.h, yacc, true, s)) return rc;
-  if (y_dtype == MOE_BF16)
+  if (!fused)
+    MOE_TRY_HIP(run("dispatch", s, [&] { return moe::launch_dispatch(idx, T * k, E, counts, offsets, perm, inv, s); }));
+  FfnIo io{};
+  io.x = x;
+  io.T = T;
+  io.k = k;
+  io.topk_idx = fused ? idx : nullptr;
+  io.counts = counts;
+  io.offsets = offsets;
+  io.perm = perm;
+  io.inv = inv;
+  io.topk_w = tw;
+  io.h = ws + L.h;
+  io.down_out = yacc;
+  io.combine = true;
+  if (int rc = run_ffn(w, io, s)) return rc;
+  if (y_bf16)
     MOE_TRY_HIP(run("finalize", s, [&] { return moe::launch_f32_to_bf16(yacc, static_cast<uint16_t*>(y), ny, s); }));
   return ok();
 }

@@ -1,23 +1,28 @@
 // Expert FFN for decode-sized batches: a skinny grouped GEMM that streams each
-// touched expert's weights from HBM exactly once and multiplies them by that
-// expert's few activation rows on the matrix cores.
+// touched expert's weights from HBM once and multiplies them by that expert's
+// few activation rows on the matrix cores.
 //
 // Design (prior art: the small-batch GEMM of the DeepSpeed-Inference summary,
 // datalearner.com, section 3 "SBI-GeMM"):
-//  - tiling along the output dimension: one workgroup owns a 16-column tile of
-//    one expert (both SwiGLU streams of it), so the whole reduction stays in
-//    the workgroup and one kernel suffices (part 1 of that section);
-//  - the reduction dimension is split over the workgroup's four waves and the
-//    partial tiles are summed through one LDS transpose, after which each
-//    thread reads its outputs' partials contiguously (part 2, with wave64
-//    instead of 32-thread warps);
+//  - tiling along the output dimension: a workgroup owns a 16-column tile of
+//    one expert (both SwiGLU streams of it), so the reduction stays inside the
+//    workgroup (part 1 of that section).  When outputs are too few to keep
+//    every CU streaming, the reduction dimension is also split over
+//    workgroups (its two-kernel variant); here the split partials meet in the
+//    fp32 atomic combine, so no second kernel is needed;
+//  - inside the workgroup the reduction dimension is split over the waves and
+//    the partial tiles are summed through one LDS transpose, after which each
+//    thread reads its outputs' partials contiguously (part 2, with wave64);
 //  - weights are re-laid out at initialisation so a wave's load is 1 KiB of
 //    contiguous memory (part 3; see the packed layout in moe_kernels.hpp);
 //  - small-batch work is bandwidth-bound, so the activations (a few rows per
-//    expert) ride along in registers and the product runs on MFMA, which has
-//    an order of magnitude more throughput than the vector ALUs need here.
-// Work items are (column tile, expert, 16*MT-row chunk) triples generated on
-// the device from the dispatch offsets, so the host never reads the counts.
+//    expert) ride along in registers and the product runs on MFMA.
+// Work items are (column tile, reduction slice, expert, row chunk) tuples
+// generated on the device from the dispatch offsets: the host never reads the
+// expert counts.  With `topk_idx` set, each workgroup derives the dispatch
+// itself in its prologue (and logical workgroup 0 publishes it), so no
+// separate dispatch launch is needed.
+#include "moe_dispatch_block.hpp"
 #include "moe_kernels.hpp"
 
 namespace moe {
@@ -46,14 +51,21 @@ __device__ __forceinline__ bf16x8_t i8x8_to_bf16(uint32_t lo, uint32_t hi) {
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
 
-template <int MT, int G, bool I8, int EPI, int D>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MT * (I8 ? 2 : 1) >= 4 ? 2 : 4))) void k_ffn_skinny(
-    const SkinnyArgs A) {
+template <int MT, int G, bool I8, int EPI, int D, int NW>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(MT * (I8 ? 2 : 1) >= 4 ? 2 : 4))) void
+k_ffn_skinny(const SkinnyArgs A) {
+  constexpr int NT = NW * 64;
   constexpr int R = 16 * MT;        // rows per work item
   constexpr int AH = I8 ? 2 : 1;    // activation loads per K unit
   constexpr int UK = I8 ? 64 : 32;  // k per unit
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+
+  __shared__ DispatchLds<NW> DL;
+  __shared__ int offs_s[kMaxExperts + 1];
+  __shared__ int rows_s[R];
+  __shared__ float red[NW * G * MT * 256];
 
   // Block -> logical work index: consecutive logical indices stay on one XCD
   // (blocks are dealt to the 8 XCDs round-robin), so the row chunks of one
@@ -62,45 +74,72 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MT * (I8 ? 
   const int b = blockIdx.x;
   const int L = (b & 7) * (nblk >> 3) + (b >> 3);
   const int NB = A.N / 16;
-  const int ntile = L / A.W;
-  const int pair = L - ntile * A.W;
-  if (ntile >= NB) return;
-  int e = -1, chunk = 0;
-  {
-    int rem = pair;
-    for (int i = 0; i < A.E; ++i) {
-      const int c = A.offsets[i + 1] - A.offsets[i];
-      const int nch = (c + R - 1) / R;
-      if (rem < nch) {
-        e = i;
-        chunk = rem;
-        break;
-      }
-      rem -= nch;
-    }
+  const int S = A.ksplit;
+  const int ntile = L / (A.W * S);
+  const int rem0 = L - ntile * (A.W * S);
+  const int ks = rem0 / A.W;
+  const int pair = rem0 - ks * A.W;
+  const int n_assign = A.T * A.topk;
+
+  if (A.topk_idx) {
+    block_histogram<NW>(A.topk_idx, n_assign, A.E, DL);
+    if (tid <= A.E) offs_s[tid] = DL.offs[tid];
+  } else {
+    if (tid <= A.E) offs_s[tid] = A.offsets[tid];
   }
-  if (e < 0) return;
-  const int row0 = A.offsets[e] + chunk * R;
-  const int nrows = min(R, A.offsets[e + 1] - row0);
+  __syncthreads();
+
+  // (expert, chunk) of this work item and the number of valid pairs
+  int e = -1, chunk = 0, npairs = 0;
+  for (int i = 0; i < A.E; ++i) {
+    const int nch = (offs_s[i + 1] - offs_s[i] + R - 1) / R;
+    if (e < 0 && pair < npairs + nch) {
+      e = i;
+      chunk = pair - npairs;
+    }
+    npairs += nch;
+  }
+  const bool valid = ntile < NB && e >= 0;
+  const int row0 = valid ? offs_s[e] + chunk * R : 0;
+  const int nrows = valid ? min(R, offs_s[e + 1] - row0) : 0;
+
+  if (A.topk_idx) {
+    const bool publish = L == 0;
+    if (publish || valid) {
+      block_stable_positions<NW>(A.topk_idx, n_assign, A.E, DL, [&](int a, int ea, int pos) {
+        if (publish) {
+          A.d_perm[pos] = a;
+          A.d_inv[a] = pos;
+        }
+        if (valid && ea == e && pos >= row0 && pos < row0 + nrows) rows_s[pos - row0] = a;
+      });
+      if (publish) {
+        if (tid < A.E) A.d_counts[tid] = DL.cnt[tid];
+        if (tid <= A.E) A.d_offsets[tid] = DL.offs[tid];
+      }
+    }
+  } else if (valid && A.gather) {
+    if (tid < nrows) rows_s[tid] = A.perm[row0 + tid];
+    __syncthreads();
+  }
+  if (!valid) return;
 
   // Activation row pointers of this lane, one per M tile.  Lanes past the
   // chunk's last row read a valid row (the chunk's first) so every load is
   // unconditional; their output rows are never stored.
   const uint16_t* arow[MT];
-  {
-    const int src0 = A.gather ? A.perm[row0] / A.topk : row0;
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      const int r = mt * 16 + (lane & 15);
-      int src = src0;
-      if (r < nrows) src = A.gather ? A.perm[row0 + r] / A.topk : row0 + r;
-      arow[mt] = A.act + (size_t)src * A.K + 8 * (lane >> 4);
-    }
+  for (int mt = 0; mt < MT; ++mt) {
+    const int r = mt * 16 + (lane & 15);
+    const int rr = r < nrows ? r : 0;
+    const int src = A.gather ? rows_s[rr] / A.topk : row0 + rr;
+    arow[mt] = A.act + (size_t)src * A.K + 8 * (lane >> 4);
   }
 
   const int U = A.K / UK;
-  const int u0 = (wave * U) >> 2;
-  const int u1 = ((wave + 1) * U) >> 2;
+  const int part = ks * NW + wave;
+  const int u0 = (int)(((long long)part * U) / (S * NW));
+  const int u1 = (int)(((long long)(part + 1) * U) / (S * NW));
   const u32x4_t* wp = static_cast<const u32x4_t*>(A.w) + (size_t)(e * NB + ntile) * U * G * 64 + lane;
 
   floatx4_t acc[G][MT];
@@ -175,8 +214,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MT * (I8 ? 
 #undef MOE_ISSUE
 
   // Cross-wave reduction through one LDS transpose: wave w writes its partial
-  // tile; thread (i, lane) then reads the four partials of its outputs.
-  __shared__ float red[4 * G * MT * 256];
+  // tile; each output's NW partials are then read by one thread.
 #pragma unroll
   for (int g = 0; g < G; ++g)
 #pragma unroll
@@ -185,19 +223,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MT * (I8 ? 
       for (int i = 0; i < 4; ++i) red[((wave * G + g) * MT + mt) * 256 + i * 64 + lane] = acc[g][mt][i];
   __syncthreads();
 
-  const int i = threadIdx.x >> 6;  // accumulator element 0..3
-  const int ln = lane;
-  const int col = ntile * 16 + (ln & 15);
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
+  for (int o = tid; o < MT * 256; o += NT) {
+    const int mt = o >> 8, i = (o >> 6) & 3, ln = o & 63;
     const int row = mt * 16 + 4 * (ln >> 4) + i;
     if (row >= nrows) continue;
+    const int col = ntile * 16 + (ln & 15);
     float v[G];
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       float s = 0.0f;
 #pragma unroll
-      for (int w = 0; w < 4; ++w) s += red[((w * G + g) * MT + mt) * 256 + i * 64 + ln];
+      for (int w = 0; w < NW; ++w) s += red[((w * G + g) * MT + mt) * 256 + i * 64 + ln];
       v[g] = s;
     }
     const int r = row0 + row;
@@ -213,17 +249,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MT * (I8 ? 
       if constexpr (I8) gv *= A.scale0[(size_t)e * A.N + col];
       A.h_out[(size_t)r * A.N + col] = f32_to_bf16(gv > 0.0f ? gv : 0.0f);
     } else {
-      float o = v[0];
-      if constexpr (I8) o *= A.scale0[(size_t)e * A.N + col];
+      float o2 = v[0];
+      if constexpr (I8) o2 *= A.scale0[(size_t)e * A.N + col];
       if constexpr (EPI == EPI_DOWN_ACC) {
         const int a = A.perm[r];
-        const int t = a / A.topk;
-        unsafeAtomicAdd(A.f_out + (size_t)t * A.N + col, A.topk_w[a] * o);
+        unsafeAtomicAdd(A.f_out + (size_t)(a / A.topk) * A.N + col, A.topk_w[a] * o2);
       } else {
-        A.f_out[(size_t)r * A.N + col] = o;
+        A.f_out[(size_t)r * A.N + col] = o2;
       }
     }
   }
+
 }
 
 // Units in flight per wave: enough bytes outstanding per CU to cover HBM
@@ -233,14 +269,22 @@ constexpr int depth(int mt, int g, bool i8) { return (mt * (i8 ? 2 : 1) + g) <= 
 template <int MT, bool I8>
 hipError_t launch_mt(const SkinnyArgs& a, int epi, hipStream_t s) {
   const int NB = a.N / 16;
-  const long long work = (long long)NB * a.W;
+  const long long work = (long long)NB * a.W * a.ksplit;
   const long long nblk = (work + 7) / 8 * 8;
-  const dim3 grid((unsigned)nblk), block(256);
+  const dim3 grid((unsigned)nblk);
   switch (epi) {
-    case EPI_UP_SWIGLU: k_ffn_skinny<MT, 2, I8, EPI_UP_SWIGLU, depth(MT, 2, I8)><<<grid, block, 0, s>>>(a); break;
-    case EPI_UP_RELU: k_ffn_skinny<MT, 1, I8, EPI_UP_RELU, depth(MT, 1, I8)><<<grid, block, 0, s>>>(a); break;
-    case EPI_DOWN_ACC: k_ffn_skinny<MT, 1, I8, EPI_DOWN_ACC, depth(MT, 1, I8)><<<grid, block, 0, s>>>(a); break;
-    default: k_ffn_skinny<MT, 1, I8, EPI_DOWN_ROWS, depth(MT, 1, I8)><<<grid, block, 0, s>>>(a); break;
+    case EPI_UP_SWIGLU:
+      k_ffn_skinny<MT, 2, I8, EPI_UP_SWIGLU, depth(MT, 2, I8), 4><<<grid, 256, 0, s>>>(a);
+      break;
+    case EPI_UP_RELU:
+      k_ffn_skinny<MT, 1, I8, EPI_UP_RELU, depth(MT, 1, I8), 4><<<grid, 256, 0, s>>>(a);
+      break;
+    case EPI_DOWN_ACC:
+      k_ffn_skinny<MT, 1, I8, EPI_DOWN_ACC, depth(MT, 1, I8), 4><<<grid, 256, 0, s>>>(a);
+      break;
+    default:
+      k_ffn_skinny<MT, 1, I8, EPI_DOWN_ROWS, depth(MT, 1, I8), 4><<<grid, 256, 0, s>>>(a);
+      break;
   }
   return hipGetLastError();
 }

@@ -9,6 +9,8 @@
 
 namespace moe {
 
+constexpr int kMaxExperts = 64;
+
 // ---- device helpers ------------------------------------------------------
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -50,8 +52,10 @@ hipError_t launch_pack_i8(const int8_t* src, void* dst, int E, int K, int N, int
 
 // ---- routing ---------------------------------------------------------------
 
+// yacc (optional): fp32 [T][ym] accumulator that the routing pass zeroes.
 hipError_t launch_route_topk(const void* x, bool x_bf16, const float* wg, const float* bias, int T, int m, int E,
-                             int k, bool logits_in, float* logits, int32_t* idx, float* w, hipStream_t s);
+                             int k, bool logits_in, float* logits, int32_t* idx, float* w, float* yacc, int ym,
+                             hipStream_t s);
 
 hipError_t launch_dispatch(const int32_t* idx, int n, int E, int32_t* counts, int32_t* offsets, int32_t* perm,
                            int32_t* inv_perm, hipStream_t s);
@@ -66,19 +70,28 @@ enum SkinnyEpilogue {
 };
 
 struct SkinnyArgs {
-  const void* w;          // packed weights of this projection
-  const float* scale0;    // int8: per-column scales of stream 0 [E][N]
-  const float* scale1;    // int8: per-column scales of stream 1 [E][N]
-  const uint16_t* act;    // bf16 activations: x [T][K] (gather) or H [T*k][K]
-  const int32_t* perm;    // [T*k]
-  const int32_t* offsets; // [E+1]
-  const float* topk_w;    // [T*k] (EPI_DOWN_ACC)
-  uint16_t* h_out;        // [T*k][N] bf16 (up epilogues)
-  float* f_out;           // y_acc [T][N] or y_perm [T*k][N]
-  int K, N, E, topk;
-  int gather;             // 1: activation row = perm[r] / topk, 0: row r
-  int W;                  // upper bound on (expert, row-chunk) pairs
+  const void* w;           // packed weights of this projection
+  const float* scale0;     // int8: per-column scales of stream 0 [E][N]
+  const float* scale1;     // int8: per-column scales of stream 1 [E][N]
+  const uint16_t* act;     // bf16 activations: x [T][K] (gather) or H [T*k][K]
+  const int32_t* perm;     // [T*k] dispatch permutation (input unless topk_idx is set)
+  const int32_t* offsets;  // [E+1] dispatch offsets (input unless topk_idx is set)
+  const int32_t* topk_idx; // [T*k] or null: derive the dispatch in the prologue
+  int32_t* d_counts;       // with topk_idx: dispatch outputs published by logical block 0
+  int32_t* d_offsets;
+  int32_t* d_perm;
+  int32_t* d_inv;
+  const float* topk_w;     // [T*k] (EPI_DOWN_ACC)
+  uint16_t* h_out;         // [T*k][N] bf16 (up epilogues)
+  float* f_out;            // y_acc [T][N] or y_perm [T*k][N]
+  int K, N, E, topk, T;
+  int gather;              // 1: activation row = perm[r] / topk, 0: row r
+  int W;                   // upper bound on (expert, row-chunk) pairs
+  int ksplit;              // reduction slices per work item (EPI_DOWN_ACC only)
 };
+
+// Largest T*k for which the decode FFN derives the dispatch in its prologue.
+constexpr int kFusedDispatchMax = 4096;
 
 // Rows per work item for a given M-tile count (16 rows per tile).
 inline int skinny_rows(int mt) { return 16 * mt; }

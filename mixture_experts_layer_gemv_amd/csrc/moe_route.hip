@@ -7,6 +7,7 @@
 // one-GPU form of sending tokens to their experts (HARMOEny article, section
 // 3.3 step four): the assignments are grouped by expert so each expert reads
 // a contiguous run of rows.
+#include "moe_dispatch_block.hpp"
 #include "moe_kernels.hpp"
 
 namespace moe {
@@ -143,87 +144,198 @@ __global__ __launch_bounds__(256) void k_route_topk(const void* __restrict__ x, 
   }
 }
 
-// Single workgroup: counts by LDS atomics, a sequential exclusive scan over
-// E <= 64, then a stable scatter chunk by chunk: within a wave, lanes with
-// the same expert find each other through six ballots (one per bit of the
-// expert id) and rank by lane order; across waves, a per-expert running
-// cursor orders the waves.  Assignment order is therefore preserved.
+// Top-k of one token held one logit per lane (lanes >= E hold nothing):
+// k rounds of a wave-wide max over 64-bit keys (rank of the logit, then the
+// lower expert index), then the softmax over the selected logits.  Lane j < k
+// writes slot j.
+__device__ __forceinline__ void wave_topk_write(float v, bool live, int e, int k, int32_t* idx_row,
+                                                float* w_row) {
+  uint64_t key = live ? (((uint64_t)rank_key(v) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)e)) : 0ull;
+  uint64_t mine = 0ull;
+  float l0 = 0.0f;
+  for (int j = 0; j < k; ++j) {
+    uint64_t best = key;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const uint64_t o = __shfl_xor(best, off, 64);
+      best = o > best ? o : best;
+    }
+    if (j == 0) l0 = rank_key_value((uint32_t)(best >> 32));
+    if (e == j) mine = best;
+    if (key == best) key = 0ull;
+  }
+  const bool slot = e < k;
+  const float lj = rank_key_value((uint32_t)(mine >> 32));
+  const float ex = slot ? expf(lj - l0) : 0.0f;
+  float den = ex;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) den += __shfl_xor(den, off, 64);
+  if (slot) {
+    idx_row[e] = (int32_t)(0xFFFFFFFFu - (uint32_t)(mine & 0xFFFFFFFFull));
+    w_row[e] = ex / den;
+  }
+}
+
+// Recursive-halving step over lane bit B on an array of N partial sums: the
+// lane keeps the half selected by its bit B and adds the partner's copy.
+template <int B, int N>
+__device__ __forceinline__ void halve_bit(float* v, int lane) {
+  const bool upper = (lane >> B) & 1;
+#pragma unroll
+  for (int i = 0; i < N / 2; ++i) {
+    const float send = upper ? v[i] : v[i + N / 2];
+    const float keep = upper ? v[i + N / 2] : v[i];
+    v[i] = keep + __shfl_xor(send, 1 << B, 64);
+  }
+}
+
+template <int E>
+struct RouteShape {
+  static constexpr int Q = E / 4;         // lanes per router-weight row (16 B each)
+  static constexpr int LQ = E == 8 ? 1 : E == 16 ? 2 : E == 32 ? 3 : 4;
+  static constexpr int RPC = 64 / Q;      // rows per 1 KiB chunk
+  static constexpr int TB = 128 / E;      // tokens per block
+  static constexpr int NV = TB * 4;       // partial sums per lane
+};
+
+constexpr int kRouteLdsX = 128 * 1024;  // bytes of staged activations per block
+
+// Router for E in {8, 16, 32, 64}: one 1024-thread block per TB = 128/E
+// tokens.  The tokens' activation rows are staged in LDS; each wave streams
+// 1 KiB chunks of the router weights with one coalesced 16-byte load per lane
+// (lane = row-in-chunk x expert quad) and keeps TB x 4 partial sums.  Sums
+// over rows: a reduce-scatter across the lanes of a wave, then a fixed-order
+// sum over the 16 waves in LDS.  One wave per token then takes the top-k.
+// The block also zeroes its tokens' rows of the fp32 output accumulator.
+template <int E, bool XBF16>
+__global__ __launch_bounds__(1024) void k_route_fast(const void* __restrict__ x, const float* __restrict__ wg,
+                                                     const float* __restrict__ bias, int T, int m, int k,
+                                                     float* __restrict__ logits, int32_t* __restrict__ idx,
+                                                     float* __restrict__ wout, float* __restrict__ yacc, int ym) {
+  using S = RouteShape<E>;
+  __shared__ __attribute__((aligned(16))) unsigned char xs_raw[kRouteLdsX];
+  __shared__ float red[16][128];
+  __shared__ float lg[S::TB][E];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int t0 = blockIdx.x * S::TB;
+  const int nt = min(S::TB, T - t0);
+  constexpr int XB = XBF16 ? 2 : 4;
+
+  if (yacc) {
+    float4* yr = reinterpret_cast<float4*>(yacc + (size_t)t0 * ym);
+    const int n4 = nt * ym / 4;
+    for (int i = tid; i < n4; i += 1024) yr[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  // stage x rows [t0, t0 + nt) (rows past T are zero)
+  {
+    const int row16 = m * XB / 16;
+    uint4* dst = reinterpret_cast<uint4*>(xs_raw);
+    const uint4* src = reinterpret_cast<const uint4*>(static_cast<const char*>(x) + (size_t)t0 * m * XB);
+    for (int i = tid; i < S::TB * row16; i += 1024) dst[i] = (i < nt * row16) ? src[i] : make_uint4(0, 0, 0, 0);
+  }
+  __syncthreads();
+
+  float acc[S::NV];
+#pragma unroll
+  for (int i = 0; i < S::NV; ++i) acc[i] = 0.0f;
+  const int q = lane & (S::Q - 1);
+  const int rr = lane >> S::LQ;
+  const int nchunks = m / S::RPC;
+  for (int c = wave; c < nchunks; c += 16) {
+    const int r = c * S::RPC + rr;
+    const float4 wv = *reinterpret_cast<const float4*>(wg + (size_t)r * E + 4 * q);
+#pragma unroll
+    for (int t = 0; t < S::TB; ++t) {
+      float xv;
+      if constexpr (XBF16)
+        xv = bf16_to_f32(reinterpret_cast<const uint16_t*>(xs_raw)[t * m + r]);
+      else
+        xv = reinterpret_cast<const float*>(xs_raw)[t * m + r];
+      acc[t * 4 + 0] = fmaf(xv, wv.x, acc[t * 4 + 0]);
+      acc[t * 4 + 1] = fmaf(xv, wv.y, acc[t * 4 + 1]);
+      acc[t * 4 + 2] = fmaf(xv, wv.z, acc[t * 4 + 2]);
+      acc[t * 4 + 3] = fmaf(xv, wv.w, acc[t * 4 + 3]);
+    }
+  }
+  // sum over the row lanes (lane bits LQ..5), leaving 2 sums per lane
+  if constexpr (S::LQ <= 1) halve_bit<5, S::NV>(acc, lane), halve_bit<4, S::NV / 2>(acc, lane),
+      halve_bit<3, S::NV / 4>(acc, lane), halve_bit<2, S::NV / 8>(acc, lane), halve_bit<1, S::NV / 16>(acc, lane);
+  if constexpr (S::LQ == 2) halve_bit<5, S::NV>(acc, lane), halve_bit<4, S::NV / 2>(acc, lane),
+      halve_bit<3, S::NV / 4>(acc, lane), halve_bit<2, S::NV / 8>(acc, lane);
+  if constexpr (S::LQ == 3) halve_bit<5, S::NV>(acc, lane), halve_bit<4, S::NV / 2>(acc, lane),
+      halve_bit<3, S::NV / 4>(acc, lane);
+  if constexpr (S::LQ == 4) halve_bit<5, S::NV>(acc, lane), halve_bit<4, S::NV / 2>(acc, lane);
+  {
+    const int L = lane >> S::LQ;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int v = 2 * L + i;  // partial index t*4 + j
+      const int t = v >> 2, e = 4 * q + (v & 3);
+      red[wave][t * E + e] = acc[i];
+    }
+  }
+  __syncthreads();
+  if (tid < S::TB * E) {
+    float s = 0.0f;
+#pragma unroll
+    for (int w = 0; w < 16; ++w) s += red[w][tid];
+    const int t = tid / E, e = tid % E;
+    if (bias) s += bias[e];
+    lg[t][e] = s;
+    if (logits && t < nt) logits[(size_t)(t0 + t) * E + e] = s;
+  }
+  __syncthreads();
+  if (wave < nt) {
+    const int t = t0 + wave;
+    const bool live = lane < E;
+    wave_topk_write(live ? lg[wave][lane] : 0.0f, live, lane, k, idx + (size_t)t * k, wout + (size_t)t * k);
+  }
+}
+
+// Single workgroup of 16 waves: the block-level dispatch (LDS histogram,
+// prefix sum, ballot-ranked stable positions).
 __global__ __launch_bounds__(1024) void k_dispatch(const int32_t* __restrict__ idx, int n, int E,
                                                     int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
                                                     int32_t* __restrict__ perm, int32_t* __restrict__ inv_perm) {
-  __shared__ int cnt[64];
-  __shared__ int offs[65];
-  __shared__ int cursor[64];
-  __shared__ int wbase[16][64];
+  __shared__ DispatchLds<16> L;
+  block_histogram<16>(idx, n, E, L);
   const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  if (tid < 64) {
-    cnt[tid] = 0;
-    cursor[tid] = 0;
-  }
-  __syncthreads();
-  for (int a = tid; a < n; a += 1024) {
-    int e = idx[a];
-    e = e < 0 ? 0 : (e >= E ? E - 1 : e);
-    atomicAdd(&cnt[e], 1);
-  }
-  __syncthreads();
-  if (tid == 0) {
-    int run = 0;
-    for (int e = 0; e < E; ++e) {
-      offs[e] = run;
-      run += cnt[e];
-    }
-    offs[E] = run;
-  }
-  __syncthreads();
-  if (tid < E) counts[tid] = cnt[tid];
-  if (tid <= E) offsets[tid] = offs[tid];
-
-  const uint64_t lt = (lane == 0) ? 0ull : ((~0ull) >> (64 - lane));
-  for (int base = 0; base < n; base += 1024) {
-    const int a = base + tid;
-    const bool valid = a < n;
-    int e = 0;
-    if (valid) {
-      e = idx[a];
-      e = e < 0 ? 0 : (e >= E ? E - 1 : e);
-    }
-    uint64_t peers = __ballot(valid);
-#pragma unroll
-    for (int b = 0; b < 6; ++b) {
-      const uint64_t mb = __ballot((e >> b) & 1);
-      peers &= ((e >> b) & 1) ? mb : ~mb;
-    }
-    const int rank = __popcll(peers & lt);
-    wbase[wave][lane] = 0;
-    __syncthreads();
-    if (valid && rank == 0) wbase[wave][e] = __popcll(peers);
-    __syncthreads();
-    if (tid < E) {
-      int run = cursor[tid];
-      for (int w = 0; w < 16; ++w) {
-        const int c = wbase[w][tid];
-        wbase[w][tid] = run;
-        run += c;
-      }
-      cursor[tid] = run;
-    }
-    __syncthreads();
-    if (valid) {
-      const int pos = offs[e] + wbase[wave][e] + rank;
-      perm[pos] = a;
-      inv_perm[a] = pos;
-    }
-    __syncthreads();
-  }
+  if (tid < E) counts[tid] = L.cnt[tid];
+  if (tid <= E) offsets[tid] = L.offs[tid];
+  block_stable_positions<16>(idx, n, E, L, [&](int a, int, int pos) {
+    perm[pos] = a;
+    inv_perm[a] = pos;
+  });
 }
 
 }  // namespace
 
 hipError_t launch_route_topk(const void* x, bool x_bf16, const float* wg, const float* bias, int T, int m, int E,
-                             int k, bool logits_in, float* logits, int32_t* idx, float* w, hipStream_t s) {
+                             int k, bool logits_in, float* logits, int32_t* idx, float* w, float* yacc, int ym,
+                             hipStream_t s) {
+  const int xb = x_bf16 ? 2 : 4;
+  const bool fast = !logits_in && (E == 8 || E == 16 || E == 32 || E == 64) && (128 / E) * m * xb <= kRouteLdsX &&
+                    (yacc == nullptr || ym % 4 == 0);
+  if (fast) {
+    const unsigned grid = (unsigned)((T + 128 / E - 1) / (128 / E));
+#define MOE_ROUTE_FAST(EE)                                                                                  \
+  if (E == EE) {                                                                                            \
+    if (x_bf16)                                                                                             \
+      k_route_fast<EE, true><<<grid, 1024, 0, s>>>(x, wg, bias, T, m, k, logits, idx, w, yacc, ym);         \
+    else                                                                                                    \
+      k_route_fast<EE, false><<<grid, 1024, 0, s>>>(x, wg, bias, T, m, k, logits, idx, w, yacc, ym);        \
+    return hipGetLastError();                                                                               \
+  }
+    MOE_ROUTE_FAST(8)
+    MOE_ROUTE_FAST(16)
+    MOE_ROUTE_FAST(32)
+    MOE_ROUTE_FAST(64)
+#undef MOE_ROUTE_FAST
+  }
+  if (yacc) {
+    const hipError_t e = launch_fill_zero(yacc, (size_t)T * ym, s);
+    if (e != hipSuccess) return e;
+  }
   if (E <= 8) {
     const int tpb = 4 * 8;
     k_route_topk<8, 8><<<(T + tpb - 1) / tpb, 256, 0, s>>>(x, x_bf16, wg, bias, T, m, E, k, logits_in, logits,
