@@ -152,6 +152,18 @@ int down_ksplit(long long items) {
   return 4;
 }
 
+// Column tiles per workgroup: enough to amortise each activation load over
+// several weight streams when the activation side is wide (several M tiles,
+// or int8 weights whose 16-byte unit spans 64 k).
+int skinny_ct(int mt, bool i8, int g, const char* env) {
+  const int forced = env_int(env, 0);
+  if (forced > 0) return forced >= 4 ? 4 : (forced >= 2 ? 2 : 1);
+  const int aw = mt * (i8 ? 2 : 1);
+  if (aw <= 1) return 1;
+  if (mt >= 4) return 2;
+  return 4;
+}
+
 // Inputs and outputs of the two FFN projections.
 struct FfnIo {
   const void* x;
@@ -230,7 +242,8 @@ int run_ffn(const moe_weights* W, const FfnIo& io, hipStream_t s) {
     a.d_inv = io.inv;
   }
   const int up_epi = swiglu ? moe::EPI_UP_SWIGLU : moe::EPI_UP_RELU;
-  MOE_TRY_HIP(run("ffn_up", s, [&] { return moe::launch_ffn_skinny(a, up_epi, i8, mt, s); }));
+  const int up_ct = skinny_ct(mt, i8, swiglu ? 2 : 1, "MOE_UP_CT");
+  MOE_TRY_HIP(run("ffn_up", s, [&] { return moe::launch_ffn_skinny(a, up_epi, i8, mt, up_ct, s); }));
   // down: H -> weighted combine (or unweighted rows)
   a.topk_idx = nullptr;
   a.d_counts = a.d_offsets = a.d_perm = a.d_inv = nullptr;
@@ -243,9 +256,10 @@ int run_ffn(const moe_weights* W, const FfnIo& io, hipStream_t s) {
   a.K = p;
   a.N = m;
   a.gather = 0;
-  if (io.combine) a.ksplit = down_ksplit((long long)(m / 16) * a.W);
+  if (io.combine) a.ksplit = down_ksplit((long long)(m / 16 / skinny_ct(mt, i8, 1, "MOE_DOWN_CT")) * a.W);
   const int dn_epi = io.combine ? moe::EPI_DOWN_ACC : moe::EPI_DOWN_ROWS;
-  MOE_TRY_HIP(run("ffn_down", s, [&] { return moe::launch_ffn_skinny(a, dn_epi, i8, mt, s); }));
+  const int dn_ct = skinny_ct(mt, i8, 1, "MOE_DOWN_CT");
+  MOE_TRY_HIP(run("ffn_down", s, [&] { return moe::launch_ffn_skinny(a, dn_epi, i8, mt, dn_ct, s); }));
   return MOE_OK;
 }
 

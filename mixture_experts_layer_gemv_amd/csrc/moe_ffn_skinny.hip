@@ -23,6 +23,7 @@
 // itself in its prologue (and logical workgroup 0 publishes it), so no
 // separate dispatch launch is needed.
 #include "moe_dispatch_block.hpp"
+#include "moe_index.hpp"
 #include "moe_kernels.hpp"
 
 namespace moe {
@@ -51,9 +52,26 @@ __device__ __forceinline__ bf16x8_t i8x8_to_bf16(uint32_t lo, uint32_t hi) {
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
 
-template <int MT, int G, bool I8, int EPI, int D, int NW>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(MT * (I8 ? 2 : 1) >= 4 ? 2 : 4))) void
+// Register plan of one variant: accumulators, registers per pipeline stage,
+// and the deepest pipeline that fits 128 VGPRs (4 waves per SIMD) or else
+// 256 VGPRs (2 waves per SIMD).
+struct Plan {
+  int acc, stage, wpe, depth;
+};
+constexpr Plan plan(int mt, int g, int ct, bool i8) {
+  const int acc = ct * g * mt * 4;
+  const int stage = ct * g * 4 + mt * (i8 ? 2 : 1) * 4;
+  const int fixed = i8 ? 64 : 40;  // addresses, loop state, int8 conversion temporaries
+  const int d128 = (128 - fixed - acc) / stage;
+  if (d128 >= 4) return Plan{acc, stage, 4, d128 < 6 ? d128 : 6};
+  const int d256 = (256 - fixed - acc) / stage;
+  return Plan{acc, stage, 2, d256 < 2 ? 2 : (d256 < 6 ? d256 : 6)};
+}
+
+template <int MT, int G, int CT, bool I8, int EPI, int NW>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(plan(MT, G, CT, I8).wpe))) void
 k_ffn_skinny(const SkinnyArgs A) {
+  constexpr int D = plan(MT, G, CT, I8).depth;
   constexpr int NT = NW * 64;
   constexpr int R = 16 * MT;        // rows per work item
   constexpr int AH = I8 ? 2 : 1;    // activation loads per K unit
@@ -65,20 +83,17 @@ k_ffn_skinny(const SkinnyArgs A) {
   __shared__ DispatchLds<NW> DL;
   __shared__ int offs_s[kMaxExperts + 1];
   __shared__ int rows_s[R];
-  __shared__ float red[NW * G * MT * 256];
+  __shared__ float red[NW * CT * G * MT * 256];
 
   // Block -> logical work index: consecutive logical indices stay on one XCD
   // (blocks are dealt to the 8 XCDs round-robin), so the row chunks of one
   // (expert, tile) run together and share that XCD's L2 copy of the weights.
-  const int nblk = gridDim.x;  // multiple of 8
-  const int b = blockIdx.x;
-  const int L = (b & 7) * (nblk >> 3) + (b >> 3);
-  const int NB = A.N / 16;
+  const int L = xcd_logical(blockIdx.x, gridDim.x);  // gridDim.x is a multiple of 8
+  const int NB = A.N / 16;  // a multiple of 4 (N is a multiple of 64)
   const int S = A.ksplit;
-  const int ntile = L / (A.W * S);
-  const int rem0 = L - ntile * (A.W * S);
-  const int ks = rem0 / A.W;
-  const int pair = rem0 - ks * A.W;
+  const SkinnyWork wk = skinny_work(L, A.W, S);
+  const int ntile = wk.ngroup * CT;  // first of this group's CT column tiles
+  const int ks = wk.ks;
   const int n_assign = A.T * A.topk;
 
   if (A.topk_idx) {
@@ -90,16 +105,9 @@ k_ffn_skinny(const SkinnyArgs A) {
   __syncthreads();
 
   // (expert, chunk) of this work item and the number of valid pairs
-  int e = -1, chunk = 0, npairs = 0;
-  for (int i = 0; i < A.E; ++i) {
-    const int nch = (offs_s[i + 1] - offs_s[i] + R - 1) / R;
-    if (e < 0 && pair < npairs + nch) {
-      e = i;
-      chunk = pair - npairs;
-    }
-    npairs += nch;
-  }
-  const bool valid = ntile < NB && e >= 0;
+  int e, chunk, npairs;
+  const bool has_pair = skinny_pair(offs_s, A.E, R, wk.pair, &e, &chunk, &npairs);
+  const bool valid = ntile < NB && has_pair;
   const int row0 = valid ? offs_s[e] + chunk * R : 0;
   const int nrows = valid ? min(R, offs_s[e + 1] - row0) : 0;
 
@@ -137,44 +145,49 @@ k_ffn_skinny(const SkinnyArgs A) {
   }
 
   const int U = A.K / UK;
-  const int part = ks * NW + wave;
-  const int u0 = (int)(((long long)part * U) / (S * NW));
-  const int u1 = (int)(((long long)(part + 1) * U) / (S * NW));
+  int u0, u1;
+  unit_range(ks * NW + wave, S * NW, U, &u0, &u1);
+  // the CT column tiles of this group are consecutive streams of U*G units
   const u32x4_t* wp = static_cast<const u32x4_t*>(A.w) + (size_t)(e * NB + ntile) * U * G * 64 + lane;
+  const size_t tile_stride = (size_t)U * G * 64;
 
-  floatx4_t acc[G][MT];
+  floatx4_t acc[CT][G][MT];
 #pragma unroll
-  for (int g = 0; g < G; ++g)
+  for (int c = 0; c < CT; ++c)
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) acc[g][mt] = floatx4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) acc[c][g][mt] = floatx4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
-  u32x4_t wb[D][G];
+  u32x4_t wb[D][CT][G];
   u32x4_t ab[D][MT][AH];
 
 #define MOE_ISSUE(slot, u)                                                                             \
   do {                                                                                                 \
-    _Pragma("unroll") for (int g = 0; g < G; ++g) wb[slot][g] =                                        \
-        __builtin_nontemporal_load(wp + ((size_t)(u) * G + g) * 64);                                   \
+    _Pragma("unroll") for (int c = 0; c < CT; ++c) _Pragma("unroll") for (int g = 0; g < G; ++g)      \
+        wb[slot][c][g] = __builtin_nontemporal_load(wp + c * tile_stride + ((size_t)(u) * G + g) * 64); \
     _Pragma("unroll") for (int mt = 0; mt < MT; ++mt) _Pragma("unroll") for (int h = 0; h < AH; ++h)   \
         ab[slot][mt][h] = *reinterpret_cast<const u32x4_t*>(arow[mt] + (size_t)(u) * UK + 32 * h);     \
   } while (0)
 
 #define MOE_CONSUME(slot)                                                                              \
   do {                                                                                                 \
-    if constexpr (I8) {                                                                                \
-      _Pragma("unroll") for (int h = 0; h < 2; ++h) {                                                  \
-        _Pragma("unroll") for (int g = 0; g < G; ++g) {                                                \
-          const u32x4_t q = wb[slot][g];                                                               \
-          const bf16x8_t bw = h == 0 ? i8x8_to_bf16(q[0], q[1]) : i8x8_to_bf16(q[2], q[3]);            \
-          _Pragma("unroll") for (int mt = 0; mt < MT; ++mt) acc[g][mt] =                               \
-              __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ab[slot][mt][h]), bw, acc[g][mt], 0, 0, 0); \
+    _Pragma("unroll") for (int c = 0; c < CT; ++c) {                                                   \
+      if constexpr (I8) {                                                                              \
+        _Pragma("unroll") for (int h = 0; h < 2; ++h) {                                                \
+          _Pragma("unroll") for (int g = 0; g < G; ++g) {                                              \
+            const u32x4_t q = wb[slot][c][g];                                                          \
+            const bf16x8_t bw = h == 0 ? i8x8_to_bf16(q[0], q[1]) : i8x8_to_bf16(q[2], q[3]);          \
+            _Pragma("unroll") for (int mt = 0; mt < MT; ++mt) acc[c][g][mt] =                          \
+                __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ab[slot][mt][h]), bw, acc[c][g][mt], 0, 0, 0); \
+          }                                                                                            \
         }                                                                                              \
-      }                                                                                                \
-    } else {                                                                                           \
-      _Pragma("unroll") for (int g = 0; g < G; ++g) {                                                  \
-        const bf16x8_t bw = as_bf16x8(wb[slot][g]);                                                    \
-        _Pragma("unroll") for (int mt = 0; mt < MT; ++mt) acc[g][mt] =                                 \
-            __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ab[slot][mt][0]), bw, acc[g][mt], 0, 0, 0); \
+      } else {                                                                                         \
+        _Pragma("unroll") for (int g = 0; g < G; ++g) {                                                \
+          const bf16x8_t bw = as_bf16x8(wb[slot][c][g]);                                               \
+          _Pragma("unroll") for (int mt = 0; mt < MT; ++mt) acc[c][g][mt] =                            \
+              __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ab[slot][mt][0]), bw, acc[c][g][mt], 0, 0, 0); \
+        }                                                                                              \
       }                                                                                                \
     }                                                                                                  \
   } while (0)
@@ -214,26 +227,29 @@ k_ffn_skinny(const SkinnyArgs A) {
 #undef MOE_ISSUE
 
   // Cross-wave reduction through one LDS transpose: wave w writes its partial
-  // tile; each output's NW partials are then read by one thread.
+  // tiles; each output's NW partials are then read by one thread.
 #pragma unroll
-  for (int g = 0; g < G; ++g)
+  for (int c = 0; c < CT; ++c)
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
+    for (int g = 0; g < G; ++g)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) red[((wave * G + g) * MT + mt) * 256 + i * 64 + lane] = acc[g][mt][i];
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          red[(((wave * CT + c) * G + g) * MT + mt) * 256 + i * 64 + lane] = acc[c][g][mt][i];
   __syncthreads();
 
-  for (int o = tid; o < MT * 256; o += NT) {
-    const int mt = o >> 8, i = (o >> 6) & 3, ln = o & 63;
+  for (int o = tid; o < CT * MT * 256; o += NT) {
+    const int c = o / (MT * 256), mt = (o >> 8) % MT, i = (o >> 6) & 3, ln = o & 63;
     const int row = mt * 16 + 4 * (ln >> 4) + i;
     if (row >= nrows) continue;
-    const int col = ntile * 16 + (ln & 15);
+    const int col = (ntile + c) * 16 + (ln & 15);
     float v[G];
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       float s = 0.0f;
 #pragma unroll
-      for (int w = 0; w < NW; ++w) s += red[((w * G + g) * MT + mt) * 256 + i * 64 + ln];
+      for (int w = 0; w < NW; ++w) s += red[(((w * CT + c) * G + g) * MT + mt) * 256 + i * 64 + ln];
       v[g] = s;
     }
     const int r = row0 + row;
@@ -259,47 +275,43 @@ k_ffn_skinny(const SkinnyArgs A) {
       }
     }
   }
-
 }
 
-// Units in flight per wave: enough bytes outstanding per CU to cover HBM
-// latency while the register budget keeps several waves per SIMD.
-constexpr int depth(int mt, int g, bool i8) { return (mt * (i8 ? 2 : 1) + g) <= 3 ? 6 : 4; }
-
-template <int MT, bool I8>
-hipError_t launch_mt(const SkinnyArgs& a, int epi, hipStream_t s) {
-  const int NB = a.N / 16;
-  const long long work = (long long)NB * a.W * a.ksplit;
+template <int MT, int CT, bool I8>
+hipError_t launch_ct(const SkinnyArgs& a, int epi, hipStream_t s) {
+  const int NG = a.N / 16 / CT;
+  const long long work = (long long)NG * a.W * a.ksplit;
   const long long nblk = (work + 7) / 8 * 8;
   const dim3 grid((unsigned)nblk);
   switch (epi) {
-    case EPI_UP_SWIGLU:
-      k_ffn_skinny<MT, 2, I8, EPI_UP_SWIGLU, depth(MT, 2, I8), 4><<<grid, 256, 0, s>>>(a);
-      break;
-    case EPI_UP_RELU:
-      k_ffn_skinny<MT, 1, I8, EPI_UP_RELU, depth(MT, 1, I8), 4><<<grid, 256, 0, s>>>(a);
-      break;
-    case EPI_DOWN_ACC:
-      k_ffn_skinny<MT, 1, I8, EPI_DOWN_ACC, depth(MT, 1, I8), 4><<<grid, 256, 0, s>>>(a);
-      break;
-    default:
-      k_ffn_skinny<MT, 1, I8, EPI_DOWN_ROWS, depth(MT, 1, I8), 4><<<grid, 256, 0, s>>>(a);
-      break;
+    case EPI_UP_SWIGLU: k_ffn_skinny<MT, 2, CT, I8, EPI_UP_SWIGLU, 4><<<grid, 256, 0, s>>>(a); break;
+    case EPI_UP_RELU: k_ffn_skinny<MT, 1, CT, I8, EPI_UP_RELU, 4><<<grid, 256, 0, s>>>(a); break;
+    case EPI_DOWN_ACC: k_ffn_skinny<MT, 1, CT, I8, EPI_DOWN_ACC, 4><<<grid, 256, 0, s>>>(a); break;
+    default: k_ffn_skinny<MT, 1, CT, I8, EPI_DOWN_ROWS, 4><<<grid, 256, 0, s>>>(a); break;
   }
   return hipGetLastError();
 }
 
+template <int MT, bool I8>
+hipError_t launch_mt(const SkinnyArgs& a, int epi, int ct, hipStream_t s) {
+  if constexpr (MT < 4) {
+    if (ct >= 4) return launch_ct<MT, 4, I8>(a, epi, s);
+  }
+  if (ct >= 2) return launch_ct<MT, 2, I8>(a, epi, s);
+  return launch_ct<MT, 1, I8>(a, epi, s);
+}
+
 }  // namespace
 
-hipError_t launch_ffn_skinny(const SkinnyArgs& a, int epi, bool i8, int mt, hipStream_t s) {
+hipError_t launch_ffn_skinny(const SkinnyArgs& a, int epi, bool i8, int mt, int ct, hipStream_t s) {
   if (i8) {
-    if (mt <= 1) return launch_mt<1, true>(a, epi, s);
-    if (mt == 2) return launch_mt<2, true>(a, epi, s);
-    return launch_mt<4, true>(a, epi, s);
+    if (mt <= 1) return launch_mt<1, true>(a, epi, ct, s);
+    if (mt == 2) return launch_mt<2, true>(a, epi, ct, s);
+    return launch_mt<4, true>(a, epi, ct, s);
   }
-  if (mt <= 1) return launch_mt<1, false>(a, epi, s);
-  if (mt == 2) return launch_mt<2, false>(a, epi, s);
-  return launch_mt<4, false>(a, epi, s);
+  if (mt <= 1) return launch_mt<1, false>(a, epi, ct, s);
+  if (mt == 2) return launch_mt<2, false>(a, epi, ct, s);
+  return launch_mt<4, false>(a, epi, ct, s);
 }
 
 }  // namespace moe

@@ -96,7 +96,9 @@ constexpr int kFusedDispatchMax = 4096;
 // Rows per work item for a given M-tile count (16 rows per tile).
 inline int skinny_rows(int mt) { return 16 * mt; }
 
-hipError_t launch_ffn_skinny(const SkinnyArgs& a, int epi, bool i8, int mt, hipStream_t s);
+// mt: 16-row M tiles per work item (1, 2, 4); ct: 16-column tiles per
+// workgroup sharing each activation load (1, 2, 4).
+hipError_t launch_ffn_skinny(const SkinnyArgs& a, int epi, bool i8, int mt, int ct, hipStream_t s);
 
 // ---- expert FFN, fp32 path ----------------------------------------------------
 

@@ -189,37 +189,61 @@ __device__ __forceinline__ void halve_bit(float* v, int lane) {
   }
 }
 
-template <int E>
+template <int E, int TB>
 struct RouteShape {
-  static constexpr int Q = E / 4;         // lanes per router-weight row (16 B each)
+  static constexpr int Q = E / 4;                                  // lanes per router-weight row (16 B each)
   static constexpr int LQ = E == 8 ? 1 : E == 16 ? 2 : E == 32 ? 3 : 4;
-  static constexpr int RPC = 64 / Q;      // rows per 1 KiB chunk
-  static constexpr int TB = 128 / E;      // tokens per block
-  static constexpr int NV = TB * 4;       // partial sums per lane
+  static constexpr int RPC = 64 / Q;                               // rows per 1 KiB chunk
+  static constexpr int NV = TB * 4;                                // partial sums per lane
+  static constexpr int STEPS = 6 - LQ;                             // lane bits that index rows
+  static constexpr bool HALVING = NV >= (2 << STEPS);              // enough sums for a reduce-scatter
+  static constexpr int PER = HALVING ? (NV >> STEPS) : NV;         // sums a lane holds afterwards
 };
 
-constexpr int kRouteLdsX = 128 * 1024;  // bytes of staged activations per block
+template <int B, int LQ, int N>
+__device__ __forceinline__ void halve_down(float* v, int lane) {
+  if constexpr (B >= LQ) {
+    halve_bit<B, N>(v, lane);
+    halve_down<B - 1, LQ, N / 2>(v, lane);
+  }
+}
 
-// Router for E in {8, 16, 32, 64}: one 1024-thread block per TB = 128/E
-// tokens.  The tokens' activation rows are staged in LDS; each wave streams
-// 1 KiB chunks of the router weights with one coalesced 16-byte load per lane
-// (lane = row-in-chunk x expert quad) and keeps TB x 4 partial sums.  Sums
-// over rows: a reduce-scatter across the lanes of a wave, then a fixed-order
-// sum over the 16 waves in LDS.  One wave per token then takes the top-k.
-// The block also zeroes its tokens' rows of the fp32 output accumulator.
-template <int E, bool XBF16>
+template <int LQ, int N>
+__device__ __forceinline__ void butterfly_rows(float* v) {
+#pragma unroll
+  for (int i = 0; i < N; ++i)
+#pragma unroll
+    for (int b = LQ; b < 6; ++b) v[i] += __shfl_xor(v[i], 1 << b, 64);
+}
+
+constexpr int kRouteLdsX = 128 * 1024;  // most bytes of staged activations per block
+
+// Bytes of activations a block of TB tokens can stage; the host checks
+// TB * m * sizeof(x) against the same figure.
+constexpr int route_lds_bytes(int tb) { return tb * 65536 < kRouteLdsX ? tb * 65536 : kRouteLdsX; }
+
+// Router for E in {8, 16, 32, 64}: one 1024-thread block per TB tokens
+// (TB * E <= 128).  The tokens' activation rows are staged in LDS; each wave
+// streams 1 KiB chunks of the router weights with one coalesced 16-byte load
+// per lane (lane = row-in-chunk x expert quad) and keeps TB x 4 partial sums.
+// Sums over rows: across the lanes of a wave (reduce-scatter when there are
+// enough partials, butterfly otherwise), then a fixed-order sum over the 16
+// waves in LDS.  One wave per token then takes the top-k.  The block also
+// zeroes its tokens' rows of the fp32 output accumulator.
+template <int E, int TB, bool XBF16>
 __global__ __launch_bounds__(1024) void k_route_fast(const void* __restrict__ x, const float* __restrict__ wg,
                                                      const float* __restrict__ bias, int T, int m, int k,
                                                      float* __restrict__ logits, int32_t* __restrict__ idx,
                                                      float* __restrict__ wout, float* __restrict__ yacc, int ym) {
-  using S = RouteShape<E>;
-  __shared__ __attribute__((aligned(16))) unsigned char xs_raw[kRouteLdsX];
-  __shared__ float red[16][128];
-  __shared__ float lg[S::TB][E];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int t0 = blockIdx.x * S::TB;
-  const int nt = min(S::TB, T - t0);
+  using S = RouteShape<E, TB>;
+  static_assert(TB * E <= 128 && TB <= 16, "block shape");
   constexpr int XB = XBF16 ? 2 : 4;
+  __shared__ __attribute__((aligned(16))) unsigned char xs_raw[route_lds_bytes(TB)];
+  __shared__ float red[16][TB * E];
+  __shared__ float lg[TB][E];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int t0 = blockIdx.x * TB;
+  const int nt = min(TB, T - t0);
 
   if (yacc) {
     float4* yr = reinterpret_cast<float4*>(yacc + (size_t)t0 * ym);
@@ -231,7 +255,7 @@ __global__ __launch_bounds__(1024) void k_route_fast(const void* __restrict__ x,
     const int row16 = m * XB / 16;
     uint4* dst = reinterpret_cast<uint4*>(xs_raw);
     const uint4* src = reinterpret_cast<const uint4*>(static_cast<const char*>(x) + (size_t)t0 * m * XB);
-    for (int i = tid; i < S::TB * row16; i += 1024) dst[i] = (i < nt * row16) ? src[i] : make_uint4(0, 0, 0, 0);
+    for (int i = tid; i < TB * row16; i += 1024) dst[i] = (i < nt * row16) ? src[i] : make_uint4(0, 0, 0, 0);
   }
   __syncthreads();
 
@@ -241,11 +265,12 @@ __global__ __launch_bounds__(1024) void k_route_fast(const void* __restrict__ x,
   const int q = lane & (S::Q - 1);
   const int rr = lane >> S::LQ;
   const int nchunks = m / S::RPC;
+#pragma unroll 2
   for (int c = wave; c < nchunks; c += 16) {
     const int r = c * S::RPC + rr;
     const float4 wv = *reinterpret_cast<const float4*>(wg + (size_t)r * E + 4 * q);
 #pragma unroll
-    for (int t = 0; t < S::TB; ++t) {
+    for (int t = 0; t < TB; ++t) {
       float xv;
       if constexpr (XBF16)
         xv = bf16_to_f32(reinterpret_cast<const uint16_t*>(xs_raw)[t * m + r]);
@@ -257,25 +282,24 @@ __global__ __launch_bounds__(1024) void k_route_fast(const void* __restrict__ x,
       acc[t * 4 + 3] = fmaf(xv, wv.w, acc[t * 4 + 3]);
     }
   }
-  // sum over the row lanes (lane bits LQ..5), leaving 2 sums per lane
-  if constexpr (S::LQ <= 1) halve_bit<5, S::NV>(acc, lane), halve_bit<4, S::NV / 2>(acc, lane),
-      halve_bit<3, S::NV / 4>(acc, lane), halve_bit<2, S::NV / 8>(acc, lane), halve_bit<1, S::NV / 16>(acc, lane);
-  if constexpr (S::LQ == 2) halve_bit<5, S::NV>(acc, lane), halve_bit<4, S::NV / 2>(acc, lane),
-      halve_bit<3, S::NV / 4>(acc, lane), halve_bit<2, S::NV / 8>(acc, lane);
-  if constexpr (S::LQ == 3) halve_bit<5, S::NV>(acc, lane), halve_bit<4, S::NV / 2>(acc, lane),
-      halve_bit<3, S::NV / 4>(acc, lane);
-  if constexpr (S::LQ == 4) halve_bit<5, S::NV>(acc, lane), halve_bit<4, S::NV / 2>(acc, lane);
-  {
+  // sum over the row lanes (lane bits LQ..5)
+  if constexpr (S::HALVING) {
+    halve_down<5, S::LQ, S::NV>(acc, lane);
     const int L = lane >> S::LQ;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int v = 2 * L + i;  // partial index t*4 + j
-      const int t = v >> 2, e = 4 * q + (v & 3);
-      red[wave][t * E + e] = acc[i];
+    for (int i = 0; i < S::PER; ++i) {
+      const int v = L * S::PER + i;  // partial index t*4 + j
+      red[wave][(v >> 2) * E + 4 * q + (v & 3)] = acc[i];
+    }
+  } else {
+    butterfly_rows<S::LQ, S::NV>(acc);
+    if (rr == 0) {
+#pragma unroll
+      for (int v = 0; v < S::NV; ++v) red[wave][(v >> 2) * E + 4 * q + (v & 3)] = acc[v];
     }
   }
   __syncthreads();
-  if (tid < S::TB * E) {
+  if (tid < TB * E) {
     float s = 0.0f;
 #pragma unroll
     for (int w = 0; w < 16; ++w) s += red[w][tid];
@@ -314,23 +338,33 @@ hipError_t launch_route_topk(const void* x, bool x_bf16, const float* wg, const 
                              int k, bool logits_in, float* logits, int32_t* idx, float* w, float* yacc, int ym,
                              hipStream_t s) {
   const int xb = x_bf16 ? 2 : 4;
-  const bool fast = !logits_in && (E == 8 || E == 16 || E == 32 || E == 64) && (128 / E) * m * xb <= kRouteLdsX &&
-                    (yacc == nullptr || ym % 4 == 0);
-  if (fast) {
-    const unsigned grid = (unsigned)((T + 128 / E - 1) / (128 / E));
-#define MOE_ROUTE_FAST(EE)                                                                                  \
-  if (E == EE) {                                                                                            \
-    if (x_bf16)                                                                                             \
-      k_route_fast<EE, true><<<grid, 1024, 0, s>>>(x, wg, bias, T, m, k, logits, idx, w, yacc, ym);         \
-    else                                                                                                    \
-      k_route_fast<EE, false><<<grid, 1024, 0, s>>>(x, wg, bias, T, m, k, logits, idx, w, yacc, ym);        \
-    return hipGetLastError();                                                                               \
+  if (!logits_in && (E == 8 || E == 16 || E == 32 || E == 64) && (yacc == nullptr || ym % 4 == 0)) {
+    // tokens per block: one for decode batches (spreads the router weights'
+    // reads over T CUs), up to 128 / E for large batches
+    const int tb_max = 128 / E < 16 ? 128 / E : 16;
+    const int tb = T <= 64 ? 1 : (T <= 1024 ? (4 < tb_max ? 4 : tb_max) : tb_max);
+    if (tb * m * xb <= route_lds_bytes(tb)) {
+      const unsigned grid = (unsigned)((T + tb - 1) / tb);
+#define MOE_ROUTE_FAST(EE, TT)                                                                               \
+  if (E == EE && tb == TT) {                                                                                 \
+    if (x_bf16)                                                                                              \
+      k_route_fast<EE, TT, true><<<grid, 1024, 0, s>>>(x, wg, bias, T, m, k, logits, idx, w, yacc, ym);      \
+    else                                                                                                     \
+      k_route_fast<EE, TT, false><<<grid, 1024, 0, s>>>(x, wg, bias, T, m, k, logits, idx, w, yacc, ym);     \
+    return hipGetLastError();                                                                                \
   }
-    MOE_ROUTE_FAST(8)
-    MOE_ROUTE_FAST(16)
-    MOE_ROUTE_FAST(32)
-    MOE_ROUTE_FAST(64)
+      MOE_ROUTE_FAST(8, 1)
+      MOE_ROUTE_FAST(8, 4)
+      MOE_ROUTE_FAST(8, 16)
+      MOE_ROUTE_FAST(16, 1)
+      MOE_ROUTE_FAST(16, 4)
+      MOE_ROUTE_FAST(16, 8)
+      MOE_ROUTE_FAST(32, 1)
+      MOE_ROUTE_FAST(32, 4)
+      MOE_ROUTE_FAST(64, 1)
+      MOE_ROUTE_FAST(64, 2)
 #undef MOE_ROUTE_FAST
+    }
   }
   if (yacc) {
     const hipError_t e = launch_fill_zero(yacc, (size_t)T * ym, s);

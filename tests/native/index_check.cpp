@@ -1,0 +1,123 @@
+// Exhaustive host check of the decode FFN launch's index arithmetic
+// (moe_index.hpp, the same code the kernel runs).  Exit status 0 = pass.
+#include <cstdio>
+#include <cstdlib>
+#include <random>
+#include <set>
+#include <tuple>
+#include <vector>
+
+#include "moe_index.hpp"
+
+static int fails = 0;
+#define CHECK(c, ...)                         \
+  do {                                        \
+    if (!(c)) {                               \
+      if (fails < 20) {                       \
+        fprintf(stderr, "FAIL %s: ", #c);     \
+        fprintf(stderr, __VA_ARGS__);         \
+        fprintf(stderr, "\n");                \
+      }                                       \
+      ++fails;                                \
+    }                                         \
+  } while (0)
+
+// One launch: NG column groups x S slices x W pairs, grid padded to 8.
+static void check_launch(int NG, int W, int S, const std::vector<int>& offsets, int R) {
+  const int E = (int)offsets.size() - 1;
+  const long long work = (long long)NG * W * S;
+  const int nblk = (int)((work + 7) / 8 * 8);
+  std::set<int> logical;
+  std::set<std::tuple<int, int, int>> items;
+  std::vector<std::vector<int>> rows_seen(E);
+  for (int b = 0; b < nblk; ++b) {
+    const int L = moe::xcd_logical(b, nblk);
+    CHECK(L >= 0 && L < nblk, "b=%d L=%d nblk=%d", b, L, nblk);
+    logical.insert(L);
+    const moe::SkinnyWork w = moe::skinny_work(L, W, S);
+    CHECK(w.ks >= 0 && w.ks < S && w.pair >= 0 && w.pair < W && w.ngroup >= 0, "L=%d -> (%d,%d,%d)", L, w.ngroup,
+          w.ks, w.pair);
+    if (w.ngroup >= NG) continue;  // padding block
+    CHECK(items.insert({w.ngroup, w.ks, w.pair}).second, "duplicate item L=%d", L);
+    int e, chunk, npairs;
+    const bool ok = moe::skinny_pair(offsets.data(), E, R, w.pair, &e, &chunk, &npairs);
+    CHECK(npairs <= W, "npairs %d > W %d", npairs, W);
+    if (!ok) continue;
+    CHECK(e >= 0 && e < E && chunk >= 0, "pair %d -> e=%d chunk=%d", w.pair, e, chunk);
+    const int row0 = offsets[e] + chunk * R;
+    const int nrows = std::min(R, offsets[e + 1] - row0);
+    CHECK(nrows >= 1 && row0 >= offsets[e] && row0 + nrows <= offsets[e + 1], "rows [%d,+%d) outside expert %d",
+          row0, nrows, e);
+    if (w.ngroup == 0 && w.ks == 0)
+      for (int r = row0; r < row0 + nrows; ++r) rows_seen[e].push_back(r);
+  }
+  CHECK((int)logical.size() == nblk, "xcd_logical not a bijection (nblk=%d)", nblk);
+  CHECK((long long)items.size() == work, "items %zu != %lld", items.size(), work);
+  for (int e = 0; e < E; ++e) {
+    std::vector<int>& v = rows_seen[e];
+    std::sort(v.begin(), v.end());
+    CHECK((int)v.size() == offsets[e + 1] - offsets[e], "expert %d rows covered %zu of %d", e, v.size(),
+          offsets[e + 1] - offsets[e]);
+    for (size_t i = 0; i < v.size(); ++i) CHECK(v[i] == offsets[e] + (int)i, "expert %d row %zu", e, i);
+  }
+}
+
+static void check_units(int U, int parts) {
+  int prev = 0;
+  for (int p = 0; p < parts; ++p) {
+    int u0, u1;
+    moe::unit_range(p, parts, U, &u0, &u1);
+    CHECK(u0 == prev && u1 >= u0 && u1 <= U, "U=%d parts=%d p=%d [%d,%d)", U, parts, p, u0, u1);
+    prev = u1;
+  }
+  CHECK(prev == U, "U=%d parts=%d ends at %d", U, parts, prev);
+}
+
+static std::vector<int> offsets_from(const std::vector<int>& counts) {
+  std::vector<int> o(counts.size() + 1, 0);
+  for (size_t i = 0; i < counts.size(); ++i) o[i + 1] = o[i] + counts[i];
+  return o;
+}
+
+int main() {
+  std::mt19937 rng(1234);
+  // the measured layers' shapes, with their realised or typical counts
+  struct Case {
+    int N, E, n, R, CT, S;
+    std::vector<int> counts;
+  };
+  std::vector<Case> cases = {
+      {14336, 8, 32, 16, 1, 1, {5, 8, 3, 3, 4, 4, 4, 1}},
+      {4096, 8, 32, 16, 1, 4, {5, 8, 3, 3, 4, 4, 4, 1}},
+      {6400, 16, 512, 64, 2, 1, {165, 106, 61, 38, 36, 22, 19, 12, 11, 8, 9, 3, 11, 3, 5, 3}},
+      {4096, 16, 512, 64, 2, 4, {165, 106, 61, 38, 36, 22, 19, 12, 11, 8, 9, 3, 11, 3, 5, 3}},
+      {14336, 8, 128, 32, 4, 1, {20, 11, 15, 16, 22, 16, 15, 13}},
+      {4096, 8, 128, 32, 4, 4, {20, 11, 15, 16, 22, 16, 15, 13}},
+  };
+  for (auto& c : cases) {
+    const int W = c.E + c.n / c.R;
+    check_launch(c.N / 16 / c.CT, W, c.S, offsets_from(c.counts), c.R);
+  }
+  // random shapes, including empty experts and one expert holding everything
+  for (int it = 0; it < 300; ++it) {
+    const int E = 1 + (int)(rng() % 64);
+    const int R = 16 << (rng() % 3);
+    const int CT = 1 << (rng() % 3);
+    const int S = 1 + (int)(rng() % 4);
+    const int NB = 4 * (1 + (int)(rng() % 64));
+    const int n = (int)(rng() % 3000);
+    std::vector<int> counts(E, 0);
+    const int mode = it % 3;
+    for (int a = 0; a < n; ++a) counts[mode == 0 ? (int)(rng() % E) : (mode == 1 ? 0 : (int)(rng() % (1 + E / 4)))]++;
+    const int W = E + n / R;
+    check_launch(NB / CT, W, S, offsets_from(counts), R);
+  }
+  for (int U : {1, 2, 7, 50, 112, 128, 200, 448})
+    for (int parts : {1, 4, 8, 16, 32}) check_units(U, parts);
+  if (fails) {
+    fprintf(stderr, "%d failures\n", fails);
+    return 1;
+  }
+  printf("index check ok\n");
+  return 0;
+}
