@@ -27,10 +27,9 @@ HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
 METRIC = "MoE layer tokens/s; achieved HBM GB/s (T≤64) or MFMA TFLOP/s (T≥4096)"
 TRAFFIC_DIR = os.path.join(ROOT, "profiles")
-KERNEL_SOURCES = {
-    "ffn_up": ["mixture_experts_layer_gemv_amd/csrc/moe_ffn_skinny.hip"],
-    "ffn_down": ["mixture_experts_layer_gemv_amd/csrc/moe_ffn_skinny.hip"],
-}
+_SKINNY = ["mixture_experts_layer_gemv_amd/csrc/" + f for f in
+           ("moe_ffn_skinny.hip", "moe_index.hpp", "moe_dispatch_block.hpp", "moe_kernels.hpp")]
+KERNEL_SOURCES = {"ffn_up": _SKINNY, "ffn_down": _SKINNY}
 
 
 def parse():
