@@ -29,7 +29,8 @@ METRIC = "MoE layer tokens/s; achieved HBM GB/s (T≤64) or MFMA TFLOP/s (T≥40
 TRAFFIC_DIR = os.path.join(ROOT, "profiles")
 _SKINNY = ["mixture_experts_layer_gemv_amd/csrc/" + f for f in
            ("moe_ffn_skinny.hip", "moe_index.hpp", "moe_dispatch_block.hpp", "moe_kernels.hpp")]
-KERNEL_SOURCES = {"ffn_up": _SKINNY, "ffn_down": _SKINNY}
+_GEMM = ["mixture_experts_layer_gemv_amd/csrc/" + f for f in ("moe_ffn_gemm.hip", "moe_index.hpp", "moe_kernels.hpp")]
+KERNEL_SOURCES = {"ffn_up": _SKINNY, "ffn_down": _SKINNY, "gemm_up": _GEMM, "gemm_down": _GEMM}
 
 
 def parse():
@@ -171,7 +172,7 @@ def main():
     ms_events = ev0.elapsed_time(ev1) / args.steps
     kern = {}
     for name in ("fill", "route_topk", "dispatch", "ffn_up", "ffn_down", "ffn_f32_up", "ffn_f32_down", "finalize",
-                 "gemm_up", "gemm_down"):
+                 "gemm_up", "gemm_down", "combine"):
         tot, n = M.moe_profile_query(name)
         if n:
             kern[name] = round(tot / n * 1000.0, 3)  # us per launch
@@ -185,9 +186,9 @@ def main():
         torch.cuda.synchronize()
 
     A = algorithmic(sp, counts)
-    dominant = "ffn_up" if "ffn_up" in kern else "ffn_f32_up"
+    dominant = next(n for n in ("gemm_up", "ffn_up", "ffn_f32_up") if n in kern)
     up_us = kern.get(dominant, float("nan"))
-    mfma_bound = sp.T >= 4096
+    mfma_bound = dominant == "gemm_up"
     if mfma_bound:
         achieved = A["up_flop"] / (up_us * 1e-6) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",

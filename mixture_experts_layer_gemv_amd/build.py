@@ -15,7 +15,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmoe_gemv.so")
-SOURCES = ["moe_api.cpp", "moe_route.hip", "moe_ffn_skinny.hip", "moe_misc.hip"]
+SOURCES = ["moe_api.cpp", "moe_route.hip", "moe_ffn_skinny.hip", "moe_ffn_gemm.hip", "moe_misc.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 COMMON = [

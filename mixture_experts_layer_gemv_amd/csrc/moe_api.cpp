@@ -105,9 +105,28 @@ int check_combo(int x_dtype, int w_dtype) {
   return MOE_OK;
 }
 
+// The grouped-GEMM path serves bf16 layers whose experts average at least
+// kGemmMinRows rows; smaller batches stream weights through the skinny path.
+constexpr int kGemmMinRows = 128;
+
+bool use_gemm(const moe_weights* W, int T, int k) {
+  if (W->w_dtype != MOE_BF16) return false;
+  // The GEMM addresses activations and one projection's packed weights with
+  // 32-bit byte offsets from a uniform base.
+  const unsigned long long lim = 1ull << 32;
+  const unsigned long long mp = (unsigned long long)W->m * W->p;
+  const unsigned long long G = W->kind == MOE_SWIGLU ? 2 : 1;
+  if ((unsigned long long)W->E * mp * 2 * G >= lim || (unsigned long long)T * W->m * 2 >= lim ||
+      (unsigned long long)T * k * W->p * 2 >= lim)
+    return false;
+  const char* v = getenv("MOE_FFN_PATH");
+  if (v && *v) return v[0] == 'g';
+  return (long long)T * k >= (long long)kGemmMinRows * W->E;
+}
+
 // Workspace carving, in the order listed.
 struct Ws {
-  size_t logits, idx, w, counts, offsets, perm, inv, h, yacc, total;
+  size_t logits, idx, w, counts, offsets, perm, inv, h, yacc, yperm, total;
 };
 
 Ws ws_layout(const moe_weights* W, int T, int k) {
@@ -128,6 +147,7 @@ Ws ws_layout(const moe_weights* W, int T, int k) {
   L.inv = take(n * 4);
   L.h = take(n * (size_t)W->p * (W->w_dtype == MOE_F32 ? 4 : 2));
   L.yacc = take((size_t)T * W->m * 4);
+  L.yperm = use_gemm(W, T, k) ? take(n * (size_t)W->m * 4) : off;
   L.total = off;
   return L;
 }
@@ -174,6 +194,7 @@ struct FfnIo {
   void* h;                  // hidden activations [T*k][p]
   float* down_out;          // y_acc [T][m] (combine) or y_perm [T*k][m]
   bool combine;
+  float* yperm;             // grouped-GEMM path with combine: unweighted rows [T*k][m]
 };
 
 int run_ffn(const moe_weights* W, const FfnIo& io, hipStream_t s) {
@@ -207,6 +228,34 @@ int run_ffn(const moe_weights* W, const FfnIo& io, hipStream_t s) {
     a.gather = 0;
     a.epi = io.combine ? moe::EPI_DOWN_ACC : moe::EPI_DOWN_ROWS;
     MOE_TRY_HIP(run("ffn_f32_down", s, [&] { return moe::launch_ffn_f32(a, s); }));
+    return MOE_OK;
+  }
+  if (use_gemm(W, T, k)) {
+    moe::GemmArgs g{};
+    g.perm = io.perm;
+    g.offsets = io.offsets;
+    g.topk = k;
+    g.E = E;
+    g.W = E + (int)((long long)T * k / moe::gemm_rows_per_block());
+    g.topk_w = io.topk_w;
+    // up: x -> H
+    g.w = W->up;
+    g.act = static_cast<const uint16_t*>(io.x);
+    g.h_out = static_cast<uint16_t*>(io.h);
+    g.K = m;
+    g.N = p;
+    g.gather = 1;
+    const int up_epi = swiglu ? moe::EPI_UP_SWIGLU : moe::EPI_UP_RELU;
+    MOE_TRY_HIP(run("gemm_up", s, [&] { return moe::launch_ffn_gemm(g, up_epi, s); }));
+    // down: H -> unweighted rows (the combine follows) or weighted atomics
+    g.w = W->down;
+    g.act = static_cast<const uint16_t*>(io.h);
+    g.h_out = nullptr;
+    g.f_out = io.combine ? io.yperm : io.down_out;
+    g.K = p;
+    g.N = m;
+    g.gather = 0;
+    MOE_TRY_HIP(run("gemm_down", s, [&] { return moe::launch_ffn_gemm(g, moe::EPI_DOWN_ROWS, s); }));
     return MOE_OK;
   }
   const bool i8 = W->w_dtype == MOE_I8;
@@ -480,11 +529,12 @@ int moe_layer_forward(const moe_weights* w, const float* w_router, const float* 
   const size_t ny = (size_t)T * m;
   // decode-sized layers on the MFMA path: the up projection derives the
   // dispatch itself
-  const bool fused = w->w_dtype != MOE_F32 && (long long)T * k <= moe::kFusedDispatchMax;
+  const bool gemm = use_gemm(w, T, k);
+  const bool fused = !gemm && w->w_dtype != MOE_F32 && (long long)T * k <= moe::kFusedDispatchMax;
 
   MOE_TRY_HIP(run("route_topk", s, [&] {
     return moe::launch_route_topk(x, x_dtype == MOE_BF16, w_router, b_router, T, m, E, k, false, logits, idx, tw,
-                                  yacc, m, s);
+                                  gemm ? nullptr : yacc, m, s);
   }));
   if (!fused)
     MOE_TRY_HIP(run("dispatch", s, [&] { return moe::launch_dispatch(idx, T * k, E, counts, offsets, perm, inv, s); }));
@@ -501,7 +551,14 @@ int moe_layer_forward(const moe_weights* w, const float* w_router, const float* 
   io.h = ws + L.h;
   io.down_out = yacc;
   io.combine = true;
+  io.yperm = reinterpret_cast<float*>(ws + L.yperm);
   if (int rc = run_ffn(w, io, s)) return rc;
+  if (gemm) {
+    MOE_TRY_HIP(run("combine", s, [&] {
+      return moe::launch_combine(io.yperm, inv, tw, T, m, k, y, y_bf16, s);
+    }));
+    return ok();
+  }
   if (y_bf16)
     MOE_TRY_HIP(run("finalize", s, [&] { return moe::launch_f32_to_bf16(yacc, static_cast<uint16_t*>(y), ny, s); }));
   return ok();

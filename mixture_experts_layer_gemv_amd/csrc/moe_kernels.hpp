@@ -100,6 +100,25 @@ inline int skinny_rows(int mt) { return 16 * mt; }
 // workgroup sharing each activation load (1, 2, 4).
 hipError_t launch_ffn_skinny(const SkinnyArgs& a, int epi, bool i8, int mt, int ct, hipStream_t s);
 
+// ---- expert FFN, grouped GEMM (prefill-sized) path ----------------------------
+
+struct GemmArgs {
+  const void* w;           // packed bf16 weights of this projection
+  const uint16_t* act;     // bf16 activations: x [T][K] (gather) or H [T*k][K]
+  const int32_t* perm;     // [T*k]
+  const int32_t* offsets;  // [E+1]
+  const float* topk_w;     // [T*k] (EPI_DOWN_ACC)
+  uint16_t* h_out;         // [T*k][N] bf16 (up epilogues)
+  float* f_out;            // y_acc [T][N] (EPI_DOWN_ACC) or y_perm [T*k][N] (EPI_DOWN_ROWS)
+  int K, N, E, topk;
+  int gather;              // 1: activation row = perm[r] / topk, 0: row r
+  int W;                   // upper bound on (expert, 256-row block) pairs
+};
+
+// K a multiple of 64, N a multiple of 64, bf16 weights.
+hipError_t launch_ffn_gemm(const GemmArgs& a, int epi, hipStream_t s);
+int gemm_rows_per_block();
+
 // ---- expert FFN, fp32 path ----------------------------------------------------
 
 struct F32Args {

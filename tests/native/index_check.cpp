@@ -62,6 +62,82 @@ static void check_launch(int NG, int W, int S, const std::vector<int>& offsets, 
   }
 }
 
+// Grouped GEMM launch: 256-row blocks, 2 x 4 waves of 128 x (nf fragments),
+// each wave copying A and B fragments 2w, 2w+1 of every stage.  Checks that
+// every copy stays inside its operand and its 32-bit offset, that the B
+// fragment a wave reads is the tile and half its epilogue writes, and (when
+// `cover`) that every output element is written exactly once.
+static void check_gemm(int K, int N, int G, int T, int topk, bool gather, const std::vector<int>& offsets,
+                       bool cover, std::mt19937& rng) {
+  const int BM = 256, NF = 4, TPW = NF / G;
+  const int E = (int)offsets.size() - 1;
+  const int n = offsets[E];
+  const int NB = N / 16, U = K / 32;
+  std::vector<int> perm(n);
+  for (int i = 0; i < n; ++i) perm[i] = i;
+  std::shuffle(perm.begin(), perm.end(), rng);
+  const int W = E + n / BM;
+  const int tiles = 4 * TPW;
+  const long long work = (long long)((NB + tiles - 1) / tiles) * W;
+  const int nblk = (int)((work + 7) / 8 * 8);
+  const unsigned long long act_bytes = (unsigned long long)(gather ? T : n) * K * 2;
+  const unsigned long long w_bytes = (unsigned long long)E * NB * U * G * 1024;
+  std::vector<unsigned char> seen(cover ? (size_t)n * (N / 16) : 0, 0);
+  int npairs_max = 0;
+  for (int b = 0; b < nblk; ++b) {
+    const moe::GemmWork gw = moe::gemm_work(moe::xcd_logical(b, nblk), W);
+    int e, mb, npairs;
+    if (!moe::skinny_pair(offsets.data(), E, BM, gw.mpair, &e, &mb, &npairs)) continue;
+    npairs_max = std::max(npairs_max, npairs);
+    const int tile_base = gw.nblock * tiles;
+    if (tile_base >= NB) continue;
+    const int row0 = offsets[e] + mb * BM;
+    const int nrows = std::min(BM, offsets[e + 1] - row0);
+    CHECK(nrows >= 1 && row0 + nrows <= offsets[e + 1], "gemm rows [%d,+%d) e=%d", row0, nrows, e);
+    std::vector<int> rows_s(BM);
+    for (int t = 0; t < BM; ++t) {
+      const int r = t < nrows ? t : 0;
+      rows_s[t] = gather ? perm[row0 + r] / topk : row0 + r;
+    }
+    for (int wave = 0; wave < 8; ++wave)
+      for (int j = 0; j < 2; ++j) {
+        const int f = 2 * wave + j;
+        CHECK(16 + f < 32, "lds slot %d", 16 + f);
+        for (int lane = 0; lane < 64; ++lane) {
+          const unsigned long long a = moe::gemm_a_offset(rows_s[f * 16 + (lane & 15)], K, lane);
+          CHECK(a < (1ull << 32) && a + (U - 1) * 64ull + 16 <= act_bytes, "A offset %llu of %llu", a, act_bytes);
+          const unsigned long long bo = moe::gemm_b_offset(e, NB, U, G, tile_base, NF, f, lane);
+          CHECK(bo < (1ull << 32) && bo + (U - 1) * (unsigned long long)G * 1024 + 16 <= w_bytes,
+                "B offset %llu of %llu", bo, w_bytes);
+        }
+      }
+    for (int wm = 0; wm < 2; ++wm)
+      for (int wn = 0; wn < 4; ++wn)
+        for (int t = 0; t < TPW; ++t) {
+          const int nb = tile_base + wn * TPW + t;
+          if (nb >= NB) continue;
+          for (int g = 0; g < G; ++g) {
+            const unsigned long long bo = moe::gemm_b_offset(e, NB, U, G, tile_base, NF, wn * NF + t * G + g, 0);
+            CHECK(bo == ((unsigned long long)(e * NB + nb) * U * G + g) * 1024ull, "B fragment of tile %d g=%d", nb,
+                  g);
+          }
+          if (!cover) continue;
+          for (int i = 0; i < 8; ++i)
+            for (int r16 = 0; r16 < 16; ++r16) {
+              const int row = wm * 128 + i * 16 + r16;
+              if (row >= nrows) continue;
+              unsigned char& c = seen[(size_t)(row0 + row) * (N / 16) + nb];
+              CHECK(c == 0, "row %d tile %d written twice", row0 + row, nb);
+              c = 1;
+            }
+        }
+  }
+  CHECK(npairs_max <= W, "gemm npairs %d > W %d", npairs_max, W);
+  if (cover)
+    for (size_t i = 0; i < seen.size(); ++i) CHECK(seen[i] == 1, "row %zu tile %zu never written", i / (N / 16),
+                                                   i % (N / 16));
+}
+
 static void check_units(int U, int parts) {
   int prev = 0;
   for (int p = 0; p < parts; ++p) {
@@ -111,6 +187,27 @@ int main() {
     for (int a = 0; a < n; ++a) counts[mode == 0 ? (int)(rng() % E) : (mode == 1 ? 0 : (int)(rng() % (1 + E / 4)))]++;
     const int W = E + n / R;
     check_launch(NB / CT, W, S, offsets_from(counts), R);
+  }
+  // grouped GEMM: the measured prefill layer (T=8192, top-2 of 8) and
+  // random small shapes with ragged and empty experts
+  {
+    std::vector<int> counts = {2110, 1980, 2051, 2003, 2090, 2046, 2049, 2055};
+    const std::vector<int> off = offsets_from(counts);
+    check_gemm(4096, 14336, 2, 8192, 2, true, off, false, rng);
+    check_gemm(14336, 4096, 1, 8192, 2, false, off, false, rng);
+  }
+  for (int it = 0; it < 120; ++it) {
+    const int E = 1 + (int)(rng() % 16);
+    const int topk = 1 + (int)(rng() % std::min(E, 4));
+    const int T = (int)(rng() % 1500);
+    const int K = 64 * (1 + (int)(rng() % 12));
+    const int N = 64 * (1 + (int)(rng() % 12));
+    std::vector<int> counts(E, 0);
+    for (int a = 0; a < T * topk; ++a) counts[it % 2 ? (int)(rng() % E) : (int)(rng() % (1 + E / 3))]++;
+    const std::vector<int> off = offsets_from(counts);
+    check_gemm(K, N, 2, T, topk, true, off, true, rng);
+    check_gemm(K, N, 1, T, topk, true, off, true, rng);
+    check_gemm(N, K, 1, T, topk, false, off, true, rng);
   }
   for (int U : {1, 2, 7, 50, 112, 128, 200, 448})
     for (int parts : {1, 4, 8, 16, 32}) check_units(U, parts);
