@@ -172,7 +172,7 @@ def main():
     ms_events = ev0.elapsed_time(ev1) / args.steps
     kern = {}
     for name in ("fill", "route_topk", "dispatch", "ffn_up", "ffn_down", "ffn_f32_up", "ffn_f32_down", "finalize",
-                 "gemm_up", "gemm_down", "combine"):
+                 "pack_rows", "gemm_up", "gemm_down", "combine"):
         tot, n = M.moe_profile_query(name)
         if n:
             kern[name] = round(tot / n * 1000.0, 3)  # us per launch
@@ -197,7 +197,7 @@ def main():
         achieved = A["up_bytes"] / (up_us * 1e-6) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4)}
-    roof["traffic"] = load_traffic(dominant, args.workload)
+    roof["traffic"] = load_traffic(dominant, sp.name)
     roof["kernel"] = dominant
     roof["algorithmic_bytes" if not mfma_bound else "algorithmic_flop"] = (
         A["up_bytes"] if not mfma_bound else A["up_flop"])

@@ -13,6 +13,7 @@
 #include <vector>
 
 #include "moe_gemv.h"
+#include "moe_index.hpp"
 #include "moe_kernels.hpp"
 
 struct moe_weights {
@@ -116,8 +117,8 @@ bool use_gemm(const moe_weights* W, int T, int k) {
   const unsigned long long lim = 1ull << 32;
   const unsigned long long mp = (unsigned long long)W->m * W->p;
   const unsigned long long G = W->kind == MOE_SWIGLU ? 2 : 1;
-  if ((unsigned long long)W->E * mp * 2 * G >= lim || (unsigned long long)T * W->m * 2 >= lim ||
-      (unsigned long long)T * k * W->p * 2 >= lim)
+  const unsigned long long rows = (unsigned long long)moe::packed_rows_max((long long)T * k, W->E);
+  if ((unsigned long long)W->E * mp * 2 * G >= lim || rows * W->m * 2 >= lim || rows * W->p * 2 >= lim)
     return false;
   const char* v = getenv("MOE_FFN_PATH");
   if (v && *v) return v[0] == 'g';
@@ -126,7 +127,7 @@ bool use_gemm(const moe_weights* W, int T, int k) {
 
 // Workspace carving, in the order listed.
 struct Ws {
-  size_t logits, idx, w, counts, offsets, perm, inv, h, yacc, yperm, total;
+  size_t logits, idx, w, counts, offsets, perm, inv, h, yacc, yperm, xp, total;
 };
 
 Ws ws_layout(const moe_weights* W, int T, int k) {
@@ -145,9 +146,13 @@ Ws ws_layout(const moe_weights* W, int T, int k) {
   L.offsets = take((size_t)(W->E + 1) * 4);
   L.perm = take(n * 4);
   L.inv = take(n * 4);
-  L.h = take(n * (size_t)W->p * (W->w_dtype == MOE_F32 ? 4 : 2));
+  const bool gemm = use_gemm(W, T, k);
+  // the grouped GEMM keeps H and the gathered x in the packed row layout
+  const size_t hrows = gemm ? (size_t)moe::packed_rows_max((long long)n, W->E) : n;
+  L.h = take(hrows * (size_t)W->p * (W->w_dtype == MOE_F32 ? 4 : 2));
   L.yacc = take((size_t)T * W->m * 4);
-  L.yperm = use_gemm(W, T, k) ? take(n * (size_t)W->m * 4) : off;
+  L.yperm = gemm ? take(n * (size_t)W->m * 4) : off;
+  L.xp = gemm ? take(hrows * (size_t)W->m * 2) : off;
   L.total = off;
   return L;
 }
@@ -191,7 +196,8 @@ struct FfnIo {
   const int32_t* topk_idx;  // non-null: the up projection derives the dispatch
   int32_t *counts, *offsets, *perm, *inv;
   const float* topk_w;
-  void* h;                  // hidden activations [T*k][p]
+  void* h;                  // hidden activations [T*k][p] (packed rows on the GEMM path)
+  void* xp;                 // GEMM path: x rows gathered into the packed row layout
   float* down_out;          // y_acc [T][m] (combine) or y_perm [T*k][m]
   bool combine;
   float* yperm;             // grouped-GEMM path with combine: unweighted rows [T*k][m]
@@ -231,30 +237,36 @@ int run_ffn(const moe_weights* W, const FfnIo& io, hipStream_t s) {
     return MOE_OK;
   }
   if (use_gemm(W, T, k)) {
+    moe::PackArgs pk{};
+    pk.x = static_cast<const uint16_t*>(io.x);
+    pk.perm = io.perm;
+    pk.offsets = io.offsets;
+    pk.out = static_cast<uint16_t*>(io.xp);
+    pk.T = T;
+    pk.K = m;
+    pk.E = E;
+    pk.topk = k;
+    MOE_TRY_HIP(run("pack_rows", s, [&] { return moe::launch_pack_rows(pk, s); }));
     moe::GemmArgs g{};
-    g.perm = io.perm;
     g.offsets = io.offsets;
-    g.topk = k;
     g.E = E;
     g.W = E + (int)((long long)T * k / moe::gemm_rows_per_block());
-    g.topk_w = io.topk_w;
-    // up: x -> H
+    g.cg = std::max(1, env_int("MOE_GEMM_CG", 4));
+    // up: packed x -> packed H
     g.w = W->up;
-    g.act = static_cast<const uint16_t*>(io.x);
+    g.act = static_cast<const uint16_t*>(io.xp);
     g.h_out = static_cast<uint16_t*>(io.h);
     g.K = m;
     g.N = p;
-    g.gather = 1;
     const int up_epi = swiglu ? moe::EPI_UP_SWIGLU : moe::EPI_UP_RELU;
     MOE_TRY_HIP(run("gemm_up", s, [&] { return moe::launch_ffn_gemm(g, up_epi, s); }));
-    // down: H -> unweighted rows (the combine follows) or weighted atomics
+    // down: packed H -> unweighted rows in dispatch order (the combine follows)
     g.w = W->down;
     g.act = static_cast<const uint16_t*>(io.h);
     g.h_out = nullptr;
     g.f_out = io.combine ? io.yperm : io.down_out;
     g.K = p;
     g.N = m;
-    g.gather = 0;
     MOE_TRY_HIP(run("gemm_down", s, [&] { return moe::launch_ffn_gemm(g, moe::EPI_DOWN_ROWS, s); }));
     return MOE_OK;
   }
@@ -478,6 +490,7 @@ int moe_expert_ffn(const moe_weights* w, const void* x, int x_dtype, int T, int 
   io.perm = const_cast<int32_t*>(perm);
   io.offsets = const_cast<int32_t*>(offsets);
   io.h = ws + L.h;
+  io.xp = ws + L.xp;
   io.down_out = y_perm;
   io.combine = false;
   if (int rc = run_ffn(w, io, as_stream(stream))) return rc;
@@ -549,6 +562,7 @@ int moe_layer_forward(const moe_weights* w, const float* w_router, const float* 
   io.inv = inv;
   io.topk_w = tw;
   io.h = ws + L.h;
+  io.xp = ws + L.xp;
   io.down_out = yacc;
   io.combine = true;
   io.yperm = reinterpret_cast<float*>(ws + L.yperm);

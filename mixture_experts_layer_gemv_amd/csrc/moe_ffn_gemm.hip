@@ -5,22 +5,33 @@
 // roof: MoE-Lightning note, FFN roofline against batch size), so each weight
 // byte is read from HBM about once and reused from LDS and L2.
 //
-// A workgroup computes a 256-row block of one expert against a block of
-// column tiles with 2 x 4 waves (two per SIMD); each wave owns a 128 x 64
-// tile (8 x 4 fragments of v_mfma_f32_16x16x32_bf16, 128 fp32 accumulators
-// per lane).
-// Both operands stream through a 4-stage LDS ring, 32 k per stage:
-//  - the 256 activation rows (gathered through the dispatch permutation) are
-//    copied global -> LDS with global_load_lds_dwordx4 straight into MFMA
-//    A-operand order (lane l of a copy lands at base + 16 l), so every wave
-//    reads a fragment with one conflict-free 16-byte ds_read per lane;
-//  - the weight fragments are already packed in B-operand order in HBM, so a
-//    copy of 1 KiB per fragment lands them in LDS ready to read;
-//  - copies run three stages ahead of the MFMAs; a stage is consumed after a
-//    vmcnt wait for its own copies and one barrier.
-// No staging registers are needed for either operand.  Workgroups are ordered
-// so the row blocks of one (expert, column block) run together on one XCD:
-// its weight panel comes from HBM once and the other row blocks hit in L2.
+// A workgroup computes a 256-row block of one expert against a 256-column
+// block (128 hidden columns of gate and up for SwiGLU) with 2 x 4 waves, two
+// per SIMD; each wave owns a 128 x 64 tile: 8 x 4 fragments of
+// v_mfma_f32_16x16x32_bf16, 128 fp32 accumulators per lane.
+//
+// Both operands are packed in HBM as 1 KiB fragments in MFMA operand order
+// (lane l's 16 bytes at byte 16 l): the weights once at load time, the
+// activations by k_pack_rows (the rows gathered through the dispatch
+// permutation, for the up projection) or by the up projection's epilogue
+// (the hidden rows, for the down projection).  Gathering rows in place
+// instead (16 rows x 64 bytes per copy, rows a multiple of 4 KiB apart)
+// halves the copy rate.  Fragments stream through a 5-stage LDS ring of
+// 32 KiB stages (32 k each; all 160 KiB of a CU's LDS), copied global -> LDS
+// with global_load_lds_dwordx4 (lane l of a copy lands at base + 16 l): each
+// copy is one contiguous 1 KiB read, and each wave reads a fragment with one
+// conflict-free 16-byte ds_read per lane.  Every wave reads stage s+1 into a
+// second register set while the products of stage s run, so products issue
+// right after each step's barrier; four stages of copies stay in flight.
+// Workgroups run expert by expert, in groups of A.cg (4) column blocks x all
+// of the expert's row blocks, on one XCD at a time: the ~32 resident
+// workgroups then read ~8 activation tiles and ~4 weight tiles per stage,
+// the rest hits in L2.
+//
+// Measured on the Mixtral-shaped prefill layer (T = 8192), the kernel runs
+// the matrix cores about half the time: the copies, the LDS reads and the
+// barrier each cost a share, and with all three running the clock drops
+// from ~2.4 to ~2.0 GHz.
 #include "moe_index.hpp"
 #include "moe_kernels.hpp"
 
@@ -33,10 +44,19 @@ __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
 
 constexpr int kBM = 256;     // rows per workgroup
-constexpr int kWaves = 8;    // 2 wave rows x 4 wave columns
+constexpr int kWR = 2;       // wave rows
+constexpr int kWC = 4;       // wave columns
+constexpr int kWaves = kWR * kWC;  // two waves per SIMD
 constexpr int kMF = 8;       // row fragments per wave (128 rows)
-constexpr int kNF = 4;       // column fragments per wave
-constexpr int kStages = 4;   // LDS ring depth (copies run kStages-1 steps ahead)
+constexpr int kNF = 4;       // column fragments per wave (64 columns)
+constexpr int kCPW = 16 / kWaves;  // A (and B) fragments each wave copies per stage
+constexpr int kCPS = 2 * kCPW;     // copies per wave per stage
+constexpr int kStages = 5;   // LDS ring depth: 5 x 32 KiB, all of a CU's LDS
+#ifndef MOE_GEMM_REGBUF
+#define MOE_GEMM_REGBUF 1
+#endif
+// 1: every wave reads stage s+1 into a second register set during step s
+constexpr bool kRegDoubleBuffer = MOE_GEMM_REGBUF != 0;
 constexpr int kFrag = 1024;  // bytes of one 64-lane x 16-byte fragment
 
 // s_waitcnt immediate that waits until at most n vector-memory operations of
@@ -50,6 +70,51 @@ constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) |
 // free once every wave has passed; the memory clobber keeps LDS accesses on
 // their side of the barrier.
 __device__ __forceinline__ void ring_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// acc += a * b on the matrix cores, accumulating in place.  Written as
+// inline assembly because the compiler otherwise gives each product a fresh
+// destination and copies the accumulators around the loop, which doubles
+// their register footprint.  The accumulator is reused only 32 products
+// later, so consecutive products carry no dependence.
+__device__ __forceinline__ void mfma_acc(floatx4_t& acc, const bf16x8_t& a, const bf16x8_t& b) {
+  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
+}
+
+// The compiler cannot see that the assembly above is a matrix instruction,
+// so the required gaps between ordinary vector instructions and products
+// that touch the same registers are inserted here: before the first product
+// (the accumulators were just zeroed) and after the last (the epilogue reads
+// them; a 16x16x32 product needs fewer than 32 wait states).  The empty
+// statements tie every accumulator to the gap so no access moves across it.
+template <int MF, int NF>
+__device__ __forceinline__ void mfma_fence_in(floatx4_t (&acc)[MF][NF]) {
+#pragma unroll
+  for (int i = 0; i < MF; ++i)
+#pragma unroll
+    for (int j = 0; j < NF; ++j) asm volatile("" : "+v"(acc[i][j]));
+  asm volatile("s_nop 7\n\ts_nop 7" ::: "memory");
+}
+template <int MF, int NF>
+__device__ __forceinline__ void mfma_fence_out(floatx4_t (&acc)[MF][NF]) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+#pragma unroll
+  for (int i = 0; i < MF; ++i)
+#pragma unroll
+    for (int j = 0; j < NF; ++j) asm volatile("" : "+v"(acc[i][j]));
+}
+
+// Waits until at most n stages of this wave's copies (kCPS copies each) are
+// outstanding.  n is uniform; n > 3 waits as for 3.
+__device__ __forceinline__ void wait_copies(int n) {
+  if (n >= 3)
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(3 * kCPS));
+  else if (n == 2)
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * kCPS));
+  else if (n == 1)
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(kCPS));
+  else
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+}
 
 // global -> LDS copy of one fragment: lane l moves the 16 bytes at
 // sbase + voff (a uniform base and its own 32-bit offset) into LDS byte
@@ -67,58 +132,51 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
   constexpr int G = EPI == EPI_UP_SWIGLU ? 2 : 1;
   constexpr int TPW = kNF / G;  // column tiles per wave
   // stage layout: 16 A fragments (256 rows x 32 k), then 16 B fragments
-  // (4 wave columns x 4 fragments)
+  // (kWC wave columns x kNF fragments)
   __shared__ __attribute__((aligned(1024))) unsigned char ring[kStages][32 * kFrag];
-  __shared__ int rows_s[kBM];
-  __shared__ int offs_s[kMaxExperts + 1];
+  const int* const offs_s = A.offsets;  // uniform: scalar loads
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave & 1, wn = wave >> 1;  // wave row (128 rows), wave column
-  const GemmWork gw = gemm_work(xcd_logical(blockIdx.x, gridDim.x), A.W);
-  const int nblock = gw.nblock, mpair = gw.mpair;
+  const int wm = wave % kWR, wn = wave / kWR;  // wave row (128 rows), wave column
   const int NB = A.N / 16;
+  const int NBL = (NB + kWC * TPW - 1) / (kWC * TPW);  // column blocks
 
-  if (tid <= A.E) offs_s[tid] = A.offsets[tid];
-  __syncthreads();
-  int e, mb, npairs;
-  if (!skinny_pair(offs_s, A.E, kBM, mpair, &e, &mb, &npairs)) return;
-  const int tile_base = nblock * 4 * TPW;
-  if (tile_base >= NB) return;
-  const int row0 = offs_s[e] + mb * kBM;
+  int e, mb, nblock;
+  if (!gemm_item(offs_s, A.E, kBM, NBL, A.cg, xcd_logical(blockIdx.x, gridDim.x), &e, &mb, &nblock)) return;
+  const int tile_base = nblock * kWC * TPW;
+  const int row0 = offs_s[e] + mb * kBM;  // first dispatched row
   const int nrows = min(kBM, offs_s[e + 1] - row0);
-  if (tid < kBM) {
-    const int r = tid < nrows ? tid : 0;
-    rows_s[tid] = A.gather ? A.perm[row0 + r] / A.topk : row0 + r;
-  }
-  __syncthreads();
+  const int prow0 = padded_offset(offs_s, e) + mb * kBM;  // its packed row
+  const int nfrag = (nrows + 15) >> 4;  // packed fragments holding real rows
 
-  // This wave copies A fragments 2w, 2w+1 and B fragments 2w, 2w+1 of every
-  // stage.  Sources are a uniform base that advances one 32-k unit per stage
-  // plus a constant 32-bit byte offset per lane (activations and one
-  // projection's packed weights are each well under 4 GiB; checked on the
-  // host).
+  // This wave copies A fragments and B fragments kCPW w .. kCPW w + kCPW-1 of
+  // every stage.  Sources are a uniform base that advances one 32-k unit per stage
+  // plus a constant 32-bit byte offset per lane (the packed activations and
+  // one projection's packed weights are each under 4 GiB; checked on the
+  // host).  A fragments past the expert's last row re-read its last
+  // fragment; their rows are never stored.
   const int U = A.K / 32;
   const char* const abase = reinterpret_cast<const char*>(A.act);
   const char* const bbase = static_cast<const char*>(A.w);
-  uint32_t aoff[2], boff[2];
+  uint32_t aoff[kCPW], boff[kCPW];
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int f = 2 * wave + j;  // A fragment f: rows f*16 .. +15; B fragment f
-    aoff[j] = (uint32_t)gemm_a_offset(rows_s[f * 16 + (lane & 15)], A.K, lane);
+  for (int j = 0; j < kCPW; ++j) {
+    const int f = kCPW * wave + j;  // A fragment f: rows f*16 .. +15; B fragment f
+    aoff[j] = (uint32_t)gemm_a_offset((prow0 >> 4) + min(f, nfrag - 1), A.K, lane);
     boff[j] = (uint32_t)gemm_b_offset(e, NB, U, G, tile_base, kNF, f, lane);
   }
 
   // LDS byte address of the ring and of this wave's first fragment slot
   const uint32_t ring_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)ring;
-  const uint32_t wave_lds = ring_lds + (uint32_t)(2 * wave) * kFrag;
+  const uint32_t wave_lds = ring_lds + (uint32_t)(kCPW * wave) * kFrag;
 
 #define MOE_ISSUE(step)                                                                          \
   do {                                                                                           \
-    const char* ab_ = abase + (size_t)(step) * 64;                                               \
+    const char* ab_ = abase + (size_t)(step) * kFrag;                                            \
     const char* bb_ = bbase + (size_t)(step) * G * kFrag;                                        \
     const uint32_t st_ = wave_lds + (uint32_t)((step) % kStages) * (32 * kFrag);                 \
-    _Pragma("unroll") for (int j = 0; j < 2; ++j) {                                              \
+    _Pragma("unroll") for (int j = 0; j < kCPW; ++j) {                                           \
       copy_frag(ab_, aoff[j], st_ + j * kFrag);                                                  \
       copy_frag(bb_, boff[j], st_ + (16 + j) * kFrag);                                           \
     }                                                                                            \
@@ -129,53 +187,98 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
   for (int i = 0; i < kMF; ++i)
 #pragma unroll
     for (int j = 0; j < kNF; ++j) acc[i][j] = floatx4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  mfma_fence_in(acc);
 
-#define MOE_COMPUTE(step)                                                                        \
+  // The fragments of one stage, held in registers.
+  struct {
+    bf16x8_t a[kMF], b[kNF];
+  } f;
+#define MOE_LOAD_B(F, step)                                                                      \
   do {                                                                                           \
     const u32x4_t* st_ = reinterpret_cast<const u32x4_t*>(ring[(step) % kStages]);               \
-    bf16x8_t af[kMF], bfr[kNF];                                                                  \
-    _Pragma("unroll") for (int i = 0; i < kMF; ++i) af[i] = as_bf16x8(st_[(wm * kMF + i) * 64 + lane]); \
-    _Pragma("unroll") for (int j = 0; j < kNF; ++j) bfr[j] = as_bf16x8(st_[(16 + wn * kNF + j) * 64 + lane]); \
-    _Pragma("unroll") for (int i = 0; i < kMF; ++i) _Pragma("unroll") for (int j = 0; j < kNF; ++j) \
-        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);  \
+    _Pragma("unroll") for (int j = 0; j < kNF; ++j) F.b[j] = as_bf16x8(st_[(16 + wn * kNF + j) * 64 + lane]); \
   } while (0)
+#define MOE_LOAD_A(F, step, i0, i1)                                                              \
+  do {                                                                                           \
+    const u32x4_t* st_ = reinterpret_cast<const u32x4_t*>(ring[(step) % kStages]);               \
+    _Pragma("unroll") for (int i = (i0); i < (i1); ++i) F.a[i] = as_bf16x8(st_[(wm * kMF + i) * 64 + lane]); \
+  } while (0)
+#define MOE_MMA(F)                                                                               \
+  _Pragma("unroll") for (int i = 0; i < kMF; ++i) _Pragma("unroll") for (int j = 0; j < kNF; ++j) \
+      mfma_acc(acc[i][j], F.a[i], F.b[j])
 
-  // Each wave issues 4 copies per stage, kStages-1 stages ahead.  Before
-  // consuming a stage a wave waits until only the copies of later stages are
-  // outstanding (copies complete in order), then one barrier makes every
-  // wave's copies of that stage visible and frees the stage consumed last.
-  const int nsteps = U;
-  if (nsteps >= kStages - 1) {
-    MOE_ISSUE(0);
-    MOE_ISSUE(1);
-    MOE_ISSUE(2);
+  const int nsteps = U;  // >= 2: K is a multiple of 64
+  if constexpr (!kRegDoubleBuffer) {
+    // Copies run kStages-1 stages ahead.  Step s: wait until this wave's
+    // copies of stage s have landed (copies complete in order, so "at most
+    // n later stages outstanding"), one barrier (every wave's copies of s
+    // are visible; every wave has finished reading stage s-1), refill the
+    // ring slot of stage s-1 with stage s + kStages-1, read stage s (B
+    // fragments first) and multiply it row by row as its A fragments
+    // arrive.  kStages-1 stages of copies stay in flight.  The steady-state
+    // loop has no branch, so nothing makes the compiler drain the counters.
+    const int pre = nsteps < kStages - 1 ? nsteps : kStages - 1;
+    for (int s = 0; s < pre; ++s) MOE_ISSUE(s);
     int ks = 0;
     for (; ks + kStages - 1 < nsteps; ++ks) {
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(8));
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(kCPS * (kStages - 2)));
       ring_barrier();
       MOE_ISSUE(ks + kStages - 1);
-      MOE_COMPUTE(ks);
+      MOE_LOAD_B(f, ks);
+      MOE_LOAD_A(f, ks, 0, kMF);
+      MOE_MMA(f);
     }
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(8));
-    ring_barrier();
-    MOE_COMPUTE(ks);
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(4));
-    ring_barrier();
-    MOE_COMPUTE(ks + 1);
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-    ring_barrier();
-    MOE_COMPUTE(ks + 2);
+    for (; ks < nsteps; ++ks) {
+      wait_copies(nsteps - ks - 1);
+      ring_barrier();
+      MOE_LOAD_B(f, ks);
+      MOE_LOAD_A(f, ks, 0, kMF);
+      MOE_MMA(f);
+    }
   } else {
-    for (int ks = 0; ks < nsteps; ++ks) {
-      MOE_ISSUE(ks);
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-      ring_barrier();
-      MOE_COMPUTE(ks);
-      ring_barrier();
+    // Double-buffered registers: a wave enters step s holding all of stage
+    // s's fragments (read during step s-1), so its products issue right
+    // after the barrier and the LDS reads of stage s+1 overlap them.  Once
+    // every wave has read stage s into registers its ring slot is free, so
+    // step s refills it with stage s + kStages: kStages-1 stages of copies
+    // stay in flight.  Copies past the last stage re-copy the last stage
+    // into a free slot and the reads of "stage nsteps" read such a slot, so
+    // every step issues and waits for the same counts and the loop has no
+    // branch.  nsteps is even (K is a multiple of 64), so the loop runs in
+    // pairs of steps with the two register sets swapping roles.
+    struct {
+      bf16x8_t a[kMF], b[kNF];
+    } g;
+#define MOE_ISSUE_CLAMPED(step) MOE_ISSUE((step) < nsteps ? (step) : nsteps - 1)
+#pragma unroll
+    for (int s = 0; s < kStages; ++s) MOE_ISSUE_CLAMPED(s);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(kCPS * (kStages - 1)));
+    ring_barrier();
+    MOE_LOAD_B(f, 0);
+    MOE_LOAD_A(f, 0, 0, kMF);
+#define MOE_STEP_FULL(CUR, NXT)                                                                  \
+  do {                                                                                           \
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(kCPS * (kStages - 2)));                                 \
+    ring_barrier();                                                                              \
+    MOE_ISSUE_CLAMPED(ks + kStages);                                                             \
+    MOE_LOAD_B(NXT, ks + 1);                                                                     \
+    MOE_LOAD_A(NXT, ks + 1, 0, kMF);                                                             \
+    MOE_MMA(CUR);                                                                                \
+    ++ks;                                                                                        \
+  } while (0)
+    for (int ks = 0; ks < nsteps;) {
+      MOE_STEP_FULL(f, g);
+      MOE_STEP_FULL(g, f);
     }
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+#undef MOE_STEP_FULL
+#undef MOE_ISSUE_CLAMPED
   }
+  mfma_fence_out(acc);
+#undef MOE_LOAD_A
+#undef MOE_LOAD_B
+#undef MOE_MMA
 #undef MOE_ISSUE
-#undef MOE_COMPUTE
 
   // Epilogue.  Lane l of fragment (i, j) holds rows i*16 + 4*(l>>4) + q,
   // q = 0..3, of column (l & 15) of the fragment's tile.
@@ -190,39 +293,74 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
       for (int q = 0; q < 4; ++q) {
         const int row = wm * 16 * kMF + i * 16 + 4 * (lane >> 4) + q;
         if (row >= nrows) continue;
-        const int r = row0 + row;
         if constexpr (EPI == EPI_UP_SWIGLU) {
           const float gv = acc[i][t * 2][q], uv = acc[i][t * 2 + 1][q];
-          A.h_out[(size_t)r * A.N + col] = f32_to_bf16(silu(gv) * uv);
+          A.h_out[packed_index(prow0 + row, col, A.N)] = f32_to_bf16(silu(gv) * uv);
         } else if constexpr (EPI == EPI_UP_RELU) {
           const float gv = acc[i][t][q];
-          A.h_out[(size_t)r * A.N + col] = f32_to_bf16(gv > 0.0f ? gv : 0.0f);
-        } else if constexpr (EPI == EPI_DOWN_ACC) {
-          const int a = A.perm[r];
-          unsafeAtomicAdd(A.f_out + (size_t)(a / A.topk) * A.N + col, A.topk_w[a] * acc[i][t][q]);
+          A.h_out[packed_index(prow0 + row, col, A.N)] = f32_to_bf16(gv > 0.0f ? gv : 0.0f);
         } else {
-          A.f_out[(size_t)r * A.N + col] = acc[i][t][q];
+          A.f_out[(size_t)(row0 + row) * A.N + col] = acc[i][t][q];
         }
       }
     }
   }
 }
 
+// Gathers the rows of x that the dispatch permutation lists into the packed
+// fragment layout, expert by expert, each expert starting on a 16-row
+// boundary; padding rows are zero.  One wave writes one 1 KiB fragment
+// (lane l: 16 bytes of row l % 16 at k = 8 (l / 16)), fragments in packed
+// order, so the writes are contiguous.
+__global__ __launch_bounds__(256) void k_pack_rows(const PackArgs A) {
+  __shared__ int offs_s[kMaxExperts + 1];
+  __shared__ int poffs_s[kMaxExperts + 1];
+  const int tid = threadIdx.x, lane = tid & 63;
+  if (tid <= A.E) offs_s[tid] = A.offsets[tid];
+  __syncthreads();
+  if (tid <= A.E) poffs_s[tid] = padded_offset(offs_s, tid);
+  __syncthreads();
+  const int U = A.K / 32;
+  const long long frag = (long long)blockIdx.x * 4 + (tid >> 6);
+  const long long rb = frag / U;
+  const int u = (int)(frag - rb * U);
+  const long long prow = rb * 16 + (lane & 15);
+  if (prow >= poffs_s[A.E]) return;  // past the last expert's padded rows
+  int e = 0;
+  while (poffs_s[e + 1] <= prow) ++e;
+  const int local = (int)(prow - poffs_s[e]);
+  u32x4_t v = {0u, 0u, 0u, 0u};
+  if (local < offs_s[e + 1] - offs_s[e]) {
+    const int token = A.perm[offs_s[e] + local] / A.topk;
+    v = *reinterpret_cast<const u32x4_t*>(A.x + (size_t)token * A.K + u * 32 + 8 * (lane >> 4));
+  }
+  reinterpret_cast<u32x4_t*>(A.out)[frag * 64 + lane] = v;
+}
+
 }  // namespace
 
 hipError_t launch_ffn_gemm(const GemmArgs& a, int epi, hipStream_t s) {
+  if (a.K % 64 || a.N % 64 || a.K <= 0 || a.N <= 0) return hipErrorInvalidValue;  // even step count, whole tiles
   const int G = epi == EPI_UP_SWIGLU ? 2 : 1;
-  const int tiles_per_block = 4 * (kNF / G);
+  const int tiles_per_block = kWC * (kNF / G);
   const int NB = a.N / 16;
   const long long nbl = (NB + tiles_per_block - 1) / tiles_per_block;
-  const long long work = nbl * a.W;
+  const long long work = nbl * a.W;  // a.W bounds the number of row blocks
   const dim3 grid((unsigned)((work + 7) / 8 * 8));
   switch (epi) {
     case EPI_UP_SWIGLU: k_ffn_gemm<EPI_UP_SWIGLU><<<grid, kWaves * 64, 0, s>>>(a); break;
     case EPI_UP_RELU: k_ffn_gemm<EPI_UP_RELU><<<grid, kWaves * 64, 0, s>>>(a); break;
-    case EPI_DOWN_ACC: k_ffn_gemm<EPI_DOWN_ACC><<<grid, kWaves * 64, 0, s>>>(a); break;
-    default: k_ffn_gemm<EPI_DOWN_ROWS><<<grid, kWaves * 64, 0, s>>>(a); break;
+    case EPI_DOWN_ROWS: k_ffn_gemm<EPI_DOWN_ROWS><<<grid, kWaves * 64, 0, s>>>(a); break;
+    default: return hipErrorInvalidValue;
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_pack_rows(const PackArgs& a, hipStream_t s) {
+  const long long frags = packed_rows_max((long long)a.T * a.topk, a.E) / 16 * (a.K / 32);
+  const long long blocks = (frags + 3) / 4;  // one wave per fragment
+  if (blocks <= 0) return hipSuccess;
+  k_pack_rows<<<dim3((unsigned)blocks), 256, 0, s>>>(a);
   return hipGetLastError();
 }
 

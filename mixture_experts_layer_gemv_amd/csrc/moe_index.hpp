@@ -57,17 +57,32 @@ MOE_HD inline void unit_range(int part, int parts, int U, int* u0, int* u1) {
   *u1 = (int)(((long long)(part + 1) * U) / parts);
 }
 
-// Grouped GEMM.  Logical workgroup -> (column block, (expert, row block)
-// pair), pair fastest, for W pairs.
-struct GemmWork {
-  int nblock, mpair;
-};
-
-MOE_HD inline GemmWork gemm_work(int L, int W) {
-  GemmWork w;
-  w.nblock = L / W;
-  w.mpair = L - w.nblock * W;
-  return w;
+// Grouped GEMM work order.  Logical workgroup L -> (expert e, row block mb,
+// column block nblock): experts in turn; within an expert, groups of CG
+// column blocks; within a group, each row block across the group's column
+// blocks.  Consecutive logical indices run together on one XCD, so the
+// workgroups resident at once share both their activation rows and their
+// weight panels in that XCD's L2.  BM rows per row block, NBL column blocks.
+// Returns false for logical indices past the last item (grid padding).
+MOE_HD inline bool gemm_item(const int* offsets, int E, int BM, int NBL, int CG, int L, int* e, int* mb,
+                             int* nblock) {
+  int base = 0;
+  for (int i = 0; i < E; ++i) {
+    const int nrb = (offsets[i + 1] - offsets[i] + BM - 1) / BM;
+    const int work = nrb * NBL;
+    if (L < base + work) {
+      const int li = L - base;
+      const int g = li / (nrb * CG);
+      const int rem = li - g * nrb * CG;
+      const int gw = NBL - g * CG < CG ? NBL - g * CG : CG;
+      *e = i;
+      *mb = rem / gw;
+      *nblock = g * CG + (rem - *mb * gw);
+      return true;
+    }
+    base += work;
+  }
+  return false;
 }
 
 // Byte offset of the 16 bytes lane `lane` copies for B fragment `bi` of a
@@ -83,11 +98,31 @@ MOE_HD inline unsigned long long gemm_b_offset(int e, int NB, int U, int G, int 
   return ((unsigned long long)(e * NB + nb) * U * G + f % G) * 1024ull + 16ull * lane;
 }
 
-// Byte offset of lane `lane`'s 16 bytes of an A fragment whose rows start at
-// activation row `row` (bf16, K per row), at reduction unit 0 (unit u adds
-// 64 bytes).
-MOE_HD inline unsigned long long gemm_a_offset(int row, int K, int lane) {
-  return (unsigned long long)row * K * 2ull + 16ull * (lane >> 4);
+// Packed activations.  The grouped GEMM reads its activation operand from a
+// copy laid out like the packed weights: 16-row x 32-k fragments of 1 KiB
+// (lane l holds row l % 16, k = 8 (l / 16) .. +7), fragment (rb, u) at
+// (rb * K/32 + u) KiB.  Each expert's dispatched rows start on a 16-row
+// boundary: expert e's rows begin at packed row padded_offset(e), the rows
+// past its count up to that boundary are padding.
+MOE_HD inline int padded_offset(const int* offsets, int e) {
+  int s = 0;
+  for (int j = 0; j < e; ++j) s += (offsets[j + 1] - offsets[j] + 15) & ~15;
+  return s;
+}
+
+// Upper bound on packed rows for n dispatched rows over E experts.
+MOE_HD inline long long packed_rows_max(long long n, int E) { return n + 15ll * E; }
+
+// Element index of (packed row prow, column k) in a packed [rows][K] matrix.
+MOE_HD inline unsigned long long packed_index(long long prow, int k, int K) {
+  const unsigned long long frag = (unsigned long long)(prow >> 4) * (unsigned)(K >> 5) + (unsigned)(k >> 5);
+  return (frag * 64ull + (unsigned long long)((prow & 15) + 16 * ((k & 31) >> 3))) * 8ull + (unsigned)(k & 7);
+}
+
+// Byte offset of lane `lane`'s 16 bytes of packed A fragment (rb, unit 0);
+// unit u adds u KiB.
+MOE_HD inline unsigned long long gemm_a_offset(long long rb, int K, int lane) {
+  return (unsigned long long)rb * (unsigned)(K >> 5) * 1024ull + 16ull * lane;
 }
 
 }  // namespace moe

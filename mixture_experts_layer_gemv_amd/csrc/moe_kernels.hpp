@@ -102,22 +102,34 @@ hipError_t launch_ffn_skinny(const SkinnyArgs& a, int epi, bool i8, int mt, int 
 
 // ---- expert FFN, grouped GEMM (prefill-sized) path ----------------------------
 
+// Grouped GEMM over packed operands.  Activations and the hidden rows it
+// writes are in the packed row layout of moe_index.hpp (16-row x 32-k
+// fragments, each expert starting on a 16-row boundary).
 struct GemmArgs {
   const void* w;           // packed bf16 weights of this projection
-  const uint16_t* act;     // bf16 activations: x [T][K] (gather) or H [T*k][K]
-  const int32_t* perm;     // [T*k]
-  const int32_t* offsets;  // [E+1]
-  const float* topk_w;     // [T*k] (EPI_DOWN_ACC)
-  uint16_t* h_out;         // [T*k][N] bf16 (up epilogues)
-  float* f_out;            // y_acc [T][N] (EPI_DOWN_ACC) or y_perm [T*k][N] (EPI_DOWN_ROWS)
-  int K, N, E, topk;
-  int gather;              // 1: activation row = perm[r] / topk, 0: row r
+  const uint16_t* act;     // packed bf16 activations [packed rows][K]
+  const int32_t* offsets;  // [E+1] dispatch offsets
+  uint16_t* h_out;         // packed H [packed rows][N] (up epilogues)
+  float* f_out;            // y_perm [T*k][N] in dispatch order (EPI_DOWN_ROWS)
+  int cg;                  // column blocks per group of the work order (>= 1)
+  int K, N, E;
   int W;                   // upper bound on (expert, 256-row block) pairs
 };
 
-// K a multiple of 64, N a multiple of 64, bf16 weights.
+// K a multiple of 64, N a multiple of 64, bf16 weights.  epi: EPI_UP_SWIGLU,
+// EPI_UP_RELU or EPI_DOWN_ROWS.
 hipError_t launch_ffn_gemm(const GemmArgs& a, int epi, hipStream_t s);
 int gemm_rows_per_block();
+
+// Gathers x rows in dispatch order into the packed row layout.
+struct PackArgs {
+  const uint16_t* x;       // [T][K] bf16
+  const int32_t* perm;     // [T*k]
+  const int32_t* offsets;  // [E+1]
+  uint16_t* out;           // [packed_rows_max(T*k, E)][K] packed
+  int T, K, E, topk;
+};
+hipError_t launch_pack_rows(const PackArgs& a, hipStream_t s);
 
 // ---- expert FFN, fp32 path ----------------------------------------------------
 

@@ -62,57 +62,65 @@ static void check_launch(int NG, int W, int S, const std::vector<int>& offsets, 
   }
 }
 
-// Grouped GEMM launch: 256-row blocks, 2 x 4 waves of 128 x (nf fragments),
-// each wave copying A and B fragments 2w, 2w+1 of every stage.  Checks that
-// every copy stays inside its operand and its 32-bit offset, that the B
-// fragment a wave reads is the tile and half its epilogue writes, and (when
-// `cover`) that every output element is written exactly once.
-static void check_gemm(int K, int N, int G, int T, int topk, bool gather, const std::vector<int>& offsets,
-                       bool cover, std::mt19937& rng) {
-  const int BM = 256, NF = 4, TPW = NF / G;
+// Grouped GEMM launch over packed operands: 256-row blocks, 2 x 4 waves of
+// 128 x 64 (8 x 4 fragments), each wave copying A and B fragments 2w, 2w+1
+// of every stage.  Checks that every copy stays inside its operand, inside its
+// 32-bit offset and inside its own expert's packed rows; that the B fragment
+// a wave reads is the tile and half its epilogue writes; that the packed H
+// stores stay in the buffer and (when `cover`) write every output element
+// exactly once; and that the row-packing kernel's reads and writes stay in
+// bounds and fill every packed fragment of every expert.
+static void check_gemm(int K, int N, int G, int T, int topk, const std::vector<int>& offsets, bool cover,
+                       std::mt19937& rng) {
+  const int BM = 256, NF = 4, WR = 2, WC = 4, WAVES = WR * WC, CPW = 16 / WAVES, TPW = NF / G, CG = 4;
+  std::set<std::tuple<int, int, int>> items;
   const int E = (int)offsets.size() - 1;
   const int n = offsets[E];
   const int NB = N / 16, U = K / 32;
-  std::vector<int> perm(n);
-  for (int i = 0; i < n; ++i) perm[i] = i;
-  std::shuffle(perm.begin(), perm.end(), rng);
   const int W = E + n / BM;
-  const int tiles = 4 * TPW;
-  const long long work = (long long)((NB + tiles - 1) / tiles) * W;
+  const int tiles = WC * TPW;
+  const int NBL = (NB + tiles - 1) / tiles;
+  const long long work = (long long)NBL * W;
   const int nblk = (int)((work + 7) / 8 * 8);
-  const unsigned long long act_bytes = (unsigned long long)(gather ? T : n) * K * 2;
+  const long long prows = moe::packed_rows_max(n, E);
+  const unsigned long long act_bytes = (unsigned long long)prows * K * 2;
+  const unsigned long long h_elems = (unsigned long long)prows * N;
   const unsigned long long w_bytes = (unsigned long long)E * NB * U * G * 1024;
-  std::vector<unsigned char> seen(cover ? (size_t)n * (N / 16) : 0, 0);
-  int npairs_max = 0;
+  const int pend = moe::padded_offset(offsets.data(), E);
+  CHECK(pend % 16 == 0 && pend <= prows, "padded rows %d of %lld", pend, prows);
+  std::vector<unsigned char> seen(cover ? (size_t)n * NB : 0, 0);
+  std::vector<unsigned char> hwritten(cover ? (size_t)h_elems : 0, 0);
   for (int b = 0; b < nblk; ++b) {
-    const moe::GemmWork gw = moe::gemm_work(moe::xcd_logical(b, nblk), W);
-    int e, mb, npairs;
-    if (!moe::skinny_pair(offsets.data(), E, BM, gw.mpair, &e, &mb, &npairs)) continue;
-    npairs_max = std::max(npairs_max, npairs);
-    const int tile_base = gw.nblock * tiles;
-    if (tile_base >= NB) continue;
+    int e, mb, nblock;
+    if (!moe::gemm_item(offsets.data(), E, BM, NBL, CG, moe::xcd_logical(b, nblk), &e, &mb, &nblock)) continue;
+    CHECK(items.insert({e, mb, nblock}).second, "gemm item (%d,%d,%d) twice", e, mb, nblock);
+    CHECK(e >= 0 && e < E && nblock >= 0 && nblock < NBL, "gemm item e=%d nblock=%d", e, nblock);
+    const int tile_base = nblock * tiles;
     const int row0 = offsets[e] + mb * BM;
     const int nrows = std::min(BM, offsets[e + 1] - row0);
     CHECK(nrows >= 1 && row0 + nrows <= offsets[e + 1], "gemm rows [%d,+%d) e=%d", row0, nrows, e);
-    std::vector<int> rows_s(BM);
-    for (int t = 0; t < BM; ++t) {
-      const int r = t < nrows ? t : 0;
-      rows_s[t] = gather ? perm[row0 + r] / topk : row0 + r;
-    }
-    for (int wave = 0; wave < 8; ++wave)
-      for (int j = 0; j < 2; ++j) {
-        const int f = 2 * wave + j;
+    const int pe = moe::padded_offset(offsets.data(), e);
+    const int pe_end = pe + ((offsets[e + 1] - offsets[e] + 15) & ~15);
+    const int prow0 = pe + mb * BM;
+    const int nfrag = (nrows + 15) >> 4;
+    CHECK(prow0 % 16 == 0, "prow0 %d", prow0);
+    for (int wave = 0; wave < WAVES; ++wave)
+      for (int j = 0; j < CPW; ++j) {
+        const int f = CPW * wave + j;
         CHECK(16 + f < 32, "lds slot %d", 16 + f);
+        const long long rb = (prow0 >> 4) + std::min(f, nfrag - 1);
+        CHECK(rb * 16 >= pe && rb * 16 + 16 <= pe_end, "A fragment %lld outside expert %d rows [%d,%d)", rb, e, pe,
+              pe_end);
         for (int lane = 0; lane < 64; ++lane) {
-          const unsigned long long a = moe::gemm_a_offset(rows_s[f * 16 + (lane & 15)], K, lane);
-          CHECK(a < (1ull << 32) && a + (U - 1) * 64ull + 16 <= act_bytes, "A offset %llu of %llu", a, act_bytes);
+          const unsigned long long a = moe::gemm_a_offset(rb, K, lane);
+          CHECK(a < (1ull << 32) && a + (U - 1) * 1024ull + 16 <= act_bytes, "A offset %llu of %llu", a, act_bytes);
           const unsigned long long bo = moe::gemm_b_offset(e, NB, U, G, tile_base, NF, f, lane);
           CHECK(bo < (1ull << 32) && bo + (U - 1) * (unsigned long long)G * 1024 + 16 <= w_bytes,
                 "B offset %llu of %llu", bo, w_bytes);
         }
       }
-    for (int wm = 0; wm < 2; ++wm)
-      for (int wn = 0; wn < 4; ++wn)
+    for (int wm = 0; wm < WR; ++wm)
+      for (int wn = 0; wn < WC; ++wn)
         for (int t = 0; t < TPW; ++t) {
           const int nb = tile_base + wn * TPW + t;
           if (nb >= NB) continue;
@@ -121,21 +129,59 @@ static void check_gemm(int K, int N, int G, int T, int topk, bool gather, const 
             CHECK(bo == ((unsigned long long)(e * NB + nb) * U * G + g) * 1024ull, "B fragment of tile %d g=%d", nb,
                   g);
           }
-          if (!cover) continue;
           for (int i = 0; i < 8; ++i)
             for (int r16 = 0; r16 < 16; ++r16) {
               const int row = wm * 128 + i * 16 + r16;
               if (row >= nrows) continue;
-              unsigned char& c = seen[(size_t)(row0 + row) * (N / 16) + nb];
-              CHECK(c == 0, "row %d tile %d written twice", row0 + row, nb);
-              c = 1;
+              for (int c = 0; c < 16; ++c) {
+                const unsigned long long hi = moe::packed_index(prow0 + row, nb * 16 + c, N);
+                CHECK(hi < h_elems, "packed H index %llu of %llu", hi, h_elems);
+                if (cover && hi < h_elems) CHECK(hwritten[hi]++ == 0, "packed H element %llu written twice", hi);
+              }
+              if (!cover) continue;
+              unsigned char& cs = seen[(size_t)(row0 + row) * NB + nb];
+              CHECK(cs == 0, "row %d tile %d written twice", row0 + row, nb);
+              cs = 1;
             }
         }
   }
-  CHECK(npairs_max <= W, "gemm npairs %d > W %d", npairs_max, W);
+  long long nitems = 0;
+  for (int i = 0; i < E; ++i) nitems += (long long)((offsets[i + 1] - offsets[i] + BM - 1) / BM) * NBL;
+  CHECK((long long)items.size() == nitems, "gemm items %zu of %lld", items.size(), nitems);
+  CHECK(nitems <= work, "gemm items %lld > grid work %lld", nitems, work);
   if (cover)
-    for (size_t i = 0; i < seen.size(); ++i) CHECK(seen[i] == 1, "row %zu tile %zu never written", i / (N / 16),
-                                                   i % (N / 16));
+    for (size_t i = 0; i < seen.size(); ++i) CHECK(seen[i] == 1, "row %zu tile %zu never written", i / NB, i % NB);
+  // the row-packing kernel: 4 waves per block, one fragment per wave
+  if (!cover) return;
+  std::vector<int> perm(n);
+  for (int i = 0; i < n; ++i) perm[i] = (int)(rng() % std::max(1, T * topk));
+  const long long frags = prows / 16 * U;
+  const long long pblocks = (frags + 3) / 4;
+  std::vector<unsigned char> filled((size_t)(pend / 16) * U, 0);
+  std::vector<int> poffs(E + 1);
+  for (int i = 0; i <= E; ++i) poffs[i] = moe::padded_offset(offsets.data(), i);
+  for (long long blk = 0; blk < pblocks; ++blk)
+    for (int w = 0; w < 4; ++w)
+      for (int lane = 0; lane < 64; ++lane) {
+        const long long frag = blk * 4 + w;
+        const long long rb = frag / U;
+        const int u = (int)(frag - rb * U);
+        const long long prow = rb * 16 + (lane & 15);
+        if (prow >= pend) continue;
+        int e = 0;
+        while (poffs[e + 1] <= prow) ++e;
+        CHECK(e < E, "pack: row %lld has no expert", prow);
+        const int local = (int)(prow - poffs[e]);
+        if (local < offsets[e + 1] - offsets[e]) {
+          const int token = perm[offsets[e] + local] / topk;
+          const unsigned long long src = (unsigned long long)token * K + u * 32 + 8 * (lane >> 4);
+          CHECK(token < T && src + 8 <= (unsigned long long)T * K, "pack read %llu", src);
+        }
+        const unsigned long long dst = (unsigned long long)frag * 1024 + 16 * lane;
+        CHECK(dst + 16 <= act_bytes, "pack write %llu of %llu", dst, act_bytes);
+        if (lane == 0 && frag < (long long)filled.size()) filled[frag] = 1;
+      }
+  for (size_t i = 0; i < filled.size(); ++i) CHECK(filled[i], "packed fragment %zu never written", i);
 }
 
 static void check_units(int U, int parts) {
@@ -193,8 +239,8 @@ int main() {
   {
     std::vector<int> counts = {2110, 1980, 2051, 2003, 2090, 2046, 2049, 2055};
     const std::vector<int> off = offsets_from(counts);
-    check_gemm(4096, 14336, 2, 8192, 2, true, off, false, rng);
-    check_gemm(14336, 4096, 1, 8192, 2, false, off, false, rng);
+    check_gemm(4096, 14336, 2, 8192, 2, off, false, rng);
+    check_gemm(14336, 4096, 1, 8192, 2, off, false, rng);
   }
   for (int it = 0; it < 120; ++it) {
     const int E = 1 + (int)(rng() % 16);
@@ -205,9 +251,9 @@ int main() {
     std::vector<int> counts(E, 0);
     for (int a = 0; a < T * topk; ++a) counts[it % 2 ? (int)(rng() % E) : (int)(rng() % (1 + E / 3))]++;
     const std::vector<int> off = offsets_from(counts);
-    check_gemm(K, N, 2, T, topk, true, off, true, rng);
-    check_gemm(K, N, 1, T, topk, true, off, true, rng);
-    check_gemm(N, K, 1, T, topk, false, off, true, rng);
+    check_gemm(K, N, 2, T, topk, off, true, rng);
+    check_gemm(K, N, 1, T, topk, off, true, rng);
+    check_gemm(N, K, 1, T, topk, off, true, rng);
   }
   for (int U : {1, 2, 7, 50, 112, 128, 200, 448})
     for (int parts : {1, 4, 8, 16, 32}) check_units(U, parts);
