@@ -26,6 +26,13 @@ struct moe_weights {
   float* s_gate = nullptr;
   float* s_up = nullptr;
   float* s_down = nullptr;
+  // bf16 weights: a second stream on which the grouped GEMM serves the hot
+  // experts while the caller's stream runs the skinny kernels on the rest,
+  // and the events of that fork and join (guarded by mu, so concurrent calls
+  // enqueue consistent pairs)
+  hipStream_t side = nullptr;
+  hipEvent_t ev_fork = nullptr, ev_join = nullptr;
+  mutable std::mutex mu;
 };
 
 namespace {
@@ -106,28 +113,59 @@ int check_combo(int x_dtype, int w_dtype) {
   return MOE_OK;
 }
 
-// The grouped-GEMM path serves bf16 layers whose experts average at least
-// kGemmMinRows rows; smaller batches stream weights through the skinny path.
+// Which kernels serve the expert FFN.
+//  - GEMM: bf16 layers whose experts average at least kGemmMinRows rows run
+//    the grouped MFMA GEMM on every expert.
+//  - HYBRID (only when forced): experts with at least hot_rows() rows run the
+//    grouped GEMM on a second stream (weights read once for up to 256 rows),
+//    the others run the skinny kernels on the caller's stream, concurrently.
+//    On the skewed Phi-3.5-shaped layer it measured slower than the skinny
+//    path alone: each GEMM workgroup holds a whole CU for its 128-step loop
+//    and waits for skinny workgroups to drain, so it is not chosen by default.
+//  - SKINNY: decode-sized bf16 and all int8 layers.
+//  - F32: fp32 layers.
+// MOE_FFN_PATH=g|h|s forces a path where the weights allow it.
+enum class Path { F32, SKINNY, GEMM, HYBRID };
 constexpr int kGemmMinRows = 128;
 
-bool use_gemm(const moe_weights* W, int T, int k) {
+int env_int(const char* name, int dflt) {
+  const char* v = getenv(name);
+  return v && *v ? atoi(v) : dflt;
+}
+
+// Experts with at least this many rows count as hot: more than one 64-row
+// chunk of the skinny kernel.
+int hot_rows() { return std::max(1, env_int("MOE_HOT_ROWS", 65)); }
+
+// The GEMM addresses packed activations and one projection's packed weights
+// with 32-bit byte offsets from a uniform base.
+bool gemm_fits(const moe_weights* W, int T, int k) {
   if (W->w_dtype != MOE_BF16) return false;
-  // The GEMM addresses activations and one projection's packed weights with
-  // 32-bit byte offsets from a uniform base.
   const unsigned long long lim = 1ull << 32;
   const unsigned long long mp = (unsigned long long)W->m * W->p;
   const unsigned long long G = W->kind == MOE_SWIGLU ? 2 : 1;
   const unsigned long long rows = (unsigned long long)moe::packed_rows_max((long long)T * k, W->E);
-  if ((unsigned long long)W->E * mp * 2 * G >= lim || rows * W->m * 2 >= lim || rows * W->p * 2 >= lim)
-    return false;
+  return (unsigned long long)W->E * mp * 2 * G < lim && rows * W->m * 2 < lim && rows * W->p * 2 < lim;
+}
+
+Path ffn_path(const moe_weights* W, int T, int k) {
+  if (W->w_dtype == MOE_F32) return Path::F32;
+  const bool fits = gemm_fits(W, T, k) && W->side;
   const char* v = getenv("MOE_FFN_PATH");
-  if (v && *v) return v[0] == 'g';
-  return (long long)T * k >= (long long)kGemmMinRows * W->E;
+  if (v && *v) {
+    if (v[0] == 'g' && fits) return Path::GEMM;
+    if (v[0] == 'h' && fits) return Path::HYBRID;
+    return Path::SKINNY;
+  }
+  if (!fits) return Path::SKINNY;
+  const long long n = (long long)T * k;
+  if (n >= (long long)kGemmMinRows * W->E) return Path::GEMM;
+  return Path::SKINNY;
 }
 
 // Workspace carving, in the order listed.
 struct Ws {
-  size_t logits, idx, w, counts, offsets, perm, inv, h, yacc, yperm, xp, total;
+  size_t logits, idx, w, counts, offsets, perm, inv, h, yacc, yperm, xp, hp, total;
 };
 
 Ws ws_layout(const moe_weights* W, int T, int k) {
@@ -146,13 +184,16 @@ Ws ws_layout(const moe_weights* W, int T, int k) {
   L.offsets = take((size_t)(W->E + 1) * 4);
   L.perm = take(n * 4);
   L.inv = take(n * 4);
-  const bool gemm = use_gemm(W, T, k);
-  // the grouped GEMM keeps H and the gathered x in the packed row layout
-  const size_t hrows = gemm ? (size_t)moe::packed_rows_max((long long)n, W->E) : n;
-  L.h = take(hrows * (size_t)W->p * (W->w_dtype == MOE_F32 ? 4 : 2));
+  const Path path = ffn_path(W, T, k);
+  const bool gemm = path == Path::GEMM, hybrid = path == Path::HYBRID;
+  // the grouped GEMM keeps H and the gathered x in the packed row layout;
+  // the hybrid path keeps both layouts of H (skinny rows, GEMM rows)
+  const size_t prows = (size_t)moe::packed_rows_max((long long)n, W->E);
+  L.h = take((gemm ? prows : n) * (size_t)W->p * (W->w_dtype == MOE_F32 ? 4 : 2));
   L.yacc = take((size_t)T * W->m * 4);
   L.yperm = gemm ? take(n * (size_t)W->m * 4) : off;
-  L.xp = gemm ? take(hrows * (size_t)W->m * 2) : off;
+  L.xp = gemm || hybrid ? take(prows * (size_t)W->m * 2) : off;
+  L.hp = hybrid ? take(prows * (size_t)W->p * 2) : off;
   L.total = off;
   return L;
 }
@@ -162,29 +203,27 @@ int skinny_mt(int T, int k, int E) {
   return avg <= 12 ? 1 : (avg <= 24 ? 2 : 4);
 }
 
-int env_int(const char* name, int dflt) {
-  const char* v = getenv(name);
-  return v && *v ? atoi(v) : dflt;
-}
-
-// Reduction slices per down-projection work item: enough work items that
-// every CU keeps several in flight and the last round is short.
+// Reduction slices per down-projection work item.  Splitting adds fp32
+// atomics on the output; measured on the decode layers (512 to 1536 work
+// items) one slice is as fast or faster, so only very small launches split.
 int down_ksplit(long long items) {
   const int forced = env_int("MOE_DOWN_KSPLIT", 0);
   if (forced > 0) return forced;
-  if (items >= 8192) return 1;
-  if (items >= 4096) return 2;
+  if (items >= 512) return 1;
+  if (items >= 256) return 2;
   return 4;
 }
 
 // Column tiles per workgroup: enough to amortise each activation load over
 // several weight streams when the activation side is wide (several M tiles,
 // or int8 weights whose 16-byte unit spans 64 k).
+// The down projection (one stream per tile) always takes 4 (2 with four M
+// tiles, for registers); measured on the decode layers.
 int skinny_ct(int mt, bool i8, int g, const char* env) {
   const int forced = env_int(env, 0);
   if (forced > 0) return forced >= 4 ? 4 : (forced >= 2 ? 2 : 1);
   const int aw = mt * (i8 ? 2 : 1);
-  if (aw <= 1) return 1;
+  if (aw <= 1 && g > 1) return 1;
   if (mt >= 4) return 2;
   return 4;
 }
@@ -197,11 +236,124 @@ struct FfnIo {
   int32_t *counts, *offsets, *perm, *inv;
   const float* topk_w;
   void* h;                  // hidden activations [T*k][p] (packed rows on the GEMM path)
-  void* xp;                 // GEMM path: x rows gathered into the packed row layout
+  void* xp;                 // GEMM/hybrid path: x rows gathered into the packed row layout
+  void* hp;                 // hybrid path: the hot experts' H rows, packed
   float* down_out;          // y_acc [T][m] (combine) or y_perm [T*k][m]
   bool combine;
   float* yperm;             // grouped-GEMM path with combine: unweighted rows [T*k][m]
 };
+
+// Gathers x rows into the packed row layout for the grouped GEMM.
+int run_pack(const moe_weights* W, const FfnIo& io, hipStream_t s) {
+  moe::PackArgs pk{};
+  pk.x = static_cast<const uint16_t*>(io.x);
+  pk.perm = io.perm;
+  pk.offsets = io.offsets;
+  pk.out = static_cast<uint16_t*>(io.xp);
+  pk.T = io.T;
+  pk.K = W->m;
+  pk.E = W->E;
+  pk.topk = io.k;
+  MOE_TRY_HIP(run("pack_rows", s, [&] { return moe::launch_pack_rows(pk, s); }));
+  return MOE_OK;
+}
+
+// Grouped GEMM over the experts holding at least min_rows rows: packed x ->
+// packed H (hpk) -> down_out with the given down epilogue.
+int run_gemm(const moe_weights* W, const FfnIo& io, int min_rows, uint16_t* hpk, int down_epi, float* down_out,
+             hipStream_t s) {
+  const long long n = (long long)io.T * io.k;
+  moe::GemmArgs g{};
+  g.offsets = io.offsets;
+  g.perm = io.perm;
+  g.topk_w = io.topk_w;
+  g.topk = io.k;
+  g.E = W->E;
+  g.min_rows = min_rows;
+  // row blocks: at most n/256 full ones plus one partial per served expert
+  g.W = (int)(n / moe::gemm_rows_per_block() + std::min<long long>(W->E, n / min_rows));
+  g.cg = std::max(1, env_int("MOE_GEMM_CG", 4));
+  // experts averaging under one full row block: skip the products of empty
+  // row fragments
+  g.skip_empty = env_int("MOE_GEMM_SKIP", n < (long long)moe::gemm_rows_per_block() * W->E ? 1 : 0) != 0;
+  // up: packed x -> packed H
+  g.w = W->up;
+  g.act = static_cast<const uint16_t*>(io.xp);
+  g.h_out = hpk;
+  g.K = W->m;
+  g.N = W->p;
+  const int up_epi = W->kind == MOE_SWIGLU ? moe::EPI_UP_SWIGLU : moe::EPI_UP_RELU;
+  MOE_TRY_HIP(run("gemm_up", s, [&] { return moe::launch_ffn_gemm(g, up_epi, s); }));
+  // down: packed H -> rows in dispatch order, or the weighted combine
+  g.w = W->down;
+  g.act = hpk;
+  g.h_out = nullptr;
+  g.f_out = down_out;
+  g.K = W->p;
+  g.N = W->m;
+  MOE_TRY_HIP(run("gemm_down", s, [&] { return moe::launch_ffn_gemm(g, down_epi, s); }));
+  return MOE_OK;
+}
+
+// Skinny decode kernels over the experts holding at most max_rows rows (all
+// of them when max_rows <= 0).
+int run_skinny(const moe_weights* W, const FfnIo& io, int max_rows, hipStream_t s) {
+  const int m = W->m, p = W->p, E = W->E, T = io.T, k = io.k;
+  const bool swiglu = W->kind == MOE_SWIGLU;
+  const bool i8 = W->w_dtype == MOE_I8;
+  const long long avg = ((long long)T * k + E - 1) / E;
+  int mt = env_int("MOE_SKINNY_MT", avg <= 12 ? 1 : (avg <= 24 ? 2 : 4));
+  mt = mt <= 1 ? 1 : (mt == 2 ? 2 : 4);
+  const int R = moe::skinny_rows(mt);
+  moe::SkinnyArgs a{};
+  a.perm = io.perm;
+  a.offsets = io.offsets;
+  a.topk = k;
+  a.T = T;
+  a.E = E;
+  a.W = E + (int)((long long)T * k / R);
+  a.topk_w = io.topk_w;
+  a.ksplit = 1;
+  a.max_rows = max_rows;
+  if ((long long)(p / 16) * a.W * 4 >= 0x7FFFFFF0LL || (long long)(m / 16) * a.W * 4 >= 0x7FFFFFF0LL)
+    return fail(MOE_ERR_UNSUPPORTED, "too many work items for one launch (T*k=%lld)", (long long)T * k);
+  // up: gate (+up) projection with the activation epilogue, x -> H
+  a.w = W->up;
+  a.scale0 = W->s_gate;
+  a.scale1 = W->s_up;
+  a.act = static_cast<const uint16_t*>(io.x);
+  a.h_out = static_cast<uint16_t*>(io.h);
+  a.K = m;
+  a.N = p;
+  a.gather = 1;
+  if (io.topk_idx) {
+    a.topk_idx = io.topk_idx;
+    a.d_counts = io.counts;
+    a.d_offsets = io.offsets;
+    a.d_perm = io.perm;
+    a.d_inv = io.inv;
+  }
+  const int up_epi = swiglu ? moe::EPI_UP_SWIGLU : moe::EPI_UP_RELU;
+  const int up_ct = skinny_ct(mt, i8, swiglu ? 2 : 1, "MOE_UP_CT");
+  MOE_TRY_HIP(run("ffn_up", s, [&] { return moe::launch_ffn_skinny(a, up_epi, i8, mt, up_ct, s); }));
+  // down: H -> weighted combine (or unweighted rows)
+  a.topk_idx = nullptr;
+  a.d_counts = a.d_offsets = a.d_perm = a.d_inv = nullptr;
+  a.w = W->down;
+  a.scale0 = W->s_down;
+  a.scale1 = nullptr;
+  a.act = static_cast<const uint16_t*>(io.h);
+  a.h_out = nullptr;
+  a.f_out = io.down_out;
+  a.K = p;
+  a.N = m;
+  a.gather = 0;
+  if (io.combine) a.ksplit = down_ksplit((long long)moe::skinny_groups(m, skinny_ct(mt, i8, 1, "MOE_DOWN_CT")) * a.W);
+  const int dn_epi = io.combine ? moe::EPI_DOWN_ACC : moe::EPI_DOWN_ROWS;
+  const int dn_ct = skinny_ct(mt, i8, 1, "MOE_DOWN_CT");
+  MOE_TRY_HIP(run("ffn_down", s, [&] { return moe::launch_ffn_skinny(a, dn_epi, i8, mt, dn_ct, s); }));
+  return MOE_OK;
+}
 
 int run_ffn(const moe_weights* W, const FfnIo& io, hipStream_t s) {
   const int m = W->m, p = W->p, E = W->E, T = io.T, k = io.k;
@@ -236,92 +388,33 @@ int run_ffn(const moe_weights* W, const FfnIo& io, hipStream_t s) {
     MOE_TRY_HIP(run("ffn_f32_down", s, [&] { return moe::launch_ffn_f32(a, s); }));
     return MOE_OK;
   }
-  if (use_gemm(W, T, k)) {
-    moe::PackArgs pk{};
-    pk.x = static_cast<const uint16_t*>(io.x);
-    pk.perm = io.perm;
-    pk.offsets = io.offsets;
-    pk.out = static_cast<uint16_t*>(io.xp);
-    pk.T = T;
-    pk.K = m;
-    pk.E = E;
-    pk.topk = k;
-    MOE_TRY_HIP(run("pack_rows", s, [&] { return moe::launch_pack_rows(pk, s); }));
-    moe::GemmArgs g{};
-    g.offsets = io.offsets;
-    g.E = E;
-    g.W = E + (int)((long long)T * k / moe::gemm_rows_per_block());
-    g.cg = std::max(1, env_int("MOE_GEMM_CG", 4));
-    // up: packed x -> packed H
-    g.w = W->up;
-    g.act = static_cast<const uint16_t*>(io.xp);
-    g.h_out = static_cast<uint16_t*>(io.h);
-    g.K = m;
-    g.N = p;
-    const int up_epi = swiglu ? moe::EPI_UP_SWIGLU : moe::EPI_UP_RELU;
-    MOE_TRY_HIP(run("gemm_up", s, [&] { return moe::launch_ffn_gemm(g, up_epi, s); }));
-    // down: packed H -> unweighted rows in dispatch order (the combine follows)
-    g.w = W->down;
-    g.act = static_cast<const uint16_t*>(io.h);
-    g.h_out = nullptr;
-    g.f_out = io.combine ? io.yperm : io.down_out;
-    g.K = p;
-    g.N = m;
-    MOE_TRY_HIP(run("gemm_down", s, [&] { return moe::launch_ffn_gemm(g, moe::EPI_DOWN_ROWS, s); }));
-    return MOE_OK;
+  switch (ffn_path(W, T, k)) {
+    case Path::GEMM:
+      if (int rc = run_pack(W, io, s)) return rc;
+      // with the combine following: unweighted rows into y_perm
+      return run_gemm(W, io, 1, static_cast<uint16_t*>(io.h), moe::EPI_DOWN_ROWS,
+                      io.combine ? io.yperm : io.down_out, s);
+    case Path::HYBRID: {
+      if (int rc = run_pack(W, io, s)) return rc;
+      const int hot = hot_rows();
+      const int down_epi = io.combine ? moe::EPI_DOWN_ACC : moe::EPI_DOWN_ROWS;
+      std::lock_guard<std::mutex> lk(W->mu);
+      MOE_TRY_HIP(hipEventRecord(W->ev_fork, s));
+      MOE_TRY_HIP(hipStreamWaitEvent(W->side, W->ev_fork, 0));
+      const int rc_g = run_gemm(W, io, hot, static_cast<uint16_t*>(io.hp), down_epi, io.down_out, W->side);
+      const int rc_s = rc_g ? MOE_OK : run_skinny(W, io, hot - 1, s);
+      // join even after a failed launch, so the side stream never runs ahead
+      const hipError_t e1 = hipEventRecord(W->ev_join, W->side);
+      const hipError_t e2 = hipStreamWaitEvent(s, W->ev_join, 0);
+      if (rc_g) return rc_g;
+      if (rc_s) return rc_s;
+      MOE_TRY_HIP(e1);
+      MOE_TRY_HIP(e2);
+      return MOE_OK;
+    }
+    default:
+      return run_skinny(W, io, 0, s);
   }
-  const bool i8 = W->w_dtype == MOE_I8;
-  const long long avg = ((long long)T * k + E - 1) / E;
-  int mt = env_int("MOE_SKINNY_MT", avg <= 12 ? 1 : (avg <= 24 ? 2 : 4));
-  mt = mt <= 1 ? 1 : (mt == 2 ? 2 : 4);
-  const int R = moe::skinny_rows(mt);
-  moe::SkinnyArgs a{};
-  a.perm = io.perm;
-  a.offsets = io.offsets;
-  a.topk = k;
-  a.T = T;
-  a.E = E;
-  a.W = E + (int)((long long)T * k / R);
-  a.topk_w = io.topk_w;
-  a.ksplit = 1;
-  if ((long long)(p / 16) * a.W * 4 >= 0x7FFFFFF0LL || (long long)(m / 16) * a.W * 4 >= 0x7FFFFFF0LL)
-    return fail(MOE_ERR_UNSUPPORTED, "too many work items for one launch (T*k=%lld)", (long long)T * k);
-  // up: gate (+up) projection with the activation epilogue, x -> H
-  a.w = W->up;
-  a.scale0 = W->s_gate;
-  a.scale1 = W->s_up;
-  a.act = static_cast<const uint16_t*>(io.x);
-  a.h_out = static_cast<uint16_t*>(io.h);
-  a.K = m;
-  a.N = p;
-  a.gather = 1;
-  if (io.topk_idx) {
-    a.topk_idx = io.topk_idx;
-    a.d_counts = io.counts;
-    a.d_offsets = io.offsets;
-    a.d_perm = io.perm;
-    a.d_inv = io.inv;
-  }
-  const int up_epi = swiglu ? moe::EPI_UP_SWIGLU : moe::EPI_UP_RELU;
-  const int up_ct = skinny_ct(mt, i8, swiglu ? 2 : 1, "MOE_UP_CT");
-  MOE_TRY_HIP(run("ffn_up", s, [&] { return moe::launch_ffn_skinny(a, up_epi, i8, mt, up_ct, s); }));
-  // down: H -> weighted combine (or unweighted rows)
-  a.topk_idx = nullptr;
-  a.d_counts = a.d_offsets = a.d_perm = a.d_inv = nullptr;
-  a.w = W->down;
-  a.scale0 = W->s_down;
-  a.scale1 = nullptr;
-  a.act = static_cast<const uint16_t*>(io.h);
-  a.h_out = nullptr;
-  a.f_out = io.down_out;
-  a.K = p;
-  a.N = m;
-  a.gather = 0;
-  if (io.combine) a.ksplit = down_ksplit((long long)(m / 16 / skinny_ct(mt, i8, 1, "MOE_DOWN_CT")) * a.W);
-  const int dn_epi = io.combine ? moe::EPI_DOWN_ACC : moe::EPI_DOWN_ROWS;
-  const int dn_ct = skinny_ct(mt, i8, 1, "MOE_DOWN_CT");
-  MOE_TRY_HIP(run("ffn_down", s, [&] { return moe::launch_ffn_skinny(a, dn_epi, i8, mt, dn_ct, s); }));
-  return MOE_OK;
 }
 
 int check_weights_match(const moe_weights* w, int m, int p, int E) {
@@ -414,7 +507,16 @@ int moe_weights_create(int m, int p, int E, int kind, int w_dtype, const void* w
     if (e == hipSuccess) e = moe::launch_pack_bf16(static_cast<const uint16_t*>(w2), W->down, E, p, m, 1, 0, s);
   }
   if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e == hipSuccess && w_dtype == MOE_BF16) {
+    // the hybrid path's side stream (default priority) and fork/join events
+    e = hipStreamCreateWithFlags(&W->side, hipStreamNonBlocking);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&W->ev_fork, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&W->ev_join, hipEventDisableTiming);
+  }
   if (e != hipSuccess) {
+    if (W->ev_fork) (void)hipEventDestroy(W->ev_fork);
+    if (W->ev_join) (void)hipEventDestroy(W->ev_join);
+    if (W->side) (void)hipStreamDestroy(W->side);
     (void)hipFree(W->buf);
     delete W;
     return fail(MOE_ERR_HIP, "packing the weights failed: %s", hipGetErrorString(e));
@@ -425,6 +527,12 @@ int moe_weights_create(int m, int p, int E, int kind, int w_dtype, const void* w
 
 int moe_weights_destroy(moe_weights* w) {
   if (!w) return ok();
+  if (w->side) {
+    (void)hipStreamSynchronize(w->side);
+    (void)hipEventDestroy(w->ev_fork);
+    (void)hipEventDestroy(w->ev_join);
+    (void)hipStreamDestroy(w->side);
+  }
   const hipError_t e = hipFree(w->buf);
   delete w;
   if (e != hipSuccess) return fail(MOE_ERR_HIP, "hipFree failed: %s", hipGetErrorString(e));
@@ -491,6 +599,7 @@ int moe_expert_ffn(const moe_weights* w, const void* x, int x_dtype, int T, int 
   io.offsets = const_cast<int32_t*>(offsets);
   io.h = ws + L.h;
   io.xp = ws + L.xp;
+  io.hp = ws + L.hp;
   io.down_out = y_perm;
   io.combine = false;
   if (int rc = run_ffn(w, io, as_stream(stream))) return rc;
@@ -542,8 +651,9 @@ int moe_layer_forward(const moe_weights* w, const float* w_router, const float* 
   const size_t ny = (size_t)T * m;
   // decode-sized layers on the MFMA path: the up projection derives the
   // dispatch itself
-  const bool gemm = use_gemm(w, T, k);
-  const bool fused = !gemm && w->w_dtype != MOE_F32 && (long long)T * k <= moe::kFusedDispatchMax;
+  const Path path = ffn_path(w, T, k);
+  const bool gemm = path == Path::GEMM;
+  const bool fused = path == Path::SKINNY && (long long)T * k <= moe::kFusedDispatchMax;
 
   MOE_TRY_HIP(run("route_topk", s, [&] {
     return moe::launch_route_topk(x, x_dtype == MOE_BF16, w_router, b_router, T, m, E, k, false, logits, idx, tw,
@@ -563,6 +673,7 @@ int moe_layer_forward(const moe_weights* w, const float* w_router, const float* 
   io.topk_w = tw;
   io.h = ws + L.h;
   io.xp = ws + L.xp;
+  io.hp = ws + L.hp;
   io.down_out = yacc;
   io.combine = true;
   io.yperm = reinterpret_cast<float*>(ws + L.yperm);

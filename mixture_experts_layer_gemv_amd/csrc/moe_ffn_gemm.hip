@@ -126,7 +126,10 @@ __device__ __forceinline__ void copy_frag(const void* sbase, uint32_t voff, uint
   asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(lds) : "memory");
 }
 
-template <int EPI>
+// SKIP: row fragments past the row block's last real row skip their
+// products (the fragment reads still run, so the steady state keeps no branch
+// around a load); for layers whose experts hold few rows.
+template <int EPI, bool SKIP>
 __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_ffn_gemm(
     const GemmArgs A) {
   constexpr int G = EPI == EPI_UP_SWIGLU ? 2 : 1;
@@ -143,12 +146,15 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
   const int NBL = (NB + kWC * TPW - 1) / (kWC * TPW);  // column blocks
 
   int e, mb, nblock;
-  if (!gemm_item(offs_s, A.E, kBM, NBL, A.cg, xcd_logical(blockIdx.x, gridDim.x), &e, &mb, &nblock)) return;
+  if (!gemm_item(offs_s, A.E, kBM, NBL, A.cg, xcd_logical(blockIdx.x, gridDim.x), &e, &mb, &nblock, A.min_rows))
+    return;
   const int tile_base = nblock * kWC * TPW;
   const int row0 = offs_s[e] + mb * kBM;  // first dispatched row
   const int nrows = min(kBM, offs_s[e + 1] - row0);
   const int prow0 = padded_offset(offs_s, e) + mb * kBM;  // its packed row
   const int nfrag = (nrows + 15) >> 4;  // packed fragments holding real rows
+  // this wave's row fragments that hold real rows (uniform)
+  const int nf_w = __builtin_amdgcn_readfirstlane(min(max(nfrag - wm * kMF, 0), kMF));
 
   // This wave copies A fragments and B fragments kCPW w .. kCPW w + kCPW-1 of
   // every stage.  Sources are a uniform base that advances one 32-k unit per stage
@@ -204,8 +210,11 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
     _Pragma("unroll") for (int i = (i0); i < (i1); ++i) F.a[i] = as_bf16x8(st_[(wm * kMF + i) * 64 + lane]); \
   } while (0)
 #define MOE_MMA(F)                                                                               \
-  _Pragma("unroll") for (int i = 0; i < kMF; ++i) _Pragma("unroll") for (int j = 0; j < kNF; ++j) \
-      mfma_acc(acc[i][j], F.a[i], F.b[j])
+  _Pragma("unroll") for (int i = 0; i < kMF; ++i) {                                              \
+    if (!SKIP || i < nf_w) {                                                                     \
+      _Pragma("unroll") for (int j = 0; j < kNF; ++j) mfma_acc(acc[i][j], F.a[i], F.b[j]);       \
+    }                                                                                            \
+  }
 
   const int nsteps = U;  // >= 2: K is a multiple of 64
   if constexpr (!kRegDoubleBuffer) {
@@ -299,6 +308,9 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
         } else if constexpr (EPI == EPI_UP_RELU) {
           const float gv = acc[i][t][q];
           A.h_out[packed_index(prow0 + row, col, A.N)] = f32_to_bf16(gv > 0.0f ? gv : 0.0f);
+        } else if constexpr (EPI == EPI_DOWN_ACC) {
+          const int a = A.perm[row0 + row];
+          unsafeAtomicAdd(A.f_out + (size_t)(a / A.topk) * A.N + col, A.topk_w[a] * acc[i][t][q]);
         } else {
           A.f_out[(size_t)(row0 + row) * A.N + col] = acc[i][t][q];
         }
@@ -340,19 +352,29 @@ __global__ __launch_bounds__(256) void k_pack_rows(const PackArgs A) {
 }  // namespace
 
 hipError_t launch_ffn_gemm(const GemmArgs& a, int epi, hipStream_t s) {
-  if (a.K % 64 || a.N % 64 || a.K <= 0 || a.N <= 0) return hipErrorInvalidValue;  // even step count, whole tiles
+  if (a.K % 64 || a.N % 64 || a.K <= 0 || a.N <= 0 || a.min_rows < 1 || a.cg < 1)
+    return hipErrorInvalidValue;  // even step count, whole tiles
   const int G = epi == EPI_UP_SWIGLU ? 2 : 1;
   const int tiles_per_block = kWC * (kNF / G);
   const int NB = a.N / 16;
   const long long nbl = (NB + tiles_per_block - 1) / tiles_per_block;
   const long long work = nbl * a.W;  // a.W bounds the number of row blocks
+  if (work <= 0) return hipSuccess;  // no expert is served
   const dim3 grid((unsigned)((work + 7) / 8 * 8));
-  switch (epi) {
-    case EPI_UP_SWIGLU: k_ffn_gemm<EPI_UP_SWIGLU><<<grid, kWaves * 64, 0, s>>>(a); break;
-    case EPI_UP_RELU: k_ffn_gemm<EPI_UP_RELU><<<grid, kWaves * 64, 0, s>>>(a); break;
-    case EPI_DOWN_ROWS: k_ffn_gemm<EPI_DOWN_ROWS><<<grid, kWaves * 64, 0, s>>>(a); break;
-    default: return hipErrorInvalidValue;
+#define MOE_LAUNCH(SK)                                                                               \
+  switch (epi) {                                                                                     \
+    case EPI_UP_SWIGLU: k_ffn_gemm<EPI_UP_SWIGLU, SK><<<grid, kWaves * 64, 0, s>>>(a); break;           \
+    case EPI_UP_RELU: k_ffn_gemm<EPI_UP_RELU, SK><<<grid, kWaves * 64, 0, s>>>(a); break;               \
+    case EPI_DOWN_ROWS: k_ffn_gemm<EPI_DOWN_ROWS, SK><<<grid, kWaves * 64, 0, s>>>(a); break;           \
+    case EPI_DOWN_ACC: k_ffn_gemm<EPI_DOWN_ACC, SK><<<grid, kWaves * 64, 0, s>>>(a); break;             \
+    default: return hipErrorInvalidValue;                                                            \
   }
+  if (a.skip_empty) {
+    MOE_LAUNCH(true)
+  } else {
+    MOE_LAUNCH(false)
+  }
+#undef MOE_LAUNCH
   return hipGetLastError();
 }
 

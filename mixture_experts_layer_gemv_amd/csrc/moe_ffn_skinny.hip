@@ -4,15 +4,20 @@
 //
 // Design (prior art: the small-batch GEMM of the DeepSpeed-Inference summary,
 // datalearner.com, section 3 "SBI-GeMM"):
-//  - tiling along the output dimension: a workgroup owns a 16-column tile of
-//    one expert (both SwiGLU streams of it), so the reduction stays inside the
-//    workgroup (part 1 of that section).  When outputs are too few to keep
-//    every CU streaming, the reduction dimension is also split over
-//    workgroups (its two-kernel variant); here the split partials meet in the
-//    fp32 atomic combine, so no second kernel is needed;
-//  - inside the workgroup the reduction dimension is split over the waves and
-//    the partial tiles are summed through one LDS transpose, after which each
-//    thread reads its outputs' partials contiguously (part 2, with wave64);
+//  - tiling along the output dimension: each wave owns CT 16-column tiles of
+//    one expert (both SwiGLU streams of them) over the work item's whole
+//    reduction range, so no partial sums cross waves (part 1 of that
+//    section).  When outputs are too few to keep every CU streaming, the
+//    reduction dimension is split over workgroups (its two-kernel variant);
+//    the split partials meet in the fp32 atomic combine, so no second kernel
+//    is needed;
+//  - the four waves of a workgroup cover neighbouring tiles over the same
+//    reduction range, so they load the same activation fragments at about
+//    the same time and all but the first hit in the CU's L1: activation
+//    traffic to L2 is a quarter of what one wave per K-slice would cause.
+//    (The page splits the reduction over the threads of a block and sums
+//    the partials; on gfx950 the activation re-reads that layout causes
+//    bound the decode layers with several row tiles, so it is not used.)
 //  - weights are re-laid out at initialisation so a wave's load is 1 KiB of
 //    contiguous memory (part 3; see the packed layout in moe_kernels.hpp);
 //  - small-batch work is bandwidth-bound, so the activations (a few rows per
@@ -72,7 +77,6 @@ template <int MT, int G, int CT, bool I8, int EPI, int NW>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(plan(MT, G, CT, I8).wpe))) void
 k_ffn_skinny(const SkinnyArgs A) {
   constexpr int D = plan(MT, G, CT, I8).depth;
-  constexpr int NT = NW * 64;
   constexpr int R = 16 * MT;        // rows per work item
   constexpr int AH = I8 ? 2 : 1;    // activation loads per K unit
   constexpr int UK = I8 ? 64 : 32;  // k per unit
@@ -83,7 +87,6 @@ k_ffn_skinny(const SkinnyArgs A) {
   __shared__ DispatchLds<NW> DL;
   __shared__ int offs_s[kMaxExperts + 1];
   __shared__ int rows_s[R];
-  __shared__ float red[NW * CT * G * MT * 256];
 
   // Block -> logical work index: consecutive logical indices stay on one XCD
   // (blocks are dealt to the 8 XCDs round-robin), so the row chunks of one
@@ -92,7 +95,7 @@ k_ffn_skinny(const SkinnyArgs A) {
   const int NB = A.N / 16;  // a multiple of 4 (N is a multiple of 64)
   const int S = A.ksplit;
   const SkinnyWork wk = skinny_work(L, A.W, S);
-  const int ntile = wk.ngroup * CT;  // first of this group's CT column tiles
+  const int ntile = (wk.ngroup * NW + wave) * CT;  // first of this wave's CT column tiles
   const int ks = wk.ks;
   const int n_assign = A.T * A.topk;
 
@@ -107,7 +110,8 @@ k_ffn_skinny(const SkinnyArgs A) {
   // (expert, chunk) of this work item and the number of valid pairs
   int e, chunk, npairs;
   const bool has_pair = skinny_pair(offs_s, A.E, R, wk.pair, &e, &chunk, &npairs);
-  const bool valid = ntile < NB && has_pair;
+  const bool valid =
+      wk.ngroup * NW * CT < NB && has_pair && (A.max_rows <= 0 || offs_s[e + 1] - offs_s[e] <= A.max_rows);
   const int row0 = valid ? offs_s[e] + chunk * R : 0;
   const int nrows = valid ? min(R, offs_s[e + 1] - row0) : 0;
 
@@ -130,7 +134,7 @@ k_ffn_skinny(const SkinnyArgs A) {
     if (tid < nrows) rows_s[tid] = A.perm[row0 + tid];
     __syncthreads();
   }
-  if (!valid) return;
+  if (!valid || ntile >= NB) return;  // (NB is a multiple of 4, so a wave's tiles are all in or all out)
 
   // Activation row pointers of this lane, one per M tile.  Lanes past the
   // chunk's last row read a valid row (the chunk's first) so every load is
@@ -146,7 +150,7 @@ k_ffn_skinny(const SkinnyArgs A) {
 
   const int U = A.K / UK;
   int u0, u1;
-  unit_range(ks * NW + wave, S * NW, U, &u0, &u1);
+  unit_range(ks, S, U, &u0, &u1);
   // the CT column tiles of this group are consecutive streams of U*G units
   const u32x4_t* wp = static_cast<const u32x4_t*>(A.w) + (size_t)(e * NB + ntile) * U * G * 64 + lane;
   const size_t tile_stride = (size_t)U * G * 64;
@@ -226,52 +230,39 @@ k_ffn_skinny(const SkinnyArgs A) {
 #undef MOE_CONSUME
 #undef MOE_ISSUE
 
-  // Cross-wave reduction through one LDS transpose: wave w writes its partial
-  // tiles; each output's NW partials are then read by one thread.
+  // Epilogue straight from the accumulators: lane l of tile (c, g, mt) holds
+  // rows mt*16 + 4*(l>>4) + i, i = 0..3, of column (ntile + c)*16 + (l & 15).
 #pragma unroll
-  for (int c = 0; c < CT; ++c)
+  for (int c = 0; c < CT; ++c) {
+    const int col = (ntile + c) * 16 + (lane & 15);
 #pragma unroll
-    for (int g = 0; g < G; ++g)
+    for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          red[(((wave * CT + c) * G + g) * MT + mt) * 256 + i * 64 + lane] = acc[c][g][mt][i];
-  __syncthreads();
-
-  for (int o = tid; o < CT * MT * 256; o += NT) {
-    const int c = o / (MT * 256), mt = (o >> 8) % MT, i = (o >> 6) & 3, ln = o & 63;
-    const int row = mt * 16 + 4 * (ln >> 4) + i;
-    if (row >= nrows) continue;
-    const int col = (ntile + c) * 16 + (ln & 15);
-    float v[G];
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      float s = 0.0f;
-#pragma unroll
-      for (int w = 0; w < NW; ++w) s += red[(((w * CT + c) * G + g) * MT + mt) * 256 + i * 64 + ln];
-      v[g] = s;
-    }
-    const int r = row0 + row;
-    if constexpr (EPI == EPI_UP_SWIGLU) {
-      float gv = v[0], uv = v[G - 1];
-      if constexpr (I8) {
-        gv *= A.scale0[(size_t)e * A.N + col];
-        uv *= A.scale1[(size_t)e * A.N + col];
-      }
-      A.h_out[(size_t)r * A.N + col] = f32_to_bf16(silu(gv) * uv);
-    } else if constexpr (EPI == EPI_UP_RELU) {
-      float gv = v[0];
-      if constexpr (I8) gv *= A.scale0[(size_t)e * A.N + col];
-      A.h_out[(size_t)r * A.N + col] = f32_to_bf16(gv > 0.0f ? gv : 0.0f);
-    } else {
-      float o2 = v[0];
-      if constexpr (I8) o2 *= A.scale0[(size_t)e * A.N + col];
-      if constexpr (EPI == EPI_DOWN_ACC) {
-        const int a = A.perm[r];
-        unsafeAtomicAdd(A.f_out + (size_t)(a / A.topk) * A.N + col, A.topk_w[a] * o2);
-      } else {
-        A.f_out[(size_t)r * A.N + col] = o2;
+      for (int i = 0; i < 4; ++i) {
+        const int row = mt * 16 + 4 * (lane >> 4) + i;
+        if (row >= nrows) continue;
+        const int r = row0 + row;
+        if constexpr (EPI == EPI_UP_SWIGLU) {
+          float gv = acc[c][0][mt][i], uv = acc[c][G - 1][mt][i];
+          if constexpr (I8) {
+            gv *= A.scale0[(size_t)e * A.N + col];
+            uv *= A.scale1[(size_t)e * A.N + col];
+          }
+          A.h_out[(size_t)r * A.N + col] = f32_to_bf16(silu(gv) * uv);
+        } else if constexpr (EPI == EPI_UP_RELU) {
+          float gv = acc[c][0][mt][i];
+          if constexpr (I8) gv *= A.scale0[(size_t)e * A.N + col];
+          A.h_out[(size_t)r * A.N + col] = f32_to_bf16(gv > 0.0f ? gv : 0.0f);
+        } else {
+          float o2 = acc[c][0][mt][i];
+          if constexpr (I8) o2 *= A.scale0[(size_t)e * A.N + col];
+          if constexpr (EPI == EPI_DOWN_ACC) {
+            const int a = A.perm[r];
+            unsafeAtomicAdd(A.f_out + (size_t)(a / A.topk) * A.N + col, A.topk_w[a] * o2);
+          } else {
+            A.f_out[(size_t)r * A.N + col] = o2;
+          }
+        }
       }
     }
   }
@@ -279,7 +270,7 @@ k_ffn_skinny(const SkinnyArgs A) {
 
 template <int MT, int CT, bool I8>
 hipError_t launch_ct(const SkinnyArgs& a, int epi, hipStream_t s) {
-  const int NG = a.N / 16 / CT;
+  const int NG = skinny_groups(a.N, CT);
   const long long work = (long long)NG * a.W * a.ksplit;
   const long long nblk = (work + 7) / 8 * 8;
   const dim3 grid((unsigned)nblk);

@@ -32,6 +32,12 @@ MOE_HD inline SkinnyWork skinny_work(int L, int W, int S) {
   return w;
 }
 
+// Column groups of the decode FFN launch: each workgroup's 4 waves own CT
+// consecutive 16-column tiles each.  Wave w of group g owns tiles
+// (4 g + w) CT .. +CT-1; with N a multiple of 64 and CT in {1, 2, 4} a wave's
+// tiles are either all below N/16 or all past it.
+MOE_HD inline int skinny_groups(int N, int CT) { return (N / 16 + 4 * CT - 1) / (4 * CT); }
+
 // The pair-th (expert, row chunk) in expert order, chunks of R rows, given
 // dispatch offsets[0..E].  Returns false when pair is past the last chunk.
 // npairs receives the total number of chunks.
@@ -62,13 +68,16 @@ MOE_HD inline void unit_range(int part, int parts, int U, int* u0, int* u1) {
 // column blocks; within a group, each row block across the group's column
 // blocks.  Consecutive logical indices run together on one XCD, so the
 // workgroups resident at once share both their activation rows and their
-// weight panels in that XCD's L2.  BM rows per row block, NBL column blocks.
-// Returns false for logical indices past the last item (grid padding).
+// weight panels in that XCD's L2.  BM rows per row block, NBL column blocks;
+// experts with fewer than min_rows rows get no work (another kernel serves
+// them).  Returns false for logical indices past the last item (grid
+// padding).
 MOE_HD inline bool gemm_item(const int* offsets, int E, int BM, int NBL, int CG, int L, int* e, int* mb,
-                             int* nblock) {
+                             int* nblock, int min_rows = 1) {
   int base = 0;
   for (int i = 0; i < E; ++i) {
-    const int nrb = (offsets[i + 1] - offsets[i] + BM - 1) / BM;
+    const int cnt = offsets[i + 1] - offsets[i];
+    const int nrb = cnt >= min_rows ? (cnt + BM - 1) / BM : 0;
     const int work = nrb * NBL;
     if (L < base + work) {
       const int li = L - base;

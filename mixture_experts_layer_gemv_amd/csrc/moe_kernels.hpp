@@ -88,6 +88,7 @@ struct SkinnyArgs {
   int gather;              // 1: activation row = perm[r] / topk, 0: row r
   int W;                   // upper bound on (expert, row-chunk) pairs
   int ksplit;              // reduction slices per work item (EPI_DOWN_ACC only)
+  int max_rows;            // > 0: experts with more rows are skipped (another kernel serves them)
 };
 
 // Largest T*k for which the decode FFN derives the dispatch in its prologue.
@@ -110,14 +111,20 @@ struct GemmArgs {
   const uint16_t* act;     // packed bf16 activations [packed rows][K]
   const int32_t* offsets;  // [E+1] dispatch offsets
   uint16_t* h_out;         // packed H [packed rows][N] (up epilogues)
-  float* f_out;            // y_perm [T*k][N] in dispatch order (EPI_DOWN_ROWS)
+  float* f_out;            // y_perm [T*k][N] in dispatch order (EPI_DOWN_ROWS) or y_acc [T][N] (EPI_DOWN_ACC)
+  const int32_t* perm;     // [T*k] (EPI_DOWN_ACC)
+  const float* topk_w;     // [T*k] (EPI_DOWN_ACC)
+  int topk;                // (EPI_DOWN_ACC)
   int cg;                  // column blocks per group of the work order (>= 1)
+  int min_rows;            // experts with fewer rows are skipped (>= 1)
+  int skip_empty;          // 1: skip the products of row fragments past the last real row
   int K, N, E;
   int W;                   // upper bound on (expert, 256-row block) pairs
 };
 
 // K a multiple of 64, N a multiple of 64, bf16 weights.  epi: EPI_UP_SWIGLU,
-// EPI_UP_RELU or EPI_DOWN_ROWS.
+// EPI_UP_RELU, EPI_DOWN_ROWS, or EPI_DOWN_ACC (y_acc[token] += gate weight x
+// row, fp32 atomics).
 hipError_t launch_ffn_gemm(const GemmArgs& a, int epi, hipStream_t s);
 int gemm_rows_per_block();
 

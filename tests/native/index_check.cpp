@@ -71,13 +71,14 @@ static void check_launch(int NG, int W, int S, const std::vector<int>& offsets, 
 // exactly once; and that the row-packing kernel's reads and writes stay in
 // bounds and fill every packed fragment of every expert.
 static void check_gemm(int K, int N, int G, int T, int topk, const std::vector<int>& offsets, bool cover,
-                       std::mt19937& rng) {
+                       std::mt19937& rng, int min_rows = 1) {
   const int BM = 256, NF = 4, WR = 2, WC = 4, WAVES = WR * WC, CPW = 16 / WAVES, TPW = NF / G, CG = 4;
   std::set<std::tuple<int, int, int>> items;
   const int E = (int)offsets.size() - 1;
   const int n = offsets[E];
   const int NB = N / 16, U = K / 32;
-  const int W = E + n / BM;
+  // the host's bound: n/256 full row blocks plus one partial per served expert
+  const int W = n / BM + std::min(E, n / min_rows);
   const int tiles = WC * TPW;
   const int NBL = (NB + tiles - 1) / tiles;
   const long long work = (long long)NBL * W;
@@ -92,7 +93,10 @@ static void check_gemm(int K, int N, int G, int T, int topk, const std::vector<i
   std::vector<unsigned char> hwritten(cover ? (size_t)h_elems : 0, 0);
   for (int b = 0; b < nblk; ++b) {
     int e, mb, nblock;
-    if (!moe::gemm_item(offsets.data(), E, BM, NBL, CG, moe::xcd_logical(b, nblk), &e, &mb, &nblock)) continue;
+    if (!moe::gemm_item(offsets.data(), E, BM, NBL, CG, moe::xcd_logical(b, nblk), &e, &mb, &nblock, min_rows))
+      continue;
+    CHECK(offsets[e + 1] - offsets[e] >= min_rows, "expert %d with %d rows served (min %d)", e,
+          offsets[e + 1] - offsets[e], min_rows);
     CHECK(items.insert({e, mb, nblock}).second, "gemm item (%d,%d,%d) twice", e, mb, nblock);
     CHECK(e >= 0 && e < E && nblock >= 0 && nblock < NBL, "gemm item e=%d nblock=%d", e, nblock);
     const int tile_base = nblock * tiles;
@@ -146,11 +150,17 @@ static void check_gemm(int K, int N, int G, int T, int topk, const std::vector<i
         }
   }
   long long nitems = 0;
-  for (int i = 0; i < E; ++i) nitems += (long long)((offsets[i + 1] - offsets[i] + BM - 1) / BM) * NBL;
+  for (int i = 0; i < E; ++i)
+    if (offsets[i + 1] - offsets[i] >= min_rows) nitems += (long long)((offsets[i + 1] - offsets[i] + BM - 1) / BM) * NBL;
   CHECK((long long)items.size() == nitems, "gemm items %zu of %lld", items.size(), nitems);
   CHECK(nitems <= work, "gemm items %lld > grid work %lld", nitems, work);
   if (cover)
-    for (size_t i = 0; i < seen.size(); ++i) CHECK(seen[i] == 1, "row %zu tile %zu never written", i / NB, i % NB);
+    for (size_t i = 0; i < seen.size(); ++i) {
+      int ei = 0;
+      while (offsets[ei + 1] <= (int)(i / NB)) ++ei;
+      const bool served = offsets[ei + 1] - offsets[ei] >= min_rows;
+      CHECK(seen[i] == (served ? 1 : 0), "row %zu tile %zu written %d times", i / NB, i % NB, (int)seen[i]);
+    }
   // the row-packing kernel: 4 waves per block, one fragment per wave
   if (!cover) return;
   std::vector<int> perm(n);
@@ -182,6 +192,25 @@ static void check_gemm(int K, int N, int G, int T, int topk, const std::vector<i
         if (lane == 0 && frag < (long long)filled.size()) filled[frag] = 1;
       }
   for (size_t i = 0; i < filled.size(); ++i) CHECK(filled[i], "packed fragment %zu never written", i);
+}
+
+// Decode FFN column groups: every 16-column tile is owned by exactly one
+// (group, wave), and no wave owns tiles on both sides of N/16.
+static void check_skinny_tiles(int N, int CT) {
+  const int NB = N / 16, NG = moe::skinny_groups(N, CT);
+  std::vector<int> owned(NB, 0);
+  for (int g = 0; g < NG; ++g)
+    for (int w = 0; w < 4; ++w) {
+      const int t0 = (g * 4 + w) * CT;
+      int in = 0;
+      for (int c = 0; c < CT; ++c)
+        if (t0 + c < NB) {
+          ++owned[t0 + c];
+          ++in;
+        }
+      CHECK(in == 0 || in == CT, "N=%d CT=%d group %d wave %d owns %d of %d tiles", N, CT, g, w, in, CT);
+    }
+  for (int t = 0; t < NB; ++t) CHECK(owned[t] == 1, "N=%d CT=%d tile %d owned %d times", N, CT, t, owned[t]);
 }
 
 static void check_units(int U, int parts) {
@@ -218,7 +247,7 @@ int main() {
   };
   for (auto& c : cases) {
     const int W = c.E + c.n / c.R;
-    check_launch(c.N / 16 / c.CT, W, c.S, offsets_from(c.counts), c.R);
+    check_launch(moe::skinny_groups(c.N, c.CT), W, c.S, offsets_from(c.counts), c.R);
   }
   // random shapes, including empty experts and one expert holding everything
   for (int it = 0; it < 300; ++it) {
@@ -232,7 +261,7 @@ int main() {
     const int mode = it % 3;
     for (int a = 0; a < n; ++a) counts[mode == 0 ? (int)(rng() % E) : (mode == 1 ? 0 : (int)(rng() % (1 + E / 4)))]++;
     const int W = E + n / R;
-    check_launch(NB / CT, W, S, offsets_from(counts), R);
+    check_launch(moe::skinny_groups(NB * 16, CT), W, S, offsets_from(counts), R);
   }
   // grouped GEMM: the measured prefill layer (T=8192, top-2 of 8) and
   // random small shapes with ragged and empty experts
@@ -254,7 +283,12 @@ int main() {
     check_gemm(K, N, 2, T, topk, off, true, rng);
     check_gemm(K, N, 1, T, topk, off, true, rng);
     check_gemm(N, K, 1, T, topk, off, true, rng);
+    const int hot = 1 + (int)(rng() % 130);  // the hybrid split: experts with >= hot rows
+    check_gemm(K, N, 2, T, topk, off, true, rng, hot);
+    check_gemm(N, K, 1, T, topk, off, true, rng, hot);
   }
+  for (int N = 64; N <= 14336 * 2; N += 64)
+    for (int CT : {1, 2, 4}) check_skinny_tiles(N, CT);
   for (int U : {1, 2, 7, 50, 112, 128, 200, 448})
     for (int parts : {1, 4, 8, 16, 32}) check_units(U, parts);
   if (fails) {
