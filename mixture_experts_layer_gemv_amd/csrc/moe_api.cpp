@@ -163,6 +163,27 @@ Path ffn_path(const moe_weights* W, int T, int k) {
   return Path::SKINNY;
 }
 
+// M tiles (16 rows each) per work item of the skinny kernels, from the mean
+// rows per expert (MOE_SKINNY_MT overrides).
+int skinny_mt(const moe_weights* W, int T, int k) {
+  const long long avg = ((long long)T * k + W->E - 1) / W->E;
+  const int mt = env_int("MOE_SKINNY_MT", avg <= 12 ? 1 : (avg <= 24 ? 2 : 4));
+  return mt <= 1 ? 1 : (mt == 2 ? 2 : 4);
+}
+
+// With four M tiles per work item the skinny kernels read their activations
+// as packed 1 KiB fragments (x gathered by k_pack_rows, H written packed by
+// the up projection): one contiguous load per tile and K unit instead of 16
+// half-line rows, which measured as the dominant cost of the skewed layer
+// (-11 % there).  With one or two tiles the extra dispatch and packing
+// launches cost more than they save, so rows are gathered directly and the
+// dispatch stays fused into the up projection (MOE_SKINNY_PACK=0/1
+// overrides).
+bool skinny_packed(const moe_weights* W, int T, int k) {
+  if (W->w_dtype == MOE_F32) return false;
+  return env_int("MOE_SKINNY_PACK", skinny_mt(W, T, k) >= 4 ? 1 : 0) != 0;
+}
+
 // Workspace carving, in the order listed.
 struct Ws {
   size_t logits, idx, w, counts, offsets, perm, inv, h, yacc, yperm, xp, hp, total;
@@ -186,21 +207,17 @@ Ws ws_layout(const moe_weights* W, int T, int k) {
   L.inv = take(n * 4);
   const Path path = ffn_path(W, T, k);
   const bool gemm = path == Path::GEMM, hybrid = path == Path::HYBRID;
-  // the grouped GEMM keeps H and the gathered x in the packed row layout;
-  // the hybrid path keeps both layouts of H (skinny rows, GEMM rows)
+  const bool spack = (path == Path::SKINNY || hybrid) && skinny_packed(W, T, k);
+  // the grouped GEMM and the packed skinny kernels keep H and the gathered x
+  // in the packed row layout; the hybrid path keeps the GEMM's H separately
   const size_t prows = (size_t)moe::packed_rows_max((long long)n, W->E);
-  L.h = take((gemm ? prows : n) * (size_t)W->p * (W->w_dtype == MOE_F32 ? 4 : 2));
+  L.h = take((gemm || spack ? prows : n) * (size_t)W->p * (W->w_dtype == MOE_F32 ? 4 : 2));
   L.yacc = take((size_t)T * W->m * 4);
   L.yperm = gemm ? take(n * (size_t)W->m * 4) : off;
-  L.xp = gemm || hybrid ? take(prows * (size_t)W->m * 2) : off;
+  L.xp = gemm || hybrid || spack ? take(prows * (size_t)W->m * 2) : off;
   L.hp = hybrid ? take(prows * (size_t)W->p * 2) : off;
   L.total = off;
   return L;
-}
-
-int skinny_mt(int T, int k, int E) {
-  const long long avg = ((long long)T * k + E - 1) / E;
-  return avg <= 12 ? 1 : (avg <= 24 ? 2 : 4);
 }
 
 // Reduction slices per down-projection work item.  Splitting adds fp32
@@ -296,14 +313,19 @@ int run_gemm(const moe_weights* W, const FfnIo& io, int min_rows, uint16_t* hpk,
 }
 
 // Skinny decode kernels over the experts holding at most max_rows rows (all
-// of them when max_rows <= 0).
-int run_skinny(const moe_weights* W, const FfnIo& io, int max_rows, hipStream_t s) {
+// of them when max_rows <= 0).  x_packed: io.xp already holds the packed x
+// rows (the hybrid path packs once for both kernels).
+int run_skinny(const moe_weights* W, const FfnIo& io, int max_rows, hipStream_t s, bool x_packed = false) {
   const int m = W->m, p = W->p, E = W->E, T = io.T, k = io.k;
   const bool swiglu = W->kind == MOE_SWIGLU;
   const bool i8 = W->w_dtype == MOE_I8;
-  const long long avg = ((long long)T * k + E - 1) / E;
-  int mt = env_int("MOE_SKINNY_MT", avg <= 12 ? 1 : (avg <= 24 ? 2 : 4));
-  mt = mt <= 1 ? 1 : (mt == 2 ? 2 : 4);
+  const int mt = skinny_mt(W, T, k);
+  const bool packed = skinny_packed(W, T, k);
+  // waves split the reduction unless the activations are packed (measured)
+  const char* wv = getenv("MOE_SKINNY_WAVES");
+  const bool splitk = wv && *wv ? wv[0] == 'k' : !packed;
+  if (packed && !x_packed)
+    if (int rc = run_pack(W, io, s)) return rc;
   const int R = moe::skinny_rows(mt);
   moe::SkinnyArgs a{};
   a.perm = io.perm;
@@ -321,11 +343,13 @@ int run_skinny(const moe_weights* W, const FfnIo& io, int max_rows, hipStream_t 
   a.w = W->up;
   a.scale0 = W->s_gate;
   a.scale1 = W->s_up;
-  a.act = static_cast<const uint16_t*>(io.x);
+  a.act = static_cast<const uint16_t*>(packed ? io.xp : io.x);
   a.h_out = static_cast<uint16_t*>(io.h);
   a.K = m;
   a.N = p;
-  a.gather = 1;
+  a.gather = packed ? 0 : 1;
+  a.packed = packed;
+  a.h_packed = packed;
   if (io.topk_idx) {
     a.topk_idx = io.topk_idx;
     a.d_counts = io.counts;
@@ -335,7 +359,7 @@ int run_skinny(const moe_weights* W, const FfnIo& io, int max_rows, hipStream_t 
   }
   const int up_epi = swiglu ? moe::EPI_UP_SWIGLU : moe::EPI_UP_RELU;
   const int up_ct = skinny_ct(mt, i8, swiglu ? 2 : 1, "MOE_UP_CT");
-  MOE_TRY_HIP(run("ffn_up", s, [&] { return moe::launch_ffn_skinny(a, up_epi, i8, mt, up_ct, s); }));
+  MOE_TRY_HIP(run("ffn_up", s, [&] { return moe::launch_ffn_skinny(a, up_epi, i8, mt, up_ct, splitk, s); }));
   // down: H -> weighted combine (or unweighted rows)
   a.topk_idx = nullptr;
   a.d_counts = a.d_offsets = a.d_perm = a.d_inv = nullptr;
@@ -348,10 +372,15 @@ int run_skinny(const moe_weights* W, const FfnIo& io, int max_rows, hipStream_t 
   a.K = p;
   a.N = m;
   a.gather = 0;
-  if (io.combine) a.ksplit = down_ksplit((long long)moe::skinny_groups(m, skinny_ct(mt, i8, 1, "MOE_DOWN_CT")) * a.W);
+  a.packed = packed;
+  a.h_packed = 0;
+  if (io.combine) {
+    const int ct = skinny_ct(mt, i8, 1, "MOE_DOWN_CT");
+    a.ksplit = down_ksplit((long long)(splitk ? m / 16 / ct : moe::skinny_groups(m, ct)) * a.W);
+  }
   const int dn_epi = io.combine ? moe::EPI_DOWN_ACC : moe::EPI_DOWN_ROWS;
   const int dn_ct = skinny_ct(mt, i8, 1, "MOE_DOWN_CT");
-  MOE_TRY_HIP(run("ffn_down", s, [&] { return moe::launch_ffn_skinny(a, dn_epi, i8, mt, dn_ct, s); }));
+  MOE_TRY_HIP(run("ffn_down", s, [&] { return moe::launch_ffn_skinny(a, dn_epi, i8, mt, dn_ct, splitk, s); }));
   return MOE_OK;
 }
 
@@ -402,7 +431,7 @@ int run_ffn(const moe_weights* W, const FfnIo& io, hipStream_t s) {
       MOE_TRY_HIP(hipEventRecord(W->ev_fork, s));
       MOE_TRY_HIP(hipStreamWaitEvent(W->side, W->ev_fork, 0));
       const int rc_g = run_gemm(W, io, hot, static_cast<uint16_t*>(io.hp), down_epi, io.down_out, W->side);
-      const int rc_s = rc_g ? MOE_OK : run_skinny(W, io, hot - 1, s);
+      const int rc_s = rc_g ? MOE_OK : run_skinny(W, io, hot - 1, s, true);
       // join even after a failed launch, so the side stream never runs ahead
       const hipError_t e1 = hipEventRecord(W->ev_join, W->side);
       const hipError_t e2 = hipStreamWaitEvent(s, W->ev_join, 0);
@@ -653,7 +682,8 @@ int moe_layer_forward(const moe_weights* w, const float* w_router, const float* 
   // dispatch itself
   const Path path = ffn_path(w, T, k);
   const bool gemm = path == Path::GEMM;
-  const bool fused = path == Path::SKINNY && (long long)T * k <= moe::kFusedDispatchMax;
+  const bool fused =
+      path == Path::SKINNY && !skinny_packed(w, T, k) && (long long)T * k <= moe::kFusedDispatchMax;
 
   MOE_TRY_HIP(run("route_topk", s, [&] {
     return moe::launch_route_topk(x, x_dtype == MOE_BF16, w_router, b_router, T, m, E, k, false, logits, idx, tw,

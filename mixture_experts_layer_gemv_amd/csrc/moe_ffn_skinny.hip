@@ -4,20 +4,20 @@
 //
 // Design (prior art: the small-batch GEMM of the DeepSpeed-Inference summary,
 // datalearner.com, section 3 "SBI-GeMM"):
-//  - tiling along the output dimension: each wave owns CT 16-column tiles of
-//    one expert (both SwiGLU streams of them) over the work item's whole
-//    reduction range, so no partial sums cross waves (part 1 of that
-//    section).  When outputs are too few to keep every CU streaming, the
-//    reduction dimension is split over workgroups (its two-kernel variant);
-//    the split partials meet in the fp32 atomic combine, so no second kernel
-//    is needed;
-//  - the four waves of a workgroup cover neighbouring tiles over the same
-//    reduction range, so they load the same activation fragments at about
-//    the same time and all but the first hit in the CU's L1: activation
-//    traffic to L2 is a quarter of what one wave per K-slice would cause.
-//    (The page splits the reduction over the threads of a block and sums
-//    the partials; on gfx950 the activation re-reads that layout causes
-//    bound the decode layers with several row tiles, so it is not used.)
+//  - tiling along the output dimension: a workgroup owns CT 16-column tiles
+//    of one expert (both SwiGLU streams of them), so the reduction stays
+//    inside the workgroup (part 1 of that section).  When outputs are too few
+//    to keep every CU streaming, the reduction dimension is also split over
+//    workgroups (its two-kernel variant); the split partials meet in the fp32
+//    atomic combine, so no second kernel is needed;
+//  - SPLITK: the reduction is split over the workgroup's four waves and the
+//    partial tiles meet in one LDS transpose, after which each thread reads
+//    its outputs' partials contiguously (part 2, with wave64).  Otherwise each
+//    wave owns CT neighbouring tiles over the whole reduction range and the
+//    four waves load the same activation fragments at about the same time
+//    (all but the first hit in L1), with no partial sums crossing waves.
+//    Measured, the first is faster with one or two M tiles and the second
+//    with four M tiles over packed activations;
 //  - weights are re-laid out at initialisation so a wave's load is 1 KiB of
 //    contiguous memory (part 3; see the packed layout in moe_kernels.hpp);
 //  - small-batch work is bandwidth-bound, so the activations (a few rows per
@@ -73,7 +73,7 @@ constexpr Plan plan(int mt, int g, int ct, bool i8) {
   return Plan{acc, stage, 2, d256 < 2 ? 2 : (d256 < 6 ? d256 : 6)};
 }
 
-template <int MT, int G, int CT, bool I8, int EPI, int NW>
+template <int MT, int G, int CT, bool I8, int EPI, int NW, bool SPLITK>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(plan(MT, G, CT, I8).wpe))) void
 k_ffn_skinny(const SkinnyArgs A) {
   constexpr int D = plan(MT, G, CT, I8).depth;
@@ -95,7 +95,8 @@ k_ffn_skinny(const SkinnyArgs A) {
   const int NB = A.N / 16;  // a multiple of 4 (N is a multiple of 64)
   const int S = A.ksplit;
   const SkinnyWork wk = skinny_work(L, A.W, S);
-  const int ntile = (wk.ngroup * NW + wave) * CT;  // first of this wave's CT column tiles
+  // first of this wave's CT column tiles (the workgroup's, with SPLITK)
+  const int ntile = SPLITK ? wk.ngroup * CT : (wk.ngroup * NW + wave) * CT;
   const int ks = wk.ks;
   const int n_assign = A.T * A.topk;
 
@@ -110,8 +111,8 @@ k_ffn_skinny(const SkinnyArgs A) {
   // (expert, chunk) of this work item and the number of valid pairs
   int e, chunk, npairs;
   const bool has_pair = skinny_pair(offs_s, A.E, R, wk.pair, &e, &chunk, &npairs);
-  const bool valid =
-      wk.ngroup * NW * CT < NB && has_pair && (A.max_rows <= 0 || offs_s[e + 1] - offs_s[e] <= A.max_rows);
+  const bool valid = wk.ngroup * (SPLITK ? 1 : NW) * CT < NB && has_pair &&
+                     (A.max_rows <= 0 || offs_s[e + 1] - offs_s[e] <= A.max_rows);
   const int row0 = valid ? offs_s[e] + chunk * R : 0;
   const int nrows = valid ? min(R, offs_s[e + 1] - row0) : 0;
 
@@ -136,21 +137,44 @@ k_ffn_skinny(const SkinnyArgs A) {
   }
   if (!valid || ntile >= NB) return;  // (NB is a multiple of 4, so a wave's tiles are all in or all out)
 
-  // Activation row pointers of this lane, one per M tile.  Lanes past the
-  // chunk's last row read a valid row (the chunk's first) so every load is
-  // unconditional; their output rows are never stored.
+  // Activation pointers of this lane, one per M tile, and the element strides
+  // of a K unit (su) and of its second 32-k half for int8 (sh).
+  //  - packed rows (moe_index.hpp layout): the chunk's M tile mt is the 1 KiB
+  //    fragment row (prow0/16 + mt), one contiguous load per K unit; tiles
+  //    past the chunk's last real row re-read its last fragment;
+  //  - row-major rows: lane l reads 16 bytes of row (l mod 16) of the tile,
+  //    gathered through the dispatch for the up projection; lanes past the
+  //    chunk's last row read the chunk's first row.
+  // Either way every load is unconditional and the extra rows are never
+  // stored.
+  const int prow0 = A.packed || A.h_packed ? padded_offset(offs_s, e) + chunk * R : 0;
   const uint16_t* arow[MT];
+  int su, sh;
+  if (A.packed) {
+    const int nfrag = (nrows + 15) >> 4;
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    const int r = mt * 16 + (lane & 15);
-    const int rr = r < nrows ? r : 0;
-    const int src = A.gather ? rows_s[rr] / A.topk : row0 + rr;
-    arow[mt] = A.act + (size_t)src * A.K + 8 * (lane >> 4);
+    for (int mt = 0; mt < MT; ++mt)
+      arow[mt] = A.act + ((size_t)(prow0 >> 4) + min(mt, nfrag - 1)) * (A.K / 32) * 512 + 8 * lane;
+    su = AH * 512;
+    sh = 512;
+  } else {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const int r = mt * 16 + (lane & 15);
+      const int rr = r < nrows ? r : 0;
+      const int src = A.gather ? rows_s[rr] / A.topk : row0 + rr;
+      arow[mt] = A.act + (size_t)src * A.K + 8 * (lane >> 4);
+    }
+    su = UK;
+    sh = 32;
   }
 
   const int U = A.K / UK;
   int u0, u1;
-  unit_range(ks, S, U, &u0, &u1);
+  if constexpr (SPLITK)
+    unit_range(ks * NW + wave, S * NW, U, &u0, &u1);
+  else
+    unit_range(ks, S, U, &u0, &u1);
   // the CT column tiles of this group are consecutive streams of U*G units
   const u32x4_t* wp = static_cast<const u32x4_t*>(A.w) + (size_t)(e * NB + ntile) * U * G * 64 + lane;
   const size_t tile_stride = (size_t)U * G * 64;
@@ -171,7 +195,7 @@ k_ffn_skinny(const SkinnyArgs A) {
     _Pragma("unroll") for (int c = 0; c < CT; ++c) _Pragma("unroll") for (int g = 0; g < G; ++g)      \
         wb[slot][c][g] = __builtin_nontemporal_load(wp + c * tile_stride + ((size_t)(u) * G + g) * 64); \
     _Pragma("unroll") for (int mt = 0; mt < MT; ++mt) _Pragma("unroll") for (int h = 0; h < AH; ++h)   \
-        ab[slot][mt][h] = *reinterpret_cast<const u32x4_t*>(arow[mt] + (size_t)(u) * UK + 32 * h);     \
+        ab[slot][mt][h] = *reinterpret_cast<const u32x4_t*>(arow[mt] + (size_t)(u) * su + sh * h);     \
   } while (0)
 
 #define MOE_CONSUME(slot)                                                                              \
@@ -230,79 +254,121 @@ k_ffn_skinny(const SkinnyArgs A) {
 #undef MOE_CONSUME
 #undef MOE_ISSUE
 
-  // Epilogue straight from the accumulators: lane l of tile (c, g, mt) holds
-  // rows mt*16 + 4*(l>>4) + i, i = 0..3, of column (ntile + c)*16 + (l & 15).
-#pragma unroll
-  for (int c = 0; c < CT; ++c) {
-    const int col = (ntile + c) * 16 + (lane & 15);
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = mt * 16 + 4 * (lane >> 4) + i;
-        if (row >= nrows) continue;
-        const int r = row0 + row;
-        if constexpr (EPI == EPI_UP_SWIGLU) {
-          float gv = acc[c][0][mt][i], uv = acc[c][G - 1][mt][i];
-          if constexpr (I8) {
-            gv *= A.scale0[(size_t)e * A.N + col];
-            uv *= A.scale1[(size_t)e * A.N + col];
-          }
-          A.h_out[(size_t)r * A.N + col] = f32_to_bf16(silu(gv) * uv);
-        } else if constexpr (EPI == EPI_UP_RELU) {
-          float gv = acc[c][0][mt][i];
-          if constexpr (I8) gv *= A.scale0[(size_t)e * A.N + col];
-          A.h_out[(size_t)r * A.N + col] = f32_to_bf16(gv > 0.0f ? gv : 0.0f);
-        } else {
-          float o2 = acc[c][0][mt][i];
-          if constexpr (I8) o2 *= A.scale0[(size_t)e * A.N + col];
-          if constexpr (EPI == EPI_DOWN_ACC) {
-            const int a = A.perm[r];
-            unsafeAtomicAdd(A.f_out + (size_t)(a / A.topk) * A.N + col, A.topk_w[a] * o2);
-          } else {
-            A.f_out[(size_t)r * A.N + col] = o2;
-          }
-        }
+  // Stores one output element (row of the chunk, column) from its G sums.
+  auto store = [&](int row, int col, const float* v) {
+    const int r = row0 + row;
+    if constexpr (EPI == EPI_UP_SWIGLU) {
+      float gv = v[0], uv = v[G - 1];
+      if constexpr (I8) {
+        gv *= A.scale0[(size_t)e * A.N + col];
+        uv *= A.scale1[(size_t)e * A.N + col];
+      }
+      A.h_out[A.h_packed ? packed_index(prow0 + row, col, A.N) : (size_t)r * A.N + col] =
+          f32_to_bf16(silu(gv) * uv);
+    } else if constexpr (EPI == EPI_UP_RELU) {
+      float gv = v[0];
+      if constexpr (I8) gv *= A.scale0[(size_t)e * A.N + col];
+      A.h_out[A.h_packed ? packed_index(prow0 + row, col, A.N) : (size_t)r * A.N + col] =
+          f32_to_bf16(gv > 0.0f ? gv : 0.0f);
+    } else {
+      float o2 = v[0];
+      if constexpr (I8) o2 *= A.scale0[(size_t)e * A.N + col];
+      if constexpr (EPI == EPI_DOWN_ACC) {
+        const int a = A.perm[r];
+        unsafeAtomicAdd(A.f_out + (size_t)(a / A.topk) * A.N + col, A.topk_w[a] * o2);
+      } else {
+        A.f_out[(size_t)r * A.N + col] = o2;
       }
     }
+  };
+
+  // Lane l of tile (c, g, mt) holds rows mt*16 + 4*(l>>4) + i, i = 0..3, of
+  // column (ntile + c)*16 + (l & 15).
+  if constexpr (SPLITK) {
+    // Cross-wave reduction through one LDS transpose: wave w writes its
+    // partial tiles; each output's NW partials are then read by one thread.
+    __shared__ float red[NW * CT * G * MT * 256];
+#pragma unroll
+    for (int c = 0; c < CT; ++c)
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            red[(((wave * CT + c) * G + g) * MT + mt) * 256 + i * 64 + lane] = acc[c][g][mt][i];
+    __syncthreads();
+    for (int o = tid; o < CT * MT * 256; o += NW * 64) {
+      const int c = o / (MT * 256), mt = (o >> 8) % MT, i = (o >> 6) & 3, ln = o & 63;
+      const int row = mt * 16 + 4 * (ln >> 4) + i;
+      if (row >= nrows) continue;
+      float v[G];
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        float sum = 0.0f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) sum += red[(((w * CT + c) * G + g) * MT + mt) * 256 + i * 64 + ln];
+        v[g] = sum;
+      }
+      store(row, (ntile + c) * 16 + (ln & 15), v);
+    }
+  } else {
+#pragma unroll
+    for (int c = 0; c < CT; ++c)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int row = mt * 16 + 4 * (lane >> 4) + i;
+          if (row >= nrows) continue;
+          float v[G];
+#pragma unroll
+          for (int g = 0; g < G; ++g) v[g] = acc[c][g][mt][i];
+          store(row, (ntile + c) * 16 + (lane & 15), v);
+        }
   }
 }
 
-template <int MT, int CT, bool I8>
+template <int MT, int CT, bool I8, bool SPLITK>
 hipError_t launch_ct(const SkinnyArgs& a, int epi, hipStream_t s) {
-  const int NG = skinny_groups(a.N, CT);
+  const int NG = SPLITK ? a.N / 16 / CT : skinny_groups(a.N, CT);
   const long long work = (long long)NG * a.W * a.ksplit;
   const long long nblk = (work + 7) / 8 * 8;
   const dim3 grid((unsigned)nblk);
   switch (epi) {
-    case EPI_UP_SWIGLU: k_ffn_skinny<MT, 2, CT, I8, EPI_UP_SWIGLU, 4><<<grid, 256, 0, s>>>(a); break;
-    case EPI_UP_RELU: k_ffn_skinny<MT, 1, CT, I8, EPI_UP_RELU, 4><<<grid, 256, 0, s>>>(a); break;
-    case EPI_DOWN_ACC: k_ffn_skinny<MT, 1, CT, I8, EPI_DOWN_ACC, 4><<<grid, 256, 0, s>>>(a); break;
-    default: k_ffn_skinny<MT, 1, CT, I8, EPI_DOWN_ROWS, 4><<<grid, 256, 0, s>>>(a); break;
+    case EPI_UP_SWIGLU: k_ffn_skinny<MT, 2, CT, I8, EPI_UP_SWIGLU, 4, SPLITK><<<grid, 256, 0, s>>>(a); break;
+    case EPI_UP_RELU: k_ffn_skinny<MT, 1, CT, I8, EPI_UP_RELU, 4, SPLITK><<<grid, 256, 0, s>>>(a); break;
+    case EPI_DOWN_ACC: k_ffn_skinny<MT, 1, CT, I8, EPI_DOWN_ACC, 4, SPLITK><<<grid, 256, 0, s>>>(a); break;
+    default: k_ffn_skinny<MT, 1, CT, I8, EPI_DOWN_ROWS, 4, SPLITK><<<grid, 256, 0, s>>>(a); break;
   }
   return hipGetLastError();
 }
 
-template <int MT, bool I8>
+template <int MT, bool I8, bool SPLITK>
 hipError_t launch_mt(const SkinnyArgs& a, int epi, int ct, hipStream_t s) {
   if constexpr (MT < 4) {
-    if (ct >= 4) return launch_ct<MT, 4, I8>(a, epi, s);
+    if (ct >= 4) return launch_ct<MT, 4, I8, SPLITK>(a, epi, s);
   }
-  if (ct >= 2) return launch_ct<MT, 2, I8>(a, epi, s);
-  return launch_ct<MT, 1, I8>(a, epi, s);
+  if (ct >= 2) return launch_ct<MT, 2, I8, SPLITK>(a, epi, s);
+  return launch_ct<MT, 1, I8, SPLITK>(a, epi, s);
+}
+
+template <bool SPLITK>
+hipError_t launch_split(const SkinnyArgs& a, int epi, bool i8, int mt, int ct, hipStream_t s) {
+  if (i8) {
+    if (mt <= 1) return launch_mt<1, true, SPLITK>(a, epi, ct, s);
+    if (mt == 2) return launch_mt<2, true, SPLITK>(a, epi, ct, s);
+    return launch_mt<4, true, SPLITK>(a, epi, ct, s);
+  }
+  if (mt <= 1) return launch_mt<1, false, SPLITK>(a, epi, ct, s);
+  if (mt == 2) return launch_mt<2, false, SPLITK>(a, epi, ct, s);
+  return launch_mt<4, false, SPLITK>(a, epi, ct, s);
 }
 
 }  // namespace
 
-hipError_t launch_ffn_skinny(const SkinnyArgs& a, int epi, bool i8, int mt, int ct, hipStream_t s) {
-  if (i8) {
-    if (mt <= 1) return launch_mt<1, true>(a, epi, ct, s);
-    if (mt == 2) return launch_mt<2, true>(a, epi, ct, s);
-    return launch_mt<4, true>(a, epi, ct, s);
-  }
-  if (mt <= 1) return launch_mt<1, false>(a, epi, ct, s);
-  if (mt == 2) return launch_mt<2, false>(a, epi, ct, s);
-  return launch_mt<4, false>(a, epi, ct, s);
+hipError_t launch_ffn_skinny(const SkinnyArgs& a, int epi, bool i8, int mt, int ct, bool splitk, hipStream_t s) {
+  return splitk ? launch_split<true>(a, epi, i8, mt, ct, s) : launch_split<false>(a, epi, i8, mt, ct, s);
 }
 
 }  // namespace moe

@@ -89,6 +89,8 @@ struct SkinnyArgs {
   int W;                   // upper bound on (expert, row-chunk) pairs
   int ksplit;              // reduction slices per work item (EPI_DOWN_ACC only)
   int max_rows;            // > 0: experts with more rows are skipped (another kernel serves them)
+  int packed;              // 1: act is in the packed row layout (moe_index.hpp), no gather
+  int h_packed;            // 1: the up epilogue writes H in the packed row layout
 };
 
 // Largest T*k for which the decode FFN derives the dispatch in its prologue.
@@ -99,7 +101,9 @@ inline int skinny_rows(int mt) { return 16 * mt; }
 
 // mt: 16-row M tiles per work item (1, 2, 4); ct: 16-column tiles per
 // workgroup sharing each activation load (1, 2, 4).
-hipError_t launch_ffn_skinny(const SkinnyArgs& a, int epi, bool i8, int mt, int ct, hipStream_t s);
+// splitk: the four waves of a workgroup split the reduction (partials summed
+// through LDS); otherwise each wave owns its column tiles over the whole range.
+hipError_t launch_ffn_skinny(const SkinnyArgs& a, int epi, bool i8, int mt, int ct, bool splitk, hipStream_t s);
 
 // ---- expert FFN, grouped GEMM (prefill-sized) path ----------------------------
 

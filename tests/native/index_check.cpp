@@ -48,6 +48,22 @@ static void check_launch(int NG, int W, int S, const std::vector<int>& offsets, 
     const int nrows = std::min(R, offsets[e + 1] - row0);
     CHECK(nrows >= 1 && row0 >= offsets[e] && row0 + nrows <= offsets[e + 1], "rows [%d,+%d) outside expert %d",
           row0, nrows, e);
+    // packed activations: M tile mt reads fragment row prow0/16 + min(mt, nfrag-1),
+    // which must lie inside expert e's padded rows; the packed H rows written
+    // are prow0 + row for row < nrows
+    {
+      const int pe = moe::padded_offset(offsets.data(), e);
+      const int pe_end = pe + ((offsets[e + 1] - offsets[e] + 15) & ~15);
+      const int prow0 = pe + chunk * R;
+      const int nfrag = (nrows + 15) >> 4;
+      CHECK(prow0 % 16 == 0, "skinny prow0 %d", prow0);
+      for (int mt = 0; mt < R / 16; ++mt) {
+        const int rb = (prow0 >> 4) + std::min(mt, nfrag - 1);
+        CHECK(rb * 16 >= pe && rb * 16 + 16 <= pe_end, "skinny A fragment %d outside expert %d", rb, e);
+      }
+      CHECK(prow0 + nrows <= pe_end && (long long)pe_end <= moe::packed_rows_max(offsets[E], E),
+            "skinny packed rows [%d,+%d) beyond expert %d end %d", prow0, nrows, e, pe_end);
+    }
     if (w.ngroup == 0 && w.ks == 0)
       for (int r = row0; r < row0 + nrows; ++r) rows_seen[e].push_back(r);
   }
@@ -247,7 +263,8 @@ int main() {
   };
   for (auto& c : cases) {
     const int W = c.E + c.n / c.R;
-    check_launch(moe::skinny_groups(c.N, c.CT), W, c.S, offsets_from(c.counts), c.R);
+    check_launch(moe::skinny_groups(c.N, c.CT), W, c.S, offsets_from(c.counts), c.R);  // waves split columns
+    check_launch(c.N / 16 / c.CT, W, c.S, offsets_from(c.counts), c.R);                 // waves split K
   }
   // random shapes, including empty experts and one expert holding everything
   for (int it = 0; it < 300; ++it) {
@@ -262,6 +279,7 @@ int main() {
     for (int a = 0; a < n; ++a) counts[mode == 0 ? (int)(rng() % E) : (mode == 1 ? 0 : (int)(rng() % (1 + E / 4)))]++;
     const int W = E + n / R;
     check_launch(moe::skinny_groups(NB * 16, CT), W, S, offsets_from(counts), R);
+    check_launch(NB / CT, W, S, offsets_from(counts), R);
   }
   // grouped GEMM: the measured prefill layer (T=8192, top-2 of 8) and
   // random small shapes with ragged and empty experts
