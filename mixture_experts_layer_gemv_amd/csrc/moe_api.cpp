@@ -168,6 +168,7 @@ Path ffn_path(const moe_weights* W, int T, int k) {
 int skinny_mt(const moe_weights* W, int T, int k) {
   const long long avg = ((long long)T * k + W->E - 1) / W->E;
   const int mt = env_int("MOE_SKINNY_MT", avg <= 12 ? 1 : (avg <= 24 ? 2 : 4));
+  if (W->w_dtype == MOE_I8) return mt <= 1 ? 1 : 2;  // the int8 kernels stop at two M tiles
   return mt <= 1 ? 1 : (mt == 2 ? 2 : 4);
 }
 
@@ -276,9 +277,10 @@ int run_pack(const moe_weights* W, const FfnIo& io, hipStream_t s) {
 }
 
 // Grouped GEMM over the experts holding at least min_rows rows: packed x ->
-// packed H (hpk) -> down_out with the given down epilogue.
+// packed H (hpk) -> down_out with the given down epilogue, whose reduction
+// is split into down_ksplit slices (EPI_DOWN_ACC only).
 int run_gemm(const moe_weights* W, const FfnIo& io, int min_rows, uint16_t* hpk, int down_epi, float* down_out,
-             hipStream_t s) {
+             hipStream_t s, int down_ksplit = 1) {
   const long long n = (long long)io.T * io.k;
   moe::GemmArgs g{};
   g.offsets = io.offsets;
@@ -293,6 +295,7 @@ int run_gemm(const moe_weights* W, const FfnIo& io, int min_rows, uint16_t* hpk,
   // experts averaging under one full row block: skip the products of empty
   // row fragments
   g.skip_empty = env_int("MOE_GEMM_SKIP", n < (long long)moe::gemm_rows_per_block() * W->E ? 1 : 0) != 0;
+  g.ksplit = 1;
   // up: packed x -> packed H
   g.w = W->up;
   g.act = static_cast<const uint16_t*>(io.xp);
@@ -308,6 +311,7 @@ int run_gemm(const moe_weights* W, const FfnIo& io, int min_rows, uint16_t* hpk,
   g.f_out = down_out;
   g.K = W->p;
   g.N = W->m;
+  g.ksplit = down_epi == moe::EPI_DOWN_ACC ? std::max(1, std::min(down_ksplit, W->p / 64)) : 1;
   MOE_TRY_HIP(run("gemm_down", s, [&] { return moe::launch_ffn_gemm(g, down_epi, s); }));
   return MOE_OK;
 }
@@ -427,11 +431,16 @@ int run_ffn(const moe_weights* W, const FfnIo& io, hipStream_t s) {
       if (int rc = run_pack(W, io, s)) return rc;
       const int hot = hot_rows();
       const int down_epi = io.combine ? moe::EPI_DOWN_ACC : moe::EPI_DOWN_ROWS;
+      // The hot experts' GEMM goes first on the caller's stream, so its
+      // workgroups (a whole CU's LDS each) take CUs before the skinny
+      // workgroups of the side stream fill the rest; its down projection
+      // splits the reduction so its few row blocks spread over more CUs.
       std::lock_guard<std::mutex> lk(W->mu);
       MOE_TRY_HIP(hipEventRecord(W->ev_fork, s));
       MOE_TRY_HIP(hipStreamWaitEvent(W->side, W->ev_fork, 0));
-      const int rc_g = run_gemm(W, io, hot, static_cast<uint16_t*>(io.hp), down_epi, io.down_out, W->side);
-      const int rc_s = rc_g ? MOE_OK : run_skinny(W, io, hot - 1, s, true);
+      const int rc_g = run_gemm(W, io, hot, static_cast<uint16_t*>(io.hp), down_epi, io.down_out, s,
+                                env_int("MOE_GEMM_KSPLIT", 4));
+      const int rc_s = rc_g ? MOE_OK : run_skinny(W, io, hot - 1, W->side, true);
       // join even after a failed launch, so the side stream never runs ahead
       const hipError_t e1 = hipEventRecord(W->ev_join, W->side);
       const hipError_t e2 = hipStreamWaitEvent(s, W->ev_join, 0);

@@ -146,8 +146,13 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
   const int NBL = (NB + kWC * TPW - 1) / (kWC * TPW);  // column blocks
 
   int e, mb, nblock;
-  if (!gemm_item(offs_s, A.E, kBM, NBL, A.cg, xcd_logical(blockIdx.x, gridDim.x), &e, &mb, &nblock, A.min_rows))
-    return;
+  // logical index -> (reduction slice, item); slices slowest, so the
+  // workgroups resident together work on the same slice of K
+  const int Lg = xcd_logical(blockIdx.x, gridDim.x);
+  const int items = NBL * A.W;
+  const int kslice = Lg / items;
+  if (kslice >= A.ksplit) return;
+  if (!gemm_item(offs_s, A.E, kBM, NBL, A.cg, Lg - kslice * items, &e, &mb, &nblock, A.min_rows)) return;
   const int tile_base = nblock * kWC * TPW;
   const int row0 = offs_s[e] + mb * kBM;  // first dispatched row
   const int nrows = min(kBM, offs_s[e + 1] - row0);
@@ -163,8 +168,12 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
   // host).  A fragments past the expert's last row re-read its last
   // fragment; their rows are never stored.
   const int U = A.K / 32;
-  const char* const abase = reinterpret_cast<const char*>(A.act);
-  const char* const bbase = static_cast<const char*>(A.w);
+  // this slice's 32-k units: whole pairs of units, so every slice has an even
+  // number of steps
+  int p0, p1;
+  unit_range(kslice, A.ksplit, U / 2, &p0, &p1);
+  const char* const abase = reinterpret_cast<const char*>(A.act) + (size_t)(2 * p0) * kFrag;
+  const char* const bbase = static_cast<const char*>(A.w) + (size_t)(2 * p0) * G * kFrag;
   uint32_t aoff[kCPW], boff[kCPW];
 #pragma unroll
   for (int j = 0; j < kCPW; ++j) {
@@ -216,7 +225,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
     }                                                                                            \
   }
 
-  const int nsteps = U;  // >= 2: K is a multiple of 64
+  const int nsteps = 2 * (p1 - p0);  // even, >= 2 (ksplit <= K/64)
   if constexpr (!kRegDoubleBuffer) {
     // Copies run kStages-1 stages ahead.  Step s: wait until this wave's
     // copies of stage s have landed (copies complete in order, so "at most
@@ -352,13 +361,14 @@ __global__ __launch_bounds__(256) void k_pack_rows(const PackArgs A) {
 }  // namespace
 
 hipError_t launch_ffn_gemm(const GemmArgs& a, int epi, hipStream_t s) {
-  if (a.K % 64 || a.N % 64 || a.K <= 0 || a.N <= 0 || a.min_rows < 1 || a.cg < 1)
-    return hipErrorInvalidValue;  // even step count, whole tiles
+  if (a.K % 64 || a.N % 64 || a.K <= 0 || a.N <= 0 || a.min_rows < 1 || a.cg < 1 || a.ksplit < 1 ||
+      a.ksplit > a.K / 64 || (a.ksplit > 1 && epi != EPI_DOWN_ACC))
+    return hipErrorInvalidValue;  // even step count per slice, whole tiles; partial sums only into atomics
   const int G = epi == EPI_UP_SWIGLU ? 2 : 1;
   const int tiles_per_block = kWC * (kNF / G);
   const int NB = a.N / 16;
   const long long nbl = (NB + tiles_per_block - 1) / tiles_per_block;
-  const long long work = nbl * a.W;  // a.W bounds the number of row blocks
+  const long long work = nbl * a.W * a.ksplit;  // a.W bounds the number of row blocks
   if (work <= 0) return hipSuccess;  // no expert is served
   const dim3 grid((unsigned)((work + 7) / 8 * 8));
 #define MOE_LAUNCH(SK)                                                                               \

@@ -355,10 +355,9 @@ hipError_t launch_mt(const SkinnyArgs& a, int epi, int ct, hipStream_t s) {
 
 template <bool SPLITK>
 hipError_t launch_split(const SkinnyArgs& a, int epi, bool i8, int mt, int ct, hipStream_t s) {
-  if (i8) {
+  if (i8) {  // int8 stops at two M tiles: four spill registers
     if (mt <= 1) return launch_mt<1, true, SPLITK>(a, epi, ct, s);
-    if (mt == 2) return launch_mt<2, true, SPLITK>(a, epi, ct, s);
-    return launch_mt<4, true, SPLITK>(a, epi, ct, s);
+    return launch_mt<2, true, SPLITK>(a, epi, ct, s);
   }
   if (mt <= 1) return launch_mt<1, false, SPLITK>(a, epi, ct, s);
   if (mt == 2) return launch_mt<2, false, SPLITK>(a, epi, ct, s);

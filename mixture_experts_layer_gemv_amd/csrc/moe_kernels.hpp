@@ -122,6 +122,7 @@ struct GemmArgs {
   int cg;                  // column blocks per group of the work order (>= 1)
   int min_rows;            // experts with fewer rows are skipped (>= 1)
   int skip_empty;          // 1: skip the products of row fragments past the last real row
+  int ksplit;              // reduction slices per item (> 1 only with EPI_DOWN_ACC; <= K/64)
   int K, N, E;
   int W;                   // upper bound on (expert, 256-row block) pairs
 };

@@ -87,9 +87,9 @@ static void check_launch(int NG, int W, int S, const std::vector<int>& offsets, 
 // exactly once; and that the row-packing kernel's reads and writes stay in
 // bounds and fill every packed fragment of every expert.
 static void check_gemm(int K, int N, int G, int T, int topk, const std::vector<int>& offsets, bool cover,
-                       std::mt19937& rng, int min_rows = 1) {
+                       std::mt19937& rng, int min_rows = 1, int S = 1) {
   const int BM = 256, NF = 4, WR = 2, WC = 4, WAVES = WR * WC, CPW = 16 / WAVES, TPW = NF / G, CG = 4;
-  std::set<std::tuple<int, int, int>> items;
+  std::set<std::tuple<int, int, int, int>> items;
   const int E = (int)offsets.size() - 1;
   const int n = offsets[E];
   const int NB = N / 16, U = K / 32;
@@ -97,7 +97,7 @@ static void check_gemm(int K, int N, int G, int T, int topk, const std::vector<i
   const int W = n / BM + std::min(E, n / min_rows);
   const int tiles = WC * TPW;
   const int NBL = (NB + tiles - 1) / tiles;
-  const long long work = (long long)NBL * W;
+  const long long work = (long long)NBL * W * S;
   const int nblk = (int)((work + 7) / 8 * 8);
   const long long prows = moe::packed_rows_max(n, E);
   const unsigned long long act_bytes = (unsigned long long)prows * K * 2;
@@ -109,11 +109,20 @@ static void check_gemm(int K, int N, int G, int T, int topk, const std::vector<i
   std::vector<unsigned char> hwritten(cover ? (size_t)h_elems : 0, 0);
   for (int b = 0; b < nblk; ++b) {
     int e, mb, nblock;
-    if (!moe::gemm_item(offsets.data(), E, BM, NBL, CG, moe::xcd_logical(b, nblk), &e, &mb, &nblock, min_rows))
+    const int Lg = moe::xcd_logical(b, nblk);
+    const int kslice = Lg / (NBL * W);
+    if (kslice >= S) continue;
+    if (!moe::gemm_item(offsets.data(), E, BM, NBL, CG, Lg - kslice * NBL * W, &e, &mb, &nblock, min_rows))
       continue;
+    {
+      int p0, p1;
+      moe::unit_range(kslice, S, U / 2, &p0, &p1);
+      CHECK(p1 > p0 && 2 * p1 <= U, "gemm slice %d of %d: units [%d,%d) of %d", kslice, S, 2 * p0, 2 * p1, U);
+    }
     CHECK(offsets[e + 1] - offsets[e] >= min_rows, "expert %d with %d rows served (min %d)", e,
           offsets[e + 1] - offsets[e], min_rows);
-    CHECK(items.insert({e, mb, nblock}).second, "gemm item (%d,%d,%d) twice", e, mb, nblock);
+    CHECK(items.insert({kslice, e, mb, nblock}).second, "gemm item (%d,%d,%d,%d) twice", kslice, e, mb, nblock);
+    if (kslice > 0) continue;  // the rest of the checks are per item
     CHECK(e >= 0 && e < E && nblock >= 0 && nblock < NBL, "gemm item e=%d nblock=%d", e, nblock);
     const int tile_base = nblock * tiles;
     const int row0 = offsets[e] + mb * BM;
@@ -168,8 +177,8 @@ static void check_gemm(int K, int N, int G, int T, int topk, const std::vector<i
   long long nitems = 0;
   for (int i = 0; i < E; ++i)
     if (offsets[i + 1] - offsets[i] >= min_rows) nitems += (long long)((offsets[i + 1] - offsets[i] + BM - 1) / BM) * NBL;
-  CHECK((long long)items.size() == nitems, "gemm items %zu of %lld", items.size(), nitems);
-  CHECK(nitems <= work, "gemm items %lld > grid work %lld", nitems, work);
+  CHECK((long long)items.size() == nitems * S, "gemm items %zu of %lld x %d", items.size(), nitems, S);
+  CHECK(nitems * S <= work, "gemm items %lld > grid work %lld", nitems * S, work);
   if (cover)
     for (size_t i = 0; i < seen.size(); ++i) {
       int ei = 0;
@@ -304,6 +313,7 @@ int main() {
     const int hot = 1 + (int)(rng() % 130);  // the hybrid split: experts with >= hot rows
     check_gemm(K, N, 2, T, topk, off, true, rng, hot);
     check_gemm(N, K, 1, T, topk, off, true, rng, hot);
+    check_gemm(N, K, 1, T, topk, off, true, rng, hot, 1 + (int)(rng() % std::min(8, N / 64)));
   }
   for (int N = 64; N <= 14336 * 2; N += 64)
     for (int CT : {1, 2, 4}) check_skinny_tiles(N, CT);
