@@ -52,11 +52,15 @@ constexpr int kNF = 4;       // column fragments per wave (64 columns)
 constexpr int kCPW = 16 / kWaves;  // A (and B) fragments each wave copies per stage
 constexpr int kCPS = 2 * kCPW;     // copies per wave per stage
 constexpr int kStages = 5;   // LDS ring depth: 5 x 32 KiB, all of a CU's LDS
-#ifndef MOE_GEMM_REGBUF
-#define MOE_GEMM_REGBUF 1
+#ifndef MOE_GEMM_SCHED
+#define MOE_GEMM_SCHED 2
 #endif
-// 1: every wave reads stage s+1 into a second register set during step s
-constexpr bool kRegDoubleBuffer = MOE_GEMM_REGBUF != 0;
+// Main-loop schedule.  0: every wave waits for stage s, reads it and
+// multiplies it; 1: every wave reads stage s+1 into a second register set
+// during step s; 2: ping-pong, the two waves of each SIMD in opposite
+// phases (one multiplies while the other reads the next stage and issues
+// copies).
+constexpr int kSched = MOE_GEMM_SCHED;
 constexpr int kFrag = 1024;  // bytes of one 64-lane x 16-byte fragment
 
 // s_waitcnt immediate that waits until at most n vector-memory operations of
@@ -141,7 +145,10 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave % kWR, wn = wave / kWR;  // wave row (128 rows), wave column
+  // wave row (128 rows) and wave column; ping-pong makes each wave row one
+  // group of four waves, one per SIMD
+  const int wm = kSched == 2 ? wave / kWC : wave % kWR;
+  const int wn = kSched == 2 ? wave % kWC : wave / kWR;
   const int NB = A.N / 16;
   const int NBL = (NB + kWC * TPW - 1) / (kWC * TPW);  // column blocks
 
@@ -226,7 +233,58 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
   }
 
   const int nsteps = 2 * (p1 - p0);  // even, >= 2 (ksplit <= K/64)
-  if constexpr (!kRegDoubleBuffer) {
+  if constexpr (kSched == 2) {
+    // Ping-pong.  Waves 0-3 (group 0, rows 0-127) and 4-7 (group 1, rows
+    // 128-255) put one wave of each group on every SIMD.  Two barriers per
+    // step: between B1(s) and B2(s) group 0 multiplies stage s while group 1
+    // reads stage s and issues its copies of stage s+4; between B2(s) and
+    // B1(s+1) group 1 multiplies stage s while group 0 reads stage s+1 and
+    // issues its copies of stage s+5.  So the matrix cores always have one
+    // wave's products while the other wave waits for LDS and the barrier.
+    // Both groups run the same loop body [barrier, multiply, barrier, read
+    // the next stage, copy]; group 1 enters it one barrier later and group 0
+    // passes one extra barrier at the end, so the counts match.
+    // A slot is refilled only after the barrier that follows both groups'
+    // reads of it.  Before the barrier ahead of a stage's first read (B2(s-1)
+    // for stage s) every wave's copies of it have landed: group 0 then has
+    // stages up to s+3 issued, group 1 up to s+3, so at most 12 copies may
+    // stay outstanding; group 0's wait before B1(s) (16) and group 1's before
+    // B1(s+1) (12) only keep the loop body the same.
+    const bool g0 = wave < kWC;
+#define MOE_ISSUE_CLAMPED(step) MOE_ISSUE((step) < nsteps ? (step) : nsteps - 1)
+#pragma unroll
+    for (int s = 0; s < kStages - 1; ++s) MOE_ISSUE_CLAMPED(s);
+    if (g0) {
+      MOE_ISSUE_CLAMPED(kStages - 1);
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(kCPS * (kStages - 1)));
+      ring_barrier();  // B0
+    } else {
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(kCPS * (kStages - 2)));
+      ring_barrier();  // B0
+      ring_barrier();  // B1(0)
+    }
+    MOE_LOAD_B(f, 0);
+    MOE_LOAD_A(f, 0, 0, kMF);
+    if (!g0) MOE_ISSUE_CLAMPED(kStages - 1);
+    for (int ks = 0; ks < nsteps; ++ks) {
+      if (g0)
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(kCPS * (kStages - 1)));
+      else
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(kCPS * (kStages - 2)));
+      ring_barrier();  // group 0: B1(ks); group 1: B2(ks)
+      asm volatile("s_setprio 1");
+      MOE_MMA(f);
+      asm volatile("s_setprio 0");
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(kCPS * (kStages - 2)));
+      ring_barrier();  // group 0: B2(ks); group 1: B1(ks+1)
+      MOE_LOAD_B(f, ks + 1);
+      MOE_LOAD_A(f, ks + 1, 0, kMF);
+      MOE_ISSUE_CLAMPED(ks + kStages);
+    }
+    if (g0) ring_barrier();
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+#undef MOE_ISSUE_CLAMPED
+  } else if constexpr (kSched == 0) {
     // Copies run kStages-1 stages ahead.  Step s: wait until this wave's
     // copies of stage s have landed (copies complete in order, so "at most
     // n later stages outstanding"), one barrier (every wave's copies of s
