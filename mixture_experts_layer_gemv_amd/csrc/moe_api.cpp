@@ -354,6 +354,10 @@ int run_skinny(const moe_weights* W, const FfnIo& io, int max_rows, hipStream_t 
   a.gather = packed ? 0 : 1;
   a.packed = packed;
   a.h_packed = packed;
+  // packed rows with the columns split over the waves: every wave of a
+  // workgroup reads the same activation fragments, so they are copied into
+  // LDS once per workgroup (MOE_SKINNY_SA=0 turns this off)
+  a.shared_act = packed && !splitk && env_int("MOE_SKINNY_SA", 1) != 0;
   if (io.topk_idx) {
     a.topk_idx = io.topk_idx;
     a.d_counts = io.counts;

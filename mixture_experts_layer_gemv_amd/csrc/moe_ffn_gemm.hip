@@ -33,6 +33,7 @@
 // barrier each cost a share, and with all three running the clock drops
 // from ~2.4 to ~2.0 GHz.
 #include "moe_index.hpp"
+#include "moe_lds.hpp"
 #include "moe_kernels.hpp"
 
 namespace moe {
@@ -62,18 +63,6 @@ constexpr int kStages = 5;   // LDS ring depth: 5 x 32 KiB, all of a CU's LDS
 // copies).
 constexpr int kSched = MOE_GEMM_SCHED;
 constexpr int kFrag = 1024;  // bytes of one 64-lane x 16-byte fragment
-
-// s_waitcnt immediate that waits until at most n vector-memory operations of
-// this wave are outstanding (expcnt and lgkmcnt left unconstrained).
-constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
-
-// Workgroup barrier without the release/acquire fences of __syncthreads():
-// those would wait for every outstanding copy (vmcnt(0)) and collapse the
-// ring; the stage being consumed is waited for explicitly with vmcnt_imm.
-// The wave's own LDS reads finish first (lgkmcnt(0)), so a stage it read is
-// free once every wave has passed; the memory clobber keeps LDS accesses on
-// their side of the barrier.
-__device__ __forceinline__ void ring_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // acc += a * b on the matrix cores, accumulating in place.  Written as
 // inline assembly because the compiler otherwise gives each product a fresh
@@ -118,16 +107,6 @@ __device__ __forceinline__ void wait_copies(int n) {
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(kCPS));
   else
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-}
-
-// global -> LDS copy of one fragment: lane l moves the 16 bytes at
-// sbase + voff (a uniform base and its own 32-bit offset) into LDS byte
-// address lds + 16 l.  Issued as inline assembly so the compiler does not
-// add its own conservative wait for the copy before unrelated LDS reads; the
-// ring's explicit vmcnt waits and barriers order the accesses instead.
-__device__ __forceinline__ void copy_frag(const void* sbase, uint32_t voff, uint32_t lds) {
-  // m0 is set right here; nothing else in these kernels keeps a value in m0
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(lds) : "memory");
 }
 
 // SKIP: row fragments past the row block's last real row skip their
@@ -190,7 +169,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
   }
 
   // LDS byte address of the ring and of this wave's first fragment slot
-  const uint32_t ring_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)ring;
+  const uint32_t ring_lds = lds_address(ring);
   const uint32_t wave_lds = ring_lds + (uint32_t)(kCPW * wave) * kFrag;
 
 #define MOE_ISSUE(step)                                                                          \

@@ -29,6 +29,7 @@
 // separate dispatch launch is needed.
 #include "moe_dispatch_block.hpp"
 #include "moe_index.hpp"
+#include "moe_lds.hpp"
 #include "moe_kernels.hpp"
 
 namespace moe {
@@ -37,6 +38,15 @@ namespace {
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v); }
+
+// 16-byte load through a pointer the caller knows is in global memory.  The
+// activation pointers pass through a per-tile array and a select, so the
+// compiler cannot always infer their address space; a flat load then counts
+// on both the vector-memory and the LDS counters and may complete out of
+// order, which turns every wait on it into a full drain of the pipeline.
+__device__ __forceinline__ u32x4_t load_global16(const uint16_t* p) {
+  return *(const __attribute__((address_space(1))) u32x4_t*)p;
+}
 
 // 8 signed bytes (two dwords) -> 8 bf16.  |q| <= 128 is exact in bf16, so the
 // fp32 value's upper half is the bf16 pattern.
@@ -57,32 +67,61 @@ __device__ __forceinline__ bf16x8_t i8x8_to_bf16(uint32_t lo, uint32_t hi) {
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
 
+// Waits until at most n units of STEP vector-memory operations each are
+// outstanding; n is uniform, 0 <= n <= N.
+template <int STEP, int N>
+__device__ __forceinline__ void wait_units(int n) {
+  if constexpr (N <= 0) {
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  } else {
+    if (n >= N)
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(N * STEP));
+    else
+      wait_units<STEP, N - 1>(n);
+  }
+}
+
 // Register plan of one variant: accumulators, registers per pipeline stage,
 // and the deepest pipeline that fits 128 VGPRs (4 waves per SIMD) or else
 // 256 VGPRs (2 waves per SIMD).
 struct Plan {
   int acc, stage, wpe, depth;
 };
-constexpr Plan plan(int mt, int g, int ct, bool i8) {
+constexpr Plan plan(int mt, int g, int ct, bool i8, bool sa) {
   const int acc = ct * g * mt * 4;
-  const int stage = ct * g * 4 + mt * (i8 ? 2 : 1) * 4;
-  const int fixed = i8 ? 64 : 40;  // addresses, loop state, int8 conversion temporaries
+  const int act = mt * (i8 ? 2 : 1) * 4;  // one K unit of activations
+  // with shared activations (sa) only the weights are in flight in
+  // registers; the unit being consumed is read from LDS
+  const int stage = ct * g * 4 + (sa ? 0 : act);
+  // addresses, loop state, int8 conversion (and, shared, the unit read from LDS)
+  const int fixed = (i8 ? 64 : 40) + (sa ? act + (i8 ? 8 : 0) : 0);
   const int d128 = (128 - fixed - acc) / stage;
   if (d128 >= 4) return Plan{acc, stage, 4, d128 < 6 ? d128 : 6};
   const int d256 = (256 - fixed - acc) / stage;
   return Plan{acc, stage, 2, d256 < 2 ? 2 : (d256 < 6 ? d256 : 6)};
 }
 
-template <int MT, int G, int CT, bool I8, int EPI, int NW, bool SPLITK>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(plan(MT, G, CT, I8).wpe))) void
+template <int MT, int G, int CT, bool I8, int EPI, int NW, bool SPLITK, bool SA>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(plan(MT, G, CT, I8, SA).wpe))) void
 k_ffn_skinny(const SkinnyArgs A) {
-  constexpr int D = plan(MT, G, CT, I8).depth;
+  static_assert(!(SA && SPLITK), "shared activations need every wave on the same K range");
+  constexpr int D = plan(MT, G, CT, I8, SA).depth;
   constexpr int R = 16 * MT;        // rows per work item
   constexpr int AH = I8 ? 2 : 1;    // activation loads per K unit
   constexpr int UK = I8 ? 64 : 32;  // k per unit
+  // Shared activations: the NAF activation fragments of a K unit are copied
+  // once per workgroup into an LDS ring of DA units (wave w copies fragments
+  // w, w + NW, ...; with fewer fragments than waves the extra waves copy one
+  // again, same bytes to the same place) and every wave reads them there.
+  constexpr int NAF = MT * AH;
+  constexpr int CPW = NAF >= NW ? NAF / NW : 1;  // copies per wave per unit
+  static_assert(!SA || NAF < NW || NAF % NW == 0, "activation fragments must split evenly over the waves");
+  constexpr int DA = D + 1;
+  constexpr int OPS = CT * G + (SA ? CPW : 0);  // vector-memory operations per unit and wave
+  static_assert(!SA || (D - 1) * OPS <= 63, "vmcnt holds at most 63");
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
   __shared__ DispatchLds<NW> DL;
   __shared__ int offs_s[kMaxExperts + 1];
@@ -135,7 +174,13 @@ k_ffn_skinny(const SkinnyArgs A) {
     if (tid < nrows) rows_s[tid] = A.perm[row0 + tid];
     __syncthreads();
   }
-  if (!valid || ntile >= NB) return;  // (NB is a multiple of 4, so a wave's tiles are all in or all out)
+  if (!valid) return;
+  // (NB is a multiple of 4, so a wave's tiles are all in or all out.)  With
+  // shared activations a wave past the last tile stays for the copies and
+  // barriers, streaming the group's first tiles, and stores nothing.
+  const bool live = ntile < NB;
+  if (!SA && !live) return;
+  const int ltile = live ? ntile : wk.ngroup * NW * CT;
 
   // Activation pointers of this lane, one per M tile, and the element strides
   // of a K unit (su) and of its second 32-k half for int8 (sh).
@@ -176,7 +221,7 @@ k_ffn_skinny(const SkinnyArgs A) {
   else
     unit_range(ks, S, U, &u0, &u1);
   // the CT column tiles of this group are consecutive streams of U*G units
-  const u32x4_t* wp = static_cast<const u32x4_t*>(A.w) + (size_t)(e * NB + ntile) * U * G * 64 + lane;
+  const u32x4_t* wp = static_cast<const u32x4_t*>(A.w) + (size_t)(e * NB + ltile) * U * G * 64 + lane;
   const size_t tile_stride = (size_t)U * G * 64;
 
   floatx4_t acc[CT][G][MT];
@@ -188,18 +233,59 @@ k_ffn_skinny(const SkinnyArgs A) {
       for (int mt = 0; mt < MT; ++mt) acc[c][g][mt] = floatx4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
   u32x4_t wb[D][CT][G];
-  u32x4_t ab[D][MT][AH];
+  u32x4_t ab[SA ? 1 : D][MT][AH];
+
+  // Shared activations: this wave's copies (fragment, uniform source of
+  // unit 0) and the ring.  Packed rows only: tiles past the chunk's last
+  // real row re-read its last fragment, as the per-wave loads do.
+  __shared__ __attribute__((aligned(16))) u32x4_t sa_ring[SA ? DA * NAF * 64 : 1];
+  const char* sa_src[CPW];
+  int sa_frag[CPW];
+  const uint32_t sa_lds = lds_address(sa_ring);
+  if constexpr (SA) {
+    const int rb = __builtin_amdgcn_readfirstlane(prow0 >> 4);
+    const int nfrag = __builtin_amdgcn_readfirstlane((nrows + 15) >> 4);
+#pragma unroll
+    for (int j = 0; j < CPW; ++j) {
+      const int f = NAF >= NW ? wave + NW * j : wave % NAF;
+      const int mt = f / AH, h = f % AH;
+      sa_frag[j] = f;
+      sa_src[j] = reinterpret_cast<const char*>(A.act + ((size_t)(rb + min(mt, nfrag - 1)) * (A.K / 32) + h) * 512);
+    }
+  }
 
 #define MOE_ISSUE(slot, u)                                                                             \
   do {                                                                                                 \
     _Pragma("unroll") for (int c = 0; c < CT; ++c) _Pragma("unroll") for (int g = 0; g < G; ++g)      \
         wb[slot][c][g] = __builtin_nontemporal_load(wp + c * tile_stride + ((size_t)(u) * G + g) * 64); \
-    _Pragma("unroll") for (int mt = 0; mt < MT; ++mt) _Pragma("unroll") for (int h = 0; h < AH; ++h)   \
-        ab[slot][mt][h] = *reinterpret_cast<const u32x4_t*>(arow[mt] + (size_t)(u) * su + sh * h);     \
+    if constexpr (SA) {                                                                                \
+      _Pragma("unroll") for (int j = 0; j < CPW; ++j)                                                  \
+          copy_frag(sa_src[j] + (size_t)(u) * (AH * 1024), 16u * lane,                                 \
+                    sa_lds + (uint32_t)((((u) % DA) * NAF + sa_frag[j]) * 1024));                      \
+    } else {                                                                                           \
+      _Pragma("unroll") for (int mt = 0; mt < MT; ++mt) _Pragma("unroll") for (int h = 0; h < AH; ++h) \
+          ab[slot][mt][h] = load_global16(arow[mt] + (size_t)(u) * su + sh * h);                       \
+    }                                                                                                  \
   } while (0)
 
-#define MOE_CONSUME(slot)                                                                              \
+  // Activations of the unit being consumed.  Shared: wait until at most
+  // `after` later units of this wave's operations are outstanding (its
+  // copies of this unit have landed), pass the barrier (so have every
+  // wave's), then read the unit's fragments from the ring.
+#define MOE_ACT_FETCH(slot, u, after)                                                                  \
+  u32x4_t av[SA ? MT : 1][AH];                                                                         \
+  if constexpr (SA) {                                                                                  \
+    wait_units<OPS, D - 1>(after);                                                                     \
+    ring_barrier();                                                                                    \
+    const u32x4_t* st_ = sa_ring + ((u) % DA) * NAF * 64 + lane;                                       \
+    _Pragma("unroll") for (int mt = 0; mt < MT; ++mt) _Pragma("unroll") for (int h = 0; h < AH; ++h)   \
+        av[mt][h] = st_[(mt * AH + h) * 64];                                                           \
+  }
+#define MOE_ACT(slot, mt, h) (SA ? av[(mt) % (SA ? MT : 1)][h] : ab[(slot) % (SA ? 1 : D)][mt][h])
+
+#define MOE_CONSUME(slot, u, after)                                                                    \
   do {                                                                                                 \
+    MOE_ACT_FETCH(slot, u, after)                                                                      \
     _Pragma("unroll") for (int c = 0; c < CT; ++c) {                                                   \
       if constexpr (I8) {                                                                              \
         _Pragma("unroll") for (int h = 0; h < 2; ++h) {                                                \
@@ -207,14 +293,14 @@ k_ffn_skinny(const SkinnyArgs A) {
             const u32x4_t q = wb[slot][c][g];                                                          \
             const bf16x8_t bw = h == 0 ? i8x8_to_bf16(q[0], q[1]) : i8x8_to_bf16(q[2], q[3]);          \
             _Pragma("unroll") for (int mt = 0; mt < MT; ++mt) acc[c][g][mt] =                          \
-                __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ab[slot][mt][h]), bw, acc[c][g][mt], 0, 0, 0); \
+                __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(MOE_ACT(slot, mt, h)), bw, acc[c][g][mt], 0, 0, 0); \
           }                                                                                            \
         }                                                                                              \
       } else {                                                                                         \
         _Pragma("unroll") for (int g = 0; g < G; ++g) {                                                \
           const bf16x8_t bw = as_bf16x8(wb[slot][c][g]);                                               \
           _Pragma("unroll") for (int mt = 0; mt < MT; ++mt) acc[c][g][mt] =                            \
-              __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ab[slot][mt][0]), bw, acc[c][g][mt], 0, 0, 0); \
+              __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(MOE_ACT(slot, mt, 0)), bw, acc[c][g][mt], 0, 0, 0); \
         }                                                                                              \
       }                                                                                                \
     }                                                                                                  \
@@ -223,7 +309,9 @@ k_ffn_skinny(const SkinnyArgs A) {
   // Software pipeline, D units in flight.  When the wave has at least 2D
   // units: an unguarded prologue and steady state (straight-line code, so the
   // compiler waits only for the unit being consumed), then a guarded tail of
-  // fewer than 2D units.  Short reductions take a plain loop.
+  // fewer than 2D units.  Short reductions take a plain loop.  The third
+  // argument of MOE_CONSUME is the number of later units already issued
+  // (the shared-activation wait depends on it).
   if (u1 - u0 >= 2 * D) {
 #pragma unroll
     for (int d = 0; d < D; ++d) MOE_ISSUE(d, u0 + d);
@@ -231,28 +319,31 @@ k_ffn_skinny(const SkinnyArgs A) {
     for (; u + 2 * D <= u1; u += D) {
 #pragma unroll
       for (int d = 0; d < D; ++d) {
-        MOE_CONSUME(d);
+        MOE_CONSUME(d, u + d, D - 1);
         MOE_ISSUE(d, u + d + D);
       }
     }
 #pragma unroll
     for (int d = 0; d < D; ++d) {
       if (u + d < u1) {
-        MOE_CONSUME(d);
+        MOE_CONSUME(d, u + d, min(D - 1, u1 - 1 - (u + d)));
         if (u + d + D < u1) MOE_ISSUE(d, u + d + D);
       }
     }
 #pragma unroll
     for (int d = 0; d < D; ++d)
-      if (u + D + d < u1) MOE_CONSUME(d);
+      if (u + D + d < u1) MOE_CONSUME(d, u + D + d, u1 - 1 - (u + D + d));
   } else {
     for (int u = u0; u < u1; ++u) {
       MOE_ISSUE(0, u);
-      MOE_CONSUME(0);
+      MOE_CONSUME(0, u, 0);
     }
   }
 #undef MOE_CONSUME
+#undef MOE_ACT
+#undef MOE_ACT_FETCH
 #undef MOE_ISSUE
+  if (!live) return;  // (shared activations only: other waves past NB returned above)
 
   // Stores one output element (row of the chunk, column) from its G sums.
   auto store = [&](int row, int col, const float* v) {
@@ -329,28 +420,38 @@ k_ffn_skinny(const SkinnyArgs A) {
   }
 }
 
-template <int MT, int CT, bool I8, bool SPLITK>
+template <int MT, int CT, bool I8, bool SPLITK, bool SA>
 hipError_t launch_ct(const SkinnyArgs& a, int epi, hipStream_t s) {
   const int NG = SPLITK ? a.N / 16 / CT : skinny_groups(a.N, CT);
   const long long work = (long long)NG * a.W * a.ksplit;
   const long long nblk = (work + 7) / 8 * 8;
   const dim3 grid((unsigned)nblk);
   switch (epi) {
-    case EPI_UP_SWIGLU: k_ffn_skinny<MT, 2, CT, I8, EPI_UP_SWIGLU, 4, SPLITK><<<grid, 256, 0, s>>>(a); break;
-    case EPI_UP_RELU: k_ffn_skinny<MT, 1, CT, I8, EPI_UP_RELU, 4, SPLITK><<<grid, 256, 0, s>>>(a); break;
-    case EPI_DOWN_ACC: k_ffn_skinny<MT, 1, CT, I8, EPI_DOWN_ACC, 4, SPLITK><<<grid, 256, 0, s>>>(a); break;
-    default: k_ffn_skinny<MT, 1, CT, I8, EPI_DOWN_ROWS, 4, SPLITK><<<grid, 256, 0, s>>>(a); break;
+    case EPI_UP_SWIGLU: k_ffn_skinny<MT, 2, CT, I8, EPI_UP_SWIGLU, 4, SPLITK, SA><<<grid, 256, 0, s>>>(a); break;
+    case EPI_UP_RELU: k_ffn_skinny<MT, 1, CT, I8, EPI_UP_RELU, 4, SPLITK, SA><<<grid, 256, 0, s>>>(a); break;
+    case EPI_DOWN_ACC: k_ffn_skinny<MT, 1, CT, I8, EPI_DOWN_ACC, 4, SPLITK, SA><<<grid, 256, 0, s>>>(a); break;
+    default: k_ffn_skinny<MT, 1, CT, I8, EPI_DOWN_ROWS, 4, SPLITK, SA><<<grid, 256, 0, s>>>(a); break;
   }
   return hipGetLastError();
+}
+
+// Shared activations only where the waves of a workgroup share a K range
+// (columns split over the waves) and the rows are packed.
+template <int MT, int CT, bool I8, bool SPLITK>
+hipError_t launch_sa(const SkinnyArgs& a, int epi, hipStream_t s) {
+  if constexpr (!SPLITK) {
+    if (a.shared_act) return launch_ct<MT, CT, I8, SPLITK, true>(a, epi, s);
+  }
+  return launch_ct<MT, CT, I8, SPLITK, false>(a, epi, s);
 }
 
 template <int MT, bool I8, bool SPLITK>
 hipError_t launch_mt(const SkinnyArgs& a, int epi, int ct, hipStream_t s) {
   if constexpr (MT < 4) {
-    if (ct >= 4) return launch_ct<MT, 4, I8, SPLITK>(a, epi, s);
+    if (ct >= 4) return launch_sa<MT, 4, I8, SPLITK>(a, epi, s);
   }
-  if (ct >= 2) return launch_ct<MT, 2, I8, SPLITK>(a, epi, s);
-  return launch_ct<MT, 1, I8, SPLITK>(a, epi, s);
+  if (ct >= 2) return launch_sa<MT, 2, I8, SPLITK>(a, epi, s);
+  return launch_sa<MT, 1, I8, SPLITK>(a, epi, s);
 }
 
 template <bool SPLITK>
@@ -367,6 +468,7 @@ hipError_t launch_split(const SkinnyArgs& a, int epi, bool i8, int mt, int ct, h
 }  // namespace
 
 hipError_t launch_ffn_skinny(const SkinnyArgs& a, int epi, bool i8, int mt, int ct, bool splitk, hipStream_t s) {
+  if (a.shared_act && (splitk || !a.packed)) return hipErrorInvalidValue;
   return splitk ? launch_split<true>(a, epi, i8, mt, ct, s) : launch_split<false>(a, epi, i8, mt, ct, s);
 }
 

@@ -91,6 +91,8 @@ struct SkinnyArgs {
   int max_rows;            // > 0: experts with more rows are skipped (another kernel serves them)
   int packed;              // 1: act is in the packed row layout (moe_index.hpp), no gather
   int h_packed;            // 1: the up epilogue writes H in the packed row layout
+  int shared_act;          // 1: each workgroup copies a unit's activation fragments once into LDS
+                           //    for all its waves (packed rows, columns split over the waves)
 };
 
 // Largest T*k for which the decode FFN derives the dispatch in its prologue.
