@@ -176,13 +176,16 @@ int skinny_mt(const moe_weights* W, int T, int k) {
 // as packed 1 KiB fragments (x gathered by k_pack_rows, H written packed by
 // the up projection): one contiguous load per tile and K unit instead of 16
 // half-line rows, which measured as the dominant cost of the skewed layer
-// (-11 % there).  With one or two tiles the extra dispatch and packing
+// (-11 % there).  With one or two bf16 tiles the extra dispatch and packing
 // launches cost more than they save, so rows are gathered directly and the
 // dispatch stays fused into the up projection (MOE_SKINNY_PACK=0/1
 // overrides).
 bool skinny_packed(const moe_weights* W, int T, int k) {
   if (W->w_dtype == MOE_F32) return false;
-  return env_int("MOE_SKINNY_PACK", skinny_mt(W, T, k) >= 4 ? 1 : 0) != 0;
+  // int8 weights span 64 k per unit, so two M tiles already read four
+  // activation fragments per unit: packed and shared measured ahead there
+  const int dflt = skinny_mt(W, T, k) >= (W->w_dtype == MOE_I8 ? 2 : 4) ? 1 : 0;
+  return env_int("MOE_SKINNY_PACK", dflt) != 0;
 }
 
 // Workspace carving, in the order listed.
@@ -365,10 +368,51 @@ int run_skinny(const moe_weights* W, const FfnIo& io, int max_rows, hipStream_t 
     a.d_perm = io.perm;
     a.d_inv = io.inv;
   }
+  // Experts holding more than one chunk of four M tiles (the hot experts of a
+  // skewed routing) would have their gate/up weights streamed once per 64-row
+  // chunk.  With shared activations the up projection serves them with the
+  // twelve-tile kernel instead (192-row chunks), launched first on the
+  // caller's stream so its workgroups take CUs before the four-tile kernel's,
+  // which runs beside it on the side stream and skips them; the profiled span
+  // covers both (MOE_SKINNY_WIDE=0 turns this off).  The down projection
+  // keeps the four-tile kernel for every expert: its twelve-tile form has too
+  // few workgroups (N = m columns, reduction not splittable without more
+  // atomics) and measured slower.
+  const bool wide = max_rows <= 0 && mt == 4 && a.shared_act && !io.topk_idx && W->side &&
+                    env_int("MOE_SKINNY_WIDE", 1) != 0;
+  constexpr int kWideMt = 12;
+  moe::SkinnyArgs aw{};
+  std::unique_lock<std::mutex> lk(W->mu, std::defer_lock);
+  if (wide) {
+    lk.lock();
+    a.max_rows = R;
+    aw = a;
+    aw.max_rows = 0;
+    aw.min_rows = R;
+    // chunks: at most n/192 full ones plus one partial per expert above R rows
+    const long long n = (long long)T * k;
+    aw.W = (int)(n / moe::skinny_rows(kWideMt) + n / (R + 1) + 1);
+  }
   const int up_epi = swiglu ? moe::EPI_UP_SWIGLU : moe::EPI_UP_RELU;
   const int up_ct = skinny_ct(mt, i8, swiglu ? 2 : 1, "MOE_UP_CT");
-  MOE_TRY_HIP(run("ffn_up", s, [&] { return moe::launch_ffn_skinny(a, up_epi, i8, mt, up_ct, splitk, s); }));
-  // down: H -> weighted combine (or unweighted rows)
+  // twelve M tiles keep one column tile per wave for SwiGLU (two streams)
+  const int up_ct_wide = swiglu ? 1 : 2;
+  MOE_TRY_HIP(run("ffn_up", s, [&]() -> hipError_t {
+    if (!wide) return moe::launch_ffn_skinny(a, up_epi, i8, mt, up_ct, splitk, s);
+    hipError_t e = hipEventRecord(W->ev_fork, s);
+    if (e == hipSuccess) e = hipStreamWaitEvent(W->side, W->ev_fork, 0);
+    if (e != hipSuccess) return e;
+    const hipError_t e_w = moe::launch_ffn_skinny(aw, up_epi, i8, kWideMt, up_ct_wide, false, s);
+    const hipError_t e_n = e_w == hipSuccess ? moe::launch_ffn_skinny(a, up_epi, i8, mt, up_ct, splitk, W->side)
+                                             : hipSuccess;
+    // joined even after a failed launch, so the side stream never runs ahead
+    const hipError_t e1 = hipEventRecord(W->ev_join, W->side);
+    const hipError_t e2 = hipStreamWaitEvent(s, W->ev_join, 0);
+    return e_w != hipSuccess ? e_w : (e_n != hipSuccess ? e_n : (e1 != hipSuccess ? e1 : e2));
+  }));
+  if (wide) lk.unlock();
+  // down: H -> weighted combine (or unweighted rows), every expert
+  a.max_rows = max_rows;
   a.topk_idx = nullptr;
   a.d_counts = a.d_offsets = a.d_perm = a.d_inv = nullptr;
   a.w = W->down;

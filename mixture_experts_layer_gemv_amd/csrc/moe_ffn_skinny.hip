@@ -95,10 +95,14 @@ constexpr Plan plan(int mt, int g, int ct, bool i8, bool sa) {
   const int stage = ct * g * 4 + (sa ? 0 : act);
   // addresses, loop state, int8 conversion (and, shared, the unit read from LDS)
   const int fixed = (i8 ? 64 : 40) + (sa ? act + (i8 ? 8 : 0) : 0);
+  // shared activations: DA = depth + 1 units of the ring in at most 64 KiB,
+  // so two workgroups fit a CU's LDS
+  const int dmax0 = sa ? 64 / (mt * (i8 ? 2 : 1)) - 1 : 6;
+  const int dmax = dmax0 < 6 ? dmax0 : 6;
   const int d128 = (128 - fixed - acc) / stage;
-  if (d128 >= 4) return Plan{acc, stage, 4, d128 < 6 ? d128 : 6};
+  if (d128 >= 4) return Plan{acc, stage, 4, d128 < dmax ? d128 : dmax};
   const int d256 = (256 - fixed - acc) / stage;
-  return Plan{acc, stage, 2, d256 < 2 ? 2 : (d256 < 6 ? d256 : 6)};
+  return Plan{acc, stage, 2, d256 < 2 ? 2 : (d256 < dmax ? d256 : dmax)};
 }
 
 template <int MT, int G, int CT, bool I8, int EPI, int NW, bool SPLITK, bool SA>
@@ -149,9 +153,8 @@ k_ffn_skinny(const SkinnyArgs A) {
 
   // (expert, chunk) of this work item and the number of valid pairs
   int e, chunk, npairs;
-  const bool has_pair = skinny_pair(offs_s, A.E, R, wk.pair, &e, &chunk, &npairs);
-  const bool valid = wk.ngroup * (SPLITK ? 1 : NW) * CT < NB && has_pair &&
-                     (A.max_rows <= 0 || offs_s[e + 1] - offs_s[e] <= A.max_rows);
+  const bool has_pair = skinny_pair(offs_s, A.E, R, wk.pair, &e, &chunk, &npairs, A.min_rows, A.max_rows);
+  const bool valid = wk.ngroup * (SPLITK ? 1 : NW) * CT < NB && has_pair;
   const int row0 = valid ? offs_s[e] + chunk * R : 0;
   const int nrows = valid ? min(R, offs_s[e + 1] - row0) : 0;
 
@@ -420,6 +423,18 @@ k_ffn_skinny(const SkinnyArgs A) {
   }
 }
 
+// One variant; variants whose accumulators exceed the register budget are
+// never built (the host does not ask for them).
+template <int MT, int G, int CT, bool I8, int EPI, bool SPLITK, bool SA>
+hipError_t launch_one(const SkinnyArgs& a, dim3 grid, hipStream_t s) {
+  if constexpr (CT * G * MT * 4 > 96) {
+    return hipErrorInvalidValue;
+  } else {
+    k_ffn_skinny<MT, G, CT, I8, EPI, 4, SPLITK, SA><<<grid, 256, 0, s>>>(a);
+    return hipGetLastError();
+  }
+}
+
 template <int MT, int CT, bool I8, bool SPLITK, bool SA>
 hipError_t launch_ct(const SkinnyArgs& a, int epi, hipStream_t s) {
   const int NG = SPLITK ? a.N / 16 / CT : skinny_groups(a.N, CT);
@@ -427,22 +442,26 @@ hipError_t launch_ct(const SkinnyArgs& a, int epi, hipStream_t s) {
   const long long nblk = (work + 7) / 8 * 8;
   const dim3 grid((unsigned)nblk);
   switch (epi) {
-    case EPI_UP_SWIGLU: k_ffn_skinny<MT, 2, CT, I8, EPI_UP_SWIGLU, 4, SPLITK, SA><<<grid, 256, 0, s>>>(a); break;
-    case EPI_UP_RELU: k_ffn_skinny<MT, 1, CT, I8, EPI_UP_RELU, 4, SPLITK, SA><<<grid, 256, 0, s>>>(a); break;
-    case EPI_DOWN_ACC: k_ffn_skinny<MT, 1, CT, I8, EPI_DOWN_ACC, 4, SPLITK, SA><<<grid, 256, 0, s>>>(a); break;
-    default: k_ffn_skinny<MT, 1, CT, I8, EPI_DOWN_ROWS, 4, SPLITK, SA><<<grid, 256, 0, s>>>(a); break;
+    case EPI_UP_SWIGLU: return launch_one<MT, 2, CT, I8, EPI_UP_SWIGLU, SPLITK, SA>(a, grid, s);
+    case EPI_UP_RELU: return launch_one<MT, 1, CT, I8, EPI_UP_RELU, SPLITK, SA>(a, grid, s);
+    case EPI_DOWN_ACC: return launch_one<MT, 1, CT, I8, EPI_DOWN_ACC, SPLITK, SA>(a, grid, s);
+    default: return launch_one<MT, 1, CT, I8, EPI_DOWN_ROWS, SPLITK, SA>(a, grid, s);
   }
-  return hipGetLastError();
 }
 
 // Shared activations only where the waves of a workgroup share a K range
-// (columns split over the waves) and the rows are packed.
+// (columns split over the waves) and the rows are packed; twelve M tiles
+// exist only in that form.
 template <int MT, int CT, bool I8, bool SPLITK>
 hipError_t launch_sa(const SkinnyArgs& a, int epi, hipStream_t s) {
   if constexpr (!SPLITK) {
     if (a.shared_act) return launch_ct<MT, CT, I8, SPLITK, true>(a, epi, s);
   }
-  return launch_ct<MT, CT, I8, SPLITK, false>(a, epi, s);
+  if constexpr (MT > 4) {
+    return hipErrorInvalidValue;
+  } else {
+    return launch_ct<MT, CT, I8, SPLITK, false>(a, epi, s);
+  }
 }
 
 template <int MT, bool I8, bool SPLITK>
@@ -462,13 +481,19 @@ hipError_t launch_split(const SkinnyArgs& a, int epi, bool i8, int mt, int ct, h
   }
   if (mt <= 1) return launch_mt<1, false, SPLITK>(a, epi, ct, s);
   if (mt == 2) return launch_mt<2, false, SPLITK>(a, epi, ct, s);
-  return launch_mt<4, false, SPLITK>(a, epi, ct, s);
+  if (mt <= 4) return launch_mt<4, false, SPLITK>(a, epi, ct, s);
+  if constexpr (SPLITK) {
+    return hipErrorInvalidValue;
+  } else {
+    return launch_mt<12, false, SPLITK>(a, epi, ct, s);
+  }
 }
 
 }  // namespace
 
 hipError_t launch_ffn_skinny(const SkinnyArgs& a, int epi, bool i8, int mt, int ct, bool splitk, hipStream_t s) {
   if (a.shared_act && (splitk || !a.packed)) return hipErrorInvalidValue;
+  if (mt > 4 && (mt != 12 || i8 || splitk || !a.shared_act)) return hipErrorInvalidValue;
   return splitk ? launch_split<true>(a, epi, i8, mt, ct, s) : launch_split<false>(a, epi, i8, mt, ct, s);
 }
 

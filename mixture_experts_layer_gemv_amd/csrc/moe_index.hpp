@@ -39,14 +39,18 @@ MOE_HD inline SkinnyWork skinny_work(int L, int W, int S) {
 MOE_HD inline int skinny_groups(int N, int CT) { return (N / 16 + 4 * CT - 1) / (4 * CT); }
 
 // The pair-th (expert, row chunk) in expert order, chunks of R rows, given
-// dispatch offsets[0..E].  Returns false when pair is past the last chunk.
-// npairs receives the total number of chunks.
-MOE_HD inline bool skinny_pair(const int* offsets, int E, int R, int pair, int* e, int* chunk, int* npairs) {
+// dispatch offsets[0..E], counting only experts whose row count lies in
+// (min_rows, max_rows] (a bound <= 0 is absent).  Returns false when pair is
+// past the last chunk.  npairs receives the total number of chunks.
+MOE_HD inline bool skinny_pair(const int* offsets, int E, int R, int pair, int* e, int* chunk, int* npairs,
+                               int min_rows = 0, int max_rows = 0) {
   int n = 0;
   *e = -1;
   *chunk = 0;
   for (int i = 0; i < E; ++i) {
-    const int nch = (offsets[i + 1] - offsets[i] + R - 1) / R;
+    const int cnt = offsets[i + 1] - offsets[i];
+    const bool in = (min_rows <= 0 || cnt > min_rows) && (max_rows <= 0 || cnt <= max_rows);
+    const int nch = in ? (cnt + R - 1) / R : 0;
     if (*e < 0 && pair >= n && pair < n + nch) {
       *e = i;
       *chunk = pair - n;

@@ -89,6 +89,7 @@ struct SkinnyArgs {
   int W;                   // upper bound on (expert, row-chunk) pairs
   int ksplit;              // reduction slices per work item (EPI_DOWN_ACC only)
   int max_rows;            // > 0: experts with more rows are skipped (another kernel serves them)
+  int min_rows;            // > 0: experts with at most this many rows are skipped
   int packed;              // 1: act is in the packed row layout (moe_index.hpp), no gather
   int h_packed;            // 1: the up epilogue writes H in the packed row layout
   int shared_act;          // 1: each workgroup copies a unit's activation fragments once into LDS
@@ -101,8 +102,9 @@ constexpr int kFusedDispatchMax = 4096;
 // Rows per work item for a given M-tile count (16 rows per tile).
 inline int skinny_rows(int mt) { return 16 * mt; }
 
-// mt: 16-row M tiles per work item (1, 2, 4); ct: 16-column tiles per
-// workgroup sharing each activation load (1, 2, 4).
+// mt: 16-row M tiles per work item (1, 2, 4; 12 for bf16 weights with shared
+// activations, ct <= 2 and one column tile for SwiGLU); ct: 16-column tiles
+// per wave sharing each activation load (1, 2, 4).
 // splitk: the four waves of a workgroup split the reduction (partials summed
 // through LDS); otherwise each wave owns its column tiles over the whole range.
 hipError_t launch_ffn_skinny(const SkinnyArgs& a, int epi, bool i8, int mt, int ct, bool splitk, hipStream_t s);

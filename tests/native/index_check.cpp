@@ -22,8 +22,11 @@ static int fails = 0;
     }                                         \
   } while (0)
 
-// One launch: NG column groups x S slices x W pairs, grid padded to 8.
-static void check_launch(int NG, int W, int S, const std::vector<int>& offsets, int R) {
+// One launch: NG column groups x S slices x W pairs, grid padded to 8, over
+// the experts whose row count lies in (min_rows, max_rows].  Returns the rows
+// served per expert (from column group 0, slice 0).
+static std::vector<std::vector<int>> check_launch(int NG, int W, int S, const std::vector<int>& offsets, int R,
+                                                  int min_rows = 0, int max_rows = 0) {
   const int E = (int)offsets.size() - 1;
   const long long work = (long long)NG * W * S;
   const int nblk = (int)((work + 7) / 8 * 8);
@@ -40,7 +43,7 @@ static void check_launch(int NG, int W, int S, const std::vector<int>& offsets, 
     if (w.ngroup >= NG) continue;  // padding block
     CHECK(items.insert({w.ngroup, w.ks, w.pair}).second, "duplicate item L=%d", L);
     int e, chunk, npairs;
-    const bool ok = moe::skinny_pair(offsets.data(), E, R, w.pair, &e, &chunk, &npairs);
+    const bool ok = moe::skinny_pair(offsets.data(), E, R, w.pair, &e, &chunk, &npairs, min_rows, max_rows);
     CHECK(npairs <= W, "npairs %d > W %d", npairs, W);
     if (!ok) continue;
     CHECK(e >= 0 && e < E && chunk >= 0, "pair %d -> e=%d chunk=%d", w.pair, e, chunk);
@@ -72,10 +75,27 @@ static void check_launch(int NG, int W, int S, const std::vector<int>& offsets, 
   for (int e = 0; e < E; ++e) {
     std::vector<int>& v = rows_seen[e];
     std::sort(v.begin(), v.end());
-    CHECK((int)v.size() == offsets[e + 1] - offsets[e], "expert %d rows covered %zu of %d", e, v.size(),
-          offsets[e + 1] - offsets[e]);
+    const int cnt = offsets[e + 1] - offsets[e];
+    const bool in = (min_rows <= 0 || cnt > min_rows) && (max_rows <= 0 || cnt <= max_rows);
+    CHECK((int)v.size() == (in ? cnt : 0), "expert %d (%d rows, window (%d,%d]) rows covered %zu", e, cnt, min_rows,
+          max_rows, v.size());
     for (size_t i = 0; i < v.size(); ++i) CHECK(v[i] == offsets[e] + (int)i, "expert %d row %zu", e, i);
   }
+  return rows_seen;
+}
+
+// The split decode launch: experts with at most `hot` rows in chunks of 64
+// (4 M tiles), the others in chunks of 192 (12 M tiles), with the host's
+// pair-slot bounds; together they serve every row exactly once.
+static void check_split(int N, const std::vector<int>& offsets, int hot) {
+  const int E = (int)offsets.size() - 1, n = offsets[E];
+  const int Wn = E + n / 64;
+  const int Ww = n / 192 + n / (hot + 1) + 1;
+  const auto a = check_launch(moe::skinny_groups(N, 2), Wn, 1, offsets, 64, 0, hot);
+  const auto b = check_launch(moe::skinny_groups(N, 1), Ww, 1, offsets, 192, hot, 0);
+  for (int e = 0; e < E; ++e)
+    CHECK((int)(a[e].size() + b[e].size()) == offsets[e + 1] - offsets[e], "split: expert %d served %zu + %zu rows",
+          e, a[e].size(), b[e].size());
 }
 
 // Grouped GEMM launch over packed operands: 256-row blocks, 2 x 4 waves of
@@ -289,6 +309,17 @@ int main() {
     const int W = E + n / R;
     check_launch(moe::skinny_groups(NB * 16, CT), W, S, offsets_from(counts), R);
     check_launch(NB / CT, W, S, offsets_from(counts), R);
+  }
+  // split decode launch: Zipf-like skews with one to a few hot experts
+  for (int it = 0; it < 300; ++it) {
+    const int E = 1 + (int)(rng() % 64);
+    const int n = (int)(rng() % 2500);
+    std::vector<int> counts(E, 0);
+    for (int a = 0; a < n; ++a) {
+      const double r = std::uniform_real_distribution<double>(0.0, 1.0)(rng);
+      counts[std::min(E - 1, (int)(E * r * r * r))]++;
+    }
+    check_split(64 * (1 + (int)(rng() % 200)), offsets_from(counts), 64);
   }
   // grouped GEMM: the measured prefill layer (T=8192, top-2 of 8) and
   // random small shapes with ragged and empty experts
