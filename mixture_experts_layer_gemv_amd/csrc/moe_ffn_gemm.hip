@@ -44,23 +44,27 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v); }
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
 
-constexpr int kBM = 256;     // rows per workgroup
-constexpr int kWR = 2;       // wave rows
-constexpr int kWC = 4;       // wave columns
-constexpr int kWaves = kWR * kWC;  // two waves per SIMD
-constexpr int kMF = 8;       // row fragments per wave (128 rows)
-constexpr int kNF = 4;       // column fragments per wave (64 columns)
-constexpr int kCPW = 16 / kWaves;  // A (and B) fragments each wave copies per stage
-constexpr int kCPS = 2 * kCPW;     // copies per wave per stage
-constexpr int kStages = 5;   // LDS ring depth: 5 x 32 KiB, all of a CU's LDS
 #ifndef MOE_GEMM_SCHED
 #define MOE_GEMM_SCHED 2
 #endif
+// Schedule 3 runs one wave per SIMD with a 128 x 128 tile each (accumulators
+// in AGPRs); the others two waves per SIMD with 128 x 64 tiles.
+constexpr bool kOnePerSimd = MOE_GEMM_SCHED == 3;
+constexpr int kBM = 256;     // rows per workgroup
+constexpr int kWR = 2;       // wave rows
+constexpr int kWC = kOnePerSimd ? 2 : 4;  // wave columns
+constexpr int kWaves = kWR * kWC;
+constexpr int kMF = 8;       // row fragments per wave (128 rows)
+constexpr int kNF = kOnePerSimd ? 8 : 4;  // column fragments per wave
+constexpr int kCPW = 16 / kWaves;  // A (and B) fragments each wave copies per stage
+constexpr int kCPS = 2 * kCPW;     // copies per wave per stage
+constexpr int kStages = 5;   // LDS ring depth: 5 x 32 KiB, all of a CU's LDS
 // Main-loop schedule.  0: every wave waits for stage s, reads it and
 // multiplies it; 1: every wave reads stage s+1 into a second register set
 // during step s; 2: ping-pong, the two waves of each SIMD in opposite
 // phases (one multiplies while the other reads the next stage and issues
-// copies).
+// copies); 3: one wave per SIMD, reading stage s+1 into a second register set
+// between the groups of products of stage s, with one copy per group.
 constexpr int kSched = MOE_GEMM_SCHED;
 constexpr int kFrag = 1024;  // bytes of one 64-lane x 16-byte fragment
 
@@ -70,7 +74,18 @@ constexpr int kFrag = 1024;  // bytes of one 64-lane x 16-byte fragment
 // their register footprint.  The accumulator is reused only 32 products
 // later, so consecutive products carry no dependence.
 __device__ __forceinline__ void mfma_acc(floatx4_t& acc, const bf16x8_t& a, const bf16x8_t& b) {
-  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
+  if constexpr (kOnePerSimd)
+    asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+  else
+    asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
+}
+
+// Ties an accumulator to the surrounding statements in its register file.
+__device__ __forceinline__ void acc_tie(floatx4_t& acc) {
+  if constexpr (kOnePerSimd)
+    asm volatile("" : "+a"(acc));
+  else
+    asm volatile("" : "+v"(acc));
 }
 
 // The compiler cannot see that the assembly above is a matrix instruction,
@@ -84,7 +99,7 @@ __device__ __forceinline__ void mfma_fence_in(floatx4_t (&acc)[MF][NF]) {
 #pragma unroll
   for (int i = 0; i < MF; ++i)
 #pragma unroll
-    for (int j = 0; j < NF; ++j) asm volatile("" : "+v"(acc[i][j]));
+    for (int j = 0; j < NF; ++j) acc_tie(acc[i][j]);
   asm volatile("s_nop 7\n\ts_nop 7" ::: "memory");
 }
 template <int MF, int NF>
@@ -93,7 +108,7 @@ __device__ __forceinline__ void mfma_fence_out(floatx4_t (&acc)[MF][NF]) {
 #pragma unroll
   for (int i = 0; i < MF; ++i)
 #pragma unroll
-    for (int j = 0; j < NF; ++j) asm volatile("" : "+v"(acc[i][j]));
+    for (int j = 0; j < NF; ++j) acc_tie(acc[i][j]);
 }
 
 // Waits until at most n stages of this wave's copies (kCPS copies each) are
@@ -113,7 +128,8 @@ __device__ __forceinline__ void wait_copies(int n) {
 // products (the fragment reads still run, so the steady state keeps no branch
 // around a load); for layers whose experts hold few rows.
 template <int EPI, bool SKIP>
-__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_ffn_gemm(
+__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(kOnePerSimd ? 1 : 2,
+                                                                                   kOnePerSimd ? 1 : 2))) void k_ffn_gemm(
     const GemmArgs A) {
   constexpr int G = EPI == EPI_UP_SWIGLU ? 2 : 1;
   constexpr int TPW = kNF / G;  // column tiles per wave
@@ -262,6 +278,59 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
     }
     if (g0) ring_barrier();
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+#undef MOE_ISSUE_CLAMPED
+  } else if constexpr (kSched == 3) {
+    // One wave per SIMD, so nothing else covers its LDS reads and copies:
+    // they are placed between the products.  A wave enters step s holding
+    // stage s's fragments; after the step's barrier it issues its products
+    // in kMF groups (row fragment i against every column fragment), each
+    // followed by the reads of row fragment i and column fragment i of stage
+    // s+1 into the other register set and one of its kCPS copies of stage
+    // s + kStages into stage s's slot (every wave read stage s before this
+    // barrier).  The copy assembly orders the reads into their group.  Copy
+    // counts, waits and clamping as in schedule 1.
+    static_assert(kMF == kNF && kCPS == kMF, "one read pair and one copy per product group");
+    struct {
+      bf16x8_t a[kMF], b[kNF];
+    } g;
+#define MOE_ISSUE_CLAMPED(step) MOE_ISSUE((step) < nsteps ? (step) : nsteps - 1)
+#define MOE_COPY_ONE(step, jj)                                                                   \
+  do {                                                                                           \
+    const int cs_ = (step) < nsteps ? (step) : nsteps - 1;                                       \
+    const uint32_t st_ = wave_lds + (uint32_t)(cs_ % kStages) * (32 * kFrag);                    \
+    if ((jj) < kCPW)                                                                             \
+      copy_frag(abase + (size_t)cs_ * kFrag, aoff[(jj) % kCPW], st_ + ((jj) % kCPW) * kFrag);    \
+    else                                                                                         \
+      copy_frag(bbase + (size_t)cs_ * G * kFrag, boff[(jj) % kCPW], st_ + (16 + (jj) % kCPW) * kFrag); \
+  } while (0)
+#pragma unroll
+    for (int s = 0; s < kStages; ++s) MOE_ISSUE_CLAMPED(s);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(kCPS * (kStages - 1)));
+    ring_barrier();
+    MOE_LOAD_B(f, 0);
+    MOE_LOAD_A(f, 0, 0, kMF);
+#define MOE_STEP3(CUR, NXT)                                                                      \
+  do {                                                                                           \
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(kCPS * (kStages - 2)));                                 \
+    ring_barrier();                                                                              \
+    const u32x4_t* nx_ = reinterpret_cast<const u32x4_t*>(ring[(ks + 1) % kStages]);             \
+    _Pragma("unroll") for (int i = 0; i < kMF; ++i) {                                            \
+      if (!SKIP || i < nf_w) {                                                                   \
+        _Pragma("unroll") for (int j = 0; j < kNF; ++j) mfma_acc(acc[i][j], CUR.a[i], CUR.b[j]); \
+      }                                                                                          \
+      NXT.a[i] = as_bf16x8(nx_[(wm * kMF + i) * 64 + lane]);                                     \
+      NXT.b[i] = as_bf16x8(nx_[(16 + wn * kNF + i) * 64 + lane]);                                \
+      MOE_COPY_ONE(ks + kStages, i);                                                             \
+    }                                                                                            \
+    ++ks;                                                                                        \
+  } while (0)
+    for (int ks = 0; ks < nsteps;) {
+      MOE_STEP3(f, g);
+      MOE_STEP3(g, f);
+    }
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+#undef MOE_STEP3
+#undef MOE_COPY_ONE
 #undef MOE_ISSUE_CLAMPED
   } else if constexpr (kSched == 0) {
     // Copies run kStages-1 stages ahead.  Step s: wait until this wave's
