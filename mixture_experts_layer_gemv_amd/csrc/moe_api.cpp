@@ -369,22 +369,21 @@ int run_skinny(const moe_weights* W, const FfnIo& io, int max_rows, hipStream_t 
     a.d_inv = io.inv;
   }
   // Experts holding more than one chunk of four M tiles (the hot experts of a
-  // skewed routing) would have their gate/up weights streamed once per 64-row
-  // chunk.  With shared activations the up projection serves them with the
-  // twelve-tile kernel instead (192-row chunks), launched first on the
-  // caller's stream so its workgroups take CUs before the four-tile kernel's,
-  // which runs beside it on the side stream and skips them; the profiled span
-  // covers both (MOE_SKINNY_WIDE=0 turns this off).  The down projection
-  // keeps the four-tile kernel for every expert: its twelve-tile form has too
-  // few workgroups (N = m columns, reduction not splittable without more
-  // atomics) and measured slower.
-  const bool wide = max_rows <= 0 && mt == 4 && a.shared_act && !io.topk_idx && W->side &&
+  // skewed routing) would have their weights streamed once per 64-row chunk.
+  // With shared activations both projections serve them with twelve-tile
+  // work items instead (192-row chunks), in the same launch as the four-tile
+  // items of the other experts (MOE_SKINNY_WIDE=0 turns this off).  The down
+  // projection does the same only on request (MOE_SKINNY_WIDE_DOWN=1): the
+  // split launch runs at two waves per SIMD where the four-tile down kernel
+  // runs at four, which measured faster on the skewed layer despite the
+  // re-read weights (182 against 196 us).
+  const int up_epi = swiglu ? moe::EPI_UP_SWIGLU : moe::EPI_UP_RELU;
+  const int up_ct = skinny_ct(mt, i8, swiglu ? 2 : 1, "MOE_UP_CT");
+  const bool wide = max_rows <= 0 && mt == 4 && up_ct == 2 && a.shared_act && !i8 && !io.topk_idx &&
                     env_int("MOE_SKINNY_WIDE", 1) != 0;
   constexpr int kWideMt = 12;
   moe::SkinnyArgs aw{};
-  std::unique_lock<std::mutex> lk(W->mu, std::defer_lock);
   if (wide) {
-    lk.lock();
     a.max_rows = R;
     aw = a;
     aw.max_rows = 0;
@@ -393,26 +392,11 @@ int run_skinny(const moe_weights* W, const FfnIo& io, int max_rows, hipStream_t 
     const long long n = (long long)T * k;
     aw.W = (int)(n / moe::skinny_rows(kWideMt) + n / (R + 1) + 1);
   }
-  const int up_epi = swiglu ? moe::EPI_UP_SWIGLU : moe::EPI_UP_RELU;
-  const int up_ct = skinny_ct(mt, i8, swiglu ? 2 : 1, "MOE_UP_CT");
-  // twelve M tiles keep one column tile per wave for SwiGLU (two streams)
-  const int up_ct_wide = swiglu ? 1 : 2;
   MOE_TRY_HIP(run("ffn_up", s, [&]() -> hipError_t {
-    if (!wide) return moe::launch_ffn_skinny(a, up_epi, i8, mt, up_ct, splitk, s);
-    hipError_t e = hipEventRecord(W->ev_fork, s);
-    if (e == hipSuccess) e = hipStreamWaitEvent(W->side, W->ev_fork, 0);
-    if (e != hipSuccess) return e;
-    const hipError_t e_w = moe::launch_ffn_skinny(aw, up_epi, i8, kWideMt, up_ct_wide, false, s);
-    const hipError_t e_n = e_w == hipSuccess ? moe::launch_ffn_skinny(a, up_epi, i8, mt, up_ct, splitk, W->side)
-                                             : hipSuccess;
-    // joined even after a failed launch, so the side stream never runs ahead
-    const hipError_t e1 = hipEventRecord(W->ev_join, W->side);
-    const hipError_t e2 = hipStreamWaitEvent(s, W->ev_join, 0);
-    return e_w != hipSuccess ? e_w : (e_n != hipSuccess ? e_n : (e1 != hipSuccess ? e1 : e2));
+    return wide ? moe::launch_ffn_skinny_split(a, aw, up_epi, s)
+                : moe::launch_ffn_skinny(a, up_epi, i8, mt, up_ct, splitk, s);
   }));
-  if (wide) lk.unlock();
-  // down: H -> weighted combine (or unweighted rows), every expert
-  a.max_rows = max_rows;
+  // down: H -> weighted combine (or unweighted rows)
   a.topk_idx = nullptr;
   a.d_counts = a.d_offsets = a.d_perm = a.d_inv = nullptr;
   a.w = W->down;
@@ -432,7 +416,19 @@ int run_skinny(const moe_weights* W, const FfnIo& io, int max_rows, hipStream_t 
   }
   const int dn_epi = io.combine ? moe::EPI_DOWN_ACC : moe::EPI_DOWN_ROWS;
   const int dn_ct = skinny_ct(mt, i8, 1, "MOE_DOWN_CT");
-  MOE_TRY_HIP(run("ffn_down", s, [&] { return moe::launch_ffn_skinny(a, dn_epi, i8, mt, dn_ct, splitk, s); }));
+  const bool wide_dn = wide && a.ksplit == 1 && dn_ct == 2 && env_int("MOE_SKINNY_WIDE_DOWN", 0) != 0;
+  if (wide && !wide_dn) a.max_rows = max_rows;  // the four-tile launch serves every expert
+  if (wide_dn) {
+    const int W_wide = aw.W;
+    aw = a;
+    aw.W = W_wide;
+    aw.max_rows = 0;
+    aw.min_rows = R;
+  }
+  MOE_TRY_HIP(run("ffn_down", s, [&]() -> hipError_t {
+    return wide_dn ? moe::launch_ffn_skinny_split(a, aw, dn_epi, s)
+                   : moe::launch_ffn_skinny(a, dn_epi, i8, mt, dn_ct, splitk, s);
+  }));
   return MOE_OK;
 }
 

@@ -105,9 +105,18 @@ constexpr Plan plan(int mt, int g, int ct, bool i8, bool sa) {
   return Plan{acc, stage, 2, d256 < 2 ? 2 : (d256 < dmax ? d256 : dmax)};
 }
 
+typedef u32x4_t __attribute__((address_space(3))) lds_u32x4_t;
+
+// Units of the shared-activation ring of one variant (16-byte lanes x 64).
+constexpr int sa_ring_units(int mt, int g, int ct, bool i8, bool sa) {
+  return sa ? (plan(mt, g, ct, i8, sa).depth + 1) * mt * (i8 ? 2 : 1) : 0;
+}
+
+// One workgroup's work: logical block `bid` of a launch of `nblk` blocks (a
+// multiple of 8, dealt to the XCDs round-robin).  sa_ring: the workgroup's
+// shared-activation ring, at least sa_ring_units() KiB (unused otherwise).
 template <int MT, int G, int CT, bool I8, int EPI, int NW, bool SPLITK, bool SA>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(plan(MT, G, CT, I8, SA).wpe))) void
-k_ffn_skinny(const SkinnyArgs A) {
+__device__ __forceinline__ void skinny_body(const SkinnyArgs& A, int bid, int nblk, lds_u32x4_t* sa_ring) {
   static_assert(!(SA && SPLITK), "shared activations need every wave on the same K range");
   constexpr int D = plan(MT, G, CT, I8, SA).depth;
   constexpr int R = 16 * MT;        // rows per work item
@@ -134,7 +143,7 @@ k_ffn_skinny(const SkinnyArgs A) {
   // Block -> logical work index: consecutive logical indices stay on one XCD
   // (blocks are dealt to the 8 XCDs round-robin), so the row chunks of one
   // (expert, tile) run together and share that XCD's L2 copy of the weights.
-  const int L = xcd_logical(blockIdx.x, gridDim.x);  // gridDim.x is a multiple of 8
+  const int L = xcd_logical(bid, nblk);
   const int NB = A.N / 16;  // a multiple of 4 (N is a multiple of 64)
   const int S = A.ksplit;
   const SkinnyWork wk = skinny_work(L, A.W, S);
@@ -241,10 +250,9 @@ k_ffn_skinny(const SkinnyArgs A) {
   // Shared activations: this wave's copies (fragment, uniform source of
   // unit 0) and the ring.  Packed rows only: tiles past the chunk's last
   // real row re-read its last fragment, as the per-wave loads do.
-  __shared__ __attribute__((aligned(16))) u32x4_t sa_ring[SA ? DA * NAF * 64 : 1];
   const char* sa_src[CPW];
   int sa_frag[CPW];
-  const uint32_t sa_lds = lds_address(sa_ring);
+  const uint32_t sa_lds = (uint32_t)(uintptr_t)sa_ring;
   if constexpr (SA) {
     const int rb = __builtin_amdgcn_readfirstlane(prow0 >> 4);
     const int nfrag = __builtin_amdgcn_readfirstlane((nrows + 15) >> 4);
@@ -280,7 +288,7 @@ k_ffn_skinny(const SkinnyArgs A) {
   if constexpr (SA) {                                                                                  \
     wait_units<OPS, D - 1>(after);                                                                     \
     ring_barrier();                                                                                    \
-    const u32x4_t* st_ = sa_ring + ((u) % DA) * NAF * 64 + lane;                                       \
+    const lds_u32x4_t* st_ = sa_ring + ((u) % DA) * NAF * 64 + lane;                                   \
     _Pragma("unroll") for (int mt = 0; mt < MT; ++mt) _Pragma("unroll") for (int h = 0; h < AH; ++h)   \
         av[mt][h] = st_[(mt * AH + h) * 64];                                                           \
   }
@@ -423,6 +431,35 @@ k_ffn_skinny(const SkinnyArgs A) {
   }
 }
 
+template <int MT, int G, int CT, bool I8, int EPI, int NW, bool SPLITK, bool SA>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(plan(MT, G, CT, I8, SA).wpe))) void
+k_ffn_skinny(const SkinnyArgs A) {
+  constexpr int units = sa_ring_units(MT, G, CT, I8, SA);
+  __shared__ __attribute__((aligned(16))) u32x4_t ring[units > 0 ? units * 64 : 1];
+  skinny_body<MT, G, CT, I8, EPI, NW, SPLITK, SA>(A, blockIdx.x, gridDim.x, (lds_u32x4_t*)ring);
+}
+
+// A projection split by expert size in one launch: blocks [0, nwide) run the
+// twelve-tile items of the experts above one four-tile chunk (first, so they
+// take CUs first), the rest the four-tile items of the others.  Both kinds
+// stream 2 KiB of weights per wave and K unit (one column tile of gate and
+// up, or two of ReLU), so the blocks are of one size and the launch's last
+// round stays short.  Both kinds share one ring allocation; the launch runs
+// at two waves per SIMD (the twelve-tile variant's budget).
+constexpr int split_ct(int g) { return g == 2 ? 1 : 2; }
+
+template <int G, int EPI>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_ffn_skinny_split(
+    const SkinnyArgs AN, const SkinnyArgs AW, int nwide) {
+  constexpr int CT = split_ct(G);
+  constexpr int uw = sa_ring_units(12, G, CT, false, true), un = sa_ring_units(4, G, CT, false, true);
+  __shared__ __attribute__((aligned(16))) u32x4_t ring[(uw > un ? uw : un) * 64];
+  if ((int)blockIdx.x < nwide)
+    skinny_body<12, G, CT, false, EPI, 4, false, true>(AW, blockIdx.x, nwide, (lds_u32x4_t*)ring);
+  else
+    skinny_body<4, G, CT, false, EPI, 4, false, true>(AN, blockIdx.x - nwide, gridDim.x - nwide, (lds_u32x4_t*)ring);
+}
+
 // One variant; variants whose accumulators exceed the register budget are
 // never built (the host does not ask for them).
 template <int MT, int G, int CT, bool I8, int EPI, bool SPLITK, bool SA>
@@ -490,6 +527,26 @@ hipError_t launch_split(const SkinnyArgs& a, int epi, bool i8, int mt, int ct, h
 }
 
 }  // namespace
+
+hipError_t launch_ffn_skinny_split(const SkinnyArgs& narrow, const SkinnyArgs& wide, int epi, hipStream_t s) {
+  if (!narrow.shared_act || !wide.shared_act || !narrow.packed || !wide.packed) return hipErrorInvalidValue;
+  if (narrow.ksplit != 1 || wide.ksplit != 1) return hipErrorInvalidValue;
+  const int G = epi == EPI_UP_SWIGLU ? 2 : 1;
+  auto blocks = [](const SkinnyArgs& x, int ct) {
+    const long long work = (long long)skinny_groups(x.N, ct) * x.W;
+    return (work + 7) / 8 * 8;
+  };
+  const long long nw = blocks(wide, split_ct(G)), nn = blocks(narrow, split_ct(G));
+  if (nw + nn > 0x7FFFFFF0LL) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)(nw + nn));
+  switch (epi) {
+    case EPI_UP_SWIGLU: k_ffn_skinny_split<2, EPI_UP_SWIGLU><<<grid, 256, 0, s>>>(narrow, wide, (int)nw); break;
+    case EPI_UP_RELU: k_ffn_skinny_split<1, EPI_UP_RELU><<<grid, 256, 0, s>>>(narrow, wide, (int)nw); break;
+    case EPI_DOWN_ACC: k_ffn_skinny_split<1, EPI_DOWN_ACC><<<grid, 256, 0, s>>>(narrow, wide, (int)nw); break;
+    default: k_ffn_skinny_split<1, EPI_DOWN_ROWS><<<grid, 256, 0, s>>>(narrow, wide, (int)nw); break;
+  }
+  return hipGetLastError();
+}
 
 hipError_t launch_ffn_skinny(const SkinnyArgs& a, int epi, bool i8, int mt, int ct, bool splitk, hipStream_t s) {
   if (a.shared_act && (splitk || !a.packed)) return hipErrorInvalidValue;

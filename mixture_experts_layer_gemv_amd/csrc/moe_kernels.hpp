@@ -109,6 +109,12 @@ inline int skinny_rows(int mt) { return 16 * mt; }
 // through LDS); otherwise each wave owns its column tiles over the whole range.
 hipError_t launch_ffn_skinny(const SkinnyArgs& a, int epi, bool i8, int mt, int ct, bool splitk, hipStream_t s);
 
+// A projection split by expert size in one launch: `narrow` (four M tiles)
+// for the experts it admits and `wide` (twelve M tiles) for the others, both
+// with one column tile per wave for SwiGLU and two otherwise; bf16 weights,
+// packed rows, shared activations, no split K.
+hipError_t launch_ffn_skinny_split(const SkinnyArgs& narrow, const SkinnyArgs& wide, int epi, hipStream_t s);
+
 // ---- expert FFN, grouped GEMM (prefill-sized) path ----------------------------
 
 // Grouped GEMM over packed operands.  Activations and the hidden rows it

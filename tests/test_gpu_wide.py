@@ -1,9 +1,11 @@
 """The split decode launch against the CPU oracle.
 
 With four M tiles and packed, shared activations, experts holding more than
-one 64-row chunk go to the twelve-tile kernel (192-row chunks) on a second
-stream while the four-tile kernel serves the others.  The cases force hot
-experts of every size class: 65..192 rows (one wide chunk, ragged), several
+one 64-row chunk are served by twelve-tile work items (192-row chunks) in the
+same launch as the four-tile items of the others: always for the up
+projection, on request (MOE_SKINNY_WIDE_DOWN=1) for the down projection.
+The cases force hot experts of every size class: 65..192 rows (one wide
+chunk, ragged), several
 wide chunks (over 192 rows), a mix of hot and cold experts, and none hot;
 for the layer (weighted combine by atomics) and the expert-FFN stage
 (unweighted rows), SwiGLU and ReLU.  Bars as in the other parity tests.
@@ -58,10 +60,13 @@ def _layer(T, m, p, E, k, bias, kind, seed):
     return L
 
 
+@pytest.mark.parametrize("down", ["0", "1"])
 @pytest.mark.parametrize("kind", ["swiglu", "relu"])
 @pytest.mark.parametrize("T,m,p,E,k,bias", CASES)
-def test_wide_layer(kind, T, m, p, E, k, bias):
-    log(f"wide layer kind={kind} T={T} m={m} p={p} E={E} k={k} bias={bias}")
+def test_wide_layer(kind, T, m, p, E, k, bias, down, monkeypatch):
+    """down=1 also splits the down projection (opt-in)."""
+    monkeypatch.setenv("MOE_SKINNY_WIDE_DOWN", down)
+    log(f"wide layer kind={kind} down={down} T={T} m={m} p={p} E={E} k={k} bias={bias}")
     L = _layer(T, m, p, E, k, bias, kind, seed=T + p)
     layer = MoELayer(L)
     dbg = layer.debug_buffers()
@@ -76,10 +81,12 @@ def test_wide_layer(kind, T, m, p, E, k, bias):
     layer.close()
 
 
+@pytest.mark.parametrize("down", ["0", "1"])
 @pytest.mark.parametrize("kind", ["swiglu", "relu"])
 @pytest.mark.parametrize("hot", [100, 300])
-def test_wide_expert_ffn_stage(kind, hot):
+def test_wide_expert_ffn_stage(kind, hot, down, monkeypatch):
     """Expert 2 holds `hot` rows (one or two wide chunks); rows are unweighted."""
+    monkeypatch.setenv("MOE_SKINNY_WIDE_DOWN", down)
     T, m, p, E, k = 320, 128, 384, 6, 2
     L = synth.make_layer(spec(T, m, p, E, k, kind, "bf16", seed=hot, sw=0.05))
     layer = MoELayer(L)
