@@ -28,8 +28,9 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
 METRIC = "MoE layer tokens/s; achieved HBM GB/s (T≤64) or MFMA TFLOP/s (T≥4096)"
 TRAFFIC_DIR = os.path.join(ROOT, "profiles")
 _SKINNY = ["mixture_experts_layer_gemv_amd/csrc/" + f for f in
-           ("moe_ffn_skinny.hip", "moe_index.hpp", "moe_dispatch_block.hpp", "moe_kernels.hpp")]
-_GEMM = ["mixture_experts_layer_gemv_amd/csrc/" + f for f in ("moe_ffn_gemm.hip", "moe_index.hpp", "moe_kernels.hpp")]
+           ("moe_ffn_skinny.hip", "moe_index.hpp", "moe_dispatch_block.hpp", "moe_kernels.hpp", "moe_lds.hpp")]
+_GEMM = ["mixture_experts_layer_gemv_amd/csrc/" + f for f in
+         ("moe_ffn_gemm.hip", "moe_index.hpp", "moe_kernels.hpp", "moe_lds.hpp")]
 KERNEL_SOURCES = {"ffn_up": _SKINNY, "ffn_down": _SKINNY, "gemm_up": _GEMM, "gemm_down": _GEMM}
 
 
