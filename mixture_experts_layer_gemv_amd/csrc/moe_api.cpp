@@ -176,10 +176,10 @@ int skinny_mt(const moe_weights* W, int T, int k) {
 // as packed 1 KiB fragments (x gathered by k_pack_rows, H written packed by
 // the up projection): one contiguous load per tile and K unit instead of 16
 // half-line rows, which measured as the dominant cost of the skewed layer
-// (-11 % there).  With one or two bf16 tiles the extra dispatch and packing
-// launches cost more than they save, so rows are gathered directly and the
-// dispatch stays fused into the up projection (MOE_SKINNY_PACK=0/1
-// overrides).
+// (-11 % there).  With one or two bf16 tiles the extra packing launch costs
+// more than it saves, so rows are gathered directly (MOE_SKINNY_PACK=0/1
+// overrides).  At decode sizes the dispatch is derived by the first kernel
+// either way: the packing, or the up projection's prologue.
 bool skinny_packed(const moe_weights* W, int T, int k) {
   if (W->w_dtype == MOE_F32) return false;
   // int8 weights span 64 k per unit, so two M tiles already read four
@@ -306,6 +306,13 @@ int run_pack(const moe_weights* W, const FfnIo& io, hipStream_t s) {
   pk.K = W->m;
   pk.E = W->E;
   pk.topk = io.k;
+  if (io.topk_idx) {  // the dispatch is derived while packing
+    pk.topk_idx = io.topk_idx;
+    pk.d_counts = io.counts;
+    pk.d_offsets = io.offsets;
+    pk.d_perm = io.perm;
+    pk.d_inv = io.inv;
+  }
   MOE_TRY_HIP(run("pack_rows", s, [&] { return moe::launch_pack_rows(pk, s); }));
   return MOE_OK;
 }
@@ -392,7 +399,9 @@ int run_skinny(const moe_weights* W, const FfnIo& io, int max_rows, hipStream_t 
   // workgroup reads the same activation fragments, so they are copied into
   // LDS once per workgroup (MOE_SKINNY_SA=0 turns this off)
   a.shared_act = packed && !splitk && env_int("MOE_SKINNY_SA", 1) != 0;
-  if (io.topk_idx) {
+  // the dispatch is derived in this kernel's prologue (gathered rows) or was
+  // derived by the row packing
+  if (io.topk_idx && !packed) {
     a.topk_idx = io.topk_idx;
     a.d_counts = io.counts;
     a.d_offsets = io.offsets;
@@ -410,7 +419,7 @@ int run_skinny(const moe_weights* W, const FfnIo& io, int max_rows, hipStream_t 
   // re-read weights (182 against 196 us).
   const int up_epi = swiglu ? moe::EPI_UP_SWIGLU : moe::EPI_UP_RELU;
   const int up_ct = skinny_ct(mt, i8, swiglu ? 2 : 1, "MOE_UP_CT");
-  const bool wide = max_rows <= 0 && mt == 4 && up_ct == 2 && a.shared_act && !i8 && !io.topk_idx &&
+  const bool wide = max_rows <= 0 && mt == 4 && up_ct == 2 && a.shared_act && !i8 && !a.topk_idx &&
                     env_int("MOE_SKINNY_WIDE", 1) != 0;
   constexpr int kWideMt = 12;
   moe::SkinnyArgs aw{};
@@ -767,8 +776,9 @@ int moe_layer_forward(const moe_weights* w, const float* w_router, const float* 
   // dispatch itself
   const Path path = ffn_path(w, T, k);
   const bool gemm = path == Path::GEMM;
-  const bool fused =
-      path == Path::SKINNY && !skinny_packed(w, T, k) && (long long)T * k <= moe::kFusedDispatchMax;
+  // at decode sizes the dispatch is derived by the first FFN kernel: the up
+  // projection's prologue, or the row packing before it
+  const bool fused = path == Path::SKINNY && (long long)T * k <= moe::kFusedDispatchMax;
 
   MOE_TRY_HIP(run("route_topk", s, [&] {
     return moe::launch_route_topk(x, x_dtype == MOE_BF16, w_router, b_router, T, m, E, k, false, logits, idx, tw,

@@ -20,18 +20,20 @@
 // 32 KiB stages (32 k each; all 160 KiB of a CU's LDS), copied global -> LDS
 // with global_load_lds_dwordx4 (lane l of a copy lands at base + 16 l): each
 // copy is one contiguous 1 KiB read, and each wave reads a fragment with one
-// conflict-free 16-byte ds_read per lane.  Every wave reads stage s+1 into a
-// second register set while the products of stage s run, so products issue
-// right after each step's barrier; four stages of copies stay in flight.
+// conflict-free 16-byte ds_read per lane.  The two waves of each SIMD take
+// turns: one multiplies the stage it holds in registers while the other reads
+// its next stage and issues copies (ping-pong, two barriers per step); four
+// to five stages of copies stay in flight.
 // Workgroups run expert by expert, in groups of A.cg (4) column blocks x all
 // of the expert's row blocks, on one XCD at a time: the ~32 resident
 // workgroups then read ~8 activation tiles and ~4 weight tiles per stage,
 // the rest hits in L2.
 //
 // Measured on the Mixtral-shaped prefill layer (T = 8192), the kernel runs
-// the matrix cores about half the time: the copies, the LDS reads and the
-// barrier each cost a share, and with all three running the clock drops
-// from ~2.4 to ~2.0 GHz.
+// the matrix cores about half the time: the global -> LDS copies alone take
+// three quarters of its time, and with copies, LDS reads and products all
+// running the clock drops from ~2.4 to ~2.0 GHz.
+#include "moe_dispatch_block.hpp"
 #include "moe_index.hpp"
 #include "moe_lds.hpp"
 #include "moe_kernels.hpp"
@@ -442,11 +444,42 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(kOn
 __global__ __launch_bounds__(256) void k_pack_rows(const PackArgs A) {
   __shared__ int offs_s[kMaxExperts + 1];
   __shared__ int poffs_s[kMaxExperts + 1];
+  __shared__ DispatchLds<4> DL;
+  __shared__ int row_a[32];  // with the dispatch derived here: assignment of each packed row of the block
   const int tid = threadIdx.x, lane = tid & 63;
-  if (tid <= A.E) offs_s[tid] = A.offsets[tid];
-  __syncthreads();
-  if (tid <= A.E) poffs_s[tid] = padded_offset(offs_s, tid);
-  __syncthreads();
+  // first packed row of the block's first fragment; its four fragments span
+  // at most two 16-row blocks (K/32 >= 2)
+  const long long prow_base = (long long)blockIdx.x * 4 / (A.K / 32) * 16;
+  if (A.topk_idx) {
+    // The dispatch of the (small) batch, derived in every workgroup as in
+    // the dispatch kernel; workgroup 0 publishes it for the FFN kernels.
+    const int n = A.T * A.topk;
+    block_histogram<4>(A.topk_idx, n, A.E, DL);
+    if (tid <= A.E) offs_s[tid] = DL.offs[tid];
+    if (tid < 32) row_a[tid] = -1;
+    __syncthreads();
+    if (tid <= A.E) poffs_s[tid] = padded_offset(offs_s, tid);
+    __syncthreads();
+    const bool publish = blockIdx.x == 0;
+    block_stable_positions<4>(A.topk_idx, n, A.E, DL, [&](int a, int ea, int pos) {
+      if (publish) {
+        A.d_perm[pos] = a;
+        A.d_inv[a] = pos;
+      }
+      const long long r = poffs_s[ea] + (pos - offs_s[ea]) - prow_base;
+      if (r >= 0 && r < 32) row_a[r] = a;
+    });
+    if (publish) {
+      if (tid < A.E) A.d_counts[tid] = DL.cnt[tid];
+      if (tid <= A.E) A.d_offsets[tid] = DL.offs[tid];
+    }
+    __syncthreads();
+  } else {
+    if (tid <= A.E) offs_s[tid] = A.offsets[tid];
+    __syncthreads();
+    if (tid <= A.E) poffs_s[tid] = padded_offset(offs_s, tid);
+    __syncthreads();
+  }
   const int U = A.K / 32;
   const long long frag = (long long)blockIdx.x * 4 + (tid >> 6);
   const long long rb = frag / U;
@@ -458,7 +491,8 @@ __global__ __launch_bounds__(256) void k_pack_rows(const PackArgs A) {
   const int local = (int)(prow - poffs_s[e]);
   u32x4_t v = {0u, 0u, 0u, 0u};
   if (local < offs_s[e + 1] - offs_s[e]) {
-    const int token = A.perm[offs_s[e] + local] / A.topk;
+    const int a = A.topk_idx ? row_a[prow - prow_base] : A.perm[offs_s[e] + local];
+    const int token = a / A.topk;
     v = *reinterpret_cast<const u32x4_t*>(A.x + (size_t)token * A.K + u * 32 + 8 * (lane >> 4));
   }
   reinterpret_cast<u32x4_t*>(A.out)[frag * 64 + lane] = v;

@@ -96,7 +96,8 @@ struct SkinnyArgs {
                            //    for all its waves (packed rows, columns split over the waves)
 };
 
-// Largest T*k for which the decode FFN derives the dispatch in its prologue.
+// Largest T*k for which the decode FFN (or the row packing before it) derives
+// the dispatch itself.
 constexpr int kFusedDispatchMax = 4096;
 
 // Rows per work item for a given M-tile count (16 rows per tile).
@@ -146,9 +147,14 @@ int gemm_rows_per_block();
 // Gathers x rows in dispatch order into the packed row layout.
 struct PackArgs {
   const uint16_t* x;       // [T][K] bf16
-  const int32_t* perm;     // [T*k]
-  const int32_t* offsets;  // [E+1]
+  const int32_t* perm;     // [T*k] (input unless topk_idx is set)
+  const int32_t* offsets;  // [E+1] (input unless topk_idx is set)
   uint16_t* out;           // [packed_rows_max(T*k, E)][K] packed
+  const int32_t* topk_idx; // [T*k] or null: derive the dispatch here (T*k <= kFusedDispatchMax)
+  int32_t* d_counts;       // with topk_idx: dispatch outputs published by workgroup 0
+  int32_t* d_offsets;
+  int32_t* d_perm;
+  int32_t* d_inv;
   int T, K, E, topk;
 };
 hipError_t launch_pack_rows(const PackArgs& a, hipStream_t s);
