@@ -188,6 +188,13 @@ bool skinny_packed(const moe_weights* W, int T, int k) {
   return env_int("MOE_SKINNY_PACK", dflt) != 0;
 }
 
+// Launch shape of the skinny down projection inside the layer (below).
+struct DownShape {
+  int ct, ks;
+};
+DownShape skinny_down_shape(const moe_weights* W, int T, int k);
+bool skinny_rows_combine();
+
 // Workspace carving, in the order listed.
 struct Ws {
   size_t logits, idx, w, counts, offsets, perm, inv, h, yacc, yperm, xp, hp, total;
@@ -217,7 +224,9 @@ Ws ws_layout(const moe_weights* W, int T, int k) {
   const size_t prows = (size_t)moe::packed_rows_max((long long)n, W->E);
   L.h = take((gemm || spack ? prows : n) * (size_t)W->p * (W->w_dtype == MOE_F32 ? 4 : 2));
   L.yacc = take((size_t)T * W->m * 4);
-  L.yperm = gemm ? take(n * (size_t)W->m * 4) : off;
+  const size_t row_sets = gemm ? 1 : (path == Path::SKINNY && skinny_rows_combine()
+                                          ? (size_t)skinny_down_shape(W, T, k).ks : 0);
+  L.yperm = row_sets ? take(row_sets * n * (size_t)W->m * 4) : off;
   L.xp = gemm || hybrid || spack ? take(prows * (size_t)W->m * 2) : off;
   L.hp = hybrid ? take(prows * (size_t)W->p * 2) : off;
   L.total = off;
@@ -280,6 +289,33 @@ void int8_down_shape(const moe_weights* W, int T, int k, int R, int* ct, int* ks
   *ks = std::max(1, std::min(*ks, W->p / 64));
 }
 
+// Launch shape of the skinny down projection inside the layer: column tiles
+// per wave and reduction slices.  Shared by the workspace layout (the
+// unweighted rows are kept per slice) and the launch.
+DownShape skinny_down_shape(const moe_weights* W, int T, int k) {
+  const int mt = skinny_mt(W, T, k);
+  const bool i8 = W->w_dtype == MOE_I8;
+  const bool packed = skinny_packed(W, T, k);
+  const char* wv = getenv("MOE_SKINNY_WAVES");
+  const bool splitk = wv && *wv ? wv[0] == 'k' : !packed;
+  const bool shared = packed && !splitk && env_int("MOE_SKINNY_SA", 1) != 0;
+  const int R = moe::skinny_rows(mt);
+  const int Wp = W->E + (int)((long long)T * k / R);
+  DownShape d{skinny_ct(mt, i8, 1, "MOE_DOWN_CT"), 1};
+  d.ks = down_ksplit((long long)(splitk ? W->m / 16 / d.ct : moe::skinny_groups(W->m, d.ct)) * Wp);
+  if (i8 && shared && env_int("MOE_DOWN_CT", 0) <= 0 && env_int("MOE_DOWN_KSPLIT", 0) <= 0)
+    int8_down_shape(W, T, k, R, &d.ct, &d.ks);
+  d.ks = std::max(1, std::min(d.ks, W->p / 64));
+  return d;
+}
+
+// Decode layers write the down projection's unweighted rows (one set per
+// reduction slice) and finish with the combine kernel, instead of adding
+// weighted rows into an fp32 accumulator with atomics: on the skewed layer
+// one more slice of atomics cost 20 us, about 10^11 adds/s, while the rows
+// and the combine move a few MB (MOE_DOWN_ROWS=0 restores the atomics).
+bool skinny_rows_combine() { return env_int("MOE_DOWN_ROWS", 1) != 0; }
+
 // Inputs and outputs of the two FFN projections.
 struct FfnIo {
   const void* x;
@@ -291,8 +327,10 @@ struct FfnIo {
   void* xp;                 // GEMM/hybrid path: x rows gathered into the packed row layout
   void* hp;                 // hybrid path: the hot experts' H rows, packed
   float* down_out;          // y_acc [T][m] (combine) or y_perm [T*k][m]
-  bool combine;
-  float* yperm;             // grouped-GEMM path with combine: unweighted rows [T*k][m]
+  bool combine;             // inside the layer: the weighted combine follows
+  float* yperm;             // with combine on the grouped-GEMM path, or the skinny path with
+                            // rows: unweighted rows [slices][T*k][m]
+  int* slices;              // set to the number of row slices written to yperm
 };
 
 // Gathers x rows into the packed row layout for the grouped GEMM.
@@ -450,13 +488,18 @@ int run_skinny(const moe_weights* W, const FfnIo& io, int max_rows, hipStream_t 
   a.gather = 0;
   a.packed = packed;
   a.h_packed = 0;
-  int dn_ct = skinny_ct(mt, i8, 1, "MOE_DOWN_CT");
-  if (io.combine) {
-    a.ksplit = down_ksplit((long long)(splitk ? m / 16 / dn_ct : moe::skinny_groups(m, dn_ct)) * a.W);
-    if (i8 && a.shared_act && env_int("MOE_DOWN_CT", 0) <= 0 && env_int("MOE_DOWN_KSPLIT", 0) <= 0)
-      int8_down_shape(W, T, k, R, &dn_ct, &a.ksplit);
+  const DownShape ds = skinny_down_shape(W, T, k);
+  int dn_ct = ds.ct;
+  // inside the layer: unweighted rows per reduction slice for the combine,
+  // or weighted rows added into y_acc; alone: unweighted rows, one slice
+  const bool rows = io.combine && io.yperm && skinny_rows_combine();
+  if (io.combine) a.ksplit = ds.ks;
+  if (rows) {
+    a.f_out = io.yperm;
+    a.slice_stride = (size_t)T * k * m;
   }
-  const int dn_epi = io.combine ? moe::EPI_DOWN_ACC : moe::EPI_DOWN_ROWS;
+  if (io.slices) *io.slices = rows ? a.ksplit : 1;
+  const int dn_epi = io.combine && !rows ? moe::EPI_DOWN_ACC : moe::EPI_DOWN_ROWS;
   const bool wide_dn = wide && a.ksplit == 1 && dn_ct == 2 && env_int("MOE_SKINNY_WIDE_DOWN", 0) != 0;
   if (wide && !wide_dn) a.max_rows = max_rows;  // the four-tile launch serves every expert
   if (wide_dn) {
@@ -740,7 +783,7 @@ int moe_combine(const float* y_perm, const int32_t* inv_perm, const float* topk_
   if (!aligned16(y_perm) || !aligned16(y)) return fail(MOE_ERR_INVALID_ARG, "y_perm/y must be 16-byte aligned");
   const hipStream_t s = as_stream(stream);
   MOE_TRY_HIP(run("combine", s, [&] {
-    return moe::launch_combine(y_perm, inv_perm, topk_w, T, m, k, y, y_dtype == MOE_BF16, s);
+    return moe::launch_combine(y_perm, inv_perm, topk_w, T, m, k, 1, 0, y, y_dtype == MOE_BF16, s);
   }));
   return ok();
 }
@@ -779,10 +822,14 @@ int moe_layer_forward(const moe_weights* w, const float* w_router, const float* 
   // at decode sizes the dispatch is derived by the first FFN kernel: the up
   // projection's prologue, or the row packing before it
   const bool fused = path == Path::SKINNY && (long long)T * k <= moe::kFusedDispatchMax;
+  // unweighted expert rows and the combine kernel (the grouped GEMM, and the
+  // skinny kernels unless MOE_DOWN_ROWS=0), or weighted rows added into y_acc
+  // (zeroed by the router) and a final conversion
+  const bool rows = gemm || (path == Path::SKINNY && skinny_rows_combine());
 
   MOE_TRY_HIP(run("route_topk", s, [&] {
     return moe::launch_route_topk(x, x_dtype == MOE_BF16, w_router, b_router, T, m, E, k, false, logits, idx, tw,
-                                  gemm ? nullptr : yacc, m, s);
+                                  rows ? nullptr : yacc, m, s);
   }));
   if (!fused)
     MOE_TRY_HIP(run("dispatch", s, [&] { return moe::launch_dispatch(idx, T * k, E, counts, offsets, perm, inv, s); }));
@@ -801,11 +848,13 @@ int moe_layer_forward(const moe_weights* w, const float* w_router, const float* 
   io.hp = ws + L.hp;
   io.down_out = yacc;
   io.combine = true;
-  io.yperm = reinterpret_cast<float*>(ws + L.yperm);
+  io.yperm = rows ? reinterpret_cast<float*>(ws + L.yperm) : nullptr;
+  int slices = 1;
+  io.slices = &slices;
   if (int rc = run_ffn(w, io, s)) return rc;
-  if (gemm) {
+  if (rows) {
     MOE_TRY_HIP(run("combine", s, [&] {
-      return moe::launch_combine(io.yperm, inv, tw, T, m, k, y, y_bf16, s);
+      return moe::launch_combine(io.yperm, inv, tw, T, m, k, slices, (size_t)T * k * m, y, y_bf16, s);
     }));
     return ok();
   }

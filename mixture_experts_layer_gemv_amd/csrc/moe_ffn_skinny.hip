@@ -378,8 +378,8 @@ __device__ __forceinline__ void skinny_body(const SkinnyArgs& A, int bid, int nb
       if constexpr (EPI == EPI_DOWN_ACC) {
         const int a = A.perm[r];
         unsafeAtomicAdd(A.f_out + (size_t)(a / A.topk) * A.N + col, A.topk_w[a] * o2);
-      } else {
-        A.f_out[(size_t)r * A.N + col] = o2;
+      } else {  // unweighted row, this reduction slice's partial sum
+        A.f_out[(size_t)ks * A.slice_stride + (size_t)r * A.N + col] = o2;
       }
     }
   };

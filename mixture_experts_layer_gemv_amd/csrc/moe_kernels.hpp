@@ -92,6 +92,7 @@ struct SkinnyArgs {
   int min_rows;            // > 0: experts with at most this many rows are skipped
   int packed;              // 1: act is in the packed row layout (moe_index.hpp), no gather
   int h_packed;            // 1: the up epilogue writes H in the packed row layout
+  size_t slice_stride;     // EPI_DOWN_ROWS with ksplit > 1: elements between the slices' rows
   int shared_act;          // 1: each workgroup copies a unit's activation fragments once into LDS
                            //    for all its waves (packed rows, columns split over the waves)
 };
@@ -177,8 +178,10 @@ hipError_t launch_ffn_f32(const F32Args& a, hipStream_t s);
 
 // ---- combine / elementwise ------------------------------------------------------
 
+// y[t] = sum_j w[t,j] * sum_q y_perm[q][inv[t,j]]: the unweighted expert rows,
+// each the sum of `slices` partial rows slice_stride elements apart.
 hipError_t launch_combine(const float* y_perm, const int32_t* inv_perm, const float* topk_w, int T, int m, int k,
-                          void* y, bool y_bf16, hipStream_t s);
+                          int slices, size_t slice_stride, void* y, bool y_bf16, hipStream_t s);
 hipError_t launch_fill_zero(float* p, size_t n, hipStream_t s);
 hipError_t launch_f32_to_bf16(const float* src, uint16_t* dst, size_t n, hipStream_t s);
 

@@ -130,7 +130,8 @@ __global__ __launch_bounds__(256) void k_ffn_f32(const F32Args A) {
 // y[t][c] = sum_{j<k} w[t][j] * y_perm[inv_perm[t*k+j]][c], four columns per thread.
 template <bool BF16>
 __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ y_perm, const int32_t* __restrict__ inv,
-                                                 const float* __restrict__ w, int T, int m, int k, void* __restrict__ y) {
+                                                 const float* __restrict__ w, int T, int m, int k, int slices,
+                                                 size_t slice_stride, void* __restrict__ y) {
   const size_t q = (size_t)blockIdx.x * blockDim.x + threadIdx.x;  // float4 index
   const size_t per_row = (size_t)m / 4;
   if (q >= (size_t)T * per_row) return;
@@ -139,7 +140,16 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ y_per
   float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
   for (int j = 0; j < k; ++j) {
     const float wj = w[(size_t)t * k + j];
-    const float4 v = *reinterpret_cast<const float4*>(y_perm + (size_t)inv[(size_t)t * k + j] * m + c);
+    const float* row = y_perm + (size_t)inv[(size_t)t * k + j] * m + c;
+    // the row's partial sums over the reduction slices, in slice order
+    float4 v = *reinterpret_cast<const float4*>(row);
+    for (int q = 1; q < slices; ++q) {
+      const float4 u = *reinterpret_cast<const float4*>(row + (size_t)q * slice_stride);
+      v.x += u.x;
+      v.y += u.y;
+      v.z += u.z;
+      v.w += u.w;
+    }
     s.x = fmaf(wj, v.x, s.x);
     s.y = fmaf(wj, v.y, s.y);
     s.z = fmaf(wj, v.z, s.z);
@@ -207,13 +217,15 @@ hipError_t launch_ffn_f32(const F32Args& a, hipStream_t s) {
 }
 
 hipError_t launch_combine(const float* y_perm, const int32_t* inv_perm, const float* topk_w, int T, int m, int k,
-                          void* y, bool y_bf16, hipStream_t s) {
+                          int slices, size_t slice_stride, void* y, bool y_bf16, hipStream_t s) {
+  if (slices < 1) return hipErrorInvalidValue;
   const size_t work = (size_t)T * (m / 4);
   const unsigned grid = (unsigned)((work + 255) / 256);
+  if (work == 0) return hipSuccess;
   if (y_bf16)
-    k_combine<true><<<grid, 256, 0, s>>>(y_perm, inv_perm, topk_w, T, m, k, y);
+    k_combine<true><<<grid, 256, 0, s>>>(y_perm, inv_perm, topk_w, T, m, k, slices, slice_stride, y);
   else
-    k_combine<false><<<grid, 256, 0, s>>>(y_perm, inv_perm, topk_w, T, m, k, y);
+    k_combine<false><<<grid, 256, 0, s>>>(y_perm, inv_perm, topk_w, T, m, k, slices, slice_stride, y);
   return hipGetLastError();
 }
 
