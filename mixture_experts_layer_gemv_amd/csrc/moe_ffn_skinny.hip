@@ -68,7 +68,8 @@ __device__ __forceinline__ bf16x8_t i8x8_to_bf16(uint32_t lo, uint32_t hi) {
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
 
 // Waits until at most n units of STEP vector-memory operations each are
-// outstanding; n is uniform, 0 <= n <= N.
+// outstanding; n is uniform, 0 <= n <= N.  (wait_units_nc: STEP = CG + nc for
+// a uniform nc in [0, C].)
 template <int STEP, int N>
 __device__ __forceinline__ void wait_units(int n) {
   if constexpr (N <= 0) {
@@ -78,6 +79,17 @@ __device__ __forceinline__ void wait_units(int n) {
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(N * STEP));
     else
       wait_units<STEP, N - 1>(n);
+  }
+}
+template <int CG, int C, int N>
+__device__ __forceinline__ void wait_units_nc(int nc, int n) {
+  if constexpr (C <= 0) {
+    wait_units<CG, N>(n);
+  } else {
+    if (nc >= C)
+      wait_units<CG + C, N>(n);
+    else
+      wait_units_nc<CG, C - 1, N>(nc, n);
   }
 }
 
@@ -124,14 +136,13 @@ __device__ __forceinline__ void skinny_body(const SkinnyArgs& A, int bid, int nb
   constexpr int UK = I8 ? 64 : 32;  // k per unit
   // Shared activations: the NAF activation fragments of a K unit are copied
   // once per workgroup into an LDS ring of DA units (wave w copies fragments
-  // w, w + NW, ...; with fewer fragments than waves the extra waves copy one
-  // again, same bytes to the same place) and every wave reads them there.
+  // w, w + NW, ...: NC of them, at most CPW; waves past NAF copy none) and
+  // every wave reads them there.
   constexpr int NAF = MT * AH;
-  constexpr int CPW = NAF >= NW ? NAF / NW : 1;  // copies per wave per unit
-  static_assert(!SA || NAF < NW || NAF % NW == 0, "activation fragments must split evenly over the waves");
+  constexpr int CPW = (NAF + NW - 1) / NW;  // most copies per wave per unit
   constexpr int DA = D + 1;
-  constexpr int OPS = CT * G + (SA ? CPW : 0);  // vector-memory operations per unit and wave
-  static_assert(!SA || (D - 1) * OPS <= 63, "vmcnt holds at most 63");
+  constexpr int CG = CT * G;  // weight loads per unit and wave
+  static_assert(!SA || (D - 1) * (CG + CPW) <= 63, "vmcnt holds at most 63");
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -253,12 +264,13 @@ __device__ __forceinline__ void skinny_body(const SkinnyArgs& A, int bid, int nb
   const char* sa_src[CPW];
   int sa_frag[CPW];
   const uint32_t sa_lds = (uint32_t)(uintptr_t)sa_ring;
+  const int NC = wave < NAF ? (NAF - 1 - wave) / NW + 1 : 0;  // this wave's copies per unit (uniform)
   if constexpr (SA) {
     const int rb = __builtin_amdgcn_readfirstlane(prow0 >> 4);
     const int nfrag = __builtin_amdgcn_readfirstlane((nrows + 15) >> 4);
 #pragma unroll
     for (int j = 0; j < CPW; ++j) {
-      const int f = NAF >= NW ? wave + NW * j : wave % NAF;
+      const int f = min(wave + NW * j, NAF - 1);  // (used only for j < NC)
       const int mt = f / AH, h = f % AH;
       sa_frag[j] = f;
       sa_src[j] = reinterpret_cast<const char*>(A.act + ((size_t)(rb + min(mt, nfrag - 1)) * (A.K / 32) + h) * 512);
@@ -270,7 +282,7 @@ __device__ __forceinline__ void skinny_body(const SkinnyArgs& A, int bid, int nb
     _Pragma("unroll") for (int c = 0; c < CT; ++c) _Pragma("unroll") for (int g = 0; g < G; ++g)      \
         wb[slot][c][g] = __builtin_nontemporal_load(wp + c * tile_stride + ((size_t)(u) * G + g) * 64); \
     if constexpr (SA) {                                                                                \
-      _Pragma("unroll") for (int j = 0; j < CPW; ++j)                                                  \
+      _Pragma("unroll") for (int j = 0; j < CPW; ++j) if (j < NC)                                      \
           copy_frag(sa_src[j] + (size_t)(u) * (AH * 1024), 16u * lane,                                 \
                     sa_lds + (uint32_t)((((u) % DA) * NAF + sa_frag[j]) * 1024));                      \
     } else {                                                                                           \
@@ -286,7 +298,7 @@ __device__ __forceinline__ void skinny_body(const SkinnyArgs& A, int bid, int nb
 #define MOE_ACT_FETCH(slot, u, after)                                                                  \
   u32x4_t av[SA ? MT : 1][AH];                                                                         \
   if constexpr (SA) {                                                                                  \
-    wait_units<OPS, D - 1>(after);                                                                     \
+    wait_units_nc<CG, CPW, D - 1>(NC, after);                                                          \
     ring_barrier();                                                                                    \
     const lds_u32x4_t* st_ = sa_ring + ((u) % DA) * NAF * 64 + lane;                                   \
     _Pragma("unroll") for (int mt = 0; mt < MT; ++mt) _Pragma("unroll") for (int h = 0; h < AH; ++h)   \
@@ -448,16 +460,16 @@ k_ffn_skinny(const SkinnyArgs A) {
 // at two waves per SIMD (the twelve-tile variant's budget).
 constexpr int split_ct(int g) { return g == 2 ? 1 : 2; }
 
-template <int G, int EPI>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_ffn_skinny_split(
+template <int G, int EPI, int NW>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) void k_ffn_skinny_split(
     const SkinnyArgs AN, const SkinnyArgs AW, int nwide) {
   constexpr int CT = split_ct(G);
   constexpr int uw = sa_ring_units(12, G, CT, false, true), un = sa_ring_units(4, G, CT, false, true);
   __shared__ __attribute__((aligned(16))) u32x4_t ring[(uw > un ? uw : un) * 64];
   if ((int)blockIdx.x < nwide)
-    skinny_body<12, G, CT, false, EPI, 4, false, true>(AW, blockIdx.x, nwide, (lds_u32x4_t*)ring);
+    skinny_body<12, G, CT, false, EPI, NW, false, true>(AW, blockIdx.x, nwide, (lds_u32x4_t*)ring);
   else
-    skinny_body<4, G, CT, false, EPI, 4, false, true>(AN, blockIdx.x - nwide, gridDim.x - nwide, (lds_u32x4_t*)ring);
+    skinny_body<4, G, CT, false, EPI, NW, false, true>(AN, blockIdx.x - nwide, gridDim.x - nwide, (lds_u32x4_t*)ring);
 }
 
 // One variant; variants whose accumulators exceed the register budget are
@@ -532,18 +544,20 @@ hipError_t launch_ffn_skinny_split(const SkinnyArgs& narrow, const SkinnyArgs& w
   if (!narrow.shared_act || !wide.shared_act || !narrow.packed || !wide.packed) return hipErrorInvalidValue;
   if (narrow.ksplit != 1 || wide.ksplit != 1) return hipErrorInvalidValue;
   const int G = epi == EPI_UP_SWIGLU ? 2 : 1;
-  auto blocks = [](const SkinnyArgs& x, int ct) {
-    const long long work = (long long)skinny_groups(x.N, ct) * x.W;
+  constexpr int NW = 4;  // (8 waves sharing one ring measured slower on the skewed layer)
+  auto blocks = [&](const SkinnyArgs& x, int ct) {
+    const int tiles = NW * ct;
+    const long long work = (long long)((x.N / 16 + tiles - 1) / tiles) * x.W;
     return (work + 7) / 8 * 8;
   };
   const long long nw = blocks(wide, split_ct(G)), nn = blocks(narrow, split_ct(G));
   if (nw + nn > 0x7FFFFFF0LL) return hipErrorInvalidValue;
   const dim3 grid((unsigned)(nw + nn));
   switch (epi) {
-    case EPI_UP_SWIGLU: k_ffn_skinny_split<2, EPI_UP_SWIGLU><<<grid, 256, 0, s>>>(narrow, wide, (int)nw); break;
-    case EPI_UP_RELU: k_ffn_skinny_split<1, EPI_UP_RELU><<<grid, 256, 0, s>>>(narrow, wide, (int)nw); break;
-    case EPI_DOWN_ACC: k_ffn_skinny_split<1, EPI_DOWN_ACC><<<grid, 256, 0, s>>>(narrow, wide, (int)nw); break;
-    default: k_ffn_skinny_split<1, EPI_DOWN_ROWS><<<grid, 256, 0, s>>>(narrow, wide, (int)nw); break;
+    case EPI_UP_SWIGLU: k_ffn_skinny_split<2, EPI_UP_SWIGLU, NW><<<grid, NW * 64, 0, s>>>(narrow, wide, (int)nw); break;
+    case EPI_UP_RELU: k_ffn_skinny_split<1, EPI_UP_RELU, NW><<<grid, NW * 64, 0, s>>>(narrow, wide, (int)nw); break;
+    case EPI_DOWN_ACC: k_ffn_skinny_split<1, EPI_DOWN_ACC, NW><<<grid, NW * 64, 0, s>>>(narrow, wide, (int)nw); break;
+    default: k_ffn_skinny_split<1, EPI_DOWN_ROWS, NW><<<grid, NW * 64, 0, s>>>(narrow, wide, (int)nw); break;
   }
   return hipGetLastError();
 }

@@ -265,7 +265,7 @@ __global__ __launch_bounds__(1024) void k_route_fast(const void* __restrict__ x,
   const int q = lane & (S::Q - 1);
   const int rr = lane >> S::LQ;
   const int nchunks = m / S::RPC;
-#pragma unroll 2
+#pragma unroll 8
   for (int c = wave; c < nchunks; c += 16) {
     const int r = c * S::RPC + rr;
     const float4 wv = *reinterpret_cast<const float4*>(wg + (size_t)r * E + 4 * q);
