@@ -8,7 +8,9 @@ and split a work item over their four waves either along the reduction
 from the mean rows per expert; here every combination is forced
 (MOE_SKINNY_MT, MOE_SKINNY_PACK, MOE_SKINNY_WAVES) on bf16 and int8 layers
 with ragged experts, for the layer and the expert-FFN stage, at the bars of
-the other parity tests.
+the other parity tests; so are the activation sharing through LDS
+(MOE_SKINNY_SA), the down projection's epilogue (unweighted rows and the
+combine kernel, or weighted atomics: MOE_DOWN_ROWS) and its reduction slices.
 """
 import numpy as np
 import pytest
@@ -83,4 +85,52 @@ def test_skinny_packed_expert_ffn_stage(kind, mt, waves, monkeypatch):
     got = y_perm.cpu().numpy()
     assert np.all(np.isfinite(got)), "rows left unwritten"
     assert_close(got, ref, "bf16", "y_perm")
+    layer.close()
+
+
+@pytest.mark.parametrize("w_dtype", ["bf16", "i8"])
+@pytest.mark.parametrize("rows", ["0", "1"])
+@pytest.mark.parametrize("sa", ["0", "1"])
+@pytest.mark.parametrize("ks", ["1", "2"])
+def test_skinny_epilogue_and_sharing(w_dtype, rows, sa, ks, monkeypatch):
+    """Packed rows with the columns split over the waves: activations copied
+    once per workgroup into LDS (sa=1) or loaded by every wave (sa=0); the down
+    projection's unweighted rows summed by the combine kernel (rows=1, per
+    reduction slice) or weighted rows added with atomics (rows=0); one or two
+    reduction slices."""
+    monkeypatch.setenv("MOE_FFN_PATH", "s")
+    monkeypatch.setenv("MOE_SKINNY_MT", "2")
+    monkeypatch.setenv("MOE_SKINNY_PACK", "1")
+    monkeypatch.setenv("MOE_SKINNY_WAVES", "n")
+    monkeypatch.setenv("MOE_SKINNY_SA", sa)
+    monkeypatch.setenv("MOE_DOWN_ROWS", rows)
+    monkeypatch.setenv("MOE_DOWN_KSPLIT", ks)
+    T, m, p, E, k = 70, 256, 384, 8, 2
+    log(f"skinny epilogue w={w_dtype} rows={rows} sa={sa} ks={ks}")
+    L = synth.make_layer(spec(T, m, p, E, k, "swiglu", w_dtype, seed=17 + 3 * int(ks), zipf=1.2, sw=0.05,
+                              sr=0.05))
+    layer = MoELayer(L)
+    dbg = layer.debug_buffers()
+    y = layer.forward(dbg=dbg)
+    torch.cuda.synchronize()
+    lg, idx_g, _, counts, _ = check_routing(L, dbg, T, E, k)
+    ref, i_o, _, _ = oracle.forward_tokens(oracle.Experts.from_layer(L), L["x"], L["wg"], L["bias"], k,
+                                           np.arange(T), logits=lg)
+    assert np.array_equal(i_o, idx_g)
+    assert_close(y_to_np(y), ref, w_dtype, "y")
+    layer.close()
+
+
+@pytest.mark.parametrize("w_dtype", ["bf16", "i8"])
+def test_skinny_rows_repeat_is_bitwise(w_dtype, monkeypatch):
+    """With unweighted rows and the combine kernel the layer has no atomics:
+    two calls, with two reduction slices, give identical bits."""
+    monkeypatch.setenv("MOE_FFN_PATH", "s")
+    monkeypatch.setenv("MOE_DOWN_KSPLIT", "2")
+    L = synth.make_layer(spec(200, 256, 384, 8, 2, "swiglu", w_dtype, seed=23, zipf=1.2, sw=0.05))
+    layer = MoELayer(L)
+    y1 = layer.forward().clone()
+    y2 = layer.forward()
+    torch.cuda.synchronize()
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
     layer.close()
