@@ -450,11 +450,12 @@ int run_skinny(const moe_weights* W, const FfnIo& io, int max_rows, hipStream_t 
   // skewed routing) would have their weights streamed once per 64-row chunk.
   // With shared activations both projections serve them with twelve-tile
   // work items instead (192-row chunks), in the same launch as the four-tile
-  // items of the other experts (MOE_SKINNY_WIDE=0 turns this off).  The down
-  // projection does the same only on request (MOE_SKINNY_WIDE_DOWN=1): the
-  // split launch runs at two waves per SIMD where the four-tile down kernel
-  // runs at four, which measured faster on the skewed layer despite the
-  // re-read weights (182 against 196 us).
+  // items of the other experts (MOE_SKINNY_WIDE=0 turns this off; for the
+  // down projection alone MOE_SKINNY_WIDE_DOWN=0).  For the down projection
+  // the split launch runs at two waves per SIMD where the four-tile kernel
+  // alone runs at four; with only the activation fragments that hold real
+  // rows copied, the split still measured ahead on the skewed layer (167
+  // against 173 us).
   const int up_epi = swiglu ? moe::EPI_UP_SWIGLU : moe::EPI_UP_RELU;
   const int up_ct = skinny_ct(mt, i8, swiglu ? 2 : 1, "MOE_UP_CT");
   const bool wide = max_rows <= 0 && mt == 4 && up_ct == 2 && a.shared_act && !i8 && !a.topk_idx &&
@@ -500,7 +501,7 @@ int run_skinny(const moe_weights* W, const FfnIo& io, int max_rows, hipStream_t 
   }
   if (io.slices) *io.slices = rows ? a.ksplit : 1;
   const int dn_epi = io.combine && !rows ? moe::EPI_DOWN_ACC : moe::EPI_DOWN_ROWS;
-  const bool wide_dn = wide && a.ksplit == 1 && dn_ct == 2 && env_int("MOE_SKINNY_WIDE_DOWN", 0) != 0;
+  const bool wide_dn = wide && a.ksplit == 1 && dn_ct == 2 && env_int("MOE_SKINNY_WIDE_DOWN", 1) != 0;
   if (wide && !wide_dn) a.max_rows = max_rows;  // the four-tile launch serves every expert
   if (wide_dn) {
     const int W_wide = aw.W;

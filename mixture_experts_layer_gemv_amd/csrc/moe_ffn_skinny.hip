@@ -124,11 +124,62 @@ constexpr int sa_ring_units(int mt, int g, int ct, bool i8, bool sa) {
   return sa ? (plan(mt, g, ct, i8, sa).depth + 1) * mt * (i8 ? 2 : 1) : 0;
 }
 
-// One workgroup's work: logical block `bid` of a launch of `nblk` blocks (a
-// multiple of 8, dealt to the XCDs round-robin).  sa_ring: the workgroup's
-// shared-activation ring, at least sa_ring_units() KiB (unused otherwise).
+// The dispatch offsets of a launch in LDS (offs_s[0..E]): read, or derived
+// from topk_idx in every workgroup (DL then holds the histogram).
+template <int NW>
+__device__ __forceinline__ void skinny_offsets(const SkinnyArgs& A, DispatchLds<NW>& DL, int* offs_s) {
+  const int tid = threadIdx.x;
+  if (A.topk_idx) {
+    block_histogram<NW>(A.topk_idx, A.T * A.topk, A.E, DL);
+    if (tid <= A.E) offs_s[tid] = DL.offs[tid];
+  } else {
+    if (tid <= A.E) offs_s[tid] = A.offsets[tid];
+  }
+  __syncthreads();
+}
+
+// The (expert, chunk) pairs of R rows among the experts a launch admits, one
+// lane per expert (E <= 64): its chunks, the pairs before it, and the total
+// (skinny_pair's numbering, found without a serial walk over the experts).
+struct PairScan {
+  int nch, start, total;
+};
+__device__ __forceinline__ PairScan pair_scan(const SkinnyArgs& A, const int* offs_s, int R) {
+  const int lane = threadIdx.x & 63;
+  const int nch = lane < A.E ? pair_chunks(offs_s, lane, R, A.min_rows, A.max_rows) : 0;
+  int incl = nch;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int v = __shfl_up(incl, d, 64);
+    if (lane >= d) incl += v;
+  }
+  return PairScan{nch, incl - nch, __builtin_amdgcn_readlane(incl, 63)};
+}
+// Expert and chunk of pair p (uniform); false if p is past the last pair.
+__device__ __forceinline__ bool pair_find(const PairScan& ps, int p, int* e, int* chunk) {
+  const unsigned long long m = __ballot(p >= ps.start && p < ps.start + ps.nch);
+  if (m == 0) return false;
+  const int l = __builtin_amdgcn_readfirstlane(__ffsll((long long)m) - 1);
+  *e = l;
+  *chunk = p - __builtin_amdgcn_readlane(ps.start, l);
+  return true;
+}
+
+// Work items of one kind: column groups x reduction slices x pairs.
+template <bool SPLITK, int CT>
+__device__ __forceinline__ int skinny_items(const SkinnyArgs& A, const PairScan& ps) {
+  const int NG = SPLITK ? A.N / 16 / CT : skinny_groups(A.N, CT);
+  return NG * A.ksplit * ps.total;
+}
+
+// One workgroup's work: item wk (none unless `real`) over the pairs in ps.  offs_s: the offsets in LDS (skinny_offsets); publish: this
+// workgroup writes the derived dispatch (with topk_idx).  sa_ring: the
+// workgroup's shared-activation ring, at least sa_ring_units() KiB (unused
+// otherwise).
 template <int MT, int G, int CT, bool I8, int EPI, int NW, bool SPLITK, bool SA>
-__device__ __forceinline__ void skinny_body(const SkinnyArgs& A, int bid, int nblk, lds_u32x4_t* sa_ring) {
+__device__ __forceinline__ void skinny_body(const SkinnyArgs& A, const SkinnyWork& wk, bool real, const PairScan& ps,
+                                            bool publish, const int* offs_s, DispatchLds<NW>& DL,
+                                            lds_u32x4_t* sa_ring) {
   static_assert(!(SA && SPLITK), "shared activations need every wave on the same K range");
   constexpr int D = plan(MT, G, CT, I8, SA).depth;
   constexpr int R = 16 * MT;        // rows per work item
@@ -137,7 +188,9 @@ __device__ __forceinline__ void skinny_body(const SkinnyArgs& A, int bid, int nb
   // Shared activations: the NAF activation fragments of a K unit are copied
   // once per workgroup into an LDS ring of DA units (wave w copies fragments
   // w, w + NW, ...: NC of them, at most CPW; waves past NAF copy none) and
-  // every wave reads them there.
+  // every wave reads them there.  Only the fragments holding real rows are
+  // copied; the slots of the others keep stale data, which feeds only
+  // accumulator rows that are never stored.
   constexpr int NAF = MT * AH;
   constexpr int CPW = (NAF + NW - 1) / NW;  // most copies per wave per unit
   constexpr int DA = D + 1;
@@ -147,39 +200,23 @@ __device__ __forceinline__ void skinny_body(const SkinnyArgs& A, int bid, int nb
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
-  __shared__ DispatchLds<NW> DL;
-  __shared__ int offs_s[kMaxExperts + 1];
   __shared__ int rows_s[R];
 
-  // Block -> logical work index: consecutive logical indices stay on one XCD
-  // (blocks are dealt to the 8 XCDs round-robin), so the row chunks of one
-  // (expert, tile) run together and share that XCD's L2 copy of the weights.
-  const int L = xcd_logical(bid, nblk);
   const int NB = A.N / 16;  // a multiple of 4 (N is a multiple of 64)
   const int S = A.ksplit;
-  const SkinnyWork wk = skinny_work(L, A.W, S);
   // first of this wave's CT column tiles (the workgroup's, with SPLITK)
   const int ntile = SPLITK ? wk.ngroup * CT : (wk.ngroup * NW + wave) * CT;
   const int ks = wk.ks;
   const int n_assign = A.T * A.topk;
 
-  if (A.topk_idx) {
-    block_histogram<NW>(A.topk_idx, n_assign, A.E, DL);
-    if (tid <= A.E) offs_s[tid] = DL.offs[tid];
-  } else {
-    if (tid <= A.E) offs_s[tid] = A.offsets[tid];
-  }
-  __syncthreads();
-
-  // (expert, chunk) of this work item and the number of valid pairs
-  int e, chunk, npairs;
-  const bool has_pair = skinny_pair(offs_s, A.E, R, wk.pair, &e, &chunk, &npairs, A.min_rows, A.max_rows);
+  // (expert, chunk) of this work item
+  int e = 0, chunk = 0;
+  const bool has_pair = real && pair_find(ps, wk.pair, &e, &chunk);
   const bool valid = wk.ngroup * (SPLITK ? 1 : NW) * CT < NB && has_pair;
   const int row0 = valid ? offs_s[e] + chunk * R : 0;
   const int nrows = valid ? min(R, offs_s[e + 1] - row0) : 0;
 
   if (A.topk_idx) {
-    const bool publish = L == 0;
     if (publish || valid) {
       block_stable_positions<NW>(A.topk_idx, n_assign, A.E, DL, [&](int a, int ea, int pos) {
         if (publish) {
@@ -264,10 +301,12 @@ __device__ __forceinline__ void skinny_body(const SkinnyArgs& A, int bid, int nb
   const char* sa_src[CPW];
   int sa_frag[CPW];
   const uint32_t sa_lds = (uint32_t)(uintptr_t)sa_ring;
-  const int NC = wave < NAF ? (NAF - 1 - wave) / NW + 1 : 0;  // this wave's copies per unit (uniform)
+  int NC = 0;  // this wave's copies per unit (uniform)
   if constexpr (SA) {
     const int rb = __builtin_amdgcn_readfirstlane(prow0 >> 4);
     const int nfrag = __builtin_amdgcn_readfirstlane((nrows + 15) >> 4);
+    const int naf = min(NAF, nfrag * AH);  // fragments holding real rows
+    NC = wave < naf ? (naf - 1 - wave) / NW + 1 : 0;
 #pragma unroll
     for (int j = 0; j < CPW; ++j) {
       const int f = min(wave + NW * j, NAF - 1);  // (used only for j < NC)
@@ -443,17 +482,30 @@ __device__ __forceinline__ void skinny_body(const SkinnyArgs& A, int bid, int nb
   }
 }
 
+// Block b takes logical item xcd_logical(b) of the upper-bound grid (the
+// padding pairs past the last real one interleaved, so none of them is left
+// for the end of a many-round launch); block 0 publishes the derived
+// dispatch.
 template <int MT, int G, int CT, bool I8, int EPI, int NW, bool SPLITK, bool SA>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(plan(MT, G, CT, I8, SA).wpe))) void
 k_ffn_skinny(const SkinnyArgs A) {
   constexpr int units = sa_ring_units(MT, G, CT, I8, SA);
   __shared__ __attribute__((aligned(16))) u32x4_t ring[units > 0 ? units * 64 : 1];
-  skinny_body<MT, G, CT, I8, EPI, NW, SPLITK, SA>(A, blockIdx.x, gridDim.x, (lds_u32x4_t*)ring);
+  __shared__ DispatchLds<NW> DL;
+  __shared__ int offs_s[kMaxExperts + 1];
+  skinny_offsets<NW>(A, DL, offs_s);
+  const PairScan ps = pair_scan(A, offs_s, 16 * MT);
+  skinny_body<MT, G, CT, I8, EPI, NW, SPLITK, SA>(A, skinny_work(xcd_logical(blockIdx.x, gridDim.x), A.W, A.ksplit),
+                                                  true, ps, blockIdx.x == 0, offs_s, DL, (lds_u32x4_t*)ring);
 }
 
-// A projection split by expert size in one launch: blocks [0, nwide) run the
-// twelve-tile items of the experts above one four-tile chunk (first, so they
-// take CUs first), the rest the four-tile items of the others.  Both kinds
+// A projection split by expert size in one launch: the twelve-tile items of
+// the experts above one four-tile chunk and the four-tile items of the
+// others.  Every XCD starts its share of the twelve-tile items first (the
+// longest), then its four-tile items, then the grid's padding (xcd_item): a
+// launch of about one round, whose placement a padding block taking a slot
+// early would unbalance (measured: 33 CUs with one workgroup and 33 with
+// three on the skewed layer's down projection, -8 us with this order).  Both kinds
 // stream 2 KiB of weights per wave and K unit (one column tile of gate and
 // up, or two of ReLU), so the blocks are of one size and the launch's last
 // round stays short.  Both kinds share one ring allocation; the launch runs
@@ -462,14 +514,22 @@ constexpr int split_ct(int g) { return g == 2 ? 1 : 2; }
 
 template <int G, int EPI, int NW>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) void k_ffn_skinny_split(
-    const SkinnyArgs AN, const SkinnyArgs AW, int nwide) {
+    const SkinnyArgs AN, const SkinnyArgs AW) {
   constexpr int CT = split_ct(G);
   constexpr int uw = sa_ring_units(12, G, CT, false, true), un = sa_ring_units(4, G, CT, false, true);
   __shared__ __attribute__((aligned(16))) u32x4_t ring[(uw > un ? uw : un) * 64];
-  if ((int)blockIdx.x < nwide)
-    skinny_body<12, G, CT, false, EPI, NW, false, true>(AW, blockIdx.x, nwide, (lds_u32x4_t*)ring);
+  __shared__ DispatchLds<NW> DL;
+  __shared__ int offs_s[kMaxExperts + 1];
+  skinny_offsets<NW>(AN, DL, offs_s);  // (packed rows: read, never derived)
+  const PairScan pw = pair_scan(AW, offs_s, 16 * 12), pn = pair_scan(AN, offs_s, 16 * 4);
+  const int nw = skinny_items<false, CT>(AW, pw), nn = skinny_items<false, CT>(AN, pn);
+  const int item = xcd_item(blockIdx.x, nw, nn);
+  if (item >= 0 && item < nw)
+    skinny_body<12, G, CT, false, EPI, NW, false, true>(AW, skinny_work(item, max(pw.total, 1), 1), true, pw, false, offs_s,
+                                                        DL, (lds_u32x4_t*)ring);
   else
-    skinny_body<4, G, CT, false, EPI, NW, false, true>(AN, blockIdx.x - nwide, gridDim.x - nwide, (lds_u32x4_t*)ring);
+    skinny_body<4, G, CT, false, EPI, NW, false, true>(AN, skinny_work(item < 0 ? 0 : item - nw, max(pn.total, 1), 1),
+                                                       item >= 0, pn, false, offs_s, DL, (lds_u32x4_t*)ring);
 }
 
 // One variant; variants whose accumulators exceed the register budget are
@@ -545,6 +605,7 @@ hipError_t launch_ffn_skinny_split(const SkinnyArgs& narrow, const SkinnyArgs& w
   if (narrow.ksplit != 1 || wide.ksplit != 1) return hipErrorInvalidValue;
   const int G = epi == EPI_UP_SWIGLU ? 2 : 1;
   constexpr int NW = 4;  // (8 waves sharing one ring measured slower on the skewed layer)
+  // each kind's upper bound on items, rounded up per XCD (xcd_item)
   auto blocks = [&](const SkinnyArgs& x, int ct) {
     const int tiles = NW * ct;
     const long long work = (long long)((x.N / 16 + tiles - 1) / tiles) * x.W;
@@ -554,10 +615,10 @@ hipError_t launch_ffn_skinny_split(const SkinnyArgs& narrow, const SkinnyArgs& w
   if (nw + nn > 0x7FFFFFF0LL) return hipErrorInvalidValue;
   const dim3 grid((unsigned)(nw + nn));
   switch (epi) {
-    case EPI_UP_SWIGLU: k_ffn_skinny_split<2, EPI_UP_SWIGLU, NW><<<grid, NW * 64, 0, s>>>(narrow, wide, (int)nw); break;
-    case EPI_UP_RELU: k_ffn_skinny_split<1, EPI_UP_RELU, NW><<<grid, NW * 64, 0, s>>>(narrow, wide, (int)nw); break;
-    case EPI_DOWN_ACC: k_ffn_skinny_split<1, EPI_DOWN_ACC, NW><<<grid, NW * 64, 0, s>>>(narrow, wide, (int)nw); break;
-    default: k_ffn_skinny_split<1, EPI_DOWN_ROWS, NW><<<grid, NW * 64, 0, s>>>(narrow, wide, (int)nw); break;
+    case EPI_UP_SWIGLU: k_ffn_skinny_split<2, EPI_UP_SWIGLU, NW><<<grid, NW * 64, 0, s>>>(narrow, wide); break;
+    case EPI_UP_RELU: k_ffn_skinny_split<1, EPI_UP_RELU, NW><<<grid, NW * 64, 0, s>>>(narrow, wide); break;
+    case EPI_DOWN_ACC: k_ffn_skinny_split<1, EPI_DOWN_ACC, NW><<<grid, NW * 64, 0, s>>>(narrow, wide); break;
+    default: k_ffn_skinny_split<1, EPI_DOWN_ROWS, NW><<<grid, NW * 64, 0, s>>>(narrow, wide); break;
   }
   return hipGetLastError();
 }

@@ -11,11 +11,30 @@
 
 namespace moe {
 
-// Workgroups are dealt to the 8 XCDs round-robin (b -> XCD b % 8).  This
-// renumbering gives each XCD a contiguous range of logical indices, so work
-// items with neighbouring logical indices share that XCD's L2.
-// nblk must be a multiple of 8.
+// Workgroups are dealt to the 8 XCDs round-robin (blocks b with one value of
+// b % 8 run on one XCD).  This renumbering gives each XCD a contiguous range
+// of logical indices, so work items with neighbouring logical indices share
+// that XCD's L2.  nblk must be a multiple of 8.
 MOE_HD inline int xcd_logical(int b, int nblk) { return (b & 7) * (nblk >> 3) + (b >> 3); }
+
+// The same for launches whose grid is an upper bound on the work: n0 items of
+// kind 0 and n1 of kind 1 (known only on the device), each kind's range cut
+// into 8 contiguous parts, one per XCD.  The XCD's j-th block (b = 8 j + x)
+// takes its part of kind 0, then its part of kind 1, then is padding (-1):
+// in dispatch order every XCD starts all its real items before any padding
+// block, so padding never holds a slot that a real item is waiting for.
+// Items n0.. are kind 1.  Over all blocks of a grid with at least
+// ceil(n0 / 8) + ceil(n1 / 8) blocks per XCD every item comes out exactly
+// once.
+MOE_HD inline int xcd_item(int b, int n0, int n1) {
+  const int x = b & 7;
+  const unsigned j = (unsigned)b >> 3;
+  const int a0 = (int)((long long)x * n0 / 8), b0 = (int)((long long)(x + 1) * n0 / 8);
+  const int a1 = (int)((long long)x * n1 / 8), b1 = (int)((long long)(x + 1) * n1 / 8);
+  if (j < (unsigned)(b0 - a0)) return a0 + (int)j;
+  if (j < (unsigned)(b0 - a0 + b1 - a1)) return n0 + a1 + (int)(j - (unsigned)(b0 - a0));
+  return -1;
+}
 
 // Logical index -> (column-tile group, reduction slice, (expert, chunk) pair),
 // pair fastest, for W pairs and S slices per group.
@@ -38,6 +57,15 @@ MOE_HD inline SkinnyWork skinny_work(int L, int W, int S) {
 // tiles are either all below N/16 or all past it.
 MOE_HD inline int skinny_groups(int N, int CT) { return (N / 16 + 4 * CT - 1) / (4 * CT); }
 
+// Row chunks of expert e admitted by the window (min_rows, max_rows] (a bound
+// <= 0 is absent): the pairs skinny_pair counts for e.  The kernels give each
+// expert a lane and take a prefix sum of these across the wave.
+MOE_HD inline int pair_chunks(const int* offsets, int e, int R, int min_rows = 0, int max_rows = 0) {
+  const int cnt = offsets[e + 1] - offsets[e];
+  const bool in = (min_rows <= 0 || cnt > min_rows) && (max_rows <= 0 || cnt <= max_rows);
+  return in ? (cnt + R - 1) / R : 0;
+}
+
 // The pair-th (expert, row chunk) in expert order, chunks of R rows, given
 // dispatch offsets[0..E], counting only experts whose row count lies in
 // (min_rows, max_rows] (a bound <= 0 is absent).  Returns false when pair is
@@ -48,9 +76,7 @@ MOE_HD inline bool skinny_pair(const int* offsets, int E, int R, int pair, int* 
   *e = -1;
   *chunk = 0;
   for (int i = 0; i < E; ++i) {
-    const int cnt = offsets[i + 1] - offsets[i];
-    const bool in = (min_rows <= 0 || cnt > min_rows) && (max_rows <= 0 || cnt <= max_rows);
-    const int nch = in ? (cnt + R - 1) / R : 0;
+    const int nch = pair_chunks(offsets, i, R, min_rows, max_rows);
     if (*e < 0 && pair >= n && pair < n + nch) {
       *e = i;
       *chunk = pair - n;

@@ -1,5 +1,6 @@
 // Exhaustive host check of the decode FFN launch's index arithmetic
 // (moe_index.hpp, the same code the kernel runs).  Exit status 0 = pass.
+#include <algorithm>
 #include <cstdio>
 #include <cstdlib>
 #include <random>
@@ -22,33 +23,99 @@ static int fails = 0;
     }                                         \
   } while (0)
 
-// One launch: NG column groups x S slices x W pairs, grid padded to 8, over
-// the experts whose row count lies in (min_rows, max_rows].  Returns the rows
-// served per expert (from column group 0, slice 0).
-static std::vector<std::vector<int>> check_launch(int NG, int W, int S, const std::vector<int>& offsets, int R,
-                                                  int min_rows = 0, int max_rows = 0) {
+// The kernels number (expert, chunk) pairs with one lane per expert: lane e
+// holds pair_chunks(e), the pairs before it are the prefix sum, and pair p
+// belongs to the lane whose [start, start + chunks) holds it.  That must be
+// skinny_pair's numbering, for every pair and the total.
+static void check_pair_scan(const std::vector<int>& offsets, int R, int min_rows, int max_rows) {
   const int E = (int)offsets.size() - 1;
-  const long long work = (long long)NG * W * S;
-  const int nblk = (int)((work + 7) / 8 * 8);
-  std::set<int> logical;
-  std::set<std::tuple<int, int, int>> items;
+  std::vector<int> nch(64, 0), start(64, 0);
+  int total = 0;
+  for (int l = 0; l < 64; ++l) {
+    nch[l] = l < E ? moe::pair_chunks(offsets.data(), l, R, min_rows, max_rows) : 0;
+    start[l] = total;
+    total += nch[l];
+  }
+  int e, chunk, np;
+  moe::skinny_pair(offsets.data(), E, R, 0, &e, &chunk, &np, min_rows, max_rows);
+  CHECK(total == np, "pair scan total %d != %d", total, np);
+  for (int p = 0; p <= total; ++p) {
+    int le = -1;
+    for (int l = 0; l < 64; ++l)
+      if (p >= start[l] && p < start[l] + nch[l]) {
+        le = l;
+        break;
+      }
+    const bool ok = moe::skinny_pair(offsets.data(), E, R, p, &e, &chunk, &np, min_rows, max_rows);
+    CHECK(ok == (le >= 0), "pair %d: found %d vs %d", p, le >= 0, ok);
+    if (ok && le >= 0) CHECK(le == e && p - start[le] == chunk, "pair %d: (%d,%d) vs (%d,%d)", p, le, p - start[le], e, chunk);
+  }
+}
+
+// One kind of decode work item: NG column groups x S slices x pairs of R-row
+// chunks over the experts whose row count lies in (min_rows, max_rows]; W is
+// the host's upper bound on the pairs.
+struct Kind {
+  int NG, W, S, R, min_rows, max_rows;
+};
+
+// A decode launch of nblk blocks over kind k1, after kind k0 (the split
+// launch's twelve-tile items) when given, as the kernels map blocks: the
+// split launch (`real_first`) takes the pair counts derived from the offsets,
+// then xcd_item and skinny_work; the one-kind launch renumbers blocks with
+// xcd_logical and decodes the upper-bound grid with skinny_work, past pairs
+// and column groups being padding.  Checks that every item comes out of
+// exactly one block, that (real_first) on every XCD no real item follows a
+// padding block in dispatch order, that each item's rows and packed fragments
+// stay inside its expert, and returns the rows served per expert (from column
+// group 0, slice 0).
+static std::vector<std::vector<int>> check_grid(int nblk, const Kind* k0, const Kind& k1,
+                                                const std::vector<int>& offsets, bool real_first) {
+  const int E = (int)offsets.size() - 1;
+  if (k0) check_pair_scan(offsets, k0->R, k0->min_rows, k0->max_rows);
+  check_pair_scan(offsets, k1.R, k1.min_rows, k1.max_rows);
+  int e, chunk, np0 = 0, np1 = 0;
+  if (k0) moe::skinny_pair(offsets.data(), E, k0->R, 0, &e, &chunk, &np0, k0->min_rows, k0->max_rows);
+  moe::skinny_pair(offsets.data(), E, k1.R, 0, &e, &chunk, &np1, k1.min_rows, k1.max_rows);
+  CHECK(np0 <= (k0 ? k0->W : 0) && np1 <= k1.W, "pairs %d/%d above the bounds", np0, np1);
+  const int n0 = k0 ? k0->NG * k0->S * np0 : 0, n1 = k1.NG * k1.S * np1;
+  CHECK(nblk % 8 == 0, "grid %d", nblk);
+  std::vector<int> taken(n0 + n1, 0);
+  std::vector<bool> padded(8, false);
   std::vector<std::vector<int>> rows_seen(E);
   for (int b = 0; b < nblk; ++b) {
-    const int L = moe::xcd_logical(b, nblk);
-    CHECK(L >= 0 && L < nblk, "b=%d L=%d nblk=%d", b, L, nblk);
-    logical.insert(L);
-    const moe::SkinnyWork w = moe::skinny_work(L, W, S);
-    CHECK(w.ks >= 0 && w.ks < S && w.pair >= 0 && w.pair < W && w.ngroup >= 0, "L=%d -> (%d,%d,%d)", L, w.ngroup,
-          w.ks, w.pair);
-    if (w.ngroup >= NG) continue;  // padding block
-    CHECK(items.insert({w.ngroup, w.ks, w.pair}).second, "duplicate item L=%d", L);
-    int e, chunk, npairs;
-    const bool ok = moe::skinny_pair(offsets.data(), E, R, w.pair, &e, &chunk, &npairs, min_rows, max_rows);
-    CHECK(npairs <= W, "npairs %d > W %d", npairs, W);
+    int it;
+    if (real_first) {
+      it = moe::xcd_item(b, n0, n1);
+    } else {
+      CHECK(!k0, "the one-kind launch has no kind 0");
+      const int L = moe::xcd_logical(b, nblk);
+      CHECK(L >= 0 && L < nblk, "b=%d L=%d nblk=%d", b, L, nblk);
+      const moe::SkinnyWork w = moe::skinny_work(L, k1.W, k1.S);
+      // real items, in the numbering skinny_work(item, np1, S) decodes
+      it = w.ngroup < k1.NG && w.pair < np1 ? (w.ngroup * k1.S + w.ks) * np1 + w.pair : -1;
+    }
+    if (it < 0) {
+      padded[b & 7] = true;
+      continue;
+    }
+    CHECK(!real_first || !padded[b & 7], "block %d: a real item after padding on XCD %d", b, b & 7);
+    CHECK(it < n0 + n1, "block %d: item %d of %d", b, it, n0 + n1);
+    if (it >= n0 + n1) continue;
+    taken[it]++;
+    const bool first = it < n0;
+    const Kind& k = first ? *k0 : k1;
+    const int np = first ? np0 : np1;
+    const moe::SkinnyWork w = moe::skinny_work(first ? it : it - n0, np, k.S);
+    CHECK(w.ngroup >= 0 && w.ngroup < k.NG && w.ks >= 0 && w.ks < k.S && w.pair >= 0 && w.pair < np,
+          "item %d -> (%d,%d,%d)", it, w.ngroup, w.ks, w.pair);
+    int npairs;
+    const bool ok = moe::skinny_pair(offsets.data(), E, k.R, w.pair, &e, &chunk, &npairs, k.min_rows, k.max_rows);
+    CHECK(ok && npairs == np, "item %d: pair %d invalid", it, w.pair);
     if (!ok) continue;
     CHECK(e >= 0 && e < E && chunk >= 0, "pair %d -> e=%d chunk=%d", w.pair, e, chunk);
-    const int row0 = offsets[e] + chunk * R;
-    const int nrows = std::min(R, offsets[e + 1] - row0);
+    const int row0 = offsets[e] + chunk * k.R;
+    const int nrows = std::min(k.R, offsets[e + 1] - row0);
     CHECK(nrows >= 1 && row0 >= offsets[e] && row0 + nrows <= offsets[e + 1], "rows [%d,+%d) outside expert %d",
           row0, nrows, e);
     // packed activations: M tile mt reads fragment row prow0/16 + min(mt, nfrag-1),
@@ -57,10 +124,10 @@ static std::vector<std::vector<int>> check_launch(int NG, int W, int S, const st
     {
       const int pe = moe::padded_offset(offsets.data(), e);
       const int pe_end = pe + ((offsets[e + 1] - offsets[e] + 15) & ~15);
-      const int prow0 = pe + chunk * R;
+      const int prow0 = pe + chunk * k.R;
       const int nfrag = (nrows + 15) >> 4;
       CHECK(prow0 % 16 == 0, "skinny prow0 %d", prow0);
-      for (int mt = 0; mt < R / 16; ++mt) {
+      for (int mt = 0; mt < k.R / 16; ++mt) {
         const int rb = (prow0 >> 4) + std::min(mt, nfrag - 1);
         CHECK(rb * 16 >= pe && rb * 16 + 16 <= pe_end, "skinny A fragment %d outside expert %d", rb, e);
       }
@@ -70,11 +137,21 @@ static std::vector<std::vector<int>> check_launch(int NG, int W, int S, const st
     if (w.ngroup == 0 && w.ks == 0)
       for (int r = row0; r < row0 + nrows; ++r) rows_seen[e].push_back(r);
   }
-  CHECK((int)logical.size() == nblk, "xcd_logical not a bijection (nblk=%d)", nblk);
-  CHECK((long long)items.size() == work, "items %zu != %lld", items.size(), work);
+  for (int i = 0; i < n0 + n1; ++i) CHECK(taken[i] == 1, "item %d taken %d times (grid %d)", i, taken[i], nblk);
+  for (int q = 0; q < E; ++q) std::sort(rows_seen[q].begin(), rows_seen[q].end());
+  return rows_seen;
+}
+
+// One launch of one kind, grid = the host's bound rounded up to 8.  Every
+// expert inside the window has each of its rows served once.
+static std::vector<std::vector<int>> check_launch(int NG, int W, int S, const std::vector<int>& offsets, int R,
+                                                  int min_rows = 0, int max_rows = 0) {
+  const int E = (int)offsets.size() - 1;
+  const long long work = (long long)NG * W * S;
+  const int nblk = (int)((work + 7) / 8 * 8);
+  const auto rows_seen = check_grid(nblk, nullptr, Kind{NG, W, S, R, min_rows, max_rows}, offsets, false);
   for (int e = 0; e < E; ++e) {
-    std::vector<int>& v = rows_seen[e];
-    std::sort(v.begin(), v.end());
+    const std::vector<int>& v = rows_seen[e];
     const int cnt = offsets[e + 1] - offsets[e];
     const bool in = (min_rows <= 0 || cnt > min_rows) && (max_rows <= 0 || cnt <= max_rows);
     CHECK((int)v.size() == (in ? cnt : 0), "expert %d (%d rows, window (%d,%d]) rows covered %zu", e, cnt, min_rows,
@@ -86,16 +163,21 @@ static std::vector<std::vector<int>> check_launch(int NG, int W, int S, const st
 
 // The split decode launch: experts with at most `hot` rows in chunks of 64
 // (4 M tiles), the others in chunks of 192 (12 M tiles), with the host's
-// pair-slot bounds; together they serve every row exactly once.
-static void check_split(int N, const std::vector<int>& offsets, int hot) {
+// pair-slot bounds and grid (each kind's bound rounded up to 8); together
+// they serve every row exactly once.
+static void check_split(int N, const std::vector<int>& offsets, int hot, int ct) {
   const int E = (int)offsets.size() - 1, n = offsets[E];
   const int Wn = E + n / 64;
   const int Ww = n / 192 + n / (hot + 1) + 1;
-  const auto a = check_launch(moe::skinny_groups(N, 2), Wn, 1, offsets, 64, 0, hot);
-  const auto b = check_launch(moe::skinny_groups(N, 1), Ww, 1, offsets, 192, hot, 0);
-  for (int e = 0; e < E; ++e)
-    CHECK((int)(a[e].size() + b[e].size()) == offsets[e + 1] - offsets[e], "split: expert %d served %zu + %zu rows",
-          e, a[e].size(), b[e].size());
+  const Kind kw{moe::skinny_groups(N, ct), Ww, 1, 192, hot, 0}, kn{moe::skinny_groups(N, ct), Wn, 1, 64, 0, hot};
+  auto round8 = [](long long v) { return (int)((v + 7) / 8 * 8); };
+  const int nblk = round8((long long)kw.NG * kw.W) + round8((long long)kn.NG * kn.W);
+  const auto rows = check_grid(nblk, &kw, kn, offsets, true);
+  for (int e = 0; e < E; ++e) {
+    CHECK((int)rows[e].size() == offsets[e + 1] - offsets[e], "split: expert %d served %zu of %d rows", e,
+          rows[e].size(), offsets[e + 1] - offsets[e]);
+    for (size_t i = 0; i < rows[e].size(); ++i) CHECK(rows[e][i] == offsets[e] + (int)i, "split: expert %d row %zu", e, i);
+  }
 }
 
 // Grouped GEMM launch over packed operands: 256-row blocks, 2 x 4 waves of
@@ -319,7 +401,7 @@ int main() {
       const double r = std::uniform_real_distribution<double>(0.0, 1.0)(rng);
       counts[std::min(E - 1, (int)(E * r * r * r))]++;
     }
-    check_split(64 * (1 + (int)(rng() % 200)), offsets_from(counts), 64);
+    check_split(64 * (1 + (int)(rng() % 200)), offsets_from(counts), 64, 1 + (int)(rng() % 2));
   }
   // grouped GEMM: the measured prefill layer (T=8192, top-2 of 8) and
   // random small shapes with ragged and empty experts

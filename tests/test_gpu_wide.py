@@ -2,13 +2,13 @@
 
 With four M tiles and packed, shared activations, experts holding more than
 one 64-row chunk are served by twelve-tile work items (192-row chunks) in the
-same launch as the four-tile items of the others: always for the up
-projection, on request (MOE_SKINNY_WIDE_DOWN=1) for the down projection.
+same launch as the four-tile items of the others: for both projections by
+default; MOE_SKINNY_WIDE_DOWN=0 keeps the down projection on four-tile items.
 The cases force hot experts of every size class: 65..192 rows (one wide
 chunk, ragged), several
 wide chunks (over 192 rows), a mix of hot and cold experts, and none hot;
-for the layer (weighted combine by atomics) and the expert-FFN stage
-(unweighted rows), SwiGLU and ReLU.  Bars as in the other parity tests.
+for the layer (unweighted rows and the combine kernel) and the expert-FFN
+stage (unweighted rows), SwiGLU and ReLU.  Bars as in the other parity tests.
 """
 import numpy as np
 import pytest
@@ -64,7 +64,7 @@ def _layer(T, m, p, E, k, bias, kind, seed):
 @pytest.mark.parametrize("kind", ["swiglu", "relu"])
 @pytest.mark.parametrize("T,m,p,E,k,bias", CASES)
 def test_wide_layer(kind, T, m, p, E, k, bias, down, monkeypatch):
-    """down=1 also splits the down projection (opt-in)."""
+    """down=0 keeps the down projection on four-tile items."""
     monkeypatch.setenv("MOE_SKINNY_WIDE_DOWN", down)
     log(f"wide layer kind={kind} down={down} T={T} m={m} p={p} E={E} k={k} bias={bias}")
     L = _layer(T, m, p, E, k, bias, kind, seed=T + p)
@@ -108,7 +108,7 @@ def test_wide_expert_ffn_stage(kind, hot, down, monkeypatch):
 
 def test_wide_matches_narrow(monkeypatch):
     """The split launch and the four-tile kernel alone agree to fp32 rounding
-    (the atomic combine makes the order of additions vary)."""
+    (the two group a row's products into different accumulation orders)."""
     L = _layer(300, 128, 384, 6, 2, {0: 50.0, 3: 0.5}, "swiglu", seed=5)
     layer = MoELayer(L)
     y_split = layer.forward().float().clone()
