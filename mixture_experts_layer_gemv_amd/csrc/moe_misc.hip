@@ -57,13 +57,21 @@ __global__ __launch_bounds__(256) void k_pack_i8(const int8_t* __restrict__ src,
 //
 // True fp32 arithmetic (one fused multiply-add per term, in increasing k) for
 // fp32 layers.  Block = (expert, 16-row chunk) x 256 output columns; each
-// thread owns one column and up to 16 rows.
+// thread owns one column and up to 16 rows.  The chunk's activation rows are
+// staged in LDS, kKc columns at a time (rows past the chunk's last are zero
+// and never stored), so the k loop issues only the weight loads, unrolled to
+// keep several in flight.
 
 __device__ __forceinline__ float silu_f(float z) { return z / (1.0f + expf(-z)); }
 
+constexpr int kF32Rows = 16;
+constexpr int kKc = 256;  // staged activation columns per round (16 KiB)
+
 template <int EPI>
 __global__ __launch_bounds__(256) void k_ffn_f32(const F32Args A) {
-  constexpr int R = 16;
+  constexpr int R = kF32Rows;
+  __shared__ float xs[R][kKc];
+  __shared__ int src_s[R];
   int e = -1, chunk = 0;
   {
     int rem = blockIdx.x;
@@ -79,35 +87,44 @@ __global__ __launch_bounds__(256) void k_ffn_f32(const F32Args A) {
     }
   }
   if (e < 0) return;
-  const int n = blockIdx.y * 256 + threadIdx.x;
-  if (n >= A.N) return;
+  const int tid = threadIdx.x;
+  const int n = blockIdx.y * 256 + tid;
+  const bool col = n < A.N;
   const int row0 = A.offsets[e] + chunk * R;
   const int nrows = min(R, A.offsets[e + 1] - row0);
-  const float* src[R];
-#pragma unroll
-  for (int r = 0; r < R; ++r) {
-    int s = 0;
-    if (r < nrows) s = A.gather ? A.perm[row0 + r] / A.topk : row0 + r;
-    src[r] = A.act + (size_t)s * A.K;
-  }
+  if (tid < R) src_s[tid] = tid < nrows ? (A.gather ? A.perm[row0 + tid] / A.topk : row0 + tid) : -1;
+  __syncthreads();
   constexpr bool GATED = EPI == EPI_UP_SWIGLU;
   float acc1[R], acc3[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) acc1[r] = acc3[r] = 0.0f;
-  const float* w1 = A.w1 + (size_t)e * A.K * A.N + n;
-  const float* w3 = GATED ? A.w3 + (size_t)e * A.K * A.N + n : nullptr;
-  for (int kk = 0; kk < A.K; ++kk) {
-    const float a1 = w1[(size_t)kk * A.N];
-    const float a3 = GATED ? w3[(size_t)kk * A.N] : 0.0f;
+  const float* w1 = A.w1 + (size_t)e * A.K * A.N + (col ? n : 0);
+  const float* w3 = GATED ? A.w3 + (size_t)e * A.K * A.N + (col ? n : 0) : nullptr;
+  for (int k0 = 0; k0 < A.K; k0 += kKc) {
+    const int kc = min(kKc, A.K - k0);
+    // stage rows x columns [k0, k0 + kc) (zeros past the chunk's rows)
+    for (int q = tid; q < R * kKc; q += 256) {
+      const int r = q / kKc, c = q - r * kKc;
+      const int sr = src_s[r];
+      xs[r][c] = sr >= 0 && c < kc ? A.act[(size_t)sr * A.K + k0 + c] : 0.0f;
+    }
+    __syncthreads();
+    if (col) {
+#pragma unroll 8
+      for (int kk = 0; kk < kc; ++kk) {
+        const float a1 = w1[(size_t)(k0 + kk) * A.N];
+        const float a3 = GATED ? w3[(size_t)(k0 + kk) * A.N] : 0.0f;
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-      if (r < nrows) {
-        const float xv = src[r][kk];
-        acc1[r] = fmaf(xv, a1, acc1[r]);
-        if (GATED) acc3[r] = fmaf(xv, a3, acc3[r]);
+        for (int r = 0; r < R; ++r) {
+          const float xv = xs[r][kk];
+          acc1[r] = fmaf(xv, a1, acc1[r]);
+          if (GATED) acc3[r] = fmaf(xv, a3, acc3[r]);
+        }
       }
     }
+    __syncthreads();
   }
+  if (!col) return;
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     if (r >= nrows) continue;
