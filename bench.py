@@ -158,6 +158,21 @@ def main():
     torch.cuda.synchronize()
     ms = ev0.elapsed_time(ev1) / args.steps
 
+    # The same K steps replayed from a HIP graph of the forward
+    # (moe_layer_graph_create: the launches recorded once, one graph launch
+    # per step), on the same stream between the same kind of events.
+    g, _ = layer.capture(y=y)
+    for _ in range(3):
+        M.moe_graph_launch(g)
+    torch.cuda.synchronize()
+    ev0.record()
+    for _ in range(args.steps):
+        M.moe_graph_launch(g)
+    ev1.record()
+    torch.cuda.synchronize()
+    ms_graph = ev0.elapsed_time(ev1) / args.steps
+    M.moe_graph_destroy(g)
+
     # Kernel timing: K more steps in which the library brackets every launch
     # with HIP events recorded on the stream the kernel runs on.  (The events
     # add small gaps between launches, so the step time above is taken
@@ -213,6 +228,7 @@ def main():
         "warmup": args.warmup,
         "ms_per_step": round(ms, 5),
         "ms_per_step_with_kernel_events": round(ms_events, 5),
+        "graph": {"ms_per_step": round(ms_graph, 5), "value": round(sp.T / (ms_graph * 1e-3), 2)},
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

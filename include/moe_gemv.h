@@ -186,6 +186,32 @@ int moe_layer_forward(const moe_weights* w, const float* w_router, const float* 
                       int32_t* dbg_offsets, int32_t* dbg_perm, void* stream);
 
 /*
+ * moe_layer_graph_create / moe_graph_launch / moe_graph_destroy -- the layer
+ * forward captured once into a HIP graph and replayed with one launch (the
+ * CUDA-Graph capture of the DeepSpeed-Inference summary, section 4, as HIP
+ * graphs).  moe_layer_graph_create records exactly the launches
+ * moe_layer_forward makes for these arguments (same meaning as there; no
+ * dbg outputs) on a capture stream of its own; nothing runs until a launch.
+ * The graph holds the pointers, sizes and launch shapes: each
+ * moe_graph_launch recomputes y from whatever x, router and expert weights
+ * then hold, on `stream` (NULL: the default stream), with no host
+ * synchronisation.  The caller keeps x, y, the workspace and the weights
+ * alive and unmoved while the graph exists, and must not run two launches of
+ * one graph (or a launch and moe_layer_forward on the same workspace) at the
+ * same time.  Shapes, dtypes or T need a new graph.  *out receives the handle
+ * (NULL on error); destroy frees it.  Capture is refused while
+ * moe_profile_begin is active.
+ * Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE, HIP (as moe_layer_forward),
+ * OOM.
+ */
+typedef struct moe_graph moe_graph;
+int moe_layer_graph_create(const moe_weights* w, const float* w_router, const float* b_router, const void* x,
+                           int x_dtype, int T, int m, int p, int E, int k, void* y, int y_dtype, void* workspace,
+                           size_t ws_bytes, moe_graph** out);
+int moe_graph_launch(const moe_graph* g, void* stream);
+int moe_graph_destroy(moe_graph* g);
+
+/*
  * Measurement aid (not part of the layer).  Between moe_profile_begin and
  * moe_profile_end every kernel the library launches is bracketed by HIP
  * events on its own stream.  moe_profile_end waits for the last event and

@@ -49,6 +49,10 @@ _SIGS = {
     "moe_combine": ([_vp, _vp, _vp, _i32, _i32, _i32, _vp, _i32, _vp], _i32),
     "moe_layer_forward": ([_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _i32, _vp, _sz,
                            _vp, _vp, _vp, _vp, _vp, _vp, _vp], _i32),
+    "moe_layer_graph_create": ([_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _i32, _vp, _sz,
+                                ctypes.POINTER(_vp)], _i32),
+    "moe_graph_launch": ([_vp, _vp], _i32),
+    "moe_graph_destroy": ([_vp], _i32),
     "moe_profile_begin": ([_i32], _i32),
     "moe_profile_end": ([], _i32),
     "moe_profile_query": ([ctypes.c_char_p, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_i32)], _i32),
@@ -146,6 +150,23 @@ def moe_layer_forward(w, w_router, b_router, x, x_dtype, T, m, p, E, k, y, y_dty
         w, _p(w_router), _p(b_router), _p(x), x_dtype, T, m, p, E, k, _p(y), y_dtype, _p(workspace), ws_bytes,
         _p(dbg_topk_idx), _p(dbg_topk_w), _p(dbg_logits), _p(dbg_counts), _p(dbg_offsets), _p(dbg_perm),
         _s(stream)))
+
+
+def moe_layer_graph_create(w, w_router, b_router, x, x_dtype, T, m, p, E, k, y, y_dtype, workspace, ws_bytes):
+    """Returns the graph handle (an int)."""
+    g = _vp()
+    _check("moe_layer_graph_create", lib().moe_layer_graph_create(
+        w, _p(w_router), _p(b_router), _p(x), x_dtype, T, m, p, E, k, _p(y), y_dtype, _p(workspace), ws_bytes,
+        ctypes.byref(g)))
+    return g.value
+
+
+def moe_graph_launch(g, stream=None):
+    _check("moe_graph_launch", lib().moe_graph_launch(g, _s(stream)))
+
+
+def moe_graph_destroy(g):
+    _check("moe_graph_destroy", lib().moe_graph_destroy(g))
 
 
 def moe_profile_begin(max_launches: int):

@@ -9,6 +9,7 @@
 #include <cstdlib>
 #include <map>
 #include <mutex>
+#include <new>
 #include <string>
 #include <vector>
 
@@ -861,6 +862,79 @@ int moe_layer_forward(const moe_weights* w, const float* w_router, const float* 
   }
   if (y_bf16)
     MOE_TRY_HIP(run("finalize", s, [&] { return moe::launch_f32_to_bf16(yacc, static_cast<uint16_t*>(y), ny, s); }));
+  return ok();
+}
+
+}  // extern "C"
+
+struct moe_graph {
+  hipGraph_t graph;
+  hipGraphExec_t exec;  // null for a forward with no launches (T = 0)
+};
+
+extern "C" {
+
+int moe_layer_graph_create(const moe_weights* w, const float* w_router, const float* b_router, const void* x,
+                           int x_dtype, int T, int m, int p, int E, int k, void* y, int y_dtype, void* workspace,
+                           size_t ws_bytes, moe_graph** out) {
+  if (!out) return fail(MOE_ERR_INVALID_ARG, "out is NULL");
+  *out = nullptr;
+  {
+    std::lock_guard<std::mutex> lk(g_prof.mu);
+    if (g_prof.on) return fail(MOE_ERR_INVALID_ARG, "cannot capture while moe_profile_begin is active");
+  }
+  hipStream_t cs = nullptr;
+  MOE_TRY_HIP(hipStreamCreateWithFlags(&cs, hipStreamNonBlocking));
+  hipError_t e = hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal);
+  if (e != hipSuccess) {
+    (void)hipStreamDestroy(cs);
+    return fail(MOE_ERR_HIP, "hipStreamBeginCapture: %s", hipGetErrorString(e));
+  }
+  const int rc = moe_layer_forward(w, w_router, b_router, x, x_dtype, T, m, p, E, k, y, y_dtype, workspace,
+                                   ws_bytes, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, cs);
+  const std::string err = rc ? g_err : std::string();
+  hipGraph_t graph = nullptr;
+  e = hipStreamEndCapture(cs, &graph);  // ends the capture even after a failed forward
+  (void)hipStreamDestroy(cs);
+  if (rc) {
+    if (graph) (void)hipGraphDestroy(graph);
+    g_err = err;
+    return rc;
+  }
+  if (e != hipSuccess || !graph) return fail(MOE_ERR_HIP, "hipStreamEndCapture: %s", hipGetErrorString(e));
+  size_t nodes = 0;
+  e = hipGraphGetNodes(graph, nullptr, &nodes);
+  hipGraphExec_t exec = nullptr;
+  if (e == hipSuccess && nodes > 0) e = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
+  if (e != hipSuccess) {
+    (void)hipGraphDestroy(graph);
+    return fail(MOE_ERR_HIP, "graph instantiation: %s", hipGetErrorString(e));
+  }
+  moe_graph* g = new (std::nothrow) moe_graph{graph, exec};
+  if (!g) {
+    if (exec) (void)hipGraphExecDestroy(exec);
+    (void)hipGraphDestroy(graph);
+    return fail(MOE_ERR_OOM, "graph handle allocation failed");
+  }
+  *out = g;
+  return ok();
+}
+
+int moe_graph_launch(const moe_graph* g, void* stream) {
+  if (!g) return fail(MOE_ERR_INVALID_ARG, "graph is NULL");
+  if (!g->exec) return ok();
+  MOE_TRY_HIP(hipGraphLaunch(g->exec, as_stream(stream)));
+  return ok();
+}
+
+int moe_graph_destroy(moe_graph* g) {
+  if (!g) return ok();
+  hipError_t e = hipSuccess;
+  if (g->exec) e = hipGraphExecDestroy(g->exec);
+  const hipError_t e2 = hipGraphDestroy(g->graph);
+  delete g;
+  if (e != hipSuccess || e2 != hipSuccess)
+    return fail(MOE_ERR_HIP, "graph destruction: %s", hipGetErrorString(e != hipSuccess ? e : e2));
   return ok();
 }
 

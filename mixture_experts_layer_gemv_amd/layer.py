@@ -8,8 +8,8 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-from . import (MOE_BF16, MOE_F32, MOE_I8, MOE_MLP_RELU, MOE_SWIGLU, moe_layer_forward, moe_weights_create,
-               moe_weights_destroy, moe_workspace_size)
+from . import (MOE_BF16, MOE_F32, MOE_I8, MOE_MLP_RELU, MOE_SWIGLU, moe_layer_forward, moe_layer_graph_create,
+               moe_weights_create, moe_weights_destroy, moe_workspace_size)
 
 DTYPE_CODE = {"f32": MOE_F32, "bf16": MOE_BF16, "i8": MOE_I8}
 KIND_CODE = {"relu": MOE_MLP_RELU, "swiglu": MOE_SWIGLU}
@@ -68,6 +68,18 @@ class MoELayer:
                           self.y_dtype, ws, self.ws_bytes, dbg.get("topk_idx"), dbg.get("topk_w"),
                           dbg.get("logits"), dbg.get("counts"), dbg.get("offsets"), dbg.get("perm"), stream=stream)
         return y
+
+    def capture(self, x=None, y=None, T=None):
+        """The forward into y captured as a HIP graph (moe_layer_graph_create);
+        returns (graph handle, y).  Replay with moe_graph_launch, free with
+        moe_graph_destroy; x, y and the workspace must stay alive meanwhile."""
+        x = self.x if x is None else x
+        T = x.shape[0] if T is None else T
+        y = self.new_output(T) if y is None else y
+        ws = self.ensure_workspace(T)
+        g = moe_layer_graph_create(self.handle, self.wg, self.bias, x, self.x_dtype, T, self.m, self.p, self.E,
+                                   self.k, y, self.y_dtype, ws, self.ws_bytes)
+        return g, y
 
     def debug_buffers(self, T=None):
         T = self.T if T is None else T
