@@ -65,8 +65,9 @@ def lib():
         L.orc_forward_tokens.argtypes = [P, vp, i32, vp, vp, vp, i32, i32, vp, i32, vp, vp, vp, vp]
         L.orc_dense_masked.argtypes = [P, vp, i32, vp, vp, i32, i32, vp]
         L.orc_max_threads.argtypes = []
+        L.orc_norm.argtypes = [vp, i32, i32, i32, i32, vp, vp, ctypes.c_double, vp]
         L.orc_max_threads.restype = ctypes.c_int
-        for f in ("orc_router_logits", "orc_topk", "orc_dispatch", "orc_expert_apply", "orc_expert_rows",
+        for f in ("orc_norm", "orc_router_logits", "orc_topk", "orc_dispatch", "orc_expert_apply", "orc_expert_rows",
                   "orc_combine", "orc_forward_tokens", "orc_dense_masked"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
@@ -138,6 +139,20 @@ def router_logits(x, wg, bias=None):
     E = wg.shape[1]
     out = np.empty((T, E), np.float32)
     _check(lib().orc_router_logits(_ptr(x), _xdt(x), _ptr(wg), _ptr(bias), T, m, E, _ptr(out)), "router")
+    return out
+
+
+NORM_LAYER, NORM_RMS = 1, 2
+
+
+def norm(x, kind, gamma, beta=None, eps=1e-5):
+    """Layer norm (NORM_LAYER) or RMS norm (NORM_RMS) of each row, in double."""
+    x = _c(x)
+    gamma = _c(gamma, np.float32)
+    beta = _c(beta, np.float32)
+    T, m = x.shape
+    out = np.empty((T, m), np.float64)
+    _check(lib().orc_norm(_ptr(x), _xdt(x), T, m, kind, _ptr(gamma), _ptr(beta), float(eps), _ptr(out)), "norm")
     return out
 
 

@@ -29,6 +29,15 @@
  *    index, of w * o  (HARMOEny article, section 3.3 step six: finished
  *    tokens are collected).
  *
+ *  - neighbouring ops (DeepSpeed-Inference summary, datalearner.com, section
+ *    4: the post-attention layer norm fused with the intermediate GeMM, and
+ *    the bias and residual addition; section 2: a layer norm's reductions
+ *    run along the row inside one tile).  Layer norm of a row x of m:
+ *    mu = sum x / m, var = sum (x - mu)^2 / m, out = (x - mu) / sqrt(var +
+ *    eps) * gamma + beta; the RMS form drops the mean and beta:
+ *    out = x / sqrt(sum x^2 / m + eps) * gamma.  The residual is added to
+ *    the combined output (in the tests, beside the layer).
+ *
  * Return codes: 0 on success, -1 on a bad argument.
  */
 #include "moe_oracle.h"
@@ -78,6 +87,35 @@ int orc_router_logits(const void* x, int x_dtype, const float* wg, const float* 
       for (int i = 1; i < m; ++i) s += act_at(x, x_dtype, (int64_t)t * m + i) * (double)wg[(int64_t)i * E + e];
       if (bias) s += (double)bias[e];
       logits[(int64_t)t * E + e] = (float)s;
+    }
+  }
+  return 0;
+}
+
+/* ---- norm of the layer's input rows ------------------------------------- */
+
+int orc_norm(const void* x, int x_dtype, int T, int m, int kind, const float* gamma, const float* beta, double eps,
+             double* out) {
+  if (T < 0 || m < 1 || (T > 0 && (!x || !gamma || !out)) || eps < 0) return -1;
+  if (x_dtype != ORC_F32 && x_dtype != ORC_BF16) return -1;
+  if (kind != ORC_NORM_LAYER && kind != ORC_NORM_RMS) return -1;
+  for (int t = 0; t < T; ++t) {
+    const int64_t r = (int64_t)t * m;
+    double mu = 0.0;
+    if (kind == ORC_NORM_LAYER) {
+      for (int i = 0; i < m; ++i) mu += act_at(x, x_dtype, r + i);
+      mu /= m;
+    }
+    double ss = 0.0;
+    for (int i = 0; i < m; ++i) {
+      const double d = act_at(x, x_dtype, r + i) - mu;
+      ss += d * d;
+    }
+    const double den = sqrt(ss / m + eps);
+    for (int i = 0; i < m; ++i) {
+      double v = (act_at(x, x_dtype, r + i) - mu) / den * (double)gamma[i];
+      if (kind == ORC_NORM_LAYER && beta) v += (double)beta[i];
+      out[r + i] = v;
     }
   }
   return 0;

@@ -39,6 +39,12 @@ int orc_forward_tokens(const orc_experts* X, const void* x, int x_dtype, const f
 int orc_dense_masked(const orc_experts* X, const void* x, int x_dtype, const int32_t* idx, const float* w, int T,
                      int k, double* y);
 
+/* Norm before the layer: ORC_NORM_LAYER (mean and biased variance over the
+ * row) or ORC_NORM_RMS (root mean square); out in double. */
+enum { ORC_NORM_LAYER = 1, ORC_NORM_RMS = 2 };
+int orc_norm(const void* x, int x_dtype, int T, int m, int kind, const float* gamma, const float* beta, double eps,
+             double* out);
+
 int orc_max_threads(void);
 
 #endif

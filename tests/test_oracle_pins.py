@@ -343,3 +343,56 @@ def test_combine_reassembles_tokens(orc):
     for t in range(T):
         want = sum(float(w[t, j]) * vals[t * k + j] for j in np.argsort(idx[t]))
         assert np.array_equal(y[t], want)
+
+
+# ---- norm of the layer's input rows (DeepSpeed-Inference summary, section 4
+# fusion regions: post-attention layer norm with the intermediate GeMM) ----
+
+def _bf16_bits(a):
+    """fp32 values exactly representable in bf16 -> their bf16 bit patterns."""
+    u = np.asarray(a, np.float32).view(np.uint32)
+    assert np.all(u & 0xFFFF == 0)
+    return (u >> 16).astype(np.uint16)
+
+
+def test_norm_worked_examples(orc):
+    # layer norm of [1, 2, 3, 4]: mean 2.5, biased variance 5/4, so
+    # (x - 2.5) * 2 / sqrt(5) = [-3, -1, 1, 3] / sqrt(5)
+    out = orc.norm(np.array([[1, 2, 3, 4]], np.float32), orc.NORM_LAYER, np.ones(4, np.float32), eps=0.0)
+    assert np.allclose(out[0], np.array([-3, -1, 1, 3]) / math.sqrt(5), rtol=0, atol=1e-15)
+    # RMS norm of [3, 4]: mean square 25/2, so [3, 4] * sqrt(2) / 5
+    out = orc.norm(np.array([[3, 4]], np.float32), orc.NORM_RMS, np.ones(2, np.float32), eps=0.0)
+    assert np.allclose(out[0], np.array([3, 4]) * math.sqrt(2) / 5, rtol=0, atol=1e-15)
+    # gamma and beta per column; eps inside the square root
+    g = np.array([2.0, -1.0, 0.5, 4.0], np.float32)
+    b = np.array([0.25, 0.0, -1.0, 8.0], np.float32)
+    out = orc.norm(np.array([[1, 2, 3, 4]], np.float32), orc.NORM_LAYER, g, b, eps=0.75)
+    assert np.allclose(out[0], (np.array([-1.5, -0.5, 0.5, 1.5]) / math.sqrt(1.25 + 0.75)) * g + b, rtol=0,
+                       atol=1e-14)
+
+
+def test_norm_properties(orc):
+    rng = np.random.default_rng(7)
+    x = rng.integers(-100, 101, size=(6, 96)).astype(np.float32)
+    one, zero = np.ones(96, np.float32), np.zeros(96, np.float32)
+    ln = orc.norm(x, orc.NORM_LAYER, one, zero, eps=0.0)
+    assert np.allclose(ln.mean(axis=1), 0.0, atol=1e-13)
+    assert np.allclose((ln ** 2).mean(axis=1), 1.0, atol=1e-12)
+    # invariant to a positive scale and a shift of the row (exact in fp32)
+    assert np.allclose(orc.norm(2 * x + 16, orc.NORM_LAYER, one, zero, eps=0.0), ln, atol=1e-12)
+    rms = orc.norm(x, orc.NORM_RMS, one, eps=0.0)
+    assert np.allclose((rms ** 2).mean(axis=1), 1.0, atol=1e-12)
+    assert np.allclose(orc.norm(4 * x, orc.NORM_RMS, one, eps=0.0), rms, atol=1e-12)
+    # the RMS form keeps the mean: a shift changes it
+    assert not np.allclose(orc.norm(x + 16, orc.NORM_RMS, one, eps=0.0), rms, atol=1e-3)
+    # gamma and beta act per column on the normalised row
+    g = rng.normal(size=96).astype(np.float32)
+    b = rng.normal(size=96).astype(np.float32)
+    assert np.allclose(orc.norm(x, orc.NORM_LAYER, g, b, eps=0.0), ln * g.astype(np.float64) + b, atol=1e-12)
+    # a constant row: zero variance, so layer norm gives beta; RMS gives c / sqrt(c^2 + eps)
+    c = np.full((1, 96), 3.0, np.float32)
+    assert np.allclose(orc.norm(c, orc.NORM_LAYER, g, b, eps=1e-5)[0], b, atol=1e-12)
+    assert np.allclose(orc.norm(c, orc.NORM_RMS, one, eps=1e-5)[0], 3.0 / math.sqrt(9.0 + 1e-5), atol=1e-15)
+    # bf16 rows read as the same values
+    assert np.array_equal(orc.norm(_bf16_bits(x), orc.NORM_LAYER, one, zero, eps=1e-5),
+                          orc.norm(x, orc.NORM_LAYER, one, zero, eps=1e-5))
