@@ -173,6 +173,29 @@ def main():
     ms_graph = ev0.elapsed_time(ev1) / args.steps
     M.moe_graph_destroy(g)
 
+    # The fused forward (moe_layer_forward_fused): layer norm of x in the
+    # routing pass and a residual added at the end, K steps.
+    gen = torch.Generator().manual_seed(1)
+    gamma = (1.0 + 0.1 * torch.randn(sp.m, generator=gen)).to("cuda")
+    beta = (0.05 * torch.randn(sp.m, generator=gen)).to("cuda")
+    resid = (0.5 * torch.randn(sp.T, sp.m, generator=gen)).to(y.dtype).to("cuda")
+    ws = layer.ensure_workspace(sp.T)
+
+    def fused_step():
+        M.moe_layer_forward_fused(layer.handle, layer.wg, layer.bias, layer.x, layer.x_dtype, M.MOE_NORM_LAYER, gamma,
+                                  beta, 1e-5, resid, sp.T, sp.m, sp.p, sp.E, sp.k, y, layer.y_dtype, ws,
+                                  layer.ws_bytes)
+
+    for _ in range(3):
+        fused_step()
+    torch.cuda.synchronize()
+    ev0.record()
+    for _ in range(args.steps):
+        fused_step()
+    ev1.record()
+    torch.cuda.synchronize()
+    ms_fused = ev0.elapsed_time(ev1) / args.steps
+
     # Kernel timing: K more steps in which the library brackets every launch
     # with HIP events recorded on the stream the kernel runs on.  (The events
     # add small gaps between launches, so the step time above is taken
@@ -229,6 +252,7 @@ def main():
         "ms_per_step": round(ms, 5),
         "ms_per_step_with_kernel_events": round(ms_events, 5),
         "graph": {"ms_per_step": round(ms_graph, 5), "value": round(sp.T / (ms_graph * 1e-3), 2)},
+        "fused_norm_residual": {"ms_per_step": round(ms_fused, 5), "value": round(sp.T / (ms_fused * 1e-3), 2)},
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

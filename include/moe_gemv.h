@@ -186,6 +186,35 @@ int moe_layer_forward(const moe_weights* w, const float* w_router, const float* 
                       int32_t* dbg_offsets, int32_t* dbg_perm, void* stream);
 
 /*
+ * moe_layer_forward_fused -- moe_layer_forward with the layer's neighbouring
+ * ops done inside it (DeepSpeed-Inference summary, section 4, fusion regions
+ * "post-attention layer norm + intermediate GeMM" and "bias and residual
+ * add"; section 2: a norm's reductions run along the row within one tile):
+ *   x' = norm(x);  y = residual + MoE(x')
+ *  norm      MOE_NORM_NONE, MOE_NORM_LAYER (per row: mean and biased
+ *            variance over the m columns, (x - mean) / sqrt(var + eps) *
+ *            gamma + beta) or MOE_NORM_RMS (x / sqrt(mean(x^2) + eps) *
+ *            gamma).  The norm is computed in fp32 inside the routing pass
+ *            and rounded to x's dtype; routing and experts use x'.
+ *  gamma     device fp32 [m] (required with a norm); beta device fp32 [m] or
+ *            NULL (layer norm only).  eps in [0, 1].
+ *  residual  device [T][m] in y_dtype, or NULL; added to the fp32 sum before
+ *            y is rounded.
+ *  x_norm    optional device [T][m] in x_dtype, 16-byte aligned: receives x'
+ *            (else it stays in the workspace).  Needs a norm.
+ *  dbg_*     as in moe_layer_forward (may be NULL).
+ * Other arguments and errors as moe_layer_forward.
+ */
+#define MOE_NORM_NONE 0
+#define MOE_NORM_LAYER 1
+#define MOE_NORM_RMS 2
+int moe_layer_forward_fused(const moe_weights* w, const float* w_router, const float* b_router, const void* x,
+                            int x_dtype, int norm, const float* gamma, const float* beta, float eps,
+                            const void* residual, int T, int m, int p, int E, int k, void* y, int y_dtype,
+                            void* workspace, size_t ws_bytes, void* x_norm, int32_t* dbg_topk_idx,
+                            float* dbg_topk_w, float* dbg_logits, void* stream);
+
+/*
  * moe_layer_graph_create / moe_graph_launch / moe_graph_destroy -- the layer
  * forward captured once into a HIP graph and replayed with one launch (the
  * CUDA-Graph capture of the DeepSpeed-Inference summary, section 4, as HIP

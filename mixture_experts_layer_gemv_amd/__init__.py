@@ -20,6 +20,7 @@ MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP
 MOE_F32, MOE_BF16, MOE_I8 = 0, 1, 2
 MOE_MLP_RELU, MOE_SWIGLU = 0, 1
 MOE_ROUTE_LOGITS_IN = 1
+MOE_NORM_NONE, MOE_NORM_LAYER, MOE_NORM_RMS = 0, 1, 2
 MOE_MAX_EXPERTS = 64
 
 STATUS_NAMES = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARG", 2: "MOE_ERR_UNSUPPORTED", 3: "MOE_ERR_WORKSPACE",
@@ -49,6 +50,8 @@ _SIGS = {
     "moe_combine": ([_vp, _vp, _vp, _i32, _i32, _i32, _vp, _i32, _vp], _i32),
     "moe_layer_forward": ([_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _i32, _vp, _sz,
                            _vp, _vp, _vp, _vp, _vp, _vp, _vp], _i32),
+    "moe_layer_forward_fused": ([_vp, _vp, _vp, _vp, _i32, _i32, _vp, _vp, ctypes.c_float, _vp, _i32, _i32, _i32,
+                                 _i32, _i32, _vp, _i32, _vp, _sz, _vp, _vp, _vp, _vp, _vp], _i32),
     "moe_layer_graph_create": ([_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _i32, _vp, _sz,
                                 ctypes.POINTER(_vp)], _i32),
     "moe_graph_launch": ([_vp, _vp], _i32),
@@ -150,6 +153,15 @@ def moe_layer_forward(w, w_router, b_router, x, x_dtype, T, m, p, E, k, y, y_dty
         w, _p(w_router), _p(b_router), _p(x), x_dtype, T, m, p, E, k, _p(y), y_dtype, _p(workspace), ws_bytes,
         _p(dbg_topk_idx), _p(dbg_topk_w), _p(dbg_logits), _p(dbg_counts), _p(dbg_offsets), _p(dbg_perm),
         _s(stream)))
+
+
+def moe_layer_forward_fused(w, w_router, b_router, x, x_dtype, norm, gamma, beta, eps, residual, T, m, p, E, k, y,
+                            y_dtype, workspace, ws_bytes, x_norm=None, dbg_topk_idx=None, dbg_topk_w=None,
+                            dbg_logits=None, stream=None):
+    _check("moe_layer_forward_fused", lib().moe_layer_forward_fused(
+        w, _p(w_router), _p(b_router), _p(x), x_dtype, norm, _p(gamma), _p(beta), float(eps), _p(residual), T, m, p,
+        E, k, _p(y), y_dtype, _p(workspace), ws_bytes, _p(x_norm), _p(dbg_topk_idx), _p(dbg_topk_w),
+        _p(dbg_logits), _s(stream)))
 
 
 def moe_layer_graph_create(w, w_router, b_router, x, x_dtype, T, m, p, E, k, y, y_dtype, workspace, ws_bytes):

@@ -198,7 +198,7 @@ bool skinny_rows_combine();
 
 // Workspace carving, in the order listed.
 struct Ws {
-  size_t logits, idx, w, counts, offsets, perm, inv, h, yacc, yperm, xp, hp, total;
+  size_t logits, idx, w, counts, offsets, perm, inv, xn, h, yacc, yperm, xp, hp, total;
 };
 
 Ws ws_layout(const moe_weights* W, int T, int k) {
@@ -217,6 +217,8 @@ Ws ws_layout(const moe_weights* W, int T, int k) {
   L.offsets = take((size_t)(W->E + 1) * 4);
   L.perm = take(n * 4);
   L.inv = take(n * 4);
+  // the normalised input rows of the fused forward (x's dtype)
+  L.xn = take((size_t)T * W->m * (W->w_dtype == MOE_F32 ? 4 : 2));
   const Path path = ffn_path(W, T, k);
   const bool gemm = path == Path::GEMM, hybrid = path == Path::HYBRID;
   const bool spack = (path == Path::SKINNY || hybrid) && skinny_packed(W, T, k);
@@ -790,10 +792,24 @@ int moe_combine(const float* y_perm, const int32_t* inv_perm, const float* topk_
   return ok();
 }
 
-int moe_layer_forward(const moe_weights* w, const float* w_router, const float* b_router, const void* x, int x_dtype,
-                      int T, int m, int p, int E, int k, void* y, int y_dtype, void* workspace, size_t ws_bytes,
-                      int32_t* dbg_topk_idx, float* dbg_topk_w, float* dbg_logits, int32_t* dbg_counts,
-                      int32_t* dbg_offsets, int32_t* dbg_perm, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// The neighbouring ops of the fused forward (none by default).
+struct Fusion {
+  int norm = MOE_NORM_NONE;
+  const float* gamma = nullptr;
+  const float* beta = nullptr;
+  float eps = 0.0f;
+  const void* residual = nullptr;
+  void* x_norm = nullptr;
+};
+
+int layer_forward(const moe_weights* w, const float* w_router, const float* b_router, const void* x, int x_dtype,
+                  int T, int m, int p, int E, int k, void* y, int y_dtype, void* workspace, size_t ws_bytes,
+                  int32_t* dbg_topk_idx, float* dbg_topk_w, float* dbg_logits, int32_t* dbg_counts,
+                  int32_t* dbg_offsets, int32_t* dbg_perm, void* stream, const Fusion& f) {
   if (int rc = check_weights_match(w, m, p, E)) return rc;
   if (int rc = check_shape(T, m, p, E, k)) return rc;
   if (int rc = check_combo(x_dtype, w->w_dtype)) return rc;
@@ -829,14 +845,19 @@ int moe_layer_forward(const moe_weights* w, const float* w_router, const float* 
   // (zeroed by the router) and a final conversion
   const bool rows = gemm || (path == Path::SKINNY && skinny_rows_combine());
 
+  // the neighbouring ops: the input rows' norm in the routing pass (the
+  // experts then read the normalised rows), the residual added by the combine
+  // or, on the accumulator paths, used as the accumulator's starting value
+  void* xn = f.norm ? (f.x_norm ? f.x_norm : static_cast<void*>(ws + L.xn)) : nullptr;
+  const moe::RouteFuse rf{f.norm, f.gamma, f.beta, f.eps, xn, f.residual, y_bf16 ? 1 : 0};
   MOE_TRY_HIP(run("route_topk", s, [&] {
     return moe::launch_route_topk(x, x_dtype == MOE_BF16, w_router, b_router, T, m, E, k, false, logits, idx, tw,
-                                  rows ? nullptr : yacc, m, s);
+                                  rows ? nullptr : yacc, m, s, &rf);
   }));
   if (!fused)
     MOE_TRY_HIP(run("dispatch", s, [&] { return moe::launch_dispatch(idx, T * k, E, counts, offsets, perm, inv, s); }));
   FfnIo io{};
-  io.x = x;
+  io.x = f.norm ? xn : x;
   io.T = T;
   io.k = k;
   io.topk_idx = fused ? idx : nullptr;
@@ -856,13 +877,50 @@ int moe_layer_forward(const moe_weights* w, const float* w_router, const float* 
   if (int rc = run_ffn(w, io, s)) return rc;
   if (rows) {
     MOE_TRY_HIP(run("combine", s, [&] {
-      return moe::launch_combine(io.yperm, inv, tw, T, m, k, slices, (size_t)T * k * m, y, y_bf16, s);
+      return moe::launch_combine(io.yperm, inv, tw, T, m, k, slices, (size_t)T * k * m, y, y_bf16, s, f.residual);
     }));
     return ok();
   }
   if (y_bf16)
     MOE_TRY_HIP(run("finalize", s, [&] { return moe::launch_f32_to_bf16(yacc, static_cast<uint16_t*>(y), ny, s); }));
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_layer_forward(const moe_weights* w, const float* w_router, const float* b_router, const void* x, int x_dtype,
+                      int T, int m, int p, int E, int k, void* y, int y_dtype, void* workspace, size_t ws_bytes,
+                      int32_t* dbg_topk_idx, float* dbg_topk_w, float* dbg_logits, int32_t* dbg_counts,
+                      int32_t* dbg_offsets, int32_t* dbg_perm, void* stream) {
+  return layer_forward(w, w_router, b_router, x, x_dtype, T, m, p, E, k, y, y_dtype, workspace, ws_bytes,
+                       dbg_topk_idx, dbg_topk_w, dbg_logits, dbg_counts, dbg_offsets, dbg_perm, stream, Fusion{});
+}
+
+int moe_layer_forward_fused(const moe_weights* w, const float* w_router, const float* b_router, const void* x,
+                            int x_dtype, int norm, const float* gamma, const float* beta, float eps,
+                            const void* residual, int T, int m, int p, int E, int k, void* y, int y_dtype,
+                            void* workspace, size_t ws_bytes, void* x_norm, int32_t* dbg_topk_idx,
+                            float* dbg_topk_w, float* dbg_logits, void* stream) {
+  if (norm != MOE_NORM_NONE && norm != MOE_NORM_LAYER && norm != MOE_NORM_RMS)
+    return fail(MOE_ERR_INVALID_ARG, "norm kind %d", norm);
+  if (norm == MOE_NORM_NONE && (gamma || beta || x_norm))
+    return fail(MOE_ERR_INVALID_ARG, "gamma, beta and x_norm need a norm");
+  if (norm == MOE_NORM_RMS && beta) return fail(MOE_ERR_INVALID_ARG, "the RMS norm takes no beta");
+  if (!(eps >= 0.0f) || eps > 1.0f) return fail(MOE_ERR_INVALID_ARG, "eps=%g must be in [0, 1]", (double)eps);
+  if (T > 0 && norm != MOE_NORM_NONE && !gamma) return fail(MOE_ERR_INVALID_ARG, "gamma is NULL");
+  if (residual && !aligned16(residual)) return fail(MOE_ERR_INVALID_ARG, "residual must be 16-byte aligned");
+  if (x_norm && !aligned16(x_norm)) return fail(MOE_ERR_INVALID_ARG, "x_norm must be 16-byte aligned");
+  Fusion f;
+  f.norm = norm;
+  f.gamma = gamma;
+  f.beta = beta;
+  f.eps = eps;
+  f.residual = residual;
+  f.x_norm = x_norm;
+  return layer_forward(w, w_router, b_router, x, x_dtype, T, m, p, E, k, y, y_dtype, workspace, ws_bytes,
+                       dbg_topk_idx, dbg_topk_w, dbg_logits, nullptr, nullptr, nullptr, stream, f);
 }
 
 }  // extern "C"

@@ -52,10 +52,25 @@ hipError_t launch_pack_i8(const int8_t* src, void* dst, int E, int K, int N, int
 
 // ---- routing ---------------------------------------------------------------
 
-// yacc (optional): fp32 [T][ym] accumulator that the routing pass zeroes.
+// Neighbouring ops done by the routing pass (DeepSpeed-Inference summary,
+// section 4: the layer norm before the intermediate GeMM; the residual add).
+struct RouteFuse {
+  int norm;              // 0: none; 1: layer norm; 2: RMS norm of each x row
+  const float* gamma;    // [m]
+  const float* beta;     // [m] or null (layer norm only)
+  float eps;
+  void* xn;              // with a norm: the normalised rows [T][m] in x's dtype (routed and returned)
+  const void* residual;  // or null: the accumulator starts from it instead of zero ([T][ym])
+  int res_bf16;          // residual dtype: bf16 (1) or fp32 (0)
+};
+
+// yacc (optional): fp32 [T][ym] accumulator that the routing pass zeroes (or
+// fills with fuse->residual).  With fuse->norm the routing uses, and writes to
+// fuse->xn, the normalised rows: inside the staged router, else by a row-norm
+// kernel first.
 hipError_t launch_route_topk(const void* x, bool x_bf16, const float* wg, const float* bias, int T, int m, int E,
                              int k, bool logits_in, float* logits, int32_t* idx, float* w, float* yacc, int ym,
-                             hipStream_t s);
+                             hipStream_t s, const RouteFuse* fuse = nullptr);
 
 hipError_t launch_dispatch(const int32_t* idx, int n, int E, int32_t* counts, int32_t* offsets, int32_t* perm,
                            int32_t* inv_perm, hipStream_t s);
@@ -180,8 +195,10 @@ hipError_t launch_ffn_f32(const F32Args& a, hipStream_t s);
 
 // y[t] = sum_j w[t,j] * sum_q y_perm[q][inv[t,j]]: the unweighted expert rows,
 // each the sum of `slices` partial rows slice_stride elements apart.
+// residual (optional): [T][m] in y's dtype, added to each sum last.
 hipError_t launch_combine(const float* y_perm, const int32_t* inv_perm, const float* topk_w, int T, int m, int k,
-                          int slices, size_t slice_stride, void* y, bool y_bf16, hipStream_t s);
+                          int slices, size_t slice_stride, void* y, bool y_bf16, hipStream_t s,
+                          const void* residual = nullptr);
 hipError_t launch_fill_zero(float* p, size_t n, hipStream_t s);
 hipError_t launch_f32_to_bf16(const float* src, uint16_t* dst, size_t n, hipStream_t s);
 

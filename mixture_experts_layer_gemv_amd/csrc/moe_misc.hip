@@ -144,11 +144,13 @@ __global__ __launch_bounds__(256) void k_ffn_f32(const F32Args A) {
 
 // ---- combine and elementwise ----------------------------------------------------
 
-// y[t][c] = sum_{j<k} w[t][j] * y_perm[inv_perm[t*k+j]][c], four columns per thread.
+// y[t][c] = sum_{j<k} w[t][j] * y_perm[inv_perm[t*k+j]][c] (+ residual[t][c],
+// in y's dtype, added last), four columns per thread.
 template <bool BF16>
 __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ y_perm, const int32_t* __restrict__ inv,
                                                  const float* __restrict__ w, int T, int m, int k, int slices,
-                                                 size_t slice_stride, void* __restrict__ y) {
+                                                 size_t slice_stride, const void* __restrict__ residual,
+                                                 void* __restrict__ y) {
   const size_t q = (size_t)blockIdx.x * blockDim.x + threadIdx.x;  // float4 index
   const size_t per_row = (size_t)m / 4;
   if (q >= (size_t)T * per_row) return;
@@ -171,6 +173,21 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ y_per
     s.y = fmaf(wj, v.y, s.y);
     s.z = fmaf(wj, v.z, s.z);
     s.w = fmaf(wj, v.w, s.w);
+  }
+  if (residual) {
+    if (BF16) {
+      const uint2 r = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(residual) + (size_t)t * m + c);
+      s.x += bf16_to_f32((uint16_t)(r.x & 0xFFFFu));
+      s.y += bf16_to_f32((uint16_t)(r.x >> 16));
+      s.z += bf16_to_f32((uint16_t)(r.y & 0xFFFFu));
+      s.w += bf16_to_f32((uint16_t)(r.y >> 16));
+    } else {
+      const float4 r = *reinterpret_cast<const float4*>(static_cast<const float*>(residual) + (size_t)t * m + c);
+      s.x += r.x;
+      s.y += r.y;
+      s.z += r.z;
+      s.w += r.w;
+    }
   }
   if (BF16) {
     uint16_t* o = static_cast<uint16_t*>(y) + (size_t)t * m + c;
@@ -234,15 +251,16 @@ hipError_t launch_ffn_f32(const F32Args& a, hipStream_t s) {
 }
 
 hipError_t launch_combine(const float* y_perm, const int32_t* inv_perm, const float* topk_w, int T, int m, int k,
-                          int slices, size_t slice_stride, void* y, bool y_bf16, hipStream_t s) {
+                          int slices, size_t slice_stride, void* y, bool y_bf16, hipStream_t s,
+                          const void* residual) {
   if (slices < 1) return hipErrorInvalidValue;
   const size_t work = (size_t)T * (m / 4);
   const unsigned grid = (unsigned)((work + 255) / 256);
   if (work == 0) return hipSuccess;
   if (y_bf16)
-    k_combine<true><<<grid, 256, 0, s>>>(y_perm, inv_perm, topk_w, T, m, k, slices, slice_stride, y);
+    k_combine<true><<<grid, 256, 0, s>>>(y_perm, inv_perm, topk_w, T, m, k, slices, slice_stride, residual, y);
   else
-    k_combine<false><<<grid, 256, 0, s>>>(y_perm, inv_perm, topk_w, T, m, k, slices, slice_stride, y);
+    k_combine<false><<<grid, 256, 0, s>>>(y_perm, inv_perm, topk_w, T, m, k, slices, slice_stride, residual, y);
   return hipGetLastError();
 }
 

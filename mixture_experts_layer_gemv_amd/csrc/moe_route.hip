@@ -230,11 +230,34 @@ constexpr int route_lds_bytes(int tb) { return tb * 65536 < kRouteLdsX ? tb * 65
 // enough partials, butterfly otherwise), then a fixed-order sum over the 16
 // waves in LDS.  One wave per token then takes the top-k.  The block also
 // zeroes its tokens' rows of the fp32 output accumulator.
+__device__ __forceinline__ float wave_sum64(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// Residual element i as fp32.
+__device__ __forceinline__ float residual_at(const RouteFuse& F, size_t i) {
+  return F.res_bf16 ? bf16_to_f32(static_cast<const uint16_t*>(F.residual)[i])
+                    : static_cast<const float*>(F.residual)[i];
+}
+
+// The normalised value of x (a row element at column c) given the row's mean
+// mu and reciprocal deviation r, rounded to the activation dtype's precision.
+template <bool XBF16>
+__device__ __forceinline__ float norm_value(const RouteFuse& F, float xv, float mu, float r, int c) {
+  float v = (xv - mu) * r * F.gamma[c];
+  if (F.norm == 1 && F.beta) v += F.beta[c];
+  if constexpr (XBF16) v = bf16_to_f32(f32_to_bf16(v));
+  return v;
+}
+
 template <int E, int TB, bool XBF16>
 __global__ __launch_bounds__(1024) void k_route_fast(const void* __restrict__ x, const float* __restrict__ wg,
                                                      const float* __restrict__ bias, int T, int m, int k,
                                                      float* __restrict__ logits, int32_t* __restrict__ idx,
-                                                     float* __restrict__ wout, float* __restrict__ yacc, int ym) {
+                                                     float* __restrict__ wout, float* __restrict__ yacc, int ym,
+                                                     const RouteFuse F) {
   using S = RouteShape<E, TB>;
   static_assert(TB * E <= 128 && TB <= 16, "block shape");
   constexpr int XB = XBF16 ? 2 : 4;
@@ -245,7 +268,10 @@ __global__ __launch_bounds__(1024) void k_route_fast(const void* __restrict__ x,
   const int t0 = blockIdx.x * TB;
   const int nt = min(TB, T - t0);
 
-  if (yacc) {
+  if (yacc && F.residual) {
+    const size_t base = (size_t)t0 * ym;
+    for (int i = tid; i < nt * ym; i += 1024) yacc[base + i] = residual_at(F, base + i);
+  } else if (yacc) {
     float4* yr = reinterpret_cast<float4*>(yacc + (size_t)t0 * ym);
     const int n4 = nt * ym / 4;
     for (int i = tid; i < n4; i += 1024) yr[i] = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -258,6 +284,50 @@ __global__ __launch_bounds__(1024) void k_route_fast(const void* __restrict__ x,
     for (int i = tid; i < TB * row16; i += 1024) dst[i] = (i < nt * row16) ? src[i] : make_uint4(0, 0, 0, 0);
   }
   __syncthreads();
+  if (F.norm) {
+    // Norm of the staged rows (the reductions along the row inside this
+    // block, one wave per token), in place, so the router and the experts
+    // both see the normalised rows; they also go to F.xn for the experts.
+    __shared__ float mu_s[TB], r_s[TB];
+    auto xat = [&](int t, int c) {
+      if constexpr (XBF16)
+        return bf16_to_f32(reinterpret_cast<const uint16_t*>(xs_raw)[t * m + c]);
+      else
+        return reinterpret_cast<const float*>(xs_raw)[t * m + c];
+    };
+    if (wave < nt) {
+      float mu = 0.0f;
+      if (F.norm == 1) {
+        float sum = 0.0f;
+        for (int c = lane; c < m; c += 64) sum += xat(wave, c);
+        mu = wave_sum64(sum) / (float)m;
+      }
+      float ss = 0.0f;
+      for (int c = lane; c < m; c += 64) {
+        const float d = xat(wave, c) - mu;
+        ss = fmaf(d, d, ss);
+      }
+      ss = wave_sum64(ss);
+      if (lane == 0) {
+        mu_s[wave] = mu;
+        r_s[wave] = 1.0f / sqrtf(ss / (float)m + F.eps);
+      }
+    }
+    __syncthreads();
+    for (int i = tid; i < nt * m; i += 1024) {
+      const int t = i / m, c = i - t * m;
+      const float v = norm_value<XBF16>(F, xat(t, c), mu_s[t], r_s[t], c);
+      if constexpr (XBF16) {
+        const uint16_t b = f32_to_bf16(v);
+        reinterpret_cast<uint16_t*>(xs_raw)[i] = b;
+        static_cast<uint16_t*>(F.xn)[(size_t)t0 * m + i] = b;
+      } else {
+        reinterpret_cast<float*>(xs_raw)[i] = v;
+        static_cast<float*>(F.xn)[(size_t)t0 * m + i] = v;
+      }
+    }
+    __syncthreads();
+  }
 
   float acc[S::NV];
 #pragma unroll
@@ -332,12 +402,61 @@ __global__ __launch_bounds__(1024) void k_dispatch(const int32_t* __restrict__ i
   });
 }
 
+// One block per row: the row's norm written to F.xn (the unfused form).
+template <bool XBF16>
+__global__ __launch_bounds__(256) void k_norm_rows(const void* __restrict__ x, int m, const RouteFuse F) {
+  __shared__ float part[4];
+  const int t = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const size_t base = (size_t)t * m;
+  auto xat = [&](int c) {
+    if constexpr (XBF16)
+      return bf16_to_f32(static_cast<const uint16_t*>(x)[base + c]);
+    else
+      return static_cast<const float*>(x)[base + c];
+  };
+  auto block_sum = [&](float v) {
+    v = wave_sum64(v);
+    if (lane == 0) part[wave] = v;
+    __syncthreads();
+    const float r = part[0] + part[1] + part[2] + part[3];
+    __syncthreads();
+    return r;
+  };
+  float mu = 0.0f;
+  if (F.norm == 1) {
+    float sum = 0.0f;
+    for (int c = tid; c < m; c += 256) sum += xat(c);
+    mu = block_sum(sum) / (float)m;
+  }
+  float ss = 0.0f;
+  for (int c = tid; c < m; c += 256) {
+    const float d = xat(c) - mu;
+    ss = fmaf(d, d, ss);
+  }
+  const float r = 1.0f / sqrtf(block_sum(ss) / (float)m + F.eps);
+  for (int c = tid; c < m; c += 256) {
+    const float v = norm_value<XBF16>(F, xat(c), mu, r, c);
+    if constexpr (XBF16)
+      static_cast<uint16_t*>(F.xn)[base + c] = f32_to_bf16(v);
+    else
+      static_cast<float*>(F.xn)[base + c] = v;
+  }
+}
+
+__global__ __launch_bounds__(256) void k_fill_residual(float* __restrict__ yacc, size_t n, const RouteFuse F) {
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) yacc[i] = residual_at(F, i);
+}
+
 }  // namespace
 
 hipError_t launch_route_topk(const void* x, bool x_bf16, const float* wg, const float* bias, int T, int m, int E,
                              int k, bool logits_in, float* logits, int32_t* idx, float* w, float* yacc, int ym,
-                             hipStream_t s) {
+                             hipStream_t s, const RouteFuse* fuse) {
   const int xb = x_bf16 ? 2 : 4;
+  const RouteFuse F = fuse ? *fuse : RouteFuse{};
+  if (F.norm && (logits_in || !F.gamma || !F.xn)) return hipErrorInvalidValue;
+  if (T <= 0) return hipSuccess;
   if (!logits_in && (E == 8 || E == 16 || E == 32 || E == 64) && (yacc == nullptr || ym % 4 == 0)) {
     // tokens per block: one for decode batches (spreads the router weights'
     // reads over T CUs), up to 128 / E for large batches
@@ -348,9 +467,9 @@ hipError_t launch_route_topk(const void* x, bool x_bf16, const float* wg, const 
 #define MOE_ROUTE_FAST(EE, TT)                                                                               \
   if (E == EE && tb == TT) {                                                                                 \
     if (x_bf16)                                                                                              \
-      k_route_fast<EE, TT, true><<<grid, 1024, 0, s>>>(x, wg, bias, T, m, k, logits, idx, w, yacc, ym);      \
+      k_route_fast<EE, TT, true><<<grid, 1024, 0, s>>>(x, wg, bias, T, m, k, logits, idx, w, yacc, ym, F);   \
     else                                                                                                     \
-      k_route_fast<EE, TT, false><<<grid, 1024, 0, s>>>(x, wg, bias, T, m, k, logits, idx, w, yacc, ym);     \
+      k_route_fast<EE, TT, false><<<grid, 1024, 0, s>>>(x, wg, bias, T, m, k, logits, idx, w, yacc, ym, F);  \
     return hipGetLastError();                                                                                \
   }
       MOE_ROUTE_FAST(8, 1)
@@ -366,7 +485,20 @@ hipError_t launch_route_topk(const void* x, bool x_bf16, const float* wg, const 
 #undef MOE_ROUTE_FAST
     }
   }
-  if (yacc) {
+  if (F.norm) {  // unfused: the rows' norm first, then the router on them
+    if (x_bf16)
+      k_norm_rows<true><<<T, 256, 0, s>>>(x, m, F);
+    else
+      k_norm_rows<false><<<T, 256, 0, s>>>(x, m, F);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    x = F.xn;
+  }
+  if (yacc && F.residual) {
+    k_fill_residual<<<(unsigned)(((size_t)T * ym + 255) / 256), 256, 0, s>>>(yacc, (size_t)T * ym, F);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  } else if (yacc) {
     const hipError_t e = launch_fill_zero(yacc, (size_t)T * ym, s);
     if (e != hipSuccess) return e;
   }
