@@ -66,6 +66,8 @@ def lib():
         L.synth_fill_normal_bf16.restype = None
         L.synth_fill_int8_quant.argtypes = [u64, u32, dbl, i64, i64, i64, vp, vp]
         L.synth_fill_int8_quant.restype = ctypes.c_int
+        L.synth_fill_intq_quant.argtypes = [u64, u32, dbl, i64, i64, i64, ctypes.c_int, vp, vp]
+        L.synth_fill_intq_quant.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -92,6 +94,16 @@ def int8_quant(seed: int, tid: int, sigma: float, E: int, K: int, N: int):
     return q, s
 
 
+def int4_quant(seed: int, tid: int, sigma: float, E: int, K: int, N: int):
+    """As int8_quant with q in [-7, 7] (held one per int8 byte)."""
+    q = np.empty((E, K, N), dtype=np.int8)
+    s = np.empty((E, N), dtype=np.float32)
+    rc = lib().synth_fill_intq_quant(seed, tid, sigma, E, K, N, 7, q.ctypes.data, s.ctypes.data)
+    if rc != 0:
+        raise MemoryError("synth_fill_intq_quant failed")
+    return q, s
+
+
 def bf16_to_f32(a: np.ndarray) -> np.ndarray:
     """Exact widening of uint16 bf16 bit patterns to float32."""
     return (a.astype(np.uint32) << 16).view(np.float32)
@@ -113,7 +125,7 @@ class LayerSpec:
     k: int
     kind: str  # "relu" | "swiglu"
     x_dtype: str  # "f32" | "bf16"
-    w_dtype: str  # "f32" | "bf16" | "i8"
+    w_dtype: str  # "f32" | "bf16" | "i8" | "i4"
     seed: int
     sigma_x: float = 1.0
     sigma_router: float = 0.02
@@ -124,7 +136,7 @@ class LayerSpec:
     def expert_bytes(self) -> int:
         """|E| of one expert: (mp + pm) * dtype for the two-matrix MLP, 3*m*p*dtype for SwiGLU."""
         nmat = 2 if self.kind == "relu" else 3
-        return nmat * self.m * self.p * {"f32": 4, "bf16": 2, "i8": 1}[self.w_dtype]
+        return int(nmat * self.m * self.p * {"f32": 4, "bf16": 2, "i8": 1, "i4": 0.5}[self.w_dtype])
 
 
 # The five measured layers.  Shapes follow Mixtral-8x7B (E=8, m=4096, p=14336)
@@ -142,6 +154,9 @@ CONFIGS = {
                     note="Mixtral-8x7B-shaped prefill, uniform routing"),
     "c5": LayerSpec("mixtral_decode_int8", 64, 4096, 14336, 8, 2, "swiglu", "bf16", "i8", 4,
                     note="Mixtral-8x7B-shaped decode, int8 weights with per-channel fp32 scales"),
+    # a next row (lower-precision weights): the int8 layer with int4 weights
+    "c6": LayerSpec("mixtral_decode_int4", 64, 4096, 14336, 8, 2, "swiglu", "bf16", "i4", 5,
+                    note="Mixtral-8x7B-shaped decode, int4 weights with per-channel fp32 scales"),
 }
 
 
@@ -179,7 +194,8 @@ def make_layer(sp: LayerSpec, with_x: bool = True, with_weights: bool = True) ->
             elif sp.w_dtype == "bf16":
                 out[key] = normal_bf16(sp.seed, tid, sp.sigma_w, shape)
             else:
-                q, s = int8_quant(sp.seed, tid, sp.sigma_w, *shape)
+                quant = int8_quant if sp.w_dtype == "i8" else int4_quant
+                q, s = quant(sp.seed, tid, sp.sigma_w, *shape)
                 out[key] = q
                 out["s" + key[1:]] = s
     return out

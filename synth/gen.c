@@ -72,17 +72,19 @@ void synth_fill_normal_bf16(uint64_t seed, uint32_t tensor_id, double sigma, int
 }
 
 /*
- * Symmetric per-output-channel int8 quantisation of a freshly generated
+ * Symmetric per-output-channel integer quantisation of a freshly generated
  * weight tensor W[E][K][N] ~ N(0, sigma^2) (fp32 values of the same stream as
- * synth_fill_normal_f32): for every expert e and column n,
- *   s[e][n] = max_k |W[e][k][n]| / 127      (fp32)
- *   q[e][k][n] = clamp(nearbyint(W / s), -127, 127)   (W / s in double,
+ * synth_fill_normal_f32), to qmax = 127 (int8) or 7 (int4): for every expert
+ * e and column n,
+ *   s[e][n] = max_k |W[e][k][n]| / qmax      (fp32)
+ *   q[e][k][n] = clamp(nearbyint(W / s), -qmax, qmax)   (W / s in double,
  *                round half to even), q = 0 where s == 0.
  * Quantisation is part of building the synthetic layer; the layer itself
  * then computes with q * s.
  */
-int synth_fill_int8_quant(uint64_t seed, uint32_t tensor_id, double sigma, int64_t E, int64_t K, int64_t N,
-                          int8_t* q, float* scale) {
+int synth_fill_intq_quant(uint64_t seed, uint32_t tensor_id, double sigma, int64_t E, int64_t K, int64_t N,
+                          int qmax, int8_t* q, float* scale) {
+  if (qmax < 1 || qmax > 127) return -1;
   const uint64_t s = stream_seed(seed, tensor_id);
   float* w = (float*)malloc((size_t)(K * N) * sizeof(float));
   if (!w) return -1;
@@ -98,7 +100,7 @@ int synth_fill_int8_quant(uint64_t seed, uint32_t tensor_id, double sigma, int64
         const float a = fabsf(w[k * N + n]);
         if (a > mx) mx = a;
       }
-      se[n] = mx / 127.0f;
+      se[n] = mx / (float)qmax;
     }
     int8_t* qe = q + e * K * N;
 #pragma omp parallel for schedule(static)
@@ -108,8 +110,8 @@ int synth_fill_int8_quant(uint64_t seed, uint32_t tensor_id, double sigma, int64
         double v = 0.0;
         if (sc != 0.0f) {
           v = nearbyint((double)w[k * N + n] / (double)sc);
-          if (v > 127.0) v = 127.0;
-          if (v < -127.0) v = -127.0;
+          if (v > qmax) v = qmax;
+          if (v < -qmax) v = -qmax;
         }
         qe[k * N + n] = (int8_t)v;
       }
@@ -117,4 +119,9 @@ int synth_fill_int8_quant(uint64_t seed, uint32_t tensor_id, double sigma, int64
   }
   free(w);
   return 0;
+}
+
+int synth_fill_int8_quant(uint64_t seed, uint32_t tensor_id, double sigma, int64_t E, int64_t K, int64_t N,
+                          int8_t* q, float* scale) {
+  return synth_fill_intq_quant(seed, tensor_id, sigma, E, K, N, 127, q, scale);
 }

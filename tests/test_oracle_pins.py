@@ -295,7 +295,8 @@ def test_routed_equals_dense_masked(orc, syn, kind, w_dtype, E, k):
 # --------------------------------------------------------------------------
 
 @pytest.mark.parametrize("kind,w_dtype", [("relu", "f32"), ("relu", "bf16"), ("swiglu", "f32"),
-                                          ("swiglu", "bf16"), ("swiglu", "i8"), ("relu", "i8")])
+                                          ("swiglu", "bf16"), ("swiglu", "i8"), ("relu", "i8"),
+                                          ("swiglu", "i4"), ("relu", "i4")])
 def test_single_expert_is_dense_mlp(orc, syn, kind, w_dtype):
     L = _layer(syn, 9, 48, 80, 1, 1, kind, w_dtype, seed=77)
     X = orc.Experts.from_layer(L)
@@ -304,7 +305,7 @@ def test_single_expert_is_dense_mlp(orc, syn, kind, w_dtype):
 
     def deq(key):
         w = L[key][0]
-        if w_dtype == "i8":
+        if w_dtype in ("i8", "i4"):
             return torch.from_numpy(w.astype(np.float64) * L["s" + key[1:]][0].astype(np.float64)[None, :])
         return torch.from_numpy(_to64(syn, w))
 
@@ -322,6 +323,18 @@ def test_int8_quantisation_closed_forms(syn):
     q, s = syn.int8_quant(9, syn.TID_W1, 0.02, E, K, N)
     W = syn.normal_f32(9, syn.TID_W1, 0.02, (E, K, N)).astype(np.float64)
     assert np.all(np.abs(q).max(axis=1) == 127)
+    err = np.abs(W - q.astype(np.float64) * s[:, None, :].astype(np.float64))
+    assert np.all(err <= s[:, None, :].astype(np.float64) / 2 * (1 + 1e-6))
+
+
+def test_int4_quantisation_closed_forms(syn):
+    """The int4 rule: per output channel s = max|W| / 7, max|q| = 7, q in [-7, 7] and |W - q s| <= s/2."""
+    E, K, N = 2, 64, 48
+    q, s = syn.int4_quant(9, syn.TID_W1, 0.02, E, K, N)
+    W = syn.normal_f32(9, syn.TID_W1, 0.02, (E, K, N)).astype(np.float64)
+    assert q.dtype == np.int8 and q.min() >= -7 and q.max() <= 7
+    assert np.all(np.abs(q).max(axis=1) == 7)
+    assert np.allclose(s, (np.abs(W).max(axis=1) / 7).astype(np.float32), rtol=0, atol=0)
     err = np.abs(W - q.astype(np.float64) * s[:, None, :].astype(np.float64))
     assert np.all(err <= s[:, None, :].astype(np.float64) / 2 * (1 + 1e-6))
 
