@@ -9,7 +9,7 @@ JSON line: throughput (tokens/s), the roofline position of the dominant
 kernel (timed with HIP events around its launches inside the timed region),
 and the CPU oracle timed on a bounded sample of the same layer.
 
-  python bench.py [--steps K] [--warmup W] [--workload c2|c1|c3|c4|c5]
+  python bench.py [--steps K] [--warmup W] [--workload c2|c1|c3|c4|c5|c6]
 """
 from __future__ import annotations
 
@@ -39,7 +39,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="c2", help="c1..c5 (default c2: Mixtral decode, T=16)")
+    ap.add_argument("--workload", default="c2", help="c1..c5, or c6 (int4 decode, a next row) (default c2: Mixtral decode, T=16)")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
@@ -62,13 +62,14 @@ def algorithmic(sp, counts):
     and p*m (down) elements per touched expert, plus int8 scales.  Activation
     bytes: x read, hidden H written and read back (bf16), y written.
     Flops: 2*m*p per row per m x p matrix (the pages' |O| rounds to this)."""
-    wb = {"f32": 4, "bf16": 2, "i8": 1}[sp.w_dtype]
+    wb = {"f32": 4, "bf16": 2, "i8": 1, "i4": 0.5}[sp.w_dtype]
     ab = 4 if sp.x_dtype == "f32" else 2
     G = 2 if sp.kind == "swiglu" else 1
     touched = sum(1 for c in counts if c > 0)
     rows = sp.T * sp.k
-    up_w = touched * G * sp.m * sp.p * wb + (touched * G * sp.p * 4 if sp.w_dtype == "i8" else 0)
-    dn_w = touched * sp.p * sp.m * wb + (touched * sp.m * 4 if sp.w_dtype == "i8" else 0)
+    q = sp.w_dtype in ("i8", "i4")
+    up_w = int(touched * G * sp.m * sp.p * wb) + (touched * G * sp.p * 4 if q else 0)
+    dn_w = int(touched * sp.p * sp.m * wb) + (touched * sp.m * 4 if q else 0)
     h_bytes = rows * sp.p * (4 if sp.w_dtype == "f32" else 2)
     up_bytes = up_w + sp.T * sp.m * ab + h_bytes
     dn_bytes = dn_w + h_bytes + sp.T * sp.m * 4 * 2  # fp32 accumulator read-modify-write
@@ -256,7 +257,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": {"f32": "f32", "bf16": "bf16", "i8": "bf16"}[sp.w_dtype],
+        "dtype": {"f32": "f32", "bf16": "bf16", "i8": "bf16", "i4": "bf16"}[sp.w_dtype],
         "data": "synthetic",
         "config": {"workload": sp.name, "T": sp.T, "m": sp.m, "p": sp.p, "E": sp.E, "k": sp.k, "expert": sp.kind,
                    "weights": sp.w_dtype, "activations": sp.x_dtype, "parallelism": "none (1 GPU)"},

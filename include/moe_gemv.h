@@ -29,7 +29,8 @@
  *    64, T*k < 2^31.  T == 0 is a successful no-op.
  *  - Supported (activation / weight / expert) combinations: F32/F32/RELU,
  *    F32/F32/SWIGLU, BF16/BF16/RELU, BF16/BF16/SWIGLU, BF16/I8/SWIGLU,
- *    BF16/I8/RELU.  Anything else returns MOE_ERR_UNSUPPORTED.
+ *    BF16/I8/RELU, BF16/I4/SWIGLU, BF16/I4/RELU (I4: m and p multiples of
+ *    128).  Anything else returns MOE_ERR_UNSUPPORTED.
  */
 #ifndef MOE_GEMV_H
 #define MOE_GEMV_H
@@ -50,7 +51,7 @@ typedef enum {
   MOE_ERR_OOM = 5          /* device allocation failed */
 } moe_status;
 
-typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_I8 = 2 } moe_dtype;
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_I8 = 2, MOE_I4 = 3 } moe_dtype;
 typedef enum { MOE_MLP_RELU = 0, MOE_SWIGLU = 1 } moe_ffn_kind;
 
 #define MOE_MAX_EXPERTS 64
@@ -77,12 +78,14 @@ int moe_abi_version(void);
  *  m, p, E       hidden size, expert inner size, number of experts.
  *  kind          MOE_MLP_RELU (w1 = W1, w2 = W2, w_up must be NULL) or
  *                MOE_SWIGLU (w1 = gate W1, w_up = up W3, w2 = down W2).
- *  w_dtype       MOE_F32, MOE_BF16 or MOE_I8.
- *  w1, w_up      device [E][m][p] in w_dtype.
- *  w2            device [E][p][m] in w_dtype.
- *  s1, s_up      MOE_I8 only: device fp32 [E][p] per-output-channel scales
- *                of w1 and w_up (the weight is q * s); NULL otherwise.
- *  s2            MOE_I8 only: device fp32 [E][m] scales of w2; NULL otherwise.
+ *  w_dtype       MOE_F32, MOE_BF16, MOE_I8 or MOE_I4.
+ *  w1, w_up      device [E][m][p] in w_dtype (MOE_I4: one int8 per weight,
+ *                holding q in [-8, 7]; stored packed two per byte).
+ *  w2            device [E][p][m] in w_dtype (MOE_I4 as above).
+ *  s1, s_up      MOE_I8 / MOE_I4 only: device fp32 [E][p] per-output-channel
+ *                scales of w1 and w_up (the weight is q * s); NULL otherwise.
+ *  s2            MOE_I8 / MOE_I4 only: device fp32 [E][m] scales of w2; NULL
+ *                otherwise.
  *  stream        packing runs on this stream; the call synchronises it
  *                before returning, so the inputs may be freed afterwards.
  *  out           receives the handle; release it with moe_weights_destroy.

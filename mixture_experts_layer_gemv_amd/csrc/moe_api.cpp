@@ -103,7 +103,13 @@ int check_shape(int T, int m, int p, int E, int k) {
   return MOE_OK;
 }
 
-bool valid_dtype(int d) { return d == MOE_F32 || d == MOE_BF16 || d == MOE_I8; }
+bool valid_dtype(int d) { return d == MOE_F32 || d == MOE_BF16 || d == MOE_I8 || d == MOE_I4; }
+
+// Integer weights (int8 or int4, with per-output-channel scales).
+bool quantised(int d) { return d == MOE_I8 || d == MOE_I4; }
+
+// Weight bits of the skinny kernels' variants: 0 (bf16), 8 or 4.
+int weight_bits(const moe_weights* W) { return W->w_dtype == MOE_I8 ? 8 : (W->w_dtype == MOE_I4 ? 4 : 0); }
 
 int check_combo(int x_dtype, int w_dtype) {
   if (x_dtype != MOE_F32 && x_dtype != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "x dtype %d unsupported", x_dtype);
@@ -169,7 +175,7 @@ Path ffn_path(const moe_weights* W, int T, int k) {
 int skinny_mt(const moe_weights* W, int T, int k) {
   const long long avg = ((long long)T * k + W->E - 1) / W->E;
   const int mt = env_int("MOE_SKINNY_MT", avg <= 12 ? 1 : (avg <= 24 ? 2 : 4));
-  if (W->w_dtype == MOE_I8) return mt <= 1 ? 1 : 2;  // the int8 kernels stop at two M tiles
+  if (quantised(W->w_dtype)) return mt <= 1 ? 1 : 2;  // the integer kernels stop at two M tiles
   return mt <= 1 ? 1 : (mt == 2 ? 2 : 4);
 }
 
@@ -183,9 +189,10 @@ int skinny_mt(const moe_weights* W, int T, int k) {
 // either way: the packing, or the up projection's prologue.
 bool skinny_packed(const moe_weights* W, int T, int k) {
   if (W->w_dtype == MOE_F32) return false;
-  // int8 weights span 64 k per unit, so two M tiles already read four
-  // activation fragments per unit: packed and shared measured ahead there
-  const int dflt = skinny_mt(W, T, k) >= (W->w_dtype == MOE_I8 ? 2 : 4) ? 1 : 0;
+  // int8 (int4) weights span 64 (128) k per unit, so two M tiles already
+  // read four (eight) activation fragments per unit: packed and shared
+  // measured ahead there
+  const int dflt = skinny_mt(W, T, k) >= (quantised(W->w_dtype) ? 2 : 4) ? 1 : 0;
   return env_int("MOE_SKINNY_PACK", dflt) != 0;
 }
 
@@ -252,10 +259,10 @@ int down_ksplit(long long items) {
 // or int8 weights whose 16-byte unit spans 64 k).
 // The down projection (one stream per tile) always takes 4 (2 with four M
 // tiles, for registers); measured on the decode layers.
-int skinny_ct(int mt, bool i8, int g, const char* env) {
+int skinny_ct(int mt, int qb, int g, const char* env) {
   const int forced = env_int(env, 0);
   if (forced > 0) return forced >= 4 ? 4 : (forced >= 2 ? 2 : 1);
-  const int aw = mt * (i8 ? 2 : 1);
+  const int aw = mt * (qb == 8 ? 2 : (qb == 4 ? 4 : 1));
   if (aw <= 1 && g > 1) return 1;
   if (mt >= 4) return 2;
   return 4;
@@ -297,14 +304,15 @@ void int8_down_shape(const moe_weights* W, int T, int k, int R, int* ct, int* ks
 // unweighted rows are kept per slice) and the launch.
 DownShape skinny_down_shape(const moe_weights* W, int T, int k) {
   const int mt = skinny_mt(W, T, k);
-  const bool i8 = W->w_dtype == MOE_I8;
+  const int qb = weight_bits(W);
+  const bool i8 = qb != 0;  // integer weights (int8 or int4)
   const bool packed = skinny_packed(W, T, k);
   const char* wv = getenv("MOE_SKINNY_WAVES");
   const bool splitk = wv && *wv ? wv[0] == 'k' : !packed;
   const bool shared = packed && !splitk && env_int("MOE_SKINNY_SA", 1) != 0;
   const int R = moe::skinny_rows(mt);
   const int Wp = W->E + (int)((long long)T * k / R);
-  DownShape d{skinny_ct(mt, i8, 1, "MOE_DOWN_CT"), 1};
+  DownShape d{skinny_ct(mt, qb, 1, "MOE_DOWN_CT"), 1};
   d.ks = down_ksplit((long long)(splitk ? W->m / 16 / d.ct : moe::skinny_groups(W->m, d.ct)) * Wp);
   if (i8 && shared && env_int("MOE_DOWN_CT", 0) <= 0 && env_int("MOE_DOWN_KSPLIT", 0) <= 0)
     int8_down_shape(W, T, k, R, &d.ct, &d.ks);
@@ -404,7 +412,8 @@ int run_gemm(const moe_weights* W, const FfnIo& io, int min_rows, uint16_t* hpk,
 int run_skinny(const moe_weights* W, const FfnIo& io, int max_rows, hipStream_t s, bool x_packed = false) {
   const int m = W->m, p = W->p, E = W->E, T = io.T, k = io.k;
   const bool swiglu = W->kind == MOE_SWIGLU;
-  const bool i8 = W->w_dtype == MOE_I8;
+  const int qb = weight_bits(W);
+  const bool i8 = qb != 0;  // integer weights (int8 or int4)
   const int mt = skinny_mt(W, T, k);
   const bool packed = skinny_packed(W, T, k);
   // waves split the reduction unless the activations are packed (measured)
@@ -460,7 +469,7 @@ int run_skinny(const moe_weights* W, const FfnIo& io, int max_rows, hipStream_t 
   // rows copied, the split still measured ahead on the skewed layer (167
   // against 173 us).
   const int up_epi = swiglu ? moe::EPI_UP_SWIGLU : moe::EPI_UP_RELU;
-  const int up_ct = skinny_ct(mt, i8, swiglu ? 2 : 1, "MOE_UP_CT");
+  const int up_ct = skinny_ct(mt, qb, swiglu ? 2 : 1, "MOE_UP_CT");
   const bool wide = max_rows <= 0 && mt == 4 && up_ct == 2 && a.shared_act && !i8 && !a.topk_idx &&
                     env_int("MOE_SKINNY_WIDE", 1) != 0;
   constexpr int kWideMt = 12;
@@ -476,7 +485,7 @@ int run_skinny(const moe_weights* W, const FfnIo& io, int max_rows, hipStream_t 
   }
   MOE_TRY_HIP(run("ffn_up", s, [&]() -> hipError_t {
     return wide ? moe::launch_ffn_skinny_split(a, aw, up_epi, s)
-                : moe::launch_ffn_skinny(a, up_epi, i8, mt, up_ct, splitk, s);
+                : moe::launch_ffn_skinny(a, up_epi, qb, mt, up_ct, splitk, s);
   }));
   // down: H -> weighted combine (or unweighted rows)
   a.topk_idx = nullptr;
@@ -515,7 +524,7 @@ int run_skinny(const moe_weights* W, const FfnIo& io, int max_rows, hipStream_t 
   }
   MOE_TRY_HIP(run("ffn_down", s, [&]() -> hipError_t {
     return wide_dn ? moe::launch_ffn_skinny_split(a, aw, dn_epi, s)
-                   : moe::launch_ffn_skinny(a, dn_epi, i8, mt, dn_ct, splitk, s);
+                   : moe::launch_ffn_skinny(a, dn_epi, qb, mt, dn_ct, splitk, s);
   }));
   return MOE_OK;
 }
@@ -613,9 +622,12 @@ int moe_weights_create(int m, int p, int E, int kind, int w_dtype, const void* w
   const bool swiglu = kind == MOE_SWIGLU;
   if (!w1 || !w2 || (swiglu && !w_up)) return fail(MOE_ERR_INVALID_ARG, "required weight pointer is NULL");
   if (!swiglu && w_up) return fail(MOE_ERR_INVALID_ARG, "w_up must be NULL for the ReLU MLP");
-  const bool i8 = w_dtype == MOE_I8;
-  if (i8 && (!s1 || !s2 || (swiglu && !s_up))) return fail(MOE_ERR_INVALID_ARG, "int8 weights need their scales");
-  if (!i8 && (s1 || s2 || s_up)) return fail(MOE_ERR_INVALID_ARG, "scales are only for int8 weights");
+  const bool i8 = quantised(w_dtype);
+  const int qb = w_dtype == MOE_I8 ? 8 : (w_dtype == MOE_I4 ? 4 : 0);
+  if (i8 && (!s1 || !s2 || (swiglu && !s_up))) return fail(MOE_ERR_INVALID_ARG, "integer weights need their scales");
+  if (!i8 && (s1 || s2 || s_up)) return fail(MOE_ERR_INVALID_ARG, "scales are only for integer weights");
+  if (w_dtype == MOE_I4 && (m % 128 || p % 128))
+    return fail(MOE_ERR_UNSUPPORTED, "int4 weights need m=%d and p=%d to be multiples of 128", m, p);
   if (!aligned16(w1) || !aligned16(w2) || (w_up && !aligned16(w_up)) || (s1 && !aligned16(s1)) ||
       (s2 && !aligned16(s2)) || (s_up && !aligned16(s_up)))
     return fail(MOE_ERR_INVALID_ARG, "weight pointers must be 16-byte aligned");
@@ -628,8 +640,8 @@ int moe_weights_create(int m, int p, int E, int kind, int w_dtype, const void* w
     up3_b = swiglu ? up_b : 0;
     dn_b = (size_t)E * p * m * 4;
   } else {
-    up_b = moe::packed_bytes(E, m, p, G, i8);
-    dn_b = moe::packed_bytes(E, p, m, 1, i8);
+    up_b = moe::packed_bytes(E, m, p, G, qb);
+    dn_b = moe::packed_bytes(E, p, m, 1, qb);
     if (i8) sc_b = align256((size_t)E * p * 4) * (swiglu ? 2 : 1) + align256((size_t)E * m * 4);
   }
   const size_t total = align256(up_b) + align256(up3_b) + align256(dn_b) + sc_b;
@@ -665,9 +677,10 @@ int moe_weights_create(int m, int p, int E, int kind, int w_dtype, const void* w
     W->s_gate = static_cast<float*>(carve((size_t)E * p * 4));
     if (swiglu) W->s_up = static_cast<float*>(carve((size_t)E * p * 4));
     W->s_down = static_cast<float*>(carve((size_t)E * m * 4));
-    e = moe::launch_pack_i8(static_cast<const int8_t*>(w1), W->up, E, m, p, G, 0, s);
-    if (e == hipSuccess && swiglu) e = moe::launch_pack_i8(static_cast<const int8_t*>(w_up), W->up, E, m, p, G, 1, s);
-    if (e == hipSuccess) e = moe::launch_pack_i8(static_cast<const int8_t*>(w2), W->down, E, p, m, 1, 0, s);
+    auto pack = qb == 8 ? moe::launch_pack_i8 : moe::launch_pack_i4;
+    e = pack(static_cast<const int8_t*>(w1), W->up, E, m, p, G, 0, s);
+    if (e == hipSuccess && swiglu) e = pack(static_cast<const int8_t*>(w_up), W->up, E, m, p, G, 1, s);
+    if (e == hipSuccess) e = pack(static_cast<const int8_t*>(w2), W->down, E, p, m, 1, 0, s);
     if (e == hipSuccess) e = hipMemcpyAsync(W->s_gate, s1, (size_t)E * p * 4, hipMemcpyDeviceToDevice, s);
     if (e == hipSuccess && swiglu) e = hipMemcpyAsync(W->s_up, s_up, (size_t)E * p * 4, hipMemcpyDeviceToDevice, s);
     if (e == hipSuccess) e = hipMemcpyAsync(W->s_down, s2, (size_t)E * m * 4, hipMemcpyDeviceToDevice, s);

@@ -65,6 +65,24 @@ __device__ __forceinline__ bf16x8_t i8x8_to_bf16(uint32_t lo, uint32_t hi) {
   return as_bf16x8(r);
 }
 
+// 8 signed 4-bit values (one dword, nibble i = bits 4i..4i+3) -> 8 bf16;
+// |q| <= 8 is exact in bf16.
+__device__ __forceinline__ bf16x8_t i4x8_to_bf16(uint32_t d) {
+  u32x4_t r;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const float f0 = (float)((int)(d << (28 - 8 * q)) >> 28);
+    const float f1 = (float)((int)(d << (24 - 8 * q)) >> 28);
+    r[q] = __builtin_amdgcn_perm(__float_as_uint(f1), __float_as_uint(f0), 0x07060302u);
+  }
+  return as_bf16x8(r);
+}
+
+// Weight bits of a variant: 0 (bf16), 8 (int8) or 4 (int4).  A 16-byte weight
+// load of a lane covers q_ah(qb) MFMA K steps of 32, so that many activation
+// fragments go with it.
+constexpr int q_ah(int qb) { return qb == 8 ? 2 : (qb == 4 ? 4 : 1); }
+
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
 
 // Waits until at most n units of STEP vector-memory operations each are
@@ -99,17 +117,17 @@ __device__ __forceinline__ void wait_units_nc(int nc, int n) {
 struct Plan {
   int acc, stage, wpe, depth;
 };
-constexpr Plan plan(int mt, int g, int ct, bool i8, bool sa) {
+constexpr Plan plan(int mt, int g, int ct, int qb, bool sa) {
   const int acc = ct * g * mt * 4;
-  const int act = mt * (i8 ? 2 : 1) * 4;  // one K unit of activations
+  const int act = mt * q_ah(qb) * 4;  // one K unit of activations
   // with shared activations (sa) only the weights are in flight in
   // registers; the unit being consumed is read from LDS
   const int stage = ct * g * 4 + (sa ? 0 : act);
   // addresses, loop state, int8 conversion (and, shared, the unit read from LDS)
-  const int fixed = (i8 ? 64 : 40) + (sa ? act + (i8 ? 8 : 0) : 0);
+  const int fixed = (qb == 4 ? 72 : (qb ? 64 : 40)) + (sa ? act + (qb ? 8 : 0) : 0);
   // shared activations: DA = depth + 1 units of the ring in at most 64 KiB,
   // so two workgroups fit a CU's LDS
-  const int dmax0 = sa ? 64 / (mt * (i8 ? 2 : 1)) - 1 : 6;
+  const int dmax0 = sa ? 64 / (mt * q_ah(qb)) - 1 : 6;
   const int dmax = dmax0 < 6 ? dmax0 : 6;
   const int d128 = (128 - fixed - acc) / stage;
   if (d128 >= 4) return Plan{acc, stage, 4, d128 < dmax ? d128 : dmax};
@@ -120,8 +138,8 @@ constexpr Plan plan(int mt, int g, int ct, bool i8, bool sa) {
 typedef u32x4_t __attribute__((address_space(3))) lds_u32x4_t;
 
 // Units of the shared-activation ring of one variant (16-byte lanes x 64).
-constexpr int sa_ring_units(int mt, int g, int ct, bool i8, bool sa) {
-  return sa ? (plan(mt, g, ct, i8, sa).depth + 1) * mt * (i8 ? 2 : 1) : 0;
+constexpr int sa_ring_units(int mt, int g, int ct, int qb, bool sa) {
+  return sa ? (plan(mt, g, ct, qb, sa).depth + 1) * mt * q_ah(qb) : 0;
 }
 
 // The dispatch offsets of a launch in LDS (offs_s[0..E]): read, or derived
@@ -176,15 +194,15 @@ __device__ __forceinline__ int skinny_items(const SkinnyArgs& A, const PairScan&
 // workgroup writes the derived dispatch (with topk_idx).  sa_ring: the
 // workgroup's shared-activation ring, at least sa_ring_units() KiB (unused
 // otherwise).
-template <int MT, int G, int CT, bool I8, int EPI, int NW, bool SPLITK, bool SA>
+template <int MT, int G, int CT, int QB, int EPI, int NW, bool SPLITK, bool SA>
 __device__ __forceinline__ void skinny_body(const SkinnyArgs& A, const SkinnyWork& wk, bool real, const PairScan& ps,
                                             bool publish, const int* offs_s, DispatchLds<NW>& DL,
                                             lds_u32x4_t* sa_ring) {
   static_assert(!(SA && SPLITK), "shared activations need every wave on the same K range");
-  constexpr int D = plan(MT, G, CT, I8, SA).depth;
+  constexpr int D = plan(MT, G, CT, QB, SA).depth;
   constexpr int R = 16 * MT;        // rows per work item
-  constexpr int AH = I8 ? 2 : 1;    // activation loads per K unit
-  constexpr int UK = I8 ? 64 : 32;  // k per unit
+  constexpr int AH = q_ah(QB);  // activation loads per K unit
+  constexpr int UK = 32 * AH;   // k per unit
   // Shared activations: the NAF activation fragments of a K unit are copied
   // once per workgroup into an LDS ring of DA units (wave w copies fragments
   // w, w + NW, ...: NC of them, at most CPW; waves past NAF copy none) and
@@ -349,11 +367,19 @@ __device__ __forceinline__ void skinny_body(const SkinnyArgs& A, const SkinnyWor
   do {                                                                                                 \
     MOE_ACT_FETCH(slot, u, after)                                                                      \
     _Pragma("unroll") for (int c = 0; c < CT; ++c) {                                                   \
-      if constexpr (I8) {                                                                              \
+      if constexpr (QB == 8) {                                                                         \
         _Pragma("unroll") for (int h = 0; h < 2; ++h) {                                                \
           _Pragma("unroll") for (int g = 0; g < G; ++g) {                                              \
             const u32x4_t q = wb[slot][c][g];                                                          \
             const bf16x8_t bw = h == 0 ? i8x8_to_bf16(q[0], q[1]) : i8x8_to_bf16(q[2], q[3]);          \
+            _Pragma("unroll") for (int mt = 0; mt < MT; ++mt) acc[c][g][mt] =                          \
+                __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(MOE_ACT(slot, mt, h)), bw, acc[c][g][mt], 0, 0, 0); \
+          }                                                                                            \
+        }                                                                                              \
+      } else if constexpr (QB == 4) {                                                                  \
+        _Pragma("unroll") for (int h = 0; h < 4; ++h) {                                                \
+          _Pragma("unroll") for (int g = 0; g < G; ++g) {                                              \
+            const bf16x8_t bw = i4x8_to_bf16(wb[slot][c][g][h]);                                       \
             _Pragma("unroll") for (int mt = 0; mt < MT; ++mt) acc[c][g][mt] =                          \
                 __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(MOE_ACT(slot, mt, h)), bw, acc[c][g][mt], 0, 0, 0); \
           }                                                                                            \
@@ -412,7 +438,7 @@ __device__ __forceinline__ void skinny_body(const SkinnyArgs& A, const SkinnyWor
     const int r = row0 + row;
     if constexpr (EPI == EPI_UP_SWIGLU) {
       float gv = v[0], uv = v[G - 1];
-      if constexpr (I8) {
+      if constexpr (QB != 0) {
         gv *= A.scale0[(size_t)e * A.N + col];
         uv *= A.scale1[(size_t)e * A.N + col];
       }
@@ -420,12 +446,12 @@ __device__ __forceinline__ void skinny_body(const SkinnyArgs& A, const SkinnyWor
           f32_to_bf16(silu(gv) * uv);
     } else if constexpr (EPI == EPI_UP_RELU) {
       float gv = v[0];
-      if constexpr (I8) gv *= A.scale0[(size_t)e * A.N + col];
+      if constexpr (QB != 0) gv *= A.scale0[(size_t)e * A.N + col];
       A.h_out[A.h_packed ? packed_index(prow0 + row, col, A.N) : (size_t)r * A.N + col] =
           f32_to_bf16(gv > 0.0f ? gv : 0.0f);
     } else {
       float o2 = v[0];
-      if constexpr (I8) o2 *= A.scale0[(size_t)e * A.N + col];
+      if constexpr (QB != 0) o2 *= A.scale0[(size_t)e * A.N + col];
       if constexpr (EPI == EPI_DOWN_ACC) {
         const int a = A.perm[r];
         unsafeAtomicAdd(A.f_out + (size_t)(a / A.topk) * A.N + col, A.topk_w[a] * o2);
@@ -486,16 +512,16 @@ __device__ __forceinline__ void skinny_body(const SkinnyArgs& A, const SkinnyWor
 // padding pairs past the last real one interleaved, so none of them is left
 // for the end of a many-round launch); block 0 publishes the derived
 // dispatch.
-template <int MT, int G, int CT, bool I8, int EPI, int NW, bool SPLITK, bool SA>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(plan(MT, G, CT, I8, SA).wpe))) void
+template <int MT, int G, int CT, int QB, int EPI, int NW, bool SPLITK, bool SA>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(plan(MT, G, CT, QB, SA).wpe))) void
 k_ffn_skinny(const SkinnyArgs A) {
-  constexpr int units = sa_ring_units(MT, G, CT, I8, SA);
+  constexpr int units = sa_ring_units(MT, G, CT, QB, SA);
   __shared__ __attribute__((aligned(16))) u32x4_t ring[units > 0 ? units * 64 : 1];
   __shared__ DispatchLds<NW> DL;
   __shared__ int offs_s[kMaxExperts + 1];
   skinny_offsets<NW>(A, DL, offs_s);
   const PairScan ps = pair_scan(A, offs_s, 16 * MT);
-  skinny_body<MT, G, CT, I8, EPI, NW, SPLITK, SA>(A, skinny_work(xcd_logical(blockIdx.x, gridDim.x), A.W, A.ksplit),
+  skinny_body<MT, G, CT, QB, EPI, NW, SPLITK, SA>(A, skinny_work(xcd_logical(blockIdx.x, gridDim.x), A.W, A.ksplit),
                                                   true, ps, blockIdx.x == 0, offs_s, DL, (lds_u32x4_t*)ring);
 }
 
@@ -516,7 +542,7 @@ template <int G, int EPI, int NW>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) void k_ffn_skinny_split(
     const SkinnyArgs AN, const SkinnyArgs AW) {
   constexpr int CT = split_ct(G);
-  constexpr int uw = sa_ring_units(12, G, CT, false, true), un = sa_ring_units(4, G, CT, false, true);
+  constexpr int uw = sa_ring_units(12, G, CT, 0, true), un = sa_ring_units(4, G, CT, 0, true);
   __shared__ __attribute__((aligned(16))) u32x4_t ring[(uw > un ? uw : un) * 64];
   __shared__ DispatchLds<NW> DL;
   __shared__ int offs_s[kMaxExperts + 1];
@@ -525,76 +551,80 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   const int nw = skinny_items<false, CT>(AW, pw), nn = skinny_items<false, CT>(AN, pn);
   const int item = xcd_item(blockIdx.x, nw, nn);
   if (item >= 0 && item < nw)
-    skinny_body<12, G, CT, false, EPI, NW, false, true>(AW, skinny_work(item, max(pw.total, 1), 1), true, pw, false, offs_s,
+    skinny_body<12, G, CT, 0, EPI, NW, false, true>(AW, skinny_work(item, max(pw.total, 1), 1), true, pw, false, offs_s,
                                                         DL, (lds_u32x4_t*)ring);
   else
-    skinny_body<4, G, CT, false, EPI, NW, false, true>(AN, skinny_work(item < 0 ? 0 : item - nw, max(pn.total, 1), 1),
+    skinny_body<4, G, CT, 0, EPI, NW, false, true>(AN, skinny_work(item < 0 ? 0 : item - nw, max(pn.total, 1), 1),
                                                        item >= 0, pn, false, offs_s, DL, (lds_u32x4_t*)ring);
 }
 
 // One variant; variants whose accumulators exceed the register budget are
 // never built (the host does not ask for them).
-template <int MT, int G, int CT, bool I8, int EPI, bool SPLITK, bool SA>
+template <int MT, int G, int CT, int QB, int EPI, bool SPLITK, bool SA>
 hipError_t launch_one(const SkinnyArgs& a, dim3 grid, hipStream_t s) {
   if constexpr (CT * G * MT * 4 > 96) {
     return hipErrorInvalidValue;
   } else {
-    k_ffn_skinny<MT, G, CT, I8, EPI, 4, SPLITK, SA><<<grid, 256, 0, s>>>(a);
+    k_ffn_skinny<MT, G, CT, QB, EPI, 4, SPLITK, SA><<<grid, 256, 0, s>>>(a);
     return hipGetLastError();
   }
 }
 
-template <int MT, int CT, bool I8, bool SPLITK, bool SA>
+template <int MT, int CT, int QB, bool SPLITK, bool SA>
 hipError_t launch_ct(const SkinnyArgs& a, int epi, hipStream_t s) {
   const int NG = SPLITK ? a.N / 16 / CT : skinny_groups(a.N, CT);
   const long long work = (long long)NG * a.W * a.ksplit;
   const long long nblk = (work + 7) / 8 * 8;
   const dim3 grid((unsigned)nblk);
   switch (epi) {
-    case EPI_UP_SWIGLU: return launch_one<MT, 2, CT, I8, EPI_UP_SWIGLU, SPLITK, SA>(a, grid, s);
-    case EPI_UP_RELU: return launch_one<MT, 1, CT, I8, EPI_UP_RELU, SPLITK, SA>(a, grid, s);
-    case EPI_DOWN_ACC: return launch_one<MT, 1, CT, I8, EPI_DOWN_ACC, SPLITK, SA>(a, grid, s);
-    default: return launch_one<MT, 1, CT, I8, EPI_DOWN_ROWS, SPLITK, SA>(a, grid, s);
+    case EPI_UP_SWIGLU: return launch_one<MT, 2, CT, QB, EPI_UP_SWIGLU, SPLITK, SA>(a, grid, s);
+    case EPI_UP_RELU: return launch_one<MT, 1, CT, QB, EPI_UP_RELU, SPLITK, SA>(a, grid, s);
+    case EPI_DOWN_ACC: return launch_one<MT, 1, CT, QB, EPI_DOWN_ACC, SPLITK, SA>(a, grid, s);
+    default: return launch_one<MT, 1, CT, QB, EPI_DOWN_ROWS, SPLITK, SA>(a, grid, s);
   }
 }
 
 // Shared activations only where the waves of a workgroup share a K range
 // (columns split over the waves) and the rows are packed; twelve M tiles
 // exist only in that form.
-template <int MT, int CT, bool I8, bool SPLITK>
+template <int MT, int CT, int QB, bool SPLITK>
 hipError_t launch_sa(const SkinnyArgs& a, int epi, hipStream_t s) {
   if constexpr (!SPLITK) {
-    if (a.shared_act) return launch_ct<MT, CT, I8, SPLITK, true>(a, epi, s);
+    if (a.shared_act) return launch_ct<MT, CT, QB, SPLITK, true>(a, epi, s);
   }
   if constexpr (MT > 4) {
     return hipErrorInvalidValue;
   } else {
-    return launch_ct<MT, CT, I8, SPLITK, false>(a, epi, s);
+    return launch_ct<MT, CT, QB, SPLITK, false>(a, epi, s);
   }
 }
 
-template <int MT, bool I8, bool SPLITK>
+template <int MT, int QB, bool SPLITK>
 hipError_t launch_mt(const SkinnyArgs& a, int epi, int ct, hipStream_t s) {
   if constexpr (MT < 4) {
-    if (ct >= 4) return launch_sa<MT, 4, I8, SPLITK>(a, epi, s);
+    if (ct >= 4) return launch_sa<MT, 4, QB, SPLITK>(a, epi, s);
   }
-  if (ct >= 2) return launch_sa<MT, 2, I8, SPLITK>(a, epi, s);
-  return launch_sa<MT, 1, I8, SPLITK>(a, epi, s);
+  if (ct >= 2) return launch_sa<MT, 2, QB, SPLITK>(a, epi, s);
+  return launch_sa<MT, 1, QB, SPLITK>(a, epi, s);
 }
 
 template <bool SPLITK>
-hipError_t launch_split(const SkinnyArgs& a, int epi, bool i8, int mt, int ct, hipStream_t s) {
-  if (i8) {  // int8 stops at two M tiles: four spill registers
-    if (mt <= 1) return launch_mt<1, true, SPLITK>(a, epi, ct, s);
-    return launch_mt<2, true, SPLITK>(a, epi, ct, s);
+hipError_t launch_split(const SkinnyArgs& a, int epi, int qb, int mt, int ct, hipStream_t s) {
+  if (qb == 8) {  // int8 stops at two M tiles: four spill registers
+    if (mt <= 1) return launch_mt<1, 8, SPLITK>(a, epi, ct, s);
+    return launch_mt<2, 8, SPLITK>(a, epi, ct, s);
   }
-  if (mt <= 1) return launch_mt<1, false, SPLITK>(a, epi, ct, s);
-  if (mt == 2) return launch_mt<2, false, SPLITK>(a, epi, ct, s);
-  if (mt <= 4) return launch_mt<4, false, SPLITK>(a, epi, ct, s);
+  if (qb == 4) {  // int4: as int8
+    if (mt <= 1) return launch_mt<1, 4, SPLITK>(a, epi, ct, s);
+    return launch_mt<2, 4, SPLITK>(a, epi, ct, s);
+  }
+  if (mt <= 1) return launch_mt<1, 0, SPLITK>(a, epi, ct, s);
+  if (mt == 2) return launch_mt<2, 0, SPLITK>(a, epi, ct, s);
+  if (mt <= 4) return launch_mt<4, 0, SPLITK>(a, epi, ct, s);
   if constexpr (SPLITK) {
     return hipErrorInvalidValue;
   } else {
-    return launch_mt<12, false, SPLITK>(a, epi, ct, s);
+    return launch_mt<12, 0, SPLITK>(a, epi, ct, s);
   }
 }
 
@@ -623,10 +653,11 @@ hipError_t launch_ffn_skinny_split(const SkinnyArgs& narrow, const SkinnyArgs& w
   return hipGetLastError();
 }
 
-hipError_t launch_ffn_skinny(const SkinnyArgs& a, int epi, bool i8, int mt, int ct, bool splitk, hipStream_t s) {
+hipError_t launch_ffn_skinny(const SkinnyArgs& a, int epi, int qb, int mt, int ct, bool splitk, hipStream_t s) {
+  if (qb != 0 && qb != 8 && qb != 4) return hipErrorInvalidValue;
   if (a.shared_act && (splitk || !a.packed)) return hipErrorInvalidValue;
-  if (mt > 4 && (mt != 12 || i8 || splitk || !a.shared_act)) return hipErrorInvalidValue;
-  return splitk ? launch_split<true>(a, epi, i8, mt, ct, s) : launch_split<false>(a, epi, i8, mt, ct, s);
+  if (mt > 4 && (mt != 12 || qb || splitk || !a.shared_act)) return hipErrorInvalidValue;
+  return splitk ? launch_split<true>(a, epi, qb, mt, ct, s) : launch_split<false>(a, epi, qb, mt, ct, s);
 }
 
 }  // namespace moe

@@ -35,6 +35,8 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
 // n = nb*16 + (l & 15):
 //   bf16 (U = K/32): element j (0..7) is k = u*32 + 8*(l >> 4) + j
 //   int8 (U = K/64): byte j (0..15) is  k = u*64 + 32*(j >> 3) + 8*(l >> 4) + (j & 7)
+//   int4 (U = K/128): nibble j (0..31; byte j/2, low nibble first) is
+//                    k = u*128 + 32*(j >> 3) + 8*(l >> 4) + (j & 7)
 // which is the B-operand order of v_mfma_f32_16x16x32_bf16.  A wave loading
 // one unit reads 1 KiB of contiguous memory: eight full 128-byte lines.
 // G = 2 interleaves the SwiGLU gate (g = 0) and up (g = 1) matrices so one
@@ -42,13 +44,16 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
 
 constexpr int kUnitBytes = 1024;
 
-inline size_t packed_bytes(int E, int K, int N, int G, bool i8) {
-  const size_t units = (size_t)K / (i8 ? 64 : 32);
+// qb: weight bits, 0 (bf16), 8 (int8) or 4 (int4).
+inline size_t packed_bytes(int E, int K, int N, int G, int qb) {
+  const size_t units = (size_t)K / (qb == 8 ? 64 : (qb == 4 ? 128 : 32));
   return (size_t)E * (size_t)(N / 16) * units * (size_t)G * kUnitBytes;
 }
 
 hipError_t launch_pack_bf16(const uint16_t* src, void* dst, int E, int K, int N, int G, int g, hipStream_t s);
 hipError_t launch_pack_i8(const int8_t* src, void* dst, int E, int K, int N, int G, int g, hipStream_t s);
+// int4 values held one per int8 (in [-8, 7]), packed two per byte.
+hipError_t launch_pack_i4(const int8_t* src, void* dst, int E, int K, int N, int G, int g, hipStream_t s);
 
 // ---- routing ---------------------------------------------------------------
 
@@ -121,10 +126,11 @@ inline int skinny_rows(int mt) { return 16 * mt; }
 
 // mt: 16-row M tiles per work item (1, 2, 4; 12 for bf16 weights with shared
 // activations, ct <= 2 and one column tile for SwiGLU); ct: 16-column tiles
-// per wave sharing each activation load (1, 2, 4).
+// per wave sharing each activation load (1, 2, 4); qb: weight bits (0 bf16,
+// 8 int8, 4 int4; the integer kinds take at most two M tiles).
 // splitk: the four waves of a workgroup split the reduction (partials summed
 // through LDS); otherwise each wave owns its column tiles over the whole range.
-hipError_t launch_ffn_skinny(const SkinnyArgs& a, int epi, bool i8, int mt, int ct, bool splitk, hipStream_t s);
+hipError_t launch_ffn_skinny(const SkinnyArgs& a, int epi, int qb, int mt, int ct, bool splitk, hipStream_t s);
 
 // A projection split by expert size in one launch: `narrow` (four M tiles)
 // for the experts it admits and `wide` (twelve M tiles) for the others, both

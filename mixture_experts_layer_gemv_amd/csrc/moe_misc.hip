@@ -53,6 +53,31 @@ __global__ __launch_bounds__(256) void k_pack_i8(const int8_t* __restrict__ src,
   }
 }
 
+// int4 (held one per int8, in [-8, 7]): 128 k per unit; nibble j of a lane's
+// 32 (low nibble first, byte j / 2) is k = 32 (j / 8) + 8 (lane / 16) + j % 8.
+__global__ __launch_bounds__(256) void k_pack_i4(const int8_t* __restrict__ src, uint4* __restrict__ dst, int E,
+                                                 int K, int N, int G, int g) {
+  const int NB = N / 16, U = K / 128;
+  const size_t total = (size_t)E * NB * U * 64;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (size_t)gridDim.x * blockDim.x) {
+    const int lane = (int)(i & 63);
+    size_t rest = i >> 6;
+    const int u = (int)(rest % U);
+    rest /= U;
+    const int nb = (int)(rest % NB);
+    const int e = (int)(rest / NB);
+    const int n = nb * 16 + (lane & 15);
+    uint32_t d[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+      const int kk = u * 128 + 32 * (j >> 3) + 8 * (lane >> 4) + (j & 7);
+      const uint32_t nib = (uint32_t)(uint8_t)src[((size_t)e * K + kk) * N + n] & 0xFu;
+      d[j >> 3] |= nib << (4 * (j & 7));
+    }
+    dst[((((size_t)e * NB + nb) * U + u) * G + g) * 64 + lane] = make_uint4(d[0], d[1], d[2], d[3]);
+  }
+}
+
 // ---- fp32 expert FFN ------------------------------------------------------------
 //
 // True fp32 arithmetic (one fused multiply-add per term, in increasing k) for
@@ -236,6 +261,12 @@ hipError_t launch_pack_bf16(const uint16_t* src, void* dst, int E, int K, int N,
 hipError_t launch_pack_i8(const int8_t* src, void* dst, int E, int K, int N, int G, int g, hipStream_t s) {
   const size_t total = (size_t)E * (N / 16) * (K / 64) * 64;
   k_pack_i8<<<grid_for(total, 1u << 20), 256, 0, s>>>(src, static_cast<uint4*>(dst), E, K, N, G, g);
+  return hipGetLastError();
+}
+
+hipError_t launch_pack_i4(const int8_t* src, void* dst, int E, int K, int N, int G, int g, hipStream_t s) {
+  const size_t total = (size_t)E * (N / 16) * (K / 128) * 64;
+  k_pack_i4<<<grid_for(total, 1u << 20), 256, 0, s>>>(src, static_cast<uint4*>(dst), E, K, N, G, g);
   return hipGetLastError();
 }
 
