@@ -118,7 +118,7 @@ def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus > 1 or world > 1:
-        print(f"bench.py: this build runs one MoE layer on one GPU; --gpus {max(args.gpus, world)} is not "
+        print(f"bench.py: the layer runs on one GPU; --gpus {max(args.gpus, world)} is not "
               "supported (multi-GPU sharding is a design note only).", file=sys.stderr)
         sys.exit(2)
 
