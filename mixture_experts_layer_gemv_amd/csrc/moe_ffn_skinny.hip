@@ -65,18 +65,21 @@ __device__ __forceinline__ bf16x8_t i8x8_to_bf16(uint32_t lo, uint32_t hi) {
   return as_bf16x8(r);
 }
 
-// 8 signed 4-bit values (one dword, nibble i = bits 4i..4i+3) -> 8 bf16;
-// |q| <= 8 is exact in bf16.
-__device__ __forceinline__ bf16x8_t i4x8_to_bf16(uint32_t d) {
+// 8 int4 weights stored offset by 8 (nibble i = bits 4i..4i+3 holds u = q + 8)
+// -> the 8 bf16 values 128 + u, exactly: the bf16 pattern of 128 has the
+// value's integer part in its 7 mantissa bits, so each value is its nibble
+// placed under 0x4300.  One byte permute per pair (nibble 2i of byte i into
+// the low half, nibble 2i+1 into the high half) and one OR; the products'
+// constant part 136 * sum(x) is removed after the reduction.
+__device__ __forceinline__ bf16x8_t u4x8_to_bf16_biased(uint32_t d) {
+  const uint32_t t0 = d & 0x0F0F0F0Fu, t1 = (d >> 4) & 0x0F0F0F0Fu;
   u32x4_t r;
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const float f0 = (float)((int)(d << (28 - 8 * q)) >> 28);
-    const float f1 = (float)((int)(d << (24 - 8 * q)) >> 28);
-    r[q] = __builtin_amdgcn_perm(__float_as_uint(f1), __float_as_uint(f0), 0x07060302u);
-  }
+  for (int i = 0; i < 4; ++i)
+    r[i] = __builtin_amdgcn_perm(t1, t0, 0x0C000C00u | (uint32_t)i | ((uint32_t)(4 + i) << 16)) | 0x43004300u;
   return as_bf16x8(r);
 }
+constexpr float kI4Bias = 136.0f;  // 128 from the bf16 pattern + 8 from the storage offset
 
 // Weight bits of a variant: 0 (bf16), 8 (int8) or 4 (int4).  A 16-byte weight
 // load of a lane covers q_ah(qb) MFMA K steps of 32, so that many activation
@@ -124,7 +127,9 @@ constexpr Plan plan(int mt, int g, int ct, int qb, bool sa) {
   // registers; the unit being consumed is read from LDS
   const int stage = ct * g * 4 + (sa ? 0 : act);
   // addresses, loop state, int8 conversion (and, shared, the unit read from LDS)
-  const int fixed = (qb == 4 ? 72 : (qb ? 64 : 40)) + (sa ? act + (qb ? 8 : 0) : 0);
+  // (int4 with per-wave activations: the converted weights of later units
+  // are held too)
+  const int fixed = (qb == 4 ? (sa ? 72 : 96) : (qb ? 64 : 40)) + (sa ? act + (qb ? 8 : 0) : 0);
   // shared activations: DA = depth + 1 units of the ring in at most 64 KiB,
   // so two workgroups fit a CU's LDS
   const int dmax0 = sa ? 64 / (mt * q_ah(qb)) - 1 : 6;
@@ -303,6 +308,9 @@ __device__ __forceinline__ void skinny_body(const SkinnyArgs& A, const SkinnyWor
   const size_t tile_stride = (size_t)U * G * 64;
 
   floatx4_t acc[CT][G][MT];
+  floatx4_t acc_x[QB == 4 ? MT : 1];  // int4: sum of the activations over the K range, per row
+#pragma unroll
+  for (int mt = 0; mt < (QB == 4 ? MT : 1); ++mt) acc_x[mt] = floatx4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
   for (int c = 0; c < CT; ++c)
 #pragma unroll
@@ -378,8 +386,13 @@ __device__ __forceinline__ void skinny_body(const SkinnyArgs& A, const SkinnyWor
         }                                                                                              \
       } else if constexpr (QB == 4) {                                                                  \
         _Pragma("unroll") for (int h = 0; h < 4; ++h) {                                                \
+          if (c == 0) {                                                                                \
+            const bf16x8_t ones = as_bf16x8(u32x4_t{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u}); \
+            _Pragma("unroll") for (int mt = 0; mt < MT; ++mt) acc_x[mt] =                              \
+                __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(MOE_ACT(slot, mt, h)), ones, acc_x[mt], 0, 0, 0); \
+          }                                                                                            \
           _Pragma("unroll") for (int g = 0; g < G; ++g) {                                              \
-            const bf16x8_t bw = i4x8_to_bf16(wb[slot][c][g][h]);                                       \
+            const bf16x8_t bw = u4x8_to_bf16_biased(wb[slot][c][g][h]);                                \
             _Pragma("unroll") for (int mt = 0; mt < MT; ++mt) acc[c][g][mt] =                          \
                 __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(MOE_ACT(slot, mt, h)), bw, acc[c][g][mt], 0, 0, 0); \
           }                                                                                            \
@@ -431,6 +444,16 @@ __device__ __forceinline__ void skinny_body(const SkinnyArgs& A, const SkinnyWor
 #undef MOE_ACT
 #undef MOE_ACT_FETCH
 #undef MOE_ISSUE
+  if constexpr (QB == 4) {  // remove the weights' bias: acc holds sum x (q + 136)
+#pragma unroll
+    for (int c = 0; c < CT; ++c)
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[c][g][mt][i] = fmaf(-kI4Bias, acc_x[mt][i], acc[c][g][mt][i]);
+  }
   if (!live) return;  // (shared activations only: other waves past NB returned above)
 
   // Stores one output element (row of the chunk, column) from its G sums.
@@ -577,7 +600,12 @@ hipError_t launch_ct(const SkinnyArgs& a, int epi, hipStream_t s) {
   const long long nblk = (work + 7) / 8 * 8;
   const dim3 grid((unsigned)nblk);
   switch (epi) {
-    case EPI_UP_SWIGLU: return launch_one<MT, 2, CT, QB, EPI_UP_SWIGLU, SPLITK, SA>(a, grid, s);
+    case EPI_UP_SWIGLU:
+      if constexpr (QB == 4 && MT == 2 && CT == 4 && !SA) {  // (would spill: two tiles instead)
+        return launch_ct<MT, 2, QB, SPLITK, SA>(a, epi, s);
+      } else {
+        return launch_one<MT, 2, CT, QB, EPI_UP_SWIGLU, SPLITK, SA>(a, grid, s);
+      }
     case EPI_UP_RELU: return launch_one<MT, 1, CT, QB, EPI_UP_RELU, SPLITK, SA>(a, grid, s);
     case EPI_DOWN_ACC: return launch_one<MT, 1, CT, QB, EPI_DOWN_ACC, SPLITK, SA>(a, grid, s);
     default: return launch_one<MT, 1, CT, QB, EPI_DOWN_ROWS, SPLITK, SA>(a, grid, s);
