@@ -65,18 +65,21 @@ __device__ __forceinline__ bf16x8_t i8x8_to_bf16(uint32_t lo, uint32_t hi) {
   return as_bf16x8(r);
 }
 
-// 8 int4 weights stored offset by 8 (nibble i = bits 4i..4i+3 holds u = q + 8)
-// -> the 8 bf16 values 128 + u, exactly: the bf16 pattern of 128 has the
-// value's integer part in its 7 mantissa bits, so each value is its nibble
-// placed under 0x4300.  One byte permute per pair (nibble 2i of byte i into
-// the low half, nibble 2i+1 into the high half) and one OR; the products'
-// constant part 136 * sum(x) is removed after the reduction.
+// 8 int4 weights stored offset by 8 (u = q + 8; values 0-3 in the low
+// nibbles of bytes 0-3, values 4-7 in the high nibbles) -> the 8 bf16 values
+// 128 + u, exactly: the bf16 pattern of 128 (0x4300) leaves the value's
+// integer part to its 7 mantissa bits, so each value is its nibble as the low
+// byte under a high byte of 0x43.  After masking, one byte permute per pair
+// takes two nibble bytes and two 0x43 bytes; the products' constant part
+// 136 * sum(x) is removed after the reduction.
 __device__ __forceinline__ bf16x8_t u4x8_to_bf16_biased(uint32_t d) {
   const uint32_t t0 = d & 0x0F0F0F0Fu, t1 = (d >> 4) & 0x0F0F0F0Fu;
+  const uint32_t hi = 0x43434343u;  // (selector bytes 4-7)
   u32x4_t r;
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-    r[i] = __builtin_amdgcn_perm(t1, t0, 0x0C000C00u | (uint32_t)i | ((uint32_t)(4 + i) << 16)) | 0x43004300u;
+  r[0] = __builtin_amdgcn_perm(hi, t0, 0x04010400u);  // values 0, 1
+  r[1] = __builtin_amdgcn_perm(hi, t0, 0x04030402u);  // values 2, 3
+  r[2] = __builtin_amdgcn_perm(hi, t1, 0x04010400u);  // values 4, 5
+  r[3] = __builtin_amdgcn_perm(hi, t1, 0x04030402u);  // values 6, 7
   return as_bf16x8(r);
 }
 constexpr float kI4Bias = 136.0f;  // 128 from the bf16 pattern + 8 from the storage offset
@@ -129,7 +132,7 @@ constexpr Plan plan(int mt, int g, int ct, int qb, bool sa) {
   // addresses, loop state, int8 conversion (and, shared, the unit read from LDS)
   // (int4 with per-wave activations: the converted weights of later units
   // are held too)
-  const int fixed = (qb == 4 ? (sa ? 72 : 96) : (qb ? 64 : 40)) + (sa ? act + (qb ? 8 : 0) : 0);
+  const int fixed = (qb == 4 ? (sa ? 72 : 128) : (qb ? 64 : 40)) + (sa ? act + (qb ? 8 : 0) : 0);
   // shared activations: DA = depth + 1 units of the ring in at most 64 KiB,
   // so two workgroups fit a CU's LDS
   const int dmax0 = sa ? 64 / (mt * q_ah(qb)) - 1 : 6;

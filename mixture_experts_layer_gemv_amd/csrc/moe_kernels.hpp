@@ -35,8 +35,8 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
 // n = nb*16 + (l & 15):
 //   bf16 (U = K/32): element j (0..7) is k = u*32 + 8*(l >> 4) + j
 //   int8 (U = K/64): byte j (0..15) is  k = u*64 + 32*(j >> 3) + 8*(l >> 4) + (j & 7)
-//   int4 (U = K/128): nibble j (0..31; byte j/2, low nibble first) is
-//                    k = u*128 + 32*(j >> 3) + 8*(l >> 4) + (j & 7), holding q + 8
+//   int4 (U = K/128): value j (0..31) is k = u*128 + 32*(j >> 3) + 8*(l >> 4) + (j & 7),
+//                    holding q + 8 in dword j >> 3 at bit 8*(j & 3) + 4*((j >> 2) & 1)
 // which is the B-operand order of v_mfma_f32_16x16x32_bf16.  A wave loading
 // one unit reads 1 KiB of contiguous memory: eight full 128-byte lines.
 // G = 2 interleaves the SwiGLU gate (g = 0) and up (g = 1) matrices so one

@@ -53,9 +53,10 @@ __global__ __launch_bounds__(256) void k_pack_i8(const int8_t* __restrict__ src,
   }
 }
 
-// int4 (held one per int8, in [-8, 7]): 128 k per unit; nibble j of a lane's
-// 32 (low nibble first, byte j / 2) is k = 32 (j / 8) + 8 (lane / 16) + j % 8,
-// stored offset by 8 (q + 8 in [0, 15]).
+// int4 (held one per int8, in [-8, 7]): 128 k per unit; value j of a lane's
+// 32 is k = 32 (j / 8) + 8 (lane / 16) + j % 8, in dword j / 8: values 0-3 of
+// a dword in the low nibbles of its bytes 0-3, values 4-7 in the high
+// nibbles, each stored offset by 8 (q + 8 in [0, 15]).
 __global__ __launch_bounds__(256) void k_pack_i4(const int8_t* __restrict__ src, uint4* __restrict__ dst, int E,
                                                  int K, int N, int G, int g) {
   const int NB = N / 16, U = K / 128;
@@ -73,7 +74,7 @@ __global__ __launch_bounds__(256) void k_pack_i4(const int8_t* __restrict__ src,
     for (int j = 0; j < 32; ++j) {
       const int kk = u * 128 + 32 * (j >> 3) + 8 * (lane >> 4) + (j & 7);
       const uint32_t nib = (uint32_t)(src[((size_t)e * K + kk) * N + n] + 8) & 0xFu;
-      d[j >> 3] |= nib << (4 * (j & 7));
+      d[j >> 3] |= nib << (8 * (j & 3) + 4 * ((j >> 2) & 1));
     }
     dst[((((size_t)e * NB + nb) * U + u) * G + g) * 64 + lane] = make_uint4(d[0], d[1], d[2], d[3]);
   }
