@@ -91,15 +91,68 @@ int moe_abi_version(void);
  *  out           receives the handle; release it with moe_weights_destroy.
  * Errors: INVALID_ARG, UNSUPPORTED, OOM, HIP.  On error *out is NULL.
  */
-int moe_weights_create(int m, int p, int E, int kind, int w_dtype, const void* w1, const void* w_up,
-                       const void* w2, const float* s1, const float* s_up, const float* s2, void* stream,
-                       moe_weights** out);
+moe_status moe_weights_create(int m, int p, int E, int kind, int w_dtype, const void* w1, const void* w_up,
+                              const void* w2, const float* s1, const float* s_up, const float* s2, void* stream,
+                              moe_weights** out);
 
 /* Free a handle from moe_weights_create (NULL is accepted).  Synchronises the device. */
-int moe_weights_destroy(moe_weights* w);
+moe_status moe_weights_destroy(moe_weights* w);
 
-/* Bytes of device workspace moe_layer_forward / moe_expert_ffn need for T tokens at top-k. */
-int moe_workspace_size(const moe_weights* w, int T, int k, size_t* bytes);
+/* Bytes of device workspace moe_layer_forward / moe_expert_ffn need for T
+ * tokens at top-k.  A pure function of the handle (its shape, dtype and
+ * tuning), T, k and the device's compute-unit count: the process
+ * environment plays no part. */
+moe_status moe_workspace_size(const moe_weights* w, int T, int k, size_t* bytes);
+
+/*
+ * Launch tuning.  Which kernels serve the expert FFN and their launch shapes
+ * are chosen on the host from (m, p, E, expert kind, weight dtype, T, k); a
+ * moe_tuning attached to a handle overrides single choices.  Every field is
+ * 0 for "automatic"; a tri-state switch is 1 (on) or -1 (off).  The
+ * automatic choices are the measured defaults, so callers normally never set
+ * one; the fields exist so that every launch form can be tested and timed.
+ */
+typedef struct moe_tuning {
+  int ffn_path;         /* MOE_PATH_AUTO, MOE_PATH_SKINNY (decode kernels) or MOE_PATH_GEMM (grouped GEMM) */
+  int skinny_mt;        /* decode kernels: 16-row M tiles per work item (1, 2 or 4) */
+  int skinny_pack;      /* decode kernels: activations as packed fragments (1) or gathered rows (-1) */
+  int skinny_splitk;    /* decode kernels: a workgroup's waves split the reduction (1) or the columns (-1) */
+  int skinny_shared;    /* decode kernels, columns split: one LDS copy of the activations per workgroup (1/-1) */
+  int skinny_wide;      /* decode kernels: hot experts on twelve-tile items in both projections (1/-1) */
+  int skinny_wide_down; /* the same for the down projection alone (1/-1) */
+  int up_ct;            /* decode kernels: column tiles per wave of the up projection (1, 2 or 4) */
+  int down_ct;          /* the same for the down projection */
+  int down_ksplit;      /* decode down projection: reduction slices (1 .. p/64) */
+  int down_rows;        /* decode down projection: unweighted rows + combine kernel (1) or weighted fp32
+                           atomics into an accumulator (-1) */
+  int gemm_cg;          /* grouped GEMM: column blocks per group of its work order (>= 1) */
+  int gemm_skip;        /* grouped GEMM: skip the products of empty row fragments (1/-1) */
+} moe_tuning;
+#define MOE_PATH_AUTO 0
+#define MOE_PATH_SKINNY 1
+#define MOE_PATH_GEMM 2
+
+/*
+ * moe_weights_set_tuning -- attach tuning to a handle (NULL: all automatic).
+ * It applies to every later call with the handle, moe_workspace_size
+ * included, so a workspace must be sized after the tuning is set.  Not to be
+ * called while a forward pass with the handle is being enqueued on another
+ * thread.  A forced path the weights cannot take (the grouped GEMM needs
+ * bf16, int8 or int4 weights) falls back to the decode kernels.
+ * Errors: INVALID_ARG (NULL handle, a value out of range).
+ */
+moe_status moe_weights_set_tuning(moe_weights* w, const moe_tuning* t);
+moe_status moe_weights_get_tuning(const moe_weights* w, moe_tuning* t);
+
+/*
+ * moe_workspace_size_for -- moe_workspace_size for a layer that has no
+ * handle yet: the same result as moe_workspace_size on a handle created with
+ * (m, p, E, kind, w_dtype) and tuning t (NULL: automatic).  Host only; it
+ * touches no device memory.
+ * Errors: INVALID_ARG, UNSUPPORTED.
+ */
+moe_status moe_workspace_size_for(int m, int p, int E, int kind, int w_dtype, const moe_tuning* t, int T, int k,
+                                  size_t* bytes);
 
 /*
  * moe_route_topk -- router product, top-k and gate weights for T tokens.
@@ -120,8 +173,8 @@ int moe_workspace_size(const moe_weights* w, int T, int k, size_t* bytes);
  *  topk_idx   device int32 [T][k] output.   topk_w  device fp32 [T][k] output.
  * Errors: INVALID_ARG, UNSUPPORTED, HIP.
  */
-int moe_route_topk(const void* x, int x_dtype, const float* w_router, const float* b_router, int T, int m, int E,
-                   int k, unsigned flags, float* logits, int32_t* topk_idx, float* topk_w, void* stream);
+moe_status moe_route_topk(const void* x, int x_dtype, const float* w_router, const float* b_router, int T, int m, int E,
+                          int k, unsigned flags, float* logits, int32_t* topk_idx, float* topk_w, void* stream);
 
 /*
  * moe_dispatch -- group the T*k assignments (a = t*k + j) by expert: the
@@ -138,8 +191,8 @@ int moe_route_topk(const void* x, int x_dtype, const float* w_router, const floa
  *  counts [E], offsets [E+1], perm [T*k], inv_perm [T*k]: device int32 outputs.
  * Errors: INVALID_ARG, UNSUPPORTED, HIP.
  */
-int moe_dispatch(const int32_t* topk_idx, int T, int E, int k, int32_t* counts, int32_t* offsets, int32_t* perm,
-                 int32_t* inv_perm, void* stream);
+moe_status moe_dispatch(const int32_t* topk_idx, int T, int E, int k, int32_t* counts, int32_t* offsets, int32_t* perm,
+                        int32_t* inv_perm, void* stream);
 
 /*
  * moe_expert_ffn -- every expert on its rows: for each permuted row r of
@@ -156,9 +209,9 @@ int moe_dispatch(const int32_t* topk_idx, int T, int E, int k, int32_t* counts, 
  *  workspace  device, >= moe_workspace_size(w, T, k) bytes, 256-byte aligned.
  * Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE, HIP.
  */
-int moe_expert_ffn(const moe_weights* w, const void* x, int x_dtype, int T, int m, int p, int E, int k,
-                   const int32_t* perm, const int32_t* offsets, float* y_perm, void* workspace, size_t ws_bytes,
-                   void* stream);
+moe_status moe_expert_ffn(const moe_weights* w, const void* x, int x_dtype, int T, int m, int p, int E, int k,
+                          const int32_t* perm, const int32_t* offsets, float* y_perm, void* workspace, size_t ws_bytes,
+                          void* stream);
 
 /*
  * moe_combine -- gather the expert outputs back to their tokens, weighted
@@ -168,8 +221,8 @@ int moe_expert_ffn(const moe_weights* w, const void* x, int x_dtype, int T, int 
  *  topk_w     device fp32 [T][k];    y  device [T][m] in y_dtype (F32 or BF16).
  * Errors: INVALID_ARG, UNSUPPORTED, HIP.
  */
-int moe_combine(const float* y_perm, const int32_t* inv_perm, const float* topk_w, int T, int m, int k, void* y,
-                int y_dtype, void* stream);
+moe_status moe_combine(const float* y_perm, const int32_t* inv_perm, const float* topk_w, int T, int m, int k, void* y,
+                       int y_dtype, void* stream);
 
 /*
  * moe_layer_forward -- the whole layer: route + top-k, dispatch, experts and
@@ -183,10 +236,10 @@ int moe_combine(const float* y_perm, const int32_t* inv_perm, const float* topk_
  *             counts [E], offsets [E+1], perm [T*k].
  * Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE, HIP.
  */
-int moe_layer_forward(const moe_weights* w, const float* w_router, const float* b_router, const void* x, int x_dtype,
-                      int T, int m, int p, int E, int k, void* y, int y_dtype, void* workspace, size_t ws_bytes,
-                      int32_t* dbg_topk_idx, float* dbg_topk_w, float* dbg_logits, int32_t* dbg_counts,
-                      int32_t* dbg_offsets, int32_t* dbg_perm, void* stream);
+moe_status moe_layer_forward(const moe_weights* w, const float* w_router, const float* b_router, const void* x, int x_dtype,
+                             int T, int m, int p, int E, int k, void* y, int y_dtype, void* workspace, size_t ws_bytes,
+                             int32_t* dbg_topk_idx, float* dbg_topk_w, float* dbg_logits, int32_t* dbg_counts,
+                             int32_t* dbg_offsets, int32_t* dbg_perm, void* stream);
 
 /*
  * moe_layer_forward_fused -- moe_layer_forward with the layer's neighbouring
@@ -211,11 +264,11 @@ int moe_layer_forward(const moe_weights* w, const float* w_router, const float* 
 #define MOE_NORM_NONE 0
 #define MOE_NORM_LAYER 1
 #define MOE_NORM_RMS 2
-int moe_layer_forward_fused(const moe_weights* w, const float* w_router, const float* b_router, const void* x,
-                            int x_dtype, int norm, const float* gamma, const float* beta, float eps,
-                            const void* residual, int T, int m, int p, int E, int k, void* y, int y_dtype,
-                            void* workspace, size_t ws_bytes, void* x_norm, int32_t* dbg_topk_idx,
-                            float* dbg_topk_w, float* dbg_logits, void* stream);
+moe_status moe_layer_forward_fused(const moe_weights* w, const float* w_router, const float* b_router, const void* x,
+                                   int x_dtype, int norm, const float* gamma, const float* beta, float eps,
+                                   const void* residual, int T, int m, int p, int E, int k, void* y, int y_dtype,
+                                   void* workspace, size_t ws_bytes, void* x_norm, int32_t* dbg_topk_idx,
+                                   float* dbg_topk_w, float* dbg_logits, void* stream);
 
 /*
  * moe_layer_graph_create / moe_graph_launch / moe_graph_destroy -- the layer
@@ -237,11 +290,11 @@ int moe_layer_forward_fused(const moe_weights* w, const float* w_router, const f
  * OOM.
  */
 typedef struct moe_graph moe_graph;
-int moe_layer_graph_create(const moe_weights* w, const float* w_router, const float* b_router, const void* x,
-                           int x_dtype, int T, int m, int p, int E, int k, void* y, int y_dtype, void* workspace,
-                           size_t ws_bytes, moe_graph** out);
-int moe_graph_launch(const moe_graph* g, void* stream);
-int moe_graph_destroy(moe_graph* g);
+moe_status moe_layer_graph_create(const moe_weights* w, const float* w_router, const float* b_router, const void* x,
+                                  int x_dtype, int T, int m, int p, int E, int k, void* y, int y_dtype, void* workspace,
+                                  size_t ws_bytes, moe_graph** out);
+moe_status moe_graph_launch(const moe_graph* g, void* stream);
+moe_status moe_graph_destroy(moe_graph* g);
 
 /*
  * Measurement aid (not part of the layer).  Between moe_profile_begin and
@@ -253,9 +306,9 @@ int moe_graph_destroy(moe_graph* g);
  * not timed).  Kernel names: "route_topk", "dispatch", "ffn_up", "ffn_down",
  * "ffn_f32_up", "ffn_f32_down", "combine", "finalize", "fill".
  */
-int moe_profile_begin(int max_launches);
-int moe_profile_end(void);
-int moe_profile_query(const char* kernel, double* total_ms, int* launches);
+moe_status moe_profile_begin(int max_launches);
+moe_status moe_profile_end(void);
+moe_status moe_profile_query(const char* kernel, double* total_ms, int* launches);
 
 #ifdef __cplusplus
 }

@@ -22,6 +22,7 @@ MOE_MLP_RELU, MOE_SWIGLU = 0, 1
 MOE_ROUTE_LOGITS_IN = 1
 MOE_NORM_NONE, MOE_NORM_LAYER, MOE_NORM_RMS = 0, 1, 2
 MOE_MAX_EXPERTS = 64
+MOE_PATH_AUTO, MOE_PATH_SKINNY, MOE_PATH_GEMM = 0, 1, 2
 
 STATUS_NAMES = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARG", 2: "MOE_ERR_UNSUPPORTED", 3: "MOE_ERR_WORKSPACE",
                 4: "MOE_ERR_HIP", 5: "MOE_ERR_OOM"}
@@ -34,6 +35,23 @@ class MoeError(RuntimeError):
         self.message = message
 
 
+class moe_tuning(ctypes.Structure):
+    """struct moe_tuning: 0 is "automatic" in every field, switches are 1 / -1."""
+    _fields_ = [(n, ctypes.c_int) for n in (
+        "ffn_path", "skinny_mt", "skinny_pack", "skinny_splitk", "skinny_shared", "skinny_wide", "skinny_wide_down",
+        "up_ct", "down_ct", "down_ksplit", "down_rows", "gemm_cg", "gemm_skip")]
+
+
+def tuning(**fields) -> moe_tuning:
+    """A moe_tuning with the given fields set (the rest automatic)."""
+    t = moe_tuning()
+    for k, v in fields.items():
+        if not hasattr(t, k):
+            raise KeyError(k)
+        setattr(t, k, int(v))
+    return t
+
+
 _lib = None
 
 _vp, _i32, _u32, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_uint, ctypes.c_size_t
@@ -44,6 +62,10 @@ _SIGS = {
                             ctypes.POINTER(_vp)], _i32),
     "moe_weights_destroy": ([_vp], _i32),
     "moe_workspace_size": ([_vp, _i32, _i32, ctypes.POINTER(_sz)], _i32),
+    "moe_weights_set_tuning": ([_vp, ctypes.POINTER(moe_tuning)], _i32),
+    "moe_weights_get_tuning": ([_vp, ctypes.POINTER(moe_tuning)], _i32),
+    "moe_workspace_size_for": ([_i32, _i32, _i32, _i32, _i32, ctypes.POINTER(moe_tuning), _i32, _i32,
+                                ctypes.POINTER(_sz)], _i32),
     "moe_route_topk": ([_vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32, _u32, _vp, _vp, _vp, _vp], _i32),
     "moe_dispatch": ([_vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp], _i32),
     "moe_expert_ffn": ([_vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _sz, _vp], _i32),
@@ -123,6 +145,28 @@ def moe_weights_destroy(w):
 def moe_workspace_size(w, T, k) -> int:
     n = _sz()
     _check("moe_workspace_size", lib().moe_workspace_size(w, T, k, ctypes.byref(n)))
+    return n.value
+
+
+def moe_weights_set_tuning(w, t=None):
+    """t: a moe_tuning, a dict of its fields, or None (all automatic)."""
+    if isinstance(t, dict):
+        t = tuning(**t)
+    _check("moe_weights_set_tuning", lib().moe_weights_set_tuning(w, None if t is None else ctypes.byref(t)))
+
+
+def moe_weights_get_tuning(w) -> moe_tuning:
+    t = moe_tuning()
+    _check("moe_weights_get_tuning", lib().moe_weights_get_tuning(w, ctypes.byref(t)))
+    return t
+
+
+def moe_workspace_size_for(m, p, E, kind, w_dtype, t, T, k) -> int:
+    if isinstance(t, dict):
+        t = tuning(**t)
+    n = _sz()
+    _check("moe_workspace_size_for", lib().moe_workspace_size_for(
+        m, p, E, kind, w_dtype, None if t is None else ctypes.byref(t), T, k, ctypes.byref(n)))
     return n.value
 
 

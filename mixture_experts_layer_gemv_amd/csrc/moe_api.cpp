@@ -8,6 +8,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <map>
+#include <algorithm>
 #include <mutex>
 #include <new>
 #include <string>
@@ -17,30 +18,31 @@
 #include "moe_index.hpp"
 #include "moe_kernels.hpp"
 
-struct moe_weights {
+// The plan inputs of a layer: its shape, dtypes and tuning.  Every launch
+// choice and the workspace layout are functions of this, T and k (and the
+// device's compute-unit count), never of the process environment.
+struct LayerCfg {
   int m = 0, p = 0, E = 0, kind = 0, w_dtype = 0;
+  moe_tuning tune{};
+};
+
+struct moe_weights {
+  LayerCfg c;
   void* buf = nullptr;
   size_t bytes = 0;
-  void* up = nullptr;    // packed gate(+up) [E][p/16][U][G] (bf16/i8), or fp32 w1 [E][m][p]
+  void* up = nullptr;    // packed gate(+up) [E][p/16][U][G] (bf16/int), or fp32 w1 [E][m][p]
   void* up3 = nullptr;   // fp32 SwiGLU only: w3 [E][m][p]
-  void* down = nullptr;  // packed down [E][m/16][U][1] (bf16/i8), or fp32 w2 [E][p][m]
+  void* down = nullptr;  // packed down [E][m/16][U][1] (bf16/int), or fp32 w2 [E][p][m]
   float* s_gate = nullptr;
   float* s_up = nullptr;
   float* s_down = nullptr;
-  // bf16 weights: a second stream on which the grouped GEMM serves the hot
-  // experts while the caller's stream runs the skinny kernels on the rest,
-  // and the events of that fork and join (guarded by mu, so concurrent calls
-  // enqueue consistent pairs)
-  hipStream_t side = nullptr;
-  hipEvent_t ev_fork = nullptr, ev_join = nullptr;
-  mutable std::mutex mu;
 };
 
 namespace {
 
 thread_local std::string g_err;
 
-int fail(int code, const char* fmt, ...) {
+moe_status fail(moe_status code, const char* fmt, ...) {
   char buf[512];
   va_list ap;
   va_start(ap, fmt);
@@ -50,7 +52,7 @@ int fail(int code, const char* fmt, ...) {
   return code;
 }
 
-int ok() {
+moe_status ok() {
   g_err.clear();
   return MOE_OK;
 }
@@ -90,9 +92,10 @@ hipError_t run(const char* name, hipStream_t s, F&& launch) {
   return launch();
 }
 
+
 // ---- shape / dtype rules ---------------------------------------------------------
 
-int check_shape(int T, int m, int p, int E, int k) {
+moe_status check_shape(int T, int m, int p, int E, int k) {
   if (T < 0) return fail(MOE_ERR_INVALID_ARG, "T=%d must be >= 0", T);
   if (m <= 0 || p <= 0) return fail(MOE_ERR_INVALID_ARG, "m=%d and p=%d must be positive", m, p);
   if (E < 1) return fail(MOE_ERR_INVALID_ARG, "E=%d must be >= 1", E);
@@ -108,74 +111,85 @@ bool valid_dtype(int d) { return d == MOE_F32 || d == MOE_BF16 || d == MOE_I8 ||
 // Integer weights (int8 or int4, with per-output-channel scales).
 bool quantised(int d) { return d == MOE_I8 || d == MOE_I4; }
 
-// Weight bits of the skinny kernels' variants: 0 (bf16), 8 or 4.
-int weight_bits(const moe_weights* W) { return W->w_dtype == MOE_I8 ? 8 : (W->w_dtype == MOE_I4 ? 4 : 0); }
+// Weight bits of the kernels' variants: 0 (bf16), 8 or 4.
+int weight_bits(const LayerCfg& c) { return c.w_dtype == MOE_I8 ? 8 : (c.w_dtype == MOE_I4 ? 4 : 0); }
 
-int check_combo(int x_dtype, int w_dtype) {
+moe_status check_layer(int m, int p, int E, int kind, int w_dtype) {
+  if (moe_status rc = check_shape(1, m, p, E, 1)) return rc;
+  if (kind != MOE_MLP_RELU && kind != MOE_SWIGLU) return fail(MOE_ERR_INVALID_ARG, "unknown expert kind %d", kind);
+  if (!valid_dtype(w_dtype)) return fail(MOE_ERR_UNSUPPORTED, "weight dtype %d unsupported", w_dtype);
+  if (w_dtype == MOE_I4 && (m % 128 || p % 128))
+    return fail(MOE_ERR_UNSUPPORTED, "int4 weights need m=%d and p=%d to be multiples of 128", m, p);
+  return MOE_OK;
+}
+
+moe_status check_tuning(const moe_tuning& t) {
+  auto tri = [](int v) { return v == 0 || v == 1 || v == -1; };
+  auto tiles = [](int v) { return v == 0 || v == 1 || v == 2 || v == 4; };
+  if (t.ffn_path < MOE_PATH_AUTO || t.ffn_path > MOE_PATH_GEMM)
+    return fail(MOE_ERR_INVALID_ARG, "ffn_path %d", t.ffn_path);
+  if (!tiles(t.skinny_mt) || !tiles(t.up_ct) || !tiles(t.down_ct))
+    return fail(MOE_ERR_INVALID_ARG, "skinny_mt, up_ct and down_ct must be 0, 1, 2 or 4");
+  if (!tri(t.skinny_pack) || !tri(t.skinny_splitk) || !tri(t.skinny_shared) || !tri(t.skinny_wide) ||
+      !tri(t.skinny_wide_down) || !tri(t.down_rows) || !tri(t.gemm_skip))
+    return fail(MOE_ERR_INVALID_ARG, "a switch of the tuning is not 0, 1 or -1");
+  if (t.down_ksplit < 0 || t.down_ksplit > 1024) return fail(MOE_ERR_INVALID_ARG, "down_ksplit %d", t.down_ksplit);
+  if (t.gemm_cg < 0 || t.gemm_cg > 1024) return fail(MOE_ERR_INVALID_ARG, "gemm_cg %d", t.gemm_cg);
+  return MOE_OK;
+}
+
+moe_status check_combo(int x_dtype, int w_dtype) {
   if (x_dtype != MOE_F32 && x_dtype != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "x dtype %d unsupported", x_dtype);
   if (w_dtype == MOE_F32 && x_dtype != MOE_F32)
     return fail(MOE_ERR_UNSUPPORTED, "fp32 weights need fp32 activations");
   if (w_dtype != MOE_F32 && x_dtype != MOE_BF16)
-    return fail(MOE_ERR_UNSUPPORTED, "bf16/int8 weights need bf16 activations");
+    return fail(MOE_ERR_UNSUPPORTED, "bf16/int8/int4 weights need bf16 activations");
   return MOE_OK;
 }
 
 // Which kernels serve the expert FFN.
-//  - GEMM: bf16 layers whose experts average at least kGemmMinRows rows run
-//    the grouped MFMA GEMM on every expert.
-//  - HYBRID (only when forced): experts with at least hot_rows() rows run the
-//    grouped GEMM on a second stream (weights read once for up to 256 rows),
-//    the others run the skinny kernels on the caller's stream, concurrently.
-//    On the skewed Phi-3.5-shaped layer it measured slower than the skinny
-//    path alone: each GEMM workgroup holds a whole CU for its 128-step loop
-//    and waits for skinny workgroups to drain, so it is not chosen by default.
-//  - SKINNY: decode-sized bf16 and all int8 layers.
+//  - GEMM: layers whose experts average at least kGemmMinRows rows run the
+//    grouped MFMA GEMM on every expert.
+//  - SKINNY: decode-sized layers.
 //  - F32: fp32 layers.
-// MOE_FFN_PATH=g|h|s forces a path where the weights allow it.
-enum class Path { F32, SKINNY, GEMM, HYBRID };
+// (A hybrid of the two, hot experts on the GEMM on a second stream and the
+// rest on the decode kernels, measured slower than the decode kernels alone on
+// the skewed Phi-3.5-shaped layer and is not offered.)
+enum class Path { F32, SKINNY, GEMM };
 constexpr int kGemmMinRows = 128;
 
-int env_int(const char* name, int dflt) {
-  const char* v = getenv(name);
-  return v && *v ? atoi(v) : dflt;
-}
-
-// Experts with at least this many rows count as hot: more than one 64-row
-// chunk of the skinny kernel.
-int hot_rows() { return std::max(1, env_int("MOE_HOT_ROWS", 65)); }
+// 0 ("automatic") or the tuning's value.
+int tuned(int v, int dflt) { return v != 0 ? v : dflt; }
+bool tuned_on(int v, bool dflt) { return v == 0 ? dflt : v > 0; }
 
 // The GEMM addresses packed activations and one projection's packed weights
 // with 32-bit byte offsets from a uniform base.
-bool gemm_fits(const moe_weights* W, int T, int k) {
-  if (W->w_dtype != MOE_BF16) return false;
+bool gemm_fits(const LayerCfg& c, int T, int k) {
+  if (c.w_dtype != MOE_BF16) return false;
   const unsigned long long lim = 1ull << 32;
-  const unsigned long long mp = (unsigned long long)W->m * W->p;
-  const unsigned long long G = W->kind == MOE_SWIGLU ? 2 : 1;
-  const unsigned long long rows = (unsigned long long)moe::packed_rows_max((long long)T * k, W->E);
-  return (unsigned long long)W->E * mp * 2 * G < lim && rows * W->m * 2 < lim && rows * W->p * 2 < lim;
+  const int qb = weight_bits(c);
+  const unsigned long long G = c.kind == MOE_SWIGLU ? 2 : 1;
+  const unsigned long long up_w = moe::packed_bytes(c.E, c.m, c.p, (int)G, qb);
+  const unsigned long long dn_w = moe::packed_bytes(c.E, c.p, c.m, 1, qb);
+  const unsigned long long rows = (unsigned long long)moe::packed_rows_max((long long)T * k, c.E);
+  return up_w < lim && dn_w < lim && rows * c.m * 2 < lim && rows * c.p * 2 < lim;
 }
 
-Path ffn_path(const moe_weights* W, int T, int k) {
-  if (W->w_dtype == MOE_F32) return Path::F32;
-  const bool fits = gemm_fits(W, T, k) && W->side;
-  const char* v = getenv("MOE_FFN_PATH");
-  if (v && *v) {
-    if (v[0] == 'g' && fits) return Path::GEMM;
-    if (v[0] == 'h' && fits) return Path::HYBRID;
-    return Path::SKINNY;
-  }
-  if (!fits) return Path::SKINNY;
+Path ffn_path(const LayerCfg& c, int T, int k) {
+  if (c.w_dtype == MOE_F32) return Path::F32;
+  const bool fits = gemm_fits(c, T, k);
+  if (c.tune.ffn_path == MOE_PATH_GEMM) return fits ? Path::GEMM : Path::SKINNY;
+  if (c.tune.ffn_path == MOE_PATH_SKINNY || !fits) return Path::SKINNY;
   const long long n = (long long)T * k;
-  if (n >= (long long)kGemmMinRows * W->E) return Path::GEMM;
-  return Path::SKINNY;
+  return n >= (long long)kGemmMinRows * c.E ? Path::GEMM : Path::SKINNY;
 }
 
 // M tiles (16 rows each) per work item of the skinny kernels, from the mean
-// rows per expert (MOE_SKINNY_MT overrides).
-int skinny_mt(const moe_weights* W, int T, int k) {
-  const long long avg = ((long long)T * k + W->E - 1) / W->E;
-  const int mt = env_int("MOE_SKINNY_MT", avg <= 12 ? 1 : (avg <= 24 ? 2 : 4));
-  if (quantised(W->w_dtype)) return mt <= 1 ? 1 : 2;  // the integer kernels stop at two M tiles
+// rows per expert.
+int skinny_mt(const LayerCfg& c, int T, int k) {
+  const long long avg = ((long long)T * k + c.E - 1) / c.E;
+  const int mt = tuned(c.tune.skinny_mt, avg <= 12 ? 1 : (avg <= 24 ? 2 : 4));
+  if (quantised(c.w_dtype)) return mt <= 1 ? 1 : 2;  // the integer kernels stop at two M tiles
   return mt <= 1 ? 1 : (mt == 2 ? 2 : 4);
 }
 
@@ -184,83 +198,51 @@ int skinny_mt(const moe_weights* W, int T, int k) {
 // the up projection): one contiguous load per tile and K unit instead of 16
 // half-line rows, which measured as the dominant cost of the skewed layer
 // (-11 % there).  With one or two bf16 tiles the extra packing launch costs
-// more than it saves, so rows are gathered directly (MOE_SKINNY_PACK=0/1
-// overrides).  At decode sizes the dispatch is derived by the first kernel
-// either way: the packing, or the up projection's prologue.
-bool skinny_packed(const moe_weights* W, int T, int k) {
-  if (W->w_dtype == MOE_F32) return false;
+// more than it saves, so rows are gathered directly.  At decode sizes the
+// dispatch is derived by the first kernel either way: the packing, or the up
+// projection's prologue.
+bool skinny_packed(const LayerCfg& c, int T, int k) {
+  if (c.w_dtype == MOE_F32) return false;
   // int8 (int4) weights span 64 (128) k per unit, so two M tiles already
   // read four (eight) activation fragments per unit: packed and shared
   // measured ahead there
-  const int dflt = skinny_mt(W, T, k) >= (quantised(W->w_dtype) ? 2 : 4) ? 1 : 0;
-  return env_int("MOE_SKINNY_PACK", dflt) != 0;
+  const bool dflt = skinny_mt(c, T, k) >= (quantised(c.w_dtype) ? 2 : 4);
+  return tuned_on(c.tune.skinny_pack, dflt);
 }
 
-// Launch shape of the skinny down projection inside the layer (below).
-struct DownShape {
-  int ct, ks;
-};
-DownShape skinny_down_shape(const moe_weights* W, int T, int k);
-bool skinny_rows_combine();
+// Waves split the reduction unless the activations are packed (measured).
+bool skinny_splitk(const LayerCfg& c, int T, int k) { return tuned_on(c.tune.skinny_splitk, !skinny_packed(c, T, k)); }
 
-// Workspace carving, in the order listed.
-struct Ws {
-  size_t logits, idx, w, counts, offsets, perm, inv, xn, h, yacc, yperm, xp, hp, total;
-};
-
-Ws ws_layout(const moe_weights* W, int T, int k) {
-  Ws L{};
-  size_t off = 0;
-  auto take = [&](size_t bytes) {
-    const size_t o = off;
-    off += align256(bytes);
-    return o;
-  };
-  const size_t n = (size_t)T * k;
-  L.logits = take((size_t)T * W->E * 4);
-  L.idx = take(n * 4);
-  L.w = take(n * 4);
-  L.counts = take((size_t)W->E * 4);
-  L.offsets = take((size_t)(W->E + 1) * 4);
-  L.perm = take(n * 4);
-  L.inv = take(n * 4);
-  // the normalised input rows of the fused forward (x's dtype)
-  L.xn = take((size_t)T * W->m * (W->w_dtype == MOE_F32 ? 4 : 2));
-  const Path path = ffn_path(W, T, k);
-  const bool gemm = path == Path::GEMM, hybrid = path == Path::HYBRID;
-  const bool spack = (path == Path::SKINNY || hybrid) && skinny_packed(W, T, k);
-  // the grouped GEMM and the packed skinny kernels keep H and the gathered x
-  // in the packed row layout; the hybrid path keeps the GEMM's H separately
-  const size_t prows = (size_t)moe::packed_rows_max((long long)n, W->E);
-  L.h = take((gemm || spack ? prows : n) * (size_t)W->p * (W->w_dtype == MOE_F32 ? 4 : 2));
-  L.yacc = take((size_t)T * W->m * 4);
-  const size_t row_sets = gemm ? 1 : (path == Path::SKINNY && skinny_rows_combine()
-                                          ? (size_t)skinny_down_shape(W, T, k).ks : 0);
-  L.yperm = row_sets ? take(row_sets * n * (size_t)W->m * 4) : off;
-  L.xp = gemm || hybrid || spack ? take(prows * (size_t)W->m * 2) : off;
-  L.hp = hybrid ? take(prows * (size_t)W->p * 2) : off;
-  L.total = off;
-  return L;
+// Packed rows with the columns split over the waves: every wave of a
+// workgroup reads the same activation fragments, so they are copied into
+// LDS once per workgroup.
+bool skinny_shared(const LayerCfg& c, int T, int k) {
+  return skinny_packed(c, T, k) && !skinny_splitk(c, T, k) && tuned_on(c.tune.skinny_shared, true);
 }
 
-// Reduction slices per down-projection work item.  Splitting adds fp32
-// atomics on the output; measured on the decode layers (512 to 1536 work
-// items) one slice is as fast or faster, so only very small launches split.
-int down_ksplit(long long items) {
-  const int forced = env_int("MOE_DOWN_KSPLIT", 0);
-  if (forced > 0) return forced;
+// Decode layers write the down projection's unweighted rows (one set per
+// reduction slice) and finish with the combine kernel, instead of adding
+// weighted rows into an fp32 accumulator with atomics: on the skewed layer
+// one more slice of atomics cost 20 us, about 10^11 adds/s, while the rows
+// and the combine move a few MB.
+bool skinny_rows_combine(const LayerCfg& c) { return tuned_on(c.tune.down_rows, true); }
+
+// Reduction slices per down-projection work item.  Splitting adds partial
+// rows (or atomics); measured on the decode layers (512 to 1536 work items)
+// one slice is as fast or faster, so only very small launches split.
+int down_ksplit(const LayerCfg& c, long long items) {
+  if (c.tune.down_ksplit > 0) return c.tune.down_ksplit;
   if (items >= 512) return 1;
   if (items >= 256) return 2;
   return 4;
 }
 
-// Column tiles per workgroup: enough to amortise each activation load over
+// Column tiles per wave: enough to amortise each activation load over
 // several weight streams when the activation side is wide (several M tiles,
-// or int8 weights whose 16-byte unit spans 64 k).
-// The down projection (one stream per tile) always takes 4 (2 with four M
-// tiles, for registers); measured on the decode layers.
-int skinny_ct(int mt, int qb, int g, const char* env) {
-  const int forced = env_int(env, 0);
+// or int8 weights whose 16-byte unit spans 64 k).  The down projection (one
+// stream per tile) takes 4 (2 with four M tiles, for registers); measured on
+// the decode layers.
+int skinny_ct(int mt, int qb, int g, int forced) {
   if (forced > 0) return forced >= 4 ? 4 : (forced >= 2 ? 2 : 1);
   const int aw = mt * (qb == 8 ? 2 : (qb == 4 ? 4 : 1));
   if (aw <= 1 && g > 1) return 1;
@@ -273,12 +255,18 @@ int device_cus() {
   static std::mutex mu;
   static std::map<int, int> cus;
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return 256;
+  }
   std::lock_guard<std::mutex> lk(mu);
   auto it = cus.find(dev);
   if (it != cus.end()) return it->second;
   int n = 0;
-  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) {
+    (void)hipGetLastError();
+    n = 256;
+  }
   cus[dev] = n;
   return n;
 }
@@ -289,54 +277,85 @@ int device_cus() {
 // the resident slots, counted from the expected number of (expert, chunk)
 // pairs.  Measured on the int8 decode layer: 92 us against 99 us for four
 // tiles and four slices, 124 us for one slice.
-void int8_down_shape(const moe_weights* W, int T, int k, int R, int* ct, int* ks) {
+void int8_down_shape(const LayerCfg& c, int T, int k, int R, int* ct, int* ks) {
   const long long n = (long long)T * k;
-  const long long pairs = std::min<long long>(W->E, n) + std::max<long long>(0, n - (long long)W->E * R) / R;
+  const long long pairs = std::min<long long>(c.E, n) + std::max<long long>(0, n - (long long)c.E * R) / R;
   *ct = 2;
-  const long long blocks1 = (long long)moe::skinny_groups(W->m, *ct) * pairs;
+  const long long blocks1 = (long long)moe::skinny_groups(c.m, *ct) * pairs;
   const long long slots = 2LL * device_cus();
   *ks = blocks1 * 10 >= slots * 9 ? 1 : (blocks1 * 2 * 10 >= slots * 9 ? 2 : 4);
-  *ks = std::max(1, std::min(*ks, W->p / 64));
+  *ks = std::max(1, std::min(*ks, c.p / 64));
 }
 
 // Launch shape of the skinny down projection inside the layer: column tiles
 // per wave and reduction slices.  Shared by the workspace layout (the
 // unweighted rows are kept per slice) and the launch.
-DownShape skinny_down_shape(const moe_weights* W, int T, int k) {
-  const int mt = skinny_mt(W, T, k);
-  const int qb = weight_bits(W);
-  const bool i8 = qb != 0;  // integer weights (int8 or int4)
-  const bool packed = skinny_packed(W, T, k);
-  const char* wv = getenv("MOE_SKINNY_WAVES");
-  const bool splitk = wv && *wv ? wv[0] == 'k' : !packed;
-  const bool shared = packed && !splitk && env_int("MOE_SKINNY_SA", 1) != 0;
+struct DownShape {
+  int ct, ks;
+};
+DownShape skinny_down_shape(const LayerCfg& c, int T, int k) {
+  const int mt = skinny_mt(c, T, k);
+  const int qb = weight_bits(c);
+  const bool splitk = skinny_splitk(c, T, k);
   const int R = moe::skinny_rows(mt);
-  const int Wp = W->E + (int)((long long)T * k / R);
-  DownShape d{skinny_ct(mt, qb, 1, "MOE_DOWN_CT"), 1};
-  d.ks = down_ksplit((long long)(splitk ? W->m / 16 / d.ct : moe::skinny_groups(W->m, d.ct)) * Wp);
-  if (i8 && shared && env_int("MOE_DOWN_CT", 0) <= 0 && env_int("MOE_DOWN_KSPLIT", 0) <= 0)
-    int8_down_shape(W, T, k, R, &d.ct, &d.ks);
-  d.ks = std::max(1, std::min(d.ks, W->p / 64));
+  const int Wp = c.E + (int)((long long)T * k / R);
+  DownShape d{skinny_ct(mt, qb, 1, c.tune.down_ct), 1};
+  d.ks = down_ksplit(c, (long long)(splitk ? c.m / 16 / d.ct : moe::skinny_groups(c.m, d.ct)) * Wp);
+  if (qb != 0 && skinny_shared(c, T, k) && c.tune.down_ct <= 0 && c.tune.down_ksplit <= 0)
+    int8_down_shape(c, T, k, R, &d.ct, &d.ks);
+  d.ks = std::max(1, std::min(d.ks, c.p / 64));
   return d;
 }
 
-// Decode layers write the down projection's unweighted rows (one set per
-// reduction slice) and finish with the combine kernel, instead of adding
-// weighted rows into an fp32 accumulator with atomics: on the skewed layer
-// one more slice of atomics cost 20 us, about 10^11 adds/s, while the rows
-// and the combine move a few MB (MOE_DOWN_ROWS=0 restores the atomics).
-bool skinny_rows_combine() { return env_int("MOE_DOWN_ROWS", 1) != 0; }
+// Workspace carving, in the order listed.
+struct Ws {
+  size_t logits, idx, w, counts, offsets, perm, inv, xn, h, yacc, yperm, xp, total;
+};
+
+Ws ws_layout(const LayerCfg& c, int T, int k) {
+  Ws L{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += align256(bytes);
+    return o;
+  };
+  const size_t n = (size_t)T * k;
+  const bool f32 = c.w_dtype == MOE_F32;
+  L.logits = take((size_t)T * c.E * 4);
+  L.idx = take(n * 4);
+  L.w = take(n * 4);
+  L.counts = take((size_t)c.E * 4);
+  L.offsets = take((size_t)(c.E + 1) * 4);
+  L.perm = take(n * 4);
+  L.inv = take(n * 4);
+  // the normalised input rows of the fused forward (x's dtype)
+  L.xn = take((size_t)T * c.m * (f32 ? 4 : 2));
+  const Path path = ffn_path(c, T, k);
+  const bool gemm = path == Path::GEMM;
+  const bool spack = path == Path::SKINNY && skinny_packed(c, T, k);
+  // the grouped GEMM and the packed skinny kernels keep H and the gathered x
+  // in the packed row layout
+  const size_t prows = (size_t)moe::packed_rows_max((long long)n, c.E);
+  L.h = take((gemm || spack ? prows : n) * (size_t)c.p * (f32 ? 4 : 2));
+  L.yacc = take((size_t)T * c.m * 4);
+  const size_t row_sets =
+      gemm ? 1 : (path == Path::SKINNY && skinny_rows_combine(c) ? (size_t)skinny_down_shape(c, T, k).ks : 0);
+  L.yperm = row_sets ? take(row_sets * n * (size_t)c.m * 4) : off;
+  L.xp = gemm || spack ? take(prows * (size_t)c.m * 2) : off;
+  L.total = off;
+  return L;
+}
 
 // Inputs and outputs of the two FFN projections.
 struct FfnIo {
   const void* x;
   int T, k;
-  const int32_t* topk_idx;  // non-null: the up projection derives the dispatch
+  const int32_t* topk_idx;  // non-null: the first FFN kernel derives the dispatch
   int32_t *counts, *offsets, *perm, *inv;
   const float* topk_w;
   void* h;                  // hidden activations [T*k][p] (packed rows on the GEMM path)
-  void* xp;                 // GEMM/hybrid path: x rows gathered into the packed row layout
-  void* hp;                 // hybrid path: the hot experts' H rows, packed
+  void* xp;                 // packed paths: x rows gathered into the packed row layout
   float* down_out;          // y_acc [T][m] (combine) or y_perm [T*k][m]
   bool combine;             // inside the layer: the weighted combine follows
   float* yperm;             // with combine on the grouped-GEMM path, or the skinny path with
@@ -344,16 +363,16 @@ struct FfnIo {
   int* slices;              // set to the number of row slices written to yperm
 };
 
-// Gathers x rows into the packed row layout for the grouped GEMM.
-int run_pack(const moe_weights* W, const FfnIo& io, hipStream_t s) {
+// Gathers x rows into the packed row layout.
+moe_status run_pack(const LayerCfg& c, const FfnIo& io, hipStream_t s) {
   moe::PackArgs pk{};
   pk.x = static_cast<const uint16_t*>(io.x);
   pk.perm = io.perm;
   pk.offsets = io.offsets;
   pk.out = static_cast<uint16_t*>(io.xp);
   pk.T = io.T;
-  pk.K = W->m;
-  pk.E = W->E;
+  pk.K = c.m;
+  pk.E = c.E;
   pk.topk = io.k;
   if (io.topk_idx) {  // the dispatch is derived while packing
     pk.topk_idx = io.topk_idx;
@@ -366,61 +385,51 @@ int run_pack(const moe_weights* W, const FfnIo& io, hipStream_t s) {
   return MOE_OK;
 }
 
-// Grouped GEMM over the experts holding at least min_rows rows: packed x ->
-// packed H (hpk) -> down_out with the given down epilogue, whose reduction
-// is split into down_ksplit slices (EPI_DOWN_ACC only).
-int run_gemm(const moe_weights* W, const FfnIo& io, int min_rows, uint16_t* hpk, int down_epi, float* down_out,
-             hipStream_t s, int down_ksplit = 1) {
+// Grouped GEMM over every expert: packed x -> packed H -> unweighted rows in
+// dispatch order (y_rows).
+moe_status run_gemm(const moe_weights* W, const FfnIo& io, float* y_rows, hipStream_t s) {
+  const LayerCfg& c = W->c;
   const long long n = (long long)io.T * io.k;
   moe::GemmArgs g{};
   g.offsets = io.offsets;
-  g.perm = io.perm;
-  g.topk_w = io.topk_w;
-  g.topk = io.k;
-  g.E = W->E;
-  g.min_rows = min_rows;
-  // row blocks: at most n/256 full ones plus one partial per served expert
-  g.W = (int)(n / moe::gemm_rows_per_block() + std::min<long long>(W->E, n / min_rows));
-  g.cg = std::max(1, env_int("MOE_GEMM_CG", 4));
+  g.E = c.E;
+  // row blocks: at most n/256 full ones plus one partial per expert
+  g.W = (int)(n / moe::gemm_rows_per_block() + std::min<long long>(c.E, n));
+  g.cg = tuned(c.tune.gemm_cg, 4);
   // experts averaging under one full row block: skip the products of empty
   // row fragments
-  g.skip_empty = env_int("MOE_GEMM_SKIP", n < (long long)moe::gemm_rows_per_block() * W->E ? 1 : 0) != 0;
-  g.ksplit = 1;
+  g.skip_empty = tuned_on(c.tune.gemm_skip, n < (long long)moe::gemm_rows_per_block() * c.E);
   // up: packed x -> packed H
   g.w = W->up;
   g.act = static_cast<const uint16_t*>(io.xp);
-  g.h_out = hpk;
-  g.K = W->m;
-  g.N = W->p;
-  const int up_epi = W->kind == MOE_SWIGLU ? moe::EPI_UP_SWIGLU : moe::EPI_UP_RELU;
+  g.h_out = static_cast<uint16_t*>(io.h);
+  g.K = c.m;
+  g.N = c.p;
+  const int up_epi = c.kind == MOE_SWIGLU ? moe::EPI_UP_SWIGLU : moe::EPI_UP_RELU;
   MOE_TRY_HIP(run("gemm_up", s, [&] { return moe::launch_ffn_gemm(g, up_epi, s); }));
-  // down: packed H -> rows in dispatch order, or the weighted combine
+  // down: packed H -> rows in dispatch order
   g.w = W->down;
-  g.act = hpk;
+  g.act = static_cast<const uint16_t*>(io.h);
   g.h_out = nullptr;
-  g.f_out = down_out;
-  g.K = W->p;
-  g.N = W->m;
-  g.ksplit = down_epi == moe::EPI_DOWN_ACC ? std::max(1, std::min(down_ksplit, W->p / 64)) : 1;
-  MOE_TRY_HIP(run("gemm_down", s, [&] { return moe::launch_ffn_gemm(g, down_epi, s); }));
+  g.f_out = y_rows;
+  g.K = c.p;
+  g.N = c.m;
+  MOE_TRY_HIP(run("gemm_down", s, [&] { return moe::launch_ffn_gemm(g, moe::EPI_DOWN_ROWS, s); }));
   return MOE_OK;
 }
 
-// Skinny decode kernels over the experts holding at most max_rows rows (all
-// of them when max_rows <= 0).  x_packed: io.xp already holds the packed x
-// rows (the hybrid path packs once for both kernels).
-int run_skinny(const moe_weights* W, const FfnIo& io, int max_rows, hipStream_t s, bool x_packed = false) {
-  const int m = W->m, p = W->p, E = W->E, T = io.T, k = io.k;
-  const bool swiglu = W->kind == MOE_SWIGLU;
-  const int qb = weight_bits(W);
+// Skinny decode kernels over every expert.
+moe_status run_skinny(const moe_weights* W, const FfnIo& io, hipStream_t s) {
+  const LayerCfg& c = W->c;
+  const int m = c.m, p = c.p, E = c.E, T = io.T, k = io.k;
+  const bool swiglu = c.kind == MOE_SWIGLU;
+  const int qb = weight_bits(c);
   const bool i8 = qb != 0;  // integer weights (int8 or int4)
-  const int mt = skinny_mt(W, T, k);
-  const bool packed = skinny_packed(W, T, k);
-  // waves split the reduction unless the activations are packed (measured)
-  const char* wv = getenv("MOE_SKINNY_WAVES");
-  const bool splitk = wv && *wv ? wv[0] == 'k' : !packed;
-  if (packed && !x_packed)
-    if (int rc = run_pack(W, io, s)) return rc;
+  const int mt = skinny_mt(c, T, k);
+  const bool packed = skinny_packed(c, T, k);
+  const bool splitk = skinny_splitk(c, T, k);
+  if (packed)
+    if (moe_status rc = run_pack(c, io, s)) return rc;
   const int R = moe::skinny_rows(mt);
   moe::SkinnyArgs a{};
   a.perm = io.perm;
@@ -431,7 +440,6 @@ int run_skinny(const moe_weights* W, const FfnIo& io, int max_rows, hipStream_t 
   a.W = E + (int)((long long)T * k / R);
   a.topk_w = io.topk_w;
   a.ksplit = 1;
-  a.max_rows = max_rows;
   if ((long long)(p / 16) * a.W * 4 >= 0x7FFFFFF0LL || (long long)(m / 16) * a.W * 4 >= 0x7FFFFFF0LL)
     return fail(MOE_ERR_UNSUPPORTED, "too many work items for one launch (T*k=%lld)", (long long)T * k);
   // up: gate (+up) projection with the activation epilogue, x -> H
@@ -445,10 +453,7 @@ int run_skinny(const moe_weights* W, const FfnIo& io, int max_rows, hipStream_t 
   a.gather = packed ? 0 : 1;
   a.packed = packed;
   a.h_packed = packed;
-  // packed rows with the columns split over the waves: every wave of a
-  // workgroup reads the same activation fragments, so they are copied into
-  // LDS once per workgroup (MOE_SKINNY_SA=0 turns this off)
-  a.shared_act = packed && !splitk && env_int("MOE_SKINNY_SA", 1) != 0;
+  a.shared_act = skinny_shared(c, T, k);
   // the dispatch is derived in this kernel's prologue (gathered rows) or was
   // derived by the row packing
   if (io.topk_idx && !packed) {
@@ -462,16 +467,14 @@ int run_skinny(const moe_weights* W, const FfnIo& io, int max_rows, hipStream_t 
   // skewed routing) would have their weights streamed once per 64-row chunk.
   // With shared activations both projections serve them with twelve-tile
   // work items instead (192-row chunks), in the same launch as the four-tile
-  // items of the other experts (MOE_SKINNY_WIDE=0 turns this off; for the
-  // down projection alone MOE_SKINNY_WIDE_DOWN=0).  For the down projection
-  // the split launch runs at two waves per SIMD where the four-tile kernel
-  // alone runs at four; with only the activation fragments that hold real
-  // rows copied, the split still measured ahead on the skewed layer (167
-  // against 173 us).
+  // items of the other experts.  For the down projection the split launch
+  // runs at two waves per SIMD where the four-tile kernel alone runs at four;
+  // with only the activation fragments that hold real rows copied, the split
+  // still measured ahead on the skewed layer (167 against 173 us).
   const int up_epi = swiglu ? moe::EPI_UP_SWIGLU : moe::EPI_UP_RELU;
-  const int up_ct = skinny_ct(mt, qb, swiglu ? 2 : 1, "MOE_UP_CT");
-  const bool wide = max_rows <= 0 && mt == 4 && up_ct == 2 && a.shared_act && !i8 && !a.topk_idx &&
-                    env_int("MOE_SKINNY_WIDE", 1) != 0;
+  const int up_ct = skinny_ct(mt, qb, swiglu ? 2 : 1, c.tune.up_ct);
+  const bool wide =
+      mt == 4 && up_ct == 2 && a.shared_act && !i8 && !a.topk_idx && tuned_on(c.tune.skinny_wide, true);
   constexpr int kWideMt = 12;
   moe::SkinnyArgs aw{};
   if (wide) {
@@ -487,7 +490,7 @@ int run_skinny(const moe_weights* W, const FfnIo& io, int max_rows, hipStream_t 
     return wide ? moe::launch_ffn_skinny_split(a, aw, up_epi, s)
                 : moe::launch_ffn_skinny(a, up_epi, qb, mt, up_ct, splitk, s);
   }));
-  // down: H -> weighted combine (or unweighted rows)
+  // down: H -> unweighted rows (or the weighted combine)
   a.topk_idx = nullptr;
   a.d_counts = a.d_offsets = a.d_perm = a.d_inv = nullptr;
   a.w = W->down;
@@ -501,11 +504,10 @@ int run_skinny(const moe_weights* W, const FfnIo& io, int max_rows, hipStream_t 
   a.gather = 0;
   a.packed = packed;
   a.h_packed = 0;
-  const DownShape ds = skinny_down_shape(W, T, k);
-  int dn_ct = ds.ct;
+  const DownShape ds = skinny_down_shape(c, T, k);
   // inside the layer: unweighted rows per reduction slice for the combine,
   // or weighted rows added into y_acc; alone: unweighted rows, one slice
-  const bool rows = io.combine && io.yperm && skinny_rows_combine();
+  const bool rows = io.combine && io.yperm && skinny_rows_combine(c);
   if (io.combine) a.ksplit = ds.ks;
   if (rows) {
     a.f_out = io.yperm;
@@ -513,8 +515,8 @@ int run_skinny(const moe_weights* W, const FfnIo& io, int max_rows, hipStream_t 
   }
   if (io.slices) *io.slices = rows ? a.ksplit : 1;
   const int dn_epi = io.combine && !rows ? moe::EPI_DOWN_ACC : moe::EPI_DOWN_ROWS;
-  const bool wide_dn = wide && a.ksplit == 1 && dn_ct == 2 && env_int("MOE_SKINNY_WIDE_DOWN", 1) != 0;
-  if (wide && !wide_dn) a.max_rows = max_rows;  // the four-tile launch serves every expert
+  const bool wide_dn = wide && a.ksplit == 1 && ds.ct == 2 && tuned_on(c.tune.skinny_wide_down, true);
+  if (wide && !wide_dn) a.max_rows = 0;  // the four-tile launch serves every expert
   if (wide_dn) {
     const int W_wide = aw.W;
     aw = a;
@@ -524,83 +526,68 @@ int run_skinny(const moe_weights* W, const FfnIo& io, int max_rows, hipStream_t 
   }
   MOE_TRY_HIP(run("ffn_down", s, [&]() -> hipError_t {
     return wide_dn ? moe::launch_ffn_skinny_split(a, aw, dn_epi, s)
-                   : moe::launch_ffn_skinny(a, dn_epi, qb, mt, dn_ct, splitk, s);
+                   : moe::launch_ffn_skinny(a, dn_epi, qb, mt, ds.ct, splitk, s);
   }));
   return MOE_OK;
 }
 
-int run_ffn(const moe_weights* W, const FfnIo& io, hipStream_t s) {
-  const int m = W->m, p = W->p, E = W->E, T = io.T, k = io.k;
-  const bool swiglu = W->kind == MOE_SWIGLU;
-  if (W->w_dtype == MOE_F32) {
-    moe::F32Args a{};
-    a.perm = io.perm;
-    a.offsets = io.offsets;
-    a.topk = k;
-    a.E = E;
-    a.W = E + (int)((long long)T * k / 16);
-    a.topk_w = io.topk_w;
-    // up: x [T][m] -> H [T*k][p]
-    a.w1 = static_cast<const float*>(W->up);
-    a.w3 = swiglu ? static_cast<const float*>(W->up3) : nullptr;
-    a.act = static_cast<const float*>(io.x);
-    a.out = static_cast<float*>(io.h);
-    a.K = m;
-    a.N = p;
-    a.gather = 1;
-    a.epi = swiglu ? moe::EPI_UP_SWIGLU : moe::EPI_UP_RELU;
-    MOE_TRY_HIP(run("ffn_f32_up", s, [&] { return moe::launch_ffn_f32(a, s); }));
-    // down: H -> y
-    a.w1 = static_cast<const float*>(W->down);
-    a.w3 = nullptr;
-    a.act = static_cast<const float*>(io.h);
-    a.out = io.down_out;
-    a.K = p;
-    a.N = m;
-    a.gather = 0;
-    a.epi = io.combine ? moe::EPI_DOWN_ACC : moe::EPI_DOWN_ROWS;
-    MOE_TRY_HIP(run("ffn_f32_down", s, [&] { return moe::launch_ffn_f32(a, s); }));
-    return MOE_OK;
-  }
-  switch (ffn_path(W, T, k)) {
-    case Path::GEMM:
-      if (int rc = run_pack(W, io, s)) return rc;
-      // with the combine following: unweighted rows into y_perm
-      return run_gemm(W, io, 1, static_cast<uint16_t*>(io.h), moe::EPI_DOWN_ROWS,
-                      io.combine ? io.yperm : io.down_out, s);
-    case Path::HYBRID: {
-      if (int rc = run_pack(W, io, s)) return rc;
-      const int hot = hot_rows();
-      const int down_epi = io.combine ? moe::EPI_DOWN_ACC : moe::EPI_DOWN_ROWS;
-      // The hot experts' GEMM goes first on the caller's stream, so its
-      // workgroups (a whole CU's LDS each) take CUs before the skinny
-      // workgroups of the side stream fill the rest; its down projection
-      // splits the reduction so its few row blocks spread over more CUs.
-      std::lock_guard<std::mutex> lk(W->mu);
-      MOE_TRY_HIP(hipEventRecord(W->ev_fork, s));
-      MOE_TRY_HIP(hipStreamWaitEvent(W->side, W->ev_fork, 0));
-      const int rc_g = run_gemm(W, io, hot, static_cast<uint16_t*>(io.hp), down_epi, io.down_out, s,
-                                env_int("MOE_GEMM_KSPLIT", 4));
-      const int rc_s = rc_g ? MOE_OK : run_skinny(W, io, hot - 1, W->side, true);
-      // join even after a failed launch, so the side stream never runs ahead
-      const hipError_t e1 = hipEventRecord(W->ev_join, W->side);
-      const hipError_t e2 = hipStreamWaitEvent(s, W->ev_join, 0);
-      if (rc_g) return rc_g;
-      if (rc_s) return rc_s;
-      MOE_TRY_HIP(e1);
-      MOE_TRY_HIP(e2);
+moe_status run_ffn(const moe_weights* W, const FfnIo& io, hipStream_t s) {
+  const LayerCfg& c = W->c;
+  const int m = c.m, p = c.p, E = c.E, T = io.T, k = io.k;
+  const bool swiglu = c.kind == MOE_SWIGLU;
+  switch (ffn_path(c, T, k)) {
+    case Path::F32: {
+      moe::F32Args a{};
+      a.perm = io.perm;
+      a.offsets = io.offsets;
+      a.topk = k;
+      a.E = E;
+      a.W = E + (int)((long long)T * k / 16);
+      a.topk_w = io.topk_w;
+      // up: x [T][m] -> H [T*k][p]
+      a.w1 = static_cast<const float*>(W->up);
+      a.w3 = swiglu ? static_cast<const float*>(W->up3) : nullptr;
+      a.act = static_cast<const float*>(io.x);
+      a.out = static_cast<float*>(io.h);
+      a.K = m;
+      a.N = p;
+      a.gather = 1;
+      a.epi = swiglu ? moe::EPI_UP_SWIGLU : moe::EPI_UP_RELU;
+      MOE_TRY_HIP(run("ffn_f32_up", s, [&] { return moe::launch_ffn_f32(a, s); }));
+      // down: H -> y
+      a.w1 = static_cast<const float*>(W->down);
+      a.w3 = nullptr;
+      a.act = static_cast<const float*>(io.h);
+      a.out = io.down_out;
+      a.K = p;
+      a.N = m;
+      a.gather = 0;
+      a.epi = io.combine ? moe::EPI_DOWN_ACC : moe::EPI_DOWN_ROWS;
+      MOE_TRY_HIP(run("ffn_f32_down", s, [&] { return moe::launch_ffn_f32(a, s); }));
       return MOE_OK;
     }
+    case Path::GEMM:
+      if (moe_status rc = run_pack(c, io, s)) return rc;
+      // with the combine following: unweighted rows into y_perm
+      return run_gemm(W, io, io.combine ? io.yperm : io.down_out, s);
     default:
-      return run_skinny(W, io, 0, s);
+      return run_skinny(W, io, s);
   }
 }
 
-int check_weights_match(const moe_weights* w, int m, int p, int E) {
+moe_status check_weights_match(const moe_weights* w, int m, int p, int E) {
   if (!w) return fail(MOE_ERR_INVALID_ARG, "weights handle is NULL");
-  if (w->m != m || w->p != p || w->E != E)
+  if (w->c.m != m || w->c.p != p || w->c.E != E)
     return fail(MOE_ERR_INVALID_ARG, "shape (m=%d,p=%d,E=%d) does not match the weights (m=%d,p=%d,E=%d)", m, p, E,
-                w->m, w->p, w->E);
+                w->c.m, w->c.p, w->c.E);
+  return MOE_OK;
+}
+
+// The workspace a call received, checked against the layout it needs.
+moe_status check_workspace(const Ws& L, const void* workspace, size_t ws_bytes) {
+  if (!workspace || ws_bytes < L.total)
+    return fail(MOE_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", L.total, workspace ? ws_bytes : 0);
+  if (reinterpret_cast<uintptr_t>(workspace) & 255u) return fail(MOE_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
   return MOE_OK;
 }
 
@@ -610,15 +597,14 @@ extern "C" {
 
 const char* moe_last_error(void) { return g_err.c_str(); }
 
-int moe_abi_version(void) { return 1; }
+int moe_abi_version(void) { return 2; }
 
-int moe_weights_create(int m, int p, int E, int kind, int w_dtype, const void* w1, const void* w_up, const void* w2,
-                       const float* s1, const float* s_up, const float* s2, void* stream, moe_weights** out) {
+moe_status moe_weights_create(int m, int p, int E, int kind, int w_dtype, const void* w1, const void* w_up,
+                              const void* w2, const float* s1, const float* s_up, const float* s2, void* stream,
+                              moe_weights** out) {
   if (!out) return fail(MOE_ERR_INVALID_ARG, "out is NULL");
   *out = nullptr;
-  if (int rc = check_shape(1, m, p, E, 1)) return rc;
-  if (kind != MOE_MLP_RELU && kind != MOE_SWIGLU) return fail(MOE_ERR_INVALID_ARG, "unknown expert kind %d", kind);
-  if (!valid_dtype(w_dtype)) return fail(MOE_ERR_UNSUPPORTED, "weight dtype %d unsupported", w_dtype);
+  if (moe_status rc = check_layer(m, p, E, kind, w_dtype)) return rc;
   const bool swiglu = kind == MOE_SWIGLU;
   if (!w1 || !w2 || (swiglu && !w_up)) return fail(MOE_ERR_INVALID_ARG, "required weight pointer is NULL");
   if (!swiglu && w_up) return fail(MOE_ERR_INVALID_ARG, "w_up must be NULL for the ReLU MLP");
@@ -626,8 +612,6 @@ int moe_weights_create(int m, int p, int E, int kind, int w_dtype, const void* w
   const int qb = w_dtype == MOE_I8 ? 8 : (w_dtype == MOE_I4 ? 4 : 0);
   if (i8 && (!s1 || !s2 || (swiglu && !s_up))) return fail(MOE_ERR_INVALID_ARG, "integer weights need their scales");
   if (!i8 && (s1 || s2 || s_up)) return fail(MOE_ERR_INVALID_ARG, "scales are only for integer weights");
-  if (w_dtype == MOE_I4 && (m % 128 || p % 128))
-    return fail(MOE_ERR_UNSUPPORTED, "int4 weights need m=%d and p=%d to be multiples of 128", m, p);
   if (!aligned16(w1) || !aligned16(w2) || (w_up && !aligned16(w_up)) || (s1 && !aligned16(s1)) ||
       (s2 && !aligned16(s2)) || (s_up && !aligned16(s_up)))
     return fail(MOE_ERR_INVALID_ARG, "weight pointers must be 16-byte aligned");
@@ -647,11 +631,11 @@ int moe_weights_create(int m, int p, int E, int kind, int w_dtype, const void* w
   const size_t total = align256(up_b) + align256(up3_b) + align256(dn_b) + sc_b;
   moe_weights* W = new (std::nothrow) moe_weights;
   if (!W) return fail(MOE_ERR_OOM, "host allocation failed");
-  W->m = m;
-  W->p = p;
-  W->E = E;
-  W->kind = kind;
-  W->w_dtype = w_dtype;
+  W->c.m = m;
+  W->c.p = p;
+  W->c.E = E;
+  W->c.kind = kind;
+  W->c.w_dtype = w_dtype;
   W->bytes = total;
   if (hipMalloc(&W->buf, total) != hipSuccess) {
     delete W;
@@ -690,16 +674,7 @@ int moe_weights_create(int m, int p, int E, int kind, int w_dtype, const void* w
     if (e == hipSuccess) e = moe::launch_pack_bf16(static_cast<const uint16_t*>(w2), W->down, E, p, m, 1, 0, s);
   }
   if (e == hipSuccess) e = hipStreamSynchronize(s);
-  if (e == hipSuccess && w_dtype == MOE_BF16) {
-    // the hybrid path's side stream (default priority) and fork/join events
-    e = hipStreamCreateWithFlags(&W->side, hipStreamNonBlocking);
-    if (e == hipSuccess) e = hipEventCreateWithFlags(&W->ev_fork, hipEventDisableTiming);
-    if (e == hipSuccess) e = hipEventCreateWithFlags(&W->ev_join, hipEventDisableTiming);
-  }
   if (e != hipSuccess) {
-    if (W->ev_fork) (void)hipEventDestroy(W->ev_fork);
-    if (W->ev_join) (void)hipEventDestroy(W->ev_join);
-    if (W->side) (void)hipStreamDestroy(W->side);
     (void)hipFree(W->buf);
     delete W;
     return fail(MOE_ERR_HIP, "packing the weights failed: %s", hipGetErrorString(e));
@@ -708,30 +683,56 @@ int moe_weights_create(int m, int p, int E, int kind, int w_dtype, const void* w
   return ok();
 }
 
-int moe_weights_destroy(moe_weights* w) {
+moe_status moe_weights_destroy(moe_weights* w) {
   if (!w) return ok();
-  if (w->side) {
-    (void)hipStreamSynchronize(w->side);
-    (void)hipEventDestroy(w->ev_fork);
-    (void)hipEventDestroy(w->ev_join);
-    (void)hipStreamDestroy(w->side);
-  }
   const hipError_t e = hipFree(w->buf);
   delete w;
   if (e != hipSuccess) return fail(MOE_ERR_HIP, "hipFree failed: %s", hipGetErrorString(e));
   return ok();
 }
 
-int moe_workspace_size(const moe_weights* w, int T, int k, size_t* bytes) {
-  if (!w || !bytes) return fail(MOE_ERR_INVALID_ARG, "NULL argument");
-  if (int rc = check_shape(T, w->m, w->p, w->E, k)) return rc;
-  *bytes = ws_layout(w, T, k).total;
+moe_status moe_weights_set_tuning(moe_weights* w, const moe_tuning* t) {
+  if (!w) return fail(MOE_ERR_INVALID_ARG, "weights handle is NULL");
+  const moe_tuning v = t ? *t : moe_tuning{};
+  if (moe_status rc = check_tuning(v)) return rc;
+  w->c.tune = v;
   return ok();
 }
 
-int moe_route_topk(const void* x, int x_dtype, const float* w_router, const float* b_router, int T, int m, int E,
-                   int k, unsigned flags, float* logits, int32_t* topk_idx, float* topk_w, void* stream) {
-  if (int rc = check_shape(T, m, 64, E, k)) return rc;
+moe_status moe_weights_get_tuning(const moe_weights* w, moe_tuning* t) {
+  if (!w || !t) return fail(MOE_ERR_INVALID_ARG, "NULL argument");
+  *t = w->c.tune;
+  return ok();
+}
+
+moe_status moe_workspace_size(const moe_weights* w, int T, int k, size_t* bytes) {
+  if (!w || !bytes) return fail(MOE_ERR_INVALID_ARG, "NULL argument");
+  if (moe_status rc = check_shape(T, w->c.m, w->c.p, w->c.E, k)) return rc;
+  *bytes = ws_layout(w->c, T, k).total;
+  return ok();
+}
+
+moe_status moe_workspace_size_for(int m, int p, int E, int kind, int w_dtype, const moe_tuning* t, int T, int k,
+                                  size_t* bytes) {
+  if (!bytes) return fail(MOE_ERR_INVALID_ARG, "bytes is NULL");
+  if (moe_status rc = check_layer(m, p, E, kind, w_dtype)) return rc;
+  if (moe_status rc = check_shape(T, m, p, E, k)) return rc;
+  LayerCfg c;
+  c.m = m;
+  c.p = p;
+  c.E = E;
+  c.kind = kind;
+  c.w_dtype = w_dtype;
+  c.tune = t ? *t : moe_tuning{};
+  if (moe_status rc = check_tuning(c.tune)) return rc;
+  *bytes = ws_layout(c, T, k).total;
+  return ok();
+}
+
+moe_status moe_route_topk(const void* x, int x_dtype, const float* w_router, const float* b_router, int T, int m,
+                          int E, int k, unsigned flags, float* logits, int32_t* topk_idx, float* topk_w,
+                          void* stream) {
+  if (moe_status rc = check_shape(T, m, 64, E, k)) return rc;
   const bool lin = (flags & MOE_ROUTE_LOGITS_IN) != 0;
   if (flags & ~MOE_ROUTE_LOGITS_IN) return fail(MOE_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
   if (!lin && x_dtype != MOE_F32 && x_dtype != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "x dtype %d", x_dtype);
@@ -748,9 +749,9 @@ int moe_route_topk(const void* x, int x_dtype, const float* w_router, const floa
   return ok();
 }
 
-int moe_dispatch(const int32_t* topk_idx, int T, int E, int k, int32_t* counts, int32_t* offsets, int32_t* perm,
-                 int32_t* inv_perm, void* stream) {
-  if (int rc = check_shape(T, 64, 64, E, k)) return rc;
+moe_status moe_dispatch(const int32_t* topk_idx, int T, int E, int k, int32_t* counts, int32_t* offsets,
+                        int32_t* perm, int32_t* inv_perm, void* stream) {
+  if (moe_status rc = check_shape(T, 64, 64, E, k)) return rc;
   if (!counts || !offsets) return fail(MOE_ERR_INVALID_ARG, "counts/offsets are NULL");
   if (T > 0 && (!topk_idx || !perm || !inv_perm)) return fail(MOE_ERR_INVALID_ARG, "NULL argument");
   const hipStream_t s = as_stream(stream);
@@ -760,19 +761,17 @@ int moe_dispatch(const int32_t* topk_idx, int T, int E, int k, int32_t* counts, 
   return ok();
 }
 
-int moe_expert_ffn(const moe_weights* w, const void* x, int x_dtype, int T, int m, int p, int E, int k,
-                   const int32_t* perm, const int32_t* offsets, float* y_perm, void* workspace, size_t ws_bytes,
-                   void* stream) {
-  if (int rc = check_weights_match(w, m, p, E)) return rc;
-  if (int rc = check_shape(T, m, p, E, k)) return rc;
-  if (int rc = check_combo(x_dtype, w->w_dtype)) return rc;
+moe_status moe_expert_ffn(const moe_weights* w, const void* x, int x_dtype, int T, int m, int p, int E, int k,
+                          const int32_t* perm, const int32_t* offsets, float* y_perm, void* workspace,
+                          size_t ws_bytes, void* stream) {
+  if (moe_status rc = check_weights_match(w, m, p, E)) return rc;
+  if (moe_status rc = check_shape(T, m, p, E, k)) return rc;
+  if (moe_status rc = check_combo(x_dtype, w->c.w_dtype)) return rc;
   if (T == 0) return ok();
   if (!x || !perm || !offsets || !y_perm) return fail(MOE_ERR_INVALID_ARG, "NULL argument");
   if (!aligned16(x) || !aligned16(y_perm)) return fail(MOE_ERR_INVALID_ARG, "x/y_perm must be 16-byte aligned");
-  const Ws L = ws_layout(w, T, k);
-  if (!workspace || ws_bytes < L.total)
-    return fail(MOE_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", L.total, workspace ? ws_bytes : 0);
-  if (reinterpret_cast<uintptr_t>(workspace) & 255u) return fail(MOE_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  const Ws L = ws_layout(w->c, T, k);
+  if (moe_status rc = check_workspace(L, workspace, ws_bytes)) return rc;
   char* ws = static_cast<char*>(workspace);
   FfnIo io{};
   io.x = x;
@@ -782,15 +781,14 @@ int moe_expert_ffn(const moe_weights* w, const void* x, int x_dtype, int T, int 
   io.offsets = const_cast<int32_t*>(offsets);
   io.h = ws + L.h;
   io.xp = ws + L.xp;
-  io.hp = ws + L.hp;
   io.down_out = y_perm;
   io.combine = false;
-  if (int rc = run_ffn(w, io, as_stream(stream))) return rc;
+  if (moe_status rc = run_ffn(w, io, as_stream(stream))) return rc;
   return ok();
 }
 
-int moe_combine(const float* y_perm, const int32_t* inv_perm, const float* topk_w, int T, int m, int k, void* y,
-                int y_dtype, void* stream) {
+moe_status moe_combine(const float* y_perm, const int32_t* inv_perm, const float* topk_w, int T, int m, int k,
+                       void* y, int y_dtype, void* stream) {
   if (T < 0 || m <= 0 || k < 1) return fail(MOE_ERR_INVALID_ARG, "bad sizes T=%d m=%d k=%d", T, m, k);
   if (m % 64) return fail(MOE_ERR_UNSUPPORTED, "m=%d must be a multiple of 64", m);
   if (y_dtype != MOE_F32 && y_dtype != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "y dtype %d", y_dtype);
@@ -819,23 +817,28 @@ struct Fusion {
   void* x_norm = nullptr;
 };
 
-int layer_forward(const moe_weights* w, const float* w_router, const float* b_router, const void* x, int x_dtype,
-                  int T, int m, int p, int E, int k, void* y, int y_dtype, void* workspace, size_t ws_bytes,
-                  int32_t* dbg_topk_idx, float* dbg_topk_w, float* dbg_logits, int32_t* dbg_counts,
-                  int32_t* dbg_offsets, int32_t* dbg_perm, void* stream, const Fusion& f) {
-  if (int rc = check_weights_match(w, m, p, E)) return rc;
-  if (int rc = check_shape(T, m, p, E, k)) return rc;
-  if (int rc = check_combo(x_dtype, w->w_dtype)) return rc;
+// Arguments of one layer forward after validation of everything but the
+// workspace.
+moe_status check_forward(const moe_weights* w, const float* w_router, const void* x, int x_dtype, int T, int m, int p,
+                         int E, int k, const void* y, int y_dtype) {
+  if (moe_status rc = check_weights_match(w, m, p, E)) return rc;
+  if (moe_status rc = check_shape(T, m, p, E, k)) return rc;
+  if (moe_status rc = check_combo(x_dtype, w->c.w_dtype)) return rc;
   if (y_dtype != MOE_F32 && y_dtype != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "y dtype %d", y_dtype);
-  if (T == 0) return ok();
+  if (T == 0) return MOE_OK;
   if (!w_router || !x || !y) return fail(MOE_ERR_INVALID_ARG, "NULL argument");
   if (!aligned16(x) || !aligned16(y)) return fail(MOE_ERR_INVALID_ARG, "x/y must be 16-byte aligned");
-  const Ws L = ws_layout(w, T, k);
-  if (!workspace || ws_bytes < L.total)
-    return fail(MOE_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", L.total, workspace ? ws_bytes : 0);
-  if (reinterpret_cast<uintptr_t>(workspace) & 255u) return fail(MOE_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
-  char* ws = static_cast<char*>(workspace);
-  const hipStream_t s = as_stream(stream);
+  return MOE_OK;
+}
+
+// The launches of one layer forward into a checked workspace `ws` laid out
+// as L.  T > 0.
+moe_status enqueue_forward(const moe_weights* w, const float* w_router, const float* b_router, const void* x,
+                           int x_dtype, int T, int k, void* y, int y_dtype, char* ws, const Ws& L,
+                           int32_t* dbg_topk_idx, float* dbg_topk_w, float* dbg_logits, int32_t* dbg_counts,
+                           int32_t* dbg_offsets, int32_t* dbg_perm, hipStream_t s, const Fusion& f) {
+  const LayerCfg& c = w->c;
+  const int m = c.m, E = c.E;
   float* logits = dbg_logits ? dbg_logits : reinterpret_cast<float*>(ws + L.logits);
   int32_t* idx = dbg_topk_idx ? dbg_topk_idx : reinterpret_cast<int32_t*>(ws + L.idx);
   float* tw = dbg_topk_w ? dbg_topk_w : reinterpret_cast<float*>(ws + L.w);
@@ -846,17 +849,15 @@ int layer_forward(const moe_weights* w, const float* w_router, const float* b_ro
   const bool y_bf16 = y_dtype == MOE_BF16;
   float* yacc = y_bf16 ? reinterpret_cast<float*>(ws + L.yacc) : static_cast<float*>(y);
   const size_t ny = (size_t)T * m;
-  // decode-sized layers on the MFMA path: the up projection derives the
-  // dispatch itself
-  const Path path = ffn_path(w, T, k);
+  const Path path = ffn_path(c, T, k);
   const bool gemm = path == Path::GEMM;
   // at decode sizes the dispatch is derived by the first FFN kernel: the up
   // projection's prologue, or the row packing before it
   const bool fused = path == Path::SKINNY && (long long)T * k <= moe::kFusedDispatchMax;
   // unweighted expert rows and the combine kernel (the grouped GEMM, and the
-  // skinny kernels unless MOE_DOWN_ROWS=0), or weighted rows added into y_acc
+  // skinny kernels unless tuned otherwise), or weighted rows added into y_acc
   // (zeroed by the router) and a final conversion
-  const bool rows = gemm || (path == Path::SKINNY && skinny_rows_combine());
+  const bool rows = gemm || (path == Path::SKINNY && skinny_rows_combine(c));
 
   // the neighbouring ops: the input rows' norm in the routing pass (the
   // experts then read the normalised rows), the residual added by the combine
@@ -881,21 +882,36 @@ int layer_forward(const moe_weights* w, const float* w_router, const float* b_ro
   io.topk_w = tw;
   io.h = ws + L.h;
   io.xp = ws + L.xp;
-  io.hp = ws + L.hp;
   io.down_out = yacc;
   io.combine = true;
   io.yperm = rows ? reinterpret_cast<float*>(ws + L.yperm) : nullptr;
   int slices = 1;
   io.slices = &slices;
-  if (int rc = run_ffn(w, io, s)) return rc;
+  if (moe_status rc = run_ffn(w, io, s)) return rc;
   if (rows) {
     MOE_TRY_HIP(run("combine", s, [&] {
       return moe::launch_combine(io.yperm, inv, tw, T, m, k, slices, (size_t)T * k * m, y, y_bf16, s, f.residual);
     }));
-    return ok();
+    return MOE_OK;
   }
   if (y_bf16)
     MOE_TRY_HIP(run("finalize", s, [&] { return moe::launch_f32_to_bf16(yacc, static_cast<uint16_t*>(y), ny, s); }));
+  return MOE_OK;
+}
+
+moe_status layer_forward(const moe_weights* w, const float* w_router, const float* b_router, const void* x,
+                         int x_dtype, int T, int m, int p, int E, int k, void* y, int y_dtype, void* workspace,
+                         size_t ws_bytes, int32_t* dbg_topk_idx, float* dbg_topk_w, float* dbg_logits,
+                         int32_t* dbg_counts, int32_t* dbg_offsets, int32_t* dbg_perm, void* stream,
+                         const Fusion& f) {
+  if (moe_status rc = check_forward(w, w_router, x, x_dtype, T, m, p, E, k, y, y_dtype)) return rc;
+  if (T == 0) return ok();
+  const Ws L = ws_layout(w->c, T, k);
+  if (moe_status rc = check_workspace(L, workspace, ws_bytes)) return rc;
+  if (moe_status rc = enqueue_forward(w, w_router, b_router, x, x_dtype, T, k, y, y_dtype,
+                                      static_cast<char*>(workspace), L, dbg_topk_idx, dbg_topk_w, dbg_logits,
+                                      dbg_counts, dbg_offsets, dbg_perm, as_stream(stream), f))
+    return rc;
   return ok();
 }
 
@@ -903,19 +919,19 @@ int layer_forward(const moe_weights* w, const float* w_router, const float* b_ro
 
 extern "C" {
 
-int moe_layer_forward(const moe_weights* w, const float* w_router, const float* b_router, const void* x, int x_dtype,
-                      int T, int m, int p, int E, int k, void* y, int y_dtype, void* workspace, size_t ws_bytes,
-                      int32_t* dbg_topk_idx, float* dbg_topk_w, float* dbg_logits, int32_t* dbg_counts,
-                      int32_t* dbg_offsets, int32_t* dbg_perm, void* stream) {
+moe_status moe_layer_forward(const moe_weights* w, const float* w_router, const float* b_router, const void* x,
+                             int x_dtype, int T, int m, int p, int E, int k, void* y, int y_dtype, void* workspace,
+                             size_t ws_bytes, int32_t* dbg_topk_idx, float* dbg_topk_w, float* dbg_logits,
+                             int32_t* dbg_counts, int32_t* dbg_offsets, int32_t* dbg_perm, void* stream) {
   return layer_forward(w, w_router, b_router, x, x_dtype, T, m, p, E, k, y, y_dtype, workspace, ws_bytes,
                        dbg_topk_idx, dbg_topk_w, dbg_logits, dbg_counts, dbg_offsets, dbg_perm, stream, Fusion{});
 }
 
-int moe_layer_forward_fused(const moe_weights* w, const float* w_router, const float* b_router, const void* x,
-                            int x_dtype, int norm, const float* gamma, const float* beta, float eps,
-                            const void* residual, int T, int m, int p, int E, int k, void* y, int y_dtype,
-                            void* workspace, size_t ws_bytes, void* x_norm, int32_t* dbg_topk_idx,
-                            float* dbg_topk_w, float* dbg_logits, void* stream) {
+moe_status moe_layer_forward_fused(const moe_weights* w, const float* w_router, const float* b_router, const void* x,
+                                   int x_dtype, int norm, const float* gamma, const float* beta, float eps,
+                                   const void* residual, int T, int m, int p, int E, int k, void* y, int y_dtype,
+                                   void* workspace, size_t ws_bytes, void* x_norm, int32_t* dbg_topk_idx,
+                                   float* dbg_topk_w, float* dbg_logits, void* stream) {
   if (norm != MOE_NORM_NONE && norm != MOE_NORM_LAYER && norm != MOE_NORM_RMS)
     return fail(MOE_ERR_INVALID_ARG, "norm kind %d", norm);
   if (norm == MOE_NORM_NONE && (gamma || beta || x_norm))
@@ -945,9 +961,9 @@ struct moe_graph {
 
 extern "C" {
 
-int moe_layer_graph_create(const moe_weights* w, const float* w_router, const float* b_router, const void* x,
-                           int x_dtype, int T, int m, int p, int E, int k, void* y, int y_dtype, void* workspace,
-                           size_t ws_bytes, moe_graph** out) {
+moe_status moe_layer_graph_create(const moe_weights* w, const float* w_router, const float* b_router, const void* x,
+                                  int x_dtype, int T, int m, int p, int E, int k, void* y, int y_dtype,
+                                  void* workspace, size_t ws_bytes, moe_graph** out) {
   if (!out) return fail(MOE_ERR_INVALID_ARG, "out is NULL");
   *out = nullptr;
   {
@@ -961,8 +977,8 @@ int moe_layer_graph_create(const moe_weights* w, const float* w_router, const fl
     (void)hipStreamDestroy(cs);
     return fail(MOE_ERR_HIP, "hipStreamBeginCapture: %s", hipGetErrorString(e));
   }
-  const int rc = moe_layer_forward(w, w_router, b_router, x, x_dtype, T, m, p, E, k, y, y_dtype, workspace,
-                                   ws_bytes, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, cs);
+  const moe_status rc = moe_layer_forward(w, w_router, b_router, x, x_dtype, T, m, p, E, k, y, y_dtype, workspace,
+                                          ws_bytes, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, cs);
   const std::string err = rc ? g_err : std::string();
   hipGraph_t graph = nullptr;
   e = hipStreamEndCapture(cs, &graph);  // ends the capture even after a failed forward
@@ -991,14 +1007,14 @@ int moe_layer_graph_create(const moe_weights* w, const float* w_router, const fl
   return ok();
 }
 
-int moe_graph_launch(const moe_graph* g, void* stream) {
+moe_status moe_graph_launch(const moe_graph* g, void* stream) {
   if (!g) return fail(MOE_ERR_INVALID_ARG, "graph is NULL");
   if (!g->exec) return ok();
   MOE_TRY_HIP(hipGraphLaunch(g->exec, as_stream(stream)));
   return ok();
 }
 
-int moe_graph_destroy(moe_graph* g) {
+moe_status moe_graph_destroy(moe_graph* g) {
   if (!g) return ok();
   hipError_t e = hipSuccess;
   if (g->exec) e = hipGraphExecDestroy(g->exec);
@@ -1009,7 +1025,7 @@ int moe_graph_destroy(moe_graph* g) {
   return ok();
 }
 
-int moe_profile_begin(int max_launches) {
+moe_status moe_profile_begin(int max_launches) {
   std::lock_guard<std::mutex> lk(g_prof.mu);
   if (max_launches < 1 || max_launches > (1 << 20)) return fail(MOE_ERR_INVALID_ARG, "max_launches out of range");
   for (hipEvent_t e : g_prof.ev) (void)hipEventDestroy(e);
@@ -1023,7 +1039,7 @@ int moe_profile_begin(int max_launches) {
   return ok();
 }
 
-int moe_profile_end(void) {
+moe_status moe_profile_end(void) {
   std::lock_guard<std::mutex> lk(g_prof.mu);
   if (!g_prof.on) return fail(MOE_ERR_INVALID_ARG, "profiling was not started");
   g_prof.on = false;
@@ -1041,7 +1057,7 @@ int moe_profile_end(void) {
   return ok();
 }
 
-int moe_profile_query(const char* kernel, double* total_ms, int* launches) {
+moe_status moe_profile_query(const char* kernel, double* total_ms, int* launches) {
   if (!kernel || !total_ms || !launches) return fail(MOE_ERR_INVALID_ARG, "NULL argument");
   std::lock_guard<std::mutex> lk(g_prof.mu);
   auto it = g_prof.total.find(kernel);

@@ -46,28 +46,15 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v); }
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
 
-#ifndef MOE_GEMM_SCHED
-#define MOE_GEMM_SCHED 2
-#endif
-// Schedule 3 runs one wave per SIMD with a 128 x 128 tile each (accumulators
-// in AGPRs); the others two waves per SIMD with 128 x 64 tiles.
-constexpr bool kOnePerSimd = MOE_GEMM_SCHED == 3;
 constexpr int kBM = 256;     // rows per workgroup
 constexpr int kWR = 2;       // wave rows
-constexpr int kWC = kOnePerSimd ? 2 : 4;  // wave columns
+constexpr int kWC = 4;       // wave columns
 constexpr int kWaves = kWR * kWC;
 constexpr int kMF = 8;       // row fragments per wave (128 rows)
-constexpr int kNF = kOnePerSimd ? 8 : 4;  // column fragments per wave
+constexpr int kNF = 4;       // column fragments per wave
 constexpr int kCPW = 16 / kWaves;  // A (and B) fragments each wave copies per stage
 constexpr int kCPS = 2 * kCPW;     // copies per wave per stage
 constexpr int kStages = 5;   // LDS ring depth: 5 x 32 KiB, all of a CU's LDS
-// Main-loop schedule.  0: every wave waits for stage s, reads it and
-// multiplies it; 1: every wave reads stage s+1 into a second register set
-// during step s; 2: ping-pong, the two waves of each SIMD in opposite
-// phases (one multiplies while the other reads the next stage and issues
-// copies); 3: one wave per SIMD, reading stage s+1 into a second register set
-// between the groups of products of stage s, with one copy per group.
-constexpr int kSched = MOE_GEMM_SCHED;
 constexpr int kFrag = 1024;  // bytes of one 64-lane x 16-byte fragment
 
 // acc += a * b on the matrix cores, accumulating in place.  Written as
@@ -76,18 +63,12 @@ constexpr int kFrag = 1024;  // bytes of one 64-lane x 16-byte fragment
 // their register footprint.  The accumulator is reused only 32 products
 // later, so consecutive products carry no dependence.
 __device__ __forceinline__ void mfma_acc(floatx4_t& acc, const bf16x8_t& a, const bf16x8_t& b) {
-  if constexpr (kOnePerSimd)
-    asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
-  else
-    asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
+  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
 }
 
 // Ties an accumulator to the surrounding statements in its register file.
 __device__ __forceinline__ void acc_tie(floatx4_t& acc) {
-  if constexpr (kOnePerSimd)
-    asm volatile("" : "+a"(acc));
-  else
-    asm volatile("" : "+v"(acc));
+  asm volatile("" : "+v"(acc));
 }
 
 // The compiler cannot see that the assembly above is a matrix instruction,
@@ -113,25 +94,11 @@ __device__ __forceinline__ void mfma_fence_out(floatx4_t (&acc)[MF][NF]) {
     for (int j = 0; j < NF; ++j) acc_tie(acc[i][j]);
 }
 
-// Waits until at most n stages of this wave's copies (kCPS copies each) are
-// outstanding.  n is uniform; n > 3 waits as for 3.
-__device__ __forceinline__ void wait_copies(int n) {
-  if (n >= 3)
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(3 * kCPS));
-  else if (n == 2)
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * kCPS));
-  else if (n == 1)
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(kCPS));
-  else
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-}
-
 // SKIP: row fragments past the row block's last real row skip their
 // products (the fragment reads still run, so the steady state keeps no branch
 // around a load); for layers whose experts hold few rows.
 template <int EPI, bool SKIP>
-__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(kOnePerSimd ? 1 : 2,
-                                                                                   kOnePerSimd ? 1 : 2))) void k_ffn_gemm(
+__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_ffn_gemm(
     const GemmArgs A) {
   constexpr int G = EPI == EPI_UP_SWIGLU ? 2 : 1;
   constexpr int TPW = kNF / G;  // column tiles per wave
@@ -142,21 +109,15 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(kOn
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  // wave row (128 rows) and wave column; ping-pong makes each wave row one
-  // group of four waves, one per SIMD
-  const int wm = kSched == 2 ? wave / kWC : wave % kWR;
-  const int wn = kSched == 2 ? wave % kWC : wave / kWR;
+  // wave row (128 rows) and wave column; each wave row is one group of four
+  // waves, one per SIMD (the ping-pong below)
+  const int wm = wave / kWC;
+  const int wn = wave % kWC;
   const int NB = A.N / 16;
   const int NBL = (NB + kWC * TPW - 1) / (kWC * TPW);  // column blocks
 
   int e, mb, nblock;
-  // logical index -> (reduction slice, item); slices slowest, so the
-  // workgroups resident together work on the same slice of K
-  const int Lg = xcd_logical(blockIdx.x, gridDim.x);
-  const int items = NBL * A.W;
-  const int kslice = Lg / items;
-  if (kslice >= A.ksplit) return;
-  if (!gemm_item(offs_s, A.E, kBM, NBL, A.cg, Lg - kslice * items, &e, &mb, &nblock, A.min_rows)) return;
+  if (!gemm_item(offs_s, A.E, kBM, NBL, A.cg, xcd_logical(blockIdx.x, gridDim.x), &e, &mb, &nblock)) return;
   const int tile_base = nblock * kWC * TPW;
   const int row0 = offs_s[e] + mb * kBM;  // first dispatched row
   const int nrows = min(kBM, offs_s[e + 1] - row0);
@@ -172,12 +133,8 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(kOn
   // host).  A fragments past the expert's last row re-read its last
   // fragment; their rows are never stored.
   const int U = A.K / 32;
-  // this slice's 32-k units: whole pairs of units, so every slice has an even
-  // number of steps
-  int p0, p1;
-  unit_range(kslice, A.ksplit, U / 2, &p0, &p1);
-  const char* const abase = reinterpret_cast<const char*>(A.act) + (size_t)(2 * p0) * kFrag;
-  const char* const bbase = static_cast<const char*>(A.w) + (size_t)(2 * p0) * G * kFrag;
+  const char* const abase = reinterpret_cast<const char*>(A.act);
+  const char* const bbase = static_cast<const char*>(A.w);
   uint32_t aoff[kCPW], boff[kCPW];
 #pragma unroll
   for (int j = 0; j < kCPW; ++j) {
@@ -229,8 +186,8 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(kOn
     }                                                                                            \
   }
 
-  const int nsteps = 2 * (p1 - p0);  // even, >= 2 (ksplit <= K/64)
-  if constexpr (kSched == 2) {
+  const int nsteps = U;  // even, >= 2 (K is a multiple of 64)
+  {
     // Ping-pong.  Waves 0-3 (group 0, rows 0-127) and 4-7 (group 1, rows
     // 128-255) put one wave of each group on every SIMD.  Two barriers per
     // step: between B1(s) and B2(s) group 0 multiplies stage s while group 1
@@ -281,124 +238,6 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(kOn
     if (g0) ring_barrier();
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
 #undef MOE_ISSUE_CLAMPED
-  } else if constexpr (kSched == 3) {
-    // One wave per SIMD, so nothing else covers its LDS reads and copies:
-    // they are placed between the products.  A wave enters step s holding
-    // stage s's fragments; after the step's barrier it issues its products
-    // in kMF groups (row fragment i against every column fragment), each
-    // followed by the reads of row fragment i and column fragment i of stage
-    // s+1 into the other register set and one of its kCPS copies of stage
-    // s + kStages into stage s's slot (every wave read stage s before this
-    // barrier).  The copy assembly orders the reads into their group.  Copy
-    // counts, waits and clamping as in schedule 1.
-    static_assert(kMF == kNF && kCPS == kMF, "one read pair and one copy per product group");
-    struct {
-      bf16x8_t a[kMF], b[kNF];
-    } g;
-#define MOE_ISSUE_CLAMPED(step) MOE_ISSUE((step) < nsteps ? (step) : nsteps - 1)
-#define MOE_COPY_ONE(step, jj)                                                                   \
-  do {                                                                                           \
-    const int cs_ = (step) < nsteps ? (step) : nsteps - 1;                                       \
-    const uint32_t st_ = wave_lds + (uint32_t)(cs_ % kStages) * (32 * kFrag);                    \
-    if ((jj) < kCPW)                                                                             \
-      copy_frag(abase + (size_t)cs_ * kFrag, aoff[(jj) % kCPW], st_ + ((jj) % kCPW) * kFrag);    \
-    else                                                                                         \
-      copy_frag(bbase + (size_t)cs_ * G * kFrag, boff[(jj) % kCPW], st_ + (16 + (jj) % kCPW) * kFrag); \
-  } while (0)
-#pragma unroll
-    for (int s = 0; s < kStages; ++s) MOE_ISSUE_CLAMPED(s);
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(kCPS * (kStages - 1)));
-    ring_barrier();
-    MOE_LOAD_B(f, 0);
-    MOE_LOAD_A(f, 0, 0, kMF);
-#define MOE_STEP3(CUR, NXT)                                                                      \
-  do {                                                                                           \
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(kCPS * (kStages - 2)));                                 \
-    ring_barrier();                                                                              \
-    const u32x4_t* nx_ = reinterpret_cast<const u32x4_t*>(ring[(ks + 1) % kStages]);             \
-    _Pragma("unroll") for (int i = 0; i < kMF; ++i) {                                            \
-      if (!SKIP || i < nf_w) {                                                                   \
-        _Pragma("unroll") for (int j = 0; j < kNF; ++j) mfma_acc(acc[i][j], CUR.a[i], CUR.b[j]); \
-      }                                                                                          \
-      NXT.a[i] = as_bf16x8(nx_[(wm * kMF + i) * 64 + lane]);                                     \
-      NXT.b[i] = as_bf16x8(nx_[(16 + wn * kNF + i) * 64 + lane]);                                \
-      MOE_COPY_ONE(ks + kStages, i);                                                             \
-    }                                                                                            \
-    ++ks;                                                                                        \
-  } while (0)
-    for (int ks = 0; ks < nsteps;) {
-      MOE_STEP3(f, g);
-      MOE_STEP3(g, f);
-    }
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-#undef MOE_STEP3
-#undef MOE_COPY_ONE
-#undef MOE_ISSUE_CLAMPED
-  } else if constexpr (kSched == 0) {
-    // Copies run kStages-1 stages ahead.  Step s: wait until this wave's
-    // copies of stage s have landed (copies complete in order, so "at most
-    // n later stages outstanding"), one barrier (every wave's copies of s
-    // are visible; every wave has finished reading stage s-1), refill the
-    // ring slot of stage s-1 with stage s + kStages-1, read stage s (B
-    // fragments first) and multiply it row by row as its A fragments
-    // arrive.  kStages-1 stages of copies stay in flight.  The steady-state
-    // loop has no branch, so nothing makes the compiler drain the counters.
-    const int pre = nsteps < kStages - 1 ? nsteps : kStages - 1;
-    for (int s = 0; s < pre; ++s) MOE_ISSUE(s);
-    int ks = 0;
-    for (; ks + kStages - 1 < nsteps; ++ks) {
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(kCPS * (kStages - 2)));
-      ring_barrier();
-      MOE_ISSUE(ks + kStages - 1);
-      MOE_LOAD_B(f, ks);
-      MOE_LOAD_A(f, ks, 0, kMF);
-      MOE_MMA(f);
-    }
-    for (; ks < nsteps; ++ks) {
-      wait_copies(nsteps - ks - 1);
-      ring_barrier();
-      MOE_LOAD_B(f, ks);
-      MOE_LOAD_A(f, ks, 0, kMF);
-      MOE_MMA(f);
-    }
-  } else {
-    // Double-buffered registers: a wave enters step s holding all of stage
-    // s's fragments (read during step s-1), so its products issue right
-    // after the barrier and the LDS reads of stage s+1 overlap them.  Once
-    // every wave has read stage s into registers its ring slot is free, so
-    // step s refills it with stage s + kStages: kStages-1 stages of copies
-    // stay in flight.  Copies past the last stage re-copy the last stage
-    // into a free slot and the reads of "stage nsteps" read such a slot, so
-    // every step issues and waits for the same counts and the loop has no
-    // branch.  nsteps is even (K is a multiple of 64), so the loop runs in
-    // pairs of steps with the two register sets swapping roles.
-    struct {
-      bf16x8_t a[kMF], b[kNF];
-    } g;
-#define MOE_ISSUE_CLAMPED(step) MOE_ISSUE((step) < nsteps ? (step) : nsteps - 1)
-#pragma unroll
-    for (int s = 0; s < kStages; ++s) MOE_ISSUE_CLAMPED(s);
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(kCPS * (kStages - 1)));
-    ring_barrier();
-    MOE_LOAD_B(f, 0);
-    MOE_LOAD_A(f, 0, 0, kMF);
-#define MOE_STEP_FULL(CUR, NXT)                                                                  \
-  do {                                                                                           \
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(kCPS * (kStages - 2)));                                 \
-    ring_barrier();                                                                              \
-    MOE_ISSUE_CLAMPED(ks + kStages);                                                             \
-    MOE_LOAD_B(NXT, ks + 1);                                                                     \
-    MOE_LOAD_A(NXT, ks + 1, 0, kMF);                                                             \
-    MOE_MMA(CUR);                                                                                \
-    ++ks;                                                                                        \
-  } while (0)
-    for (int ks = 0; ks < nsteps;) {
-      MOE_STEP_FULL(f, g);
-      MOE_STEP_FULL(g, f);
-    }
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-#undef MOE_STEP_FULL
-#undef MOE_ISSUE_CLAMPED
   }
   mfma_fence_out(acc);
 #undef MOE_LOAD_A
@@ -425,9 +264,6 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(kOn
         } else if constexpr (EPI == EPI_UP_RELU) {
           const float gv = acc[i][t][q];
           A.h_out[packed_index(prow0 + row, col, A.N)] = f32_to_bf16(gv > 0.0f ? gv : 0.0f);
-        } else if constexpr (EPI == EPI_DOWN_ACC) {
-          const int a = A.perm[row0 + row];
-          unsafeAtomicAdd(A.f_out + (size_t)(a / A.topk) * A.N + col, A.topk_w[a] * acc[i][t][q]);
         } else {
           A.f_out[(size_t)(row0 + row) * A.N + col] = acc[i][t][q];
         }
@@ -501,14 +337,13 @@ __global__ __launch_bounds__(256) void k_pack_rows(const PackArgs A) {
 }  // namespace
 
 hipError_t launch_ffn_gemm(const GemmArgs& a, int epi, hipStream_t s) {
-  if (a.K % 64 || a.N % 64 || a.K <= 0 || a.N <= 0 || a.min_rows < 1 || a.cg < 1 || a.ksplit < 1 ||
-      a.ksplit > a.K / 64 || (a.ksplit > 1 && epi != EPI_DOWN_ACC))
-    return hipErrorInvalidValue;  // even step count per slice, whole tiles; partial sums only into atomics
+  if (a.K % 64 || a.N % 64 || a.K <= 0 || a.N <= 0 || a.cg < 1 || epi == EPI_DOWN_ACC)
+    return hipErrorInvalidValue;  // an even step count, whole tiles
   const int G = epi == EPI_UP_SWIGLU ? 2 : 1;
   const int tiles_per_block = kWC * (kNF / G);
   const int NB = a.N / 16;
   const long long nbl = (NB + tiles_per_block - 1) / tiles_per_block;
-  const long long work = nbl * a.W * a.ksplit;  // a.W bounds the number of row blocks
+  const long long work = nbl * a.W;  // a.W bounds the number of row blocks
   if (work <= 0) return hipSuccess;  // no expert is served
   const dim3 grid((unsigned)((work + 7) / 8 * 8));
 #define MOE_LAUNCH(SK)                                                                               \
@@ -516,7 +351,6 @@ hipError_t launch_ffn_gemm(const GemmArgs& a, int epi, hipStream_t s) {
     case EPI_UP_SWIGLU: k_ffn_gemm<EPI_UP_SWIGLU, SK><<<grid, kWaves * 64, 0, s>>>(a); break;           \
     case EPI_UP_RELU: k_ffn_gemm<EPI_UP_RELU, SK><<<grid, kWaves * 64, 0, s>>>(a); break;               \
     case EPI_DOWN_ROWS: k_ffn_gemm<EPI_DOWN_ROWS, SK><<<grid, kWaves * 64, 0, s>>>(a); break;           \
-    case EPI_DOWN_ACC: k_ffn_gemm<EPI_DOWN_ACC, SK><<<grid, kWaves * 64, 0, s>>>(a); break;             \
     default: return hipErrorInvalidValue;                                                            \
   }
   if (a.skip_empty) {

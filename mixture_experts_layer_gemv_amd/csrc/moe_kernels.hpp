@@ -148,21 +148,15 @@ struct GemmArgs {
   const uint16_t* act;     // packed bf16 activations [packed rows][K]
   const int32_t* offsets;  // [E+1] dispatch offsets
   uint16_t* h_out;         // packed H [packed rows][N] (up epilogues)
-  float* f_out;            // y_perm [T*k][N] in dispatch order (EPI_DOWN_ROWS) or y_acc [T][N] (EPI_DOWN_ACC)
-  const int32_t* perm;     // [T*k] (EPI_DOWN_ACC)
-  const float* topk_w;     // [T*k] (EPI_DOWN_ACC)
-  int topk;                // (EPI_DOWN_ACC)
+  float* f_out;            // y_perm [T*k][N] in dispatch order (EPI_DOWN_ROWS)
   int cg;                  // column blocks per group of the work order (>= 1)
-  int min_rows;            // experts with fewer rows are skipped (>= 1)
   int skip_empty;          // 1: skip the products of row fragments past the last real row
-  int ksplit;              // reduction slices per item (> 1 only with EPI_DOWN_ACC; <= K/64)
   int K, N, E;
   int W;                   // upper bound on (expert, 256-row block) pairs
 };
 
 // K a multiple of 64, N a multiple of 64, bf16 weights.  epi: EPI_UP_SWIGLU,
-// EPI_UP_RELU, EPI_DOWN_ROWS, or EPI_DOWN_ACC (y_acc[token] += gate weight x
-// row, fp32 atomics).
+// EPI_UP_RELU or EPI_DOWN_ROWS.
 hipError_t launch_ffn_gemm(const GemmArgs& a, int epi, hipStream_t s);
 int gemm_rows_per_block();
 

@@ -31,10 +31,20 @@ __device__ __forceinline__ void ring_barrier() { asm volatile("s_waitcnt lgkmcnt
 
 // global -> LDS copy of one fragment: lane l moves the 16 bytes at
 // sbase + voff (a uniform base and its own 32-bit offset) into LDS byte
-// address lds + 16 l.  m0 carries the LDS address; these kernels use m0 for
-// nothing else (no LDS instruction on gfx950 reads it), so it needs no saving.
+// address lds + 16 l.  The copy takes its LDS address from m0, a register the
+// compiler reserves (and may hold a value of its own in), so m0 is saved in a
+// scratch register first and restored right after the copy is issued (the
+// copy reads m0 at issue).
 __device__ __forceinline__ void copy_frag(const void* sbase, uint32_t voff, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(lds) : "memory");
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "global_load_lds_dwordx4 %1, %2\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voff), "s"(sbase), "s"(lds)
+      : "memory");
 }
 
 // LDS byte address of a __shared__ object.

@@ -9,7 +9,7 @@ import numpy as np
 import torch
 
 from . import (MOE_BF16, MOE_F32, MOE_I4, MOE_I8, MOE_MLP_RELU, MOE_SWIGLU, moe_layer_forward, moe_layer_graph_create,
-               moe_weights_create, moe_weights_destroy, moe_workspace_size)
+               moe_weights_create, moe_weights_destroy, moe_weights_set_tuning, moe_workspace_size)
 
 DTYPE_CODE = {"f32": MOE_F32, "bf16": MOE_BF16, "i8": MOE_I8, "i4": MOE_I4}
 KIND_CODE = {"relu": MOE_MLP_RELU, "swiglu": MOE_SWIGLU}
@@ -24,10 +24,15 @@ def to_device(a, device="cuda"):
     return torch.from_numpy(np.ascontiguousarray(a)).to(device)
 
 
+# Tuning fields (a dict of moe_tuning fields) applied to every MoELayer
+# created while it is set; tests use it to force one launch form.
+default_tuning: dict | None = None
+
+
 class MoELayer:
     """One MoE layer resident on the GPU, built from a synthetic layer dict."""
 
-    def __init__(self, layer: dict, device="cuda", stream=None):
+    def __init__(self, layer: dict, device="cuda", stream=None, tuning: dict | None = None):
         sp = layer["spec"]
         self.spec = sp
         self.device = device
@@ -42,9 +47,19 @@ class MoELayer:
         self.handle = moe_weights_create(self.m, self.p, self.E, KIND_CODE[sp.kind], DTYPE_CODE[sp.w_dtype],
                                          w1, w3, w2, s1, s3, s2, stream=stream)
         del w1, w3, w2, s1, s3, s2
+        tuning = default_tuning if tuning is None else tuning
+        if tuning:
+            moe_weights_set_tuning(self.handle, tuning)
         self._ws = None
         self._ws_T = -1
         self.ensure_workspace(self.T)
+
+    def set_tuning(self, tuning: dict | None):
+        """Attach moe_tuning fields to the handle (None: automatic) and resize the workspace."""
+        moe_weights_set_tuning(self.handle, tuning)
+        T = max(self._ws_T, self.T)
+        self._ws_T = -1
+        self.ensure_workspace(T)
 
     def ensure_workspace(self, T):
         if T > self._ws_T:

@@ -65,6 +65,8 @@ def lib():
         L.orc_forward_tokens.argtypes = [P, vp, i32, vp, vp, vp, i32, i32, vp, i32, vp, vp, vp, vp]
         L.orc_dense_masked.argtypes = [P, vp, i32, vp, vp, i32, i32, vp]
         L.orc_max_threads.argtypes = []
+        L.orc_set_threads.argtypes = [i32]
+        L.orc_set_threads.restype = None
         L.orc_norm.argtypes = [vp, i32, i32, i32, i32, vp, vp, ctypes.c_double, vp]
         L.orc_max_threads.restype = ctypes.c_int
         for f in ("orc_norm", "orc_router_logits", "orc_topk", "orc_dispatch", "orc_expert_apply", "orc_expert_rows",
@@ -77,6 +79,11 @@ def lib():
 def max_threads() -> int:
     """OpenMP threads the oracle's parallel loops use."""
     return int(lib().orc_max_threads())
+
+
+def set_threads(n: int) -> None:
+    """Threads of the oracle's later parallel loops."""
+    lib().orc_set_threads(int(n))
 
 
 def _ptr(a):

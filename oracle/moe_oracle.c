@@ -444,3 +444,12 @@ int orc_max_threads(void) {
   return 1;
 #endif
 }
+
+/* Sets the threads of later parallel loops (n >= 1; ignored without OpenMP). */
+void orc_set_threads(int n) {
+#ifdef _OPENMP
+  if (n >= 1) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}

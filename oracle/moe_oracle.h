@@ -46,5 +46,6 @@ int orc_norm(const void* x, int x_dtype, int T, int m, int kind, const float* ga
              double* out);
 
 int orc_max_threads(void);
+void orc_set_threads(int n);
 
 #endif

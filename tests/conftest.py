@@ -26,3 +26,20 @@ def syn():
 
     synth.lib()
     return synth
+
+
+@pytest.fixture
+def tune():
+    """Force launch choices (moe_tuning fields) on every MoELayer the test
+    creates after the call: tune(ffn_path=2, skinny_mt=4, ...)."""
+    from mixture_experts_layer_gemv_amd import layer as layer_mod
+
+    saved = layer_mod.default_tuning
+    cur = {}
+
+    def set_(**fields):
+        cur.update(fields)
+        layer_mod.default_tuning = dict(cur)
+
+    yield set_
+    layer_mod.default_tuning = saved

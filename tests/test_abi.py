@@ -42,7 +42,7 @@ def test_library_exports_every_declared_symbol(lib):
     L = lib.lib()
     for n in _declared():
         assert hasattr(L, n)
-    assert lib.moe_abi_version() == 1
+    assert lib.moe_abi_version() == 2
 
 
 def test_binding_names_match_header(lib):
@@ -125,3 +125,44 @@ def test_binding_raises_with_message(lib):
     with pytest.raises(lib.MoeError) as ei:
         lib.moe_combine(FAKE, FAKE, FAKE, 4, 96, 2, FAKE, 1, stream=0)
     assert ei.value.status == lib.MOE_ERR_UNSUPPORTED and "multiple of 64" in ei.value.message
+
+
+# the five measured layers and the int4 decode layer: (m, p, E, kind, w_dtype, T, k)
+LAYERS = [(256, 512, 8, 0, 0, 32, 2), (4096, 14336, 8, 1, 1, 16, 2), (4096, 6400, 16, 1, 1, 256, 2),
+          (4096, 14336, 8, 1, 1, 8192, 2), (4096, 14336, 8, 1, 2, 64, 2), (4096, 14336, 8, 1, 3, 64, 2)]
+# knobs that once tuned the launch plan through the environment
+STALE_ENV = {"MOE_FFN_PATH": "s", "MOE_SKINNY_MT": "1", "MOE_SKINNY_PACK": "0", "MOE_SKINNY_WAVES": "k",
+             "MOE_DOWN_KSPLIT": "4", "MOE_DOWN_ROWS": "0", "MOE_HOT_ROWS": "3", "MOE_GEMM_CG": "2"}
+
+
+def test_workspace_size_ignores_the_environment(lib, monkeypatch):
+    """The workspace (and the launch plan it is carved for) is a function of
+    the layer, its tuning, T and k only."""
+    before = [lib.moe_workspace_size_for(*L[:5], None, *L[5:]) for L in LAYERS]
+    for k, v in STALE_ENV.items():
+        monkeypatch.setenv(k, v)
+    after = [lib.moe_workspace_size_for(*L[:5], None, *L[5:]) for L in LAYERS]
+    assert before == after
+    assert all(b > 0 for b in before)
+    # an explicit tuning does change the plan: the prefill layer on the
+    # decode kernels with gathered (unpacked) rows
+    t = lib.tuning(ffn_path=lib.MOE_PATH_SKINNY, skinny_mt=1)
+    assert lib.moe_workspace_size_for(*LAYERS[3][:5], t, *LAYERS[3][5:]) != before[3]
+
+
+def test_tuning_validation(lib):
+    L = lib.lib()
+    n = ctypes.c_size_t()
+    for bad in [dict(ffn_path=3), dict(skinny_mt=3), dict(up_ct=8), dict(skinny_pack=2), dict(down_rows=-2),
+                dict(down_ksplit=-1), dict(gemm_cg=-4), dict(gemm_skip=5)]:
+        t = lib.tuning(**bad)
+        rc = L.moe_workspace_size_for(4096, 14336, 8, 1, 1, ctypes.byref(t), 16, 2, ctypes.byref(n))
+        assert rc == lib.MOE_ERR_INVALID_ARG, (bad, rc)
+    assert L.moe_weights_set_tuning(None, None) == lib.MOE_ERR_INVALID_ARG
+    assert L.moe_weights_get_tuning(None, None) == lib.MOE_ERR_INVALID_ARG
+    # shape errors of the host-only sizing
+    assert L.moe_workspace_size_for(100, 64, 8, 1, 1, None, 4, 2, ctypes.byref(n)) == lib.MOE_ERR_UNSUPPORTED
+    assert L.moe_workspace_size_for(128, 192, 8, 1, 3, None, 4, 2, ctypes.byref(n)) == lib.MOE_ERR_UNSUPPORTED
+    assert L.moe_workspace_size_for(64, 64, 8, 1, 1, None, 4, 9, ctypes.byref(n)) == lib.MOE_ERR_INVALID_ARG
+    assert L.moe_workspace_size_for(64, 64, 8, 1, 1, None, 4, 2, None) == lib.MOE_ERR_INVALID_ARG
+    assert lib.moe_workspace_size_for(64, 64, 8, 1, 1, None, 0, 2) > 0

@@ -32,14 +32,13 @@ def _gpu():
     torch.cuda.synchronize()
 
 
-# name, (T, m, p, E, k, kind, w_dtype, zipf), MOE_FFN_PATH
+# name, (T, m, p, E, k, kind, w_dtype, zipf), forced path ("g": grouped GEMM)
 PATHS = [
     ("decode_bf16", (16, 512, 1024, 8, 2, "swiglu", "bf16", None), ""),
     ("decode_int8", (64, 512, 1024, 8, 2, "swiglu", "i8", None), ""),
     ("skewed_split", (256, 256, 640, 16, 2, "swiglu", "bf16", 1.2), ""),
     ("relu_e12", (40, 256, 512, 12, 3, "relu", "bf16", None), ""),  # E=12: the unfused norm kernel
     ("prefill_gemm", (2048, 512, 768, 8, 2, "swiglu", "bf16", None), "g"),
-    ("hybrid", (512, 256, 512, 8, 2, "swiglu", "bf16", 1.2), "h"),
     ("tiny_f32", (32, 256, 512, 8, 2, "relu", "f32", None), ""),
 ]
 FUSIONS = [("layer", True), ("rms", False), ("none", True)]
@@ -53,9 +52,9 @@ def _x64(a):
 
 @pytest.mark.parametrize("norm,with_res", FUSIONS, ids=[f"{n}{'_res' if r else ''}" for n, r in FUSIONS])
 @pytest.mark.parametrize("name,shape,path", PATHS, ids=[c[0] for c in PATHS])
-def test_fused_forward(name, shape, path, norm, with_res, monkeypatch):
+def test_fused_forward(name, shape, path, norm, with_res, tune):
     if path:
-        monkeypatch.setenv("MOE_FFN_PATH", path)
+        tune(ffn_path=M.MOE_PATH_GEMM)
     T, m, p, E, k, kind, wd, zipf = shape
     log(f"fused {name} norm={norm} residual={with_res}: T={T} m={m} p={p} E={E} k={k} {kind} {wd}")
     L = synth.make_layer(spec(T, m, p, E, k, kind, wd, seed=T + 7 * m, zipf=zipf))

@@ -1,7 +1,7 @@
 """Parity of the prefill grouped GEMM (MFMA) expert FFN with the CPU oracle.
 
 The layer picks the grouped GEMM for bf16 weights once the experts average
-128 rows or more; here it is forced (MOE_FFN_PATH=gemm) on small shapes so the
+128 rows or more; here it is forced (moe_tuning.ffn_path = MOE_PATH_GEMM) on small shapes so the
 oracle finishes in seconds.  The shapes cover reductions of fewer than three
 32-k steps (the unpipelined loop) and of many, column counts that leave the
 last 256-column block partial, experts with several 256-row blocks, a ragged
@@ -32,8 +32,8 @@ def _gpu():
 
 
 @pytest.fixture(autouse=True)
-def _force_gemm(monkeypatch):
-    monkeypatch.setenv("MOE_FFN_PATH", "gemm")
+def _force_gemm(tune):
+    tune(ffn_path=M.MOE_PATH_GEMM)
 
 
 SHAPES = [

@@ -74,11 +74,9 @@ def test_int4_expert_stage_and_layer(kind, T, m, p, E, k):
 @pytest.mark.parametrize("mt", [1, 2])
 @pytest.mark.parametrize("pack", [0, 1])
 @pytest.mark.parametrize("waves", ["k", "n"])
-def test_int4_launch_modes(mt, pack, waves, monkeypatch):
-    monkeypatch.setenv("MOE_FFN_PATH", "s")
-    monkeypatch.setenv("MOE_SKINNY_MT", str(mt))
-    monkeypatch.setenv("MOE_SKINNY_PACK", str(pack))
-    monkeypatch.setenv("MOE_SKINNY_WAVES", waves)
+def test_int4_launch_modes(mt, pack, waves, tune):
+    tune(ffn_path=M.MOE_PATH_SKINNY, skinny_mt=mt, skinny_pack=1 if pack else -1,
+         skinny_splitk=1 if waves == "k" else -1)
     log(f"int4 modes mt={mt} pack={pack} waves={waves}")
     _layer_check(synth.make_layer(spec(61, 256, 384, 8, 2, "swiglu", "i4", seed=mt + 2 * pack, zipf=1.2, sw=0.05,
                                        sr=0.05)))
@@ -92,5 +90,14 @@ def test_int4_needs_multiples_of_128():
 
 
 def test_int4_decode_layer_full_size():
-    log("int4 decode layer, full size (sampled tokens)")
-    _layer_check(synth.make_layer(synth.spec("c6")), sample=12)
+    log("int4 decode layer, full size, every token")
+    _layer_check(synth.make_layer(synth.spec("c6")))
+
+
+def test_int4_relu_layer_long_reduction():
+    """ReLU experts at the Mixtral shape: the down projection reduces over
+    p = 14336 nonnegative activations, where removing the int4 storage offset
+    (136 * sum x, subtracted after the fp32 accumulation) cancels the most;
+    every token is checked at the bf16 bar."""
+    log("int4 ReLU layer, m=4096 p=14336, every token")
+    _layer_check(synth.make_layer(spec(64, 4096, 14336, 8, 2, "relu", "i4", seed=6)))

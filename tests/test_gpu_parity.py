@@ -269,11 +269,11 @@ def test_layer_workspace_too_small():
 
 
 @pytest.mark.parametrize("ksplit", ["1", "4"])
-def test_layer_repeat_is_deterministic(ksplit, monkeypatch):
+def test_layer_repeat_is_deterministic(ksplit, tune):
     """Routing repeats bit for bit.  Without a split reduction the top-2
     combine adds two terms onto zero, so the output repeats bit for bit too;
     with one, only the order of fp32 atomic adds may differ."""
-    monkeypatch.setenv("MOE_DOWN_KSPLIT", ksplit)
+    tune(down_ksplit=int(ksplit))
     L = synth.make_layer(spec(64, 512, 256, 8, 2, seed=9))
     layer = MoELayer(L)
     d1, d2 = layer.debug_buffers(), layer.debug_buffers()

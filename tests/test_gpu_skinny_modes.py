@@ -6,11 +6,11 @@ fragments (x packed by k_pack_rows, H written packed by the up projection),
 and split a work item over their four waves either along the reduction
 (partials summed through LDS) or along the columns.  The library picks these
 from the mean rows per expert; here every combination is forced
-(MOE_SKINNY_MT, MOE_SKINNY_PACK, MOE_SKINNY_WAVES) on bf16 and int8 layers
+(moe_tuning's skinny_mt, skinny_pack, skinny_splitk) on bf16 and int8 layers
 with ragged experts, for the layer and the expert-FFN stage, at the bars of
 the other parity tests; so are the activation sharing through LDS
-(MOE_SKINNY_SA), the down projection's epilogue (unweighted rows and the
-combine kernel, or weighted atomics: MOE_DOWN_ROWS) and its reduction slices.
+(skinny_shared), the down projection's epilogue (unweighted rows and the
+combine kernel, or weighted atomics: down_rows) and its reduction slices.
 """
 import numpy as np
 import pytest
@@ -40,11 +40,9 @@ def _gpu():
 @pytest.mark.parametrize("pack", [0, 1])
 @pytest.mark.parametrize("waves", ["k", "n"])
 @pytest.mark.parametrize("T,m,p,E,k,zipf", [(61, 256, 320, 8, 2, 1.2), (100, 192, 256, 4, 1, None)])
-def test_skinny_mode_layer(w_dtype, mt, pack, waves, T, m, p, E, k, zipf, monkeypatch):
-    monkeypatch.setenv("MOE_FFN_PATH", "s")
-    monkeypatch.setenv("MOE_SKINNY_MT", str(mt))
-    monkeypatch.setenv("MOE_SKINNY_PACK", str(pack))
-    monkeypatch.setenv("MOE_SKINNY_WAVES", waves)
+def test_skinny_mode_layer(w_dtype, mt, pack, waves, T, m, p, E, k, zipf, tune):
+    tune(ffn_path=M.MOE_PATH_SKINNY, skinny_mt=mt, skinny_pack=1 if pack else -1,
+         skinny_splitk=1 if waves == "k" else -1)
     log(f"skinny layer w={w_dtype} mt={mt} pack={pack} waves={waves} T={T} m={m} p={p} E={E} k={k}")
     L = synth.make_layer(spec(T, m, p, E, k, "swiglu", w_dtype, seed=T + mt + 7 * pack, zipf=zipf, sw=0.05,
                               sr=0.05))
@@ -64,11 +62,8 @@ def test_skinny_mode_layer(w_dtype, mt, pack, waves, T, m, p, E, k, zipf, monkey
 @pytest.mark.parametrize("kind", ["swiglu", "relu"])
 @pytest.mark.parametrize("mt", [2, 4])
 @pytest.mark.parametrize("waves", ["k", "n"])
-def test_skinny_packed_expert_ffn_stage(kind, mt, waves, monkeypatch):
-    monkeypatch.setenv("MOE_FFN_PATH", "s")
-    monkeypatch.setenv("MOE_SKINNY_MT", str(mt))
-    monkeypatch.setenv("MOE_SKINNY_PACK", "1")
-    monkeypatch.setenv("MOE_SKINNY_WAVES", waves)
+def test_skinny_packed_expert_ffn_stage(kind, mt, waves, tune):
+    tune(ffn_path=M.MOE_PATH_SKINNY, skinny_mt=mt, skinny_pack=1, skinny_splitk=1 if waves == "k" else -1)
     T, m, p, E, k = 90, 128, 384, 6, 2
     L = synth.make_layer(spec(T, m, p, E, k, kind, "bf16", seed=31 + mt, sw=0.05))
     layer = MoELayer(L)
@@ -92,19 +87,14 @@ def test_skinny_packed_expert_ffn_stage(kind, mt, waves, monkeypatch):
 @pytest.mark.parametrize("rows", ["0", "1"])
 @pytest.mark.parametrize("sa", ["0", "1"])
 @pytest.mark.parametrize("ks", ["1", "2"])
-def test_skinny_epilogue_and_sharing(w_dtype, rows, sa, ks, monkeypatch):
+def test_skinny_epilogue_and_sharing(w_dtype, rows, sa, ks, tune):
     """Packed rows with the columns split over the waves: activations copied
     once per workgroup into LDS (sa=1) or loaded by every wave (sa=0); the down
     projection's unweighted rows summed by the combine kernel (rows=1, per
     reduction slice) or weighted rows added with atomics (rows=0); one or two
     reduction slices."""
-    monkeypatch.setenv("MOE_FFN_PATH", "s")
-    monkeypatch.setenv("MOE_SKINNY_MT", "2")
-    monkeypatch.setenv("MOE_SKINNY_PACK", "1")
-    monkeypatch.setenv("MOE_SKINNY_WAVES", "n")
-    monkeypatch.setenv("MOE_SKINNY_SA", sa)
-    monkeypatch.setenv("MOE_DOWN_ROWS", rows)
-    monkeypatch.setenv("MOE_DOWN_KSPLIT", ks)
+    tune(ffn_path=M.MOE_PATH_SKINNY, skinny_mt=2, skinny_pack=1, skinny_splitk=-1,
+         skinny_shared=1 if sa == "1" else -1, down_rows=1 if rows == "1" else -1, down_ksplit=int(ks))
     T, m, p, E, k = 70, 256, 384, 8, 2
     log(f"skinny epilogue w={w_dtype} rows={rows} sa={sa} ks={ks}")
     L = synth.make_layer(spec(T, m, p, E, k, "swiglu", w_dtype, seed=17 + 3 * int(ks), zipf=1.2, sw=0.05,
@@ -122,11 +112,10 @@ def test_skinny_epilogue_and_sharing(w_dtype, rows, sa, ks, monkeypatch):
 
 
 @pytest.mark.parametrize("w_dtype", ["bf16", "i8"])
-def test_skinny_rows_repeat_is_bitwise(w_dtype, monkeypatch):
+def test_skinny_rows_repeat_is_bitwise(w_dtype, tune):
     """With unweighted rows and the combine kernel the layer has no atomics:
     two calls, with two reduction slices, give identical bits."""
-    monkeypatch.setenv("MOE_FFN_PATH", "s")
-    monkeypatch.setenv("MOE_DOWN_KSPLIT", "2")
+    tune(ffn_path=M.MOE_PATH_SKINNY, down_ksplit=2)
     L = synth.make_layer(spec(200, 256, 384, 8, 2, "swiglu", w_dtype, seed=23, zipf=1.2, sw=0.05))
     layer = MoELayer(L)
     y1 = layer.forward().clone()

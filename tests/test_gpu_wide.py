@@ -3,7 +3,8 @@
 With four M tiles and packed, shared activations, experts holding more than
 one 64-row chunk are served by twelve-tile work items (192-row chunks) in the
 same launch as the four-tile items of the others: for both projections by
-default; MOE_SKINNY_WIDE_DOWN=0 keeps the down projection on four-tile items.
+default; moe_tuning.skinny_wide_down = -1 keeps the down projection on
+four-tile items.
 The cases force hot experts of every size class: 65..192 rows (one wide
 chunk, ragged), several
 wide chunks (over 192 rows), a mix of hot and cold experts, and none hot;
@@ -34,10 +35,8 @@ def _gpu():
 
 
 @pytest.fixture(autouse=True)
-def _split(monkeypatch):
-    monkeypatch.setenv("MOE_FFN_PATH", "s")
-    monkeypatch.setenv("MOE_SKINNY_MT", "4")
-    monkeypatch.setenv("MOE_SKINNY_PACK", "1")
+def _split(tune):
+    tune(ffn_path=M.MOE_PATH_SKINNY, skinny_mt=4, skinny_pack=1)
 
 
 # T, m, p, E, k, bias on the hot experts (None: routing as generated)
@@ -63,9 +62,9 @@ def _layer(T, m, p, E, k, bias, kind, seed):
 @pytest.mark.parametrize("down", ["0", "1"])
 @pytest.mark.parametrize("kind", ["swiglu", "relu"])
 @pytest.mark.parametrize("T,m,p,E,k,bias", CASES)
-def test_wide_layer(kind, T, m, p, E, k, bias, down, monkeypatch):
+def test_wide_layer(kind, T, m, p, E, k, bias, down, tune):
     """down=0 keeps the down projection on four-tile items."""
-    monkeypatch.setenv("MOE_SKINNY_WIDE_DOWN", down)
+    tune(skinny_wide_down=1 if down == "1" else -1)
     log(f"wide layer kind={kind} down={down} T={T} m={m} p={p} E={E} k={k} bias={bias}")
     L = _layer(T, m, p, E, k, bias, kind, seed=T + p)
     layer = MoELayer(L)
@@ -84,9 +83,9 @@ def test_wide_layer(kind, T, m, p, E, k, bias, down, monkeypatch):
 @pytest.mark.parametrize("down", ["0", "1"])
 @pytest.mark.parametrize("kind", ["swiglu", "relu"])
 @pytest.mark.parametrize("hot", [100, 300])
-def test_wide_expert_ffn_stage(kind, hot, down, monkeypatch):
+def test_wide_expert_ffn_stage(kind, hot, down, tune):
     """Expert 2 holds `hot` rows (one or two wide chunks); rows are unweighted."""
-    monkeypatch.setenv("MOE_SKINNY_WIDE_DOWN", down)
+    tune(skinny_wide_down=1 if down == "1" else -1)
     T, m, p, E, k = 320, 128, 384, 6, 2
     L = synth.make_layer(spec(T, m, p, E, k, kind, "bf16", seed=hot, sw=0.05))
     layer = MoELayer(L)
@@ -106,13 +105,13 @@ def test_wide_expert_ffn_stage(kind, hot, down, monkeypatch):
     layer.close()
 
 
-def test_wide_matches_narrow(monkeypatch):
+def test_wide_matches_narrow():
     """The split launch and the four-tile kernel alone agree to fp32 rounding
     (the two group a row's products into different accumulation orders)."""
     L = _layer(300, 128, 384, 6, 2, {0: 50.0, 3: 0.5}, "swiglu", seed=5)
     layer = MoELayer(L)
     y_split = layer.forward().float().clone()
-    monkeypatch.setenv("MOE_SKINNY_WIDE", "0")
+    layer.set_tuning(dict(ffn_path=M.MOE_PATH_SKINNY, skinny_mt=4, skinny_pack=1, skinny_wide=-1))
     y_narrow = layer.forward().float()
     torch.cuda.synchronize()
     err = (y_split - y_narrow).abs().max().item()
