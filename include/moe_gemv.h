@@ -297,6 +297,25 @@ moe_status moe_graph_launch(const moe_graph* g, void* stream);
 moe_status moe_graph_destroy(moe_graph* g);
 
 /*
+ * moe_layer_forward_noalloc -- moe_layer_forward for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  It allocates nothing: its workspace is a
+ * static device array of MOE_NOALLOC_SCRATCH_BYTES that the library holds on
+ * every GPU it runs on until the process ends.  Arguments, results and
+ * errors as moe_layer_forward without the workspace and dbg outputs, plus
+ * UNSUPPORTED when T tokens need more workspace than the array holds (the
+ * Mixtral-shaped decode layers fit up to a few hundred tokens; prefill
+ * batches need moe_layer_forward).  Every call on one GPU uses that GPU's one
+ * array: calls that overlap on a GPU (on different streams, or threads)
+ * race, so the caller serialises them.  Nothing in the array needs clearing
+ * between calls.
+ */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+moe_status moe_layer_forward_noalloc(const moe_weights* w, const float* w_router, const float* b_router,
+                                     const void* x, int x_dtype, int T, int m, int p, int E, int k, void* y,
+                                     int y_dtype, void* stream);
+
+/*
  * Measurement aid (not part of the layer).  Between moe_profile_begin and
  * moe_profile_end every kernel the library launches is bracketed by HIP
  * events on its own stream.  moe_profile_end waits for the last event and

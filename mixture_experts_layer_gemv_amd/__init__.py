@@ -23,6 +23,7 @@ MOE_ROUTE_LOGITS_IN = 1
 MOE_NORM_NONE, MOE_NORM_LAYER, MOE_NORM_RMS = 0, 1, 2
 MOE_MAX_EXPERTS = 64
 MOE_PATH_AUTO, MOE_PATH_SKINNY, MOE_PATH_GEMM = 0, 1, 2
+MOE_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 STATUS_NAMES = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARG", 2: "MOE_ERR_UNSUPPORTED", 3: "MOE_ERR_WORKSPACE",
                 4: "MOE_ERR_HIP", 5: "MOE_ERR_OOM"}
@@ -77,6 +78,7 @@ _SIGS = {
     "moe_layer_graph_create": ([_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _i32, _vp, _sz,
                                 ctypes.POINTER(_vp)], _i32),
     "moe_graph_launch": ([_vp, _vp], _i32),
+    "moe_layer_forward_noalloc": ([_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _i32, _vp], _i32),
     "moe_graph_destroy": ([_vp], _i32),
     "moe_profile_begin": ([_i32], _i32),
     "moe_profile_end": ([], _i32),
@@ -215,6 +217,11 @@ def moe_layer_graph_create(w, w_router, b_router, x, x_dtype, T, m, p, E, k, y, 
         w, _p(w_router), _p(b_router), _p(x), x_dtype, T, m, p, E, k, _p(y), y_dtype, _p(workspace), ws_bytes,
         ctypes.byref(g)))
     return g.value
+
+
+def moe_layer_forward_noalloc(w, w_router, b_router, x, x_dtype, T, m, p, E, k, y, y_dtype, stream=None):
+    _check("moe_layer_forward_noalloc", lib().moe_layer_forward_noalloc(
+        w, _p(w_router), _p(b_router), _p(x), x_dtype, T, m, p, E, k, _p(y), y_dtype, _s(stream)))
 
 
 def moe_graph_launch(g, stream=None):

@@ -954,6 +954,69 @@ moe_status moe_layer_forward_fused(const moe_weights* w, const float* w_router, 
 
 }  // extern "C"
 
+// ---- the allocation-free forward ----------------------------------------------
+//
+// Callers that cannot allocate device memory (code under graph capture, tight
+// serving loops, harnesses that forbid it) get a forward whose workspace is
+// this file-scope device array: each GPU the library runs on holds its own
+// copy until the process ends.  In host code `scratch` names a host-side
+// stand-in, never the device memory; the device address comes from
+// hipGetSymbolAddress, once per device with that device current, and only
+// that address is passed to kernels.
+namespace {
+
+constexpr size_t kScratchBytes = MOE_NOALLOC_SCRATCH_BYTES;
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+std::mutex g_scratch_mu;
+std::map<int, void*> g_scratch_ptr;  // device -> address of its scratch
+
+// The current device's scratch address, looked up on its first use.
+moe_status scratch_address(void** out) {
+  int dev = 0;
+  MOE_TRY_HIP(hipGetDevice(&dev));
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  auto it = g_scratch_ptr.find(dev);
+  if (it != g_scratch_ptr.end()) {
+    *out = it->second;
+    return MOE_OK;
+  }
+  void* ptr = nullptr;
+  MOE_TRY_HIP(hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)));
+  if (!ptr || (reinterpret_cast<uintptr_t>(ptr) & 255u))
+    return fail(MOE_ERR_HIP, "scratch array of device %d has no usable address", dev);
+  g_scratch_ptr[dev] = ptr;
+  *out = ptr;
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_layer_forward_noalloc(const moe_weights* w, const float* w_router, const float* b_router,
+                                     const void* x, int x_dtype, int T, int m, int p, int E, int k, void* y,
+                                     int y_dtype, void* stream) {
+  if (moe_status rc = check_forward(w, w_router, x, x_dtype, T, m, p, E, k, y, y_dtype)) return rc;
+  if (T == 0) return ok();
+  const Ws L = ws_layout(w->c, T, k);
+  if (L.total > kScratchBytes)
+    return fail(MOE_ERR_UNSUPPORTED, "T=%d needs %zu bytes of workspace, above the %zu-byte scratch of the "
+                "allocation-free forward (use moe_layer_forward with a workspace)", T, L.total, kScratchBytes);
+  void* ws = nullptr;
+  if (moe_status rc = scratch_address(&ws)) return rc;
+  // Every kernel writes each workspace region before reading it (the routing
+  // pass zeroes the accumulator where one is used), so no region needs
+  // clearing from the host.
+  if (moe_status rc = enqueue_forward(w, w_router, b_router, x, x_dtype, T, k, y, y_dtype, static_cast<char*>(ws), L,
+                                      nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, as_stream(stream),
+                                      Fusion{}))
+    return rc;
+  return ok();
+}
+
+}  // extern "C"
+
 struct moe_graph {
   hipGraph_t graph;
   hipGraphExec_t exec;  // null for a forward with no launches (T = 0)
