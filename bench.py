@@ -12,7 +12,8 @@ one JSON line for it, with the roofline position of its dominant kernel
 (timed with HIP events around its launches on the launch stream) and the CPU
 oracle timed on a bounded sample of the same layer.  Beside it, under
 "configs", the same figures for the other measured layers (tiny fp32,
-Mixtral decode, Phi-3.5 skewed, Mixtral int8 decode, Mixtral int4 decode).
+Mixtral decode, Phi-3.5 skewed, Mixtral int8 and int4 decode, Mixtral int8
+and int4 prefill).
 
   python bench.py [--steps K] [--warmup W]            headline + every layer
   python bench.py --workload c2 [--steps K]           one layer only
@@ -35,12 +36,13 @@ HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
 METRIC = "MoE layer tokens/s; achieved HBM GB/s (T≤64) or MFMA TFLOP/s (T≥4096)"
 HEADLINE = "c4"
-OTHERS = ["c1", "c2", "c3", "c5", "c6"]
+OTHERS = ["c1", "c2", "c3", "c5", "c6", "c7", "c8"]
 TRAFFIC_DIR = os.path.join(ROOT, "profiles")
 _CSRC = "mixture_experts_layer_gemv_amd/csrc/"
 _SKINNY = [_CSRC + f for f in
-           ("moe_ffn_skinny.hip", "moe_index.hpp", "moe_dispatch_block.hpp", "moe_kernels.hpp", "moe_lds.hpp")]
-_GEMM = [_CSRC + f for f in ("moe_ffn_gemm.hip", "moe_index.hpp", "moe_kernels.hpp", "moe_lds.hpp")]
+           ("moe_ffn_skinny.hip", "moe_index.hpp", "moe_dispatch_block.hpp", "moe_kernels.hpp", "moe_lds.hpp",
+            "moe_convert.hpp")]
+_GEMM = [_CSRC + f for f in ("moe_ffn_gemm.hip", "moe_index.hpp", "moe_kernels.hpp", "moe_lds.hpp", "moe_convert.hpp")]
 _F32 = [_CSRC + f for f in ("moe_misc.hip", "moe_index.hpp", "moe_kernels.hpp")]
 KERNEL_SOURCES = {"ffn_up": _SKINNY, "ffn_down": _SKINNY, "gemm_up": _GEMM, "gemm_down": _GEMM,
                   "ffn_f32_up": _F32, "ffn_f32_down": _F32}
@@ -54,7 +56,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=None,
-                    help="time only this layer (c1..c6); default: the prefill layer with every other layer beside it")
+                    help="time only this layer (c1..c8); default: the prefill layer with every other layer beside it")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calib-mib", type=int, default=0,

@@ -149,7 +149,7 @@ moe_status check_combo(int x_dtype, int w_dtype) {
 
 // Which kernels serve the expert FFN.
 //  - GEMM: layers whose experts average at least kGemmMinRows rows run the
-//    grouped MFMA GEMM on every expert.
+//    grouped MFMA GEMM on every expert (bf16, int8 or int4 weights).
 //  - SKINNY: decode-sized layers.
 //  - F32: fp32 layers.
 // (A hybrid of the two, hot experts on the GEMM on a second stream and the
@@ -165,7 +165,7 @@ bool tuned_on(int v, bool dflt) { return v == 0 ? dflt : v > 0; }
 // The GEMM addresses packed activations and one projection's packed weights
 // with 32-bit byte offsets from a uniform base.
 bool gemm_fits(const LayerCfg& c, int T, int k) {
-  if (c.w_dtype != MOE_BF16) return false;
+  if (c.w_dtype == MOE_F32) return false;
   const unsigned long long lim = 1ull << 32;
   const int qb = weight_bits(c);
   const unsigned long long G = c.kind == MOE_SWIGLU ? 2 : 1;
@@ -390,31 +390,37 @@ moe_status run_pack(const LayerCfg& c, const FfnIo& io, hipStream_t s) {
 moe_status run_gemm(const moe_weights* W, const FfnIo& io, float* y_rows, hipStream_t s) {
   const LayerCfg& c = W->c;
   const long long n = (long long)io.T * io.k;
+  const int qb = weight_bits(c);
+  const int bm = moe::gemm_rows_per_block(qb);
   moe::GemmArgs g{};
   g.offsets = io.offsets;
   g.E = c.E;
-  // row blocks: at most n/256 full ones plus one partial per expert
-  g.W = (int)(n / moe::gemm_rows_per_block() + std::min<long long>(c.E, n));
+  // row blocks: at most n/bm full ones plus one partial per expert
+  g.W = (int)(n / bm + std::min<long long>(c.E, n));
   g.cg = tuned(c.tune.gemm_cg, 4);
   // experts averaging under one full row block: skip the products of empty
   // row fragments
-  g.skip_empty = tuned_on(c.tune.gemm_skip, n < (long long)moe::gemm_rows_per_block() * c.E);
+  g.skip_empty = tuned_on(c.tune.gemm_skip, n < (long long)bm * c.E);
   // up: packed x -> packed H
   g.w = W->up;
+  g.scale0 = W->s_gate;
+  g.scale1 = W->s_up;
   g.act = static_cast<const uint16_t*>(io.xp);
   g.h_out = static_cast<uint16_t*>(io.h);
   g.K = c.m;
   g.N = c.p;
   const int up_epi = c.kind == MOE_SWIGLU ? moe::EPI_UP_SWIGLU : moe::EPI_UP_RELU;
-  MOE_TRY_HIP(run("gemm_up", s, [&] { return moe::launch_ffn_gemm(g, up_epi, s); }));
+  MOE_TRY_HIP(run("gemm_up", s, [&] { return moe::launch_ffn_gemm(g, up_epi, qb, s); }));
   // down: packed H -> rows in dispatch order
   g.w = W->down;
+  g.scale0 = W->s_down;
+  g.scale1 = nullptr;
   g.act = static_cast<const uint16_t*>(io.h);
   g.h_out = nullptr;
   g.f_out = y_rows;
   g.K = c.p;
   g.N = c.m;
-  MOE_TRY_HIP(run("gemm_down", s, [&] { return moe::launch_ffn_gemm(g, moe::EPI_DOWN_ROWS, s); }));
+  MOE_TRY_HIP(run("gemm_down", s, [&] { return moe::launch_ffn_gemm(g, moe::EPI_DOWN_ROWS, qb, s); }));
   return MOE_OK;
 }
 

@@ -1,0 +1,58 @@
+// Exact conversions of packed integer weights to bf16 MFMA operands, shared
+// by the decode kernels and the grouped GEMM.  The integer kinds keep their
+// per-output-channel scale for the epilogue, so a weight enters the product
+// as its integer value (int8) or as that value plus a constant (int4, see
+// below), both exact in bf16.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "moe_kernels.hpp"
+
+namespace moe {
+
+typedef uint32_t cvt_u32x4_t __attribute__((ext_vector_type(4)));
+
+// 8 signed bytes (two dwords) -> 8 bf16.  |q| <= 128 is exact in bf16, so the
+// fp32 value's upper half is the bf16 pattern.
+__device__ __forceinline__ bf16x8_t i8x8_to_bf16(uint32_t lo, uint32_t hi) {
+  cvt_u32x4_t r;
+  const uint32_t d[2] = {lo, hi};
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const float f0 = (float)(signed char)(d[q]);
+    const float f1 = (float)(signed char)(d[q] >> 8);
+    const float f2 = (float)(signed char)(d[q] >> 16);
+    const float f3 = (float)(signed char)(d[q] >> 24);
+    r[2 * q] = __builtin_amdgcn_perm(__float_as_uint(f1), __float_as_uint(f0), 0x07060302u);
+    r[2 * q + 1] = __builtin_amdgcn_perm(__float_as_uint(f3), __float_as_uint(f2), 0x07060302u);
+  }
+  return __builtin_bit_cast(bf16x8_t, r);
+}
+
+// 8 int4 weights stored offset by 8 (u = q + 8; values 0-3 in the low
+// nibbles of bytes 0-3, values 4-7 in the high nibbles) -> the 8 bf16 values
+// 128 + u, exactly: the bf16 pattern of 128 (0x4300) leaves the value's
+// integer part to its 7 mantissa bits, so each value is its nibble as the low
+// byte under a high byte of 0x43.  After masking, one byte permute per pair
+// takes two nibble bytes and two 0x43 bytes; the products' constant part
+// 136 * sum(x) is removed after the reduction.
+__device__ __forceinline__ bf16x8_t u4x8_to_bf16_biased(uint32_t d) {
+  const uint32_t t0 = d & 0x0F0F0F0Fu, t1 = (d >> 4) & 0x0F0F0F0Fu;
+  const uint32_t hi = 0x43434343u;  // (selector bytes 4-7)
+  cvt_u32x4_t r;
+  r[0] = __builtin_amdgcn_perm(hi, t0, 0x04010400u);  // values 0, 1
+  r[1] = __builtin_amdgcn_perm(hi, t0, 0x04030402u);  // values 2, 3
+  r[2] = __builtin_amdgcn_perm(hi, t1, 0x04010400u);  // values 4, 5
+  r[3] = __builtin_amdgcn_perm(hi, t1, 0x04030402u);  // values 6, 7
+  return __builtin_bit_cast(bf16x8_t, r);
+}
+constexpr float kI4Bias = 136.0f;  // 128 from the bf16 pattern + 8 from the storage offset
+
+
+// Weight bits of a kernel variant: 0 (bf16), 8 (int8) or 4 (int4).  A
+// lane's 16-byte load of packed weights covers q_ah(qb) MFMA K steps of 32.
+constexpr int q_ah(int qb) { return qb == 8 ? 2 : (qb == 4 ? 4 : 1); }
+
+}  // namespace moe

@@ -33,6 +33,7 @@
 // the matrix cores about half the time: the global -> LDS copies alone take
 // three quarters of its time, and with copies, LDS reads and products all
 // running the clock drops from ~2.4 to ~2.0 GHz.
+#include "moe_convert.hpp"
 #include "moe_dispatch_block.hpp"
 #include "moe_index.hpp"
 #include "moe_lds.hpp"
@@ -46,24 +47,47 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v); }
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
 
-constexpr int kBM = 256;     // rows per workgroup
+// Tile shape of one weight kind.  A stage holds one 16-byte weight unit of
+// K (32 k for bf16, 64 for int8, 128 for int4: the packed weight layout's
+// unit) for the workgroup's 256 weight columns, and the matching activation
+// fragments of its BM rows.  int4 takes 128-row blocks so that a stage stays
+// at 48 KiB (three fit the LDS): its weights are a quarter of bf16's bytes,
+// so the halved weight reuse costs less than a shallower ring would.
+template <int QB>
+struct GemmShape {
+  static constexpr int AH = q_ah(QB);            // 32-k activation fragments per row fragment and stage
+  static constexpr int BM = QB == 4 ? 128 : 256;  // rows per workgroup
+  static constexpr int MF = BM / 32;             // row fragments per wave (two wave rows)
+  static constexpr int NAF = BM / 16 * AH;       // activation fragments per stage
+  static constexpr int NBF = 16;                 // weight fragments per stage
+  static constexpr int STAGE_KB = NAF + NBF;     // KiB per stage
+  static constexpr int STAGES = 160 / STAGE_KB;  // ring depth: 5 (bf16) or 3 (int8, int4)
+  static constexpr int CPA = NAF / 8;            // activation copies per wave and stage
+  static constexpr int CPB = NBF / 8;            // weight copies per wave and stage
+  static constexpr int CPS = CPA + CPB;          // copies per wave and stage
+};
+
 constexpr int kWR = 2;       // wave rows
 constexpr int kWC = 4;       // wave columns
 constexpr int kWaves = kWR * kWC;
-constexpr int kMF = 8;       // row fragments per wave (128 rows)
-constexpr int kNF = 4;       // column fragments per wave
-constexpr int kCPW = 16 / kWaves;  // A (and B) fragments each wave copies per stage
-constexpr int kCPS = 2 * kCPW;     // copies per wave per stage
-constexpr int kStages = 5;   // LDS ring depth: 5 x 32 KiB, all of a CU's LDS
+constexpr int kNF = 4;       // column fragments per wave (64 weight columns)
 constexpr int kFrag = 1024;  // bytes of one 64-lane x 16-byte fragment
 
 // acc += a * b on the matrix cores, accumulating in place.  Written as
 // inline assembly because the compiler otherwise gives each product a fresh
 // destination and copies the accumulators around the loop, which doubles
-// their register footprint.  The accumulator is reused only 32 products
-// later, so consecutive products carry no dependence.
+// their register footprint.  An accumulator is reused only 16 or more
+// products later, so consecutive products carry no dependence.
 __device__ __forceinline__ void mfma_acc(floatx4_t& acc, const bf16x8_t& a, const bf16x8_t& b) {
   asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
+}
+
+// The same for a product whose weight operand a vector instruction has just
+// written (the integer kinds' conversion): a matrix instruction reading a
+// register that a vector ALU instruction wrote needs two wait states, which
+// the compiler does not insert for inline assembly.
+__device__ __forceinline__ void mfma_acc_fresh(floatx4_t& acc, const bf16x8_t& a, const bf16x8_t& b) {
+  asm volatile("s_nop 1\n\tv_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
 }
 
 // Ties an accumulator to the surrounding statements in its register file.
@@ -78,38 +102,54 @@ __device__ __forceinline__ void acc_tie(floatx4_t& acc) {
 // them; a 16x16x32 product needs fewer than 32 wait states).  The empty
 // statements tie every accumulator to the gap so no access moves across it.
 template <int MF, int NF>
-__device__ __forceinline__ void mfma_fence_in(floatx4_t (&acc)[MF][NF]) {
+__device__ __forceinline__ void mfma_fence_in(floatx4_t (&acc)[MF][NF], floatx4_t& accx) {
 #pragma unroll
   for (int i = 0; i < MF; ++i)
 #pragma unroll
     for (int j = 0; j < NF; ++j) acc_tie(acc[i][j]);
+  acc_tie(accx);
   asm volatile("s_nop 7\n\ts_nop 7" ::: "memory");
 }
 template <int MF, int NF>
-__device__ __forceinline__ void mfma_fence_out(floatx4_t (&acc)[MF][NF]) {
+__device__ __forceinline__ void mfma_fence_out(floatx4_t (&acc)[MF][NF], floatx4_t& accx) {
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
 #pragma unroll
   for (int i = 0; i < MF; ++i)
 #pragma unroll
     for (int j = 0; j < NF; ++j) acc_tie(acc[i][j]);
+  acc_tie(accx);
 }
 
+// One expert projection tile: BM rows x 256 weight columns over the whole
+// reduction.  QB: weight bits (0 bf16, 8 int8, 4 int4); integer weights are
+// converted exactly to bf16 after their LDS read (the decode kernels'
+// conversions) and their per-column scale is applied in the epilogue; int4's
+// storage offset (each weight enters as q + 136) is removed with the rows'
+// activation sums, which the four waves of a wave row share out (one row
+// fragment each, one extra product per activation fragment).
 // SKIP: row fragments past the row block's last real row skip their
 // products (the fragment reads still run, so the steady state keeps no branch
 // around a load); for layers whose experts hold few rows.
-template <int EPI, bool SKIP>
+template <int EPI, bool SKIP, int QB>
 __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_ffn_gemm(
     const GemmArgs A) {
+  using S = GemmShape<QB>;
   constexpr int G = EPI == EPI_UP_SWIGLU ? 2 : 1;
   constexpr int TPW = kNF / G;  // column tiles per wave
-  // stage layout: 16 A fragments (256 rows x 32 k), then 16 B fragments
-  // (kWC wave columns x kNF fragments)
-  __shared__ __attribute__((aligned(1024))) unsigned char ring[kStages][32 * kFrag];
+  constexpr int MF = S::MF, AH = S::AH, NAF = S::NAF, CPA = S::CPA, CPB = S::CPB, CPS = S::CPS;
+  constexpr int STAGES = S::STAGES;
+  constexpr int STAGE_BYTES = S::STAGE_KB * kFrag;
+  static_assert(QB != 4 || MF == kWC, "int4 row sums: one row fragment per wave of a wave row");
+  static_assert(CPS * (STAGES - 1) <= 63, "vmcnt holds at most 63");
+  // stage layout: NAF activation fragments (row fragment rf, 32-k part h at
+  // rf * AH + h), then 16 weight fragments (kWC wave columns x kNF fragments)
+  __shared__ __attribute__((aligned(1024))) unsigned char ring[STAGES][STAGE_BYTES];
+  __shared__ float rowsum_s[QB == 4 ? S::BM : 1];
   const int* const offs_s = A.offsets;  // uniform: scalar loads
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  // wave row (128 rows) and wave column; each wave row is one group of four
+  // wave row (BM/2 rows) and wave column; each wave row is one group of four
   // waves, one per SIMD (the ping-pong below)
   const int wm = wave / kWC;
   const int wn = wave % kWC;
@@ -117,133 +157,192 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
   const int NBL = (NB + kWC * TPW - 1) / (kWC * TPW);  // column blocks
 
   int e, mb, nblock;
-  if (!gemm_item(offs_s, A.E, kBM, NBL, A.cg, xcd_logical(blockIdx.x, gridDim.x), &e, &mb, &nblock)) return;
+  if (!gemm_item(offs_s, A.E, S::BM, NBL, A.cg, xcd_logical(blockIdx.x, gridDim.x), &e, &mb, &nblock)) return;
   const int tile_base = nblock * kWC * TPW;
-  const int row0 = offs_s[e] + mb * kBM;  // first dispatched row
-  const int nrows = min(kBM, offs_s[e + 1] - row0);
-  const int prow0 = padded_offset(offs_s, e) + mb * kBM;  // its packed row
+  const int row0 = offs_s[e] + mb * S::BM;  // first dispatched row
+  const int nrows = min(S::BM, offs_s[e + 1] - row0);
+  const int prow0 = padded_offset(offs_s, e) + mb * S::BM;  // its packed row
   const int nfrag = (nrows + 15) >> 4;  // packed fragments holding real rows
   // this wave's row fragments that hold real rows (uniform)
-  const int nf_w = __builtin_amdgcn_readfirstlane(min(max(nfrag - wm * kMF, 0), kMF));
+  const int nf_w = __builtin_amdgcn_readfirstlane(min(max(nfrag - wm * MF, 0), MF));
 
-  // This wave copies A fragments and B fragments kCPW w .. kCPW w + kCPW-1 of
-  // every stage.  Sources are a uniform base that advances one 32-k unit per stage
-  // plus a constant 32-bit byte offset per lane (the packed activations and
-  // one projection's packed weights are each under 4 GiB; checked on the
-  // host).  A fragments past the expert's last row re-read its last
-  // fragment; their rows are never stored.
-  const int U = A.K / 32;
+  // This wave copies activation fragments CPA w .. CPA w + CPA-1 and weight
+  // fragments CPB w .. CPB w + CPB-1 of every stage.  Sources are a uniform
+  // base that advances one weight unit per stage plus a constant 32-bit byte
+  // offset per lane (the packed activations and one projection's packed
+  // weights are each under 4 GiB; checked on the host).  Activation
+  // fragments past the expert's last row re-read its last fragment; their
+  // rows are never stored.
+  const int U = A.K / (32 * AH);  // stages (weight units along K)
   const char* const abase = reinterpret_cast<const char*>(A.act);
   const char* const bbase = static_cast<const char*>(A.w);
-  uint32_t aoff[kCPW], boff[kCPW];
+  uint32_t aoff[CPA], boff[CPB];
 #pragma unroll
-  for (int j = 0; j < kCPW; ++j) {
-    const int f = kCPW * wave + j;  // A fragment f: rows f*16 .. +15; B fragment f
-    aoff[j] = (uint32_t)gemm_a_offset((prow0 >> 4) + min(f, nfrag - 1), A.K, lane);
-    boff[j] = (uint32_t)gemm_b_offset(e, NB, U, G, tile_base, kNF, f, lane);
+  for (int j = 0; j < CPA; ++j) {
+    const int f = CPA * wave + j;  // activation fragment f: row fragment f / AH, 32-k part f % AH
+    aoff[j] = (uint32_t)(gemm_a_offset((prow0 >> 4) + min(f / AH, nfrag - 1), A.K, lane) + (f % AH) * kFrag);
   }
+#pragma unroll
+  for (int j = 0; j < CPB; ++j) boff[j] = (uint32_t)gemm_b_offset(e, NB, U, G, tile_base, kNF, CPB * wave + j, lane);
 
-  // LDS byte address of the ring and of this wave's first fragment slot
+  // LDS byte addresses of this wave's first activation and weight slots
   const uint32_t ring_lds = lds_address(ring);
-  const uint32_t wave_lds = ring_lds + (uint32_t)(kCPW * wave) * kFrag;
+  const uint32_t a_lds = ring_lds + (uint32_t)(CPA * wave) * kFrag;
+  const uint32_t b_lds = ring_lds + (uint32_t)(NAF + CPB * wave) * kFrag;
 
 #define MOE_ISSUE(step)                                                                          \
   do {                                                                                           \
-    const char* ab_ = abase + (size_t)(step) * kFrag;                                            \
+    const char* ab_ = abase + (size_t)(step) * (AH * kFrag);                                     \
     const char* bb_ = bbase + (size_t)(step) * G * kFrag;                                        \
-    const uint32_t st_ = wave_lds + (uint32_t)((step) % kStages) * (32 * kFrag);                 \
-    _Pragma("unroll") for (int j = 0; j < kCPW; ++j) {                                           \
-      copy_frag(ab_, aoff[j], st_ + j * kFrag);                                                  \
-      copy_frag(bb_, boff[j], st_ + (16 + j) * kFrag);                                           \
-    }                                                                                            \
+    const uint32_t st_ = (uint32_t)((step) % STAGES) * STAGE_BYTES;                              \
+    _Pragma("unroll") for (int j = 0; j < CPA; ++j) copy_frag(ab_, aoff[j], a_lds + st_ + j * kFrag); \
+    _Pragma("unroll") for (int j = 0; j < CPB; ++j) copy_frag(bb_, boff[j], b_lds + st_ + j * kFrag); \
   } while (0)
 
-  floatx4_t acc[kMF][kNF];
+  floatx4_t acc[MF][kNF];
+  floatx4_t accx = floatx4_t{0.0f, 0.0f, 0.0f, 0.0f};  // int4: activation sums of row fragment wn
 #pragma unroll
-  for (int i = 0; i < kMF; ++i)
+  for (int i = 0; i < MF; ++i)
 #pragma unroll
     for (int j = 0; j < kNF; ++j) acc[i][j] = floatx4_t{0.0f, 0.0f, 0.0f, 0.0f};
-  mfma_fence_in(acc);
+  mfma_fence_in(acc, accx);
 
-  // The fragments of one stage, held in registers.
+  // The fragments of one stage, held in registers.  int8 weights stay raw
+  // until their products (converted one fragment half at a time, which keeps
+  // the 256-row tile's registers under the two-waves-per-SIMD budget); the
+  // other kinds are converted when read.
+  constexpr bool kLateCvt = QB == 8;
   struct {
-    bf16x8_t a[kMF], b[kNF];
+    bf16x8_t a[MF][AH], b[kNF][kLateCvt ? 1 : AH];
+    u32x4_t braw[kLateCvt ? kNF : 1];
   } f;
 #define MOE_LOAD_B(F, step)                                                                      \
   do {                                                                                           \
-    const u32x4_t* st_ = reinterpret_cast<const u32x4_t*>(ring[(step) % kStages]);               \
-    _Pragma("unroll") for (int j = 0; j < kNF; ++j) F.b[j] = as_bf16x8(st_[(16 + wn * kNF + j) * 64 + lane]); \
+    const u32x4_t* st_ = reinterpret_cast<const u32x4_t*>(ring[(step) % STAGES]);                \
+    _Pragma("unroll") for (int j = 0; j < kNF; ++j) {                                            \
+      const u32x4_t w_ = st_[(NAF + wn * kNF + j) * 64 + lane];                                  \
+      if constexpr (kLateCvt) {                                                                  \
+        F.braw[j] = w_;                                                                          \
+      } else if constexpr (QB == 4) {                                                            \
+        _Pragma("unroll") for (int h = 0; h < AH; ++h) F.b[j][h] = u4x8_to_bf16_biased(w_[h]);   \
+      } else {                                                                                   \
+        F.b[j][0] = as_bf16x8(w_);                                                               \
+      }                                                                                          \
+    }                                                                                            \
   } while (0)
-#define MOE_LOAD_A(F, step, i0, i1)                                                              \
+#define MOE_LOAD_A(F, step)                                                                      \
   do {                                                                                           \
-    const u32x4_t* st_ = reinterpret_cast<const u32x4_t*>(ring[(step) % kStages]);               \
-    _Pragma("unroll") for (int i = (i0); i < (i1); ++i) F.a[i] = as_bf16x8(st_[(wm * kMF + i) * 64 + lane]); \
+    const u32x4_t* st_ = reinterpret_cast<const u32x4_t*>(ring[(step) % STAGES]);                \
+    _Pragma("unroll") for (int i = 0; i < MF; ++i) _Pragma("unroll") for (int h = 0; h < AH; ++h) \
+        F.a[i][h] = as_bf16x8(st_[((wm * MF + i) * AH + h) * 64 + lane]);                        \
   } while (0)
 #define MOE_MMA(F)                                                                               \
-  _Pragma("unroll") for (int i = 0; i < kMF; ++i) {                                              \
-    if (!SKIP || i < nf_w) {                                                                     \
-      _Pragma("unroll") for (int j = 0; j < kNF; ++j) mfma_acc(acc[i][j], F.a[i], F.b[j]);       \
+  if constexpr (kLateCvt) {                                                                      \
+    _Pragma("unroll") for (int h = 0; h < AH; ++h) {                                             \
+      _Pragma("unroll") for (int j = 0; j < kNF; ++j) {                                          \
+        const bf16x8_t bw_ = h == 0 ? i8x8_to_bf16(F.braw[j][0], F.braw[j][1])                   \
+                                    : i8x8_to_bf16(F.braw[j][2], F.braw[j][3]);                  \
+        _Pragma("unroll") for (int i = 0; i < MF; ++i) {                                         \
+          if (!SKIP || i < nf_w) {                                                               \
+            if (i == 0)                                                                          \
+              mfma_acc_fresh(acc[i][j], F.a[i][h], bw_);                                         \
+            else                                                                                 \
+              mfma_acc(acc[i][j], F.a[i][h], bw_);                                               \
+          }                                                                                      \
+        }                                                                                        \
+      }                                                                                          \
+    }                                                                                            \
+  } else {                                                                                       \
+    _Pragma("unroll") for (int h = 0; h < AH; ++h) {                                             \
+      _Pragma("unroll") for (int i = 0; i < MF; ++i) {                                           \
+        if (!SKIP || i < nf_w) {                                                                 \
+          _Pragma("unroll") for (int j = 0; j < kNF; ++j) {                                      \
+            if (QB != 0 && i == 0)                                                               \
+              mfma_acc_fresh(acc[i][j], F.a[i][h], F.b[j][h]);                                   \
+            else                                                                                 \
+              mfma_acc(acc[i][j], F.a[i][h], F.b[j][h]);                                         \
+          }                                                                                      \
+        }                                                                                        \
+        if constexpr (QB == 4) {                                                                 \
+          if (i == wn) mfma_acc_fresh(accx, F.a[i][h], ones);                                    \
+        }                                                                                        \
+      }                                                                                          \
     }                                                                                            \
   }
 
-  const int nsteps = U;  // even, >= 2 (K is a multiple of 64)
+  const bf16x8_t ones = as_bf16x8(u32x4_t{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
+  (void)ones;
+  const int nsteps = U;  // >= 1
   {
-    // Ping-pong.  Waves 0-3 (group 0, rows 0-127) and 4-7 (group 1, rows
-    // 128-255) put one wave of each group on every SIMD.  Two barriers per
-    // step: between B1(s) and B2(s) group 0 multiplies stage s while group 1
-    // reads stage s and issues its copies of stage s+4; between B2(s) and
-    // B1(s+1) group 1 multiplies stage s while group 0 reads stage s+1 and
-    // issues its copies of stage s+5.  So the matrix cores always have one
-    // wave's products while the other wave waits for LDS and the barrier.
-    // Both groups run the same loop body [barrier, multiply, barrier, read
-    // the next stage, copy]; group 1 enters it one barrier later and group 0
-    // passes one extra barrier at the end, so the counts match.
-    // A slot is refilled only after the barrier that follows both groups'
-    // reads of it.  Before the barrier ahead of a stage's first read (B2(s-1)
-    // for stage s) every wave's copies of it have landed: group 0 then has
-    // stages up to s+3 issued, group 1 up to s+3, so at most 12 copies may
-    // stay outstanding; group 0's wait before B1(s) (16) and group 1's before
-    // B1(s+1) (12) only keep the loop body the same.
+    // Ping-pong.  Waves 0-3 (group 0, the first BM/2 rows) and 4-7 (group 1)
+    // put one wave of each group on every SIMD.  Two barriers per step:
+    // between B1(s) and B2(s) group 0 multiplies stage s while group 1 reads
+    // stage s and issues its copies of stage s + STAGES - 1; between B2(s)
+    // and B1(s+1) group 1 multiplies stage s while group 0 reads stage s+1
+    // and issues its copies of stage s + STAGES.  So the matrix cores always
+    // have one wave's products while the other wave waits for LDS and the
+    // barrier.  Both groups run the same loop body [barrier, multiply,
+    // barrier, read the next stage, copy]; group 1 enters it one barrier
+    // later and group 0 passes one extra barrier at the end, so the counts
+    // match.  A slot is refilled only after the barrier that follows both
+    // groups' reads of it (each barrier waits for the wave's own LDS reads).
+    // Before the barrier ahead of a wave's read of stage s, every wave has
+    // waited until its own copies of s have landed (copies complete in issue
+    // order): a group's copies are issued up to stage s + STAGES - 2 at that
+    // point, so at most STAGES - 2 later stages stay outstanding; group 0's
+    // wait before B1(s) (STAGES - 1 stages, its copies being one stage
+    // further) only keeps the loop body the same.
     const bool g0 = wave < kWC;
 #define MOE_ISSUE_CLAMPED(step) MOE_ISSUE((step) < nsteps ? (step) : nsteps - 1)
 #pragma unroll
-    for (int s = 0; s < kStages - 1; ++s) MOE_ISSUE_CLAMPED(s);
+    for (int s = 0; s < STAGES - 1; ++s) MOE_ISSUE_CLAMPED(s);
     if (g0) {
-      MOE_ISSUE_CLAMPED(kStages - 1);
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(kCPS * (kStages - 1)));
+      MOE_ISSUE_CLAMPED(STAGES - 1);
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(CPS * (STAGES - 1)));
       ring_barrier();  // B0
     } else {
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(kCPS * (kStages - 2)));
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(CPS * (STAGES - 2)));
       ring_barrier();  // B0
       ring_barrier();  // B1(0)
     }
     MOE_LOAD_B(f, 0);
-    MOE_LOAD_A(f, 0, 0, kMF);
-    if (!g0) MOE_ISSUE_CLAMPED(kStages - 1);
+    MOE_LOAD_A(f, 0);
+    if (!g0) MOE_ISSUE_CLAMPED(STAGES - 1);
     for (int ks = 0; ks < nsteps; ++ks) {
       if (g0)
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(kCPS * (kStages - 1)));
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(CPS * (STAGES - 1)));
       else
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(kCPS * (kStages - 2)));
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(CPS * (STAGES - 2)));
       ring_barrier();  // group 0: B1(ks); group 1: B2(ks)
       asm volatile("s_setprio 1");
       MOE_MMA(f);
       asm volatile("s_setprio 0");
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(kCPS * (kStages - 2)));
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(CPS * (STAGES - 2)));
       ring_barrier();  // group 0: B2(ks); group 1: B1(ks+1)
       MOE_LOAD_B(f, ks + 1);
-      MOE_LOAD_A(f, ks + 1, 0, kMF);
-      MOE_ISSUE_CLAMPED(ks + kStages);
+      MOE_LOAD_A(f, ks + 1);
+      MOE_ISSUE_CLAMPED(ks + STAGES);
     }
     if (g0) ring_barrier();
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
 #undef MOE_ISSUE_CLAMPED
   }
-  mfma_fence_out(acc);
+  mfma_fence_out(acc, accx);
 #undef MOE_LOAD_A
 #undef MOE_LOAD_B
 #undef MOE_MMA
 #undef MOE_ISSUE
+
+  // int4: the activation sums of every row of the block, each computed by
+  // one wave of its wave row, shared through LDS.  Lane l of accx holds rows
+  // wn*16 + 4*(l>>4) + q of this wave row (every column the same).
+  if constexpr (QB == 4) {
+    if ((lane & 15) == 0) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) rowsum_s[wm * MF * 16 + wn * 16 + 4 * (lane >> 4) + q] = accx[q];
+    }
+    __syncthreads();
+  }
 
   // Epilogue.  Lane l of fragment (i, j) holds rows i*16 + 4*(l>>4) + q,
   // q = 0..3, of column (l & 15) of the fragment's tile.
@@ -252,20 +351,31 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
     const int nb = tile_base + wn * TPW + t;
     if (nb >= NB) continue;
     const int col = nb * 16 + (lane & 15);
+    float sc0 = 1.0f, sc1 = 1.0f;
+    if constexpr (QB != 0) {
+      sc0 = A.scale0[(size_t)e * A.N + col];
+      if constexpr (G == 2) sc1 = A.scale1[(size_t)e * A.N + col];
+    }
 #pragma unroll
-    for (int i = 0; i < kMF; ++i) {
+    for (int i = 0; i < MF; ++i) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int row = wm * 16 * kMF + i * 16 + 4 * (lane >> 4) + q;
+        const int row = wm * 16 * MF + i * 16 + 4 * (lane >> 4) + q;
         if (row >= nrows) continue;
+        float v0 = acc[i][t * G][q], v1 = acc[i][t * G + G - 1][q];
+        if constexpr (QB == 4) {
+          const float bias = kI4Bias * rowsum_s[row];
+          v0 -= bias;
+          v1 -= bias;
+        }
+        v0 *= sc0;
+        v1 *= sc1;
         if constexpr (EPI == EPI_UP_SWIGLU) {
-          const float gv = acc[i][t * 2][q], uv = acc[i][t * 2 + 1][q];
-          A.h_out[packed_index(prow0 + row, col, A.N)] = f32_to_bf16(silu(gv) * uv);
+          A.h_out[packed_index(prow0 + row, col, A.N)] = f32_to_bf16(silu(v0) * v1);
         } else if constexpr (EPI == EPI_UP_RELU) {
-          const float gv = acc[i][t][q];
-          A.h_out[packed_index(prow0 + row, col, A.N)] = f32_to_bf16(gv > 0.0f ? gv : 0.0f);
+          A.h_out[packed_index(prow0 + row, col, A.N)] = f32_to_bf16(v0 > 0.0f ? v0 : 0.0f);
         } else {
-          A.f_out[(size_t)(row0 + row) * A.N + col] = acc[i][t][q];
+          A.f_out[(size_t)(row0 + row) * A.N + col] = v0;
         }
       }
     }
@@ -336,22 +446,23 @@ __global__ __launch_bounds__(256) void k_pack_rows(const PackArgs A) {
 
 }  // namespace
 
-hipError_t launch_ffn_gemm(const GemmArgs& a, int epi, hipStream_t s) {
-  if (a.K % 64 || a.N % 64 || a.K <= 0 || a.N <= 0 || a.cg < 1 || epi == EPI_DOWN_ACC)
-    return hipErrorInvalidValue;  // an even step count, whole tiles
+template <int QB>
+hipError_t launch_gemm_qb(const GemmArgs& a, int epi, hipStream_t s) {
+  using S = GemmShape<QB>;
   const int G = epi == EPI_UP_SWIGLU ? 2 : 1;
   const int tiles_per_block = kWC * (kNF / G);
   const int NB = a.N / 16;
   const long long nbl = (NB + tiles_per_block - 1) / tiles_per_block;
   const long long work = nbl * a.W;  // a.W bounds the number of row blocks
   if (work <= 0) return hipSuccess;  // no expert is served
+  if (work > 0x7FFFFFF0LL) return hipErrorInvalidValue;
   const dim3 grid((unsigned)((work + 7) / 8 * 8));
-#define MOE_LAUNCH(SK)                                                                               \
-  switch (epi) {                                                                                     \
-    case EPI_UP_SWIGLU: k_ffn_gemm<EPI_UP_SWIGLU, SK><<<grid, kWaves * 64, 0, s>>>(a); break;           \
-    case EPI_UP_RELU: k_ffn_gemm<EPI_UP_RELU, SK><<<grid, kWaves * 64, 0, s>>>(a); break;               \
-    case EPI_DOWN_ROWS: k_ffn_gemm<EPI_DOWN_ROWS, SK><<<grid, kWaves * 64, 0, s>>>(a); break;           \
-    default: return hipErrorInvalidValue;                                                            \
+#define MOE_LAUNCH(SK)                                                                                    \
+  switch (epi) {                                                                                          \
+    case EPI_UP_SWIGLU: k_ffn_gemm<EPI_UP_SWIGLU, SK, QB><<<grid, kWaves * 64, 0, s>>>(a); break;           \
+    case EPI_UP_RELU: k_ffn_gemm<EPI_UP_RELU, SK, QB><<<grid, kWaves * 64, 0, s>>>(a); break;               \
+    case EPI_DOWN_ROWS: k_ffn_gemm<EPI_DOWN_ROWS, SK, QB><<<grid, kWaves * 64, 0, s>>>(a); break;           \
+    default: return hipErrorInvalidValue;                                                                 \
   }
   if (a.skip_empty) {
     MOE_LAUNCH(true)
@@ -359,7 +470,20 @@ hipError_t launch_ffn_gemm(const GemmArgs& a, int epi, hipStream_t s) {
     MOE_LAUNCH(false)
   }
 #undef MOE_LAUNCH
+  (void)S::BM;
   return hipGetLastError();
+}
+
+hipError_t launch_ffn_gemm(const GemmArgs& a, int epi, int qb, hipStream_t s) {
+  const int uk = 32 * q_ah(qb);
+  if (a.K % 64 || a.N % 64 || a.K <= 0 || a.N <= 0 || a.K % uk || a.cg < 1) return hipErrorInvalidValue;
+  if (qb != 0 && (!a.scale0 || (epi == EPI_UP_SWIGLU && !a.scale1))) return hipErrorInvalidValue;
+  switch (qb) {
+    case 0: return launch_gemm_qb<0>(a, epi, s);
+    case 8: return launch_gemm_qb<8>(a, epi, s);
+    case 4: return launch_gemm_qb<4>(a, epi, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 hipError_t launch_pack_rows(const PackArgs& a, hipStream_t s) {
@@ -370,6 +494,6 @@ hipError_t launch_pack_rows(const PackArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-int gemm_rows_per_block() { return kBM; }
+int gemm_rows_per_block(int qb) { return qb == 4 ? GemmShape<4>::BM : (qb == 8 ? GemmShape<8>::BM : GemmShape<0>::BM); }
 
 }  // namespace moe

@@ -144,7 +144,9 @@ hipError_t launch_ffn_skinny_split(const SkinnyArgs& narrow, const SkinnyArgs& w
 // writes are in the packed row layout of moe_index.hpp (16-row x 32-k
 // fragments, each expert starting on a 16-row boundary).
 struct GemmArgs {
-  const void* w;           // packed bf16 weights of this projection
+  const void* w;           // packed weights of this projection (bf16, int8 or int4)
+  const float* scale0;     // integer weights: per-column scales [E][N] (gate, or the only stream)
+  const float* scale1;     // integer SwiGLU weights: the up stream's scales [E][N]
   const uint16_t* act;     // packed bf16 activations [packed rows][K]
   const int32_t* offsets;  // [E+1] dispatch offsets
   uint16_t* h_out;         // packed H [packed rows][N] (up epilogues)
@@ -155,10 +157,12 @@ struct GemmArgs {
   int W;                   // upper bound on (expert, 256-row block) pairs
 };
 
-// K a multiple of 64, N a multiple of 64, bf16 weights.  epi: EPI_UP_SWIGLU,
-// EPI_UP_RELU or EPI_DOWN_ROWS.
-hipError_t launch_ffn_gemm(const GemmArgs& a, int epi, hipStream_t s);
-int gemm_rows_per_block();
+// K a multiple of 64 (and of the weight unit: 64 k for int8, 128 for int4),
+// N a multiple of 64; qb: weight bits (0 bf16, 8 int8, 4 int4).  epi:
+// EPI_UP_SWIGLU, EPI_UP_RELU or EPI_DOWN_ROWS.
+hipError_t launch_ffn_gemm(const GemmArgs& a, int epi, int qb, hipStream_t s);
+// Rows per row block (work item) of the grouped GEMM for weight bits qb.
+int gemm_rows_per_block(int qb);
 
 // Gathers x rows in dispatch order into the packed row layout.
 struct PackArgs {

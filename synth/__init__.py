@@ -157,6 +157,11 @@ CONFIGS = {
     # a next row (lower-precision weights): the int8 layer with int4 weights
     "c6": LayerSpec("mixtral_decode_int4", 64, 4096, 14336, 8, 2, "swiglu", "bf16", "i4", 5,
                     note="Mixtral-8x7B-shaped decode, int4 weights with per-channel fp32 scales"),
+    # the integer weights at prefill size: the grouped GEMM with the dequant fused
+    "c7": LayerSpec("mixtral_prefill_int8", 8192, 4096, 14336, 8, 2, "swiglu", "bf16", "i8", 6,
+                    note="Mixtral-8x7B-shaped prefill, int8 weights with per-channel fp32 scales"),
+    "c8": LayerSpec("mixtral_prefill_int4", 8192, 4096, 14336, 8, 2, "swiglu", "bf16", "i4", 7,
+                    note="Mixtral-8x7B-shaped prefill, int4 weights with per-channel fp32 scales"),
 }
 
 

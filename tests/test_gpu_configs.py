@@ -1,11 +1,12 @@
 """The five measured layers at full size, in the launch configuration the
-benchmark times, against the CPU oracle.
+benchmark times, against the CPU oracle, and the int8 and int4 Mixtral
+prefill layers (the grouped GEMM with the weights' dequant fused).
 
 Routing and dispatch are checked in full.  Outputs are checked element by
 element on every token of the tiny, decode, skewed and int8 layers.  On the
-prefill layer (8192 tokens, the grouped GEMM) at least 512 tokens are
-checked, chosen so that every (expert, 256-row block) of the GEMM contributes
-rows: the first and last row of every block (so each expert's ragged last
+prefill layers (8192 tokens, the grouped GEMM) at least 512 tokens are
+checked, chosen so that every (expert, row block) of the GEMM (256 rows; 128
+for int4) contributes rows: the first and last row of every block (so each expert's ragged last
 block and the first and last packed rows) and one inside it, topped up with
 random tokens (tokens are independent rows).
 """
@@ -32,7 +33,7 @@ def _gpu():
     yield
 
 
-def prefill_tokens(offsets, perm, k, T, seed, n_min=PREFILL_MIN_TOKENS):
+def prefill_tokens(offsets, perm, k, T, seed, n_min=PREFILL_MIN_TOKENS, block=BLOCK_ROWS):
     """Tokens whose rows cover every (expert, row block): per block its first,
     last and one random row, then random tokens up to n_min.  Returns the
     sorted tokens and the number of blocks covered."""
@@ -41,8 +42,8 @@ def prefill_tokens(offsets, perm, k, T, seed, n_min=PREFILL_MIN_TOKENS):
     E = len(offsets) - 1
     for e in range(E):
         lo, hi = int(offsets[e]), int(offsets[e + 1])
-        for r0 in range(lo, hi, BLOCK_ROWS):
-            r1 = min(r0 + BLOCK_ROWS, hi) - 1
+        for r0 in range(lo, hi, block):
+            r1 = min(r0 + block, hi) - 1
             for r in (r0, r1, int(rng.integers(r0, r1 + 1))):
                 toks.add(int(perm[r]) // k)
             blocks += 1
@@ -51,7 +52,7 @@ def prefill_tokens(offsets, perm, k, T, seed, n_min=PREFILL_MIN_TOKENS):
     return np.array(sorted(toks)), blocks
 
 
-@pytest.mark.parametrize("cfg", ["c1", "c2", "c3", "c4", "c5"])
+@pytest.mark.parametrize("cfg", ["c1", "c2", "c3", "c4", "c5", "c7", "c8"])
 def test_config_full_size(cfg):
     sp = synth.spec(cfg)
     log(f"config {cfg} ({sp.name}): T={sp.T} m={sp.m} p={sp.p} E={sp.E} k={sp.k} {sp.kind} "
@@ -63,15 +64,16 @@ def test_config_full_size(cfg):
     torch.cuda.synchronize()
     lg, idx_g, w_g, counts, n_diff = check_routing(L, dbg, sp.T, sp.E, sp.k)
     log(f"  counts={counts.tolist()} tokens routed differently from oracle logits: {n_diff}")
-    if cfg == "c4":
+    if sp.T >= 4096:  # prefill layers: the grouped GEMM
         offsets = dbg["offsets"].cpu().numpy()
         perm = dbg["perm"].cpu().numpy()
-        tokens, blocks = prefill_tokens(offsets, perm, sp.k, sp.T, seed=100 + sp.seed)
+        bm = 128 if sp.w_dtype == "i4" else BLOCK_ROWS  # int4 runs 128-row blocks
+        tokens, blocks = prefill_tokens(offsets, perm, sp.k, sp.T, seed=100 + sp.seed, block=bm)
         # every block of every expert has at least one row among the checked tokens
         rows = set(np.nonzero(np.isin(perm // sp.k, tokens))[0].tolist())
         for e in range(sp.E):
-            for r0 in range(int(offsets[e]), int(offsets[e + 1]), BLOCK_ROWS):
-                assert any(r in rows for r in range(r0, min(r0 + BLOCK_ROWS, int(offsets[e + 1])))), (e, r0)
+            for r0 in range(int(offsets[e]), int(offsets[e + 1]), bm):
+                assert any(r in rows for r in range(r0, min(r0 + bm, int(offsets[e + 1])))), (e, r0)
         log(f"  checking {len(tokens)} tokens covering all {blocks} (expert, row block) pairs")
         assert len(tokens) >= PREFILL_MIN_TOKENS
     else:

@@ -48,6 +48,20 @@ SHAPES = [
 ]
 
 
+# int4 weights need m and p multiples of 128 (and take 128-row blocks)
+SHAPES_I4 = [
+    (5, 128, 128, 3, 2),
+    (37, 256, 384, 8, 2),      # 384 columns: partial column block
+    (300, 256, 512, 4, 2),     # 150 rows per expert on average: two 128-row blocks, ragged
+    (600, 1024, 1536, 8, 2),   # several row and column blocks
+    (1, 512, 384, 16, 2),      # 14 empty experts
+    (64, 128, 128, 64, 4),     # 64 experts
+    (700, 384, 256, 2, 1),     # 3 row blocks per expert, ragged tail
+]
+WEIGHTS = [("bf16", s) for s in SHAPES] + [("i8", s) for s in SHAPES] + [("i4", s) for s in SHAPES_I4]
+WIDS = [f"{w}-{'-'.join(map(str, s))}" for w, s in WEIGHTS]
+
+
 def _routing(T, E, k, seed):
     rng = np.random.default_rng(seed)
     idx = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
@@ -56,10 +70,11 @@ def _routing(T, E, k, seed):
 
 
 @pytest.mark.parametrize("kind", ["swiglu", "relu"])
-@pytest.mark.parametrize("T,m,p,E,k", SHAPES)
-def test_gemm_expert_ffn_stage(kind, T, m, p, E, k):
-    log(f"gemm expert_ffn kind={kind} T={T} m={m} p={p} E={E} k={k}")
-    L = synth.make_layer(spec(T, m, p, E, k, kind, "bf16", seed=7 * T + p, sw=0.05))
+@pytest.mark.parametrize("wd,shape", WEIGHTS, ids=WIDS)
+def test_gemm_expert_ffn_stage(kind, wd, shape):
+    T, m, p, E, k = shape
+    log(f"gemm expert_ffn kind={kind} w={wd} T={T} m={m} p={p} E={E} k={k}")
+    L = synth.make_layer(spec(T, m, p, E, k, kind, wd, seed=7 * T + p, sw=0.05))
     layer = MoELayer(L)
     idx_n, _ = _routing(T, E, k, seed=T + m + 1)
     counts, offsets, perm, _ = oracle.dispatch(idx_n, E)
@@ -70,15 +85,16 @@ def test_gemm_expert_ffn_stage(kind, T, m, p, E, k):
     ref, _ = oracle.expert_rows(oracle.Experts.from_layer(L), L["x"], k, perm, offsets)
     got = y_perm.cpu().numpy()
     assert np.all(np.isfinite(got)), "rows left unwritten"
-    assert_close(got, ref, "bf16", "y_perm")
+    assert_close(got, ref, wd, "y_perm")
     layer.close()
 
 
 @pytest.mark.parametrize("kind", ["swiglu", "relu"])
-@pytest.mark.parametrize("T,m,p,E,k", SHAPES)
-def test_gemm_layer_forward(kind, T, m, p, E, k):
-    log(f"gemm layer_forward kind={kind} T={T} m={m} p={p} E={E} k={k}")
-    L = synth.make_layer(spec(T, m, p, E, k, kind, "bf16", seed=T + 3 * E + p, sw=0.05, sr=0.05))
+@pytest.mark.parametrize("wd,shape", WEIGHTS, ids=WIDS)
+def test_gemm_layer_forward(kind, wd, shape):
+    T, m, p, E, k = shape
+    log(f"gemm layer_forward kind={kind} w={wd} T={T} m={m} p={p} E={E} k={k}")
+    L = synth.make_layer(spec(T, m, p, E, k, kind, wd, seed=T + 3 * E + p, sw=0.05, sr=0.05))
     sp = L["spec"]
     layer = MoELayer(L)
     dbg = layer.debug_buffers()
@@ -89,14 +105,15 @@ def test_gemm_layer_forward(kind, T, m, p, E, k):
     ref, i_o, _, _ = oracle.forward_tokens(oracle.Experts.from_layer(L), L["x"], L["wg"], L["bias"], sp.k,
                                            np.arange(T), logits=lg)
     assert np.array_equal(i_o, idx_g)
-    assert_close(y_to_np(y), ref, "bf16", "y")
+    assert_close(y_to_np(y), ref, wd, "y")
     layer.close()
 
 
-def test_gemm_all_rows_on_one_expert():
-    """Every token's first choice is expert 3: it holds 600 rows (three row
-    blocks, the last ragged) while most experts hold none."""
-    L = synth.make_layer(spec(600, 256, 320, 16, 2, "swiglu", "bf16", seed=11))
+@pytest.mark.parametrize("wd", ["bf16", "i8", "i4"])
+def test_gemm_all_rows_on_one_expert(wd):
+    """Every token's first choice is expert 3: it holds 600 rows (three or
+    five row blocks, the last ragged) while most experts hold none."""
+    L = synth.make_layer(spec(600, 256, 384, 16, 2, "swiglu", wd, seed=11))
     L["bias"] = np.zeros(16, np.float32)
     L["bias"][3] = 50.0
     layer = MoELayer(L)
@@ -107,13 +124,14 @@ def test_gemm_all_rows_on_one_expert():
     assert counts[3] == 600
     ref, _, _, _ = oracle.forward_tokens(oracle.Experts.from_layer(L), L["x"], L["wg"], L["bias"], 2,
                                          np.arange(600), logits=lg)
-    assert_close(y_to_np(y), ref, "bf16", "y")
+    assert_close(y_to_np(y), ref, wd, "y")
     layer.close()
 
 
-def test_gemm_repeat_is_bitwise():
+@pytest.mark.parametrize("wd", ["bf16", "i8", "i4"])
+def test_gemm_repeat_is_bitwise(wd):
     """The GEMM path has no atomics: two calls give identical bits."""
-    L = synth.make_layer(spec(300, 256, 512, 4, 2, seed=2))
+    L = synth.make_layer(spec(300, 256, 512, 4, 2, "swiglu", wd, seed=2))
     layer = MoELayer(L)
     y1 = layer.forward().clone()
     y2 = layer.forward()
