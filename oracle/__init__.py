@@ -18,10 +18,11 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "moe_oracle.c")
 _LIB = os.path.join(_HERE, "libmoe_oracle.so")
 
-F32, BF16, I8 = 0, 1, 2
+F32, BF16, I8, FP8, MXFP4 = 0, 1, 2, 3, 4
 RELU, SWIGLU = 0, 1
 MAX_E = 64
-_DT = {"f32": F32, "bf16": BF16, "i8": I8}
+# weight dtypes by name (int4 weights are int8 values in [-7, 7] to the oracle)
+_DT = {"f32": F32, "bf16": BF16, "i8": I8, "i4": I8, "fp8": FP8, "mxfp4": MXFP4}
 _KIND = {"relu": RELU, "swiglu": SWIGLU}
 
 
@@ -68,8 +69,10 @@ def lib():
         L.orc_set_threads.argtypes = [i32]
         L.orc_set_threads.restype = None
         L.orc_norm.argtypes = [vp, i32, i32, i32, i32, vp, vp, ctypes.c_double, vp]
+        i64 = ctypes.c_int64
+        L.orc_weight_value.argtypes = [vp, vp, i32, i64, i64, i64, i64, i64, ctypes.POINTER(ctypes.c_double)]
         L.orc_max_threads.restype = ctypes.c_int
-        for f in ("orc_norm", "orc_router_logits", "orc_topk", "orc_dispatch", "orc_expert_apply", "orc_expert_rows",
+        for f in ("orc_weight_value", "orc_norm", "orc_router_logits", "orc_topk", "orc_dispatch", "orc_expert_apply", "orc_expert_rows",
                   "orc_combine", "orc_forward_tokens", "orc_dense_masked"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
@@ -107,15 +110,21 @@ def _xdt(x):
 
 
 class Experts:
-    """Expert weights of one layer in canonical layout (see synth)."""
+    """Expert weights of one layer in canonical layout (see synth).  w_dtype
+    ("fp8" or "mxfp4") names the uint8 weight formats; the others follow from
+    the arrays' dtypes (fp32, bf16 as uint16, int8)."""
 
-    def __init__(self, kind, w1, w2, w3=None, s1=None, s2=None, s3=None):
+    def __init__(self, kind, w1, w2, w3=None, s1=None, s2=None, s3=None, w_dtype=None):
         self.kind = kind
         self.w1, self.w2, self.w3 = _c(w1), _c(w2), _c(w3)
-        self.s1, self.s2, self.s3 = _c(s1, np.float32), _c(s2, np.float32), _c(s3, np.float32)
+        sdt = np.uint8 if w_dtype == "mxfp4" else np.float32
+        self.s1, self.s2, self.s3 = _c(s1, sdt), _c(s2, sdt), _c(s3, sdt)
         E, m, p = self.w1.shape
         assert self.w2.shape == (E, p, m)
-        if self.w1.dtype == np.float32:
+        if w_dtype in ("fp8", "mxfp4"):
+            assert self.w1.dtype == np.uint8
+            dt = _DT[w_dtype]
+        elif self.w1.dtype == np.float32:
             dt = F32
         elif self.w1.dtype == np.uint16:
             dt = BF16
@@ -130,12 +139,25 @@ class Experts:
     @classmethod
     def from_layer(cls, layer):
         sp = layer["spec"]
-        return cls(sp.kind, layer["w1"], layer["w2"], layer["w3"], layer["s1"], layer["s2"], layer["s3"])
+        return cls(sp.kind, layer["w1"], layer["w2"], layer["w3"], layer["s1"], layer["s2"], layer["s3"],
+                   w_dtype=sp.w_dtype)
 
     def param_bytes(self) -> int:
         """Bytes of one expert's weight matrices as stored."""
         nmat = 3 if self.kind == "swiglu" else 2
         return nmat * self.m * self.p * self.w1.itemsize
+
+
+def weight_value(w, s, dtype, e, k, n):
+    """Decoded weight (e, k, n) of a [E][K][N] projection w in dtype (a name of
+    _DT) with its scales s, as the oracle's expert uses it."""
+    w = _c(w)
+    sdt = np.uint8 if dtype == "mxfp4" else np.float32
+    s = _c(s, sdt)
+    E, K, N = w.shape
+    out = ctypes.c_double()
+    _check(lib().orc_weight_value(_ptr(w), _ptr(s), _DT[dtype], e, K, N, k, n, ctypes.byref(out)), "weight_value")
+    return out.value
 
 
 def router_logits(x, wg, bias=None):

@@ -22,7 +22,9 @@
  *  - expert: the two-layer MLP x*W1*W2 with W1 m x p and W2 p x m (HARMOEny
  *    article, section 3.2 "expert prefetch"), with ReLU between the two
  *    matrices, or its SwiGLU form h = SiLU(x*W1) * (x*W3), o = h*W2.  int8
- *    weights stand for q[i][n] * s[n] (per output channel n).  Every dot
+ *    weights stand for q[i][n] * s[n] (per output channel n), fp8 weights
+ *    for e4m3(code) * s[n], MXFP4 weights for e2m1(code) times the E8M0
+ *    scale of their block of 32 consecutive i (see weight() below).  Every dot
  *    product of length n is a0*b0 followed by n-1 multiply-adds, and an
  *    operation counter records each multiply and each add.
  *  - combine: y[t] = sum over the token's selections, in ascending expert
@@ -65,14 +67,56 @@ static double act_at(const void* x, int dtype, int64_t i) {
   return bf16_bits_to_double(((const uint16_t*)x)[i]);
 }
 
-/* Weight element i of expert matrix storage; for int8 the per-output-channel
- * scale of column n multiplies the integer. */
-static double w_at(const void* w, const float* s, int dtype, int64_t i, int64_t scale_i) {
+/* The 8-bit float E4M3 of the OCP 8-bit floating point format (OFP8,
+ * "E4M3FN"): sign bit, 4 exponent bits with bias 7, 3 mantissa bits; exponent
+ * field 0 holds the subnormals m * 2^-9; no infinities; S.1111.111 is NaN, so
+ * the largest finite magnitude is 1.75 * 2^8 = 448. */
+static double e4m3_value(uint8_t c) {
+  const int sign = c >> 7, ex = (c >> 3) & 15, mt = c & 7;
+  if (ex == 15 && mt == 7) return NAN;
+  const double v = ex == 0 ? mt * ldexp(1.0, -9) : (1.0 + mt / 8.0) * ldexp(1.0, ex - 7);
+  return sign ? -v : v;
+}
+
+/* The 4-bit float E2M1 of the OCP microscaling (MX) formats: sign bit, 2
+ * exponent bits with bias 1, 1 mantissa bit; exponent field 0 holds the
+ * subnormal 0.5 m; magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6.  Codes are the low
+ * nibble of a byte (bit 3 the sign). */
+static double e2m1_value(uint8_t c) {
+  const int sign = (c >> 3) & 1, ex = (c >> 1) & 3, mt = c & 1;
+  const double v = ex == 0 ? 0.5 * mt : (1.0 + 0.5 * mt) * ldexp(1.0, ex - 1);
+  return sign ? -v : v;
+}
+
+/* The shared scale E8M0 of the MX formats: 2^(E - 127); E = 255 is NaN. */
+static double e8m0_value(uint8_t E) { return E == 255 ? NAN : ldexp(1.0, (int)E - 127); }
+
+/* Weight (e, k, n) of a projection stored [E][K][N] (k along the reduction):
+ *  - fp32, bf16: the stored value;
+ *  - int8 (int4 as well: q in [-7, 7], one per byte): q * s[e][n], one fp32
+ *    scale per output channel;
+ *  - fp8: e4m3(code) * s[e][n], one fp32 scale per output channel;
+ *  - MXFP4: e2m1(code) * e8m0(X[e][k / 32][n]): one E8M0 scale shared by the
+ *    32 consecutive k of a column (the MX block of 32 elements). */
+static double weight(const void* w, const void* s, int dtype, int64_t e, int64_t K, int64_t N, int64_t k,
+                     int64_t n) {
+  const int64_t i = (e * K + k) * N + n;
   switch (dtype) {
     case ORC_F32: return (double)((const float*)w)[i];
     case ORC_BF16: return bf16_bits_to_double(((const uint16_t*)w)[i]);
-    default: return (double)((const int8_t*)w)[i] * (double)s[scale_i];
+    case ORC_I8: return (double)((const int8_t*)w)[i] * (double)((const float*)s)[e * N + n];
+    case ORC_FP8: return e4m3_value(((const uint8_t*)w)[i]) * (double)((const float*)s)[e * N + n];
+    default: return e2m1_value(((const uint8_t*)w)[i]) * e8m0_value(((const uint8_t*)s)[(e * (K / 32) + k / 32) * N + n]);
   }
+}
+
+int orc_weight_value(const void* w, const void* s, int dtype, int64_t e, int64_t K, int64_t N, int64_t k, int64_t n,
+                     double* out) {
+  if (!w || !out || dtype < ORC_F32 || dtype > ORC_MXFP4) return -1;
+  if (dtype >= ORC_I8 && !s) return -1;
+  if (dtype == ORC_MXFP4 && K % 32) return -1;
+  *out = weight(w, s, dtype, e, K, N, k, n);
+  return 0;
 }
 
 /* ---- router ------------------------------------------------------------- */
@@ -194,31 +238,28 @@ static double silu(double z) { return z / (1.0 + exp(-z)); }
 static void expert_row(const orc_experts* X, int e, const double* x, double* g, double* u, double* o,
                        uint64_t ops[3]) {
   const int m = X->m, p = X->p;
-  const int64_t in_base = (int64_t)e * m * p;  /* [E][m][p] */
-  const int64_t out_base = (int64_t)e * p * m; /* [E][p][m] */
-  const int64_t s_in = (int64_t)e * p, s_out = (int64_t)e * m;
   const int swiglu = (X->kind == ORC_SWIGLU);
+  const int dt = X->w_dtype;
 
   /* g = x*W1 (and u = x*W3): every g[n] is the length-m dot product in
    * increasing i, started with the i = 0 product.  The counters tick once
    * per multiply and once per add actually performed. */
   uint64_t mul = 0, add = 0, act = 0, prod = 0;
   for (int n = 0; n < p; ++n) {
-    g[n] = x[0] * w_at(X->w1, X->s1, X->w_dtype, in_base + n, s_in + n);
+    g[n] = x[0] * weight(X->w1, X->s1, dt, e, m, p, 0, n);
     mul += 1;
     if (swiglu) {
-      u[n] = x[0] * w_at(X->w3, X->s3, X->w_dtype, in_base + n, s_in + n);
+      u[n] = x[0] * weight(X->w3, X->s3, dt, e, m, p, 0, n);
       mul += 1;
     }
   }
   for (int i = 1; i < m; ++i) {
-    const int64_t row = in_base + (int64_t)i * p;
     for (int n = 0; n < p; ++n) {
-      g[n] += x[i] * w_at(X->w1, X->s1, X->w_dtype, row + n, s_in + n);
+      g[n] += x[i] * weight(X->w1, X->s1, dt, e, m, p, i, n);
       mul += 1;
       add += 1;
       if (swiglu) {
-        u[n] += x[i] * w_at(X->w3, X->s3, X->w_dtype, row + n, s_in + n);
+        u[n] += x[i] * weight(X->w3, X->s3, dt, e, m, p, i, n);
         mul += 1;
         add += 1;
       }
@@ -238,13 +279,12 @@ static void expert_row(const orc_experts* X, int e, const double* x, double* g, 
 
   /* o = h*W2 */
   for (int j = 0; j < m; ++j) {
-    o[j] = g[0] * w_at(X->w2, X->s2, X->w_dtype, out_base + j, s_out + j);
+    o[j] = g[0] * weight(X->w2, X->s2, dt, e, p, m, 0, j);
     mul += 1;
   }
   for (int n = 1; n < p; ++n) {
-    const int64_t row = out_base + (int64_t)n * m;
     for (int j = 0; j < m; ++j) {
-      o[j] += g[n] * w_at(X->w2, X->s2, X->w_dtype, row + j, s_out + j);
+      o[j] += g[n] * weight(X->w2, X->s2, dt, e, p, m, n, j);
       mul += 1;
       add += 1;
     }
@@ -258,8 +298,9 @@ static int check_experts(const orc_experts* X) {
   if (!X || X->m < 1 || X->p < 1 || X->E < 1 || !X->w1 || !X->w2) return -1;
   if (X->kind != ORC_RELU && X->kind != ORC_SWIGLU) return -1;
   if (X->kind == ORC_SWIGLU && !X->w3) return -1;
-  if (X->w_dtype == ORC_I8 && (!X->s1 || !X->s2 || (X->kind == ORC_SWIGLU && !X->s3))) return -1;
-  if (X->w_dtype != ORC_F32 && X->w_dtype != ORC_BF16 && X->w_dtype != ORC_I8) return -1;
+  if (X->w_dtype < ORC_F32 || X->w_dtype > ORC_MXFP4) return -1;
+  if (X->w_dtype >= ORC_I8 && (!X->s1 || !X->s2 || (X->kind == ORC_SWIGLU && !X->s3))) return -1;
+  if (X->w_dtype == ORC_MXFP4 && (X->m % 32 || X->p % 32)) return -1;
   return 0;
 }
 

@@ -11,17 +11,23 @@
 
 #define ORC_MAX_E 64
 
-enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_I8 = 2 };
+enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_I8 = 2, ORC_FP8 = 3, ORC_MXFP4 = 4 };
 enum { ORC_RELU = 0, ORC_SWIGLU = 1 };
 
 /* Expert weights in canonical row-major layout:
  * w1 (ReLU MLP W1, or SwiGLU gate) [E][m][p], w3 (SwiGLU up) [E][m][p],
- * w2 (second / down) [E][p][m]; int8 scales s1, s3 [E][p], s2 [E][m]. */
+ * w2 (second / down) [E][p][m].  Scales: int8 and fp8 fp32 s1, s3 [E][p],
+ * s2 [E][m]; MXFP4 uint8 E8M0 s1, s3 [E][m/32][p], s2 [E][p/32][m]. */
 typedef struct {
   int m, p, E, kind, w_dtype;
   const void *w1, *w3, *w2;
-  const float *s1, *s3, *s2;
+  const void *s1, *s3, *s2;
 } orc_experts;
+
+/* One decoded weight (e, k, n) of a [E][K][N] projection in dtype, with its
+ * scales s (as in orc_experts). */
+int orc_weight_value(const void* w, const void* s, int dtype, int64_t e, int64_t K, int64_t N, int64_t k, int64_t n,
+                     double* out);
 
 int orc_router_logits(const void* x, int x_dtype, const float* wg, const float* bias, int T, int m, int E,
                       float* logits);

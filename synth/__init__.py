@@ -10,7 +10,8 @@ canonical row-major layouts the C ABI and the oracle both take:
     w1     [E][m][p]   first projection (ReLU MLP) or gate projection (SwiGLU)
     w3     [E][m][p]   up projection (SwiGLU only) or None
     w2     [E][p][m]   second / down projection
-    s1, s3 [E][p], s2 [E][m]   fp32 per-output-channel scales (int8 only)
+    s1, s3 [E][p], s2 [E][m]   fp32 per-output-channel scales (int8, int4, fp8)
+    s1, s3 [E][m/32][p], s2 [E][p/32][m]   uint8 E8M0 block scales (MXFP4)
 
 The generator is SplitMix64 in counter form with Box-Muller normals; see
 synth/gen.c.  Tensor stream ids: x=0, wg=1, w1=3, w3=4, w2=5.
@@ -68,6 +69,10 @@ def lib():
         L.synth_fill_int8_quant.restype = ctypes.c_int
         L.synth_fill_intq_quant.argtypes = [u64, u32, dbl, i64, i64, i64, ctypes.c_int, vp, vp]
         L.synth_fill_intq_quant.restype = ctypes.c_int
+        L.synth_fill_fp8_quant.argtypes = [u64, u32, dbl, i64, i64, i64, vp, vp]
+        L.synth_fill_fp8_quant.restype = ctypes.c_int
+        L.synth_fill_mxfp4_quant.argtypes = [u64, u32, dbl, i64, i64, i64, vp, vp]
+        L.synth_fill_mxfp4_quant.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -104,6 +109,26 @@ def int4_quant(seed: int, tid: int, sigma: float, E: int, K: int, N: int):
     return q, s
 
 
+def fp8_quant(seed: int, tid: int, sigma: float, E: int, K: int, N: int):
+    """OCP E4M3 codes (uint8) with per-output-channel fp32 scales, the
+    column's largest magnitude at 448."""
+    q = np.empty((E, K, N), dtype=np.uint8)
+    s = np.empty((E, N), dtype=np.float32)
+    if lib().synth_fill_fp8_quant(seed, tid, sigma, E, K, N, q.ctypes.data, s.ctypes.data) != 0:
+        raise MemoryError("synth_fill_fp8_quant failed")
+    return q, s
+
+
+def mxfp4_quant(seed: int, tid: int, sigma: float, E: int, K: int, N: int):
+    """MXFP4: E2M1 codes (one per uint8) and one E8M0 exponent (uint8) per
+    block of 32 consecutive k of a column, [E][K/32][N]."""
+    q = np.empty((E, K, N), dtype=np.uint8)
+    s = np.empty((E, K // 32, N), dtype=np.uint8)
+    if lib().synth_fill_mxfp4_quant(seed, tid, sigma, E, K, N, q.ctypes.data, s.ctypes.data) != 0:
+        raise MemoryError("synth_fill_mxfp4_quant failed")
+    return q, s
+
+
 def bf16_to_f32(a: np.ndarray) -> np.ndarray:
     """Exact widening of uint16 bf16 bit patterns to float32."""
     return (a.astype(np.uint32) << 16).view(np.float32)
@@ -125,7 +150,7 @@ class LayerSpec:
     k: int
     kind: str  # "relu" | "swiglu"
     x_dtype: str  # "f32" | "bf16"
-    w_dtype: str  # "f32" | "bf16" | "i8" | "i4"
+    w_dtype: str  # "f32" | "bf16" | "i8" | "i4" | "fp8" | "mxfp4"
     seed: int
     sigma_x: float = 1.0
     sigma_router: float = 0.02
@@ -136,7 +161,8 @@ class LayerSpec:
     def expert_bytes(self) -> int:
         """|E| of one expert: (mp + pm) * dtype for the two-matrix MLP, 3*m*p*dtype for SwiGLU."""
         nmat = 2 if self.kind == "relu" else 3
-        return int(nmat * self.m * self.p * {"f32": 4, "bf16": 2, "i8": 1, "i4": 0.5}[self.w_dtype])
+        return int(nmat * self.m * self.p * {"f32": 4, "bf16": 2, "i8": 1, "i4": 0.5, "fp8": 1,
+                                             "mxfp4": 0.5 + 1 / 32}[self.w_dtype])
 
 
 # The five measured layers.  Shapes follow Mixtral-8x7B (E=8, m=4096, p=14336)
@@ -162,6 +188,11 @@ CONFIGS = {
                     note="Mixtral-8x7B-shaped prefill, int8 weights with per-channel fp32 scales"),
     "c8": LayerSpec("mixtral_prefill_int4", 8192, 4096, 14336, 8, 2, "swiglu", "bf16", "i4", 7,
                     note="Mixtral-8x7B-shaped prefill, int4 weights with per-channel fp32 scales"),
+    # 8-bit and 4-bit float weights (OCP E4M3 with per-channel scales; MXFP4)
+    "c9": LayerSpec("mixtral_decode_fp8", 64, 4096, 14336, 8, 2, "swiglu", "bf16", "fp8", 8,
+                    note="Mixtral-8x7B-shaped decode, E4M3 weights with per-channel fp32 scales"),
+    "c10": LayerSpec("mixtral_decode_mxfp4", 64, 4096, 14336, 8, 2, "swiglu", "bf16", "mxfp4", 9,
+                     note="Mixtral-8x7B-shaped decode, MXFP4 weights (E2M1, E8M0 scale per 32 k)"),
 }
 
 
@@ -199,7 +230,7 @@ def make_layer(sp: LayerSpec, with_x: bool = True, with_weights: bool = True) ->
             elif sp.w_dtype == "bf16":
                 out[key] = normal_bf16(sp.seed, tid, sp.sigma_w, shape)
             else:
-                quant = int8_quant if sp.w_dtype == "i8" else int4_quant
+                quant = {"i8": int8_quant, "i4": int4_quant, "fp8": fp8_quant, "mxfp4": mxfp4_quant}[sp.w_dtype]
                 q, s = quant(sp.seed, tid, sp.sigma_w, *shape)
                 out[key] = q
                 out["s" + key[1:]] = s

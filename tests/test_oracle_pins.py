@@ -409,3 +409,148 @@ def test_norm_properties(orc):
     # bf16 rows read as the same values
     assert np.array_equal(orc.norm(_bf16_bits(x), orc.NORM_LAYER, one, zero, eps=1e-5),
                           orc.norm(x, orc.NORM_LAYER, one, zero, eps=1e-5))
+
+
+# --------------------------------------------------------------------------
+# float weight formats: OCP E4M3 (fp8) and MXFP4 (E2M1 + E8M0 per 32 k)
+# --------------------------------------------------------------------------
+
+def _formats():
+    with open(os.path.join(GOLDEN, "float_formats.json")) as f:
+        return json.load(f)
+
+
+def _num(v):
+    return float("nan") if v == "nan" else float(v)
+
+
+def test_fp8_decode_every_code_against_torch_and_the_definition(orc):
+    """All 256 E4M3 codes (scale 1) decode as torch's float8_e4m3fn does, and
+    the landmark codes of the format definition take their printed values."""
+    codes = np.arange(256, dtype=np.uint8).reshape(1, 1, 256)
+    ones = np.ones((1, 256), np.float32)
+    got = np.array([orc.weight_value(codes, ones, "fp8", 0, 0, n) for n in range(256)])
+    ref = torch.from_numpy(np.arange(256, dtype=np.uint8)).view(torch.float8_e4m3fn).double().numpy()
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(got[ok], ref[ok])
+    assert np.array_equal(np.signbit(got[ok]), np.signbit(ref[ok]))
+    for code, v in _formats()["e4m3_landmarks"].items():
+        g = got[int(code, 16)]
+        want = _num(v)
+        assert (math.isnan(g) and math.isnan(want)) or (g == want and math.copysign(1, g) == math.copysign(1, want)), code
+    # every finite magnitude is distinct and increasing with the code
+    pos = got[:0x7F]
+    assert np.all(np.diff(pos) > 0) and pos.max() == 448.0
+
+
+def test_fp8_scale_is_per_output_channel(orc):
+    rng = np.random.default_rng(5)
+    E, K, N = 2, 6, 5
+    codes = rng.integers(0, 0x7F, size=(E, K, N)).astype(np.uint8)
+    codes[0, 1, 2] |= 0x80
+    s = rng.random((E, N)).astype(np.float32) + 0.25
+    dec = torch.from_numpy(codes.copy()).view(torch.float8_e4m3fn).double().numpy()
+    for e in range(E):
+        for k in range(K):
+            for n in range(N):
+                assert orc.weight_value(codes, s, "fp8", e, k, n) == dec[e, k, n] * float(s[e, n])
+
+
+def test_mxfp4_decode_every_code_and_block_scales(orc):
+    """E2M1 codes decode to the MX specification's value table; the E8M0 scale
+    (decoded by torch's float8_e8m0fnu) applies to the block of 32
+    consecutive k of one column that holds the weight."""
+    F = _formats()
+    table = np.array(F["e2m1_values"])
+    E, K, N = 2, 96, 4
+    rng = np.random.default_rng(3)
+    codes = rng.integers(0, 16, size=(E, K, N)).astype(np.uint8)
+    codes[0, :16, 0] = np.arange(16)  # every code once
+    xs = rng.integers(100, 150, size=(E, K // 32, N)).astype(np.uint8)
+    xs[1, 2, 3] = 127
+    scale = torch.from_numpy(xs.copy()).view(torch.float8_e8m0fnu).double().numpy()
+    for e in range(E):
+        for k in range(K):
+            for n in range(N):
+                want = table[codes[e, k, n]] * scale[e, k // 32, n]
+                got = orc.weight_value(codes, xs, "mxfp4", e, k, n)
+                assert got == want and math.copysign(1, got) == math.copysign(1, want), (e, k, n)
+    for E8, v in F["e8m0_landmarks"].items():
+        dec = torch.tensor([int(E8)], dtype=torch.uint8).view(torch.float8_e8m0fnu).double().item()
+        assert (math.isnan(dec) and v == "nan") or dec == _num(v), E8
+
+
+@pytest.mark.parametrize("kind", ["relu", "swiglu"])
+@pytest.mark.parametrize("w_dtype", ["fp8", "mxfp4"])
+def test_single_float_weight_expert_is_dense_mlp(orc, syn, kind, w_dtype):
+    """E = 1, k = 1 equals the torch fp64 chain on the weights dequantised
+    with torch's decoders (fp8) or the MX table and torch's E8M0 decode."""
+    L = _layer(syn, 9, 64, 96, 1, 1, kind, w_dtype, seed=78)
+    X = orc.Experts.from_layer(L)
+    r = orc.layer_forward(X, L["x"], L["wg"], None, 1)
+    table = torch.tensor(_formats()["e2m1_values"], dtype=torch.float64)
+
+    def deq(key):
+        codes, s = L[key][0], L["s" + key[1:]][0]
+        if w_dtype == "fp8":
+            return torch.from_numpy(codes.copy()).view(torch.float8_e4m3fn).double() * \
+                torch.from_numpy(s.astype(np.float64))[None, :]
+        sc = torch.from_numpy(s.copy()).view(torch.float8_e8m0fnu).double()
+        return table[torch.from_numpy(codes.astype(np.int64))] * sc.repeat_interleave(32, dim=0)
+
+    x = torch.from_numpy(_to64(syn, L["x"]))
+    if kind == "relu":
+        ref = torch.relu(x @ deq("w1")) @ deq("w2")
+    else:
+        ref = (torch.nn.functional.silu(x @ deq("w1")) * (x @ deq("w3"))) @ deq("w2")
+    assert np.allclose(r["y"], ref.numpy(), rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("w_dtype", ["fp8", "mxfp4"])
+@pytest.mark.parametrize("E,k", [(3, 2), (8, 2), (8, 8)])
+def test_float_weights_routed_equals_dense_masked(orc, syn, w_dtype, E, k):
+    L = _layer(syn, 8, 64, 64, E, k, "swiglu", w_dtype, seed=E * 11 + k)
+    X = orc.Experts.from_layer(L)
+    r = orc.layer_forward(X, L["x"], L["wg"], None, k)
+    assert np.array_equal(r["y"], orc.dense_masked(X, L["x"], r["idx"], r["w"]))
+
+
+def test_fp8_quantisation_closed_forms(syn):
+    """Per output channel s = max|W| / 448 and the largest code decodes to
+    +-448; every code is within half an E4M3 step of W / s (steps 2^(e-3) for
+    normals, 2^-9 below 2^-6), as torch's round-to-nearest cast of W / s."""
+    E, K, N = 2, 64, 48
+    q, s = syn.fp8_quant(9, syn.TID_W1, 0.02, E, K, N)
+    W = syn.normal_f32(9, syn.TID_W1, 0.02, (E, K, N)).astype(np.float64)
+    dec = torch.from_numpy(q.copy()).view(torch.float8_e4m3fn).double().numpy()
+    assert np.allclose(s, (np.abs(W).max(axis=1) / 448).astype(np.float32), rtol=0, atol=0)
+    assert np.all(np.abs(dec).max(axis=1) == 448.0)
+    v = W / s[:, None, :].astype(np.float64)
+    a = np.abs(v)
+    step = np.where(a < 2.0**-6, 2.0**-9, 2.0 ** (np.floor(np.log2(np.maximum(a, 2.0**-6))) - 3))
+    assert np.all(np.abs(v - dec) <= step / 2 * (1 + 1e-12))
+    cast = torch.from_numpy(v).to(torch.float8_e4m3fn).double().numpy()
+    assert np.array_equal(dec, cast)
+
+
+def test_mxfp4_quantisation_closed_forms(syn):
+    """Per block of 32 k of a column: shared exponent floor(log2 max|W|) - 2
+    (E8M0 = it + 127), elements the nearest E2M1 value of W / 2^X (saturated
+    at 6), so within half an E2M1 step of it."""
+    E, K, N = 2, 96, 24
+    q, xs = syn.mxfp4_quant(9, syn.TID_W1, 0.02, E, K, N)
+    W = syn.normal_f32(9, syn.TID_W1, 0.02, (E, K, N)).astype(np.float64)
+    table = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+    amax = np.abs(W).reshape(E, K // 32, 32, N).max(axis=2)
+    X = np.floor(np.log2(amax)) - 2
+    assert np.array_equal(xs.astype(np.int64), (X + 127).astype(np.int64))
+    v = W / np.repeat(2.0**X, 32, axis=1)
+    mag = table[q & 7]
+    sign = np.where(q & 8, -1.0, 1.0)
+    dec = sign * mag
+    a = np.abs(v)
+    step = np.where(a < 2, 0.5, np.where(a < 4, 1.0, 2.0))
+    err = np.abs(v - dec)
+    assert np.all((err <= step / 2 * (1 + 1e-12)) | ((a > 6) & (mag == 6)))
+    assert np.all(q < 16)
