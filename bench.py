@@ -12,8 +12,8 @@ one JSON line for it, with the roofline position of its dominant kernel
 (timed with HIP events around its launches on the launch stream) and the CPU
 oracle timed on a bounded sample of the same layer.  Beside it, under
 "configs", the same figures for the other measured layers (tiny fp32,
-Mixtral decode, Phi-3.5 skewed, Mixtral int8 and int4 decode, Mixtral int8
-and int4 prefill).
+Mixtral decode, Phi-3.5 skewed, Mixtral int8, int4, fp8 and MXFP4 decode,
+Mixtral int8 and int4 prefill).
 
   python bench.py [--steps K] [--warmup W]            headline + every layer
   python bench.py --workload c2 [--steps K]           one layer only
@@ -36,7 +36,7 @@ HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
 METRIC = "MoE layer tokens/s; achieved HBM GB/s (T≤64) or MFMA TFLOP/s (T≥4096)"
 HEADLINE = "c4"
-OTHERS = ["c1", "c2", "c3", "c5", "c6", "c7", "c8"]
+OTHERS = ["c1", "c2", "c3", "c5", "c6", "c7", "c8", "c9", "c10"]
 TRAFFIC_DIR = os.path.join(ROOT, "profiles")
 _CSRC = "mixture_experts_layer_gemv_amd/csrc/"
 _SKINNY = [_CSRC + f for f in
@@ -56,7 +56,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=None,
-                    help="time only this layer (c1..c8); default: the prefill layer with every other layer beside it")
+                    help="time only this layer (c1..c10); default: the prefill layer with every other layer beside it")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
@@ -84,12 +84,12 @@ def algorithmic(sp, counts):
     Activation bytes: x read, hidden H written and read back (bf16), y
     written.  Flops: 2*m*p per row per m x p matrix (the pages' |O| rounds to
     this)."""
-    wb = {"f32": 4, "bf16": 2, "i8": 1, "i4": 0.5}[sp.w_dtype]
+    wb = {"f32": 4, "bf16": 2, "i8": 1, "i4": 0.5, "fp8": 1, "mxfp4": 0.5 + 1 / 32}[sp.w_dtype]
     ab = 4 if sp.x_dtype == "f32" else 2
     G = 2 if sp.kind == "swiglu" else 1
     touched = sum(1 for c in counts if c > 0)
     rows = sp.T * sp.k
-    q = sp.w_dtype in ("i8", "i4")
+    q = sp.w_dtype in ("i8", "i4", "fp8")  # fp32 per-channel scales (MXFP4's block scales are in wb)
     up_w = int(touched * G * sp.m * sp.p * wb) + (touched * G * sp.p * 4 if q else 0)
     dn_w = int(touched * sp.p * sp.m * wb) + (touched * sp.m * 4 if q else 0)
     h_bytes = rows * sp.p * (4 if sp.w_dtype == "f32" else 2)
@@ -267,7 +267,7 @@ def measure(key, args, headline):
     roof["launch_us"] = dom_us
     out.update({
         "ms_per_step_with_kernel_events": round(ms_events, 5),
-        "dtype": {"f32": "f32", "bf16": "bf16", "i8": "bf16", "i4": "bf16"}[sp.w_dtype],
+        "dtype": {"f32": "f32", "bf16": "bf16", "i8": "bf16", "i4": "bf16", "fp8": "bf16", "mxfp4": "bf16"}[sp.w_dtype],
         "config": {"workload": sp.name, "T": sp.T, "m": sp.m, "p": sp.p, "E": sp.E, "k": sp.k, "expert": sp.kind,
                    "weights": sp.w_dtype, "activations": sp.x_dtype, "parallelism": "none (1 GPU)"},
         "roofline": roof,

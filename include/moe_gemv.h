@@ -27,10 +27,10 @@
  *    if every in-flight call has its own workspace.
  *  - Shape limits: 1 <= E <= 64, 1 <= k <= E, m and p positive multiples of
  *    64, T*k < 2^31.  T == 0 is a successful no-op.
- *  - Supported (activation / weight / expert) combinations: F32/F32/RELU,
- *    F32/F32/SWIGLU, BF16/BF16/RELU, BF16/BF16/SWIGLU, BF16/I8/SWIGLU,
- *    BF16/I8/RELU, BF16/I4/SWIGLU, BF16/I4/RELU (I4: m and p multiples of
- *    128).  Anything else returns MOE_ERR_UNSUPPORTED.
+ *  - Supported (activation / weight / expert) combinations: F32/F32 and
+ *    BF16/BF16 with either expert kind; BF16 activations with I8, I4, FP8 or
+ *    MXFP4 weights and either expert kind (I4 and MXFP4: m and p multiples
+ *    of 128).  Anything else returns MOE_ERR_UNSUPPORTED.
  */
 #ifndef MOE_GEMV_H
 #define MOE_GEMV_H
@@ -51,7 +51,7 @@ typedef enum {
   MOE_ERR_OOM = 5          /* device allocation failed */
 } moe_status;
 
-typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_I8 = 2, MOE_I4 = 3 } moe_dtype;
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_I8 = 2, MOE_I4 = 3, MOE_FP8 = 4, MOE_MXFP4 = 5 } moe_dtype;
 typedef enum { MOE_MLP_RELU = 0, MOE_SWIGLU = 1 } moe_ffn_kind;
 
 #define MOE_MAX_EXPERTS 64
@@ -78,21 +78,26 @@ int moe_abi_version(void);
  *  m, p, E       hidden size, expert inner size, number of experts.
  *  kind          MOE_MLP_RELU (w1 = W1, w2 = W2, w_up must be NULL) or
  *                MOE_SWIGLU (w1 = gate W1, w_up = up W3, w2 = down W2).
- *  w_dtype       MOE_F32, MOE_BF16, MOE_I8 or MOE_I4.
+ *  w_dtype       MOE_F32, MOE_BF16, MOE_I8, MOE_I4, MOE_FP8 or MOE_MXFP4.
  *  w1, w_up      device [E][m][p] in w_dtype (MOE_I4: one int8 per weight,
- *                holding q in [-8, 7]; stored packed two per byte).
- *  w2            device [E][p][m] in w_dtype (MOE_I4 as above).
- *  s1, s_up      MOE_I8 / MOE_I4 only: device fp32 [E][p] per-output-channel
- *                scales of w1 and w_up (the weight is q * s); NULL otherwise.
- *  s2            MOE_I8 / MOE_I4 only: device fp32 [E][m] scales of w2; NULL
- *                otherwise.
+ *                holding q in [-8, 7], stored packed two per byte; MOE_FP8:
+ *                one OCP E4M3 code per byte; MOE_MXFP4: one E2M1 code per
+ *                byte in its low nibble, stored packed two per byte).
+ *  w2            device [E][p][m] in w_dtype (as above).
+ *  s1, s_up      MOE_I8 / MOE_I4 / MOE_FP8: device fp32 [E][p] per-output-
+ *                channel scales of w1 and w_up (the weight is q * s, or
+ *                e4m3(code) * s).  MOE_MXFP4: device uint8 [E][m/32][p] E8M0
+ *                exponents, one per block of 32 consecutive rows k of a column
+ *                (the weight is e2m1(code) * 2^(X - 127)); the kernels are
+ *                exact for X in [27, 227].  NULL for bf16 and fp32.
+ *  s2            the same for w2: fp32 [E][m], or uint8 [E][p/32][m].
  *  stream        packing runs on this stream; the call synchronises it
  *                before returning, so the inputs may be freed afterwards.
  *  out           receives the handle; release it with moe_weights_destroy.
  * Errors: INVALID_ARG, UNSUPPORTED, OOM, HIP.  On error *out is NULL.
  */
 moe_status moe_weights_create(int m, int p, int E, int kind, int w_dtype, const void* w1, const void* w_up,
-                              const void* w2, const float* s1, const float* s_up, const float* s2, void* stream,
+                              const void* w2, const void* s1, const void* s_up, const void* s2, void* stream,
                               moe_weights** out);
 
 /* Free a handle from moe_weights_create (NULL is accepted).  Synchronises the device. */

@@ -17,7 +17,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe_gemv.so")
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP, MOE_ERR_OOM = range(6)
-MOE_F32, MOE_BF16, MOE_I8, MOE_I4 = 0, 1, 2, 3
+MOE_F32, MOE_BF16, MOE_I8, MOE_I4, MOE_FP8, MOE_MXFP4 = 0, 1, 2, 3, 4, 5
 MOE_MLP_RELU, MOE_SWIGLU = 0, 1
 MOE_ROUTE_LOGITS_IN = 1
 MOE_NORM_NONE, MOE_NORM_LAYER, MOE_NORM_RMS = 0, 1, 2

@@ -33,9 +33,11 @@ struct moe_weights {
   void* up = nullptr;    // packed gate(+up) [E][p/16][U][G] (bf16/int), or fp32 w1 [E][m][p]
   void* up3 = nullptr;   // fp32 SwiGLU only: w3 [E][m][p]
   void* down = nullptr;  // packed down [E][m/16][U][1] (bf16/int), or fp32 w2 [E][p][m]
-  float* s_gate = nullptr;
+  float* s_gate = nullptr;         // int8 / int4 / fp8: per-channel scales
   float* s_up = nullptr;
   float* s_down = nullptr;
+  uint32_t* mx_up = nullptr;       // MXFP4: packed block scales of the gate(+up) projection
+  uint32_t* mx_down = nullptr;     // and of the down projection
 };
 
 namespace {
@@ -106,20 +108,32 @@ moe_status check_shape(int T, int m, int p, int E, int k) {
   return MOE_OK;
 }
 
-bool valid_dtype(int d) { return d == MOE_F32 || d == MOE_BF16 || d == MOE_I8 || d == MOE_I4; }
+bool valid_dtype(int d) { return d >= MOE_F32 && d <= MOE_MXFP4; }
 
-// Integer weights (int8 or int4, with per-output-channel scales).
-bool quantised(int d) { return d == MOE_I8 || d == MOE_I4; }
+// Quantised weights (int8, int4, fp8 or MXFP4, each with its scales).
+bool quantised(int d) { return d == MOE_I8 || d == MOE_I4 || d == MOE_FP8 || d == MOE_MXFP4; }
 
-// Weight bits of the kernels' variants: 0 (bf16), 8 or 4.
-int weight_bits(const LayerCfg& c) { return c.w_dtype == MOE_I8 ? 8 : (c.w_dtype == MOE_I4 ? 4 : 0); }
+// Weight-kind code of the kernels' variants: 0 bf16, 8 int8, 9 fp8, 4 int4,
+// 5 MXFP4 (the tens of bits of a weight, and which of its kinds).
+int weight_code(int d) {
+  switch (d) {
+    case MOE_I8: return 8;
+    case MOE_FP8: return 9;
+    case MOE_I4: return 4;
+    case MOE_MXFP4: return 5;
+    default: return 0;
+  }
+}
+int weight_bits(const LayerCfg& c) { return weight_code(c.w_dtype); }
+// Narrow (4-bit) weights.
+bool nibbles(int d) { return d == MOE_I4 || d == MOE_MXFP4; }
 
 moe_status check_layer(int m, int p, int E, int kind, int w_dtype) {
   if (moe_status rc = check_shape(1, m, p, E, 1)) return rc;
   if (kind != MOE_MLP_RELU && kind != MOE_SWIGLU) return fail(MOE_ERR_INVALID_ARG, "unknown expert kind %d", kind);
   if (!valid_dtype(w_dtype)) return fail(MOE_ERR_UNSUPPORTED, "weight dtype %d unsupported", w_dtype);
-  if (w_dtype == MOE_I4 && (m % 128 || p % 128))
-    return fail(MOE_ERR_UNSUPPORTED, "int4 weights need m=%d and p=%d to be multiples of 128", m, p);
+  if (nibbles(w_dtype) && (m % 128 || p % 128))
+    return fail(MOE_ERR_UNSUPPORTED, "4-bit weights need m=%d and p=%d to be multiples of 128", m, p);
   return MOE_OK;
 }
 
@@ -143,7 +157,7 @@ moe_status check_combo(int x_dtype, int w_dtype) {
   if (w_dtype == MOE_F32 && x_dtype != MOE_F32)
     return fail(MOE_ERR_UNSUPPORTED, "fp32 weights need fp32 activations");
   if (w_dtype != MOE_F32 && x_dtype != MOE_BF16)
-    return fail(MOE_ERR_UNSUPPORTED, "bf16/int8/int4 weights need bf16 activations");
+    return fail(MOE_ERR_UNSUPPORTED, "bf16/int8/int4/fp8/MXFP4 weights need bf16 activations");
   return MOE_OK;
 }
 
@@ -165,7 +179,7 @@ bool tuned_on(int v, bool dflt) { return v == 0 ? dflt : v > 0; }
 // The GEMM addresses packed activations and one projection's packed weights
 // with 32-bit byte offsets from a uniform base.
 bool gemm_fits(const LayerCfg& c, int T, int k) {
-  if (c.w_dtype == MOE_F32) return false;
+  if (c.w_dtype == MOE_F32 || c.w_dtype == MOE_FP8 || c.w_dtype == MOE_MXFP4) return false;
   const unsigned long long lim = 1ull << 32;
   const int qb = weight_bits(c);
   const unsigned long long G = c.kind == MOE_SWIGLU ? 2 : 1;
@@ -244,7 +258,7 @@ int down_ksplit(const LayerCfg& c, long long items) {
 // the decode layers.
 int skinny_ct(int mt, int qb, int g, int forced) {
   if (forced > 0) return forced >= 4 ? 4 : (forced >= 2 ? 2 : 1);
-  const int aw = mt * (qb == 8 ? 2 : (qb == 4 ? 4 : 1));
+  const int aw = mt * (qb >= 8 ? 2 : (qb >= 4 ? 4 : 1));
   if (aw <= 1 && g > 1) return 1;
   if (mt >= 4) return 2;
   return 4;
@@ -452,6 +466,7 @@ moe_status run_skinny(const moe_weights* W, const FfnIo& io, hipStream_t s) {
   a.w = W->up;
   a.scale0 = W->s_gate;
   a.scale1 = W->s_up;
+  a.mx = W->mx_up;
   a.act = static_cast<const uint16_t*>(packed ? io.xp : io.x);
   a.h_out = static_cast<uint16_t*>(io.h);
   a.K = m;
@@ -502,6 +517,7 @@ moe_status run_skinny(const moe_weights* W, const FfnIo& io, hipStream_t s) {
   a.w = W->down;
   a.scale0 = W->s_down;
   a.scale1 = nullptr;
+  a.mx = W->mx_down;
   a.act = static_cast<const uint16_t*>(io.h);
   a.h_out = nullptr;
   a.f_out = io.down_out;
@@ -606,7 +622,7 @@ const char* moe_last_error(void) { return g_err.c_str(); }
 int moe_abi_version(void) { return 2; }
 
 moe_status moe_weights_create(int m, int p, int E, int kind, int w_dtype, const void* w1, const void* w_up,
-                              const void* w2, const float* s1, const float* s_up, const float* s2, void* stream,
+                              const void* w2, const void* s1, const void* s_up, const void* s2, void* stream,
                               moe_weights** out) {
   if (!out) return fail(MOE_ERR_INVALID_ARG, "out is NULL");
   *out = nullptr;
@@ -615,9 +631,10 @@ moe_status moe_weights_create(int m, int p, int E, int kind, int w_dtype, const 
   if (!w1 || !w2 || (swiglu && !w_up)) return fail(MOE_ERR_INVALID_ARG, "required weight pointer is NULL");
   if (!swiglu && w_up) return fail(MOE_ERR_INVALID_ARG, "w_up must be NULL for the ReLU MLP");
   const bool i8 = quantised(w_dtype);
-  const int qb = w_dtype == MOE_I8 ? 8 : (w_dtype == MOE_I4 ? 4 : 0);
-  if (i8 && (!s1 || !s2 || (swiglu && !s_up))) return fail(MOE_ERR_INVALID_ARG, "integer weights need their scales");
-  if (!i8 && (s1 || s2 || s_up)) return fail(MOE_ERR_INVALID_ARG, "scales are only for integer weights");
+  const bool mx = w_dtype == MOE_MXFP4;
+  const int qb = weight_code(w_dtype);
+  if (i8 && (!s1 || !s2 || (swiglu && !s_up))) return fail(MOE_ERR_INVALID_ARG, "quantised weights need their scales");
+  if (!i8 && (s1 || s2 || s_up)) return fail(MOE_ERR_INVALID_ARG, "scales are only for quantised weights");
   if (!aligned16(w1) || !aligned16(w2) || (w_up && !aligned16(w_up)) || (s1 && !aligned16(s1)) ||
       (s2 && !aligned16(s2)) || (s_up && !aligned16(s_up)))
     return fail(MOE_ERR_INVALID_ARG, "weight pointers must be 16-byte aligned");
@@ -632,7 +649,10 @@ moe_status moe_weights_create(int m, int p, int E, int kind, int w_dtype, const 
   } else {
     up_b = moe::packed_bytes(E, m, p, G, qb);
     dn_b = moe::packed_bytes(E, p, m, 1, qb);
-    if (i8) sc_b = align256((size_t)E * p * 4) * (swiglu ? 2 : 1) + align256((size_t)E * m * 4);
+    if (mx)
+      sc_b = align256(moe::packed_mx_scale_bytes(E, m, p, G)) + align256(moe::packed_mx_scale_bytes(E, p, m, 1));
+    else if (i8)
+      sc_b = align256((size_t)E * p * 4) * (swiglu ? 2 : 1) + align256((size_t)E * m * 4);
   }
   const size_t total = align256(up_b) + align256(up3_b) + align256(dn_b) + sc_b;
   moe_weights* W = new (std::nothrow) moe_weights;
@@ -663,11 +683,22 @@ moe_status moe_weights_create(int m, int p, int E, int kind, int w_dtype, const 
     e = hipMemcpyAsync(W->up, w1, up_b, hipMemcpyDeviceToDevice, s);
     if (e == hipSuccess && swiglu) e = hipMemcpyAsync(W->up3, w_up, up3_b, hipMemcpyDeviceToDevice, s);
     if (e == hipSuccess) e = hipMemcpyAsync(W->down, w2, dn_b, hipMemcpyDeviceToDevice, s);
+  } else if (mx) {
+    W->mx_up = static_cast<uint32_t*>(carve(moe::packed_mx_scale_bytes(E, m, p, G)));
+    W->mx_down = static_cast<uint32_t*>(carve(moe::packed_mx_scale_bytes(E, p, m, 1)));
+    const uint8_t* const c1 = static_cast<const uint8_t*>(w1);
+    e = moe::launch_pack_fp4(c1, W->up, E, m, p, G, 0, s);
+    if (e == hipSuccess && swiglu) e = moe::launch_pack_fp4(static_cast<const uint8_t*>(w_up), W->up, E, m, p, G, 1, s);
+    if (e == hipSuccess) e = moe::launch_pack_fp4(static_cast<const uint8_t*>(w2), W->down, E, p, m, 1, 0, s);
+    if (e == hipSuccess) e = moe::launch_pack_mx_scales(static_cast<const uint8_t*>(s1), W->mx_up, E, m, p, G, 0, s);
+    if (e == hipSuccess && swiglu)
+      e = moe::launch_pack_mx_scales(static_cast<const uint8_t*>(s_up), W->mx_up, E, m, p, G, 1, s);
+    if (e == hipSuccess) e = moe::launch_pack_mx_scales(static_cast<const uint8_t*>(s2), W->mx_down, E, p, m, 1, 0, s);
   } else if (i8) {
     W->s_gate = static_cast<float*>(carve((size_t)E * p * 4));
     if (swiglu) W->s_up = static_cast<float*>(carve((size_t)E * p * 4));
     W->s_down = static_cast<float*>(carve((size_t)E * m * 4));
-    auto pack = qb == 8 ? moe::launch_pack_i8 : moe::launch_pack_i4;
+    auto pack = qb == 4 ? moe::launch_pack_i4 : moe::launch_pack_i8;  // (fp8 codes move as bytes, like int8)
     e = pack(static_cast<const int8_t*>(w1), W->up, E, m, p, G, 0, s);
     if (e == hipSuccess && swiglu) e = pack(static_cast<const int8_t*>(w_up), W->up, E, m, p, G, 1, s);
     if (e == hipSuccess) e = pack(static_cast<const int8_t*>(w2), W->down, E, p, m, 1, 0, s);

@@ -51,8 +51,42 @@ __device__ __forceinline__ bf16x8_t u4x8_to_bf16_biased(uint32_t d) {
 constexpr float kI4Bias = 136.0f;  // 128 from the bf16 pattern + 8 from the storage offset
 
 
-// Weight bits of a kernel variant: 0 (bf16), 8 (int8) or 4 (int4).  A
-// lane's 16-byte load of packed weights covers q_ah(qb) MFMA K steps of 32.
-constexpr int q_ah(int qb) { return qb == 8 ? 2 : (qb == 4 ? 4 : 1); }
+// 8 OCP E4M3 codes (two dwords, byte j = value j) -> 8 bf16, exactly (every
+// E4M3 value is a bf16 value): the hardware conversion of two codes at a
+// time, scale 1 (the per-channel scale is applied in the epilogue).
+__device__ __forceinline__ bf16x8_t fp8x8_to_bf16(uint32_t lo, uint32_t hi) {
+  cvt_u32x4_t r;
+  r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false));
+  r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true));
+  r[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false));
+  r[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true));
+  return __builtin_bit_cast(bf16x8_t, r);
+}
+
+// 8 E2M1 codes (one dword, byte b holding values 2b in its low and 2b+1 in
+// its high nibble) times their block's scale -> 8 bf16: the hardware
+// conversion of one byte at a time with the E8M0 scale applied, exact while
+// the scaled values stay inside bf16's normal range (block exponents
+// 2^-100 .. 2^100 leave a wide margin).
+__device__ __forceinline__ bf16x8_t fp4x8_to_bf16(uint32_t d, float scale) {
+  cvt_u32x4_t r;
+  r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, scale, 0));
+  r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, scale, 1));
+  r[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, scale, 2));
+  r[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, scale, 3));
+  return __builtin_bit_cast(bf16x8_t, r);
+}
+
+// The E8M0 exponent E in byte h of a scale dword as the fp32 2^(E - 127)
+// (E in 1 .. 254).
+__device__ __forceinline__ float e8m0_at(uint32_t d, int h) { return __uint_as_float(((d >> (8 * h)) & 255u) << 23); }
+
+// Weight kinds of the kernel variants, by their code qb: 0 bf16, 8 int8,
+// 9 fp8 (E4M3), 4 int4, 5 MXFP4 (E2M1 with E8M0 block scales).  A lane's
+// 16-byte load of packed weights covers q_ah(qb) MFMA K steps of 32.
+constexpr int q_bits(int qb) { return qb >= 8 ? 8 : (qb >= 4 ? 4 : 16); }
+constexpr int q_ah(int qb) { return qb >= 8 ? 2 : (qb >= 4 ? 4 : 1); }
+// per-output-channel scales applied in the epilogue (int8, fp8, int4)
+constexpr bool q_chan_scale(int qb) { return qb == 8 || qb == 9 || qb == 4; }
 
 }  // namespace moe

@@ -16,14 +16,14 @@
 // permutation, for the up projection) or by the up projection's epilogue
 // (the hidden rows, for the down projection).  Gathering rows in place
 // instead (16 rows x 64 bytes per copy, rows a multiple of 4 KiB apart)
-// halves the copy rate.  Fragments stream through a 5-stage LDS ring of
-// 32 KiB stages (32 k each; all 160 KiB of a CU's LDS), copied global -> LDS
+// halves the copy rate.  Fragments stream through a 4-stage LDS ring of
+// 32 KiB stages (32 k each), copied global -> LDS
 // with global_load_lds_dwordx4 (lane l of a copy lands at base + 16 l): each
 // copy is one contiguous 1 KiB read, and each wave reads a fragment with one
 // conflict-free 16-byte ds_read per lane.  The two waves of each SIMD take
 // turns: one multiplies the stage it holds in registers while the other reads
-// its next stage and issues copies (ping-pong, two barriers per step); four
-// to five stages of copies stay in flight.
+// its next stage and issues copies (ping-pong, two barriers per step); three
+// to four stages of copies stay in flight.
 // Workgroups run expert by expert, in groups of A.cg (4) column blocks x all
 // of the expert's row blocks, on one XCD at a time: the ~32 resident
 // workgroups then read ~8 activation tiles and ~4 weight tiles per stage,
@@ -61,7 +61,10 @@ struct GemmShape {
   static constexpr int NAF = BM / 16 * AH;       // activation fragments per stage
   static constexpr int NBF = 16;                 // weight fragments per stage
   static constexpr int STAGE_KB = NAF + NBF;     // KiB per stage
-  static constexpr int STAGES = 160 / STAGE_KB;  // ring depth: 5 (bf16) or 3 (int8, int4)
+  // ring depth: 4 stages of 32 KiB for bf16 (measured ahead of 5, which
+  // fills the LDS, and of 3: 3.24 against 3.32 and 3.38 ms for the Mixtral
+  // prefill up projection); 3 of 48 KiB for int8 and int4
+  static constexpr int STAGES = QB == 0 ? 4 : 160 / STAGE_KB;
   static constexpr int CPA = NAF / 8;            // activation copies per wave and stage
   static constexpr int CPB = NBF / 8;            // weight copies per wave and stage
   static constexpr int CPS = CPA + CPB;          // copies per wave and stage

@@ -88,11 +88,11 @@ constexpr Plan plan(int mt, int g, int ct, int qb, bool sa) {
   const int act = mt * q_ah(qb) * 4;  // one K unit of activations
   // with shared activations (sa) only the weights are in flight in
   // registers; the unit being consumed is read from LDS
-  const int stage = ct * g * 4 + (sa ? 0 : act);
+  const int stage = ct * g * 4 + (qb == 5 ? ct * g : 0) + (sa ? 0 : act);
   // addresses, loop state, int8 conversion (and, shared, the unit read from LDS)
   // (int4 with per-wave activations: the converted weights of later units
   // are held too)
-  const int fixed = (qb == 4 ? (sa ? 72 : 128) : (qb ? 64 : 40)) + (sa ? act + (qb ? 8 : 0) : 0);
+  const int fixed = (q_bits(qb) == 4 ? (sa ? 72 : 128) : (qb ? 64 : 40)) + (sa ? act + (qb ? 8 : 0) : 0);
   // shared activations: DA = depth + 1 units of the ring in at most 64 KiB,
   // so two workgroups fit a CU's LDS
   const int dmax0 = sa ? 64 / (mt * q_ah(qb)) - 1 : 6;
@@ -282,6 +282,9 @@ __device__ __forceinline__ void skinny_body(const SkinnyArgs& A, const SkinnyWor
       for (int mt = 0; mt < MT; ++mt) acc[c][g][mt] = floatx4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
   u32x4_t wb[D][CT][G];
+  uint32_t sbw[QB == 5 ? D : 1][CT][G];  // MXFP4: the lane's column's block scales of a unit (byte h: step h)
+  const uint32_t* const mxp = QB == 5 ? A.mx + (size_t)(e * NB + ltile) * U * G * 16 + (lane & 15) : nullptr;
+  const size_t mx_tile_stride = (size_t)U * G * 16;
   u32x4_t ab[SA ? 1 : D][MT][AH];
 
   // Shared activations: this wave's copies (fragment, uniform source of
@@ -309,6 +312,11 @@ __device__ __forceinline__ void skinny_body(const SkinnyArgs& A, const SkinnyWor
   do {                                                                                                 \
     _Pragma("unroll") for (int c = 0; c < CT; ++c) _Pragma("unroll") for (int g = 0; g < G; ++g)      \
         wb[slot][c][g] = __builtin_nontemporal_load(wp + c * tile_stride + ((size_t)(u) * G + g) * 64); \
+    if constexpr (QB == 5) {                                                                           \
+      _Pragma("unroll") for (int c = 0; c < CT; ++c) _Pragma("unroll") for (int g = 0; g < G; ++g)    \
+          sbw[slot % (QB == 5 ? D : 1)][c][g] =                                                       \
+              __builtin_nontemporal_load(mxp + c * mx_tile_stride + ((size_t)(u) * G + g) * 16);      \
+    }                                                                                                  \
     if constexpr (SA) {                                                                                \
       _Pragma("unroll") for (int j = 0; j < CPW; ++j) if (j < NC)                                      \
           copy_frag(sa_src[j] + (size_t)(u) * (AH * 1024), 16u * lane,                                 \
@@ -338,11 +346,20 @@ __device__ __forceinline__ void skinny_body(const SkinnyArgs& A, const SkinnyWor
   do {                                                                                                 \
     MOE_ACT_FETCH(slot, u, after)                                                                      \
     _Pragma("unroll") for (int c = 0; c < CT; ++c) {                                                   \
-      if constexpr (QB == 8) {                                                                         \
+      if constexpr (QB == 8 || QB == 9) {                                                              \
         _Pragma("unroll") for (int h = 0; h < 2; ++h) {                                                \
           _Pragma("unroll") for (int g = 0; g < G; ++g) {                                              \
             const u32x4_t q = wb[slot][c][g];                                                          \
-            const bf16x8_t bw = h == 0 ? i8x8_to_bf16(q[0], q[1]) : i8x8_to_bf16(q[2], q[3]);          \
+            const bf16x8_t bw = QB == 9 ? (h == 0 ? fp8x8_to_bf16(q[0], q[1]) : fp8x8_to_bf16(q[2], q[3])) \
+                                        : (h == 0 ? i8x8_to_bf16(q[0], q[1]) : i8x8_to_bf16(q[2], q[3])); \
+            _Pragma("unroll") for (int mt = 0; mt < MT; ++mt) acc[c][g][mt] =                          \
+                __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(MOE_ACT(slot, mt, h)), bw, acc[c][g][mt], 0, 0, 0); \
+          }                                                                                            \
+        }                                                                                              \
+      } else if constexpr (QB == 5) {                                                                  \
+        _Pragma("unroll") for (int h = 0; h < 4; ++h) {                                                \
+          _Pragma("unroll") for (int g = 0; g < G; ++g) {                                              \
+            const bf16x8_t bw = fp4x8_to_bf16(wb[slot][c][g][h], e8m0_at(sbw[slot % (QB == 5 ? D : 1)][c][g], h)); \
             _Pragma("unroll") for (int mt = 0; mt < MT; ++mt) acc[c][g][mt] =                          \
                 __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(MOE_ACT(slot, mt, h)), bw, acc[c][g][mt], 0, 0, 0); \
           }                                                                                            \
@@ -424,7 +441,7 @@ __device__ __forceinline__ void skinny_body(const SkinnyArgs& A, const SkinnyWor
     const int r = row0 + row;
     if constexpr (EPI == EPI_UP_SWIGLU) {
       float gv = v[0], uv = v[G - 1];
-      if constexpr (QB != 0) {
+      if constexpr (q_chan_scale(QB)) {
         gv *= A.scale0[(size_t)e * A.N + col];
         uv *= A.scale1[(size_t)e * A.N + col];
       }
@@ -432,12 +449,12 @@ __device__ __forceinline__ void skinny_body(const SkinnyArgs& A, const SkinnyWor
           f32_to_bf16(silu(gv) * uv);
     } else if constexpr (EPI == EPI_UP_RELU) {
       float gv = v[0];
-      if constexpr (QB != 0) gv *= A.scale0[(size_t)e * A.N + col];
+      if constexpr (q_chan_scale(QB)) gv *= A.scale0[(size_t)e * A.N + col];
       A.h_out[A.h_packed ? packed_index(prow0 + row, col, A.N) : (size_t)r * A.N + col] =
           f32_to_bf16(gv > 0.0f ? gv : 0.0f);
     } else {
       float o2 = v[0];
-      if constexpr (QB != 0) o2 *= A.scale0[(size_t)e * A.N + col];
+      if constexpr (q_chan_scale(QB)) o2 *= A.scale0[(size_t)e * A.N + col];
       if constexpr (EPI == EPI_DOWN_ACC) {
         const int a = A.perm[r];
         unsafeAtomicAdd(A.f_out + (size_t)(a / A.topk) * A.N + col, A.topk_w[a] * o2);
@@ -564,7 +581,7 @@ hipError_t launch_ct(const SkinnyArgs& a, int epi, hipStream_t s) {
   const dim3 grid((unsigned)nblk);
   switch (epi) {
     case EPI_UP_SWIGLU:
-      if constexpr (QB == 4 && MT == 2 && CT == 4 && !SA) {  // (would spill: two tiles instead)
+      if constexpr (q_bits(QB) == 4 && MT == 2 && CT == 4 && !SA) {  // (would spill: two tiles instead)
         return launch_ct<MT, 2, QB, SPLITK, SA>(a, epi, s);
       } else {
         return launch_one<MT, 2, CT, QB, EPI_UP_SWIGLU, SPLITK, SA>(a, grid, s);
@@ -605,9 +622,17 @@ hipError_t launch_split(const SkinnyArgs& a, int epi, int qb, int mt, int ct, hi
     if (mt <= 1) return launch_mt<1, 8, SPLITK>(a, epi, ct, s);
     return launch_mt<2, 8, SPLITK>(a, epi, ct, s);
   }
+  if (qb == 9) {  // fp8: as int8
+    if (mt <= 1) return launch_mt<1, 9, SPLITK>(a, epi, ct, s);
+    return launch_mt<2, 9, SPLITK>(a, epi, ct, s);
+  }
   if (qb == 4) {  // int4: as int8
     if (mt <= 1) return launch_mt<1, 4, SPLITK>(a, epi, ct, s);
     return launch_mt<2, 4, SPLITK>(a, epi, ct, s);
+  }
+  if (qb == 5) {  // MXFP4: as int4
+    if (mt <= 1) return launch_mt<1, 5, SPLITK>(a, epi, ct, s);
+    return launch_mt<2, 5, SPLITK>(a, epi, ct, s);
   }
   if (mt <= 1) return launch_mt<1, 0, SPLITK>(a, epi, ct, s);
   if (mt == 2) return launch_mt<2, 0, SPLITK>(a, epi, ct, s);
@@ -645,7 +670,8 @@ hipError_t launch_ffn_skinny_split(const SkinnyArgs& narrow, const SkinnyArgs& w
 }
 
 hipError_t launch_ffn_skinny(const SkinnyArgs& a, int epi, int qb, int mt, int ct, bool splitk, hipStream_t s) {
-  if (qb != 0 && qb != 8 && qb != 4) return hipErrorInvalidValue;
+  if (qb != 0 && qb != 8 && qb != 9 && qb != 4 && qb != 5) return hipErrorInvalidValue;
+  if (qb == 5 && !a.mx) return hipErrorInvalidValue;
   if (a.shared_act && (splitk || !a.packed)) return hipErrorInvalidValue;
   if (mt > 4 && (mt != 12 || qb || splitk || !a.shared_act)) return hipErrorInvalidValue;
   return splitk ? launch_split<true>(a, epi, qb, mt, ct, s) : launch_split<false>(a, epi, qb, mt, ct, s);

@@ -37,6 +37,12 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
 //   int8 (U = K/64): byte j (0..15) is  k = u*64 + 32*(j >> 3) + 8*(l >> 4) + (j & 7)
 //   int4 (U = K/128): value j (0..31) is k = u*128 + 32*(j >> 3) + 8*(l >> 4) + (j & 7),
 //                    holding q + 8 in dword j >> 3 at bit 8*(j & 3) + 4*((j >> 2) & 1)
+//   fp8 (as int8, one E4M3 code per byte)
+//   MXFP4 (as int4, U = K/128): value j's E2M1 code in dword j >> 3 at bit
+//                    8*((j & 7) >> 1) + 4*(j & 1); and per (expert, tile, unit,
+//                    stream) a block of 16 scale dwords, dword c holding the E8M0
+//                    exponents of column nb*16 + c for the unit's four 32-k steps
+//                    (byte h: step h)
 // which is the B-operand order of v_mfma_f32_16x16x32_bf16.  A wave loading
 // one unit reads 1 KiB of contiguous memory: eight full 128-byte lines.
 // G = 2 interleaves the SwiGLU gate (g = 0) and up (g = 1) matrices so one
@@ -44,16 +50,24 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
 
 constexpr int kUnitBytes = 1024;
 
-// qb: weight bits, 0 (bf16), 8 (int8) or 4 (int4).
+// qb: weight kind, 0 (bf16), 8 (int8), 9 (fp8), 4 (int4) or 5 (MXFP4).
 inline size_t packed_bytes(int E, int K, int N, int G, int qb) {
-  const size_t units = (size_t)K / (qb == 8 ? 64 : (qb == 4 ? 128 : 32));
+  const size_t units = (size_t)K / (qb >= 8 ? 64 : (qb >= 4 ? 128 : 32));
   return (size_t)E * (size_t)(N / 16) * units * (size_t)G * kUnitBytes;
+}
+// Bytes of an MXFP4 projection's packed block scales.
+inline size_t packed_mx_scale_bytes(int E, int K, int N, int G) {
+  return (size_t)E * (size_t)(N / 16) * (size_t)(K / 128) * (size_t)G * 64;
 }
 
 hipError_t launch_pack_bf16(const uint16_t* src, void* dst, int E, int K, int N, int G, int g, hipStream_t s);
 hipError_t launch_pack_i8(const int8_t* src, void* dst, int E, int K, int N, int G, int g, hipStream_t s);
 // int4 values held one per int8 (in [-8, 7]), packed two per byte.
 hipError_t launch_pack_i4(const int8_t* src, void* dst, int E, int K, int N, int G, int g, hipStream_t s);
+// MXFP4: E2M1 codes one per byte [E][K][N] into the packed nibble layout, and
+// E8M0 exponents [E][K/32][N] into the packed scale blocks.
+hipError_t launch_pack_fp4(const uint8_t* src, void* dst, int E, int K, int N, int G, int g, hipStream_t s);
+hipError_t launch_pack_mx_scales(const uint8_t* src, void* dst, int E, int K, int N, int G, int g, hipStream_t s);
 
 // ---- routing ---------------------------------------------------------------
 
@@ -91,8 +105,9 @@ enum SkinnyEpilogue {
 
 struct SkinnyArgs {
   const void* w;           // packed weights of this projection
-  const float* scale0;     // int8: per-column scales of stream 0 [E][N]
-  const float* scale1;     // int8: per-column scales of stream 1 [E][N]
+  const float* scale0;     // int8/int4/fp8: per-column scales of stream 0 [E][N]
+  const float* scale1;     // int8/int4/fp8: per-column scales of stream 1 [E][N]
+  const uint32_t* mx;      // MXFP4: the projection's packed block scales
   const uint16_t* act;     // bf16 activations: x [T][K] (gather) or H [T*k][K]
   const int32_t* perm;     // [T*k] dispatch permutation (input unless topk_idx is set)
   const int32_t* offsets;  // [E+1] dispatch offsets (input unless topk_idx is set)
@@ -144,9 +159,10 @@ hipError_t launch_ffn_skinny_split(const SkinnyArgs& narrow, const SkinnyArgs& w
 // writes are in the packed row layout of moe_index.hpp (16-row x 32-k
 // fragments, each expert starting on a 16-row boundary).
 struct GemmArgs {
-  const void* w;           // packed weights of this projection (bf16, int8 or int4)
-  const float* scale0;     // integer weights: per-column scales [E][N] (gate, or the only stream)
-  const float* scale1;     // integer SwiGLU weights: the up stream's scales [E][N]
+  const void* w;           // packed weights of this projection (bf16, int8, fp8, int4 or MXFP4)
+  const float* scale0;     // int8/int4/fp8 weights: per-column scales [E][N] (gate, or the only stream)
+  const float* scale1;     // int8/int4/fp8 SwiGLU weights: the up stream's scales [E][N]
+  const uint32_t* mx;      // MXFP4: the projection's packed block scales
   const uint16_t* act;     // packed bf16 activations [packed rows][K]
   const int32_t* offsets;  // [E+1] dispatch offsets
   uint16_t* h_out;         // packed H [packed rows][N] (up epilogues)

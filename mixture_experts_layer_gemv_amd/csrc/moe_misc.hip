@@ -80,6 +80,55 @@ __global__ __launch_bounds__(256) void k_pack_i4(const int8_t* __restrict__ src,
   }
 }
 
+// MXFP4 codes (one per byte, low nibble): 128 k per unit; value j of a
+// lane's 32 is k = 32 (j / 8) + 8 (lane / 16) + j % 8, in dword j / 8, byte
+// (j % 8) / 2, the low nibble for even j (the order the hardware conversion
+// takes a byte's two values in).
+__global__ __launch_bounds__(256) void k_pack_fp4(const uint8_t* __restrict__ src, uint4* __restrict__ dst, int E,
+                                                  int K, int N, int G, int g) {
+  const int NB = N / 16, U = K / 128;
+  const size_t total = (size_t)E * NB * U * 64;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (size_t)gridDim.x * blockDim.x) {
+    const int lane = (int)(i & 63);
+    size_t rest = i >> 6;
+    const int u = (int)(rest % U);
+    rest /= U;
+    const int nb = (int)(rest % NB);
+    const int e = (int)(rest / NB);
+    const int n = nb * 16 + (lane & 15);
+    uint32_t d[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+      const int kk = u * 128 + 32 * (j >> 3) + 8 * (lane >> 4) + (j & 7);
+      const uint32_t nib = (uint32_t)src[((size_t)e * K + kk) * N + n] & 0xFu;
+      d[j >> 3] |= nib << (8 * ((j & 7) >> 1) + 4 * (j & 1));
+    }
+    dst[((((size_t)e * NB + nb) * U + u) * G + g) * 64 + lane] = make_uint4(d[0], d[1], d[2], d[3]);
+  }
+}
+
+// MXFP4 block scales X[e][K/32][N] -> per (expert, tile, unit, stream) 16
+// dwords, dword c = the four E8M0 bytes of column nb*16 + c for the unit's
+// 32-k steps 0..3.
+__global__ __launch_bounds__(256) void k_pack_mx_scales(const uint8_t* __restrict__ src, uint32_t* __restrict__ dst,
+                                                        int E, int K, int N, int G, int g) {
+  const int NB = N / 16, U = K / 128;
+  const size_t total = (size_t)E * NB * U * 16;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (size_t)gridDim.x * blockDim.x) {
+    const int c = (int)(i & 15);
+    size_t rest = i >> 4;
+    const int u = (int)(rest % U);
+    rest /= U;
+    const int nb = (int)(rest % NB);
+    const int e = (int)(rest / NB);
+    const int n = nb * 16 + c;
+    uint32_t d = 0;
+#pragma unroll
+    for (int h = 0; h < 4; ++h) d |= (uint32_t)src[((size_t)e * (K / 32) + 4 * u + h) * N + n] << (8 * h);
+    dst[((((size_t)e * NB + nb) * U + u) * G + g) * 16 + c] = d;
+  }
+}
+
 // ---- fp32 expert FFN ------------------------------------------------------------
 //
 // True fp32 arithmetic (one fused multiply-add per term, in increasing k) for
@@ -269,6 +318,18 @@ hipError_t launch_pack_i8(const int8_t* src, void* dst, int E, int K, int N, int
 hipError_t launch_pack_i4(const int8_t* src, void* dst, int E, int K, int N, int G, int g, hipStream_t s) {
   const size_t total = (size_t)E * (N / 16) * (K / 128) * 64;
   k_pack_i4<<<grid_for(total, 1u << 20), 256, 0, s>>>(src, static_cast<uint4*>(dst), E, K, N, G, g);
+  return hipGetLastError();
+}
+
+hipError_t launch_pack_fp4(const uint8_t* src, void* dst, int E, int K, int N, int G, int g, hipStream_t s) {
+  const size_t total = (size_t)E * (N / 16) * (K / 128) * 64;
+  k_pack_fp4<<<grid_for(total, 1u << 20), 256, 0, s>>>(src, static_cast<uint4*>(dst), E, K, N, G, g);
+  return hipGetLastError();
+}
+
+hipError_t launch_pack_mx_scales(const uint8_t* src, void* dst, int E, int K, int N, int G, int g, hipStream_t s) {
+  const size_t total = (size_t)E * (N / 16) * (K / 128) * 16;
+  k_pack_mx_scales<<<grid_for(total, 1u << 20), 256, 0, s>>>(src, static_cast<uint32_t*>(dst), E, K, N, G, g);
   return hipGetLastError();
 }
 
