@@ -13,7 +13,7 @@ one JSON line for it, with the roofline position of its dominant kernel
 oracle timed on a bounded sample of the same layer.  Beside it, under
 "configs", the same figures for the other measured layers (tiny fp32,
 Mixtral decode, Phi-3.5 skewed, Mixtral int8, int4, fp8 and MXFP4 decode,
-Mixtral int8 and int4 prefill).
+Mixtral int8, int4 and fp8 prefill).
 
   python bench.py [--steps K] [--warmup W]            headline + every layer
   python bench.py --workload c2 [--steps K]           one layer only
@@ -36,7 +36,7 @@ HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
 METRIC = "MoE layer tokens/s; achieved HBM GB/s (T≤64) or MFMA TFLOP/s (T≥4096)"
 HEADLINE = "c4"
-OTHERS = ["c1", "c2", "c3", "c5", "c6", "c7", "c8", "c9", "c10"]
+OTHERS = ["c1", "c2", "c3", "c5", "c6", "c9", "c10", "c7", "c8", "c11"]
 TRAFFIC_DIR = os.path.join(ROOT, "profiles")
 _CSRC = "mixture_experts_layer_gemv_amd/csrc/"
 _SKINNY = [_CSRC + f for f in
@@ -56,7 +56,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=None,
-                    help="time only this layer (c1..c10); default: the prefill layer with every other layer beside it")
+                    help="time only this layer (c1..c11); default: the prefill layer with every other layer beside it")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calib-mib", type=int, default=0,

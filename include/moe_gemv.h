@@ -143,7 +143,7 @@ typedef struct moe_tuning {
  * included, so a workspace must be sized after the tuning is set.  Not to be
  * called while a forward pass with the handle is being enqueued on another
  * thread.  A forced path the weights cannot take (the grouped GEMM needs
- * bf16, int8 or int4 weights) falls back to the decode kernels.
+ * bf16, int8, int4 or fp8 weights) falls back to the decode kernels.
  * Errors: INVALID_ARG (NULL handle, a value out of range).
  */
 moe_status moe_weights_set_tuning(moe_weights* w, const moe_tuning* t);

@@ -179,7 +179,9 @@ bool tuned_on(int v, bool dflt) { return v == 0 ? dflt : v > 0; }
 // The GEMM addresses packed activations and one projection's packed weights
 // with 32-bit byte offsets from a uniform base.
 bool gemm_fits(const LayerCfg& c, int T, int k) {
-  if (c.w_dtype == MOE_F32 || c.w_dtype == MOE_FP8 || c.w_dtype == MOE_MXFP4) return false;
+  // (MXFP4 weights run the decode kernels at every batch size: the grouped
+  // GEMM would have to stage their block scales beside each weight stage)
+  if (c.w_dtype == MOE_F32 || c.w_dtype == MOE_MXFP4) return false;
   const unsigned long long lim = 1ull << 32;
   const int qb = weight_bits(c);
   const unsigned long long G = c.kind == MOE_SWIGLU ? 2 : 1;

@@ -56,7 +56,7 @@ __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
 template <int QB>
 struct GemmShape {
   static constexpr int AH = q_ah(QB);            // 32-k activation fragments per row fragment and stage
-  static constexpr int BM = QB == 4 ? 128 : 256;  // rows per workgroup
+  static constexpr int BM = q_bits(QB) == 4 ? 128 : 256;  // rows per workgroup
   static constexpr int MF = BM / 32;             // row fragments per wave (two wave rows)
   static constexpr int NAF = BM / 16 * AH;       // activation fragments per stage
   static constexpr int NBF = 16;                 // weight fragments per stage
@@ -126,7 +126,8 @@ __device__ __forceinline__ void mfma_fence_out(floatx4_t (&acc)[MF][NF], floatx4
 // One expert projection tile: BM rows x 256 weight columns over the whole
 // reduction.  QB: weight bits (0 bf16, 8 int8, 4 int4); integer weights are
 // converted exactly to bf16 after their LDS read (the decode kernels'
-// conversions) and their per-column scale is applied in the epilogue; int4's
+// conversions; fp8 takes int8's tile with the E4M3 conversion) and their
+// per-column scale is applied in the epilogue; int4's
 // storage offset (each weight enters as q + 136) is removed with the rows'
 // activation sums, which the four waves of a wave row share out (one row
 // fragment each, one extra product per activation fragment).
@@ -214,7 +215,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
   // until their products (converted one fragment half at a time, which keeps
   // the 256-row tile's registers under the two-waves-per-SIMD budget); the
   // other kinds are converted when read.
-  constexpr bool kLateCvt = QB == 8;
+  constexpr bool kLateCvt = QB == 8 || QB == 9;
   struct {
     bf16x8_t a[MF][AH], b[kNF][kLateCvt ? 1 : AH];
     u32x4_t braw[kLateCvt ? kNF : 1];
@@ -243,8 +244,10 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
   if constexpr (kLateCvt) {                                                                      \
     _Pragma("unroll") for (int h = 0; h < AH; ++h) {                                             \
       _Pragma("unroll") for (int j = 0; j < kNF; ++j) {                                          \
-        const bf16x8_t bw_ = h == 0 ? i8x8_to_bf16(F.braw[j][0], F.braw[j][1])                   \
-                                    : i8x8_to_bf16(F.braw[j][2], F.braw[j][3]);                  \
+        const bf16x8_t bw_ = QB == 9 ? (h == 0 ? fp8x8_to_bf16(F.braw[j][0], F.braw[j][1])       \
+                                               : fp8x8_to_bf16(F.braw[j][2], F.braw[j][3]))      \
+                                     : (h == 0 ? i8x8_to_bf16(F.braw[j][0], F.braw[j][1])        \
+                                               : i8x8_to_bf16(F.braw[j][2], F.braw[j][3]));      \
         _Pragma("unroll") for (int i = 0; i < MF; ++i) {                                         \
           if (!SKIP || i < nf_w) {                                                               \
             if (i == 0)                                                                          \
@@ -484,6 +487,7 @@ hipError_t launch_ffn_gemm(const GemmArgs& a, int epi, int qb, hipStream_t s) {
   switch (qb) {
     case 0: return launch_gemm_qb<0>(a, epi, s);
     case 8: return launch_gemm_qb<8>(a, epi, s);
+    case 9: return launch_gemm_qb<9>(a, epi, s);
     case 4: return launch_gemm_qb<4>(a, epi, s);
     default: return hipErrorInvalidValue;
   }
@@ -497,6 +501,6 @@ hipError_t launch_pack_rows(const PackArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-int gemm_rows_per_block(int qb) { return qb == 4 ? GemmShape<4>::BM : (qb == 8 ? GemmShape<8>::BM : GemmShape<0>::BM); }
+int gemm_rows_per_block(int qb) { return q_bits(qb) == 4 ? GemmShape<4>::BM : (qb == 0 ? GemmShape<0>::BM : GemmShape<8>::BM); }
 
 }  // namespace moe

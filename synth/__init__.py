@@ -193,6 +193,8 @@ CONFIGS = {
                     note="Mixtral-8x7B-shaped decode, E4M3 weights with per-channel fp32 scales"),
     "c10": LayerSpec("mixtral_decode_mxfp4", 64, 4096, 14336, 8, 2, "swiglu", "bf16", "mxfp4", 9,
                      note="Mixtral-8x7B-shaped decode, MXFP4 weights (E2M1, E8M0 scale per 32 k)"),
+    "c11": LayerSpec("mixtral_prefill_fp8", 8192, 4096, 14336, 8, 2, "swiglu", "bf16", "fp8", 10,
+                     note="Mixtral-8x7B-shaped prefill, E4M3 weights with per-channel fp32 scales"),
 }
 
 

@@ -1,5 +1,5 @@
 """The five measured layers at full size, in the launch configuration the
-benchmark times, against the CPU oracle, and the int8 and int4 Mixtral
+benchmark times, against the CPU oracle, and the int8, int4 and fp8 Mixtral
 prefill layers (the grouped GEMM with the weights' dequant fused).
 
 Routing and dispatch are checked in full.  Outputs are checked element by
@@ -52,7 +52,7 @@ def prefill_tokens(offsets, perm, k, T, seed, n_min=PREFILL_MIN_TOKENS, block=BL
     return np.array(sorted(toks)), blocks
 
 
-@pytest.mark.parametrize("cfg", ["c1", "c2", "c3", "c4", "c5", "c7", "c8"])
+@pytest.mark.parametrize("cfg", ["c1", "c2", "c3", "c4", "c5", "c7", "c8", "c11"])
 def test_config_full_size(cfg):
     sp = synth.spec(cfg)
     log(f"config {cfg} ({sp.name}): T={sp.T} m={sp.m} p={sp.p} E={sp.E} k={sp.k} {sp.kind} "

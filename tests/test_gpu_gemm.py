@@ -58,7 +58,8 @@ SHAPES_I4 = [
     (64, 128, 128, 64, 4),     # 64 experts
     (700, 384, 256, 2, 1),     # 3 row blocks per expert, ragged tail
 ]
-WEIGHTS = [("bf16", s) for s in SHAPES] + [("i8", s) for s in SHAPES] + [("i4", s) for s in SHAPES_I4]
+WEIGHTS = ([("bf16", s) for s in SHAPES] + [("i8", s) for s in SHAPES] + [("fp8", s) for s in SHAPES]
+           + [("i4", s) for s in SHAPES_I4])
 WIDS = [f"{w}-{'-'.join(map(str, s))}" for w, s in WEIGHTS]
 
 
@@ -109,7 +110,7 @@ def test_gemm_layer_forward(kind, wd, shape):
     layer.close()
 
 
-@pytest.mark.parametrize("wd", ["bf16", "i8", "i4"])
+@pytest.mark.parametrize("wd", ["bf16", "i8", "fp8", "i4"])
 def test_gemm_all_rows_on_one_expert(wd):
     """Every token's first choice is expert 3: it holds 600 rows (three or
     five row blocks, the last ragged) while most experts hold none."""
@@ -128,7 +129,7 @@ def test_gemm_all_rows_on_one_expert(wd):
     layer.close()
 
 
-@pytest.mark.parametrize("wd", ["bf16", "i8", "i4"])
+@pytest.mark.parametrize("wd", ["bf16", "i8", "fp8", "i4"])
 def test_gemm_repeat_is_bitwise(wd):
     """The GEMM path has no atomics: two calls give identical bits."""
     L = synth.make_layer(spec(300, 256, 512, 4, 2, "swiglu", wd, seed=2))
