@@ -292,6 +292,69 @@ def measure(key, args, headline):
     return out
 
 
+def host_link_gbs(nbytes=1 << 30, reps=5):
+    """Measured host -> device rate (GB/s) of a pinned buffer: beta of the
+    pages' prefetch threshold."""
+    import torch
+
+    src = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
+    dst = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    dst.copy_(src, non_blocking=True)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for _ in range(reps):
+        dst.copy_(src, non_blocking=True)
+    ev1.record()
+    torch.cuda.synchronize()
+    gbs = nbytes * reps / (ev0.elapsed_time(ev1) * 1e-3) / 1e9
+    del src, dst
+    return gbs
+
+
+def measure_streamed(key, args, slots, beta_gbs):
+    """The layer with its experts in host memory (moe_weights_offload, `slots`
+    device slots): step time, bytes streamed per step, and the overlap of the
+    copies with the expert compute, against the pages' threshold
+    q* = phi * dtype / (2 beta) for hiding a transfer."""
+    import torch
+
+    import synth
+    import mixture_experts_layer_gemv_amd as M
+    from mixture_experts_layer_gemv_amd.layer import MoELayer
+
+    sp = synth.spec(key)
+    log(f"{sp.name}: host-resident experts, {slots} slots")
+    L = synth.make_layer(sp)
+    layer = MoELayer(L)
+    y = layer.new_output()
+    steps = max(3, min(args.steps, 10))
+    for _ in range(2):
+        layer.forward(y=y)
+    ms_resident = time_steps(lambda: layer.forward(y=y), steps)
+    layer.offload(slots)
+    for _ in range(2):
+        layer.forward(y=y)
+    h0, m0, b0 = M.moe_weights_offload_stats(layer.handle)
+    ms = time_steps(lambda: layer.forward(y=y), steps)
+    h1, m1, b1 = M.moe_weights_offload_stats(layer.handle)
+    layer.close()
+    del L, layer, y
+    gc.collect()
+    torch.cuda.empty_cache()
+    bytes_step = (b1 - b0) / steps
+    transfer_ms = bytes_step / (beta_gbs * 1e9) * 1e3
+    wb = {"bf16": 2, "i8": 1, "i4": 0.5, "fp8": 1, "mxfp4": 0.5}[sp.w_dtype]
+    q_star = MFMA_BF16_PEAK_TFLOPS * 1e12 * wb / (2 * beta_gbs * 1e9)
+    hidden = (transfer_ms + ms_resident - ms) / max(min(transfer_ms, ms_resident), 1e-9)
+    return {"workload": sp.name, "slots": slots, "ms_per_step": round(ms, 3), "value": round(sp.T / (ms * 1e-3), 2),
+            "resident_ms_per_step": round(ms_resident, 4), "h2d_bytes_per_step": int(bytes_step),
+            "expert_misses_per_step": round((m1 - m0) / steps, 2), "expert_hits_per_step": round((h1 - h0) / steps, 2),
+            "host_link_gbs": round(beta_gbs, 2), "transfer_ms_per_step": round(transfer_ms, 3),
+            "overlap_of_shorter": round(max(0.0, min(1.0, hidden)), 3),
+            "rows_per_expert": round(sp.T * sp.k / sp.E, 1), "q_star_rows": round(q_star)}
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -330,6 +393,8 @@ def main():
             r = measure(key, args, headline=False)
             out["configs"][r["config"]["workload"]] = {
                 k: r[k] for k in ("ms_per_step", "value", "dtype", "config", "roofline", "layer")}
+        beta = host_link_gbs()
+        out["host_streamed"] = [measure_streamed(key, args, 4, beta) for key in ("c2", "c4")]
     print(json.dumps(out), flush=True)
 
 

@@ -103,6 +103,39 @@ moe_status moe_weights_create(int m, int p, int E, int kind, int w_dtype, const 
 /* Free a handle from moe_weights_create (NULL is accepted).  Synchronises the device. */
 moe_status moe_weights_destroy(moe_weights* w);
 
+/*
+ * moe_weights_offload -- keep a layer's experts in host memory and stream
+ * them to the GPU as forwards need them: the expert prefetch of the HARMOEny
+ * article (yejing.asia, section 3.2: one expert computes while the next is
+ * fetched; experts may then live in CPU memory) with the device expert cache
+ * and second copy stream of the GPU-cache article (coreui.cn, sections 2.2
+ * and 3.2).
+ *  The packed weights of every expert move to pinned host memory and their
+ *  device copy is freed; `slots` (1 <= slots <= E) device slots of one
+ *  expert each cache experts between forwards (least recently used first
+ *  out).  Scales stay on the device.  Afterwards moe_layer_forward,
+ *  moe_layer_forward_fused and moe_expert_ffn on this handle: route and
+ *  dispatch, copy the per-expert row counts to the host (the one host
+ *  synchronisation of such a forward), then run the touched experts one at a
+ *  time -- cached ones first, then the others by decreasing rows -- each
+ *  missing expert copied into a slot on the handle's copy stream (default
+ *  priority) while the experts before it compute.  Results equal those of the
+ *  device-resident handle.  Calls on one offloaded handle serialise on the
+ *  host.  Graph capture and moe_layer_forward_noalloc refuse such a handle
+ *  (MOE_ERR_UNSUPPORTED).  An expert's transfer hides behind the previous
+ *  expert's compute when that one holds more than about phi * dtype / (2 *
+ *  beta) rows (phi the compute rate, beta the host link's bytes per second;
+ *  the article's threshold q).
+ *  stream   the copies to host memory run on it; the call synchronises it.
+ * Errors: INVALID_ARG (NULL, slots out of range, already offloaded),
+ * UNSUPPORTED (fp32 weights), OOM, HIP.
+ */
+moe_status moe_weights_offload(moe_weights* w, int slots, void* stream);
+
+/* Counters of an offloaded handle since moe_weights_offload: experts found
+ * in a slot, experts copied in, and the bytes copied host -> device. */
+moe_status moe_weights_offload_stats(const moe_weights* w, long long* hits, long long* misses, long long* bytes);
+
 /* Bytes of device workspace moe_layer_forward / moe_expert_ffn need for T
  * tokens at top-k.  A pure function of the handle (its shape, dtype and
  * tuning), T, k and the device's compute-unit count: the process

@@ -62,6 +62,9 @@ _SIGS = {
     "moe_weights_create": ([_i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                             ctypes.POINTER(_vp)], _i32),
     "moe_weights_destroy": ([_vp], _i32),
+    "moe_weights_offload": ([_vp, _i32, _vp], _i32),
+    "moe_weights_offload_stats": ([_vp, ctypes.POINTER(ctypes.c_longlong), ctypes.POINTER(ctypes.c_longlong),
+                                   ctypes.POINTER(ctypes.c_longlong)], _i32),
     "moe_workspace_size": ([_vp, _i32, _i32, ctypes.POINTER(_sz)], _i32),
     "moe_weights_set_tuning": ([_vp, ctypes.POINTER(moe_tuning)], _i32),
     "moe_weights_get_tuning": ([_vp, ctypes.POINTER(moe_tuning)], _i32),
@@ -142,6 +145,18 @@ def moe_weights_create(m, p, E, kind, w_dtype, w1, w_up, w2, s1=None, s_up=None,
 
 def moe_weights_destroy(w):
     _check("moe_weights_destroy", lib().moe_weights_destroy(w))
+
+
+def moe_weights_offload(w, slots, stream=None):
+    _check("moe_weights_offload", lib().moe_weights_offload(w, slots, _s(stream)))
+
+
+def moe_weights_offload_stats(w):
+    """(hits, misses, bytes copied host -> device) of an offloaded handle."""
+    h, m_, b = ctypes.c_longlong(), ctypes.c_longlong(), ctypes.c_longlong()
+    _check("moe_weights_offload_stats", lib().moe_weights_offload_stats(w, ctypes.byref(h), ctypes.byref(m_),
+                                                                        ctypes.byref(b)))
+    return h.value, m_.value, b.value
 
 
 def moe_workspace_size(w, T, k) -> int:

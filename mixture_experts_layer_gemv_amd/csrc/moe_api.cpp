@@ -26,8 +26,31 @@ struct LayerCfg {
   moe_tuning tune{};
 };
 
+// Host-resident experts (moe_weights_offload): the packed weights of every
+// expert in pinned host memory, a few device slots caching experts, the copy
+// stream that fills them, and the host-side bookkeeping of one forward.
+struct Offload {
+  int slots = 0;
+  size_t up_stride = 0, dn_stride = 0;  // bytes of one expert's packed gate(+up) and down weights
+  char* host = nullptr;                 // pinned: expert e's up at e * (up + dn stride), its down right after
+  char* dev = nullptr;                  // slots x (up + dn stride)
+  std::vector<int> slot_expert;         // expert held by each slot (-1: none)
+  std::vector<long long> slot_used;     // last forward that used each slot (LRU)
+  std::vector<hipEvent_t> ev_ready;     // per slot: its copy has landed
+  std::vector<hipEvent_t> ev_done;      // per slot: the last FFN that read it has finished
+  hipStream_t copy = nullptr;
+  hipEvent_t ev_host = nullptr;         // the offsets copied back to the host
+  hipEvent_t ev_table = nullptr;        // the per-expert offset table copied to the device
+  int32_t* h_offs = nullptr;            // pinned [E+1]
+  int32_t* h_table = nullptr;           // pinned [E][2]: each expert's row range
+  int32_t* d_table = nullptr;           // device copy of h_table
+  long long forwards = 0, hits = 0, misses = 0, bytes = 0;
+  std::mutex mu;                        // one streamed forward at a time per handle
+};
+
 struct moe_weights {
   LayerCfg c;
+  Offload* off = nullptr;  // non-null: experts live in host memory (moe_weights_offload)
   void* buf = nullptr;
   size_t bytes = 0;
   void* up = nullptr;    // packed gate(+up) [E][p/16][U][G] (bf16/int), or fp32 w1 [E][m][p]
@@ -377,7 +400,12 @@ struct FfnIo {
   float* yperm;             // with combine on the grouped-GEMM path, or the skinny path with
                             // rows: unweighted rows [slices][T*k][m]
   int* slices;              // set to the number of row slices written to yperm
+  long long rows = -1;      // >= 0: the dispatched rows this call serves (one expert's, when
+                            // streaming experts); sizes the launch grids tightly
 };
+
+// The dispatched rows an FFN call serves: all T*k, or the caller's bound.
+long long ffn_rows(const FfnIo& io) { return io.rows >= 0 ? io.rows : (long long)io.T * io.k; }
 
 // Gathers x rows into the packed row layout.
 moe_status run_pack(const LayerCfg& c, const FfnIo& io, hipStream_t s) {
@@ -387,6 +415,7 @@ moe_status run_pack(const LayerCfg& c, const FfnIo& io, hipStream_t s) {
   pk.offsets = io.offsets;
   pk.out = static_cast<uint16_t*>(io.xp);
   pk.T = io.T;
+  pk.rows = io.rows >= 0 ? (int)io.rows : -1;
   pk.K = c.m;
   pk.E = c.E;
   pk.topk = io.k;
@@ -405,7 +434,7 @@ moe_status run_pack(const LayerCfg& c, const FfnIo& io, hipStream_t s) {
 // dispatch order (y_rows).
 moe_status run_gemm(const moe_weights* W, const FfnIo& io, float* y_rows, hipStream_t s) {
   const LayerCfg& c = W->c;
-  const long long n = (long long)io.T * io.k;
+  const long long n = ffn_rows(io);
   const int qb = weight_bits(c);
   const int bm = moe::gemm_rows_per_block(qb);
   moe::GemmArgs g{};
@@ -413,6 +442,7 @@ moe_status run_gemm(const moe_weights* W, const FfnIo& io, float* y_rows, hipStr
   g.E = c.E;
   // row blocks: at most n/bm full ones plus one partial per expert
   g.W = (int)(n / bm + std::min<long long>(c.E, n));
+  if (g.W <= 0) return MOE_OK;  // no rows
   g.cg = tuned(c.tune.gemm_cg, 4);
   // experts averaging under one full row block: skip the products of empty
   // row fragments
@@ -459,7 +489,8 @@ moe_status run_skinny(const moe_weights* W, const FfnIo& io, hipStream_t s) {
   a.topk = k;
   a.T = T;
   a.E = E;
-  a.W = E + (int)((long long)T * k / R);
+  const long long nrows = ffn_rows(io);
+  a.W = (int)std::max<long long>(1, std::min<long long>(E + nrows / R, nrows));
   a.topk_w = io.topk_w;
   a.ksplit = 1;
   if ((long long)(p / 16) * a.W * 4 >= 0x7FFFFFF0LL || (long long)(m / 16) * a.W * 4 >= 0x7FFFFFF0LL)
@@ -506,7 +537,7 @@ moe_status run_skinny(const moe_weights* W, const FfnIo& io, hipStream_t s) {
     aw.max_rows = 0;
     aw.min_rows = R;
     // chunks: at most n/192 full ones plus one partial per expert above R rows
-    const long long n = (long long)T * k;
+    const long long n = nrows;
     aw.W = (int)(n / moe::skinny_rows(kWideMt) + n / (R + 1) + 1);
   }
   MOE_TRY_HIP(run("ffn_up", s, [&]() -> hipError_t {
@@ -597,6 +628,148 @@ moe_status run_ffn(const moe_weights* W, const FfnIo& io, hipStream_t s) {
     default:
       return run_skinny(W, io, s);
   }
+}
+
+// ---- host-resident experts --------------------------------------------------
+//
+// The pages' expert prefetch (HARMOEny article, section 3.2: compute one
+// expert while the next one is fetched, so the transfer hides behind the
+// compute once an expert holds enough tokens; GPU-cache article, sections 2
+// and 3.2: a device cache of experts, and weight copies on a second stream)
+// on one GPU.  After routing, the expert row counts come back to the host
+// (one synchronisation); the touched experts are then run one at a time,
+// those already in a slot first, then the misses by decreasing rows, each
+// miss copied into a slot on the copy stream while the experts before it
+// compute.  A slot is refilled only after the FFN that read it finished.
+//
+// Each expert runs the ordinary kernels on a one-expert view of the layer:
+// its weights at its slot, its scales, its row range (a [2] offsets array),
+// and the launch choices of the whole layer pinned in the view's tuning, so
+// every row is computed exactly as by the resident forward.
+
+// The whole layer's launch choices for (T, k), pinned so that a one-expert
+// view makes the same ones.
+moe_tuning pinned_tuning(const LayerCfg& c, int T, int k) {
+  moe_tuning t = c.tune;
+  const Path path = ffn_path(c, T, k);
+  t.ffn_path = path == Path::GEMM ? MOE_PATH_GEMM : MOE_PATH_SKINNY;
+  const int qb = weight_bits(c);
+  if (path == Path::GEMM) {
+    const long long n = (long long)T * k;
+    t.gemm_skip = tuned_on(c.tune.gemm_skip, n < (long long)moe::gemm_rows_per_block(qb) * c.E) ? 1 : -1;
+    t.gemm_cg = tuned(c.tune.gemm_cg, 4);
+  } else {
+    const int mt = skinny_mt(c, T, k);
+    t.skinny_mt = mt;
+    t.skinny_pack = skinny_packed(c, T, k) ? 1 : -1;
+    t.skinny_splitk = skinny_splitk(c, T, k) ? 1 : -1;
+    t.skinny_shared = skinny_shared(c, T, k) ? 1 : -1;
+    t.up_ct = skinny_ct(mt, qb, c.kind == MOE_SWIGLU ? 2 : 1, c.tune.up_ct);
+    const DownShape ds = skinny_down_shape(c, T, k);
+    t.down_ct = ds.ct;
+    t.down_ksplit = ds.ks;
+    t.down_rows = skinny_rows_combine(c) ? 1 : -1;
+  }
+  return t;
+}
+
+moe_status run_ffn_streamed(const moe_weights* W, const FfnIo& io, hipStream_t s) {
+  Offload& O = *W->off;
+  const LayerCfg& c = W->c;
+  const int E = c.E, m = c.m, p = c.p;
+  std::lock_guard<std::mutex> lk(O.mu);
+  // the previous forward's table copy has finished reading h_table
+  MOE_TRY_HIP(hipEventSynchronize(O.ev_table));
+  MOE_TRY_HIP(hipMemcpyAsync(O.h_offs, io.offsets, (size_t)(E + 1) * 4, hipMemcpyDeviceToHost, s));
+  MOE_TRY_HIP(hipEventRecord(O.ev_host, s));
+  MOE_TRY_HIP(hipEventSynchronize(O.ev_host));
+  const long long fwd = ++O.forwards;
+
+  // touched experts: those in a slot first, then the others by decreasing rows
+  std::vector<int> resident, missing;
+  std::vector<int> slot_of_expert(E, -1);
+  for (int sl = 0; sl < O.slots; ++sl)
+    if (O.slot_expert[sl] >= 0) slot_of_expert[O.slot_expert[sl]] = sl;
+  for (int e = 0; e < E; ++e) {
+    const int rows = O.h_offs[e + 1] - O.h_offs[e];
+    if (rows < 0 || O.h_offs[e + 1] > io.T * io.k) return fail(MOE_ERR_INVALID_ARG, "offsets are not a dispatch");
+    O.h_table[2 * e] = O.h_offs[e];
+    O.h_table[2 * e + 1] = O.h_offs[e + 1];
+    if (rows == 0) continue;
+    (slot_of_expert[e] >= 0 ? resident : missing).push_back(e);
+  }
+  std::stable_sort(missing.begin(), missing.end(), [&](int a, int b) {
+    return O.h_offs[a + 1] - O.h_offs[a] > O.h_offs[b + 1] - O.h_offs[b];
+  });
+  std::vector<int> order = resident;
+  order.insert(order.end(), missing.begin(), missing.end());
+  MOE_TRY_HIP(hipMemcpyAsync(O.d_table, O.h_table, (size_t)E * 2 * 4, hipMemcpyHostToDevice, s));
+  MOE_TRY_HIP(hipEventRecord(O.ev_table, s));
+
+  // slots free for misses: those holding no touched expert, least recently used first
+  std::vector<int> reusable;
+  for (int sl = 0; sl < O.slots; ++sl) {
+    const int e = O.slot_expert[sl];
+    if (e < 0 || O.h_offs[e + 1] == O.h_offs[e]) reusable.push_back(sl);
+  }
+  std::stable_sort(reusable.begin(), reusable.end(), [&](int a, int b) { return O.slot_used[a] < O.slot_used[b]; });
+  size_t reuse_head = 0;
+
+  // the one-expert view's launch choices (of the whole layer)
+  moe_weights V;
+  V.c = c;
+  V.c.E = 1;
+  V.c.tune = pinned_tuning(c, io.T, io.k);
+  const size_t up_dw = W->mx_up ? moe::packed_mx_scale_bytes(1, m, p, c.kind == MOE_SWIGLU ? 2 : 1) / 4 : 0;
+  const size_t dn_dw = W->mx_down ? moe::packed_mx_scale_bytes(1, p, m, 1) / 4 : 0;
+
+  const int n = (int)order.size();
+  std::vector<int> slot_at(n, -1);
+  int next = 0;  // next order position whose slot is not yet arranged
+  for (int i = 0; i < n; ++i) {
+    // arrange slots (and issue copies) as far ahead as free slots allow
+    while (next < n) {
+      const int e = order[next];
+      if (slot_of_expert[e] >= 0) {
+        slot_at[next++] = slot_of_expert[e];
+        ++O.hits;
+        continue;
+      }
+      if (reuse_head >= reusable.size()) break;
+      const int sl = reusable[reuse_head++];
+      if (O.slot_expert[sl] >= 0) slot_of_expert[O.slot_expert[sl]] = -1;
+      O.slot_expert[sl] = e;
+      slot_of_expert[e] = sl;
+      char* dst = O.dev + (size_t)sl * (O.up_stride + O.dn_stride);
+      const char* src = O.host + (size_t)e * (O.up_stride + O.dn_stride);
+      MOE_TRY_HIP(hipStreamWaitEvent(O.copy, O.ev_done[sl], 0));
+      MOE_TRY_HIP(hipMemcpyAsync(dst, src, O.up_stride + O.dn_stride, hipMemcpyHostToDevice, O.copy));
+      MOE_TRY_HIP(hipEventRecord(O.ev_ready[sl], O.copy));
+      O.bytes += (long long)(O.up_stride + O.dn_stride);
+      ++O.misses;
+      slot_at[next++] = sl;
+    }
+    if (slot_at[i] < 0) return fail(MOE_ERR_HIP, "no expert slot free (internal)");
+    const int e = order[i], sl = slot_at[i];
+    char* base = O.dev + (size_t)sl * (O.up_stride + O.dn_stride);
+    V.up = base;
+    V.down = base + O.up_stride;
+    V.s_gate = W->s_gate ? W->s_gate + (size_t)e * p : nullptr;
+    V.s_up = W->s_up ? W->s_up + (size_t)e * p : nullptr;
+    V.s_down = W->s_down ? W->s_down + (size_t)e * m : nullptr;
+    V.mx_up = W->mx_up ? W->mx_up + (size_t)e * up_dw : nullptr;
+    V.mx_down = W->mx_down ? W->mx_down + (size_t)e * dn_dw : nullptr;
+    FfnIo ie = io;
+    ie.offsets = O.d_table + 2 * e;
+    ie.topk_idx = nullptr;
+    ie.rows = O.h_offs[e + 1] - O.h_offs[e];  // exact grids: the work spreads over every XCD
+    MOE_TRY_HIP(hipStreamWaitEvent(s, O.ev_ready[sl], 0));
+    if (moe_status rc = run_ffn(&V, ie, s)) return rc;
+    MOE_TRY_HIP(hipEventRecord(O.ev_done[sl], s));
+    O.slot_used[sl] = fwd;
+    reusable.push_back(sl);  // refillable once this expert's FFN is done
+  }
+  return MOE_OK;
 }
 
 moe_status check_weights_match(const moe_weights* w, int m, int p, int E) {
@@ -722,11 +895,121 @@ moe_status moe_weights_create(int m, int p, int E, int kind, int w_dtype, const 
   return ok();
 }
 
+void free_offload(Offload* O) {
+  if (!O) return;
+  if (O->copy) (void)hipStreamSynchronize(O->copy);
+  for (hipEvent_t e : O->ev_ready) if (e) (void)hipEventDestroy(e);
+  for (hipEvent_t e : O->ev_done) if (e) (void)hipEventDestroy(e);
+  if (O->ev_host) (void)hipEventDestroy(O->ev_host);
+  if (O->ev_table) (void)hipEventDestroy(O->ev_table);
+  if (O->copy) (void)hipStreamDestroy(O->copy);
+  if (O->host) (void)hipHostFree(O->host);
+  if (O->h_offs) (void)hipHostFree(O->h_offs);
+  if (O->h_table) (void)hipHostFree(O->h_table);
+  if (O->dev) (void)hipFree(O->dev);
+  if (O->d_table) (void)hipFree(O->d_table);
+  delete O;
+}
+
 moe_status moe_weights_destroy(moe_weights* w) {
   if (!w) return ok();
-  const hipError_t e = hipFree(w->buf);
+  (void)hipDeviceSynchronize();
+  free_offload(w->off);
+  const hipError_t e = w->buf ? hipFree(w->buf) : hipSuccess;
   delete w;
   if (e != hipSuccess) return fail(MOE_ERR_HIP, "hipFree failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+moe_status moe_weights_offload(moe_weights* w, int slots, void* stream) {
+  if (!w) return fail(MOE_ERR_INVALID_ARG, "weights handle is NULL");
+  if (w->off) return fail(MOE_ERR_INVALID_ARG, "the experts are already host-resident");
+  if (slots < 1 || slots > w->c.E) return fail(MOE_ERR_INVALID_ARG, "slots=%d must be in [1, E=%d]", slots, w->c.E);
+  if (w->c.w_dtype == MOE_F32) return fail(MOE_ERR_UNSUPPORTED, "fp32 weights stay device-resident");
+  const LayerCfg& c = w->c;
+  const int G = c.kind == MOE_SWIGLU ? 2 : 1, qb = weight_bits(c);
+  Offload* O = new (std::nothrow) Offload;
+  if (!O) return fail(MOE_ERR_OOM, "host allocation failed");
+  O->slots = slots;
+  O->up_stride = moe::packed_bytes(1, c.m, c.p, G, qb);
+  O->dn_stride = moe::packed_bytes(1, c.p, c.m, 1, qb);
+  const size_t per = O->up_stride + O->dn_stride;
+  const hipStream_t s = as_stream(stream);
+  hipError_t e = hipHostMalloc(reinterpret_cast<void**>(&O->host), per * (size_t)c.E, hipHostMallocDefault);
+  if (e == hipSuccess) e = hipHostMalloc(reinterpret_cast<void**>(&O->h_offs), (size_t)(c.E + 1) * 4, hipHostMallocDefault);
+  if (e == hipSuccess) e = hipHostMalloc(reinterpret_cast<void**>(&O->h_table), (size_t)c.E * 2 * 4, hipHostMallocDefault);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    free_offload(O);
+    return fail(MOE_ERR_OOM, "pinned host allocation of %zu bytes failed", per * (size_t)c.E);
+  }
+  e = hipMalloc(reinterpret_cast<void**>(&O->dev), per * (size_t)slots);
+  if (e == hipSuccess) e = hipMalloc(reinterpret_cast<void**>(&O->d_table), (size_t)c.E * 2 * 4);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    free_offload(O);
+    return fail(MOE_ERR_OOM, "device allocation of %zu bytes for %d expert slots failed", per * (size_t)slots, slots);
+  }
+  // the packed experts, expert by expert, to the host
+  for (int x = 0; x < c.E && e == hipSuccess; ++x) {
+    char* h = O->host + (size_t)x * per;
+    e = hipMemcpyAsync(h, static_cast<char*>(w->up) + (size_t)x * O->up_stride, O->up_stride, hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess)
+      e = hipMemcpyAsync(h + O->up_stride, static_cast<char*>(w->down) + (size_t)x * O->dn_stride, O->dn_stride,
+                         hipMemcpyDeviceToHost, s);
+  }
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  // the scales move to an allocation of their own; the packed weights' device copy is freed
+  void* sbuf = nullptr;
+  char* old_up = static_cast<char*>(w->up);
+  const size_t packed_end = (size_t)(static_cast<char*>(w->down) - old_up) + align256((size_t)c.E * O->dn_stride);
+  const size_t sc_bytes = w->bytes - packed_end;
+  if (e == hipSuccess && sc_bytes > 0) e = hipMalloc(&sbuf, sc_bytes);
+  if (e == hipSuccess && sc_bytes > 0) e = hipMemcpyAsync(sbuf, old_up + packed_end, sc_bytes, hipMemcpyDeviceToDevice, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  O->slot_expert.assign(slots, -1);
+  O->slot_used.assign(slots, 0);
+  O->ev_ready.assign(slots, nullptr);
+  O->ev_done.assign(slots, nullptr);
+  for (int i = 0; i < slots && e == hipSuccess; ++i) {
+    e = hipEventCreateWithFlags(&O->ev_ready[i], hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&O->ev_done[i], hipEventDisableTiming);
+  }
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&O->ev_host, hipEventDisableTiming);
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&O->ev_table, hipEventDisableTiming);
+  if (e == hipSuccess) e = hipEventRecord(O->ev_table, s);  // (so the first forward's wait on it returns)
+  if (e == hipSuccess) e = hipStreamCreateWithFlags(&O->copy, hipStreamNonBlocking);  // default priority
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    if (sbuf) (void)hipFree(sbuf);
+    free_offload(O);
+    return fail(MOE_ERR_HIP, "moving the experts to host memory failed: %s", hipGetErrorString(e));
+  }
+  // rebase the scale pointers into the new allocation, free the old one
+  auto rebase = [&](auto* ptr) -> decltype(ptr) {
+    if (!ptr) return nullptr;
+    return reinterpret_cast<decltype(ptr)>(static_cast<char*>(sbuf) +
+                                           (reinterpret_cast<char*>(ptr) - (old_up + packed_end)));
+  };
+  w->s_gate = rebase(w->s_gate);
+  w->s_up = rebase(w->s_up);
+  w->s_down = rebase(w->s_down);
+  w->mx_up = rebase(w->mx_up);
+  w->mx_down = rebase(w->mx_down);
+  (void)hipFree(w->buf);
+  w->buf = sbuf;
+  w->bytes = sc_bytes;
+  w->up = w->down = w->up3 = nullptr;
+  w->off = O;
+  return ok();
+}
+
+moe_status moe_weights_offload_stats(const moe_weights* w, long long* hits, long long* misses, long long* bytes) {
+  if (!w || !w->off || !hits || !misses || !bytes) return fail(MOE_ERR_INVALID_ARG, "no host-resident experts");
+  std::lock_guard<std::mutex> lk(w->off->mu);
+  *hits = w->off->hits;
+  *misses = w->off->misses;
+  *bytes = w->off->bytes;
   return ok();
 }
 
@@ -822,7 +1105,8 @@ moe_status moe_expert_ffn(const moe_weights* w, const void* x, int x_dtype, int 
   io.xp = ws + L.xp;
   io.down_out = y_perm;
   io.combine = false;
-  if (moe_status rc = run_ffn(w, io, as_stream(stream))) return rc;
+  if (moe_status rc = w->off ? run_ffn_streamed(w, io, as_stream(stream)) : run_ffn(w, io, as_stream(stream)))
+    return rc;
   return ok();
 }
 
@@ -892,7 +1176,7 @@ moe_status enqueue_forward(const moe_weights* w, const float* w_router, const fl
   const bool gemm = path == Path::GEMM;
   // at decode sizes the dispatch is derived by the first FFN kernel: the up
   // projection's prologue, or the row packing before it
-  const bool fused = path == Path::SKINNY && (long long)T * k <= moe::kFusedDispatchMax;
+  const bool fused = !w->off && path == Path::SKINNY && (long long)T * k <= moe::kFusedDispatchMax;
   // unweighted expert rows and the combine kernel (the grouped GEMM, and the
   // skinny kernels unless tuned otherwise), or weighted rows added into y_acc
   // (zeroed by the router) and a final conversion
@@ -926,7 +1210,7 @@ moe_status enqueue_forward(const moe_weights* w, const float* w_router, const fl
   io.yperm = rows ? reinterpret_cast<float*>(ws + L.yperm) : nullptr;
   int slices = 1;
   io.slices = &slices;
-  if (moe_status rc = run_ffn(w, io, s)) return rc;
+  if (moe_status rc = w->off ? run_ffn_streamed(w, io, s) : run_ffn(w, io, s)) return rc;
   if (rows) {
     MOE_TRY_HIP(run("combine", s, [&] {
       return moe::launch_combine(io.yperm, inv, tw, T, m, k, slices, (size_t)T * k * m, y, y_bf16, s, f.residual);
@@ -1037,6 +1321,7 @@ moe_status moe_layer_forward_noalloc(const moe_weights* w, const float* w_router
                                      const void* x, int x_dtype, int T, int m, int p, int E, int k, void* y,
                                      int y_dtype, void* stream) {
   if (moe_status rc = check_forward(w, w_router, x, x_dtype, T, m, p, E, k, y, y_dtype)) return rc;
+  if (w->off) return fail(MOE_ERR_UNSUPPORTED, "host-resident experts need moe_layer_forward");
   if (T == 0) return ok();
   const Ws L = ws_layout(w->c, T, k);
   if (L.total > kScratchBytes)
@@ -1072,6 +1357,8 @@ moe_status moe_layer_graph_create(const moe_weights* w, const float* w_router, c
     std::lock_guard<std::mutex> lk(g_prof.mu);
     if (g_prof.on) return fail(MOE_ERR_INVALID_ARG, "cannot capture while moe_profile_begin is active");
   }
+  if (w && w->off) return fail(MOE_ERR_UNSUPPORTED, "a forward over host-resident experts synchronises the host and "
+                                                    "cannot be captured");
   hipStream_t cs = nullptr;
   MOE_TRY_HIP(hipStreamCreateWithFlags(&cs, hipStreamNonBlocking));
   hipError_t e = hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal);

@@ -494,7 +494,8 @@ hipError_t launch_ffn_gemm(const GemmArgs& a, int epi, int qb, hipStream_t s) {
 }
 
 hipError_t launch_pack_rows(const PackArgs& a, hipStream_t s) {
-  const long long frags = packed_rows_max((long long)a.T * a.topk, a.E) / 16 * (a.K / 32);
+  const long long n = a.rows > 0 ? a.rows : (long long)a.T * a.topk;
+  const long long frags = packed_rows_max(n, a.E) / 16 * (a.K / 32);
   const long long blocks = (frags + 3) / 4;  // one wave per fragment
   if (blocks <= 0) return hipSuccess;
   k_pack_rows<<<dim3((unsigned)blocks), 256, 0, s>>>(a);

@@ -192,6 +192,7 @@ struct PackArgs {
   int32_t* d_perm;
   int32_t* d_inv;
   int T, K, E, topk;
+  int rows;                // > 0: bound on the dispatched rows to pack (else T*topk)
 };
 hipError_t launch_pack_rows(const PackArgs& a, hipStream_t s);
 

@@ -8,8 +8,9 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-from . import (MOE_BF16, MOE_F32, MOE_FP8, MOE_I4, MOE_I8, MOE_MLP_RELU, MOE_MXFP4, MOE_SWIGLU, moe_layer_forward, moe_layer_graph_create,
-               moe_weights_create, moe_weights_destroy, moe_weights_set_tuning, moe_workspace_size)
+from . import (MOE_BF16, MOE_F32, MOE_FP8, MOE_I4, MOE_I8, MOE_MLP_RELU, MOE_MXFP4, MOE_SWIGLU, moe_layer_forward,
+               moe_layer_graph_create, moe_weights_create, moe_weights_destroy, moe_weights_offload,
+               moe_weights_set_tuning, moe_workspace_size)
 
 DTYPE_CODE = {"f32": MOE_F32, "bf16": MOE_BF16, "i8": MOE_I8, "i4": MOE_I4, "fp8": MOE_FP8, "mxfp4": MOE_MXFP4}
 KIND_CODE = {"relu": MOE_MLP_RELU, "swiglu": MOE_SWIGLU}
@@ -53,6 +54,10 @@ class MoELayer:
         self._ws = None
         self._ws_T = -1
         self.ensure_workspace(self.T)
+
+    def offload(self, slots: int):
+        """Move the experts to host memory with `slots` device cache slots (moe_weights_offload)."""
+        moe_weights_offload(self.handle, slots)
 
     def set_tuning(self, tuning: dict | None):
         """Attach moe_tuning fields to the handle (None: automatic) and resize the workspace."""
