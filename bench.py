@@ -276,12 +276,17 @@ def measure(key, args, headline):
     })
     if headline and args.copy_calib_mib:
         n = args.copy_calib_mib * (1 << 20) // 4
+        # a fill (writes the buffer once), copies (read it once, write it
+        # once) and sums (read it once): known byte counts for the counters
         a = torch.empty(n, dtype=torch.float32, device="cuda").fill_(1.0)
         b = torch.empty_like(a)
         for _ in range(3):
             b.copy_(a)
+        s = torch.zeros((), dtype=torch.float32, device="cuda")
+        for _ in range(3):
+            s += a.sum()
         torch.cuda.synchronize()
-        del a, b
+        del a, b, s
     if headline and not args.no_cpu_baseline:
         log("timing the CPU oracle")
         out["cpu_baseline"] = cpu_baseline(L, args.cpu_budget)
