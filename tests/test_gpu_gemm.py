@@ -5,8 +5,9 @@ The layer picks the grouped GEMM for bf16 weights once the experts average
 oracle finishes in seconds.  The shapes cover reductions of fewer than three
 32-k steps (the unpipelined loop) and of many, column counts that leave the
 last 256-column block partial, experts with several 256-row blocks, a ragged
-last row block, empty experts and one expert holding every row.  Bars as in
-the other parity tests: max|gpu - oracle| <= 2e-2 max|oracle| + 1e-3.
+last row block, empty experts, one expert holding every row, and expert
+sizes just past and just short of whole 256-row blocks.  Bars as in the
+other parity tests: max|gpu - oracle| <= 2e-2 max|oracle| + 1e-3.
 """
 import numpy as np
 import pytest
@@ -138,4 +139,35 @@ def test_gemm_repeat_is_bitwise(wd):
     y2 = layer.forward()
     torch.cuda.synchronize()
     assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+    layer.close()
+
+
+# rows per expert around the 256-row block boundaries: tails of 1, 32, 33,
+# 40, 96 and 224 rows after one to eight full blocks, the measured prefill
+# layer's 2074, a small and an empty expert
+BOUNDARY_COUNTS = [257, 288, 289, 552, 864, 4 * 256 + 224, 8 * 256 + 224, 2074, 5, 0]
+
+
+@pytest.mark.parametrize("kind", ["swiglu", "relu"])
+@pytest.mark.parametrize("wd", ["bf16", "i8"])
+def test_gemm_row_block_boundaries(kind, wd):
+    """Expert row counts chosen around whole row blocks: every row of every
+    expert against the oracle, unwritten rows detected."""
+    E, m, p = len(BOUNDARY_COUNTS), 128, 256
+    T = sum(BOUNDARY_COUNTS)
+    log(f"gemm row-block boundaries kind={kind} w={wd} counts={BOUNDARY_COUNTS}")
+    L = synth.make_layer(spec(T, m, p, E, 1, kind, wd, seed=23, sw=0.05))
+    layer = MoELayer(L)
+    idx_n = np.repeat(np.arange(E, dtype=np.int32), BOUNDARY_COUNTS)
+    idx_n = np.random.default_rng(5).permutation(idx_n).reshape(T, 1)
+    counts, offsets, perm, _ = oracle.dispatch(idx_n, E)
+    assert counts.tolist() == BOUNDARY_COUNTS
+    y_perm = torch.full((T, m), float("nan"), dtype=torch.float32, device="cuda")
+    M.moe_expert_ffn(layer.handle, layer.x, layer.x_dtype, T, m, p, E, 1, to_device(perm), to_device(offsets),
+                     y_perm, layer._ws, layer.ws_bytes)
+    torch.cuda.synchronize()
+    ref, _ = oracle.expert_rows(oracle.Experts.from_layer(L), L["x"], 1, perm, offsets)
+    got = y_perm.cpu().numpy()
+    assert np.all(np.isfinite(got)), "rows left unwritten"
+    assert_close(got, ref, wd, "y_perm")
     layer.close()

@@ -40,7 +40,7 @@ def hazards(asm_text):
     """{kernel: number of VALU-write -> MFMA-read pairs closer than 2 instructions}."""
     found = {}
     for fn in re.findall(r"^(_Z\w+):", asm_text, flags=re.M):
-        body = asm_text.split(fn + ":", 1)[1].split("s_endpgm", 1)[0]
+        body = re.split(r"^\.Lfunc_end\d+:", asm_text.split(fn + ":", 1)[1], maxsplit=1, flags=re.M)[0]
         ins = list(_instructions(body))
         bad = 0
         for i, op in enumerate(ins):
@@ -63,11 +63,13 @@ def test_scanner_finds_a_planted_hazard():
 \tv_perm_b32 v225, v225, v178, s46
 \tv_mfma_f32_16x16x32_bf16 v[126:129], v[182:185], v[224:227], v[126:129]
 \ts_endpgm
+.Lfunc_end0:
 _Zok:
 \tv_perm_b32 v225, v225, v178, s46
 \ts_nop 1
 \tv_mfma_f32_16x16x32_bf16 v[126:129], v[182:185], v[224:227], v[126:129]
 \ts_endpgm
+.Lfunc_end1:
 """
     assert hazards(planted) == {"_Zk": 1, "_Zok": 0}
 
