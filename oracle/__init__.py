@@ -18,11 +18,12 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "moe_oracle.c")
 _LIB = os.path.join(_HERE, "libmoe_oracle.so")
 
-F32, BF16, I8, FP8, MXFP4 = 0, 1, 2, 3, 4
+F32, BF16, I8, FP8, MXFP4, FP8A8 = 0, 1, 2, 3, 4, 5
 RELU, SWIGLU = 0, 1
 MAX_E = 64
-# weight dtypes by name (int4 weights are int8 values in [-7, 7] to the oracle)
-_DT = {"f32": F32, "bf16": BF16, "i8": I8, "i4": I8, "fp8": FP8, "mxfp4": MXFP4}
+# weight dtypes by name (int4 weights are int8 values in [-7, 7] to the oracle;
+# "fp8a8" is fp8 weights with each token's expert input quantised to E4M3)
+_DT = {"f32": F32, "bf16": BF16, "i8": I8, "i4": I8, "fp8": FP8, "mxfp4": MXFP4, "fp8a8": FP8A8}
 _KIND = {"relu": RELU, "swiglu": SWIGLU}
 
 
@@ -71,6 +72,8 @@ def lib():
         L.orc_norm.argtypes = [vp, i32, i32, i32, i32, vp, vp, ctypes.c_double, vp]
         i64 = ctypes.c_int64
         L.orc_weight_value.argtypes = [vp, vp, i32, i64, i64, i64, i64, i64, ctypes.POINTER(ctypes.c_double)]
+        L.orc_e4m3_encode.argtypes = [vp, i64, vp]
+        L.orc_quant_rows_e4m3.argtypes = [vp, i32, i32, i32, vp, vp, vp]
         L.orc_max_threads.restype = ctypes.c_int
         for f in ("orc_weight_value", "orc_norm", "orc_router_logits", "orc_topk", "orc_dispatch", "orc_expert_apply", "orc_expert_rows",
                   "orc_combine", "orc_forward_tokens", "orc_dense_masked"):
@@ -111,8 +114,8 @@ def _xdt(x):
 
 class Experts:
     """Expert weights of one layer in canonical layout (see synth).  w_dtype
-    ("fp8" or "mxfp4") names the uint8 weight formats; the others follow from
-    the arrays' dtypes (fp32, bf16 as uint16, int8)."""
+    ("fp8", "fp8a8" or "mxfp4") names the uint8 weight formats; the others
+    follow from the arrays' dtypes (fp32, bf16 as uint16, int8)."""
 
     def __init__(self, kind, w1, w2, w3=None, s1=None, s2=None, s3=None, w_dtype=None):
         self.kind = kind
@@ -121,7 +124,7 @@ class Experts:
         self.s1, self.s2, self.s3 = _c(s1, sdt), _c(s2, sdt), _c(s3, sdt)
         E, m, p = self.w1.shape
         assert self.w2.shape == (E, p, m)
-        if w_dtype in ("fp8", "mxfp4"):
+        if w_dtype in ("fp8", "fp8a8", "mxfp4"):
             assert self.w1.dtype == np.uint8
             dt = _DT[w_dtype]
         elif self.w1.dtype == np.float32:
@@ -158,6 +161,28 @@ def weight_value(w, s, dtype, e, k, n):
     out = ctypes.c_double()
     _check(lib().orc_weight_value(_ptr(w), _ptr(s), _DT[dtype], e, K, N, k, n, ctypes.byref(out)), "weight_value")
     return out.value
+
+
+def e4m3_encode(v):
+    """E4M3 codes (uint8) of fp32 values v: round to nearest even, magnitudes
+    of 448 and above saturating to 448."""
+    v = _c(v, np.float32)
+    out = np.empty(v.shape, np.uint8)
+    _check(lib().orc_e4m3_encode(_ptr(v), v.size, _ptr(out)), "e4m3_encode")
+    return out
+
+
+def quant_rows_e4m3(x):
+    """Per-row E4M3 quantisation of activations x [T][m] (fp32, or bf16 as
+    uint16): (values in double, codes, fp32 scales)."""
+    x = _c(x)
+    T, m = x.shape
+    out = np.empty((T, m), np.float64)
+    codes = np.empty((T, m), np.uint8)
+    scales = np.empty(T, np.float32)
+    _check(lib().orc_quant_rows_e4m3(_ptr(x), _xdt(x), T, m, _ptr(out), _ptr(codes), _ptr(scales)),
+           "quant_rows_e4m3")
+    return out, codes, scales
 
 
 def router_logits(x, wg, bias=None):

@@ -24,7 +24,10 @@
  *    matrices, or its SwiGLU form h = SiLU(x*W1) * (x*W3), o = h*W2.  int8
  *    weights stand for q[i][n] * s[n] (per output channel n), fp8 weights
  *    for e4m3(code) * s[n], MXFP4 weights for e2m1(code) times the E8M0
- *    scale of their block of 32 consecutive i (see weight() below).  Every dot
+ *    scale of their block of 32 consecutive i (see weight() below).  With
+ *    fp8 activations (ORC_FP8A8) each token's row is first quantised to
+ *    E4M3 with one scale per row (quant_row_e4m3 below); the router still
+ *    reads the row unquantised.  Every dot
  *    product of length n is a0*b0 followed by n-1 multiply-adds, and an
  *    operation counter records each multiply and each add.
  *  - combine: y[t] = sum over the token's selections, in ascending expert
@@ -91,6 +94,52 @@ static double e2m1_value(uint8_t c) {
 /* The shared scale E8M0 of the MX formats: 2^(E - 127); E = 255 is NaN. */
 static double e8m0_value(uint8_t E) { return E == 255 ? NAN : ldexp(1.0, (int)E - 127); }
 
+/* E4M3 code of a finite v: round to nearest, ties to even, on the format's
+ * grid (quantum 2^-9 below the smallest normal 2^-6, 2^(e-3) in [2^e,
+ * 2^(e+1))), magnitudes that would round above 448 (the largest finite
+ * value; 480 does not exist) saturating to 448.  Negative zero keeps its
+ * sign. */
+static uint8_t e4m3_encode(double v) {
+  const uint8_t sign = signbit(v) ? 0x80 : 0;
+  const double a = fabs(v);
+  if (a >= 448.0) return sign | 0x7E;
+  if (a < ldexp(1.0, -6)) {
+    const double q = nearbyint(a * 512.0); /* multiples of 2^-9; 8 is the smallest normal */
+    return sign | (uint8_t)q;
+  }
+  int e;
+  frexp(a, &e); /* a = f * 2^e, f in [0.5, 1): a in [2^(e-1), 2^e) */
+  e -= 1;
+  double q = nearbyint(ldexp(a, 3 - e)); /* in [8, 16] */
+  if (q == 16.0) {
+    q = 8.0;
+    e += 1;
+  }
+  if (e > 8 || (e == 8 && q > 14.0)) return sign | 0x7E;
+  return sign | (uint8_t)(((e + 7) << 3) | ((int)q - 8));
+}
+
+/* One row of m activations quantised to E4M3 with a per-row scale, in fp32
+ * arithmetic: amax = max |x|, inv = 448 / amax, code = e4m3(x * inv), scale
+ * s = amax / 448; the value the experts read is e4m3(code) * s.  A row of
+ * zeros quantises to zeros (scale 0). */
+static void quant_row_e4m3(const double* x, int m, double* out, uint8_t* codes, float* scale) {
+  float amax = 0.0f;
+  for (int i = 0; i < m; ++i) {
+    const float a = fabsf((float)x[i]);
+    amax = a > amax ? a : amax;
+  }
+  const float inv = amax > 0.0f ? 448.0f / amax : 0.0f;
+  const float s = amax / 448.0f;
+  for (int i = 0; i < m; ++i) {
+    const float v = (float)x[i] * inv;
+    const uint8_t c = e4m3_encode((double)v);
+    if (codes) codes[i] = c;
+    out[i] = e4m3_value(c) * (double)s;
+  }
+  if (scale) *scale = s;
+}
+
 /* Weight (e, k, n) of a projection stored [E][K][N] (k along the reduction):
  *  - fp32, bf16: the stored value;
  *  - int8 (int4 as well: q in [-7, 7], one per byte): q * s[e][n], one fp32
@@ -105,17 +154,36 @@ static double weight(const void* w, const void* s, int dtype, int64_t e, int64_t
     case ORC_F32: return (double)((const float*)w)[i];
     case ORC_BF16: return bf16_bits_to_double(((const uint16_t*)w)[i]);
     case ORC_I8: return (double)((const int8_t*)w)[i] * (double)((const float*)s)[e * N + n];
-    case ORC_FP8: return e4m3_value(((const uint8_t*)w)[i]) * (double)((const float*)s)[e * N + n];
+    case ORC_FP8:
+    case ORC_FP8A8: return e4m3_value(((const uint8_t*)w)[i]) * (double)((const float*)s)[e * N + n];
     default: return e2m1_value(((const uint8_t*)w)[i]) * e8m0_value(((const uint8_t*)s)[(e * (K / 32) + k / 32) * N + n]);
   }
 }
 
 int orc_weight_value(const void* w, const void* s, int dtype, int64_t e, int64_t K, int64_t N, int64_t k, int64_t n,
                      double* out) {
-  if (!w || !out || dtype < ORC_F32 || dtype > ORC_MXFP4) return -1;
+  if (!w || !out || dtype < ORC_F32 || dtype > ORC_FP8A8) return -1;
   if (dtype >= ORC_I8 && !s) return -1;
   if (dtype == ORC_MXFP4 && K % 32) return -1;
   *out = weight(w, s, dtype, e, K, N, k, n);
+  return 0;
+}
+
+int orc_e4m3_encode(const float* v, int64_t n, uint8_t* codes) {
+  if ((!v || !codes) && n > 0) return -1;
+  for (int64_t i = 0; i < n; ++i) codes[i] = e4m3_encode((double)v[i]);
+  return 0;
+}
+
+int orc_quant_rows_e4m3(const void* x, int x_dtype, int T, int m, double* out, uint8_t* codes, float* scales) {
+  if (!x || !out || T < 0 || m < 1 || (x_dtype != ORC_F32 && x_dtype != ORC_BF16)) return -1;
+  double* xr = (double*)malloc(sizeof(double) * (size_t)m);
+  if (!xr) return -1;
+  for (int t = 0; t < T; ++t) {
+    for (int c = 0; c < m; ++c) xr[c] = act_at(x, x_dtype, (int64_t)t * m + c);
+    quant_row_e4m3(xr, m, out + (int64_t)t * m, codes ? codes + (int64_t)t * m : NULL, scales ? scales + t : NULL);
+  }
+  free(xr);
   return 0;
 }
 
@@ -235,11 +303,17 @@ static double silu(double z) { return z / (1.0 + exp(-z)); }
 /* x[m] (double) -> o[m] (double) through expert e.  Scratch: g[p], u[p].
  * ops[0] += multiplies+adds of the dot products, ops[1] += activation
  * evaluations (ReLU or SiLU), ops[2] += the SwiGLU elementwise products. */
-static void expert_row(const orc_experts* X, int e, const double* x, double* g, double* u, double* o,
-                       uint64_t ops[3]) {
+static void expert_row(const orc_experts* X, int e, const double* x_in, double* g, double* u, double* o,
+                       double* xq, uint64_t ops[3]) {
   const int m = X->m, p = X->p;
   const int swiglu = (X->kind == ORC_SWIGLU);
   const int dt = X->w_dtype;
+  /* fp8 activations: the first projection reads the row quantised per token */
+  const double* x = x_in;
+  if (dt == ORC_FP8A8) {
+    quant_row_e4m3(x_in, m, xq, NULL, NULL);
+    x = xq;
+  }
 
   /* g = x*W1 (and u = x*W3): every g[n] is the length-m dot product in
    * increasing i, started with the i = 0 product.  The counters tick once
@@ -298,7 +372,7 @@ static int check_experts(const orc_experts* X) {
   if (!X || X->m < 1 || X->p < 1 || X->E < 1 || !X->w1 || !X->w2) return -1;
   if (X->kind != ORC_RELU && X->kind != ORC_SWIGLU) return -1;
   if (X->kind == ORC_SWIGLU && !X->w3) return -1;
-  if (X->w_dtype < ORC_F32 || X->w_dtype > ORC_MXFP4) return -1;
+  if (X->w_dtype < ORC_F32 || X->w_dtype > ORC_FP8A8) return -1;
   if (X->w_dtype >= ORC_I8 && (!X->s1 || !X->s2 || (X->kind == ORC_SWIGLU && !X->s3))) return -1;
   if (X->w_dtype == ORC_MXFP4 && (X->m % 32 || X->p % 32)) return -1;
   return 0;
@@ -308,12 +382,14 @@ int orc_expert_apply(const orc_experts* X, int e, const double* x, double* o, ui
   if (check_experts(X) || e < 0 || e >= X->E) return -1;
   double* g = (double*)malloc(sizeof(double) * (size_t)X->p);
   double* u = (double*)malloc(sizeof(double) * (size_t)X->p);
-  if (!g || !u) { free(g); free(u); return -1; }
+  double* xq = (double*)malloc(sizeof(double) * (size_t)X->m);
+  if (!g || !u || !xq) { free(g); free(u); free(xq); return -1; }
   uint64_t ops[3] = {0, 0, 0};
-  expert_row(X, e, x, g, u, o, ops);
+  expert_row(X, e, x, g, u, o, xq, ops);
   if (ops3) { ops3[0] += ops[0]; ops3[1] += ops[1]; ops3[2] += ops[2]; }
   free(g);
   free(u);
+  free(xq);
   return 0;
 }
 
@@ -333,7 +409,8 @@ int orc_expert_rows(const orc_experts* X, const void* x, int x_dtype, int T, int
     double* g = (double*)malloc(sizeof(double) * (size_t)p);
     double* u = (double*)malloc(sizeof(double) * (size_t)p);
     double* xr = (double*)malloc(sizeof(double) * (size_t)m);
-    if (!g || !u || !xr) bad = 1;
+    double* xq = (double*)malloc(sizeof(double) * (size_t)m);
+    if (!g || !u || !xr || !xq) bad = 1;
 #pragma omp for schedule(dynamic, 1)
     for (int i = 0; i < nrows; ++i) {
       if (bad) continue;
@@ -345,10 +422,10 @@ int orc_expert_rows(const orc_experts* X, const void* x, int x_dtype, int T, int
       const int64_t t = perm[r] / k;
       for (int c = 0; c < m; ++c) xr[c] = act_at(x, x_dtype, t * m + c);
       uint64_t ops[3] = {0, 0, 0};
-      expert_row(X, e, xr, g, u, out + (int64_t)i * m, ops);
+      expert_row(X, e, xr, g, u, out + (int64_t)i * m, xq, ops);
       o0 += ops[0]; o1 += ops[1]; o2 += ops[2];
     }
-    free(g); free(u); free(xr);
+    free(g); free(u); free(xr); free(xq);
   }
   if (ops3) { ops3[0] += o0; ops3[1] += o1; ops3[2] += o2; }
   return bad ? -1 : 0;
@@ -404,7 +481,8 @@ int orc_forward_tokens(const orc_experts* X, const void* x, int x_dtype, const f
     double* u = (double*)malloc(sizeof(double) * (size_t)p);
     double* xr = (double*)malloc(sizeof(double) * (size_t)m);
     double* o = (double*)malloc(sizeof(double) * (size_t)m);
-    if (!g || !u || !xr || !o) bad = 1;
+    double* xq = (double*)malloc(sizeof(double) * (size_t)m);
+    if (!g || !u || !xr || !o || !xq) bad = 1;
 #pragma omp for schedule(dynamic, 1)
     for (int i = 0; i < ntok; ++i) {
       if (bad) continue;
@@ -428,7 +506,7 @@ int orc_forward_tokens(const orc_experts* X, const void* x, int x_dtype, const f
       uint64_t ops[3] = {0, 0, 0};
       for (int s = 0; s < k; ++s) {
         const int j = slot[s];
-        expert_row(X, sel[j], xr, g, u, o, ops);
+        expert_row(X, sel[j], xr, g, u, o, xq, ops);
         for (int c = 0; c < m; ++c) yt[c] += (double)wt[j] * o[c];
       }
       o0 += ops[0]; o1 += ops[1]; o2 += ops[2];
@@ -437,7 +515,7 @@ int orc_forward_tokens(const orc_experts* X, const void* x, int x_dtype, const f
       if (w_out)
         for (int j = 0; j < k; ++j) w_out[(int64_t)i * k + j] = wt[j];
     }
-    free(g); free(u); free(xr); free(o);
+    free(g); free(u); free(xr); free(o); free(xq);
   }
   if (ops3) { ops3[0] += o0; ops3[1] += o1; ops3[2] += o2; }
   return bad ? -1 : 0;
@@ -459,7 +537,8 @@ int orc_dense_masked(const orc_experts* X, const void* x, int x_dtype, const int
   double* u = (double*)malloc(sizeof(double) * (size_t)p);
   double* xr = (double*)malloc(sizeof(double) * (size_t)m);
   double* o = (double*)malloc(sizeof(double) * (size_t)m);
-  if (!g || !u || !xr || !o) { free(g); free(u); free(xr); free(o); return -1; }
+  double* xq = (double*)malloc(sizeof(double) * (size_t)m);
+  if (!g || !u || !xr || !o || !xq) { free(g); free(u); free(xr); free(o); free(xq); return -1; }
   uint64_t ops[3] = {0, 0, 0};
   for (int t = 0; t < T; ++t) {
     for (int c = 0; c < m; ++c) xr[c] = act_at(x, x_dtype, (int64_t)t * m + c);
@@ -469,11 +548,11 @@ int orc_dense_masked(const orc_experts* X, const void* x, int x_dtype, const int
       double gate = 0.0;
       for (int j = 0; j < k; ++j)
         if (idx[(int64_t)t * k + j] == e) gate = (double)w[(int64_t)t * k + j];
-      expert_row(X, e, xr, g, u, o, ops);
+      expert_row(X, e, xr, g, u, o, xq, ops);
       for (int c = 0; c < m; ++c) yt[c] += gate * o[c];
     }
   }
-  free(g); free(u); free(xr); free(o);
+  free(g); free(u); free(xr); free(o); free(xq);
   return 0;
 }
 

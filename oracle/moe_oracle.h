@@ -11,13 +11,15 @@
 
 #define ORC_MAX_E 64
 
-enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_I8 = 2, ORC_FP8 = 3, ORC_MXFP4 = 4 };
+enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_I8 = 2, ORC_FP8 = 3, ORC_MXFP4 = 4, ORC_FP8A8 = 5 };
 enum { ORC_RELU = 0, ORC_SWIGLU = 1 };
 
 /* Expert weights in canonical row-major layout:
  * w1 (ReLU MLP W1, or SwiGLU gate) [E][m][p], w3 (SwiGLU up) [E][m][p],
  * w2 (second / down) [E][p][m].  Scales: int8 and fp8 fp32 s1, s3 [E][p],
- * s2 [E][m]; MXFP4 uint8 E8M0 s1, s3 [E][m/32][p], s2 [E][p/32][m]. */
+ * s2 [E][m]; MXFP4 uint8 E8M0 s1, s3 [E][m/32][p], s2 [E][p/32][m].
+ * ORC_FP8A8: fp8 weights as ORC_FP8, and each token's input to the first
+ * projection quantized to E4M3 first (orc_quant_rows_e4m3). */
 typedef struct {
   int m, p, E, kind, w_dtype;
   const void *w1, *w3, *w2;
@@ -28,6 +30,13 @@ typedef struct {
  * scales s (as in orc_experts). */
 int orc_weight_value(const void* w, const void* s, int dtype, int64_t e, int64_t K, int64_t N, int64_t k, int64_t n,
                      double* out);
+
+/* E4M3 codes of fp32 values (round to nearest even, magnitudes of 448 and
+ * above saturating to 448). */
+int orc_e4m3_encode(const float* v, int64_t n, uint8_t* codes);
+/* Per-row E4M3 quantisation of T rows of m activations: scale s = amax/448,
+ * out = e4m3(code) * s (double); codes and scales when non-NULL. */
+int orc_quant_rows_e4m3(const void* x, int x_dtype, int T, int m, double* out, uint8_t* codes, float* scales);
 
 int orc_router_logits(const void* x, int x_dtype, const float* wg, const float* bias, int T, int m, int E,
                       float* logits);

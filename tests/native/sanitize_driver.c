@@ -51,6 +51,7 @@ static void layer(int dtype, int kind, int x_bf16) {
                  : synth_fill_int8_quant(3, 3 + i, 0.05, E, K, N, w[i], s[i]));
         break;
       case ORC_FP8:
+      case ORC_FP8A8:
         w[i] = malloc(n); s[i] = malloc((size_t)E * N * 4);
         OK(synth_fill_fp8_quant(3, 3 + i, 0.05, E, K, N, w[i], s[i]));
         break;
@@ -100,6 +101,14 @@ static void layer(int dtype, int kind, int x_bf16) {
   double* xn = malloc((size_t)T * m * 8);
   OK(orc_norm(x, xdt, T, m, ORC_NORM_LAYER, gamma, beta, 1e-5, xn));
   OK(orc_norm(x, xdt, T, m, ORC_NORM_RMS, gamma, NULL, 1e-5, xn));
+  {
+    uint8_t* qc = malloc((size_t)T * m);
+    float* qs = malloc((size_t)T * 4);
+    OK(orc_quant_rows_e4m3(x, xdt, T, m, xn, qc, qs));
+    OK(orc_e4m3_encode(tw, (int64_t)T * k, qc));
+    free(qc);
+    free(qs);
+  }
   /* rejected arguments return -1 without touching memory */
   if (orc_topk(logits, T, E, E + 1, idx, tw) != -1 || orc_dispatch(idx, T, 0, k, counts, offsets, perm, inv) != -1) bad = 1;
   for (int i = 0; i < 3; ++i) { free(w[i]); free(s[i]); }
@@ -108,8 +117,8 @@ static void layer(int dtype, int kind, int x_bf16) {
 }
 
 int main(void) {
-  const int dtypes[5] = {ORC_F32, ORC_BF16, ORC_I8, ORC_FP8, ORC_MXFP4};
-  for (int d = 0; d < 5; ++d)
+  const int dtypes[6] = {ORC_F32, ORC_BF16, ORC_I8, ORC_FP8, ORC_MXFP4, ORC_FP8A8};
+  for (int d = 0; d < 6; ++d)
     for (int kind = 0; kind < 2; ++kind) layer(dtypes[d], kind, dtypes[d] != ORC_F32);
   if (bad) return 1;
   printf("sanitized run ok\n");

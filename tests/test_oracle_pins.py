@@ -6,6 +6,7 @@ enumeration, an invariant, or an independent library routine (torch fp64).
 """
 import itertools
 import json
+import dataclasses
 import math
 import os
 
@@ -507,7 +508,7 @@ def test_single_float_weight_expert_is_dense_mlp(orc, syn, kind, w_dtype):
     assert np.allclose(r["y"], ref.numpy(), rtol=1e-12, atol=1e-12)
 
 
-@pytest.mark.parametrize("w_dtype", ["fp8", "mxfp4"])
+@pytest.mark.parametrize("w_dtype", ["fp8", "fp8a8", "mxfp4"])
 @pytest.mark.parametrize("E,k", [(3, 2), (8, 2), (8, 8)])
 def test_float_weights_routed_equals_dense_masked(orc, syn, w_dtype, E, k):
     L = _layer(syn, 8, 64, 64, E, k, "swiglu", w_dtype, seed=E * 11 + k)
@@ -554,3 +555,94 @@ def test_mxfp4_quantisation_closed_forms(syn):
     err = np.abs(v - dec)
     assert np.all((err <= step / 2 * (1 + 1e-12)) | ((a > 6) & (mag == 6)))
     assert np.all(q < 16)
+
+
+# ---- fp8 activations (per-token E4M3 quantisation of the expert input) ----
+
+def _torch_e4m3(v32):
+    """Codes of torch's round-to-nearest float8_e4m3fn cast after clamping to
+    the format's range (the saturating conversion)."""
+    t = torch.from_numpy(np.asarray(v32, np.float32)).clamp(-448.0, 448.0)
+    return t.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def test_e4m3_encoder_against_torch_cast(orc):
+    """Every finite bf16 value (as fp32), random fp32 values over the whole
+    range, and every midpoint between neighbouring E4M3 values (the ties,
+    which go to the even code) encode as torch's cast does; magnitudes from
+    448 up saturate to 448."""
+    bits = np.arange(1 << 16, dtype=np.uint32) << 16
+    v = bits.view(np.float32)
+    v = v[np.isfinite(v)]
+    rng = np.random.default_rng(17)
+    r = (rng.standard_normal(200000) * np.exp2(rng.integers(-14, 10, 200000))).astype(np.float32)
+    vals = torch.from_numpy(np.arange(0, 0x7F, dtype=np.uint8)).view(torch.float8_e4m3fn).double().numpy()
+    mids = ((vals[1:] + vals[:-1]) / 2).astype(np.float32)
+    assert np.array_equal(mids.astype(np.float64), (vals[1:] + vals[:-1]) / 2)  # exact in fp32
+    for arr in (v, r, mids, -mids):
+        assert np.array_equal(orc.e4m3_encode(arr), _torch_e4m3(arr))
+    # ties: each midpoint goes to the neighbour whose mantissa is even
+    got = orc.e4m3_encode(mids)
+    assert np.all(got % 2 == 0)
+    big = np.array([448, 450, 463.99, 464, 480, 1e30, -1e30], np.float32)
+    assert np.array_equal(orc.e4m3_encode(big) & 0x7F, np.full(7, 0x7E, np.uint8))
+
+
+def test_per_token_e4m3_quantisation_closed_forms(orc, syn):
+    """scale = max|x| / 448 per row (fp32); the row's largest element gets a
+    code of magnitude 448; every code is torch's cast of x * (448 / max|x|)
+    computed in fp32; the value e4m3(code) * scale is within half an E4M3 step
+    (times the scale) of x; a row of zeros stays zero."""
+    T, m = 40, 256
+    x = syn.normal_bf16(5, syn.TID_X, 1.0, (T, m))
+    x[3] = 0
+    x32 = _to64(syn, x).astype(np.float32)
+    val, codes, scales = orc.quant_rows_e4m3(x)
+    amax = np.abs(x32).max(axis=1)
+    assert np.array_equal(scales, (amax / np.float32(448)).astype(np.float32))
+    inv = np.where(amax > 0, np.float32(448) / np.where(amax > 0, amax, 1), 0).astype(np.float32)
+    v = (x32 * inv[:, None]).astype(np.float32)
+    assert np.array_equal(codes, _torch_e4m3(v))
+    nz = amax > 0
+    assert np.all((codes[nz] & 0x7F).max(axis=1) == 0x7E)
+    assert np.all(val[3] == 0) and scales[3] == 0
+    dec = torch.from_numpy(codes.copy()).view(torch.float8_e4m3fn).double().numpy()
+    assert np.array_equal(val, dec * scales[:, None].astype(np.float64))
+    a = np.abs(v.astype(np.float64))
+    step = np.where(a < 2.0**-6, 2.0**-9, 2.0 ** (np.floor(np.log2(np.maximum(a, 2.0**-6))) - 3))
+    err = np.abs(v.astype(np.float64) - dec)
+    assert np.all(err <= step / 2 * (1 + 1e-12))
+
+
+@pytest.mark.parametrize("kind", ["relu", "swiglu"])
+def test_fp8a8_single_expert_is_dense_mlp_on_quantised_rows(orc, syn, kind):
+    """E = 1, k = 1 with fp8 activations equals the torch fp64 chain on rows
+    quantised with torch (scale and product in fp32, torch's E4M3 cast) and
+    weights dequantised with torch's decoder: the first projection reads the
+    quantised row, the second the unrounded hidden row."""
+    L = _layer(syn, 9, 64, 96, 1, 1, kind, "fp8a8", seed=79)
+    X = orc.Experts.from_layer(L)
+    r = orc.layer_forward(X, L["x"], L["wg"], None, 1)
+
+    def deq(key):
+        codes, s = L[key][0], L["s" + key[1:]][0]
+        return torch.from_numpy(codes.copy()).view(torch.float8_e4m3fn).double() * \
+            torch.from_numpy(s.astype(np.float64))[None, :]
+
+    x32 = _to64(syn, L["x"]).astype(np.float32)
+    amax = np.abs(x32).max(axis=1)
+    inv = (np.float32(448) / amax).astype(np.float32)
+    codes = _torch_e4m3((x32 * inv[:, None]).astype(np.float32))
+    xq = torch.from_numpy(codes.copy()).view(torch.float8_e4m3fn).double() * \
+        torch.from_numpy((amax / np.float32(448)).astype(np.float32).astype(np.float64))[:, None]
+    if kind == "relu":
+        ref = torch.relu(xq @ deq("w1")) @ deq("w2")
+    else:
+        ref = (torch.nn.functional.silu(xq @ deq("w1")) * (xq @ deq("w3"))) @ deq("w2")
+    assert np.allclose(r["y"], ref.numpy(), rtol=1e-12, atol=1e-12)
+    # the same weights without the activation quantisation give another result
+    L8 = dict(L)
+    L8["spec"] = dataclasses.replace(L["spec"], w_dtype="fp8")
+    r8 = orc.layer_forward(orc.Experts.from_layer(L8), L["x"], L["wg"], None, 1)
+    assert not np.allclose(r8["y"], r["y"], rtol=1e-6, atol=0)
+
