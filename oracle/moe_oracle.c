@@ -26,8 +26,8 @@
  *    for e4m3(code) * s[n], MXFP4 weights for e2m1(code) times the E8M0
  *    scale of their block of 32 consecutive i (see weight() below).  With
  *    fp8 activations (ORC_FP8A8) each token's row is first quantised to
- *    E4M3 with one scale per row (quant_row_e4m3 below); the router still
- *    reads the row unquantised.  Every dot
+ *    E4M3 with one power-of-two scale per row (quant_row_e4m3 below); the
+ *    router still reads the row unquantised.  Every dot
  *    product of length n is a0*b0 followed by n-1 multiply-adds, and an
  *    operation counter records each multiply and each add.
  *  - combine: y[t] = sum over the token's selections, in ascending expert
@@ -119,25 +119,27 @@ static uint8_t e4m3_encode(double v) {
   return sign | (uint8_t)(((e + 7) << 3) | ((int)q - 8));
 }
 
-/* One row of m activations quantised to E4M3 with a per-row scale, in fp32
- * arithmetic: amax = max |x|, inv = 448 / amax, code = e4m3(x * inv), scale
- * s = amax / 448; the value the experts read is e4m3(code) * s.  A row of
- * zeros quantises to zeros (scale 0). */
+/* One row of m activations quantised to E4M3 with a per-row power-of-two
+ * scale: s = 2^X with X the smallest integer such that max|x| <= 448 * 2^X
+ * (so no element saturates), code = e4m3(x / s) (the division by a power of
+ * two is exact), and the value the experts read is e4m3(code) * s, which
+ * bf16 holds exactly.  A row of zeros quantises to zeros (s = 1). */
 static void quant_row_e4m3(const double* x, int m, double* out, uint8_t* codes, float* scale) {
-  float amax = 0.0f;
-  for (int i = 0; i < m; ++i) {
-    const float a = fabsf((float)x[i]);
-    amax = a > amax ? a : amax;
+  double amax = 0.0;
+  for (int i = 0; i < m; ++i) amax = fabs(x[i]) > amax ? fabs(x[i]) : amax;
+  int X = 0;
+  if (amax > 0.0) {
+    X = (int)ceil(log2(amax / 448.0));
+    while (amax > 448.0 * ldexp(1.0, X)) ++X; /* guard the boundary against log2's rounding */
+    while (amax <= 448.0 * ldexp(1.0, X - 1)) --X;
   }
-  const float inv = amax > 0.0f ? 448.0f / amax : 0.0f;
-  const float s = amax / 448.0f;
+  const double sc = ldexp(1.0, X);
   for (int i = 0; i < m; ++i) {
-    const float v = (float)x[i] * inv;
-    const uint8_t c = e4m3_encode((double)v);
+    const uint8_t c = e4m3_encode(x[i] / sc);
     if (codes) codes[i] = c;
-    out[i] = e4m3_value(c) * (double)s;
+    out[i] = e4m3_value(c) * sc;
   }
-  if (scale) *scale = s;
+  if (scale) *scale = (float)sc;
 }
 
 /* Weight (e, k, n) of a projection stored [E][K][N] (k along the reduction):

@@ -34,8 +34,9 @@ int orc_weight_value(const void* w, const void* s, int dtype, int64_t e, int64_t
 /* E4M3 codes of fp32 values (round to nearest even, magnitudes of 448 and
  * above saturating to 448). */
 int orc_e4m3_encode(const float* v, int64_t n, uint8_t* codes);
-/* Per-row E4M3 quantisation of T rows of m activations: scale s = amax/448,
- * out = e4m3(code) * s (double); codes and scales when non-NULL. */
+/* Per-row E4M3 quantisation of T rows of m activations: scale s = 2^X, the
+ * smallest power of two with amax <= 448 s; out = e4m3(code) * s (double);
+ * codes and scales when non-NULL. */
 int orc_quant_rows_e4m3(const void* x, int x_dtype, int T, int m, double* out, uint8_t* codes, float* scales);
 
 int orc_router_logits(const void* x, int x_dtype, const float* wg, const float* bias, int T, int m, int E,

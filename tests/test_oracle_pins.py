@@ -589,37 +589,44 @@ def test_e4m3_encoder_against_torch_cast(orc):
 
 
 def test_per_token_e4m3_quantisation_closed_forms(orc, syn):
-    """scale = max|x| / 448 per row (fp32); the row's largest element gets a
-    code of magnitude 448; every code is torch's cast of x * (448 / max|x|)
-    computed in fp32; the value e4m3(code) * scale is within half an E4M3 step
-    (times the scale) of x; a row of zeros stays zero."""
+    """The scale of a row is the smallest power of two s with max|x| <= 448 s
+    (so max|x| / s lies in (224, 448] and nothing saturates); every code is
+    torch's cast of x / s (exact in fp32); the value e4m3(code) * s is within
+    half an E4M3 step (times s) of x and is a bf16 value; a row of zeros stays
+    zero."""
     T, m = 40, 256
     x = syn.normal_bf16(5, syn.TID_X, 1.0, (T, m))
     x[3] = 0
-    x32 = _to64(syn, x).astype(np.float32)
+    x[7] *= 0  # +0 and -0 rows alike
+    x64 = _to64(syn, x)
+    x64[11] *= 2.0**-20  # a small row (power-of-two scaling: exact in bf16)
+    x = torch.from_numpy(x64.astype(np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(_to64(syn, x), x64)
     val, codes, scales = orc.quant_rows_e4m3(x)
-    amax = np.abs(x32).max(axis=1)
-    assert np.array_equal(scales, (amax / np.float32(448)).astype(np.float32))
-    inv = np.where(amax > 0, np.float32(448) / np.where(amax > 0, amax, 1), 0).astype(np.float32)
-    v = (x32 * inv[:, None]).astype(np.float32)
-    assert np.array_equal(codes, _torch_e4m3(v))
+    amax = np.abs(x64).max(axis=1)
     nz = amax > 0
-    assert np.all((codes[nz] & 0x7F).max(axis=1) == 0x7E)
-    assert np.all(val[3] == 0) and scales[3] == 0
+    sc = scales.astype(np.float64)
+    assert np.all(np.frexp(sc)[0] == 0.5)  # powers of two
+    r = amax[nz] / sc[nz]
+    assert np.all((r > 224) & (r <= 448))
+    v = (x64 / sc[:, None]).astype(np.float32)
+    assert np.array_equal(v.astype(np.float64), x64 / sc[:, None])  # exact scaling
+    assert np.array_equal(codes, _torch_e4m3(v))
+    assert np.all(val[~nz] == 0)
     dec = torch.from_numpy(codes.copy()).view(torch.float8_e4m3fn).double().numpy()
-    assert np.array_equal(val, dec * scales[:, None].astype(np.float64))
+    assert np.array_equal(val, dec * sc[:, None])
+    assert np.array_equal(torch.from_numpy(val).to(torch.bfloat16).double().numpy(), val)  # bf16 holds it
     a = np.abs(v.astype(np.float64))
     step = np.where(a < 2.0**-6, 2.0**-9, 2.0 ** (np.floor(np.log2(np.maximum(a, 2.0**-6))) - 3))
-    err = np.abs(v.astype(np.float64) - dec)
-    assert np.all(err <= step / 2 * (1 + 1e-12))
+    assert np.all(np.abs(v.astype(np.float64) - dec) <= step / 2 * (1 + 1e-12))
 
 
 @pytest.mark.parametrize("kind", ["relu", "swiglu"])
 def test_fp8a8_single_expert_is_dense_mlp_on_quantised_rows(orc, syn, kind):
     """E = 1, k = 1 with fp8 activations equals the torch fp64 chain on rows
-    quantised with torch (scale and product in fp32, torch's E4M3 cast) and
-    weights dequantised with torch's decoder: the first projection reads the
-    quantised row, the second the unrounded hidden row."""
+    quantised with torch (power-of-two scale from log2 of the row maximum,
+    torch's E4M3 cast) and weights dequantised with torch's decoder: the first
+    projection reads the quantised row, the second the unrounded hidden row."""
     L = _layer(syn, 9, 64, 96, 1, 1, kind, "fp8a8", seed=79)
     X = orc.Experts.from_layer(L)
     r = orc.layer_forward(X, L["x"], L["wg"], None, 1)
@@ -629,12 +636,10 @@ def test_fp8a8_single_expert_is_dense_mlp_on_quantised_rows(orc, syn, kind):
         return torch.from_numpy(codes.copy()).view(torch.float8_e4m3fn).double() * \
             torch.from_numpy(s.astype(np.float64))[None, :]
 
-    x32 = _to64(syn, L["x"]).astype(np.float32)
-    amax = np.abs(x32).max(axis=1)
-    inv = (np.float32(448) / amax).astype(np.float32)
-    codes = _torch_e4m3((x32 * inv[:, None]).astype(np.float32))
-    xq = torch.from_numpy(codes.copy()).view(torch.float8_e4m3fn).double() * \
-        torch.from_numpy((amax / np.float32(448)).astype(np.float32).astype(np.float64))[:, None]
+    x64 = _to64(syn, L["x"])
+    sc = 2.0 ** np.ceil(np.log2(np.abs(x64).max(axis=1) / 448.0))
+    codes = _torch_e4m3((x64 / sc[:, None]).astype(np.float32))
+    xq = torch.from_numpy(codes.copy()).view(torch.float8_e4m3fn).double() * torch.from_numpy(sc)[:, None]
     if kind == "relu":
         ref = torch.relu(xq @ deq("w1")) @ deq("w2")
     else:
