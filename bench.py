@@ -46,7 +46,7 @@ _GEMM = [_CSRC + f for f in ("moe_ffn_gemm.hip", "moe_index.hpp", "moe_kernels.h
 _F32 = [_CSRC + f for f in ("moe_misc.hip", "moe_index.hpp", "moe_kernels.hpp")]
 KERNEL_SOURCES = {"ffn_up": _SKINNY, "ffn_down": _SKINNY, "gemm_up": _GEMM, "gemm_down": _GEMM,
                   "ffn_f32_up": _F32, "ffn_f32_down": _F32}
-KERNELS = ("fill", "route_topk", "dispatch", "ffn_up", "ffn_down", "ffn_f32_up", "ffn_f32_down", "finalize",
+KERNELS = ("fill", "route_topk", "dispatch", "quant_rows", "ffn_up", "ffn_down", "ffn_f32_up", "ffn_f32_down", "finalize",
            "pack_rows", "gemm_up", "gemm_down", "combine")
 
 
@@ -84,12 +84,12 @@ def algorithmic(sp, counts):
     Activation bytes: x read, hidden H written and read back (bf16), y
     written.  Flops: 2*m*p per row per m x p matrix (the pages' |O| rounds to
     this)."""
-    wb = {"f32": 4, "bf16": 2, "i8": 1, "i4": 0.5, "fp8": 1, "mxfp4": 0.5 + 1 / 32}[sp.w_dtype]
+    wb = {"f32": 4, "bf16": 2, "i8": 1, "i4": 0.5, "fp8": 1, "fp8a8": 1, "mxfp4": 0.5 + 1 / 32}[sp.w_dtype]
     ab = 4 if sp.x_dtype == "f32" else 2
     G = 2 if sp.kind == "swiglu" else 1
     touched = sum(1 for c in counts if c > 0)
     rows = sp.T * sp.k
-    q = sp.w_dtype in ("i8", "i4", "fp8")  # fp32 per-channel scales (MXFP4's block scales are in wb)
+    q = sp.w_dtype in ("i8", "i4", "fp8", "fp8a8")  # fp32 per-channel scales (MXFP4's block scales are in wb)
     up_w = int(touched * G * sp.m * sp.p * wb) + (touched * G * sp.p * 4 if q else 0)
     dn_w = int(touched * sp.p * sp.m * wb) + (touched * sp.m * 4 if q else 0)
     h_bytes = rows * sp.p * (4 if sp.w_dtype == "f32" else 2)
@@ -267,7 +267,8 @@ def measure(key, args, headline):
     roof["launch_us"] = dom_us
     out.update({
         "ms_per_step_with_kernel_events": round(ms_events, 5),
-        "dtype": {"f32": "f32", "bf16": "bf16", "i8": "bf16", "i4": "bf16", "fp8": "bf16", "mxfp4": "bf16"}[sp.w_dtype],
+        "dtype": {"f32": "f32", "bf16": "bf16", "i8": "bf16", "i4": "bf16", "fp8": "bf16", "fp8a8": "bf16",
+                  "mxfp4": "bf16"}[sp.w_dtype],
         "config": {"workload": sp.name, "T": sp.T, "m": sp.m, "p": sp.p, "E": sp.E, "k": sp.k, "expert": sp.kind,
                    "weights": sp.w_dtype, "activations": sp.x_dtype, "parallelism": "none (1 GPU)"},
         "roofline": roof,
@@ -349,7 +350,7 @@ def measure_streamed(key, args, slots, beta_gbs):
     torch.cuda.empty_cache()
     bytes_step = (b1 - b0) / steps
     transfer_ms = bytes_step / (beta_gbs * 1e9) * 1e3
-    wb = {"bf16": 2, "i8": 1, "i4": 0.5, "fp8": 1, "mxfp4": 0.5}[sp.w_dtype]
+    wb = {"bf16": 2, "i8": 1, "i4": 0.5, "fp8": 1, "fp8a8": 1, "mxfp4": 0.5}[sp.w_dtype]
     q_star = MFMA_BF16_PEAK_TFLOPS * 1e12 * wb / (2 * beta_gbs * 1e9)
     hidden = (transfer_ms + ms_resident - ms) / max(min(transfer_ms, ms_resident), 1e-9)
     return {"workload": sp.name, "slots": slots, "ms_per_step": round(ms, 3), "value": round(sp.T / (ms * 1e-3), 2),

@@ -17,7 +17,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe_gemv.so")
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP, MOE_ERR_OOM = range(6)
-MOE_F32, MOE_BF16, MOE_I8, MOE_I4, MOE_FP8, MOE_MXFP4 = 0, 1, 2, 3, 4, 5
+MOE_F32, MOE_BF16, MOE_I8, MOE_I4, MOE_FP8, MOE_MXFP4, MOE_FP8A8 = 0, 1, 2, 3, 4, 5, 6
 MOE_MLP_RELU, MOE_SWIGLU = 0, 1
 MOE_ROUTE_LOGITS_IN = 1
 MOE_NORM_NONE, MOE_NORM_LAYER, MOE_NORM_RMS = 0, 1, 2
@@ -74,6 +74,7 @@ _SIGS = {
     "moe_dispatch": ([_vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp], _i32),
     "moe_expert_ffn": ([_vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _sz, _vp], _i32),
     "moe_combine": ([_vp, _vp, _vp, _i32, _i32, _i32, _vp, _i32, _vp], _i32),
+    "moe_quantize_rows_e4m3": ([_vp, _i32, _i32, _vp, _vp, _vp], _i32),
     "moe_layer_forward": ([_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _i32, _vp, _sz,
                            _vp, _vp, _vp, _vp, _vp, _vp, _vp], _i32),
     "moe_layer_forward_fused": ([_vp, _vp, _vp, _vp, _i32, _i32, _vp, _vp, ctypes.c_float, _vp, _i32, _i32, _i32,
@@ -205,6 +206,10 @@ def moe_expert_ffn(w, x, x_dtype, T, m, p, E, k, perm, offsets, y_perm, workspac
 def moe_combine(y_perm, inv_perm, topk_w, T, m, k, y, y_dtype, stream=None):
     _check("moe_combine", lib().moe_combine(_p(y_perm), _p(inv_perm), _p(topk_w), T, m, k, _p(y), y_dtype,
                                             _s(stream)))
+
+
+def moe_quantize_rows_e4m3(x, T, m, xq, scale, stream=None):
+    _check("moe_quantize_rows_e4m3", lib().moe_quantize_rows_e4m3(_p(x), T, m, _p(xq), _p(scale), _s(stream)))
 
 
 def moe_layer_forward(w, w_router, b_router, x, x_dtype, T, m, p, E, k, y, y_dtype, workspace, ws_bytes,

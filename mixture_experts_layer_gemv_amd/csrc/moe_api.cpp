@@ -131,17 +131,21 @@ moe_status check_shape(int T, int m, int p, int E, int k) {
   return MOE_OK;
 }
 
-bool valid_dtype(int d) { return d >= MOE_F32 && d <= MOE_MXFP4; }
+bool valid_dtype(int d) { return d >= MOE_F32 && d <= MOE_FP8A8; }
 
 // Quantised weights (int8, int4, fp8 or MXFP4, each with its scales).
-bool quantised(int d) { return d == MOE_I8 || d == MOE_I4 || d == MOE_FP8 || d == MOE_MXFP4; }
+bool quantised(int d) { return d == MOE_I8 || d == MOE_I4 || d == MOE_FP8 || d == MOE_FP8A8 || d == MOE_MXFP4; }
+
+// fp8 activations: the experts read each token's row quantised to E4M3.
+bool act8(const LayerCfg& c) { return c.w_dtype == MOE_FP8A8; }
 
 // Weight-kind code of the kernels' variants: 0 bf16, 8 int8, 9 fp8, 4 int4,
 // 5 MXFP4 (the tens of bits of a weight, and which of its kinds).
 int weight_code(int d) {
   switch (d) {
     case MOE_I8: return 8;
-    case MOE_FP8: return 9;
+    case MOE_FP8:
+    case MOE_FP8A8: return 9;
     case MOE_I4: return 4;
     case MOE_MXFP4: return 5;
     default: return 0;
@@ -348,7 +352,7 @@ DownShape skinny_down_shape(const LayerCfg& c, int T, int k) {
 
 // Workspace carving, in the order listed.
 struct Ws {
-  size_t logits, idx, w, counts, offsets, perm, inv, xn, h, yacc, yperm, xp, total;
+  size_t logits, idx, w, counts, offsets, perm, inv, xn, xq, xs, h, yacc, yperm, xp, total;
 };
 
 Ws ws_layout(const LayerCfg& c, int T, int k) {
@@ -370,6 +374,9 @@ Ws ws_layout(const LayerCfg& c, int T, int k) {
   L.inv = take(n * 4);
   // the normalised input rows of the fused forward (x's dtype)
   L.xn = take((size_t)T * c.m * (f32 ? 4 : 2));
+  // fp8 activations: the quantised rows (bf16 values) and the per-token scales
+  L.xq = act8(c) ? take((size_t)T * c.m * 2) : off;
+  L.xs = act8(c) ? take((size_t)T * 4) : off;
   const Path path = ffn_path(c, T, k);
   const bool gemm = path == Path::GEMM;
   const bool spack = path == Path::SKINNY && skinny_packed(c, T, k);
@@ -395,6 +402,7 @@ struct FfnIo {
   const float* topk_w;
   void* h;                  // hidden activations [T*k][p] (packed rows on the GEMM path)
   void* xp;                 // packed paths: x rows gathered into the packed row layout
+  const float* xs = nullptr;  // fp8 activations: each token's scale (x is then the quantised rows)
   float* down_out;          // y_acc [T][m] (combine) or y_perm [T*k][m]
   bool combine;             // inside the layer: the weighted combine follows
   float* yperm;             // with combine on the grouped-GEMM path, or the skinny path with
@@ -406,6 +414,19 @@ struct FfnIo {
 
 // The dispatched rows an FFN call serves: all T*k, or the caller's bound.
 long long ffn_rows(const FfnIo& io) { return io.rows >= 0 ? io.rows : (long long)io.T * io.k; }
+
+// fp8 activations: quantises the FFN's input rows (per token, into the
+// workspace) and points io at the quantised rows and their scales.
+moe_status quant_input(const LayerCfg& c, FfnIo& io, char* ws, const Ws& L, hipStream_t s) {
+  if (!act8(c)) return MOE_OK;
+  uint16_t* xq = reinterpret_cast<uint16_t*>(ws + L.xq);
+  float* xs = reinterpret_cast<float*>(ws + L.xs);
+  const uint16_t* x = static_cast<const uint16_t*>(io.x);
+  MOE_TRY_HIP(run("quant_rows", s, [&] { return moe::launch_quant_rows_e4m3(x, io.T, c.m, xq, xs, s); }));
+  io.x = xq;
+  io.xs = xs;
+  return MOE_OK;
+}
 
 // Gathers x rows into the packed row layout.
 moe_status run_pack(const LayerCfg& c, const FfnIo& io, hipStream_t s) {
@@ -1105,6 +1126,7 @@ moe_status moe_expert_ffn(const moe_weights* w, const void* x, int x_dtype, int 
   io.xp = ws + L.xp;
   io.down_out = y_perm;
   io.combine = false;
+  if (moe_status rc = quant_input(w->c, io, ws, L, as_stream(stream))) return rc;
   if (moe_status rc = w->off ? run_ffn_streamed(w, io, as_stream(stream)) : run_ffn(w, io, as_stream(stream)))
     return rc;
   return ok();
@@ -1122,6 +1144,19 @@ moe_status moe_combine(const float* y_perm, const int32_t* inv_perm, const float
   const hipStream_t s = as_stream(stream);
   MOE_TRY_HIP(run("combine", s, [&] {
     return moe::launch_combine(y_perm, inv_perm, topk_w, T, m, k, 1, 0, y, y_dtype == MOE_BF16, s);
+  }));
+  return ok();
+}
+
+moe_status moe_quantize_rows_e4m3(const void* x, int T, int m, void* xq, float* scale, void* stream) {
+  if (T < 0 || m <= 0) return fail(MOE_ERR_INVALID_ARG, "bad sizes T=%d m=%d", T, m);
+  if (m % 64) return fail(MOE_ERR_UNSUPPORTED, "m=%d must be a multiple of 64", m);
+  if (T == 0) return ok();
+  if (!x || !xq || !scale) return fail(MOE_ERR_INVALID_ARG, "NULL argument");
+  if (!aligned16(x) || !aligned16(xq)) return fail(MOE_ERR_INVALID_ARG, "x/xq must be 16-byte aligned");
+  const hipStream_t s = as_stream(stream);
+  MOE_TRY_HIP(run("quant_rows", s, [&] {
+    return moe::launch_quant_rows_e4m3(static_cast<const uint16_t*>(x), T, m, static_cast<uint16_t*>(xq), scale, s);
   }));
   return ok();
 }
@@ -1210,6 +1245,7 @@ moe_status enqueue_forward(const moe_weights* w, const float* w_router, const fl
   io.yperm = rows ? reinterpret_cast<float*>(ws + L.yperm) : nullptr;
   int slices = 1;
   io.slices = &slices;
+  if (moe_status rc = quant_input(c, io, ws, L, s)) return rc;
   if (moe_status rc = w->off ? run_ffn_streamed(w, io, s) : run_ffn(w, io, s)) return rc;
   if (rows) {
     MOE_TRY_HIP(run("combine", s, [&] {

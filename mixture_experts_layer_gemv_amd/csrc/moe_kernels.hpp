@@ -221,6 +221,10 @@ hipError_t launch_combine(const float* y_perm, const int32_t* inv_perm, const fl
                           int slices, size_t slice_stride, void* y, bool y_bf16, hipStream_t s,
                           const void* residual = nullptr);
 hipError_t launch_fill_zero(float* p, size_t n, hipStream_t s);
+// fp8 activations: each row of x (T rows of m bf16) quantised to E4M3 with a
+// per-row power-of-two scale; xq receives e4m3(code) * scale as bf16 (exact),
+// xs the scales.  m is a multiple of 64.
+hipError_t launch_quant_rows_e4m3(const uint16_t* x, int T, int m, uint16_t* xq, float* xs, hipStream_t s);
 hipError_t launch_f32_to_bf16(const float* src, uint16_t* dst, size_t n, hipStream_t s);
 
 }  // namespace moe

@@ -105,6 +105,12 @@ def test_stage_validation_without_gpu(lib):
     assert L.moe_combine(FAKE, FAKE, FAKE, 4, 64, 2, FAKE, 2, Z) == lib.MOE_ERR_UNSUPPORTED
     assert L.moe_combine(Z, FAKE, FAKE, 4, 64, 2, FAKE, 1, Z) == lib.MOE_ERR_INVALID_ARG
     assert L.moe_combine(FAKE, FAKE, FAKE, 0, 64, 2, FAKE, 1, Z) == lib.MOE_OK
+    # the fp8-activation quantisation step
+    assert L.moe_quantize_rows_e4m3(FAKE, 4, 96, FAKE, FAKE, Z) == lib.MOE_ERR_UNSUPPORTED
+    assert L.moe_quantize_rows_e4m3(Z, 4, 64, FAKE, FAKE, Z) == lib.MOE_ERR_INVALID_ARG
+    assert L.moe_quantize_rows_e4m3(FAKE + 8, 4, 64, FAKE, FAKE, Z) == lib.MOE_ERR_INVALID_ARG
+    assert L.moe_quantize_rows_e4m3(FAKE, -1, 64, FAKE, FAKE, Z) == lib.MOE_ERR_INVALID_ARG
+    assert L.moe_quantize_rows_e4m3(FAKE, 0, 64, FAKE, FAKE, Z) == lib.MOE_OK
     # handle-based calls with a NULL handle
     assert L.moe_expert_ffn(Z, FAKE, 1, 4, 64, 64, 8, 2, FAKE, FAKE, FAKE, FAKE, 1 << 20, Z) == lib.MOE_ERR_INVALID_ARG
     assert L.moe_layer_forward(Z, FAKE, Z, FAKE, 1, 4, 64, 64, 8, 2, FAKE, 1, FAKE, 1 << 20,
@@ -166,3 +172,8 @@ def test_tuning_validation(lib):
     assert L.moe_workspace_size_for(64, 64, 8, 1, 1, None, 4, 9, ctypes.byref(n)) == lib.MOE_ERR_INVALID_ARG
     assert L.moe_workspace_size_for(64, 64, 8, 1, 1, None, 4, 2, None) == lib.MOE_ERR_INVALID_ARG
     assert lib.moe_workspace_size_for(64, 64, 8, 1, 1, None, 0, 2) > 0
+    # fp8 activations add the quantised rows (bf16) and the per-token scales
+    fp8 = lib.moe_workspace_size_for(4096, 14336, 8, 1, lib.MOE_FP8, None, 64, 2)
+    fp8a8 = lib.moe_workspace_size_for(4096, 14336, 8, 1, lib.MOE_FP8A8, None, 64, 2)
+    assert fp8a8 - fp8 == 64 * 4096 * 2 + 256
+    assert L.moe_workspace_size_for(64, 64, 8, 1, 7, None, 4, 2, ctypes.byref(n)) == lib.MOE_ERR_UNSUPPORTED
