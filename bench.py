@@ -12,8 +12,9 @@ one JSON line for it, with the roofline position of its dominant kernel
 (timed with HIP events around its launches on the launch stream) and the CPU
 oracle timed on a bounded sample of the same layer.  Beside it, under
 "configs", the same figures for the other measured layers (tiny fp32,
-Mixtral decode, Phi-3.5 skewed, Mixtral int8, int4, fp8 and MXFP4 decode,
-Mixtral int8, int4 and fp8 prefill).
+Mixtral decode, Phi-3.5 skewed, Mixtral int8, int4, fp8, fp8a8 and MXFP4
+decode, Mixtral int8, int4, fp8 and fp8a8 prefill; fp8a8: fp8 weights and
+fp8 activations, the prefill up projection on the fp8 matrix cores).
 
   python bench.py [--steps K] [--warmup W]            headline + every layer
   python bench.py --workload c2 [--steps K]           one layer only
@@ -34,9 +35,10 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
+MFMA_FP8_PEAK_TFLOPS = 5000.0  # MI355X dense fp8
 METRIC = "MoE layer tokens/s; achieved HBM GB/s (T≤64) or MFMA TFLOP/s (T≥4096)"
 HEADLINE = "c4"
-OTHERS = ["c1", "c2", "c3", "c5", "c6", "c9", "c10", "c7", "c8", "c11"]
+OTHERS = ["c1", "c2", "c3", "c5", "c6", "c9", "c10", "c13", "c7", "c8", "c11", "c12"]
 TRAFFIC_DIR = os.path.join(ROOT, "profiles")
 _CSRC = "mixture_experts_layer_gemv_amd/csrc/"
 _SKINNY = [_CSRC + f for f in
@@ -56,7 +58,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=None,
-                    help="time only this layer (c1..c11); default: the prefill layer with every other layer beside it")
+                    help="time only this layer (c1..c13); default: the prefill layer with every other layer beside it")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
@@ -247,12 +249,16 @@ def measure(key, args, headline):
     dominant = next(n for n in ("gemm_up", "ffn_up", "ffn_f32_down") if n in kern)
     dom_us = kern[dominant]
     if dominant == "gemm_up":
+        # fp8 activations: the up projection multiplies on the fp8 matrix
+        # cores (its own peak), the down projection in bf16
+        up_peak = MFMA_FP8_PEAK_TFLOPS if sp.w_dtype == "fp8a8" else MFMA_BF16_PEAK_TFLOPS
         achieved = A["up_flop"] / (dom_us * 1e-6) / 1e12
-        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4)}
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": up_peak, "unit": "TFLOP/s",
+                "frac": round(achieved / up_peak, 4)}
         work = {"algorithmic_flop": A["up_flop"]}
+        ideal_s = (A["up_flop"] / up_peak + (A["layer_flop"] - A["up_flop"]) / MFMA_BF16_PEAK_TFLOPS) / 1e12
         layer_frac = {"bound": "mfma", "tflops": round(A["layer_flop"] / (ms * 1e-3) / 1e12, 2),
-                      "frac": round(A["layer_flop"] / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
+                      "frac": round(ideal_s / (ms * 1e-3), 4)}
     else:
         nbytes = A["up_bytes"] if dominant == "ffn_up" else A["dn_bytes"]
         achieved = nbytes / (dom_us * 1e-6) / 1e9
@@ -267,8 +273,8 @@ def measure(key, args, headline):
     roof["launch_us"] = dom_us
     out.update({
         "ms_per_step_with_kernel_events": round(ms_events, 5),
-        "dtype": {"f32": "f32", "bf16": "bf16", "i8": "bf16", "i4": "bf16", "fp8": "bf16", "fp8a8": "bf16",
-                  "mxfp4": "bf16"}[sp.w_dtype],
+        "dtype": {"f32": "f32", "bf16": "bf16", "i8": "bf16", "i4": "bf16", "fp8": "bf16",
+                  "fp8a8": "fp8" if dominant == "gemm_up" else "bf16", "mxfp4": "bf16"}[sp.w_dtype],
         "config": {"workload": sp.name, "T": sp.T, "m": sp.m, "p": sp.p, "E": sp.E, "k": sp.k, "expert": sp.kind,
                    "weights": sp.w_dtype, "activations": sp.x_dtype, "parallelism": "none (1 GPU)"},
         "roofline": roof,

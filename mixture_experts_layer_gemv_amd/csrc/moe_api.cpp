@@ -352,7 +352,7 @@ DownShape skinny_down_shape(const LayerCfg& c, int T, int k) {
 
 // Workspace carving, in the order listed.
 struct Ws {
-  size_t logits, idx, w, counts, offsets, perm, inv, xn, xq, xs, h, yacc, yperm, xp, total;
+  size_t logits, idx, w, counts, offsets, perm, inv, xn, xq, xs, h, yacc, yperm, xp, rs, total;
 };
 
 Ws ws_layout(const LayerCfg& c, int T, int k) {
@@ -389,6 +389,8 @@ Ws ws_layout(const LayerCfg& c, int T, int k) {
       gemm ? 1 : (path == Path::SKINNY && skinny_rows_combine(c) ? (size_t)skinny_down_shape(c, T, k).ks : 0);
   L.yperm = row_sets ? take(row_sets * n * (size_t)c.m * 4) : off;
   L.xp = gemm || spack ? take(prows * (size_t)c.m * 2) : off;
+  // fp8 activations on the grouped GEMM: each packed row's token scale
+  L.rs = gemm && act8(c) ? take(prows * 4) : off;
   L.total = off;
   return L;
 }
@@ -403,6 +405,8 @@ struct FfnIo {
   void* h;                  // hidden activations [T*k][p] (packed rows on the GEMM path)
   void* xp;                 // packed paths: x rows gathered into the packed row layout
   const float* xs = nullptr;  // fp8 activations: each token's scale (x is then the quantised rows)
+  const uint8_t* xc = nullptr;  // fp8 activations on the grouped GEMM: the rows' E4M3 codes [T][m]
+  float* rs = nullptr;          // and each packed row's scale
   float* down_out;          // y_acc [T][m] (combine) or y_perm [T*k][m]
   bool combine;             // inside the layer: the weighted combine follows
   float* yperm;             // with combine on the grouped-GEMM path, or the skinny path with
@@ -416,14 +420,23 @@ struct FfnIo {
 long long ffn_rows(const FfnIo& io) { return io.rows >= 0 ? io.rows : (long long)io.T * io.k; }
 
 // fp8 activations: quantises the FFN's input rows (per token, into the
-// workspace) and points io at the quantised rows and their scales.
+// workspace) and points io at them: as bf16 values for the decode kernels,
+// as E4M3 codes (with the packed rows' scales to come) for the grouped GEMM,
+// whose first projection multiplies codes on the fp8 matrix cores.
 moe_status quant_input(const LayerCfg& c, FfnIo& io, char* ws, const Ws& L, hipStream_t s) {
   if (!act8(c)) return MOE_OK;
-  uint16_t* xq = reinterpret_cast<uint16_t*>(ws + L.xq);
+  const bool gemm = ffn_path(c, io.T, io.k) == Path::GEMM;
+  uint16_t* xq = gemm ? nullptr : reinterpret_cast<uint16_t*>(ws + L.xq);
+  uint8_t* xc = gemm ? reinterpret_cast<uint8_t*>(ws + L.xq) : nullptr;
   float* xs = reinterpret_cast<float*>(ws + L.xs);
   const uint16_t* x = static_cast<const uint16_t*>(io.x);
-  MOE_TRY_HIP(run("quant_rows", s, [&] { return moe::launch_quant_rows_e4m3(x, io.T, c.m, xq, xs, s); }));
-  io.x = xq;
+  MOE_TRY_HIP(run("quant_rows", s, [&] { return moe::launch_quant_rows_e4m3(x, io.T, c.m, xq, xc, xs, s); }));
+  if (gemm) {
+    io.xc = xc;
+    io.rs = reinterpret_cast<float*>(ws + L.rs);
+  } else {
+    io.x = xq;
+  }
   io.xs = xs;
   return MOE_OK;
 }
@@ -477,7 +490,27 @@ moe_status run_gemm(const moe_weights* W, const FfnIo& io, float* y_rows, hipStr
   g.K = c.m;
   g.N = c.p;
   const int up_epi = c.kind == MOE_SWIGLU ? moe::EPI_UP_SWIGLU : moe::EPI_UP_RELU;
-  MOE_TRY_HIP(run("gemm_up", s, [&] { return moe::launch_ffn_gemm(g, up_epi, qb, s); }));
+  if (io.xc) {
+    // fp8 activations: the codes' packed units and row scales, then the
+    // up projection on the fp8 matrix cores
+    moe::PackA8Args pk{};
+    pk.codes = io.xc;
+    pk.scale = io.xs;
+    pk.perm = io.perm;
+    pk.offsets = io.offsets;
+    pk.out = static_cast<uint8_t*>(io.xp);
+    pk.row_scale = io.rs;
+    pk.T = io.T;
+    pk.K = c.m;
+    pk.E = c.E;
+    pk.topk = io.k;
+    pk.rows = io.rows >= 0 ? (int)io.rows : -1;
+    MOE_TRY_HIP(run("pack_rows", s, [&] { return moe::launch_pack_rows_a8(pk, s); }));
+    g.act = reinterpret_cast<const uint16_t*>(io.xp);
+    MOE_TRY_HIP(run("gemm_up", s, [&] { return moe::launch_ffn_gemm_a8(g, io.rs, up_epi, s); }));
+  } else {
+    MOE_TRY_HIP(run("gemm_up", s, [&] { return moe::launch_ffn_gemm(g, up_epi, qb, s); }));
+  }
   // down: packed H -> rows in dispatch order
   g.w = W->down;
   g.scale0 = W->s_down;
@@ -643,7 +676,8 @@ moe_status run_ffn(const moe_weights* W, const FfnIo& io, hipStream_t s) {
       return MOE_OK;
     }
     case Path::GEMM:
-      if (moe_status rc = run_pack(c, io, s)) return rc;
+      if (!io.xc)  // (fp8 activations pack their codes in run_gemm)
+        if (moe_status rc = run_pack(c, io, s)) return rc;
       // with the combine following: unweighted rows into y_perm
       return run_gemm(W, io, io.combine ? io.yperm : io.down_out, s);
     default:
@@ -1156,7 +1190,8 @@ moe_status moe_quantize_rows_e4m3(const void* x, int T, int m, void* xq, float* 
   if (!aligned16(x) || !aligned16(xq)) return fail(MOE_ERR_INVALID_ARG, "x/xq must be 16-byte aligned");
   const hipStream_t s = as_stream(stream);
   MOE_TRY_HIP(run("quant_rows", s, [&] {
-    return moe::launch_quant_rows_e4m3(static_cast<const uint16_t*>(x), T, m, static_cast<uint16_t*>(xq), scale, s);
+    return moe::launch_quant_rows_e4m3(static_cast<const uint16_t*>(x), T, m, static_cast<uint16_t*>(xq), nullptr,
+                                       scale, s);
   }));
   return ok();
 }

@@ -89,4 +89,30 @@ constexpr int q_ah(int qb) { return qb >= 8 ? 2 : (qb >= 4 ? 4 : 1); }
 // per-output-channel scales applied in the epilogue (int8, fp8, int4)
 constexpr bool q_chan_scale(int qb) { return qb == 8 || qb == 9 || qb == 4; }
 
+// ---- E4M3 encoding of activations ----------------------------------------------
+//
+// E4M3 magnitude code of v / 2^X for |v| / 2^X <= 448: round to nearest,
+// ties to even, on the format's grid (quantum 2^-9 below 2^-6, 2^(e-3) in
+// [2^e, 2^(e+1))).
+__device__ __forceinline__ uint32_t e4m3_code(float a) {
+  if (a >= 448.0f) return 0x7Eu;
+  if (a < 0.015625f) return (uint32_t)rintf(a * 512.0f);  // multiples of 2^-9; 8 is the smallest normal
+  int e2;
+  frexpf(a, &e2);  // a in [2^(e2-1), 2^e2)
+  int e = e2 - 1;
+  float q = rintf(ldexpf(a, 3 - e));  // in [8, 16]
+  if (q == 16.0f) {
+    q = 8.0f;
+    ++e;
+  }
+  if (e > 8 || (e == 8 && q > 14.0f)) return 0x7Eu;
+  return (uint32_t)(((e + 7) << 3) | ((int)q - 8));
+}
+
+// The value of an E4M3 magnitude code.
+__device__ __forceinline__ float e4m3_mag(uint32_t c) {
+  const int ex = (int)(c >> 3), mt = (int)(c & 7);
+  return ex == 0 ? ldexpf((float)mt, -9) : ldexpf((float)(8 + mt), ex - 10);
+}
+
 }  // namespace moe

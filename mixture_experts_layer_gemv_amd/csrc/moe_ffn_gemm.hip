@@ -450,6 +450,229 @@ __global__ __launch_bounds__(256) void k_pack_rows(const PackArgs A) {
   reinterpret_cast<u32x4_t*>(A.out)[frag * 64 + lane] = v;
 }
 
+// ---- fp8 x fp8: the up projection of fp8-activation layers -----------------------
+//
+// With the activations quantised to E4M3 per token (one power-of-two scale
+// each) and the weights in E4M3 with per-column scales, the first projection
+// multiplies codes on the fp8 matrix cores (v_mfma_f32_32x32x64_f8f6f4) and
+// applies the row scale and the column scale to the fp32 sums in the
+// epilogue.  The tile, ring and ping-pong schedule are the bf16 kernel's; a
+// stage now holds 64 k of 256 rows and 256 weight columns in the same 32 KiB
+// (16 activation units + 16 weight units of 1 KiB), so a byte moved into LDS
+// carries twice the products, and the fp8 products run at twice the bf16
+// rate.  Both operands use the packed fp8 weights' unit layout (16 rows or
+// columns x 64 k; lane l = r + 16 q holds k = 8 q + (0..7) and 32 + 8 q +
+// (0..7)); a 32 x 64 product operand is two units, lane l = r + 32 g reading
+// the 16 bytes of unit lanes 2 g and 2 g + 1, so that A and B pair the same k
+// in every position.  Without scale operands (the per-token scale is a power
+// of two applied in the epilogue), only that pairing matters.
+
+// Gathers E4M3 code rows into packed units (one wave per unit).
+__global__ __launch_bounds__(256) void k_pack_rows_a8(const PackA8Args A) {
+  __shared__ int offs_s[kMaxExperts + 1];
+  __shared__ int poffs_s[kMaxExperts + 1];
+  const int tid = threadIdx.x, lane = tid & 63;
+  if (tid <= A.E) offs_s[tid] = A.offsets[tid];
+  __syncthreads();
+  if (tid <= A.E) poffs_s[tid] = padded_offset(offs_s, tid);
+  __syncthreads();
+  const int U = A.K / 64;
+  const long long unit = (long long)blockIdx.x * 4 + (tid >> 6);
+  const long long rb = unit / U;
+  const int u = (int)(unit - rb * U);
+  const long long prow = rb * 16 + (lane & 15);
+  if (prow >= poffs_s[A.E]) return;  // past the last expert's padded rows
+  int e = 0;
+  while (poffs_s[e + 1] <= prow) ++e;
+  const int local = (int)(prow - poffs_s[e]);
+  const int q = lane >> 4;
+  uint2 lo = make_uint2(0u, 0u), hi = make_uint2(0u, 0u);
+  float rs = 0.0f;
+  if (local < offs_s[e + 1] - offs_s[e]) {
+    const int token = A.perm[offs_s[e] + local] / A.topk;
+    const uint8_t* row = A.codes + (size_t)token * A.K + u * 64 + 8 * q;
+    lo = *reinterpret_cast<const uint2*>(row);
+    hi = *reinterpret_cast<const uint2*>(row + 32);
+    rs = A.scale[token];
+  }
+  reinterpret_cast<uint4*>(A.out)[unit * 64 + lane] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+  if (u == 0 && q == 0) A.row_scale[prow] = rs;
+}
+
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+typedef float floatx16_t __attribute__((ext_vector_type(16)));
+
+// acc += a * b (32 x 32 x 64, E4M3 operands), accumulating in place.  The
+// leading s_nop covers a vector instruction that assembled an operand
+// register just before (two wait states before a matrix instruction reads
+// it).
+__device__ __forceinline__ void mfma_f8(floatx16_t& acc, const i32x8_t& a, const i32x8_t& b) {
+  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
+}
+
+template <int EPI>
+__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_ffn_gemm_a8(
+    const GemmArgs A, const float* __restrict__ row_scale) {
+  constexpr int G = EPI == EPI_UP_SWIGLU ? 2 : 1;
+  constexpr int TPW = kNF / G;  // column tiles per wave
+  constexpr int BM = 256, NAF = 16, NBF = 16, STAGES = 4, CPA = 2, CPB = 2, CPS = CPA + CPB;
+  constexpr int STAGE_BYTES = (NAF + NBF) * kFrag;
+  constexpr int RB = 4;  // 32-row blocks per wave (128 rows)
+  static_assert(CPS * (STAGES - 1) <= 63, "vmcnt holds at most 63");
+  __shared__ __attribute__((aligned(1024))) unsigned char ring[STAGES][STAGE_BYTES];
+  const int* const offs_s = A.offsets;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / kWC;
+  const int wn = wave % kWC;
+  const int NB = A.N / 16;
+  const int NBL = (NB + kWC * TPW - 1) / (kWC * TPW);
+
+  int e, mb, nblock;
+  if (!gemm_item(offs_s, A.E, BM, NBL, A.cg, xcd_logical(blockIdx.x, gridDim.x), &e, &mb, &nblock)) return;
+  const int tile_base = nblock * kWC * TPW;
+  const int row0 = offs_s[e] + mb * BM;
+  const int nrows = min(BM, offs_s[e + 1] - row0);
+  const int prow0 = padded_offset(offs_s, e) + mb * BM;
+  const int nfrag = (nrows + 15) >> 4;  // packed units holding real rows
+
+  // copies: activation units 2 w, 2 w + 1 and weight units 2 w, 2 w + 1 of
+  // every stage (units past the expert's last row re-read its last unit)
+  const int U = A.K / 64;
+  const char* const abase = reinterpret_cast<const char*>(A.act);
+  const char* const bbase = static_cast<const char*>(A.w);
+  uint32_t aoff[CPA], boff[CPB];
+#pragma unroll
+  for (int j = 0; j < CPA; ++j) {
+    const int f = CPA * wave + j;
+    aoff[j] = (uint32_t)((unsigned long long)((prow0 >> 4) + min(f, nfrag - 1)) * (unsigned)U * 1024ull + 16ull * lane);
+  }
+#pragma unroll
+  for (int j = 0; j < CPB; ++j) boff[j] = (uint32_t)gemm_b_offset(e, NB, U, G, tile_base, kNF, CPB * wave + j, lane);
+  const uint32_t ring_lds = lds_address(ring);
+  const uint32_t a_lds = ring_lds + (uint32_t)(CPA * wave) * kFrag;
+  const uint32_t b_lds = ring_lds + (uint32_t)(NAF + CPB * wave) * kFrag;
+
+#define MOE_ISSUE(step)                                                                            \
+  do {                                                                                             \
+    const char* ab_ = abase + (size_t)(step) * kFrag;                                              \
+    const char* bb_ = bbase + (size_t)(step) * G * kFrag;                                          \
+    const uint32_t st_ = (uint32_t)((step) % STAGES) * STAGE_BYTES;                                \
+    _Pragma("unroll") for (int j = 0; j < CPA; ++j) copy_frag(ab_, aoff[j], a_lds + st_ + j * kFrag); \
+    _Pragma("unroll") for (int j = 0; j < CPB; ++j) copy_frag(bb_, boff[j], b_lds + st_ + j * kFrag); \
+  } while (0)
+
+  floatx16_t acc[RB][2];
+#pragma unroll
+  for (int i = 0; i < RB; ++i)
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][c][v] = 0.0f;
+#pragma unroll
+  for (int i = 0; i < RB; ++i)
+#pragma unroll
+    for (int c = 0; c < 2; ++c) asm volatile("" : "+v"(acc[i][c]));
+  asm volatile("s_nop 7\n\ts_nop 7" ::: "memory");
+
+  // operand reads: lane l = r + 32 g of a 32 x 64 operand takes unit lanes
+  // (r % 16) + 16 (2 g) and + 16 (2 g + 1) of unit r / 16 of the pair
+  const int ul = (lane & 15) + 32 * (lane >> 5);  // first unit lane (its second is + 16)
+  const int uh = (lane >> 4) & 1;                 // which unit of the pair
+  struct {
+    i32x8_t a[RB], b[2];
+  } f;
+  auto rd = [&](const u32x4_t* st, int unit, i32x8_t& dst) {
+    const u32x4_t lo = st[unit * 64 + ul], hi = st[unit * 64 + ul + 16];
+    dst = i32x8_t{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+  };
+#define MOE_LOAD(F, step)                                                                          \
+  do {                                                                                             \
+    const u32x4_t* st_ = reinterpret_cast<const u32x4_t*>(ring[(step) % STAGES]);                  \
+    _Pragma("unroll") for (int i = 0; i < RB; ++i) rd(st_, wm * 8 + 2 * i + uh, F.a[i]);             \
+    _Pragma("unroll") for (int c = 0; c < 2; ++c)                                                  \
+        rd(st_, NAF + wn * kNF + (G == 2 ? 2 * uh + c : 2 * c + uh), F.b[c]);                      \
+  } while (0)
+#define MOE_MMA(F)                                                                                 \
+  _Pragma("unroll") for (int i = 0; i < RB; ++i) _Pragma("unroll") for (int c = 0; c < 2; ++c)     \
+      mfma_f8(acc[i][c], F.a[i], F.b[c]);
+
+  const int nsteps = U;
+  {
+    // the bf16 kernel's ping-pong (see k_ffn_gemm)
+    const bool g0 = wave < kWC;
+#define MOE_ISSUE_CLAMPED(step) MOE_ISSUE((step) < nsteps ? (step) : nsteps - 1)
+#pragma unroll
+    for (int s = 0; s < STAGES - 1; ++s) MOE_ISSUE_CLAMPED(s);
+    if (g0) {
+      MOE_ISSUE_CLAMPED(STAGES - 1);
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(CPS * (STAGES - 1)));
+      ring_barrier();
+    } else {
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(CPS * (STAGES - 2)));
+      ring_barrier();
+      ring_barrier();
+    }
+    MOE_LOAD(f, 0);
+    if (!g0) MOE_ISSUE_CLAMPED(STAGES - 1);
+    for (int ks = 0; ks < nsteps; ++ks) {
+      if (g0)
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(CPS * (STAGES - 1)));
+      else
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(CPS * (STAGES - 2)));
+      ring_barrier();
+      asm volatile("s_setprio 1");
+      MOE_MMA(f);
+      asm volatile("s_setprio 0");
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(CPS * (STAGES - 2)));
+      ring_barrier();
+      MOE_LOAD(f, ks + 1);
+      MOE_ISSUE_CLAMPED(ks + STAGES);
+    }
+    if (g0) ring_barrier();
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+#undef MOE_ISSUE_CLAMPED
+  }
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+#pragma unroll
+  for (int i = 0; i < RB; ++i)
+#pragma unroll
+    for (int c = 0; c < 2; ++c) asm volatile("" : "+v"(acc[i][c]));
+#undef MOE_LOAD
+#undef MOE_MMA
+#undef MOE_ISSUE
+
+  // Epilogue.  Element v of acc[i][c] in lane l: row 32 i + 8 (v / 4) +
+  // 4 (l / 32) + v % 4 of the wave's rows, column l % 32 of operand block c
+  // (SwiGLU: gate c = 0 and up c = 1 of the same 32 hidden columns; ReLU:
+  // 32 columns each).
+  const int c32 = lane & 31;
+#pragma unroll
+  for (int c = 0; c < (G == 2 ? 1 : 2); ++c) {
+    const int col = (tile_base + wn * TPW + 2 * c) * 16 + c32;
+    if (col >= A.N) continue;
+    const float sc0 = A.scale0[(size_t)e * A.N + col];
+    const float sc1 = G == 2 ? A.scale1[(size_t)e * A.N + col] : 1.0f;
+#pragma unroll
+    for (int i = 0; i < RB; ++i) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int row = wm * 128 + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+        if (row >= nrows) continue;
+        const float rs = row_scale[prow0 + row];
+        if constexpr (EPI == EPI_UP_SWIGLU) {
+          const float g = acc[i][0][v] * sc0 * rs, up = acc[i][1][v] * sc1 * rs;
+          A.h_out[packed_index(prow0 + row, col, A.N)] = f32_to_bf16(silu(g) * up);
+        } else {
+          const float g = acc[i][c][v] * sc0 * rs;
+          A.h_out[packed_index(prow0 + row, col, A.N)] = f32_to_bf16(g > 0.0f ? g : 0.0f);
+        }
+      }
+    }
+  }
+}
+
 }  // namespace
 
 template <int QB>
@@ -499,6 +722,34 @@ hipError_t launch_pack_rows(const PackArgs& a, hipStream_t s) {
   const long long blocks = (frags + 3) / 4;  // one wave per fragment
   if (blocks <= 0) return hipSuccess;
   k_pack_rows<<<dim3((unsigned)blocks), 256, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_pack_rows_a8(const PackA8Args& a, hipStream_t s) {
+  if (a.K % 64 || a.K <= 0) return hipErrorInvalidValue;
+  const long long n = a.rows > 0 ? a.rows : (long long)a.T * a.topk;
+  const long long units = packed_rows_max(n, a.E) / 16 * (a.K / 64);
+  const long long blocks = (units + 3) / 4;  // one wave per unit
+  if (blocks <= 0) return hipSuccess;
+  k_pack_rows_a8<<<dim3((unsigned)blocks), 256, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_ffn_gemm_a8(const GemmArgs& a, const float* row_scale, int epi, hipStream_t s) {
+  if (a.K % 64 || a.N % 64 || a.K <= 0 || a.N <= 0 || a.cg < 1 || !a.scale0 || !row_scale) return hipErrorInvalidValue;
+  if (epi == EPI_UP_SWIGLU && !a.scale1) return hipErrorInvalidValue;
+  const int G = epi == EPI_UP_SWIGLU ? 2 : 1;
+  const int tiles_per_block = kWC * (kNF / G);
+  const long long nbl = (a.N / 16 + tiles_per_block - 1) / tiles_per_block;
+  const long long work = nbl * a.W;
+  if (work <= 0) return hipSuccess;
+  if (work > 0x7FFFFFF0LL) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)((work + 7) / 8 * 8));
+  switch (epi) {
+    case EPI_UP_SWIGLU: k_ffn_gemm_a8<EPI_UP_SWIGLU><<<grid, kWaves * 64, 0, s>>>(a, row_scale); break;
+    case EPI_UP_RELU: k_ffn_gemm_a8<EPI_UP_RELU><<<grid, kWaves * 64, 0, s>>>(a, row_scale); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

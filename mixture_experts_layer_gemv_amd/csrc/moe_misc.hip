@@ -1,5 +1,6 @@
 // Supporting kernels: init-time weight packing, the fp32 expert FFN, the
 // standalone weighted combine and small elementwise passes.
+#include "moe_convert.hpp"
 #include "moe_kernels.hpp"
 
 namespace moe {
@@ -370,38 +371,15 @@ hipError_t launch_combine(const float* y_perm, const int32_t* inv_perm, const fl
 // significant bits, so bf16 holds the quantised value exactly and the decode
 // kernels read it unchanged.
 
-// E4M3 magnitude code of v / 2^X for |v| / 2^X <= 448: round to nearest,
-// ties to even, on the format's grid (quantum 2^-9 below 2^-6, 2^(e-3) in
-// [2^e, 2^(e+1))).
-__device__ __forceinline__ uint32_t e4m3_code(float a) {
-  if (a >= 448.0f) return 0x7Eu;
-  if (a < 0.015625f) return (uint32_t)rintf(a * 512.0f);  // multiples of 2^-9; 8 is the smallest normal
-  int e2;
-  frexpf(a, &e2);  // a in [2^(e2-1), 2^e2)
-  int e = e2 - 1;
-  float q = rintf(ldexpf(a, 3 - e));  // in [8, 16]
-  if (q == 16.0f) {
-    q = 8.0f;
-    ++e;
-  }
-  if (e > 8 || (e == 8 && q > 14.0f)) return 0x7Eu;
-  return (uint32_t)(((e + 7) << 3) | ((int)q - 8));
-}
-
-// The value of an E4M3 magnitude code.
-__device__ __forceinline__ float e4m3_mag(uint32_t c) {
-  const int ex = (int)(c >> 3), mt = (int)(c & 7);
-  return ex == 0 ? ldexpf((float)mt, -9) : ldexpf((float)(8 + mt), ex - 10);
-}
-
 // One workgroup per row: the row's maximum magnitude, its scale, then the
-// quantised row.
+// quantised row as bf16 values (xq) and/or as E4M3 codes (xc; the sign in
+// bit 7), each output skipped when its pointer is null.
 __global__ __launch_bounds__(256) void k_quant_rows_e4m3(const uint16_t* __restrict__ x, int m,
-                                                         uint16_t* __restrict__ xq, float* __restrict__ xs) {
+                                                         uint16_t* __restrict__ xq, uint8_t* __restrict__ xc,
+                                                         float* __restrict__ xs) {
   __shared__ float red[4];
   const int t = blockIdx.x, tid = threadIdx.x;
   const uint4* row = reinterpret_cast<const uint4*>(x + (size_t)t * m);
-  uint4* out = reinterpret_cast<uint4*>(xq + (size_t)t * m);
   const int n8 = m / 8;
   float amax = 0.0f;
   for (int i = tid; i < n8; i += 256) {
@@ -429,7 +407,7 @@ __global__ __launch_bounds__(256) void k_quant_rows_e4m3(const uint16_t* __restr
   for (int i = tid; i < n8; i += 256) {
     const uint4 v = row[i];
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-    uint32_t o[4];
+    uint32_t o[4], c8[2] = {0u, 0u};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       uint32_t pair = 0;
@@ -437,20 +415,23 @@ __global__ __launch_bounds__(256) void k_quant_rows_e4m3(const uint16_t* __restr
       for (int h = 0; h < 2; ++h) {
         const uint16_t b = (uint16_t)(h ? w[j] >> 16 : w[j] & 0xFFFFu);
         const float a = ldexpf(fabsf(bf16_to_f32(b)), -X);  // exact
-        const float q = ldexpf(e4m3_mag(e4m3_code(a)), X);  // exact, a bf16 value
-        const uint32_t qb = (__float_as_uint(q) >> 16) | (b & 0x8000u);
-        pair |= qb << (16 * h);
+        const uint32_t code = e4m3_code(a);
+        const float q = ldexpf(e4m3_mag(code), X);  // exact, a bf16 value
+        pair |= ((__float_as_uint(q) >> 16) | (b & 0x8000u)) << (16 * h);
+        c8[j >> 1] |= (code | ((b >> 8) & 0x80u)) << (8 * (2 * (j & 1) + h));
       }
       o[j] = pair;
     }
-    out[i] = make_uint4(o[0], o[1], o[2], o[3]);
+    if (xq) reinterpret_cast<uint4*>(xq + (size_t)t * m)[i] = make_uint4(o[0], o[1], o[2], o[3]);
+    if (xc) reinterpret_cast<uint2*>(xc + (size_t)t * m)[i] = make_uint2(c8[0], c8[1]);
   }
 }
 
-hipError_t launch_quant_rows_e4m3(const uint16_t* x, int T, int m, uint16_t* xq, float* xs, hipStream_t s) {
+hipError_t launch_quant_rows_e4m3(const uint16_t* x, int T, int m, uint16_t* xq, uint8_t* xc, float* xs,
+                                  hipStream_t s) {
   if (T <= 0) return hipSuccess;
   if (m % 64) return hipErrorInvalidValue;
-  k_quant_rows_e4m3<<<dim3((unsigned)T), 256, 0, s>>>(x, m, xq, xs);
+  k_quant_rows_e4m3<<<dim3((unsigned)T), 256, 0, s>>>(x, m, xq, xc, xs);
   return hipGetLastError();
 }
 
