@@ -18,12 +18,13 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "moe_oracle.c")
 _LIB = os.path.join(_HERE, "libmoe_oracle.so")
 
-F32, BF16, I8, FP8, MXFP4, FP8A8 = 0, 1, 2, 3, 4, 5
+F32, BF16, I8, FP8, MXFP4, FP8A8, I8A8 = 0, 1, 2, 3, 4, 5, 6
 RELU, SWIGLU = 0, 1
 MAX_E = 64
 # weight dtypes by name (int4 weights are int8 values in [-7, 7] to the oracle;
-# "fp8a8" is fp8 weights with each token's expert input quantised to E4M3)
-_DT = {"f32": F32, "bf16": BF16, "i8": I8, "i4": I8, "fp8": FP8, "mxfp4": MXFP4, "fp8a8": FP8A8}
+# "fp8a8" / "i8a8": fp8 / int8 weights with each token's expert input
+# quantised to E4M3 / int8)
+_DT = {"f32": F32, "bf16": BF16, "i8": I8, "i4": I8, "fp8": FP8, "mxfp4": MXFP4, "fp8a8": FP8A8, "i8a8": I8A8}
 _KIND = {"relu": RELU, "swiglu": SWIGLU}
 
 
@@ -74,6 +75,7 @@ def lib():
         L.orc_weight_value.argtypes = [vp, vp, i32, i64, i64, i64, i64, i64, ctypes.POINTER(ctypes.c_double)]
         L.orc_e4m3_encode.argtypes = [vp, i64, vp]
         L.orc_quant_rows_e4m3.argtypes = [vp, i32, i32, i32, vp, vp, vp]
+        L.orc_quant_rows_i8.argtypes = [vp, i32, i32, i32, vp, vp, vp]
         L.orc_max_threads.restype = ctypes.c_int
         for f in ("orc_weight_value", "orc_norm", "orc_router_logits", "orc_topk", "orc_dispatch", "orc_expert_apply", "orc_expert_rows",
                   "orc_combine", "orc_forward_tokens", "orc_dense_masked"):
@@ -132,7 +134,7 @@ class Experts:
         elif self.w1.dtype == np.uint16:
             dt = BF16
         elif self.w1.dtype == np.int8:
-            dt = I8
+            dt = I8A8 if w_dtype == "i8a8" else I8
         else:
             raise TypeError(self.w1.dtype)
         self.E, self.m, self.p, self.w_dtype = E, m, p, dt
@@ -182,6 +184,18 @@ def quant_rows_e4m3(x):
     scales = np.empty(T, np.float32)
     _check(lib().orc_quant_rows_e4m3(_ptr(x), _xdt(x), T, m, _ptr(out), _ptr(codes), _ptr(scales)),
            "quant_rows_e4m3")
+    return out, codes, scales
+
+
+def quant_rows_i8(x):
+    """Per-row int8 quantisation of activations x [T][m] (fp32, or bf16 as
+    uint16): (values in double, int8 codes, fp32 scales)."""
+    x = _c(x)
+    T, m = x.shape
+    out = np.empty((T, m), np.float64)
+    codes = np.empty((T, m), np.int8)
+    scales = np.empty(T, np.float32)
+    _check(lib().orc_quant_rows_i8(_ptr(x), _xdt(x), T, m, _ptr(out), _ptr(codes), _ptr(scales)), "quant_rows_i8")
     return out, codes, scales
 
 

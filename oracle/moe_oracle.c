@@ -26,8 +26,9 @@
  *    for e4m3(code) * s[n], MXFP4 weights for e2m1(code) times the E8M0
  *    scale of their block of 32 consecutive i (see weight() below).  With
  *    fp8 activations (ORC_FP8A8) each token's row is first quantised to
- *    E4M3 with one power-of-two scale per row (quant_row_e4m3 below); the
- *    router still reads the row unquantised.  Every dot
+ *    E4M3 with one power-of-two scale per row (quant_row_e4m3 below), with
+ *    int8 activations (ORC_I8A8) to int8 likewise (quant_row_i8); the router
+ *    still reads the row unquantised.  Every dot
  *    product of length n is a0*b0 followed by n-1 multiply-adds, and an
  *    operation counter records each multiply and each add.
  *  - combine: y[t] = sum over the token's selections, in ascending expert
@@ -119,6 +120,14 @@ static uint8_t e4m3_encode(double v) {
   return sign | (uint8_t)(((e + 7) << 3) | ((int)q - 8));
 }
 
+/* The smallest X with amax <= qmax * 2^X (amax > 0). */
+static int pow2_exponent(double amax, double qmax) {
+  int X = (int)ceil(log2(amax / qmax));
+  while (amax > qmax * ldexp(1.0, X)) ++X; /* guard the boundary against log2's rounding */
+  while (amax <= qmax * ldexp(1.0, X - 1)) --X;
+  return X;
+}
+
 /* One row of m activations quantised to E4M3 with a per-row power-of-two
  * scale: s = 2^X with X the smallest integer such that max|x| <= 448 * 2^X
  * (so no element saturates), code = e4m3(x / s) (the division by a power of
@@ -127,17 +136,30 @@ static uint8_t e4m3_encode(double v) {
 static void quant_row_e4m3(const double* x, int m, double* out, uint8_t* codes, float* scale) {
   double amax = 0.0;
   for (int i = 0; i < m; ++i) amax = fabs(x[i]) > amax ? fabs(x[i]) : amax;
-  int X = 0;
-  if (amax > 0.0) {
-    X = (int)ceil(log2(amax / 448.0));
-    while (amax > 448.0 * ldexp(1.0, X)) ++X; /* guard the boundary against log2's rounding */
-    while (amax <= 448.0 * ldexp(1.0, X - 1)) --X;
-  }
+  const int X = amax > 0.0 ? pow2_exponent(amax, 448.0) : 0;
   const double sc = ldexp(1.0, X);
   for (int i = 0; i < m; ++i) {
     const uint8_t c = e4m3_encode(x[i] / sc);
     if (codes) codes[i] = c;
     out[i] = e4m3_value(c) * sc;
+  }
+  if (scale) *scale = (float)sc;
+}
+
+/* One row quantised to int8 with a per-row power-of-two scale s = 2^X, X the
+ * smallest integer with max|x| <= 127 * 2^X: q = x / s rounded to the nearest
+ * integer, ties to even (|q| <= 127; the division is exact), value q * s
+ * (exact in bf16: seven significant bits).  A row of zeros gives zeros
+ * (s = 1). */
+static void quant_row_i8(const double* x, int m, double* out, int8_t* codes, float* scale) {
+  double amax = 0.0;
+  for (int i = 0; i < m; ++i) amax = fabs(x[i]) > amax ? fabs(x[i]) : amax;
+  const int X = amax > 0.0 ? pow2_exponent(amax, 127.0) : 0;
+  const double sc = ldexp(1.0, X);
+  for (int i = 0; i < m; ++i) {
+    const double q = nearbyint(x[i] / sc);
+    if (codes) codes[i] = (int8_t)q;
+    out[i] = q * sc;
   }
   if (scale) *scale = (float)sc;
 }
@@ -155,7 +177,8 @@ static double weight(const void* w, const void* s, int dtype, int64_t e, int64_t
   switch (dtype) {
     case ORC_F32: return (double)((const float*)w)[i];
     case ORC_BF16: return bf16_bits_to_double(((const uint16_t*)w)[i]);
-    case ORC_I8: return (double)((const int8_t*)w)[i] * (double)((const float*)s)[e * N + n];
+    case ORC_I8:
+    case ORC_I8A8: return (double)((const int8_t*)w)[i] * (double)((const float*)s)[e * N + n];
     case ORC_FP8:
     case ORC_FP8A8: return e4m3_value(((const uint8_t*)w)[i]) * (double)((const float*)s)[e * N + n];
     default: return e2m1_value(((const uint8_t*)w)[i]) * e8m0_value(((const uint8_t*)s)[(e * (K / 32) + k / 32) * N + n]);
@@ -164,7 +187,7 @@ static double weight(const void* w, const void* s, int dtype, int64_t e, int64_t
 
 int orc_weight_value(const void* w, const void* s, int dtype, int64_t e, int64_t K, int64_t N, int64_t k, int64_t n,
                      double* out) {
-  if (!w || !out || dtype < ORC_F32 || dtype > ORC_FP8A8) return -1;
+  if (!w || !out || dtype < ORC_F32 || dtype > ORC_I8A8) return -1;
   if (dtype >= ORC_I8 && !s) return -1;
   if (dtype == ORC_MXFP4 && K % 32) return -1;
   *out = weight(w, s, dtype, e, K, N, k, n);
@@ -184,6 +207,18 @@ int orc_quant_rows_e4m3(const void* x, int x_dtype, int T, int m, double* out, u
   for (int t = 0; t < T; ++t) {
     for (int c = 0; c < m; ++c) xr[c] = act_at(x, x_dtype, (int64_t)t * m + c);
     quant_row_e4m3(xr, m, out + (int64_t)t * m, codes ? codes + (int64_t)t * m : NULL, scales ? scales + t : NULL);
+  }
+  free(xr);
+  return 0;
+}
+
+int orc_quant_rows_i8(const void* x, int x_dtype, int T, int m, double* out, int8_t* codes, float* scales) {
+  if (!x || !out || T < 0 || m < 1 || (x_dtype != ORC_F32 && x_dtype != ORC_BF16)) return -1;
+  double* xr = (double*)malloc(sizeof(double) * (size_t)m);
+  if (!xr) return -1;
+  for (int t = 0; t < T; ++t) {
+    for (int c = 0; c < m; ++c) xr[c] = act_at(x, x_dtype, (int64_t)t * m + c);
+    quant_row_i8(xr, m, out + (int64_t)t * m, codes ? codes + (int64_t)t * m : NULL, scales ? scales + t : NULL);
   }
   free(xr);
   return 0;
@@ -312,8 +347,11 @@ static void expert_row(const orc_experts* X, int e, const double* x_in, double* 
   const int dt = X->w_dtype;
   /* fp8 activations: the first projection reads the row quantised per token */
   const double* x = x_in;
-  if (dt == ORC_FP8A8) {
-    quant_row_e4m3(x_in, m, xq, NULL, NULL);
+  if (dt == ORC_FP8A8 || dt == ORC_I8A8) {
+    if (dt == ORC_FP8A8)
+      quant_row_e4m3(x_in, m, xq, NULL, NULL);
+    else
+      quant_row_i8(x_in, m, xq, NULL, NULL);
     x = xq;
   }
 
@@ -374,7 +412,7 @@ static int check_experts(const orc_experts* X) {
   if (!X || X->m < 1 || X->p < 1 || X->E < 1 || !X->w1 || !X->w2) return -1;
   if (X->kind != ORC_RELU && X->kind != ORC_SWIGLU) return -1;
   if (X->kind == ORC_SWIGLU && !X->w3) return -1;
-  if (X->w_dtype < ORC_F32 || X->w_dtype > ORC_FP8A8) return -1;
+  if (X->w_dtype < ORC_F32 || X->w_dtype > ORC_I8A8) return -1;
   if (X->w_dtype >= ORC_I8 && (!X->s1 || !X->s2 || (X->kind == ORC_SWIGLU && !X->s3))) return -1;
   if (X->w_dtype == ORC_MXFP4 && (X->m % 32 || X->p % 32)) return -1;
   return 0;

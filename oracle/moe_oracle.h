@@ -11,7 +11,7 @@
 
 #define ORC_MAX_E 64
 
-enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_I8 = 2, ORC_FP8 = 3, ORC_MXFP4 = 4, ORC_FP8A8 = 5 };
+enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_I8 = 2, ORC_FP8 = 3, ORC_MXFP4 = 4, ORC_FP8A8 = 5, ORC_I8A8 = 6 };
 enum { ORC_RELU = 0, ORC_SWIGLU = 1 };
 
 /* Expert weights in canonical row-major layout:
@@ -38,6 +38,9 @@ int orc_e4m3_encode(const float* v, int64_t n, uint8_t* codes);
  * smallest power of two with amax <= 448 s; out = e4m3(code) * s (double);
  * codes and scales when non-NULL. */
 int orc_quant_rows_e4m3(const void* x, int x_dtype, int T, int m, double* out, uint8_t* codes, float* scales);
+/* Per-row int8 quantisation: scale s = 2^X, the smallest power of two with
+ * amax <= 127 s; q = round-to-nearest-even(x / s); out = q * s. */
+int orc_quant_rows_i8(const void* x, int x_dtype, int T, int m, double* out, int8_t* codes, float* scales);
 
 int orc_router_logits(const void* x, int x_dtype, const float* wg, const float* bias, int T, int m, int E,
                       float* logits);

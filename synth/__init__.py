@@ -150,7 +150,7 @@ class LayerSpec:
     k: int
     kind: str  # "relu" | "swiglu"
     x_dtype: str  # "f32" | "bf16"
-    w_dtype: str  # "f32" | "bf16" | "i8" | "i4" | "fp8" | "fp8a8" | "mxfp4"
+    w_dtype: str  # "f32" | "bf16" | "i8" | "i8a8" | "i4" | "fp8" | "fp8a8" | "mxfp4"
     seed: int
     sigma_x: float = 1.0
     sigma_router: float = 0.02
@@ -161,7 +161,7 @@ class LayerSpec:
     def expert_bytes(self) -> int:
         """|E| of one expert: (mp + pm) * dtype for the two-matrix MLP, 3*m*p*dtype for SwiGLU."""
         nmat = 2 if self.kind == "relu" else 3
-        return int(nmat * self.m * self.p * {"f32": 4, "bf16": 2, "i8": 1, "i4": 0.5, "fp8": 1, "fp8a8": 1,
+        return int(nmat * self.m * self.p * {"f32": 4, "bf16": 2, "i8": 1, "i8a8": 1, "i4": 0.5, "fp8": 1, "fp8a8": 1,
                                              "mxfp4": 0.5 + 1 / 32}[self.w_dtype])
 
 
@@ -201,6 +201,10 @@ CONFIGS = {
                      note="Mixtral-8x7B-shaped prefill, E4M3 weights and per-token E4M3 activations"),
     "c13": LayerSpec("mixtral_decode_fp8a8", 64, 4096, 14336, 8, 2, "swiglu", "bf16", "fp8a8", 8,
                      note="Mixtral-8x7B-shaped decode, E4M3 weights and per-token E4M3 activations"),
+    # int8 weights and int8 activations (the INT8 GeMM with both operands
+    # quantised): the first projection on the int8 matrix cores
+    "c14": LayerSpec("mixtral_prefill_i8a8", 8192, 4096, 14336, 8, 2, "swiglu", "bf16", "i8a8", 6,
+                     note="Mixtral-8x7B-shaped prefill, int8 weights and per-token int8 activations"),
 }
 
 
@@ -238,7 +242,7 @@ def make_layer(sp: LayerSpec, with_x: bool = True, with_weights: bool = True) ->
             elif sp.w_dtype == "bf16":
                 out[key] = normal_bf16(sp.seed, tid, sp.sigma_w, shape)
             else:
-                quant = {"i8": int8_quant, "i4": int4_quant, "fp8": fp8_quant, "fp8a8": fp8_quant,
+                quant = {"i8": int8_quant, "i8a8": int8_quant, "i4": int4_quant, "fp8": fp8_quant, "fp8a8": fp8_quant,
                          "mxfp4": mxfp4_quant}[sp.w_dtype]
                 q, s = quant(sp.seed, tid, sp.sigma_w, *shape)
                 out[key] = q

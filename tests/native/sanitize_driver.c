@@ -46,6 +46,7 @@ static void layer(int dtype, int kind, int x_bf16) {
       case ORC_F32: w[i] = malloc(n * 4); synth_fill_normal_f32(3, 3 + i, 0.05, (int64_t)n, w[i]); break;
       case ORC_BF16: w[i] = malloc(n * 2); synth_fill_normal_bf16(3, 3 + i, 0.05, (int64_t)n, w[i]); break;
       case ORC_I8:
+      case ORC_I8A8:
         w[i] = malloc(n); s[i] = malloc((size_t)E * N * 4);
         OK(i % 2 ? synth_fill_intq_quant(3, 3 + i, 0.05, E, K, N, 7, w[i], s[i])
                  : synth_fill_int8_quant(3, 3 + i, 0.05, E, K, N, w[i], s[i]));
@@ -105,6 +106,7 @@ static void layer(int dtype, int kind, int x_bf16) {
     uint8_t* qc = malloc((size_t)T * m);
     float* qs = malloc((size_t)T * 4);
     OK(orc_quant_rows_e4m3(x, xdt, T, m, xn, qc, qs));
+    OK(orc_quant_rows_i8(x, xdt, T, m, xn, (int8_t*)qc, qs));
     OK(orc_e4m3_encode(tw, (int64_t)T * k, qc));
     free(qc);
     free(qs);
@@ -117,8 +119,8 @@ static void layer(int dtype, int kind, int x_bf16) {
 }
 
 int main(void) {
-  const int dtypes[6] = {ORC_F32, ORC_BF16, ORC_I8, ORC_FP8, ORC_MXFP4, ORC_FP8A8};
-  for (int d = 0; d < 6; ++d)
+  const int dtypes[7] = {ORC_F32, ORC_BF16, ORC_I8, ORC_FP8, ORC_MXFP4, ORC_FP8A8, ORC_I8A8};
+  for (int d = 0; d < 7; ++d)
     for (int kind = 0; kind < 2; ++kind) layer(dtypes[d], kind, dtypes[d] != ORC_F32);
   if (bad) return 1;
   printf("sanitized run ok\n");

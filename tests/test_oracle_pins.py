@@ -508,7 +508,7 @@ def test_single_float_weight_expert_is_dense_mlp(orc, syn, kind, w_dtype):
     assert np.allclose(r["y"], ref.numpy(), rtol=1e-12, atol=1e-12)
 
 
-@pytest.mark.parametrize("w_dtype", ["fp8", "fp8a8", "mxfp4"])
+@pytest.mark.parametrize("w_dtype", ["fp8", "fp8a8", "i8a8", "mxfp4"])
 @pytest.mark.parametrize("E,k", [(3, 2), (8, 2), (8, 8)])
 def test_float_weights_routed_equals_dense_masked(orc, syn, w_dtype, E, k):
     L = _layer(syn, 8, 64, 64, E, k, "swiglu", w_dtype, seed=E * 11 + k)
@@ -648,6 +648,65 @@ def test_fp8a8_single_expert_is_dense_mlp_on_quantised_rows(orc, syn, kind):
     # the same weights without the activation quantisation give another result
     L8 = dict(L)
     L8["spec"] = dataclasses.replace(L["spec"], w_dtype="fp8")
+    r8 = orc.layer_forward(orc.Experts.from_layer(L8), L["x"], L["wg"], None, 1)
+    assert not np.allclose(r8["y"], r["y"], rtol=1e-6, atol=0)
+
+
+# ---- int8 activations (per-token int8 quantisation of the expert input) ----
+
+def test_per_token_int8_quantisation_closed_forms(orc, syn):
+    """The scale of a row is the smallest power of two s with max|x| <= 127 s
+    (so max|x| / s lies in (63.5, 127]); q is numpy's round-half-even of x / s
+    (exact in fp64); |q| <= 127; the value q * s is a bf16 value within s / 2
+    of x; a row of zeros stays zero."""
+    T, m = 40, 256
+    x = syn.normal_bf16(6, syn.TID_X, 1.0, (T, m))
+    x[3] = 0
+    x64 = _to64(syn, x)
+    x64[9] *= 2.0**-25
+    x64[10, :4] = [127.0, -63.5, 0.5, 1.5]  # max 127 (scale 1); ties at 0.5 and 1.5 and -63.5
+    x64[10, 4:] = 0.0
+    x = torch.from_numpy(x64.astype(np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(_to64(syn, x), x64)
+    val, codes, scales = orc.quant_rows_i8(x)
+    amax = np.abs(x64).max(axis=1)
+    nz = amax > 0
+    sc = scales.astype(np.float64)
+    assert np.all(np.frexp(sc)[0] == 0.5)
+    r = amax[nz] / sc[nz]
+    assert np.all((r > 63.5) & (r <= 127))
+    q = np.rint(x64 / sc[:, None])
+    assert np.array_equal(codes.astype(np.float64), q)
+    assert np.abs(codes.astype(np.int64)).max() <= 127
+    assert np.array_equal(val, q * sc[:, None])
+    assert np.all(val[~nz] == 0)
+    assert np.array_equal(torch.from_numpy(val).to(torch.bfloat16).double().numpy(), val)
+    assert np.all(np.abs(val - x64) <= sc[:, None] / 2)
+    assert sc[10] == 1.0 and codes[10, :4].tolist() == [127, -64, 0, 2]
+
+
+@pytest.mark.parametrize("kind", ["relu", "swiglu"])
+def test_i8a8_single_expert_is_dense_mlp_on_quantised_rows(orc, syn, kind):
+    """E = 1, k = 1 with int8 activations equals the torch fp64 chain on rows
+    quantised with numpy (power-of-two scale, round half to even) and the int8
+    weights times their per-channel scales."""
+    L = _layer(syn, 9, 64, 96, 1, 1, kind, "i8a8", seed=80)
+    X = orc.Experts.from_layer(L)
+    r = orc.layer_forward(X, L["x"], L["wg"], None, 1)
+
+    def deq(key):
+        return torch.from_numpy(L[key][0].astype(np.float64) * L["s" + key[1:]][0].astype(np.float64)[None, :])
+
+    x64 = _to64(syn, L["x"])
+    sc = 2.0 ** np.ceil(np.log2(np.abs(x64).max(axis=1) / 127.0))
+    xq = torch.from_numpy(np.rint(x64 / sc[:, None]) * sc[:, None])
+    if kind == "relu":
+        ref = torch.relu(xq @ deq("w1")) @ deq("w2")
+    else:
+        ref = (torch.nn.functional.silu(xq @ deq("w1")) * (xq @ deq("w3"))) @ deq("w2")
+    assert np.allclose(r["y"], ref.numpy(), rtol=1e-12, atol=1e-12)
+    L8 = dict(L)
+    L8["spec"] = dataclasses.replace(L["spec"], w_dtype="i8")
     r8 = orc.layer_forward(orc.Experts.from_layer(L8), L["x"], L["wg"], None, 1)
     assert not np.allclose(r8["y"], r["y"], rtol=1e-6, atol=0)
 
