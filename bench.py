@@ -35,10 +35,10 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
-MFMA_FP8_PEAK_TFLOPS = 5000.0  # MI355X dense fp8
+MFMA_FP8_PEAK_TFLOPS = 5000.0  # MI355X dense fp8 (and int8, in TOP/s)
 METRIC = "MoE layer tokens/s; achieved HBM GB/s (T≤64) or MFMA TFLOP/s (T≥4096)"
 HEADLINE = "c4"
-OTHERS = ["c1", "c2", "c3", "c5", "c6", "c9", "c10", "c13", "c7", "c8", "c11", "c12"]
+OTHERS = ["c1", "c2", "c3", "c5", "c6", "c9", "c10", "c13", "c7", "c8", "c11", "c12", "c14"]
 TRAFFIC_DIR = os.path.join(ROOT, "profiles")
 _CSRC = "mixture_experts_layer_gemv_amd/csrc/"
 _SKINNY = [_CSRC + f for f in
@@ -58,7 +58,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=None,
-                    help="time only this layer (c1..c13); default: the prefill layer with every other layer beside it")
+                    help="time only this layer (c1..c14); default: the prefill layer with every other layer beside it")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
@@ -86,12 +86,12 @@ def algorithmic(sp, counts):
     Activation bytes: x read, hidden H written and read back (bf16), y
     written.  Flops: 2*m*p per row per m x p matrix (the pages' |O| rounds to
     this)."""
-    wb = {"f32": 4, "bf16": 2, "i8": 1, "i4": 0.5, "fp8": 1, "fp8a8": 1, "mxfp4": 0.5 + 1 / 32}[sp.w_dtype]
+    wb = {"f32": 4, "bf16": 2, "i8": 1, "i8a8": 1, "i4": 0.5, "fp8": 1, "fp8a8": 1, "mxfp4": 0.5 + 1 / 32}[sp.w_dtype]
     ab = 4 if sp.x_dtype == "f32" else 2
     G = 2 if sp.kind == "swiglu" else 1
     touched = sum(1 for c in counts if c > 0)
     rows = sp.T * sp.k
-    q = sp.w_dtype in ("i8", "i4", "fp8", "fp8a8")  # fp32 per-channel scales (MXFP4's block scales are in wb)
+    q = sp.w_dtype in ("i8", "i8a8", "i4", "fp8", "fp8a8")  # fp32 per-channel scales (MXFP4's are in wb)
     up_w = int(touched * G * sp.m * sp.p * wb) + (touched * G * sp.p * 4 if q else 0)
     dn_w = int(touched * sp.p * sp.m * wb) + (touched * sp.m * 4 if q else 0)
     h_bytes = rows * sp.p * (4 if sp.w_dtype == "f32" else 2)
@@ -251,10 +251,10 @@ def measure(key, args, headline):
     if dominant == "gemm_up":
         # fp8 activations: the up projection multiplies on the fp8 matrix
         # cores (its own peak), the down projection in bf16
-        up_peak = MFMA_FP8_PEAK_TFLOPS if sp.w_dtype == "fp8a8" else MFMA_BF16_PEAK_TFLOPS
+        up_peak = MFMA_FP8_PEAK_TFLOPS if sp.w_dtype in ("fp8a8", "i8a8") else MFMA_BF16_PEAK_TFLOPS
         achieved = A["up_flop"] / (dom_us * 1e-6) / 1e12
-        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": up_peak, "unit": "TFLOP/s",
-                "frac": round(achieved / up_peak, 4)}
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": up_peak,
+                "unit": "TOP/s" if sp.w_dtype == "i8a8" else "TFLOP/s", "frac": round(achieved / up_peak, 4)}
         work = {"algorithmic_flop": A["up_flop"]}
         ideal_s = (A["up_flop"] / up_peak + (A["layer_flop"] - A["up_flop"]) / MFMA_BF16_PEAK_TFLOPS) / 1e12
         layer_frac = {"bound": "mfma", "tflops": round(A["layer_flop"] / (ms * 1e-3) / 1e12, 2),
@@ -274,7 +274,8 @@ def measure(key, args, headline):
     out.update({
         "ms_per_step_with_kernel_events": round(ms_events, 5),
         "dtype": {"f32": "f32", "bf16": "bf16", "i8": "bf16", "i4": "bf16", "fp8": "bf16",
-                  "fp8a8": "fp8" if dominant == "gemm_up" else "bf16", "mxfp4": "bf16"}[sp.w_dtype],
+                  "fp8a8": "fp8" if dominant == "gemm_up" else "bf16",
+                  "i8a8": "int8" if dominant == "gemm_up" else "bf16", "mxfp4": "bf16"}[sp.w_dtype],
         "config": {"workload": sp.name, "T": sp.T, "m": sp.m, "p": sp.p, "E": sp.E, "k": sp.k, "expert": sp.kind,
                    "weights": sp.w_dtype, "activations": sp.x_dtype, "parallelism": "none (1 GPU)"},
         "roofline": roof,
@@ -356,7 +357,7 @@ def measure_streamed(key, args, slots, beta_gbs):
     torch.cuda.empty_cache()
     bytes_step = (b1 - b0) / steps
     transfer_ms = bytes_step / (beta_gbs * 1e9) * 1e3
-    wb = {"bf16": 2, "i8": 1, "i4": 0.5, "fp8": 1, "fp8a8": 1, "mxfp4": 0.5}[sp.w_dtype]
+    wb = {"bf16": 2, "i8": 1, "i8a8": 1, "i4": 0.5, "fp8": 1, "fp8a8": 1, "mxfp4": 0.5}[sp.w_dtype]
     q_star = MFMA_BF16_PEAK_TFLOPS * 1e12 * wb / (2 * beta_gbs * 1e9)
     hidden = (transfer_ms + ms_resident - ms) / max(min(transfer_ms, ms_resident), 1e-9)
     return {"workload": sp.name, "slots": slots, "ms_per_step": round(ms, 3), "value": round(sp.T / (ms * 1e-3), 2),

@@ -58,7 +58,8 @@ typedef enum {
   MOE_I4 = 3,
   MOE_FP8 = 4,
   MOE_MXFP4 = 5,
-  MOE_FP8A8 = 6 /* fp8 weights and fp8 activations (moe_weights_create) */
+  MOE_FP8A8 = 6, /* fp8 weights and fp8 activations (moe_weights_create) */
+  MOE_I8A8 = 7   /* int8 weights and int8 activations (moe_weights_create) */
 } moe_dtype;
 typedef enum { MOE_MLP_RELU = 0, MOE_SWIGLU = 1 } moe_ffn_kind;
 
@@ -86,21 +87,26 @@ int moe_abi_version(void);
  *  m, p, E       hidden size, expert inner size, number of experts.
  *  kind          MOE_MLP_RELU (w1 = W1, w2 = W2, w_up must be NULL) or
  *                MOE_SWIGLU (w1 = gate W1, w_up = up W3, w2 = down W2).
- *  w_dtype       MOE_F32, MOE_BF16, MOE_I8, MOE_I4, MOE_FP8, MOE_FP8A8 or
- *                MOE_MXFP4.  MOE_FP8A8 takes the weights and scales of
+ *  w_dtype       MOE_F32, MOE_BF16, MOE_I8, MOE_I8A8, MOE_I4, MOE_FP8,
+ *                MOE_FP8A8 or MOE_MXFP4.  MOE_FP8A8 takes the weights and scales of
  *                MOE_FP8 and also quantises each token's input to the experts
  *                to E4M3 with one power-of-two scale per token (2^X, X the
  *                smallest integer with max|x| <= 448 * 2^X), as the
  *                DeepSpeed-Inference summary's INT8 GeMM quantises its
  *                activations (section 4); routing reads x unquantised.  At
  *                prefill sizes its first projection then runs on the fp8
- *                matrix cores.
+ *                matrix cores.  MOE_I8A8 likewise with the weights and scales
+ *                of MOE_I8 and the input quantised to int8 (scale 2^X, X the
+ *                smallest integer with max|x| <= 127 * 2^X, q = round-half-
+ *                even(x / 2^X)): the INT8 GeMM with both operands quantised,
+ *                its first projection on the int8 matrix cores at prefill
+ *                sizes.
  *  w1, w_up      device [E][m][p] in w_dtype (MOE_I4: one int8 per weight,
  *                holding q in [-8, 7], stored packed two per byte; MOE_FP8:
  *                (and MOE_FP8A8) one OCP E4M3 code per byte; MOE_MXFP4: one E2M1 code per
  *                byte in its low nibble, stored packed two per byte).
  *  w2            device [E][p][m] in w_dtype (as above).
- *  s1, s_up      MOE_I8 / MOE_I4 / MOE_FP8 / MOE_FP8A8: device fp32 [E][p] per-output-
+ *  s1, s_up      MOE_I8 / MOE_I8A8 / MOE_I4 / MOE_FP8 / MOE_FP8A8: device fp32 [E][p] per-output-
  *                channel scales of w1 and w_up (the weight is q * s, or
  *                e4m3(code) * s).  MOE_MXFP4: device uint8 [E][m/32][p] E8M0
  *                exponents, one per block of 32 consecutive rows k of a column
@@ -293,6 +299,10 @@ moe_status moe_combine(const float* y_perm, const int32_t* inv_perm, const float
  *  16-byte aligned x and xq.  Errors: INVALID_ARG, UNSUPPORTED, HIP.
  */
 moe_status moe_quantize_rows_e4m3(const void* x, int T, int m, void* xq, float* scale, void* stream);
+/* The int8 form for MOE_I8A8 layers: scale[t] = 2^X, X the smallest integer
+ * with max_i |x[t][i]| <= 127 * 2^X; xq[t][i] = round-half-even(x[t][i] /
+ * scale[t]) * scale[t] (bf16, exact).  Arguments and errors as above. */
+moe_status moe_quantize_rows_i8(const void* x, int T, int m, void* xq, float* scale, void* stream);
 
 /*
  * moe_layer_forward -- the whole layer: route + top-k, dispatch, experts and

@@ -17,7 +17,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe_gemv.so")
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP, MOE_ERR_OOM = range(6)
-MOE_F32, MOE_BF16, MOE_I8, MOE_I4, MOE_FP8, MOE_MXFP4, MOE_FP8A8 = 0, 1, 2, 3, 4, 5, 6
+MOE_F32, MOE_BF16, MOE_I8, MOE_I4, MOE_FP8, MOE_MXFP4, MOE_FP8A8, MOE_I8A8 = 0, 1, 2, 3, 4, 5, 6, 7
 MOE_MLP_RELU, MOE_SWIGLU = 0, 1
 MOE_ROUTE_LOGITS_IN = 1
 MOE_NORM_NONE, MOE_NORM_LAYER, MOE_NORM_RMS = 0, 1, 2
@@ -75,6 +75,7 @@ _SIGS = {
     "moe_expert_ffn": ([_vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _sz, _vp], _i32),
     "moe_combine": ([_vp, _vp, _vp, _i32, _i32, _i32, _vp, _i32, _vp], _i32),
     "moe_quantize_rows_e4m3": ([_vp, _i32, _i32, _vp, _vp, _vp], _i32),
+    "moe_quantize_rows_i8": ([_vp, _i32, _i32, _vp, _vp, _vp], _i32),
     "moe_layer_forward": ([_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _i32, _vp, _sz,
                            _vp, _vp, _vp, _vp, _vp, _vp, _vp], _i32),
     "moe_layer_forward_fused": ([_vp, _vp, _vp, _vp, _i32, _i32, _vp, _vp, ctypes.c_float, _vp, _i32, _i32, _i32,
@@ -210,6 +211,10 @@ def moe_combine(y_perm, inv_perm, topk_w, T, m, k, y, y_dtype, stream=None):
 
 def moe_quantize_rows_e4m3(x, T, m, xq, scale, stream=None):
     _check("moe_quantize_rows_e4m3", lib().moe_quantize_rows_e4m3(_p(x), T, m, _p(xq), _p(scale), _s(stream)))
+
+
+def moe_quantize_rows_i8(x, T, m, xq, scale, stream=None):
+    _check("moe_quantize_rows_i8", lib().moe_quantize_rows_i8(_p(x), T, m, _p(xq), _p(scale), _s(stream)))
 
 
 def moe_layer_forward(w, w_router, b_router, x, x_dtype, T, m, p, E, k, y, y_dtype, workspace, ws_bytes,

@@ -131,19 +131,24 @@ moe_status check_shape(int T, int m, int p, int E, int k) {
   return MOE_OK;
 }
 
-bool valid_dtype(int d) { return d >= MOE_F32 && d <= MOE_FP8A8; }
+bool valid_dtype(int d) { return d >= MOE_F32 && d <= MOE_I8A8; }
 
 // Quantised weights (int8, int4, fp8 or MXFP4, each with its scales).
-bool quantised(int d) { return d == MOE_I8 || d == MOE_I4 || d == MOE_FP8 || d == MOE_FP8A8 || d == MOE_MXFP4; }
+bool quantised(int d) {
+  return d == MOE_I8 || d == MOE_I8A8 || d == MOE_I4 || d == MOE_FP8 || d == MOE_FP8A8 || d == MOE_MXFP4;
+}
 
-// fp8 activations: the experts read each token's row quantised to E4M3.
-bool act8(const LayerCfg& c) { return c.w_dtype == MOE_FP8A8; }
+// 8-bit activations: the experts read each token's row quantised to E4M3
+// (MOE_FP8A8) or int8 (MOE_I8A8).
+bool act8(const LayerCfg& c) { return c.w_dtype == MOE_FP8A8 || c.w_dtype == MOE_I8A8; }
+bool act_int8(const LayerCfg& c) { return c.w_dtype == MOE_I8A8; }
 
 // Weight-kind code of the kernels' variants: 0 bf16, 8 int8, 9 fp8, 4 int4,
 // 5 MXFP4 (the tens of bits of a weight, and which of its kinds).
 int weight_code(int d) {
   switch (d) {
-    case MOE_I8: return 8;
+    case MOE_I8:
+    case MOE_I8A8: return 8;
     case MOE_FP8:
     case MOE_FP8A8: return 9;
     case MOE_I4: return 4;
@@ -430,7 +435,7 @@ moe_status quant_input(const LayerCfg& c, FfnIo& io, char* ws, const Ws& L, hipS
   uint8_t* xc = gemm ? reinterpret_cast<uint8_t*>(ws + L.xq) : nullptr;
   float* xs = reinterpret_cast<float*>(ws + L.xs);
   const uint16_t* x = static_cast<const uint16_t*>(io.x);
-  MOE_TRY_HIP(run("quant_rows", s, [&] { return moe::launch_quant_rows_e4m3(x, io.T, c.m, xq, xc, xs, s); }));
+  MOE_TRY_HIP(run("quant_rows", s, [&] { return moe::launch_quant_rows(x, io.T, c.m, act_int8(c), xq, xc, xs, s); }));
   if (gemm) {
     io.xc = xc;
     io.rs = reinterpret_cast<float*>(ws + L.rs);
@@ -507,7 +512,7 @@ moe_status run_gemm(const moe_weights* W, const FfnIo& io, float* y_rows, hipStr
     pk.rows = io.rows >= 0 ? (int)io.rows : -1;
     MOE_TRY_HIP(run("pack_rows", s, [&] { return moe::launch_pack_rows_a8(pk, s); }));
     g.act = reinterpret_cast<const uint16_t*>(io.xp);
-    MOE_TRY_HIP(run("gemm_up", s, [&] { return moe::launch_ffn_gemm_a8(g, io.rs, up_epi, s); }));
+    MOE_TRY_HIP(run("gemm_up", s, [&] { return moe::launch_ffn_gemm_a8(g, io.rs, up_epi, act_int8(c), s); }));
   } else {
     MOE_TRY_HIP(run("gemm_up", s, [&] { return moe::launch_ffn_gemm(g, up_epi, qb, s); }));
   }
@@ -1182,7 +1187,8 @@ moe_status moe_combine(const float* y_perm, const int32_t* inv_perm, const float
   return ok();
 }
 
-moe_status moe_quantize_rows_e4m3(const void* x, int T, int m, void* xq, float* scale, void* stream) {
+// (shared by the two quantisation entry points)
+static moe_status quantize_rows(const void* x, int T, int m, bool int8, void* xq, float* scale, void* stream) {
   if (T < 0 || m <= 0) return fail(MOE_ERR_INVALID_ARG, "bad sizes T=%d m=%d", T, m);
   if (m % 64) return fail(MOE_ERR_UNSUPPORTED, "m=%d must be a multiple of 64", m);
   if (T == 0) return ok();
@@ -1190,10 +1196,18 @@ moe_status moe_quantize_rows_e4m3(const void* x, int T, int m, void* xq, float* 
   if (!aligned16(x) || !aligned16(xq)) return fail(MOE_ERR_INVALID_ARG, "x/xq must be 16-byte aligned");
   const hipStream_t s = as_stream(stream);
   MOE_TRY_HIP(run("quant_rows", s, [&] {
-    return moe::launch_quant_rows_e4m3(static_cast<const uint16_t*>(x), T, m, static_cast<uint16_t*>(xq), nullptr,
-                                       scale, s);
+    return moe::launch_quant_rows(static_cast<const uint16_t*>(x), T, m, int8, static_cast<uint16_t*>(xq), nullptr,
+                                  scale, s);
   }));
   return ok();
+}
+
+moe_status moe_quantize_rows_e4m3(const void* x, int T, int m, void* xq, float* scale, void* stream) {
+  return quantize_rows(x, T, m, false, xq, scale, stream);
+}
+
+moe_status moe_quantize_rows_i8(const void* x, int T, int m, void* xq, float* scale, void* stream) {
+  return quantize_rows(x, T, m, true, xq, scale, stream);
 }
 
 }  // extern "C"

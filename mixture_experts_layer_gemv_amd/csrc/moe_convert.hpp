@@ -115,4 +115,16 @@ __device__ __forceinline__ float e4m3_mag(uint32_t c) {
   return ex == 0 ? ldexpf((float)mt, -9) : ldexpf((float)(8 + mt), ex - 10);
 }
 
+// The power-of-two exponent X of a row's activation scale: the smallest
+// integer with amax <= qmax * 2^X, qmax = 448 (E4M3) or 127 (int8), from the
+// exact binary form amax = f * 2^e, f in [1, 2): X = e - 8 when f <= 1.75
+// (E4M3), e - 6 when f <= 127/64 (int8), else one more.  0 for amax = 0.
+template <bool INT8>
+__device__ __forceinline__ int act_scale_exponent(float amax) {
+  if (!(amax > 0.0f)) return 0;
+  int e2;
+  const float f = 2.0f * frexpf(amax, &e2);  // amax = f * 2^(e2 - 1)
+  return INT8 ? (e2 - 1) - (f <= 127.0f / 64.0f ? 6 : 5) : (e2 - 1) - (f <= 1.75f ? 8 : 7);
+}
+
 }  // namespace moe

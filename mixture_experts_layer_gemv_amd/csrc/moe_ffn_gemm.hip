@@ -33,6 +33,8 @@
 // the matrix cores about half the time: the global -> LDS copies alone take
 // three quarters of its time, and with copies, LDS reads and products all
 // running the clock drops from ~2.4 to ~2.0 GHz.
+#include <type_traits>
+
 #include "moe_convert.hpp"
 #include "moe_dispatch_block.hpp"
 #include "moe_index.hpp"
@@ -450,7 +452,7 @@ __global__ __launch_bounds__(256) void k_pack_rows(const PackArgs A) {
   reinterpret_cast<u32x4_t*>(A.out)[frag * 64 + lane] = v;
 }
 
-// ---- fp8 x fp8: the up projection of fp8-activation layers -----------------------
+// ---- fp8 x fp8 and int8 x int8: the up projection of 8-bit-activation layers ------
 //
 // With the activations quantised to E4M3 per token (one power-of-two scale
 // each) and the weights in E4M3 with per-column scales, the first projection
@@ -465,7 +467,10 @@ __global__ __launch_bounds__(256) void k_pack_rows(const PackArgs A) {
 // (0..7)); a 32 x 64 product operand is two units, lane l = r + 32 g reading
 // the 16 bytes of unit lanes 2 g and 2 g + 1, so that A and B pair the same k
 // in every position.  Without scale operands (the per-token scale is a power
-// of two applied in the epilogue), only that pairing matters.
+// of two applied in the epilogue), only that pairing matters.  int8 layers
+// (the INT8 GeMM with both operands quantised) take the same units and
+// operands, with the stage's 64 k as two v_mfma_i32_32x32x32_i8 products
+// (exact int32 sums, converted in the epilogue).
 
 // Gathers E4M3 code rows into packed units (one wave per unit).
 __global__ __launch_bounds__(256) void k_pack_rows_a8(const PackA8Args A) {
@@ -500,6 +505,8 @@ __global__ __launch_bounds__(256) void k_pack_rows_a8(const PackA8Args A) {
 }
 
 typedef int i32x8_t __attribute__((ext_vector_type(8)));
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+typedef int i32x16_t __attribute__((ext_vector_type(16)));
 typedef float floatx16_t __attribute__((ext_vector_type(16)));
 
 // acc += a * b (32 x 32 x 64, E4M3 operands), accumulating in place.  The
@@ -510,9 +517,19 @@ __device__ __forceinline__ void mfma_f8(floatx16_t& acc, const i32x8_t& a, const
   asm volatile("s_nop 1\n\tv_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
 }
 
-template <int EPI>
+// The int8 form: the 64 k of a stage as two 32 x 32 x 32 products (the
+// operand's bytes 0-15, then 16-31), exact int32 sums.
+__device__ __forceinline__ void mfma_i8(i32x16_t& acc, const i32x8_t& a, const i32x8_t& b) {
+  const i32x4_t a0 = {a[0], a[1], a[2], a[3]}, a1 = {a[4], a[5], a[6], a[7]};
+  const i32x4_t b0 = {b[0], b[1], b[2], b[3]}, b1 = {b[4], b[5], b[6], b[7]};
+  asm volatile("s_nop 1\n\tv_mfma_i32_32x32x32_i8 %0, %1, %2, %0" : "+v"(acc) : "v"(a0), "v"(b0));
+  asm volatile("s_nop 1\n\tv_mfma_i32_32x32x32_i8 %0, %1, %2, %0" : "+v"(acc) : "v"(a1), "v"(b1));
+}
+
+template <int EPI, bool I8>
 __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_ffn_gemm_a8(
     const GemmArgs A, const float* __restrict__ row_scale) {
+  using acc_t = std::conditional_t<I8, i32x16_t, floatx16_t>;
   constexpr int G = EPI == EPI_UP_SWIGLU ? 2 : 1;
   constexpr int TPW = kNF / G;  // column tiles per wave
   constexpr int BM = 256, NAF = 16, NBF = 16, STAGES = 4, CPA = 2, CPB = 2, CPS = CPA + CPB;
@@ -563,13 +580,13 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
     _Pragma("unroll") for (int j = 0; j < CPB; ++j) copy_frag(bb_, boff[j], b_lds + st_ + j * kFrag); \
   } while (0)
 
-  floatx16_t acc[RB][2];
+  acc_t acc[RB][2];
 #pragma unroll
   for (int i = 0; i < RB; ++i)
 #pragma unroll
     for (int c = 0; c < 2; ++c)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) acc[i][c][v] = 0.0f;
+      for (int v = 0; v < 16; ++v) acc[i][c][v] = 0;
 #pragma unroll
   for (int i = 0; i < RB; ++i)
 #pragma unroll
@@ -595,8 +612,12 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
         rd(st_, NAF + wn * kNF + (G == 2 ? 2 * uh + c : 2 * c + uh), F.b[c]);                      \
   } while (0)
 #define MOE_MMA(F)                                                                                 \
-  _Pragma("unroll") for (int i = 0; i < RB; ++i) _Pragma("unroll") for (int c = 0; c < 2; ++c)     \
-      mfma_f8(acc[i][c], F.a[i], F.b[c]);
+  _Pragma("unroll") for (int i = 0; i < RB; ++i) _Pragma("unroll") for (int c = 0; c < 2; ++c) {   \
+    if constexpr (I8)                                                                              \
+      mfma_i8(acc[i][c], F.a[i], F.b[c]);                                                          \
+    else                                                                                           \
+      mfma_f8(acc[i][c], F.a[i], F.b[c]);                                                          \
+  }
 
   const int nsteps = U;
   {
@@ -662,10 +683,10 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
         if (row >= nrows) continue;
         const float rs = row_scale[prow0 + row];
         if constexpr (EPI == EPI_UP_SWIGLU) {
-          const float g = acc[i][0][v] * sc0 * rs, up = acc[i][1][v] * sc1 * rs;
+          const float g = (float)acc[i][0][v] * sc0 * rs, up = (float)acc[i][1][v] * sc1 * rs;
           A.h_out[packed_index(prow0 + row, col, A.N)] = f32_to_bf16(silu(g) * up);
         } else {
-          const float g = acc[i][c][v] * sc0 * rs;
+          const float g = (float)acc[i][c][v] * sc0 * rs;
           A.h_out[packed_index(prow0 + row, col, A.N)] = f32_to_bf16(g > 0.0f ? g : 0.0f);
         }
       }
@@ -735,7 +756,7 @@ hipError_t launch_pack_rows_a8(const PackA8Args& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_ffn_gemm_a8(const GemmArgs& a, const float* row_scale, int epi, hipStream_t s) {
+hipError_t launch_ffn_gemm_a8(const GemmArgs& a, const float* row_scale, int epi, bool int8, hipStream_t s) {
   if (a.K % 64 || a.N % 64 || a.K <= 0 || a.N <= 0 || a.cg < 1 || !a.scale0 || !row_scale) return hipErrorInvalidValue;
   if (epi == EPI_UP_SWIGLU && !a.scale1) return hipErrorInvalidValue;
   const int G = epi == EPI_UP_SWIGLU ? 2 : 1;
@@ -745,11 +766,17 @@ hipError_t launch_ffn_gemm_a8(const GemmArgs& a, const float* row_scale, int epi
   if (work <= 0) return hipSuccess;
   if (work > 0x7FFFFFF0LL) return hipErrorInvalidValue;
   const dim3 grid((unsigned)((work + 7) / 8 * 8));
-  switch (epi) {
-    case EPI_UP_SWIGLU: k_ffn_gemm_a8<EPI_UP_SWIGLU><<<grid, kWaves * 64, 0, s>>>(a, row_scale); break;
-    case EPI_UP_RELU: k_ffn_gemm_a8<EPI_UP_RELU><<<grid, kWaves * 64, 0, s>>>(a, row_scale); break;
+#define MOE_A8(EP, I8_)                                                       \
+  k_ffn_gemm_a8<EP, I8_><<<grid, kWaves * 64, 0, s>>>(a, row_scale);          \
+  break;
+  switch (epi * 2 + (int8 ? 1 : 0)) {
+    case EPI_UP_SWIGLU * 2: MOE_A8(EPI_UP_SWIGLU, false)
+    case EPI_UP_SWIGLU * 2 + 1: MOE_A8(EPI_UP_SWIGLU, true)
+    case EPI_UP_RELU * 2: MOE_A8(EPI_UP_RELU, false)
+    case EPI_UP_RELU * 2 + 1: MOE_A8(EPI_UP_RELU, true)
     default: return hipErrorInvalidValue;
   }
+#undef MOE_A8
   return hipGetLastError();
 }
 

@@ -203,7 +203,7 @@ hipError_t launch_pack_rows(const PackArgs& a, hipStream_t s);
 // starting on a 16-row boundary; padding rows are zero.  row_scale receives
 // each packed row's token scale (0 for padding rows).
 struct PackA8Args {
-  const uint8_t* codes;    // [T][K] E4M3 codes
+  const uint8_t* codes;    // [T][K] E4M3 (or int8) codes
   const float* scale;      // [T] per-token power-of-two scales
   const int32_t* perm;     // [T*k]
   const int32_t* offsets;  // [E+1]
@@ -214,11 +214,12 @@ struct PackA8Args {
 };
 hipError_t launch_pack_rows_a8(const PackA8Args& a, hipStream_t s);
 
-// The up projection on the fp8 matrix cores: packed E4M3 activation units
-// (act, with row_scale per packed row) times packed fp8 weights (w with
-// scale0/scale1 per column); epi EPI_UP_SWIGLU or EPI_UP_RELU; H out as for
-// launch_ffn_gemm.  K a multiple of 64, N a multiple of 64.
-hipError_t launch_ffn_gemm_a8(const GemmArgs& a, const float* row_scale, int epi, hipStream_t s);
+// The up projection on the fp8 (or, int8 true, the int8) matrix cores:
+// packed E4M3 (int8) activation units (act, with row_scale per packed row)
+// times packed fp8 (int8) weights (w with scale0/scale1 per column); epi
+// EPI_UP_SWIGLU or EPI_UP_RELU; H out as for launch_ffn_gemm.  K a multiple
+// of 64, N a multiple of 64.
+hipError_t launch_ffn_gemm_a8(const GemmArgs& a, const float* row_scale, int epi, bool int8, hipStream_t s);
 
 // ---- expert FFN, fp32 path ----------------------------------------------------
 
@@ -245,12 +246,12 @@ hipError_t launch_combine(const float* y_perm, const int32_t* inv_perm, const fl
                           int slices, size_t slice_stride, void* y, bool y_bf16, hipStream_t s,
                           const void* residual = nullptr);
 hipError_t launch_fill_zero(float* p, size_t n, hipStream_t s);
-// fp8 activations: each row of x (T rows of m bf16) quantised to E4M3 with a
-// per-row power-of-two scale; xq (if not null) receives e4m3(code) * scale as
-// bf16 (exact), xc (if not null) the codes, xs the scales.  m is a multiple
-// of 64.
-hipError_t launch_quant_rows_e4m3(const uint16_t* x, int T, int m, uint16_t* xq, uint8_t* xc, float* xs,
-                                  hipStream_t s);
+// fp8 / int8 activations: each row of x (T rows of m bf16) quantised to E4M3
+// (or int8) with a per-row power-of-two scale; xq (if not null) receives the
+// quantised values as bf16 (exact), xc (if not null) the codes, xs the
+// scales.  m is a multiple of 64.
+hipError_t launch_quant_rows(const uint16_t* x, int T, int m, bool int8, uint16_t* xq, uint8_t* xc, float* xs,
+                             hipStream_t s);
 hipError_t launch_f32_to_bf16(const float* src, uint16_t* dst, size_t n, hipStream_t s);
 
 }  // namespace moe

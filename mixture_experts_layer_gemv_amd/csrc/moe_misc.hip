@@ -372,11 +372,14 @@ hipError_t launch_combine(const float* y_perm, const int32_t* inv_perm, const fl
 // kernels read it unchanged.
 
 // One workgroup per row: the row's maximum magnitude, its scale, then the
-// quantised row as bf16 values (xq) and/or as E4M3 codes (xc; the sign in
-// bit 7), each output skipped when its pointer is null.
-__global__ __launch_bounds__(256) void k_quant_rows_e4m3(const uint16_t* __restrict__ x, int m,
-                                                         uint16_t* __restrict__ xq, uint8_t* __restrict__ xc,
-                                                         float* __restrict__ xs) {
+// quantised row as bf16 values (xq) and/or as codes (xc: E4M3 with the sign
+// in bit 7, or int8), each output skipped when its pointer is null.  The
+// int8 form: scale 2^X, X the smallest integer with max|x| <= 127 * 2^X, q =
+// x / 2^X rounded half to even (|q| <= 127); q * 2^X has seven significant
+// bits, so bf16 holds it exactly too.
+template <bool INT8>
+__global__ __launch_bounds__(256) void k_quant_rows(const uint16_t* __restrict__ x, int m, uint16_t* __restrict__ xq,
+                                                    uint8_t* __restrict__ xc, float* __restrict__ xs) {
   __shared__ float red[4];
   const int t = blockIdx.x, tid = threadIdx.x;
   const uint4* row = reinterpret_cast<const uint4*>(x + (size_t)t * m);
@@ -396,13 +399,7 @@ __global__ __launch_bounds__(256) void k_quant_rows_e4m3(const uint16_t* __restr
   if ((tid & 63) == 0) red[tid >> 6] = amax;
   __syncthreads();
   amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  // X: amax = f * 2^e with f in [1, 2); amax <= 448 * 2^X = 1.75 * 2^(X + 8)
-  int X = 0;
-  if (amax > 0.0f) {
-    int e2;
-    const float fr = frexpf(amax, &e2);  // amax = fr * 2^e2, fr in [0.5, 1)
-    X = (e2 - 1) - (2.0f * fr <= 1.75f ? 8 : 7);
-  }
+  const int X = act_scale_exponent<INT8>(amax);
   if (tid == 0) xs[t] = ldexpf(1.0f, X);
   for (int i = tid; i < n8; i += 256) {
     const uint4 v = row[i];
@@ -415,10 +412,13 @@ __global__ __launch_bounds__(256) void k_quant_rows_e4m3(const uint16_t* __restr
       for (int h = 0; h < 2; ++h) {
         const uint16_t b = (uint16_t)(h ? w[j] >> 16 : w[j] & 0xFFFFu);
         const float a = ldexpf(fabsf(bf16_to_f32(b)), -X);  // exact
-        const uint32_t code = e4m3_code(a);
-        const float q = ldexpf(e4m3_mag(code), X);  // exact, a bf16 value
+        // E4M3: the magnitude's code and the sign bit; int8: the magnitude
+        // rounded half to even (<= 127), its two's complement with the sign
+        const uint32_t mag = INT8 ? (uint32_t)rintf(a) : e4m3_code(a);
+        const float q = ldexpf(INT8 ? (float)mag : e4m3_mag(mag), X);  // exact, a bf16 value
         pair |= ((__float_as_uint(q) >> 16) | (b & 0x8000u)) << (16 * h);
-        c8[j >> 1] |= (code | ((b >> 8) & 0x80u)) << (8 * (2 * (j & 1) + h));
+        const uint32_t code = INT8 ? ((b & 0x8000u) ? (0u - mag) & 0xFFu : mag) : (mag | ((b >> 8) & 0x80u));
+        c8[j >> 1] |= code << (8 * (2 * (j & 1) + h));
       }
       o[j] = pair;
     }
@@ -427,11 +427,14 @@ __global__ __launch_bounds__(256) void k_quant_rows_e4m3(const uint16_t* __restr
   }
 }
 
-hipError_t launch_quant_rows_e4m3(const uint16_t* x, int T, int m, uint16_t* xq, uint8_t* xc, float* xs,
-                                  hipStream_t s) {
+hipError_t launch_quant_rows(const uint16_t* x, int T, int m, bool int8, uint16_t* xq, uint8_t* xc, float* xs,
+                             hipStream_t s) {
   if (T <= 0) return hipSuccess;
   if (m % 64) return hipErrorInvalidValue;
-  k_quant_rows_e4m3<<<dim3((unsigned)T), 256, 0, s>>>(x, m, xq, xc, xs);
+  if (int8)
+    k_quant_rows<true><<<dim3((unsigned)T), 256, 0, s>>>(x, m, xq, xc, xs);
+  else
+    k_quant_rows<false><<<dim3((unsigned)T), 256, 0, s>>>(x, m, xq, xc, xs);
   return hipGetLastError();
 }
 

@@ -8,12 +8,12 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-from . import (MOE_BF16, MOE_F32, MOE_FP8, MOE_FP8A8, MOE_I4, MOE_I8, MOE_MLP_RELU, MOE_MXFP4, MOE_SWIGLU, moe_layer_forward,
+from . import (MOE_BF16, MOE_F32, MOE_FP8, MOE_FP8A8, MOE_I4, MOE_I8A8, MOE_I8, MOE_MLP_RELU, MOE_MXFP4, MOE_SWIGLU, moe_layer_forward,
                moe_layer_graph_create, moe_weights_create, moe_weights_destroy, moe_weights_offload,
                moe_weights_set_tuning, moe_workspace_size)
 
 DTYPE_CODE = {"f32": MOE_F32, "bf16": MOE_BF16, "i8": MOE_I8, "i4": MOE_I4, "fp8": MOE_FP8, "mxfp4": MOE_MXFP4,
-              "fp8a8": MOE_FP8A8}
+              "fp8a8": MOE_FP8A8, "i8a8": MOE_I8A8}
 KIND_CODE = {"relu": MOE_MLP_RELU, "swiglu": MOE_SWIGLU}
 
 

@@ -68,7 +68,7 @@ def test_weights_create_validation(lib):
         ((64, 64, 0, 1, 1, FAKE, FAKE, FAKE, Z, Z, Z), lib.MOE_ERR_INVALID_ARG),  # E < 1
         ((100, 64, 8, 1, 1, FAKE, FAKE, FAKE, Z, Z, Z), lib.MOE_ERR_UNSUPPORTED),  # m % 64
         ((64, 96, 8, 1, 1, FAKE, FAKE, FAKE, Z, Z, Z), lib.MOE_ERR_UNSUPPORTED),  # p % 64
-        ((64, 64, 8, 1, 7, FAKE, FAKE, FAKE, Z, Z, Z), lib.MOE_ERR_UNSUPPORTED),  # dtype
+        ((64, 64, 8, 1, 8, FAKE, FAKE, FAKE, Z, Z, Z), lib.MOE_ERR_UNSUPPORTED),  # dtype
         ((64, 64, 8, 5, 1, FAKE, FAKE, FAKE, Z, Z, Z), lib.MOE_ERR_INVALID_ARG),  # kind
         ((64, 64, 8, 1, 1, FAKE, Z, FAKE, Z, Z, Z), lib.MOE_ERR_INVALID_ARG),  # SwiGLU without w_up
         ((64, 64, 8, 0, 1, FAKE, FAKE, FAKE, Z, Z, Z), lib.MOE_ERR_INVALID_ARG),  # ReLU with w_up
@@ -111,6 +111,8 @@ def test_stage_validation_without_gpu(lib):
     assert L.moe_quantize_rows_e4m3(FAKE + 8, 4, 64, FAKE, FAKE, Z) == lib.MOE_ERR_INVALID_ARG
     assert L.moe_quantize_rows_e4m3(FAKE, -1, 64, FAKE, FAKE, Z) == lib.MOE_ERR_INVALID_ARG
     assert L.moe_quantize_rows_e4m3(FAKE, 0, 64, FAKE, FAKE, Z) == lib.MOE_OK
+    assert L.moe_quantize_rows_i8(FAKE, 4, 96, FAKE, FAKE, Z) == lib.MOE_ERR_UNSUPPORTED
+    assert L.moe_quantize_rows_i8(FAKE, 4, 64, Z, FAKE, Z) == lib.MOE_ERR_INVALID_ARG
     # handle-based calls with a NULL handle
     assert L.moe_expert_ffn(Z, FAKE, 1, 4, 64, 64, 8, 2, FAKE, FAKE, FAKE, FAKE, 1 << 20, Z) == lib.MOE_ERR_INVALID_ARG
     assert L.moe_layer_forward(Z, FAKE, Z, FAKE, 1, 4, 64, 64, 8, 2, FAKE, 1, FAKE, 1 << 20,
@@ -176,4 +178,6 @@ def test_tuning_validation(lib):
     fp8 = lib.moe_workspace_size_for(4096, 14336, 8, 1, lib.MOE_FP8, None, 64, 2)
     fp8a8 = lib.moe_workspace_size_for(4096, 14336, 8, 1, lib.MOE_FP8A8, None, 64, 2)
     assert fp8a8 - fp8 == 64 * 4096 * 2 + 256
-    assert L.moe_workspace_size_for(64, 64, 8, 1, 7, None, 4, 2, ctypes.byref(n)) == lib.MOE_ERR_UNSUPPORTED
+    i8a8 = lib.moe_workspace_size_for(4096, 14336, 8, 1, lib.MOE_I8A8, None, 64, 2)
+    assert i8a8 - lib.moe_workspace_size_for(4096, 14336, 8, 1, lib.MOE_I8, None, 64, 2) == 64 * 4096 * 2 + 256
+    assert L.moe_workspace_size_for(64, 64, 8, 1, 8, None, 4, 2, ctypes.byref(n)) == lib.MOE_ERR_UNSUPPORTED

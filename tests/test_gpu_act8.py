@@ -1,13 +1,15 @@
-"""fp8 activations (MOE_FP8A8 layers) against the CPU oracle.
+"""8-bit activations (MOE_FP8A8 and MOE_I8A8 layers) against the CPU oracle.
 
-Each token's input to the experts is quantised to E4M3 with one power-of-two
-scale per token; the quantised values are bf16 values, so the layer's
-numbers are those of the oracle's fp8a8 expert on every path.  Checked: the
-quantisation step alone, bit for bit (codes are decided by floating point on
-both sides in the same exact arithmetic: a division by a power of two and a
-round-to-nearest-even), then the expert stage and the whole layer at the bf16
-bar over expert kinds, ragged and empty experts, every decode launch form and
-the grouped GEMM forced onto small shapes.
+Each token's input to the experts is quantised to E4M3 (or int8) with one
+power-of-two scale per token; the quantised values are bf16 values, so the
+layer's numbers are those of the oracle's fp8a8 (i8a8) expert on every path,
+and at prefill sizes the first projection multiplies the codes on the fp8
+(int8) matrix cores.  Checked: the quantisation step alone, bit for bit
+(codes are decided by floating point on both sides in the same exact
+arithmetic: a division by a power of two and a round-to-nearest-even), then
+the expert stage and the whole layer at the bf16 bar over expert kinds,
+ragged and empty experts, every decode launch form and the grouped GEMM
+forced onto small shapes.
 """
 import numpy as np
 import pytest
@@ -58,14 +60,20 @@ def _rows_under_test(T, m, seed):
     return xb
 
 
+@pytest.mark.parametrize("fmt", ["e4m3", "i8"])
 @pytest.mark.parametrize("T,m", [(8, 64), (40, 256), (300, 4096)])
-def test_quantize_rows_is_bit_exact(T, m):
+def test_quantize_rows_is_bit_exact(fmt, T, m):
     xb = _rows_under_test(T, m, seed=T + m)
-    val, codes, scales = oracle.quant_rows_e4m3(xb)
+    if fmt == "i8":  # rows whose maximum sits on 127 * 2^X, and the int8 ties
+        x64 = torch.from_numpy(xb.view(np.int16).copy()).view(torch.bfloat16).double().numpy()
+        x64[5, :8] = [127, 0.5, 1.5, -2.5, 126.5, -63.5, 3.5, 100]
+        x64[6] = x64[5] * 2.0**-9
+        xb = _bf16_bits(x64)
+    val, codes, scales = (oracle.quant_rows_i8 if fmt == "i8" else oracle.quant_rows_e4m3)(xb)
     x = to_device(xb)
     xq = torch.empty((T, m), dtype=torch.int16, device="cuda")
     sc = torch.empty(T, dtype=torch.float32, device="cuda")
-    M.moe_quantize_rows_e4m3(x, T, m, xq, sc)
+    (M.moe_quantize_rows_i8 if fmt == "i8" else M.moe_quantize_rows_e4m3)(x, T, m, xq, sc)
     torch.cuda.synchronize()
     got_s = sc.cpu().numpy()
     assert np.array_equal(got_s, scales), "scales"
@@ -94,11 +102,12 @@ def _layer_check(L):
     layer.close()
 
 
+@pytest.mark.parametrize("wd", ["fp8a8", "i8a8"])
 @pytest.mark.parametrize("kind", ["swiglu", "relu"])
 @pytest.mark.parametrize("T,m,p,E,k", SHAPES)
-def test_fp8a8_expert_stage_and_layer(kind, T, m, p, E, k):
-    log(f"fp8a8 kind={kind} T={T} m={m} p={p} E={E} k={k}")
-    L = synth.make_layer(spec(T, m, p, E, k, kind, "fp8a8", seed=T + p + 4, sw=0.05, sr=0.05))
+def test_act8_expert_stage_and_layer(wd, kind, T, m, p, E, k):
+    log(f"{wd} kind={kind} T={T} m={m} p={p} E={E} k={k}")
+    L = synth.make_layer(spec(T, m, p, E, k, kind, wd, seed=T + p + 4, sw=0.05, sr=0.05))
     layer = MoELayer(L)
     rng = np.random.default_rng(T + 1)
     idx = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
@@ -115,14 +124,15 @@ def test_fp8a8_expert_stage_and_layer(kind, T, m, p, E, k):
     _layer_check(L)
 
 
+@pytest.mark.parametrize("wd", ["fp8a8", "i8a8"])
 @pytest.mark.parametrize("mt", [1, 2])
 @pytest.mark.parametrize("pack", [0, 1])
 @pytest.mark.parametrize("waves", ["k", "n"])
-def test_fp8a8_decode_launch_modes(mt, pack, waves, tune):
+def test_act8_decode_launch_modes(wd, mt, pack, waves, tune):
     tune(ffn_path=M.MOE_PATH_SKINNY, skinny_mt=mt, skinny_pack=1 if pack else -1,
          skinny_splitk=1 if waves == "k" else -1)
-    log(f"fp8a8 modes mt={mt} pack={pack} waves={waves}")
-    _layer_check(synth.make_layer(spec(61, 256, 384, 8, 2, "swiglu", "fp8a8", seed=mt + 2 * pack + 1, zipf=1.2,
+    log(f"{wd} modes mt={mt} pack={pack} waves={waves}")
+    _layer_check(synth.make_layer(spec(61, 256, 384, 8, 2, "swiglu", wd, seed=mt + 2 * pack + 1, zipf=1.2,
                                        sw=0.05, sr=0.05)))
 
 
@@ -130,12 +140,13 @@ GEMM_SHAPES = [(5, 64, 128, 3, 2), (37, 192, 320, 8, 2), (300, 256, 512, 4, 2), 
                (1, 512, 384, 16, 2), (64, 128, 128, 64, 4), (700, 320, 192, 2, 1)]
 
 
+@pytest.mark.parametrize("wd", ["fp8a8", "i8a8"])
 @pytest.mark.parametrize("kind", ["swiglu", "relu"])
 @pytest.mark.parametrize("T,m,p,E,k", GEMM_SHAPES)
-def test_fp8a8_grouped_gemm(kind, T, m, p, E, k, tune):
+def test_act8_grouped_gemm(wd, kind, T, m, p, E, k, tune):
     tune(ffn_path=M.MOE_PATH_GEMM)
-    log(f"fp8a8 gemm kind={kind} T={T} m={m} p={p} E={E} k={k}")
-    L = synth.make_layer(spec(T, m, p, E, k, kind, "fp8a8", seed=T + 3 * E + p, sw=0.05, sr=0.05))
+    log(f"{wd} gemm kind={kind} T={T} m={m} p={p} E={E} k={k}")
+    L = synth.make_layer(spec(T, m, p, E, k, kind, wd, seed=T + 3 * E + p, sw=0.05, sr=0.05))
     layer = MoELayer(L)
     rng = np.random.default_rng(T + 2)
     idx = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)

@@ -1,7 +1,7 @@
 """The five measured layers at full size, in the launch configuration the
-benchmark times, against the CPU oracle, and the int8, int4, fp8 and fp8a8
-(fp8 weights and activations) Mixtral prefill layers (the grouped GEMM with
-the weights' dequant fused, or on the fp8 matrix cores).
+benchmark times, against the CPU oracle, and the int8, int4, fp8, fp8a8 and
+i8a8 (8-bit weights and activations) Mixtral prefill layers (the grouped GEMM
+with the weights' dequant fused, or on the fp8 / int8 matrix cores).
 
 Routing and dispatch are checked in full.  Outputs are checked element by
 element on every token of the tiny, decode, skewed and int8 layers.  On the
@@ -53,7 +53,7 @@ def prefill_tokens(offsets, perm, k, T, seed, n_min=PREFILL_MIN_TOKENS, block=BL
     return np.array(sorted(toks)), blocks
 
 
-@pytest.mark.parametrize("cfg", ["c1", "c2", "c3", "c4", "c5", "c7", "c8", "c11", "c12"])
+@pytest.mark.parametrize("cfg", ["c1", "c2", "c3", "c4", "c5", "c7", "c8", "c11", "c12", "c14"])
 def test_config_full_size(cfg):
     sp = synth.spec(cfg)
     log(f"config {cfg} ({sp.name}): T={sp.T} m={sp.m} p={sp.p} E={sp.E} k={sp.k} {sp.kind} "
