@@ -13,8 +13,9 @@ one JSON line for it, with the roofline position of its dominant kernel
 oracle timed on a bounded sample of the same layer.  Beside it, under
 "configs", the same figures for the other measured layers (tiny fp32,
 Mixtral decode, Phi-3.5 skewed, Mixtral int8, int4, fp8, fp8a8 and MXFP4
-decode, Mixtral int8, int4, fp8 and fp8a8 prefill; fp8a8: fp8 weights and
-fp8 activations, the prefill up projection on the fp8 matrix cores).
+decode, Mixtral int8, int4, fp8, fp8a8 and i8a8 prefill; fp8a8 and i8a8: fp8
+or int8 weights with activations quantised to the same format, the prefill up
+projection on the fp8 or int8 matrix cores).
 
   python bench.py [--steps K] [--warmup W]            headline + every layer
   python bench.py --workload c2 [--steps K]           one layer only
