@@ -42,15 +42,18 @@ __device__ void block_histogram(const int32_t* __restrict__ idx, int n, int E, D
   __syncthreads();
 }
 
-// Calls fn(a, e, pos) for every assignment a with its stable position pos.
-// Needs block_histogram first; leaves L.cursor at the counts.  All threads call.
+// Calls fn(a, e, pos) for every assignment a in [lo, hi) with its stable
+// position pos.  Needs L.offs (the experts' first positions) and L.cursor (per
+// expert, the assignments before lo that it holds); advances L.cursor past
+// hi.  All threads call.
 template <int NW, class F>
-__device__ void block_stable_positions(const int32_t* __restrict__ idx, int n, int E, DispatchLds<NW>& L, F&& fn) {
+__device__ void block_stable_positions_range(const int32_t* __restrict__ idx, int lo, int hi, int E,
+                                             DispatchLds<NW>& L, F&& fn) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const uint64_t lt = (lane == 0) ? 0ull : ((~0ull) >> (64 - lane));
-  for (int base = 0; base < n; base += NW * 64) {
-    const int a = base + tid;
-    const bool valid = a < n;
+  for (long long base = lo; base < hi; base += NW * 64) {  // 64-bit: hi may be near 2^31
+    const bool valid = base + tid < hi;
+    const int a = valid ? (int)(base + tid) : 0;
     const int e = valid ? clamp_expert(idx[a], E) : 0;
     uint64_t peers = __ballot(valid);
 #pragma unroll
@@ -76,6 +79,13 @@ __device__ void block_stable_positions(const int32_t* __restrict__ idx, int n, i
     if (valid) fn(a, e, L.offs[e] + L.wbase[wave][e] + rank);
     __syncthreads();
   }
+}
+
+// Calls fn(a, e, pos) for every assignment a with its stable position pos.
+// Needs block_histogram first; leaves L.cursor at the counts.  All threads call.
+template <int NW, class F>
+__device__ void block_stable_positions(const int32_t* __restrict__ idx, int n, int E, DispatchLds<NW>& L, F&& fn) {
+  block_stable_positions_range<NW>(idx, 0, n, E, L, static_cast<F&&>(fn));
 }
 
 }  // namespace moe

@@ -452,6 +452,38 @@ __global__ __launch_bounds__(256) void k_pack_rows(const PackArgs A) {
   reinterpret_cast<u32x4_t*>(A.out)[frag * 64 + lane] = v;
 }
 
+// The same gather with the dispatch given (offsets, perm) and K / 32 a
+// multiple of 4: a wave writes four consecutive fragments of one 16-row block,
+// so each lane looks its row's assignment up once and issues the four loads
+// of its row (64 contiguous bytes apart) together.
+__global__ __launch_bounds__(256) void k_pack_rows4(const PackArgs A) {
+  __shared__ int offs_s[kMaxExperts + 1];
+  __shared__ int poffs_s[kMaxExperts + 1];
+  const int tid = threadIdx.x, lane = tid & 63;
+  if (tid <= A.E) offs_s[tid] = A.offsets[tid];
+  __syncthreads();
+  if (tid <= A.E) poffs_s[tid] = padded_offset(offs_s, tid);
+  __syncthreads();
+  const int U = A.K / 32;
+  const long long frag0 = ((long long)blockIdx.x * 4 + (tid >> 6)) * 4;
+  const long long rb = frag0 / U;
+  const int u0 = (int)(frag0 - rb * U);
+  const long long prow = rb * 16 + (lane & 15);
+  if (prow >= poffs_s[A.E]) return;  // past the last expert's padded rows
+  int e = 0;
+  while (poffs_s[e + 1] <= prow) ++e;
+  const int local = (int)(prow - poffs_s[e]);
+  u32x4_t v[4] = {};
+  if (local < offs_s[e + 1] - offs_s[e]) {
+    const int token = A.perm[offs_s[e] + local] / A.topk;
+    const u32x4_t* src = reinterpret_cast<const u32x4_t*>(A.x + (size_t)token * A.K + u0 * 32 + 8 * (lane >> 4));
+#pragma unroll
+    for (int f = 0; f < 4; ++f) v[f] = src[4 * f];
+  }
+#pragma unroll
+  for (int f = 0; f < 4; ++f) reinterpret_cast<u32x4_t*>(A.out)[(frag0 + f) * 64 + lane] = v[f];
+}
+
 // ---- fp8 x fp8 and int8 x int8: the up projection of 8-bit-activation layers ------
 //
 // With the activations quantised to E4M3 per token (one power-of-two scale
@@ -740,9 +772,14 @@ hipError_t launch_ffn_gemm(const GemmArgs& a, int epi, int qb, hipStream_t s) {
 hipError_t launch_pack_rows(const PackArgs& a, hipStream_t s) {
   const long long n = a.rows > 0 ? a.rows : (long long)a.T * a.topk;
   const long long frags = packed_rows_max(n, a.E) / 16 * (a.K / 32);
-  const long long blocks = (frags + 3) / 4;  // one wave per fragment
-  if (blocks <= 0) return hipSuccess;
-  k_pack_rows<<<dim3((unsigned)blocks), 256, 0, s>>>(a);
+  if (frags <= 0) return hipSuccess;
+  if (!a.topk_idx && (a.K / 32) % 4 == 0) {
+    const long long blocks = (frags / 4 + 3) / 4;  // one wave per four fragments
+    k_pack_rows4<<<dim3((unsigned)blocks), 256, 0, s>>>(a);
+  } else {
+    const long long blocks = (frags + 3) / 4;  // one wave per fragment
+    k_pack_rows<<<dim3((unsigned)blocks), 256, 0, s>>>(a);
+  }
   return hipGetLastError();
 }
 

@@ -222,57 +222,74 @@ __global__ __launch_bounds__(256) void k_ffn_f32(const F32Args A) {
 // ---- combine and elementwise ----------------------------------------------------
 
 // y[t][c] = sum_{j<k} w[t][j] * y_perm[inv_perm[t*k+j]][c] (+ residual[t][c],
-// in y's dtype, added last), four columns per thread.
-template <bool BF16>
+// in y's dtype, added last).  A thread takes V float4 columns of one row,
+// R = m / (4 V) float4 apart (so each of its V loads is coalesced across the
+// row's threads), and issues the V loads of a row slice together.
+template <bool BF16, int V>
 __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ y_perm, const int32_t* __restrict__ inv,
                                                  const float* __restrict__ w, int T, int m, int k, int slices,
                                                  size_t slice_stride, const void* __restrict__ residual,
                                                  void* __restrict__ y) {
-  const size_t q = (size_t)blockIdx.x * blockDim.x + threadIdx.x;  // float4 index
-  const size_t per_row = (size_t)m / 4;
-  if (q >= (size_t)T * per_row) return;
-  const int t = (int)(q / per_row);
-  const int c = (int)(q - (size_t)t * per_row) * 4;
-  float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+  const size_t g = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int R = m / (4 * V);  // threads per row
+  if (g >= (size_t)T * R) return;
+  const int t = (int)(g / R);
+  const int c0 = (int)(g - (size_t)t * R) * 4;  // first column; the others 4 R apart
+  float4 s[V];
+#pragma unroll
+  for (int v = 0; v < V; ++v) s[v] = make_float4(0.f, 0.f, 0.f, 0.f);
   for (int j = 0; j < k; ++j) {
     const float wj = w[(size_t)t * k + j];
-    const float* row = y_perm + (size_t)inv[(size_t)t * k + j] * m + c;
+    const float* row = y_perm + (size_t)inv[(size_t)t * k + j] * m + c0;
     // the row's partial sums over the reduction slices, in slice order
-    float4 v = *reinterpret_cast<const float4*>(row);
+    float4 acc[V];
+#pragma unroll
+    for (int v = 0; v < V; ++v) acc[v] = *reinterpret_cast<const float4*>(row + v * 4 * R);
     for (int q = 1; q < slices; ++q) {
-      const float4 u = *reinterpret_cast<const float4*>(row + (size_t)q * slice_stride);
-      v.x += u.x;
-      v.y += u.y;
-      v.z += u.z;
-      v.w += u.w;
+      float4 u[V];
+#pragma unroll
+      for (int v = 0; v < V; ++v) u[v] = *reinterpret_cast<const float4*>(row + (size_t)q * slice_stride + v * 4 * R);
+#pragma unroll
+      for (int v = 0; v < V; ++v) {
+        acc[v].x += u[v].x;
+        acc[v].y += u[v].y;
+        acc[v].z += u[v].z;
+        acc[v].w += u[v].w;
+      }
     }
-    s.x = fmaf(wj, v.x, s.x);
-    s.y = fmaf(wj, v.y, s.y);
-    s.z = fmaf(wj, v.z, s.z);
-    s.w = fmaf(wj, v.w, s.w);
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+      s[v].x = fmaf(wj, acc[v].x, s[v].x);
+      s[v].y = fmaf(wj, acc[v].y, s[v].y);
+      s[v].z = fmaf(wj, acc[v].z, s[v].z);
+      s[v].w = fmaf(wj, acc[v].w, s[v].w);
+    }
   }
-  if (residual) {
+#pragma unroll
+  for (int v = 0; v < V; ++v) {
+    const size_t off = (size_t)t * m + c0 + v * 4 * R;
+    if (residual) {
+      if (BF16) {
+        const uint2 r = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(residual) + off);
+        s[v].x += bf16_to_f32((uint16_t)(r.x & 0xFFFFu));
+        s[v].y += bf16_to_f32((uint16_t)(r.x >> 16));
+        s[v].z += bf16_to_f32((uint16_t)(r.y & 0xFFFFu));
+        s[v].w += bf16_to_f32((uint16_t)(r.y >> 16));
+      } else {
+        const float4 r = *reinterpret_cast<const float4*>(static_cast<const float*>(residual) + off);
+        s[v].x += r.x;
+        s[v].y += r.y;
+        s[v].z += r.z;
+        s[v].w += r.w;
+      }
+    }
     if (BF16) {
-      const uint2 r = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(residual) + (size_t)t * m + c);
-      s.x += bf16_to_f32((uint16_t)(r.x & 0xFFFFu));
-      s.y += bf16_to_f32((uint16_t)(r.x >> 16));
-      s.z += bf16_to_f32((uint16_t)(r.y & 0xFFFFu));
-      s.w += bf16_to_f32((uint16_t)(r.y >> 16));
+      const uint2 pk = make_uint2((uint32_t)f32_to_bf16(s[v].x) | ((uint32_t)f32_to_bf16(s[v].y) << 16),
+                                  (uint32_t)f32_to_bf16(s[v].z) | ((uint32_t)f32_to_bf16(s[v].w) << 16));
+      *reinterpret_cast<uint2*>(static_cast<uint16_t*>(y) + off) = pk;
     } else {
-      const float4 r = *reinterpret_cast<const float4*>(static_cast<const float*>(residual) + (size_t)t * m + c);
-      s.x += r.x;
-      s.y += r.y;
-      s.z += r.z;
-      s.w += r.w;
+      *reinterpret_cast<float4*>(static_cast<float*>(y) + off) = s[v];
     }
-  }
-  if (BF16) {
-    uint16_t* o = static_cast<uint16_t*>(y) + (size_t)t * m + c;
-    const uint2 pk = make_uint2((uint32_t)f32_to_bf16(s.x) | ((uint32_t)f32_to_bf16(s.y) << 16),
-                                (uint32_t)f32_to_bf16(s.z) | ((uint32_t)f32_to_bf16(s.w) << 16));
-    *reinterpret_cast<uint2*>(o) = pk;
-  } else {
-    *reinterpret_cast<float4*>(static_cast<float*>(y) + (size_t)t * m + c) = s;
   }
 }
 
@@ -348,14 +365,24 @@ hipError_t launch_ffn_f32(const F32Args& a, hipStream_t s) {
 hipError_t launch_combine(const float* y_perm, const int32_t* inv_perm, const float* topk_w, int T, int m, int k,
                           int slices, size_t slice_stride, void* y, bool y_bf16, hipStream_t s,
                           const void* residual) {
-  if (slices < 1) return hipErrorInvalidValue;
-  const size_t work = (size_t)T * (m / 4);
-  const unsigned grid = (unsigned)((work + 255) / 256);
+  if (slices < 1 || m % 16) return hipErrorInvalidValue;
+  const size_t work = (size_t)T * (m / 4);  // float4 columns
   if (work == 0) return hipSuccess;
-  if (y_bf16)
-    k_combine<true><<<grid, 256, 0, s>>>(y_perm, inv_perm, topk_w, T, m, k, slices, slice_stride, residual, y);
-  else
-    k_combine<false><<<grid, 256, 0, s>>>(y_perm, inv_perm, topk_w, T, m, k, slices, slice_stride, residual, y);
+  // four float4 per thread once there are enough rows to fill the GPU with
+  // the fewer threads (prefill); one at decode sizes
+  const bool wide = work >= ((size_t)1 << 20);
+  const unsigned grid = (unsigned)(((wide ? work / 4 : work) + 255) / 256);
+  if (wide) {
+    if (y_bf16)
+      k_combine<true, 4><<<grid, 256, 0, s>>>(y_perm, inv_perm, topk_w, T, m, k, slices, slice_stride, residual, y);
+    else
+      k_combine<false, 4><<<grid, 256, 0, s>>>(y_perm, inv_perm, topk_w, T, m, k, slices, slice_stride, residual, y);
+  } else {
+    if (y_bf16)
+      k_combine<true, 1><<<grid, 256, 0, s>>>(y_perm, inv_perm, topk_w, T, m, k, slices, slice_stride, residual, y);
+    else
+      k_combine<false, 1><<<grid, 256, 0, s>>>(y_perm, inv_perm, topk_w, T, m, k, slices, slice_stride, residual, y);
+  }
   return hipGetLastError();
 }
 

@@ -276,12 +276,26 @@ __global__ __launch_bounds__(1024) void k_route_fast(const void* __restrict__ x,
     const int n4 = nt * ym / 4;
     for (int i = tid; i < n4; i += 1024) yr[i] = make_float4(0.f, 0.f, 0.f, 0.f);
   }
-  // stage x rows [t0, t0 + nt) (rows past T are zero)
+  // stage x rows [t0, t0 + nt) (rows past T are zero), eight loads in flight
+  // per thread before the first LDS write
   {
-    const int row16 = m * XB / 16;
+    const int row16 = m * XB / 16, n16 = TB * row16, live16 = nt * row16;
     uint4* dst = reinterpret_cast<uint4*>(xs_raw);
     const uint4* src = reinterpret_cast<const uint4*>(static_cast<const char*>(x) + (size_t)t0 * m * XB);
-    for (int i = tid; i < TB * row16; i += 1024) dst[i] = (i < nt * row16) ? src[i] : make_uint4(0, 0, 0, 0);
+    constexpr int U = 8;
+    for (int i0 = tid; i0 < n16; i0 += 1024 * U) {
+      uint4 v[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int i = i0 + 1024 * u;
+        v[u] = i < live16 ? src[i] : make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int i = i0 + 1024 * u;
+        if (i < n16) dst[i] = v[u];
+      }
+    }
   }
   __syncthreads();
   if (F.norm) {
@@ -335,21 +349,35 @@ __global__ __launch_bounds__(1024) void k_route_fast(const void* __restrict__ x,
   const int q = lane & (S::Q - 1);
   const int rr = lane >> S::LQ;
   const int nchunks = m / S::RPC;
-#pragma unroll 8
-  for (int c = wave; c < nchunks; c += 16) {
-    const int r = c * S::RPC + rr;
-    const float4 wv = *reinterpret_cast<const float4*>(wg + (size_t)r * E + 4 * q);
+  // The wave's chunks are c = wave, wave + 16, ...; each group of WU of them
+  // issues all its weight loads before the first product (a chunk past the
+  // end reloads the group's first), and the products keep increasing c.
+  constexpr int WU = 8;
+  for (int c0 = wave; c0 < nchunks; c0 += 16 * WU) {
+    float4 wv[WU];
 #pragma unroll
-    for (int t = 0; t < TB; ++t) {
-      float xv;
-      if constexpr (XBF16)
-        xv = bf16_to_f32(reinterpret_cast<const uint16_t*>(xs_raw)[t * m + r]);
-      else
-        xv = reinterpret_cast<const float*>(xs_raw)[t * m + r];
-      acc[t * 4 + 0] = fmaf(xv, wv.x, acc[t * 4 + 0]);
-      acc[t * 4 + 1] = fmaf(xv, wv.y, acc[t * 4 + 1]);
-      acc[t * 4 + 2] = fmaf(xv, wv.z, acc[t * 4 + 2]);
-      acc[t * 4 + 3] = fmaf(xv, wv.w, acc[t * 4 + 3]);
+    for (int u = 0; u < WU; ++u) {
+      const int c = c0 + 16 * u < nchunks ? c0 + 16 * u : c0;
+      wv[u] = *reinterpret_cast<const float4*>(wg + (size_t)(c * S::RPC + rr) * E + 4 * q);
+    }
+#pragma unroll
+    for (int u = 0; u < WU; ++u) {
+      const int c = c0 + 16 * u;
+      if (c < nchunks) {
+        const int r = c * S::RPC + rr;
+#pragma unroll
+        for (int t = 0; t < TB; ++t) {
+          float xv;
+          if constexpr (XBF16)
+            xv = bf16_to_f32(reinterpret_cast<const uint16_t*>(xs_raw)[t * m + r]);
+          else
+            xv = reinterpret_cast<const float*>(xs_raw)[t * m + r];
+          acc[t * 4 + 0] = fmaf(xv, wv[u].x, acc[t * 4 + 0]);
+          acc[t * 4 + 1] = fmaf(xv, wv[u].y, acc[t * 4 + 1]);
+          acc[t * 4 + 2] = fmaf(xv, wv[u].z, acc[t * 4 + 2]);
+          acc[t * 4 + 3] = fmaf(xv, wv[u].w, acc[t * 4 + 3]);
+        }
+      }
     }
   }
   // sum over the row lanes (lane bits LQ..5)
@@ -386,17 +414,77 @@ __global__ __launch_bounds__(1024) void k_route_fast(const void* __restrict__ x,
   }
 }
 
-// Single workgroup of 16 waves: the block-level dispatch (LDS histogram,
-// prefix sum, ballot-ranked stable positions).
-__global__ __launch_bounds__(1024) void k_dispatch(const int32_t* __restrict__ idx, int n, int E,
+// The dispatch over workgroups of 16 waves, workgroup b placing assignments
+// [b * chunk, (b + 1) * chunk).  Every workgroup counts all n expert ids
+// itself, so no workgroup waits for another: a wave finds the lanes holding
+// the same expert with six ballots (as in the ranking) and the lowest of them
+// adds the group's size to the wave's own LDS row of counts, once for every
+// id and once for the ids before the workgroup's range.  The sums over the
+// waves give the experts' counts (hence offsets) and each expert's
+// assignments ahead of the range; the range is then ranked as in the one-
+// workgroup dispatch, its cursors starting there.  Workgroup 0 publishes
+// counts and offsets.
+__global__ __launch_bounds__(1024) void k_dispatch(const int32_t* __restrict__ idx, int n, int E, int chunk,
                                                     int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
                                                     int32_t* __restrict__ perm, int32_t* __restrict__ inv_perm) {
-  __shared__ DispatchLds<16> L;
-  block_histogram<16>(idx, n, E, L);
-  const int tid = threadIdx.x;
-  if (tid < E) counts[tid] = L.cnt[tid];
-  if (tid <= E) offsets[tid] = L.offs[tid];
-  block_stable_positions<16>(idx, n, E, L, [&](int a, int, int pos) {
+  constexpr int NW = 16, U = 4;
+  __shared__ DispatchLds<NW> L;
+  __shared__ int wtot[NW][64], wpre[NW][64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lo = blockIdx.x * chunk, hi = min(n, lo + chunk);
+  wtot[wave][lane] = 0;
+  wpre[wave][lane] = 0;
+  const uint64_t lt = (lane == 0) ? 0ull : ((~0ull) >> (64 - lane));
+  for (long long base = 0; base < n; base += NW * 64 * U) {  // 64-bit: n may be near 2^31
+    int ev[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const long long a = base + u * NW * 64 + tid;
+      ev[u] = a < n ? idx[a] : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const long long a = base + u * NW * 64 + tid;
+      const bool valid = a < n;
+      const int e = valid ? clamp_expert(ev[u], E) : 0;
+      uint64_t peers = __ballot(valid);
+#pragma unroll
+      for (int b = 0; b < 6; ++b) {
+        const uint64_t mb = __ballot((e >> b) & 1);
+        peers &= ((e >> b) & 1) ? mb : ~mb;
+      }
+      const uint64_t before = __ballot(a < lo);
+      if (valid && __popcll(peers & lt) == 0) {  // the group's lowest lane; distinct experts per wave
+        wtot[wave][e] += __popcll(peers);
+        wpre[wave][e] += __popcll(peers & before);
+      }
+    }
+  }
+  __syncthreads();
+  if (tid < 64) {
+    int tot = 0, pre = 0;
+    for (int w = 0; w < NW; ++w) {
+      tot += wtot[w][tid];
+      pre += wpre[w][tid];
+    }
+    L.cnt[tid] = tot;
+    L.cursor[tid] = pre;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int run = 0;
+    for (int e = 0; e < E; ++e) {
+      L.offs[e] = run;
+      run += L.cnt[e];
+    }
+    L.offs[E] = run;
+  }
+  __syncthreads();
+  if (blockIdx.x == 0) {
+    if (tid < E) counts[tid] = L.cnt[tid];
+    if (tid <= E) offsets[tid] = L.offs[tid];
+  }
+  block_stable_positions_range<NW>(idx, lo, hi, E, L, [&](int a, int, int pos) {
     perm[pos] = a;
     inv_perm[a] = pos;
   });
@@ -525,7 +613,13 @@ hipError_t launch_route_topk(const void* x, bool x_bf16, const float* wg, const 
 
 hipError_t launch_dispatch(const int32_t* idx, int n, int E, int32_t* counts, int32_t* offsets, int32_t* perm,
                            int32_t* inv_perm, hipStream_t s) {
-  k_dispatch<<<1, 1024, 0, s>>>(idx, n, E, counts, offsets, perm, inv_perm);
+  if (n < 0 || E < 1 || E > 64) return hipErrorInvalidValue;
+  // ranges of whole 1024-assignment passes, at most 64 workgroups (each one
+  // reads all n ids to count them)
+  const int passes = (n + 1023) / 1024;
+  const int chunk = 1024 * ((passes + 63) / 64 > 1 ? (passes + 63) / 64 : 1);
+  const int grid = n > 0 ? (n + chunk - 1) / chunk : 1;
+  k_dispatch<<<grid, 1024, 0, s>>>(idx, n, E, chunk, counts, offsets, perm, inv_perm);
   return hipGetLastError();
 }
 

@@ -319,6 +319,39 @@ static void check_gemm(int K, int N, int G, int T, int topk, const std::vector<i
         if (lane == 0 && frag < (long long)filled.size()) filled[frag] = 1;
       }
   for (size_t i = 0; i < filled.size(); ++i) CHECK(filled[i], "packed fragment %zu never written", i);
+  // the four-fragment packing kernel (dispatch given, K / 32 a multiple of 4):
+  // a wave writes fragments 4 w' .. 4 w' + 3 of one 16-row block, each lane
+  // reading 16 bytes of its row at k = u0 * 32 + 8 (lane / 16) + 32 f
+  if (U % 4) return;
+  std::fill(filled.begin(), filled.end(), 0);
+  const long long pblocks4 = (frags / 4 + 3) / 4;
+  for (long long blk = 0; blk < pblocks4; ++blk)
+    for (int w = 0; w < 4; ++w)
+      for (int lane = 0; lane < 64; ++lane) {
+        const long long frag0 = (blk * 4 + w) * 4;
+        const long long rb = frag0 / U;
+        const int u0 = (int)(frag0 - rb * U);
+        CHECK(u0 + 3 < U, "pack4: fragments %lld..+3 cross a row block", frag0);
+        const long long prow = rb * 16 + (lane & 15);
+        if (prow >= pend) continue;
+        int e = 0;
+        while (poffs[e + 1] <= prow) ++e;
+        CHECK(e < E, "pack4: row %lld has no expert", prow);
+        const int local = (int)(prow - poffs[e]);
+        for (int f = 0; f < 4; ++f) {
+          if (local < offsets[e + 1] - offsets[e]) {
+            const int token = perm[offsets[e] + local] / topk;
+            const unsigned long long src = (unsigned long long)token * K + u0 * 32 + 8 * (lane >> 4) + 32 * f;
+            CHECK(token < T && src + 8 <= (unsigned long long)T * K, "pack4 read %llu", src);
+            CHECK(src / K == (unsigned long long)token, "pack4 read %llu leaves row %d", src, token);
+          }
+          const unsigned long long dst = (unsigned long long)(frag0 + f) * 1024 + 16 * lane;
+          CHECK(dst + 16 <= act_bytes, "pack4 write %llu of %llu", dst, act_bytes);
+          if (lane == 0 && frag0 + f < (long long)filled.size()) filled[frag0 + f] += 1;
+        }
+      }
+  for (size_t i = 0; i < filled.size(); ++i) CHECK(filled[i] == 1, "pack4: packed fragment %zu written %d times", i,
+                                                   (int)filled[i]);
 }
 
 // Decode FFN column groups: every 16-column tile is owned by exactly one
