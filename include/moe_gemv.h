@@ -187,6 +187,8 @@ typedef struct moe_tuning {
                            atomics into an accumulator (-1) */
   int gemm_cg;          /* grouped GEMM: column blocks per group of its work order (>= 1) */
   int gemm_skip;        /* grouped GEMM: skip the products of empty row fragments (1/-1) */
+  int route_quant;      /* 8-bit-activation layers: quantise the experts' input rows in the routing pass
+                           (1) or in a kernel of their own (-1) */
 } moe_tuning;
 #define MOE_PATH_AUTO 0
 #define MOE_PATH_SKINNY 1

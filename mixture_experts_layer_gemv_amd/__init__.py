@@ -40,7 +40,7 @@ class moe_tuning(ctypes.Structure):
     """struct moe_tuning: 0 is "automatic" in every field, switches are 1 / -1."""
     _fields_ = [(n, ctypes.c_int) for n in (
         "ffn_path", "skinny_mt", "skinny_pack", "skinny_splitk", "skinny_shared", "skinny_wide", "skinny_wide_down",
-        "up_ct", "down_ct", "down_ksplit", "down_rows", "gemm_cg", "gemm_skip")]
+        "up_ct", "down_ct", "down_ksplit", "down_rows", "gemm_cg", "gemm_skip", "route_quant")]
 
 
 def tuning(**fields) -> moe_tuning:

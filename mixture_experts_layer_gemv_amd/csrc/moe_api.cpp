@@ -177,7 +177,7 @@ moe_status check_tuning(const moe_tuning& t) {
   if (!tiles(t.skinny_mt) || !tiles(t.up_ct) || !tiles(t.down_ct))
     return fail(MOE_ERR_INVALID_ARG, "skinny_mt, up_ct and down_ct must be 0, 1, 2 or 4");
   if (!tri(t.skinny_pack) || !tri(t.skinny_splitk) || !tri(t.skinny_shared) || !tri(t.skinny_wide) ||
-      !tri(t.skinny_wide_down) || !tri(t.down_rows) || !tri(t.gemm_skip))
+      !tri(t.skinny_wide_down) || !tri(t.down_rows) || !tri(t.gemm_skip) || !tri(t.route_quant))
     return fail(MOE_ERR_INVALID_ARG, "a switch of the tuning is not 0, 1 or -1");
   if (t.down_ksplit < 0 || t.down_ksplit > 1024) return fail(MOE_ERR_INVALID_ARG, "down_ksplit %d", t.down_ksplit);
   if (t.gemm_cg < 0 || t.gemm_cg > 1024) return fail(MOE_ERR_INVALID_ARG, "gemm_cg %d", t.gemm_cg);
@@ -424,18 +424,34 @@ struct FfnIo {
 // The dispatched rows an FFN call serves: all T*k, or the caller's bound.
 long long ffn_rows(const FfnIo& io) { return io.rows >= 0 ? io.rows : (long long)io.T * io.k; }
 
-// fp8 activations: quantises the FFN's input rows (per token, into the
-// workspace) and points io at them: as bf16 values for the decode kernels,
-// as E4M3 codes (with the packed rows' scales to come) for the grouped GEMM,
-// whose first projection multiplies codes on the fp8 matrix cores.
-moe_status quant_input(const LayerCfg& c, FfnIo& io, char* ws, const Ws& L, hipStream_t s) {
+// 8-bit activations: where the FFN's quantised input rows go in the
+// workspace: as bf16 values for the decode kernels, as E4M3 (int8) codes for
+// the grouped GEMM, whose first projection multiplies codes on the fp8 (int8)
+// matrix cores; and each token's scale.
+struct QuantOut {
+  uint16_t* xq;  // bf16 values (decode kernels) or null
+  uint8_t* xc;   // codes (grouped GEMM) or null
+  float* xs;
+};
+QuantOut quant_out(const LayerCfg& c, const FfnIo& io, char* ws, const Ws& L) {
+  const bool gemm = ffn_path(c, io.T, io.k) == Path::GEMM;
+  return QuantOut{gemm ? nullptr : reinterpret_cast<uint16_t*>(ws + L.xq),
+                  gemm ? reinterpret_cast<uint8_t*>(ws + L.xq) : nullptr, reinterpret_cast<float*>(ws + L.xs)};
+}
+
+// Quantises the FFN's input rows (per token, into the workspace; already
+// done when in_route, by the routing pass) and points io at them, with the
+// packed rows' scales to come on the grouped GEMM.
+moe_status quant_input(const LayerCfg& c, FfnIo& io, char* ws, const Ws& L, hipStream_t s, bool in_route = false) {
   if (!act8(c)) return MOE_OK;
   const bool gemm = ffn_path(c, io.T, io.k) == Path::GEMM;
-  uint16_t* xq = gemm ? nullptr : reinterpret_cast<uint16_t*>(ws + L.xq);
-  uint8_t* xc = gemm ? reinterpret_cast<uint8_t*>(ws + L.xq) : nullptr;
-  float* xs = reinterpret_cast<float*>(ws + L.xs);
+  const QuantOut q = quant_out(c, io, ws, L);
+  uint16_t* xq = q.xq;
+  uint8_t* xc = q.xc;
+  float* xs = q.xs;
   const uint16_t* x = static_cast<const uint16_t*>(io.x);
-  MOE_TRY_HIP(run("quant_rows", s, [&] { return moe::launch_quant_rows(x, io.T, c.m, act_int8(c), xq, xc, xs, s); }));
+  if (!in_route)
+    MOE_TRY_HIP(run("quant_rows", s, [&] { return moe::launch_quant_rows(x, io.T, c.m, act_int8(c), xq, xc, xs, s); }));
   if (gemm) {
     io.xc = xc;
     io.rs = reinterpret_cast<float*>(ws + L.rs);
@@ -1270,7 +1286,20 @@ moe_status enqueue_forward(const moe_weights* w, const float* w_router, const fl
   // experts then read the normalised rows), the residual added by the combine
   // or, on the accumulator paths, used as the accumulator's starting value
   void* xn = f.norm ? (f.x_norm ? f.x_norm : static_cast<void*>(ws + L.xn)) : nullptr;
-  const moe::RouteFuse rf{f.norm, f.gamma, f.beta, f.eps, xn, f.residual, y_bf16 ? 1 : 0};
+  moe::RouteFuse rf{f.norm, f.gamma, f.beta, f.eps, xn, f.residual, y_bf16 ? 1 : 0, 0, nullptr, nullptr, nullptr};
+  // 8-bit activations: the routing pass quantises the experts' input rows
+  // (from its LDS copy of them), unless tuned off
+  const bool q_in_route = act8(c) && tuned_on(c.tune.route_quant, true);
+  if (q_in_route) {
+    FfnIo shape{};
+    shape.T = T;
+    shape.k = k;
+    const QuantOut q = quant_out(c, shape, ws, L);
+    rf.quant = act_int8(c) ? 2 : 1;
+    rf.xq = q.xq;
+    rf.xc = q.xc;
+    rf.xs = q.xs;
+  }
   MOE_TRY_HIP(run("route_topk", s, [&] {
     return moe::launch_route_topk(x, x_dtype == MOE_BF16, w_router, b_router, T, m, E, k, false, logits, idx, tw,
                                   rows ? nullptr : yacc, m, s, &rf);
@@ -1294,7 +1323,7 @@ moe_status enqueue_forward(const moe_weights* w, const float* w_router, const fl
   io.yperm = rows ? reinterpret_cast<float*>(ws + L.yperm) : nullptr;
   int slices = 1;
   io.slices = &slices;
-  if (moe_status rc = quant_input(c, io, ws, L, s)) return rc;
+  if (moe_status rc = quant_input(c, io, ws, L, s, q_in_route)) return rc;
   if (moe_status rc = w->off ? run_ffn_streamed(w, io, s) : run_ffn(w, io, s)) return rc;
   if (rows) {
     MOE_TRY_HIP(run("combine", s, [&] {

@@ -89,25 +89,7 @@ constexpr int q_ah(int qb) { return qb >= 8 ? 2 : (qb >= 4 ? 4 : 1); }
 // per-output-channel scales applied in the epilogue (int8, fp8, int4)
 constexpr bool q_chan_scale(int qb) { return qb == 8 || qb == 9 || qb == 4; }
 
-// ---- E4M3 encoding of activations ----------------------------------------------
-//
-// E4M3 magnitude code of v / 2^X for |v| / 2^X <= 448: round to nearest,
-// ties to even, on the format's grid (quantum 2^-9 below 2^-6, 2^(e-3) in
-// [2^e, 2^(e+1))).
-__device__ __forceinline__ uint32_t e4m3_code(float a) {
-  if (a >= 448.0f) return 0x7Eu;
-  if (a < 0.015625f) return (uint32_t)rintf(a * 512.0f);  // multiples of 2^-9; 8 is the smallest normal
-  int e2;
-  frexpf(a, &e2);  // a in [2^(e2-1), 2^e2)
-  int e = e2 - 1;
-  float q = rintf(ldexpf(a, 3 - e));  // in [8, 16]
-  if (q == 16.0f) {
-    q = 8.0f;
-    ++e;
-  }
-  if (e > 8 || (e == 8 && q > 14.0f)) return 0x7Eu;
-  return (uint32_t)(((e + 7) << 3) | ((int)q - 8));
-}
+// ---- 8-bit activations ------------------------------------------------------------
 
 // The value of an E4M3 magnitude code.
 __device__ __forceinline__ float e4m3_mag(uint32_t c) {
@@ -125,6 +107,43 @@ __device__ __forceinline__ int act_scale_exponent(float amax) {
   int e2;
   const float f = 2.0f * frexpf(amax, &e2);  // amax = f * 2^(e2 - 1)
   return INT8 ? (e2 - 1) - (f <= 127.0f / 64.0f ? 6 : 5) : (e2 - 1) - (f <= 1.75f ? 8 : 7);
+}
+
+// Quantises eight bf16 activations of a row (one 16-byte load) with the row's
+// scale 2^X: their codes (bytes in element order; E4M3 with the sign in bit
+// 7, or int8 two's complement) and, with VALUES, the quantised values as
+// bf16.  The division by 2^X is exact.  E4M3 codes come from the hardware
+// conversion (round to nearest, ties to even, onto the OCP E4M3 grid; |v| <=
+// 448 never saturates), which was checked against a plain encoder of the
+// grid on the GPU for every bf16 input of magnitude <= 448, both signs; int8
+// codes round the quotient half to even (|q| <= 127).  A value is the code's
+// number times 2^X with the input's sign (zero included): at most seven
+// significant bits, so bf16 holds it exactly.
+template <bool INT8, bool VALUES>
+__device__ __forceinline__ void quant8(const uint32_t (&w)[4], int X, uint32_t (&q)[4], uint32_t (&c)[2]) {
+  c[0] = c[1] = 0u;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t b0 = w[j] & 0xFFFFu, b1 = w[j] >> 16;
+    uint32_t code2;
+    if constexpr (INT8) {
+      // the signed quotient rounded (a rounded -0 keeps its sign for the value)
+      const float r0 = rintf(ldexpf(__uint_as_float(b0 << 16), -X));
+      const float r1 = rintf(ldexpf(__uint_as_float(b1 << 16), -X));
+      code2 = ((uint32_t)(int)r0 & 0xFFu) | (((uint32_t)(int)r1 & 0xFFu) << 8);
+      if constexpr (VALUES)
+        q[j] = (__float_as_uint(ldexpf(r0, X)) >> 16) | (__float_as_uint(ldexpf(r1, X)) & 0xFFFF0000u);
+    } else {
+      code2 = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(__uint_as_float(b0 << 16), -X),
+                                                        ldexpf(__uint_as_float(b1 << 16), -X), 0, false) &
+              0xFFFFu;
+      if constexpr (VALUES) {
+        const float v0 = ldexpf(e4m3_mag(code2 & 0x7Fu), X), v1 = ldexpf(e4m3_mag((code2 >> 8) & 0x7Fu), X);
+        q[j] = ((__float_as_uint(v0) >> 16) | (b0 & 0x8000u)) | (((__float_as_uint(v1) >> 16) | (b1 & 0x8000u)) << 16);
+      }
+    }
+    c[j >> 1] |= code2 << (16 * (j & 1));
+  }
 }
 
 }  // namespace moe

@@ -81,12 +81,19 @@ struct RouteFuse {
   void* xn;              // with a norm: the normalised rows [T][m] in x's dtype (routed and returned)
   const void* residual;  // or null: the accumulator starts from it instead of zero ([T][ym])
   int res_bf16;          // residual dtype: bf16 (1) or fp32 (0)
+  int quant;             // 8-bit activations: 0 none, 1 E4M3, 2 int8 (bf16 rows only)
+  uint16_t* xq;          // with quant: the (normalised) rows quantised, as bf16 values [T][m], or null
+  uint8_t* xc;           // with quant: their codes [T][m], or null
+  float* xs;             // with quant: each row's scale [T]
 };
 
 // yacc (optional): fp32 [T][ym] accumulator that the routing pass zeroes (or
 // fills with fuse->residual).  With fuse->norm the routing uses, and writes to
 // fuse->xn, the normalised rows: inside the staged router, else by a row-norm
-// kernel first.
+// kernel first.  With fuse->quant the experts' input rows (normalised ones
+// with a norm) are also quantised to 8 bits, per row, as launch_quant_rows
+// does: inside the staged router from its LDS copy of the rows, else by that
+// kernel after the routing.
 hipError_t launch_route_topk(const void* x, bool x_bf16, const float* wg, const float* bias, int T, int m, int E,
                              int k, bool logits_in, float* logits, int32_t* idx, float* w, float* yacc, int ym,
                              hipStream_t s, const RouteFuse* fuse = nullptr);

@@ -404,7 +404,7 @@ hipError_t launch_combine(const float* y_perm, const int32_t* inv_perm, const fl
 // int8 form: scale 2^X, X the smallest integer with max|x| <= 127 * 2^X, q =
 // x / 2^X rounded half to even (|q| <= 127); q * 2^X has seven significant
 // bits, so bf16 holds it exactly too.
-template <bool INT8>
+template <bool INT8, bool VALUES>
 __global__ __launch_bounds__(256) void k_quant_rows(const uint16_t* __restrict__ x, int m, uint16_t* __restrict__ xq,
                                                     uint8_t* __restrict__ xc, float* __restrict__ xs) {
   __shared__ float red[4];
@@ -431,25 +431,9 @@ __global__ __launch_bounds__(256) void k_quant_rows(const uint16_t* __restrict__
   for (int i = tid; i < n8; i += 256) {
     const uint4 v = row[i];
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-    uint32_t o[4], c8[2] = {0u, 0u};
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      uint32_t pair = 0;
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const uint16_t b = (uint16_t)(h ? w[j] >> 16 : w[j] & 0xFFFFu);
-        const float a = ldexpf(fabsf(bf16_to_f32(b)), -X);  // exact
-        // E4M3: the magnitude's code and the sign bit; int8: the magnitude
-        // rounded half to even (<= 127), its two's complement with the sign
-        const uint32_t mag = INT8 ? (uint32_t)rintf(a) : e4m3_code(a);
-        const float q = ldexpf(INT8 ? (float)mag : e4m3_mag(mag), X);  // exact, a bf16 value
-        pair |= ((__float_as_uint(q) >> 16) | (b & 0x8000u)) << (16 * h);
-        const uint32_t code = INT8 ? ((b & 0x8000u) ? (0u - mag) & 0xFFu : mag) : (mag | ((b >> 8) & 0x80u));
-        c8[j >> 1] |= code << (8 * (2 * (j & 1) + h));
-      }
-      o[j] = pair;
-    }
-    if (xq) reinterpret_cast<uint4*>(xq + (size_t)t * m)[i] = make_uint4(o[0], o[1], o[2], o[3]);
+    uint32_t o[4], c8[2];
+    quant8<INT8, VALUES>(w, X, o, c8);
+    if (VALUES) reinterpret_cast<uint4*>(xq + (size_t)t * m)[i] = make_uint4(o[0], o[1], o[2], o[3]);
     if (xc) reinterpret_cast<uint2*>(xc + (size_t)t * m)[i] = make_uint2(c8[0], c8[1]);
   }
 }
@@ -458,10 +442,15 @@ hipError_t launch_quant_rows(const uint16_t* x, int T, int m, bool int8, uint16_
                              hipStream_t s) {
   if (T <= 0) return hipSuccess;
   if (m % 64) return hipErrorInvalidValue;
-  if (int8)
-    k_quant_rows<true><<<dim3((unsigned)T), 256, 0, s>>>(x, m, xq, xc, xs);
+  const dim3 g((unsigned)T);
+  if (int8 && xq)
+    k_quant_rows<true, true><<<g, 256, 0, s>>>(x, m, xq, xc, xs);
+  else if (int8)
+    k_quant_rows<true, false><<<g, 256, 0, s>>>(x, m, xq, xc, xs);
+  else if (xq)
+    k_quant_rows<false, true><<<g, 256, 0, s>>>(x, m, xq, xc, xs);
   else
-    k_quant_rows<false><<<dim3((unsigned)T), 256, 0, s>>>(x, m, xq, xc, xs);
+    k_quant_rows<false, false><<<g, 256, 0, s>>>(x, m, xq, xc, xs);
   return hipGetLastError();
 }
 

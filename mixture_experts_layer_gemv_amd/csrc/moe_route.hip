@@ -7,6 +7,7 @@
 // one-GPU form of sending tokens to their experts (HARMOEny article, section
 // 3.3 step four): the assignments are grouped by expert so each expert reads
 // a contiguous run of rows.
+#include "moe_convert.hpp"
 #include "moe_dispatch_block.hpp"
 #include "moe_kernels.hpp"
 
@@ -235,6 +236,11 @@ __device__ __forceinline__ float wave_sum64(float v) {
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
   return v;
 }
+__device__ __forceinline__ float wave_max64(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
 
 // Residual element i as fp32.
 __device__ __forceinline__ float residual_at(const RouteFuse& F, size_t i) {
@@ -341,6 +347,49 @@ __global__ __launch_bounds__(1024) void k_route_fast(const void* __restrict__ x,
       }
     }
     __syncthreads();
+  }
+
+  if constexpr (XBF16) {
+    if (F.quant) {
+      // 8-bit activations: each staged row's scale (wave t reduces row t),
+      // then the rows' codes and values, eight elements per 16-byte LDS read
+      __shared__ int qx_s[TB];
+      const int m8 = m / 8;
+      const uint4* x8 = reinterpret_cast<const uint4*>(xs_raw);
+      const bool int8 = F.quant == 2;
+      if (wave < nt) {
+        float amax = 0.0f;
+        for (int c = lane; c < m8; c += 64) {
+          const uint4 v = x8[wave * m8 + c];
+          const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            amax = fmaxf(amax, fmaxf(fabsf(__uint_as_float(w[j] << 16)), fabsf(__uint_as_float(w[j] & 0xFFFF0000u))));
+        }
+        amax = wave_max64(amax);
+        const int X = int8 ? act_scale_exponent<true>(amax) : act_scale_exponent<false>(amax);
+        if (lane == 0) {
+          qx_s[wave] = X;
+          F.xs[t0 + wave] = ldexpf(1.0f, X);
+        }
+      }
+      __syncthreads();
+      uint4* q8 = F.xq ? reinterpret_cast<uint4*>(F.xq + (size_t)t0 * m) : nullptr;
+      uint2* c8 = F.xc ? reinterpret_cast<uint2*>(F.xc + (size_t)t0 * m) : nullptr;
+      for (int i = tid; i < nt * m8; i += 1024) {
+        const uint4 v = x8[i];
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+        const int X = qx_s[i / m8];
+        uint32_t o[4], c[2];
+        if (int8) {
+          if (q8) quant8<true, true>(w, X, o, c); else quant8<true, false>(w, X, o, c);
+        } else {
+          if (q8) quant8<false, true>(w, X, o, c); else quant8<false, false>(w, X, o, c);
+        }
+        if (q8) q8[i] = make_uint4(o[0], o[1], o[2], o[3]);
+        if (c8) c8[i] = make_uint2(c[0], c[1]);
+      }
+    }
   }
 
   float acc[S::NV];
@@ -544,6 +593,7 @@ hipError_t launch_route_topk(const void* x, bool x_bf16, const float* wg, const 
   const int xb = x_bf16 ? 2 : 4;
   const RouteFuse F = fuse ? *fuse : RouteFuse{};
   if (F.norm && (logits_in || !F.gamma || !F.xn)) return hipErrorInvalidValue;
+  if (F.quant && (logits_in || !x_bf16 || !F.xs || (!F.xq && !F.xc) || m % 64)) return hipErrorInvalidValue;
   if (T <= 0) return hipSuccess;
   if (!logits_in && (E == 8 || E == 16 || E == 32 || E == 64) && (yacc == nullptr || ym % 4 == 0)) {
     // tokens per block: one up to 256 tokens (spreads the router weights'
@@ -589,6 +639,10 @@ hipError_t launch_route_topk(const void* x, bool x_bf16, const float* wg, const 
     if (e != hipSuccess) return e;
   } else if (yacc) {
     const hipError_t e = launch_fill_zero(yacc, (size_t)T * ym, s);
+    if (e != hipSuccess) return e;
+  }
+  if (F.quant) {  // the experts' rows: x, or the normalised rows written above
+    const hipError_t e = launch_quant_rows(static_cast<const uint16_t*>(x), T, m, F.quant == 2, F.xq, F.xc, F.xs, s);
     if (e != hipSuccess) return e;
   }
   if (E <= 8) {

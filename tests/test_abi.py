@@ -162,7 +162,7 @@ def test_tuning_validation(lib):
     L = lib.lib()
     n = ctypes.c_size_t()
     for bad in [dict(ffn_path=3), dict(skinny_mt=3), dict(up_ct=8), dict(skinny_pack=2), dict(down_rows=-2),
-                dict(down_ksplit=-1), dict(gemm_cg=-4), dict(gemm_skip=5)]:
+                dict(down_ksplit=-1), dict(gemm_cg=-4), dict(gemm_skip=5), dict(route_quant=2)]:
         t = lib.tuning(**bad)
         rc = L.moe_workspace_size_for(4096, 14336, 8, 1, 1, ctypes.byref(t), 16, 2, ctypes.byref(n))
         assert rc == lib.MOE_ERR_INVALID_ARG, (bad, rc)

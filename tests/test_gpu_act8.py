@@ -163,6 +163,29 @@ def test_act8_grouped_gemm(wd, kind, T, m, p, E, k, tune):
     _layer_check(L)
 
 
+@pytest.mark.parametrize("wd", ["fp8a8", "i8a8"])
+@pytest.mark.parametrize("path", ["skinny", "gemm"])
+@pytest.mark.parametrize("T,m,p,E,k", [(40, 256, 384, 8, 2), (300, 512, 256, 16, 2), (3, 128, 128, 64, 4)])
+def test_act8_quantised_in_routing_pass(wd, path, T, m, p, E, k, tune):
+    """The layer quantises its experts' input rows inside the routing pass
+    (route_quant on, the default); the same layer with the quantisation
+    kernel instead (off) must give the same output bits, and both the
+    oracle's numbers."""
+    log(f"{wd} {path} route_quant on/off T={T} m={m} p={p} E={E} k={k}")
+    L = synth.make_layer(spec(T, m, p, E, k, "swiglu", wd, seed=T + E, sw=0.05, sr=0.05))
+    outs = []
+    for rq in (1, -1):
+        tune(ffn_path=M.MOE_PATH_GEMM if path == "gemm" else M.MOE_PATH_SKINNY, route_quant=rq)
+        layer = MoELayer(L)
+        y = layer.forward()
+        torch.cuda.synchronize()
+        outs.append(y.clone())
+        layer.close()
+    assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16)), "route_quant on/off differ"
+    tune(route_quant=0)
+    _layer_check(L)
+
+
 def test_fp8a8_decode_layer_full_size():
     sp = synth.spec("c13")
     log(f"{sp.name}, full size, every token")
