@@ -47,7 +47,9 @@ namespace {
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v); }
-__device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
+// SiLU with the hardware exponential and reciprocal (a few ulp of fp32,
+// far inside the bf16 rounding of H).
+__device__ __forceinline__ float silu_fast(float z) { return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }
 
 // Tile shape of one weight kind.  A stage holds one 16-byte weight unit of
 // K (32 k for bf16, 64 for int8, 128 for int4: the packed weight layout's
@@ -353,37 +355,94 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
   }
 
   // Epilogue.  Lane l of fragment (i, j) holds rows i*16 + 4*(l>>4) + q,
-  // q = 0..3, of column (l & 15) of the fragment's tile.
+  // q = 0..3, of column (l & 15) of the fragment's tile.  The results go
+  // through LDS (the ring is free once every wave is past its last read and
+  // copy; each wave then uses a region of its own) so that every global
+  // store writes 16 contiguous bytes per lane: a lane's four rows of one
+  // column would otherwise take one narrow store each, and those stores
+  // measured at ~10 % of the kernel (the CU's matrix cores idle meanwhile).
+  const int nb0 = tile_base + wn * TPW;  // the wave's first column tile
+  const bool live = nb0 < NB;            // NB is a multiple of 4: all of the wave's tiles or none
+  __syncthreads();
+  if constexpr (EPI == EPI_UP_SWIGLU || EPI == EPI_UP_RELU) {
+    // H in the packed layout: the wave's TPW tiles are KF whole 32-column
+    // fragments of each of its MF row fragments; staged in that layout, then
+    // copied out fragment by fragment (fragments past the expert's last row
+    // are not written: they belong to the next expert).
+    constexpr int KF = TPW / 2;
+    uint16_t* st = reinterpret_cast<uint16_t*>(&ring[0][0]) + wave * (MF * KF * 512);
+    if (live) {
 #pragma unroll
-  for (int t = 0; t < TPW; ++t) {
-    const int nb = tile_base + wn * TPW + t;
-    if (nb >= NB) continue;
-    const int col = nb * 16 + (lane & 15);
-    float sc0 = 1.0f, sc1 = 1.0f;
-    if constexpr (QB != 0) {
-      sc0 = A.scale0[(size_t)e * A.N + col];
-      if constexpr (G == 2) sc1 = A.scale1[(size_t)e * A.N + col];
-    }
-#pragma unroll
-    for (int i = 0; i < MF; ++i) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int row = wm * 16 * MF + i * 16 + 4 * (lane >> 4) + q;
-        if (row >= nrows) continue;
-        float v0 = acc[i][t * G][q], v1 = acc[i][t * G + G - 1][q];
-        if constexpr (QB == 4) {
-          const float bias = kI4Bias * rowsum_s[row];
-          v0 -= bias;
-          v1 -= bias;
+      for (int t = 0; t < TPW; ++t) {
+        const int col = (nb0 + t) * 16 + (lane & 15);
+        float sc0 = 1.0f, sc1 = 1.0f;
+        if constexpr (QB != 0) {
+          sc0 = A.scale0[(size_t)e * A.N + col];
+          if constexpr (G == 2) sc1 = A.scale1[(size_t)e * A.N + col];
         }
-        v0 *= sc0;
-        v1 *= sc1;
-        if constexpr (EPI == EPI_UP_SWIGLU) {
-          A.h_out[packed_index(prow0 + row, col, A.N)] = f32_to_bf16(silu(v0) * v1);
-        } else if constexpr (EPI == EPI_UP_RELU) {
-          A.h_out[packed_index(prow0 + row, col, A.N)] = f32_to_bf16(v0 > 0.0f ? v0 : 0.0f);
-        } else {
-          A.f_out[(size_t)(row0 + row) * A.N + col] = v0;
+        const int c = 16 * (t & 1) + (lane & 15);  // column inside the 32-column fragment
+#pragma unroll
+        for (int i = 0; i < MF; ++i) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int r = 4 * (lane >> 4) + q;
+            float v0 = acc[i][t * G][q], v1 = acc[i][t * G + G - 1][q];
+            if constexpr (QB == 4) {
+              const float bias = kI4Bias * rowsum_s[wm * 16 * MF + i * 16 + r];
+              v0 -= bias;
+              v1 -= bias;
+            }
+            v0 *= sc0;
+            v1 *= sc1;
+            const float h = EPI == EPI_UP_SWIGLU ? silu_fast(v0) * v1 : (v0 > 0.0f ? v0 : 0.0f);
+            st[(i * KF + (t >> 1)) * 512 + (r + 16 * (c >> 3)) * 8 + (c & 7)] = f32_to_bf16(h);
+          }
+        }
+      }
+      const long long fr0 = (long long)((prow0 + wm * 16 * MF) >> 4) * (A.N >> 5) + (nb0 >> 1);
+#pragma unroll
+      for (int i = 0; i < MF; ++i) {
+        if (wm * 16 * MF + 16 * i >= nrows) break;
+#pragma unroll
+        for (int kf = 0; kf < KF; ++kf) {
+          const u32x4_t v = reinterpret_cast<const u32x4_t*>(st + (i * KF + kf) * 512)[lane];
+          reinterpret_cast<u32x4_t*>(A.h_out)[(fr0 + (long long)i * (A.N >> 5) + kf) * 64 + lane] = v;
+        }
+      }
+    }
+  } else {
+    // fp32 rows [row][N]: two row fragments (32 rows x the wave's 64 columns)
+    // at a time, rows padded to RS floats against bank conflicts, then four
+    // rows of 16 lanes x 16 bytes per store.
+    static_assert(TPW == 4 && MF % 2 == 0, "down tile: 64 columns per wave, row fragments in pairs");
+    constexpr int RS = 64 + 16;
+    float* st = reinterpret_cast<float*>(&ring[0][0]) + wave * (32 * RS);
+    if (live) {
+      const int c0 = nb0 * 16;
+      float sc[TPW];
+#pragma unroll
+      for (int t = 0; t < TPW; ++t) sc[t] = QB != 0 ? A.scale0[(size_t)e * A.N + c0 + 16 * t + (lane & 15)] : 1.0f;
+#pragma unroll
+      for (int pp = 0; pp < MF / 2; ++pp) {
+#pragma unroll
+        for (int ii = 0; ii < 2; ++ii) {
+          const int i = 2 * pp + ii;
+#pragma unroll
+          for (int t = 0; t < TPW; ++t)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const int r = 16 * ii + 4 * (lane >> 4) + q;
+              float v0 = acc[i][t][q];
+              if constexpr (QB == 4) v0 -= kI4Bias * rowsum_s[wm * 16 * MF + 16 * i + 4 * (lane >> 4) + q];
+              st[r * RS + 16 * t + (lane & 15)] = v0 * sc[t];
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int r = 4 * j + (lane >> 4);
+          const float4 v = *reinterpret_cast<const float4*>(st + r * RS + 4 * (lane & 15));
+          const int row = wm * 16 * MF + 32 * pp + r;
+          if (row < nrows) *reinterpret_cast<float4*>(A.f_out + (size_t)(row0 + row) * A.N + c0 + 4 * (lane & 15)) = v;
         }
       }
     }
@@ -699,28 +758,48 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
   // Epilogue.  Element v of acc[i][c] in lane l: row 32 i + 8 (v / 4) +
   // 4 (l / 32) + v % 4 of the wave's rows, column l % 32 of operand block c
   // (SwiGLU: gate c = 0 and up c = 1 of the same 32 hidden columns; ReLU:
-  // 32 columns each).
-  const int c32 = lane & 31;
+  // 32 columns each).  H is staged in LDS in the packed layout (KF 32-column
+  // fragments per 16-row fragment) and copied out 16 bytes per lane, as in
+  // the bf16 kernel.
+  constexpr int KF = TPW / 2;
+  const int nb0 = tile_base + wn * TPW;
+  const bool live = nb0 < NB;  // NB is a multiple of 4: all of the wave's tiles or none
+  __syncthreads();
+  uint16_t* st = reinterpret_cast<uint16_t*>(&ring[0][0]) + wave * (8 * KF * 512);
+  if (live) {
+    const int c32 = lane & 31;
 #pragma unroll
-  for (int c = 0; c < (G == 2 ? 1 : 2); ++c) {
-    const int col = (tile_base + wn * TPW + 2 * c) * 16 + c32;
-    if (col >= A.N) continue;
-    const float sc0 = A.scale0[(size_t)e * A.N + col];
-    const float sc1 = G == 2 ? A.scale1[(size_t)e * A.N + col] : 1.0f;
+    for (int c = 0; c < KF; ++c) {
+      const int col = (nb0 + 2 * c) * 16 + c32;
+      const float sc0 = A.scale0[(size_t)e * A.N + col];
+      const float sc1 = G == 2 ? A.scale1[(size_t)e * A.N + col] : 1.0f;
 #pragma unroll
-    for (int i = 0; i < RB; ++i) {
+      for (int i = 0; i < RB; ++i) {
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int row = wm * 128 + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-        if (row >= nrows) continue;
-        const float rs = row_scale[prow0 + row];
-        if constexpr (EPI == EPI_UP_SWIGLU) {
-          const float g = (float)acc[i][0][v] * sc0 * rs, up = (float)acc[i][1][v] * sc1 * rs;
-          A.h_out[packed_index(prow0 + row, col, A.N)] = f32_to_bf16(silu(g) * up);
-        } else {
-          const float g = (float)acc[i][c][v] * sc0 * rs;
-          A.h_out[packed_index(prow0 + row, col, A.N)] = f32_to_bf16(g > 0.0f ? g : 0.0f);
+        for (int v = 0; v < 16; ++v) {
+          const int R = 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);  // row of the wave's 128
+          const int row = wm * 128 + R;
+          const float rs = row < nrows ? row_scale[prow0 + row] : 0.0f;
+          float h;
+          if constexpr (EPI == EPI_UP_SWIGLU) {
+            const float g = (float)acc[i][0][v] * sc0 * rs, up = (float)acc[i][1][v] * sc1 * rs;
+            h = silu_fast(g) * up;
+          } else {
+            const float g = (float)acc[i][c][v] * sc0 * rs;
+            h = g > 0.0f ? g : 0.0f;
+          }
+          st[((R >> 4) * KF + c) * 512 + ((R & 15) + 16 * (c32 >> 3)) * 8 + (c32 & 7)] = f32_to_bf16(h);
         }
+      }
+    }
+    const long long fr0 = (long long)((prow0 + wm * 128) >> 4) * (A.N >> 5) + (nb0 >> 1);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if (wm * 128 + 16 * i >= nrows) break;
+#pragma unroll
+      for (int kf = 0; kf < KF; ++kf) {
+        const u32x4_t v = reinterpret_cast<const u32x4_t*>(st + (i * KF + kf) * 512)[lane];
+        reinterpret_cast<u32x4_t*>(A.h_out)[(fr0 + (long long)i * (A.N >> 5) + kf) * 64 + lane] = v;
       }
     }
   }

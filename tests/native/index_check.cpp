@@ -251,10 +251,33 @@ static void check_gemm(int K, int N, int G, int T, int topk, const std::vector<i
         }
       }
     for (int wm = 0; wm < WR; ++wm)
-      for (int wn = 0; wn < WC; ++wn)
+      for (int wn = 0; wn < WC; ++wn) {
+        // the epilogue: a wave's TPW tiles are KF whole 32-column packed
+        // fragments of each of its 8 row fragments; the fragments that start
+        // before the block's last real row are copied out whole (their
+        // padding rows included), the others not at all
+        const int nb0 = tile_base + wn * TPW;
+        CHECK(NB % 4 == 0 && nb0 % TPW == 0, "wave tiles %d.. of %d", nb0, NB);
+        if (nb0 >= NB) continue;
+        CHECK(nb0 + TPW <= NB && (nb0 * 16) % 32 == 0, "wave columns %d..+%d of %d", nb0 * 16, TPW * 16, N);
+        const int KF = TPW / 2;
+        for (int i = 0; i < 8; ++i) {
+          if (wm * 128 + 16 * i >= nrows) break;
+          const int fprow = prow0 + wm * 128 + 16 * i;
+          CHECK(fprow >= pe && fprow + 16 <= pe_end, "H fragment rows [%d,+16) outside expert %d [%d,%d)", fprow, e, pe,
+                pe_end);
+          for (int kf = 0; kf < KF; ++kf) {
+            const unsigned long long frag = (unsigned long long)(fprow >> 4) * (N >> 5) + (nb0 >> 1) + kf;
+            CHECK(frag == moe::packed_index(fprow, nb0 * 16 + 32 * kf, N) / 512, "H fragment %llu", frag);
+            for (int x = 0; x < 512; ++x) {
+              const unsigned long long hi = frag * 512 + x;
+              CHECK(hi < h_elems, "packed H index %llu of %llu", hi, h_elems);
+              if (cover && hi < h_elems) CHECK(hwritten[hi]++ == 0, "packed H element %llu written twice", hi);
+            }
+          }
+        }
         for (int t = 0; t < TPW; ++t) {
-          const int nb = tile_base + wn * TPW + t;
-          if (nb >= NB) continue;
+          const int nb = nb0 + t;
           for (int g = 0; g < G; ++g) {
             const unsigned long long bo = moe::gemm_b_offset(e, NB, U, G, tile_base, NF, wn * NF + t * G + g, 0);
             CHECK(bo == ((unsigned long long)(e * NB + nb) * U * G + g) * 1024ull, "B fragment of tile %d g=%d", nb,
@@ -264,10 +287,9 @@ static void check_gemm(int K, int N, int G, int T, int topk, const std::vector<i
             for (int r16 = 0; r16 < 16; ++r16) {
               const int row = wm * 128 + i * 16 + r16;
               if (row >= nrows) continue;
-              for (int c = 0; c < 16; ++c) {
-                const unsigned long long hi = moe::packed_index(prow0 + row, nb * 16 + c, N);
-                CHECK(hi < h_elems, "packed H index %llu of %llu", hi, h_elems);
-                if (cover && hi < h_elems) CHECK(hwritten[hi]++ == 0, "packed H element %llu written twice", hi);
+              if (cover) {  // every real row's element is inside a copied fragment
+                const unsigned long long hi = moe::packed_index(prow0 + row, nb * 16, N);
+                CHECK(hi < h_elems && hwritten[hi] == 1, "real H element %llu not written", hi);
               }
               if (!cover) continue;
               unsigned char& cs = seen[(size_t)(row0 + row) * NB + nb];
@@ -275,6 +297,7 @@ static void check_gemm(int K, int N, int G, int T, int topk, const std::vector<i
               cs = 1;
             }
         }
+      }
   }
   long long nitems = 0;
   for (int i = 0; i < E; ++i)

@@ -83,6 +83,42 @@ def test_quantize_rows_is_bit_exact(fmt, T, m):
     assert bad.size == 0, f"{len(bad)} values differ, first at {bad[:5].tolist()}"
 
 
+@pytest.mark.parametrize("fmt", ["e4m3", "i8"])
+def test_quantize_rows_every_bf16_value(fmt):
+    """Every bf16 value of magnitude up to the format's largest (448 for
+    E4M3, 127 for int8), both signs, in rows whose maximum is exactly that
+    bound, so the scale is 1 and each value's code is the format's rounding
+    of the value itself: the kernel's codes (as their values) against the
+    oracle's for the whole input range of the encoder."""
+    qmax = 448.0 if fmt == "e4m3" else 127.0
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    v = torch.from_numpy(bits.view(np.int16).copy()).view(torch.bfloat16).double().numpy()
+    keep = np.isfinite(v) & (np.abs(v) <= qmax)
+    vals = bits[keep]
+    m = 4096
+    per = m - 1
+    T = (len(vals) + per - 1) // per
+    xb = np.zeros((T, m), np.uint16)
+    top = _bf16_bits(np.array([qmax]))[0]
+    xb[:, 0] = top
+    flat = np.zeros(T * per, np.uint16)
+    flat[: len(vals)] = vals
+    xb[:, 1:] = flat.reshape(T, per)
+    val, codes, scales = (oracle.quant_rows_i8 if fmt == "i8" else oracle.quant_rows_e4m3)(xb)
+    assert np.all(scales == 1.0)
+    x = to_device(xb)
+    xq = torch.empty((T, m), dtype=torch.int16, device="cuda")
+    sc = torch.empty(T, dtype=torch.float32, device="cuda")
+    (M.moe_quantize_rows_i8 if fmt == "i8" else M.moe_quantize_rows_e4m3)(x, T, m, xq, sc)
+    torch.cuda.synchronize()
+    assert np.all(sc.cpu().numpy() == 1.0), "scales"
+    got = xq.cpu().numpy().view(np.uint16)
+    want = _bf16_bits(val)
+    bad = np.argwhere(got != want)
+    log(f"{fmt}: {len(vals)} bf16 values over {T} rows, {len(bad)} differ")
+    assert bad.size == 0, f"{len(bad)} values differ, first inputs {[hex(xb[i, j]) for i, j in bad[:5]]}"
+
+
 SHAPES = [(1, 128, 256, 4, 1), (16, 512, 1024, 8, 2), (64, 256, 384, 8, 2), (257, 256, 512, 16, 2),
           (3, 128, 128, 8, 8)]
 
