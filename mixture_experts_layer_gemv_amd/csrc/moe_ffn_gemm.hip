@@ -24,10 +24,10 @@
 // turns: one multiplies the stage it holds in registers while the other reads
 // its next stage and issues copies (ping-pong, two barriers per step); three
 // to four stages of copies stay in flight.
-// Workgroups run expert by expert, in groups of A.cg (4) column blocks x all
+// Workgroups run expert by expert, in groups of A.cg (2) column blocks x all
 // of the expert's row blocks, on one XCD at a time: the ~32 resident
-// workgroups then read ~8 activation tiles and ~4 weight tiles per stage,
-// the rest hits in L2.
+// workgroups (about two groups) then read ~8 activation tiles and ~4 weight
+// tiles per stage, the rest hits in L2.
 //
 // Measured on the Mixtral-shaped prefill layer (T = 8192), the kernel runs
 // the matrix cores about half the time: the global -> LDS copies alone take
