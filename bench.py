@@ -13,9 +13,9 @@ one JSON line for it, with the roofline position of its dominant kernel
 oracle timed on a bounded sample of the same layer.  Beside it, under
 "configs", the same figures for the other measured layers (tiny fp32,
 Mixtral decode, Phi-3.5 skewed, Mixtral int8, int4, fp8, fp8a8 and MXFP4
-decode, Mixtral int8, int4, fp8, fp8a8 and i8a8 prefill; fp8a8 and i8a8: fp8
-or int8 weights with activations quantised to the same format, the prefill up
-projection on the fp8 or int8 matrix cores).
+decode, Mixtral int8, int4, fp8, fp8a8, i8a8 and MXFP4 prefill; fp8a8 and
+i8a8: fp8 or int8 weights with activations quantised to the same format, the
+prefill up projection on the fp8 or int8 matrix cores).
 
   python bench.py [--steps K] [--warmup W]            headline + every layer
   python bench.py --workload c2 [--steps K]           one layer only
@@ -39,7 +39,7 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
 MFMA_FP8_PEAK_TFLOPS = 5000.0  # MI355X dense fp8 (and int8, in TOP/s)
 METRIC = "MoE layer tokens/s; achieved HBM GB/s (T≤64) or MFMA TFLOP/s (T≥4096)"
 HEADLINE = "c4"
-OTHERS = ["c1", "c2", "c3", "c5", "c6", "c9", "c10", "c13", "c7", "c8", "c11", "c12", "c14"]
+OTHERS = ["c1", "c2", "c3", "c5", "c6", "c9", "c10", "c13", "c7", "c8", "c11", "c12", "c14", "c15"]
 TRAFFIC_DIR = os.path.join(ROOT, "profiles")
 _CSRC = "mixture_experts_layer_gemv_amd/csrc/"
 _SKINNY = [_CSRC + f for f in
@@ -49,7 +49,7 @@ _GEMM = [_CSRC + f for f in ("moe_ffn_gemm.hip", "moe_index.hpp", "moe_kernels.h
 _F32 = [_CSRC + f for f in ("moe_misc.hip", "moe_index.hpp", "moe_kernels.hpp")]
 KERNEL_SOURCES = {"ffn_up": _SKINNY, "ffn_down": _SKINNY, "gemm_up": _GEMM, "gemm_down": _GEMM,
                   "ffn_f32_up": _F32, "ffn_f32_down": _F32}
-KERNELS = ("fill", "route_topk", "dispatch", "quant_rows", "ffn_up", "ffn_down", "ffn_f32_up", "ffn_f32_down", "finalize",
+KERNELS = ("fill", "route_topk", "dispatch", "quant_rows", "expand_w", "ffn_up", "ffn_down", "ffn_f32_up", "ffn_f32_down", "finalize",
            "pack_rows", "gemm_up", "gemm_down", "combine")
 
 
@@ -59,7 +59,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=None,
-                    help="time only this layer (c1..c14); default: the prefill layer with every other layer beside it")
+                    help="time only this layer (c1..c15); default: the prefill layer with every other layer beside it")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calib-mib", type=int, default=0,

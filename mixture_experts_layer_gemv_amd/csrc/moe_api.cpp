@@ -212,14 +212,18 @@ constexpr int kGemmCg = 2;
 int tuned(int v, int dflt) { return v != 0 ? v : dflt; }
 bool tuned_on(int v, bool dflt) { return v == 0 ? dflt : v > 0; }
 
+// The weight kind the grouped GEMM multiplies: MXFP4 layers expand their
+// weights exactly to packed bf16 in the workspace first (each E2M1 value
+// times its E8M0 block scale is a bf16 value) and run the bf16 kernel, whose
+// ring has no room to stage block scales beside each weight stage.
+int gemm_qb(const LayerCfg& c) { return c.w_dtype == MOE_MXFP4 ? 0 : weight_bits(c); }
+
 // The GEMM addresses packed activations and one projection's packed weights
 // with 32-bit byte offsets from a uniform base.
 bool gemm_fits(const LayerCfg& c, int T, int k) {
-  // (MXFP4 weights run the decode kernels at every batch size: the grouped
-  // GEMM would have to stage their block scales beside each weight stage)
-  if (c.w_dtype == MOE_F32 || c.w_dtype == MOE_MXFP4) return false;
+  if (c.w_dtype == MOE_F32) return false;
   const unsigned long long lim = 1ull << 32;
-  const int qb = weight_bits(c);
+  const int qb = gemm_qb(c);
   const unsigned long long G = c.kind == MOE_SWIGLU ? 2 : 1;
   const unsigned long long up_w = moe::packed_bytes(c.E, c.m, c.p, (int)G, qb);
   const unsigned long long dn_w = moe::packed_bytes(c.E, c.p, c.m, 1, qb);
@@ -361,7 +365,7 @@ DownShape skinny_down_shape(const LayerCfg& c, int T, int k) {
 
 // Workspace carving, in the order listed.
 struct Ws {
-  size_t logits, idx, w, counts, offsets, perm, inv, xn, xq, xs, h, yacc, yperm, xp, rs, total;
+  size_t logits, idx, w, counts, offsets, perm, inv, xn, xq, xs, h, yacc, yperm, xp, rs, wdq, total;
 };
 
 Ws ws_layout(const LayerCfg& c, int T, int k) {
@@ -400,6 +404,11 @@ Ws ws_layout(const LayerCfg& c, int T, int k) {
   L.xp = gemm || spack ? take(prows * (size_t)c.m * 2) : off;
   // fp8 activations on the grouped GEMM: each packed row's token scale
   L.rs = gemm && act8(c) ? take(prows * 4) : off;
+  // MXFP4 on the grouped GEMM: one projection's weights expanded to packed bf16
+  const int G = c.kind == MOE_SWIGLU ? 2 : 1;
+  L.wdq = gemm && c.w_dtype == MOE_MXFP4
+              ? take(std::max(moe::packed_bytes(c.E, c.m, c.p, G, 0), moe::packed_bytes(c.E, c.p, c.m, 1, 0)))
+              : off;
   L.total = off;
   return L;
 }
@@ -423,6 +432,7 @@ struct FfnIo {
   int* slices;              // set to the number of row slices written to yperm
   long long rows = -1;      // >= 0: the dispatched rows this call serves (one expert's, when
                             // streaming experts); sizes the launch grids tightly
+  void* wdq = nullptr;      // MXFP4 on the grouped GEMM: room for one projection's weights in bf16
 };
 
 // The dispatched rows an FFN call serves: all T*k, or the caller's bound.
@@ -494,8 +504,11 @@ moe_status run_pack(const LayerCfg& c, const FfnIo& io, hipStream_t s) {
 moe_status run_gemm(const moe_weights* W, const FfnIo& io, float* y_rows, hipStream_t s) {
   const LayerCfg& c = W->c;
   const long long n = ffn_rows(io);
-  const int qb = weight_bits(c);
+  const int qb = gemm_qb(c);
   const int bm = moe::gemm_rows_per_block(qb);
+  const bool mx = c.w_dtype == MOE_MXFP4;
+  if (mx && !io.wdq) return fail(MOE_ERR_WORKSPACE, "MXFP4 grouped GEMM without its weight buffer (internal)");
+  const int G = c.kind == MOE_SWIGLU ? 2 : 1;
   moe::GemmArgs g{};
   g.offsets = io.offsets;
   g.E = c.E;
@@ -510,6 +523,12 @@ moe_status run_gemm(const moe_weights* W, const FfnIo& io, float* y_rows, hipStr
   g.w = W->up;
   g.scale0 = W->s_gate;
   g.scale1 = W->s_up;
+  if (mx) {
+    MOE_TRY_HIP(run("expand_w", s, [&] {
+      return moe::launch_expand_fp4(W->up, W->mx_up, io.wdq, io.offsets, c.E, c.m, c.p, G, s);
+    }));
+    g.w = io.wdq;
+  }
   g.act = static_cast<const uint16_t*>(io.xp);
   g.h_out = static_cast<uint16_t*>(io.h);
   g.K = c.m;
@@ -538,6 +557,12 @@ moe_status run_gemm(const moe_weights* W, const FfnIo& io, float* y_rows, hipStr
   }
   // down: packed H -> rows in dispatch order
   g.w = W->down;
+  if (mx) {  // the up projection has read the buffer by now (stream order)
+    MOE_TRY_HIP(run("expand_w", s, [&] {
+      return moe::launch_expand_fp4(W->down, W->mx_down, io.wdq, io.offsets, c.E, c.p, c.m, 1, s);
+    }));
+    g.w = io.wdq;
+  }
   g.scale0 = W->s_down;
   g.scale1 = nullptr;
   g.act = static_cast<const uint16_t*>(io.h);
@@ -736,7 +761,7 @@ moe_tuning pinned_tuning(const LayerCfg& c, int T, int k) {
   const int qb = weight_bits(c);
   if (path == Path::GEMM) {
     const long long n = (long long)T * k;
-    t.gemm_skip = tuned_on(c.tune.gemm_skip, n < (long long)moe::gemm_rows_per_block(qb) * c.E) ? 1 : -1;
+    t.gemm_skip = tuned_on(c.tune.gemm_skip, n < (long long)moe::gemm_rows_per_block(gemm_qb(c)) * c.E) ? 1 : -1;
     t.gemm_cg = tuned(c.tune.gemm_cg, kGemmCg);
   } else {
     const int mt = skinny_mt(c, T, k);
@@ -1185,6 +1210,7 @@ moe_status moe_expert_ffn(const moe_weights* w, const void* x, int x_dtype, int 
   io.xp = ws + L.xp;
   io.down_out = y_perm;
   io.combine = false;
+  io.wdq = ws + L.wdq;
   if (moe_status rc = quant_input(w->c, io, ws, L, as_stream(stream))) return rc;
   if (moe_status rc = w->off ? run_ffn_streamed(w, io, as_stream(stream)) : run_ffn(w, io, as_stream(stream)))
     return rc;
@@ -1325,6 +1351,7 @@ moe_status enqueue_forward(const moe_weights* w, const float* w_router, const fl
   io.down_out = yacc;
   io.combine = true;
   io.yperm = rows ? reinterpret_cast<float*>(ws + L.yperm) : nullptr;
+  io.wdq = ws + L.wdq;
   int slices = 1;
   io.slices = &slices;
   if (moe_status rc = quant_input(c, io, ws, L, s, q_in_route)) return rc;

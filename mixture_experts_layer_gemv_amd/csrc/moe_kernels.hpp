@@ -61,6 +61,11 @@ inline size_t packed_mx_scale_bytes(int E, int K, int N, int G) {
 }
 
 hipError_t launch_pack_bf16(const uint16_t* src, void* dst, int E, int K, int N, int G, int g, hipStream_t s);
+// Packed MXFP4 weights (and their packed block scales) of E experts -> the
+// packed bf16 layout, exactly; experts without rows skipped when offsets
+// ([E+1], device) is given.  dst holds packed_bytes(E, K, N, G, 0).
+hipError_t launch_expand_fp4(const void* w, const uint32_t* scales, void* dst, const int32_t* offsets, int E, int K,
+                             int N, int G, hipStream_t s);
 hipError_t launch_pack_i8(const int8_t* src, void* dst, int E, int K, int N, int G, int g, hipStream_t s);
 // int4 values held one per int8 (in [-8, 7]), packed two per byte.
 hipError_t launch_pack_i4(const int8_t* src, void* dst, int E, int K, int N, int G, int g, hipStream_t s);

@@ -130,6 +130,36 @@ __global__ __launch_bounds__(256) void k_pack_mx_scales(const uint8_t* __restric
   }
 }
 
+// MXFP4 weights expanded exactly to the packed bf16 layout of the grouped GEMM
+// (prefill sizes): one thread per lane of a packed unit (128 k of one column
+// stream); dword h of the unit holds the lane's eight values of 32-k step
+// 4u + h, whose block scale is byte h of the column's scale dword, and they
+// become the lane's 16 bytes of bf16 unit 4u + h.  E2M1 values times an E8M0
+// scale are bf16 values (two significant bits).  Experts without rows (per
+// offsets, when given) are skipped.
+__global__ __launch_bounds__(256) void k_expand_fp4(const uint4* __restrict__ src, const uint32_t* __restrict__ sc,
+                                                    uint4* __restrict__ dst, const int32_t* __restrict__ offsets,
+                                                    int E, int K, int N, int G) {
+  const int NB = N / 16, U = K / 128;
+  const size_t total = (size_t)E * NB * U * G * 64;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (size_t)gridDim.x * blockDim.x) {
+    const int lane = (int)(i & 63);
+    size_t rest = i >> 6;  // (((e * NB + nb) * U + u) * G + g)
+    const int g = (int)(rest % G);
+    const size_t eu = rest / G;  // ((e * NB + nb) * U + u)
+    const int u = (int)(eu % U);
+    const int e = (int)(eu / U / NB);
+    if (offsets && offsets[e + 1] == offsets[e]) continue;
+    const uint4 q = src[i];
+    const uint32_t d = sc[rest * 16 + (lane & 15)];
+    const size_t o = ((eu / U * (size_t)(4 * U) + 4 * (size_t)u) * G + g) * 64 + lane;  // bf16 unit 4u of the same tile
+    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+    for (int h = 0; h < 4; ++h)
+      dst[o + (size_t)h * G * 64] = __builtin_bit_cast(uint4, fp4x8_to_bf16(w[h], e8m0_at(d, h)));
+  }
+}
+
 // ---- fp32 expert FFN ------------------------------------------------------------
 //
 // True fp32 arithmetic (one fused multiply-add per term, in increasing k) for
@@ -342,6 +372,16 @@ hipError_t launch_pack_i4(const int8_t* src, void* dst, int E, int K, int N, int
 hipError_t launch_pack_fp4(const uint8_t* src, void* dst, int E, int K, int N, int G, int g, hipStream_t s) {
   const size_t total = (size_t)E * (N / 16) * (K / 128) * 64;
   k_pack_fp4<<<grid_for(total, 1u << 20), 256, 0, s>>>(src, static_cast<uint4*>(dst), E, K, N, G, g);
+  return hipGetLastError();
+}
+
+hipError_t launch_expand_fp4(const void* w, const uint32_t* scales, void* dst, const int32_t* offsets, int E, int K,
+                             int N, int G, hipStream_t s) {
+  if (K % 128 || N % 16) return hipErrorInvalidValue;
+  const size_t total = (size_t)E * (N / 16) * (K / 128) * G * 64;
+  if (total == 0) return hipSuccess;
+  k_expand_fp4<<<grid_for(total, 1u << 20), 256, 0, s>>>(static_cast<const uint4*>(w), scales, static_cast<uint4*>(dst),
+                                                           offsets, E, K, N, G);
   return hipGetLastError();
 }
 

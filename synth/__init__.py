@@ -205,6 +205,10 @@ CONFIGS = {
     # quantised): the first projection on the int8 matrix cores
     "c14": LayerSpec("mixtral_prefill_i8a8", 8192, 4096, 14336, 8, 2, "swiglu", "bf16", "i8a8", 6,
                      note="Mixtral-8x7B-shaped prefill, int8 weights and per-token int8 activations"),
+    # MXFP4 weights at prefill size: the grouped GEMM on the weights expanded
+    # to bf16
+    "c15": LayerSpec("mixtral_prefill_mxfp4", 8192, 4096, 14336, 8, 2, "swiglu", "bf16", "mxfp4", 11,
+                     note="Mixtral-8x7B-shaped prefill, MXFP4 weights (E2M1, E8M0 scale per 32 k)"),
 }
 
 

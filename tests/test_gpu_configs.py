@@ -53,7 +53,7 @@ def prefill_tokens(offsets, perm, k, T, seed, n_min=PREFILL_MIN_TOKENS, block=BL
     return np.array(sorted(toks)), blocks
 
 
-@pytest.mark.parametrize("cfg", ["c1", "c2", "c3", "c4", "c5", "c7", "c8", "c11", "c12", "c14"])
+@pytest.mark.parametrize("cfg", ["c1", "c2", "c3", "c4", "c5", "c7", "c8", "c11", "c12", "c14", "c15"])
 def test_config_full_size(cfg):
     sp = synth.spec(cfg)
     log(f"config {cfg} ({sp.name}): T={sp.T} m={sp.m} p={sp.p} E={sp.E} k={sp.k} {sp.kind} "

@@ -86,6 +86,36 @@ def test_float_weights_launch_modes(w_dtype, mt, pack, waves, tune):
                                        sw=0.05, sr=0.05)))
 
 
+MX_GEMM_SHAPES = [(5, 128, 128, 3, 2), (37, 256, 384, 8, 2), (300, 256, 512, 4, 2), (600, 1024, 1536, 8, 2),
+                  (1, 512, 384, 16, 2), (64, 128, 128, 64, 4), (700, 384, 256, 2, 1)]
+
+
+@pytest.mark.parametrize("kind", ["swiglu", "relu"])
+@pytest.mark.parametrize("T,m,p,E,k", MX_GEMM_SHAPES)
+def test_mxfp4_grouped_gemm(kind, T, m, p, E, k, tune):
+    """MXFP4 weights on the grouped GEMM (forced onto small shapes): each
+    projection's weights expanded to packed bf16 in the workspace, then the
+    bf16 kernel; the expert stage on an explicit dispatch (ragged and empty
+    experts) and the whole layer."""
+    tune(ffn_path=M.MOE_PATH_GEMM)
+    log(f"mxfp4 gemm kind={kind} T={T} m={m} p={p} E={E} k={k}")
+    L = synth.make_layer(spec(T, m, p, E, k, kind, "mxfp4", seed=T + 5 * E + p, sw=0.05, sr=0.05))
+    layer = MoELayer(L)
+    rng = np.random.default_rng(T + 3)
+    idx = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    counts, offsets, perm, _ = oracle.dispatch(idx, E)
+    y_perm = torch.full((T * k, m), float("nan"), dtype=torch.float32, device="cuda")
+    M.moe_expert_ffn(layer.handle, layer.x, layer.x_dtype, T, m, p, E, k, to_device(perm), to_device(offsets),
+                     y_perm, layer.ensure_workspace(T), layer.ws_bytes)
+    torch.cuda.synchronize()
+    ref, _ = oracle.expert_rows(oracle.Experts.from_layer(L), L["x"], k, perm, offsets)
+    got = y_perm.cpu().numpy()
+    assert np.all(np.isfinite(got)), "rows left unwritten"
+    assert_close(got, ref, "bf16", "y_perm")
+    layer.close()
+    _layer_check(L)
+
+
 @pytest.mark.parametrize("cfg", ["c9", "c10"])
 def test_float_weight_decode_layers_full_size(cfg):
     sp = synth.spec(cfg)
