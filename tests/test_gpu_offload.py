@@ -45,6 +45,7 @@ CASES = [
     ("relu_bf16", (40, 256, 512, 8, 2, "relu", "bf16", None)),
     ("prefill_gemm", (1536, 256, 512, 4, 2, "swiglu", "bf16", None)),
     ("prefill_gemm_int4", (1536, 256, 512, 4, 2, "swiglu", "i4", None)),
+    ("prefill_gemm_mxfp4", (1536, 256, 512, 4, 2, "swiglu", "mxfp4", None)),  # one expert expanded at a time
 ]
 
 
