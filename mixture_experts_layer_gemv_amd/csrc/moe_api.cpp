@@ -204,9 +204,12 @@ moe_status check_combo(int x_dtype, int w_dtype) {
 enum class Path { F32, SKINNY, GEMM };
 constexpr int kGemmMinRows = 128;
 // Grouped GEMM work order: column blocks per group (each group takes all of
-// its expert's row blocks).  Measured on the Mixtral prefill layer's up
-// projection: 2 ahead of 3, 4, 5, 6 and 8 by 0.7-2 % on two boxes.
-constexpr int kGemmCg = 2;
+// its expert's row blocks; the ~32 workgroups resident on an XCD share the
+// group's tiles in L2).  Measured on the Mixtral prefill layers: 2 ahead of
+// 3-8 by 0.7-2 % for 256-row blocks (bf16, int8; fp8 equal); 8 for int4's
+// 128-row blocks, whose activation tile per stage is twice its weight tile
+// (4.3 % ahead of 2, 1 % of 4).
+int gemm_cg_default(int qb) { return qb == 4 ? 8 : 2; }
 
 // 0 ("automatic") or the tuning's value.
 int tuned(int v, int dflt) { return v != 0 ? v : dflt; }
@@ -515,7 +518,7 @@ moe_status run_gemm(const moe_weights* W, const FfnIo& io, float* y_rows, hipStr
   // row blocks: at most n/bm full ones plus one partial per expert
   g.W = (int)(n / bm + std::min<long long>(c.E, n));
   if (g.W <= 0) return MOE_OK;  // no rows
-  g.cg = tuned(c.tune.gemm_cg, kGemmCg);
+  g.cg = tuned(c.tune.gemm_cg, gemm_cg_default(qb));
   // experts averaging under one full row block: skip the products of empty
   // row fragments
   g.skip_empty = tuned_on(c.tune.gemm_skip, n < (long long)bm * c.E);
@@ -762,7 +765,7 @@ moe_tuning pinned_tuning(const LayerCfg& c, int T, int k) {
   if (path == Path::GEMM) {
     const long long n = (long long)T * k;
     t.gemm_skip = tuned_on(c.tune.gemm_skip, n < (long long)moe::gemm_rows_per_block(gemm_qb(c)) * c.E) ? 1 : -1;
-    t.gemm_cg = tuned(c.tune.gemm_cg, kGemmCg);
+    t.gemm_cg = tuned(c.tune.gemm_cg, gemm_cg_default(gemm_qb(c)));
   } else {
     const int mt = skinny_mt(c, T, k);
     t.skinny_mt = mt;
