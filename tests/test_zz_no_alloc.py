@@ -55,6 +55,11 @@ CASES = [
     ("relu_bf16", (40, 256, 512, 8, 2, "relu", "bf16", None), 3, True),
     ("prefill_gemm", (1536, 256, 512, 4, 2, "swiglu", "bf16", None), 600, True),
     ("tiny_f32", (32, 256, 512, 8, 2, "relu", "f32", None), 9, False),
+    # the routing pass's 8-bit quantised rows, and MXFP4 weights expanded to
+    # bf16, in the scratch too
+    ("decode_fp8a8", (64, 256, 512, 8, 2, "swiglu", "fp8a8", None), 9, True),
+    ("prefill_gemm_i8a8", (1536, 256, 512, 4, 2, "swiglu", "i8a8", None), 600, True),
+    ("prefill_gemm_mxfp4", (1536, 256, 512, 4, 2, "swiglu", "mxfp4", None), 600, True),
 ]
 
 
