@@ -197,7 +197,7 @@ struct RouteShape {
   static constexpr int RPC = 64 / Q;                               // rows per 1 KiB chunk
   static constexpr int NV = TB * 4;                                // partial sums per lane
   static constexpr int STEPS = 6 - LQ;                             // lane bits that index rows
-  static constexpr bool HALVING = NV >= (2 << STEPS);              // enough sums for a reduce-scatter
+  static constexpr bool HALVING = NV >= (1 << STEPS);              // enough sums for a reduce-scatter
   static constexpr int PER = HALVING ? (NV >> STEPS) : NV;         // sums a lane holds afterwards
 };
 
@@ -223,12 +223,16 @@ constexpr int kRouteLdsX = 128 * 1024;  // most bytes of staged activations per 
 // TB * m * sizeof(x) against the same figure.
 constexpr int route_lds_bytes(int tb) { return tb * 65536 < kRouteLdsX ? tb * 65536 : kRouteLdsX; }
 
-// Router for E in {8, 16, 32, 64}: one 1024-thread block per TB tokens
-// (TB * E <= 128).  The tokens' activation rows are staged in LDS; each wave
+// Router for E in {8, 16, 32, 64}: one block of NW waves per TB tokens
+// (TB * E <= 128, NW >= TB), staging at most LX bytes of activation rows.
+// 16 waves and up to 128 KiB by default; large batches of rows up to 8 KiB
+// take 8 tokens on 8 waves in 64 KiB, so that two blocks share a CU and one
+// stages its rows while the other multiplies.  The tokens' activation rows
+// are staged in LDS; each wave
 // streams 1 KiB chunks of the router weights with one coalesced 16-byte load
 // per lane (lane = row-in-chunk x expert quad) and keeps TB x 4 partial sums.
 // Sums over rows: across the lanes of a wave (reduce-scatter when there are
-// enough partials, butterfly otherwise), then a fixed-order sum over the 16
+// enough partials, butterfly otherwise), then a fixed-order sum over the NW
 // waves in LDS.  One wave per token then takes the top-k.  The block also
 // zeroes its tokens' rows of the fp32 output accumulator.
 __device__ __forceinline__ float wave_sum64(float v) {
@@ -258,17 +262,18 @@ __device__ __forceinline__ float norm_value(const RouteFuse& F, float xv, float 
   return v;
 }
 
-template <int E, int TB, bool XBF16>
-__global__ __launch_bounds__(1024) void k_route_fast(const void* __restrict__ x, const float* __restrict__ wg,
+template <int E, int TB, bool XBF16, int NW = 16, int LX = route_lds_bytes(TB)>
+__global__ __launch_bounds__(64 * NW) void k_route_fast(const void* __restrict__ x, const float* __restrict__ wg,
                                                      const float* __restrict__ bias, int T, int m, int k,
                                                      float* __restrict__ logits, int32_t* __restrict__ idx,
                                                      float* __restrict__ wout, float* __restrict__ yacc, int ym,
                                                      const RouteFuse F) {
   using S = RouteShape<E, TB>;
-  static_assert(TB * E <= 128 && TB <= 16, "block shape");
+  static_assert(TB * E <= 128 && TB <= 16 && NW >= TB && NW <= 16, "block shape");
   constexpr int XB = XBF16 ? 2 : 4;
-  __shared__ __attribute__((aligned(16))) unsigned char xs_raw[route_lds_bytes(TB)];
-  __shared__ float red[16][TB * E];
+  constexpr int NT = 64 * NW;  // threads
+  __shared__ __attribute__((aligned(16))) unsigned char xs_raw[LX];
+  __shared__ float red[NW][TB * E];
   __shared__ float lg[TB][E];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int t0 = blockIdx.x * TB;
@@ -276,11 +281,11 @@ __global__ __launch_bounds__(1024) void k_route_fast(const void* __restrict__ x,
 
   if (yacc && F.residual) {
     const size_t base = (size_t)t0 * ym;
-    for (int i = tid; i < nt * ym; i += 1024) yacc[base + i] = residual_at(F, base + i);
+    for (int i = tid; i < nt * ym; i += NT) yacc[base + i] = residual_at(F, base + i);
   } else if (yacc) {
     float4* yr = reinterpret_cast<float4*>(yacc + (size_t)t0 * ym);
     const int n4 = nt * ym / 4;
-    for (int i = tid; i < n4; i += 1024) yr[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int i = tid; i < n4; i += NT) yr[i] = make_float4(0.f, 0.f, 0.f, 0.f);
   }
   // stage x rows [t0, t0 + nt) (rows past T are zero), eight loads in flight
   // per thread before the first LDS write
@@ -289,16 +294,16 @@ __global__ __launch_bounds__(1024) void k_route_fast(const void* __restrict__ x,
     uint4* dst = reinterpret_cast<uint4*>(xs_raw);
     const uint4* src = reinterpret_cast<const uint4*>(static_cast<const char*>(x) + (size_t)t0 * m * XB);
     constexpr int U = 8;
-    for (int i0 = tid; i0 < n16; i0 += 1024 * U) {
+    for (int i0 = tid; i0 < n16; i0 += NT * U) {
       uint4 v[U];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const int i = i0 + 1024 * u;
+        const int i = i0 + NT * u;
         v[u] = i < live16 ? src[i] : make_uint4(0, 0, 0, 0);
       }
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const int i = i0 + 1024 * u;
+        const int i = i0 + NT * u;
         if (i < n16) dst[i] = v[u];
       }
     }
@@ -334,7 +339,7 @@ __global__ __launch_bounds__(1024) void k_route_fast(const void* __restrict__ x,
       }
     }
     __syncthreads();
-    for (int i = tid; i < nt * m; i += 1024) {
+    for (int i = tid; i < nt * m; i += NT) {
       const int t = i / m, c = i - t * m;
       const float v = norm_value<XBF16>(F, xat(t, c), mu_s[t], r_s[t], c);
       if constexpr (XBF16) {
@@ -376,7 +381,7 @@ __global__ __launch_bounds__(1024) void k_route_fast(const void* __restrict__ x,
       __syncthreads();
       uint4* q8 = F.xq ? reinterpret_cast<uint4*>(F.xq + (size_t)t0 * m) : nullptr;
       uint2* c8 = F.xc ? reinterpret_cast<uint2*>(F.xc + (size_t)t0 * m) : nullptr;
-      for (int i = tid; i < nt * m8; i += 1024) {
+      for (int i = tid; i < nt * m8; i += NT) {
         const uint4 v = x8[i];
         const uint32_t w[4] = {v.x, v.y, v.z, v.w};
         const int X = qx_s[i / m8];
@@ -402,16 +407,16 @@ __global__ __launch_bounds__(1024) void k_route_fast(const void* __restrict__ x,
   // issues all its weight loads before the first product (a chunk past the
   // end reloads the group's first), and the products keep increasing c.
   constexpr int WU = 8;
-  for (int c0 = wave; c0 < nchunks; c0 += 16 * WU) {
+  for (int c0 = wave; c0 < nchunks; c0 += NW * WU) {
     float4 wv[WU];
 #pragma unroll
     for (int u = 0; u < WU; ++u) {
-      const int c = c0 + 16 * u < nchunks ? c0 + 16 * u : c0;
+      const int c = c0 + NW * u < nchunks ? c0 + NW * u : c0;
       wv[u] = *reinterpret_cast<const float4*>(wg + (size_t)(c * S::RPC + rr) * E + 4 * q);
     }
 #pragma unroll
     for (int u = 0; u < WU; ++u) {
-      const int c = c0 + 16 * u;
+      const int c = c0 + NW * u;
       if (c < nchunks) {
         const int r = c * S::RPC + rr;
 #pragma unroll
@@ -449,7 +454,7 @@ __global__ __launch_bounds__(1024) void k_route_fast(const void* __restrict__ x,
   if (tid < TB * E) {
     float s = 0.0f;
 #pragma unroll
-    for (int w = 0; w < 16; ++w) s += red[w][tid];
+    for (int w = 0; w < NW; ++w) s += red[w][tid];
     const int t = tid / E, e = tid % E;
     if (bias) s += bias[e];
     lg[t][e] = s;
@@ -600,6 +605,22 @@ hipError_t launch_route_topk(const void* x, bool x_bf16, const float* wg, const 
     // reads over T CUs; at 256 tokens of 4096 and 16 experts, 9.8 against
     // 12.7 us for four), up to 128 / E for large batches
     const int tb_max = 128 / E < 16 ? 128 / E : 16;
+    // past 1024 tokens, eight tokens per 512-thread block with 64 KiB of
+    // staged rows (two blocks per CU) where they fit
+    if (T > 1024 && tb_max >= 8 && 8 * m * xb <= 65536) {
+      const unsigned grid = (unsigned)((T + 7) / 8);
+#define MOE_ROUTE_HALF(EE)                                                                                    \
+  if (E == EE) {                                                                                              \
+    if (x_bf16)                                                                                               \
+      k_route_fast<EE, 8, true, 8, 65536><<<grid, 512, 0, s>>>(x, wg, bias, T, m, k, logits, idx, w, yacc, ym, F); \
+    else                                                                                                      \
+      k_route_fast<EE, 8, false, 8, 65536><<<grid, 512, 0, s>>>(x, wg, bias, T, m, k, logits, idx, w, yacc, ym, F); \
+    return hipGetLastError();                                                                                 \
+  }
+      MOE_ROUTE_HALF(8)
+      MOE_ROUTE_HALF(16)
+#undef MOE_ROUTE_HALF
+    }
     const int tb = T <= 256 ? 1 : (T <= 1024 ? (4 < tb_max ? 4 : tb_max) : tb_max);
     if (tb * m * xb <= route_lds_bytes(tb)) {
       const unsigned grid = (unsigned)((T + tb - 1) / tb);
@@ -613,7 +634,6 @@ hipError_t launch_route_topk(const void* x, bool x_bf16, const float* wg, const 
   }
       MOE_ROUTE_FAST(8, 1)
       MOE_ROUTE_FAST(8, 4)
-      MOE_ROUTE_FAST(8, 16)
       MOE_ROUTE_FAST(16, 1)
       MOE_ROUTE_FAST(16, 4)
       MOE_ROUTE_FAST(16, 8)

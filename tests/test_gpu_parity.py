@@ -40,7 +40,11 @@ def _gpu():
 @pytest.mark.parametrize("x_dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("T,m,E,k,zipf", [(1, 64, 1, 1, None), (5, 128, 3, 2, None), (70, 256, 8, 2, None),
                                           (33, 4096, 8, 2, None), (129, 512, 16, 2, 1.2), (40, 192, 33, 3, None),
-                                          (19, 320, 64, 4, 1.2), (8, 64, 8, 8, None)])
+                                          (19, 320, 64, 4, 1.2), (8, 64, 8, 8, None),
+                                          # the shapes for a few hundred and for past 1024 tokens
+                                          # (ragged last blocks)
+                                          (300, 1024, 8, 2, None), (1500, 4096, 8, 2, None),
+                                          (1027, 4096, 16, 4, 1.2)])
 def test_route_topk(x_dtype, T, m, E, k, zipf):
     log(f"route_topk x={x_dtype} T={T} m={m} E={E} k={k} zipf={zipf}")
     sp = synth.LayerSpec("r", T, m, 64, E, k, "swiglu", x_dtype, "bf16", seed=T + E, sigma_router=0.05, zipf_s=zipf)
