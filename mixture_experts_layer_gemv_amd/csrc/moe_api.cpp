@@ -230,7 +230,7 @@ bool gemm_fits(const LayerCfg& c, int T, int k) {
   const unsigned long long G = c.kind == MOE_SWIGLU ? 2 : 1;
   const unsigned long long up_w = moe::packed_bytes(c.E, c.m, c.p, (int)G, qb);
   const unsigned long long dn_w = moe::packed_bytes(c.E, c.p, c.m, 1, qb);
-  const unsigned long long rows = (unsigned long long)moe::packed_rows_max((long long)T * k, c.E);
+  const unsigned long long rows = (unsigned long long)moe::packed_rows_alloc((long long)T * k, c.E);
   return up_w < lim && dn_w < lim && rows * c.m * 2 < lim && rows * c.p * 2 < lim;
 }
 
@@ -398,7 +398,7 @@ Ws ws_layout(const LayerCfg& c, int T, int k) {
   const bool spack = path == Path::SKINNY && skinny_packed(c, T, k);
   // the grouped GEMM and the packed skinny kernels keep H and the gathered x
   // in the packed row layout
-  const size_t prows = (size_t)moe::packed_rows_max((long long)n, c.E);
+  const size_t prows = (size_t)moe::packed_rows_alloc((long long)n, c.E);
   L.h = take((gemm || spack ? prows : n) * (size_t)c.p * (f32 ? 4 : 2));
   L.yacc = take((size_t)T * c.m * 4);
   const size_t row_sets =

@@ -138,6 +138,15 @@ __device__ __forceinline__ void mfma_fence_out(floatx4_t (&acc)[MF][NF], floatx4
 // SKIP: row fragments past the row block's last real row skip their
 // products (the fragment reads still run, so the steady state keeps no branch
 // around a load); for layers whose experts hold few rows.
+// H's zero row block (row block zrb of the packed H, N columns), 32-column
+// fragments f0 .. f0 + nf - 1, written by the first row block of the first
+// expert served, so that the down projection can read it in place of the
+// row fragments past an expert's last row.
+__device__ __forceinline__ void zero_h_block(uint16_t* h, int zrb, int N, int f0, int nf, int lane) {
+  for (int f = 0; f < nf; ++f)
+    reinterpret_cast<u32x4_t*>(h)[((long long)zrb * (N >> 5) + f0 + f) * 64 + lane] = u32x4_t{0u, 0u, 0u, 0u};
+}
+
 template <int EPI, bool SKIP, int QB>
 __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_ffn_gemm(
     const GemmArgs A) {
@@ -173,14 +182,16 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
   const int nfrag = (nrows + 15) >> 4;  // packed fragments holding real rows
   // this wave's row fragments that hold real rows (uniform)
   const int nf_w = __builtin_amdgcn_readfirstlane(min(max(nfrag - wm * MF, 0), MF));
+  const int zrb = padded_offset(offs_s, A.E) >> 4;  // the zero row block
 
   // This wave copies activation fragments CPA w .. CPA w + CPA-1 and weight
   // fragments CPB w .. CPB w + CPB-1 of every stage.  Sources are a uniform
   // base that advances one weight unit per stage plus a constant 32-bit byte
   // offset per lane (the packed activations and one projection's packed
   // weights are each under 4 GiB; checked on the host).  Activation
-  // fragments past the expert's last row re-read its last fragment; their
-  // rows are never stored.
+  // fragments past the expert's last row read the zero row block after the
+  // last expert's rows instead (their rows are never stored): the matrix
+  // cores draw less power on zero operands, which lets the clock rise.
   const int U = A.K / (32 * AH);  // stages (weight units along K)
   const char* const abase = reinterpret_cast<const char*>(A.act);
   const char* const bbase = static_cast<const char*>(A.w);
@@ -188,7 +199,8 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
 #pragma unroll
   for (int j = 0; j < CPA; ++j) {
     const int f = CPA * wave + j;  // activation fragment f: row fragment f / AH, 32-k part f % AH
-    aoff[j] = (uint32_t)(gemm_a_offset((prow0 >> 4) + min(f / AH, nfrag - 1), A.K, lane) + (f % AH) * kFrag);
+    const int rb = f / AH < nfrag ? (prow0 >> 4) + f / AH : zrb;
+    aoff[j] = (uint32_t)(gemm_a_offset(rb, A.K, lane) + (f % AH) * kFrag);
   }
 #pragma unroll
   for (int j = 0; j < CPB; ++j) boff[j] = (uint32_t)gemm_b_offset(e, NB, U, G, tile_base, kNF, CPB * wave + j, lane);
@@ -400,6 +412,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
         }
       }
       const long long fr0 = (long long)((prow0 + wm * 16 * MF) >> 4) * (A.N >> 5) + (nb0 >> 1);
+      if (mb == 0 && offs_s[e] == 0 && wm == 0) zero_h_block(A.h_out, zrb, A.N, nb0 >> 1, KF, lane);
 #pragma unroll
       for (int i = 0; i < MF; ++i) {
         if (wm * 16 * MF + 16 * i >= nrows) break;
@@ -498,12 +511,14 @@ __global__ __launch_bounds__(256) void k_pack_rows(const PackArgs A) {
   const long long rb = frag / U;
   const int u = (int)(frag - rb * U);
   const long long prow = rb * 16 + (lane & 15);
-  if (prow >= poffs_s[A.E]) return;  // past the last expert's padded rows
+  const int pe = poffs_s[A.E];
+  if (prow >= pe + 16) return;  // past the last expert's padded rows and the zero row block
   int e = 0;
-  while (poffs_s[e + 1] <= prow) ++e;
+  if (prow < pe)
+    while (poffs_s[e + 1] <= prow) ++e;
   const int local = (int)(prow - poffs_s[e]);
   u32x4_t v = {0u, 0u, 0u, 0u};
-  if (local < offs_s[e + 1] - offs_s[e]) {
+  if (prow < pe && local < offs_s[e + 1] - offs_s[e]) {
     const int a = A.topk_idx ? row_a[prow - prow_base] : A.perm[offs_s[e] + local];
     const int token = a / A.topk;
     v = *reinterpret_cast<const u32x4_t*>(A.x + (size_t)token * A.K + u * 32 + 8 * (lane >> 4));
@@ -528,12 +543,14 @@ __global__ __launch_bounds__(256) void k_pack_rows4(const PackArgs A) {
   const long long rb = frag0 / U;
   const int u0 = (int)(frag0 - rb * U);
   const long long prow = rb * 16 + (lane & 15);
-  if (prow >= poffs_s[A.E]) return;  // past the last expert's padded rows
+  const int pe = poffs_s[A.E];
+  if (prow >= pe + 16) return;  // past the last expert's padded rows and the zero row block
   int e = 0;
-  while (poffs_s[e + 1] <= prow) ++e;
+  if (prow < pe)
+    while (poffs_s[e + 1] <= prow) ++e;
   const int local = (int)(prow - poffs_s[e]);
   u32x4_t v[4] = {};
-  if (local < offs_s[e + 1] - offs_s[e]) {
+  if (prow < pe && local < offs_s[e + 1] - offs_s[e]) {
     const int token = A.perm[offs_s[e] + local] / A.topk;
     const u32x4_t* src = reinterpret_cast<const u32x4_t*>(A.x + (size_t)token * A.K + u0 * 32 + 8 * (lane >> 4));
 #pragma unroll
@@ -577,14 +594,16 @@ __global__ __launch_bounds__(256) void k_pack_rows_a8(const PackA8Args A) {
   const long long rb = unit / U;
   const int u = (int)(unit - rb * U);
   const long long prow = rb * 16 + (lane & 15);
-  if (prow >= poffs_s[A.E]) return;  // past the last expert's padded rows
+  const int pe = poffs_s[A.E];
+  if (prow >= pe + 16) return;  // past the last expert's padded rows and the zero row block
   int e = 0;
-  while (poffs_s[e + 1] <= prow) ++e;
+  if (prow < pe)
+    while (poffs_s[e + 1] <= prow) ++e;
   const int local = (int)(prow - poffs_s[e]);
   const int q = lane >> 4;
   uint2 lo = make_uint2(0u, 0u), hi = make_uint2(0u, 0u);
   float rs = 0.0f;
-  if (local < offs_s[e + 1] - offs_s[e]) {
+  if (prow < pe && local < offs_s[e + 1] - offs_s[e]) {
     const int token = A.perm[offs_s[e] + local] / A.topk;
     const uint8_t* row = A.codes + (size_t)token * A.K + u * 64 + 8 * q;
     lo = *reinterpret_cast<const uint2*>(row);
@@ -644,9 +663,10 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
   const int nrows = min(BM, offs_s[e + 1] - row0);
   const int prow0 = padded_offset(offs_s, e) + mb * BM;
   const int nfrag = (nrows + 15) >> 4;  // packed units holding real rows
+  const int zrb = padded_offset(offs_s, A.E) >> 4;  // the zero row block
 
   // copies: activation units 2 w, 2 w + 1 and weight units 2 w, 2 w + 1 of
-  // every stage (units past the expert's last row re-read its last unit)
+  // every stage (units past the expert's last row read the zero row block)
   const int U = A.K / 64;
   const char* const abase = reinterpret_cast<const char*>(A.act);
   const char* const bbase = static_cast<const char*>(A.w);
@@ -654,7 +674,8 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
 #pragma unroll
   for (int j = 0; j < CPA; ++j) {
     const int f = CPA * wave + j;
-    aoff[j] = (uint32_t)((unsigned long long)((prow0 >> 4) + min(f, nfrag - 1)) * (unsigned)U * 1024ull + 16ull * lane);
+    const int rb = f < nfrag ? (prow0 >> 4) + f : zrb;
+    aoff[j] = (uint32_t)((unsigned long long)rb * (unsigned)U * 1024ull + 16ull * lane);
   }
 #pragma unroll
   for (int j = 0; j < CPB; ++j) boff[j] = (uint32_t)gemm_b_offset(e, NB, U, G, tile_base, kNF, CPB * wave + j, lane);
@@ -793,6 +814,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
       }
     }
     const long long fr0 = (long long)((prow0 + wm * 128) >> 4) * (A.N >> 5) + (nb0 >> 1);
+    if (mb == 0 && offs_s[e] == 0 && wm == 0) zero_h_block(A.h_out, zrb, A.N, nb0 >> 1, KF, lane);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       if (wm * 128 + 16 * i >= nrows) break;
@@ -850,7 +872,7 @@ hipError_t launch_ffn_gemm(const GemmArgs& a, int epi, int qb, hipStream_t s) {
 
 hipError_t launch_pack_rows(const PackArgs& a, hipStream_t s) {
   const long long n = a.rows > 0 ? a.rows : (long long)a.T * a.topk;
-  const long long frags = packed_rows_max(n, a.E) / 16 * (a.K / 32);
+  const long long frags = packed_rows_alloc(n, a.E) / 16 * (a.K / 32);
   if (frags <= 0) return hipSuccess;
   if (!a.topk_idx && (a.K / 32) % 4 == 0) {
     const long long blocks = (frags / 4 + 3) / 4;  // one wave per four fragments
@@ -865,7 +887,7 @@ hipError_t launch_pack_rows(const PackArgs& a, hipStream_t s) {
 hipError_t launch_pack_rows_a8(const PackA8Args& a, hipStream_t s) {
   if (a.K % 64 || a.K <= 0) return hipErrorInvalidValue;
   const long long n = a.rows > 0 ? a.rows : (long long)a.T * a.topk;
-  const long long units = packed_rows_max(n, a.E) / 16 * (a.K / 64);
+  const long long units = packed_rows_alloc(n, a.E) / 16 * (a.K / 64);
   const long long blocks = (units + 3) / 4;  // one wave per unit
   if (blocks <= 0) return hipSuccess;
   k_pack_rows_a8<<<dim3((unsigned)blocks), 256, 0, s>>>(a);

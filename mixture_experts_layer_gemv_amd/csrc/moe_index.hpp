@@ -152,6 +152,12 @@ MOE_HD inline int padded_offset(const int* offsets, int e) {
 // Upper bound on packed rows for n dispatched rows over E experts.
 MOE_HD inline long long packed_rows_max(long long n, int E) { return n + 15ll * E; }
 
+// Rows a packed buffer holds: that bound plus one 16-row block of zeros,
+// which starts where the last expert's padded rows end (packed row
+// padded_offset(E)).  The grouped GEMM reads it in place of the row
+// fragments past an expert's last row.
+MOE_HD inline long long packed_rows_alloc(long long n, int E) { return packed_rows_max(n, E) + 16; }
+
 // Element index of (packed row prow, column k) in a packed [rows][K] matrix.
 MOE_HD inline unsigned long long packed_index(long long prow, int k, int K) {
   const unsigned long long frag = (unsigned long long)(prow >> 4) * (unsigned)(K >> 5) + (unsigned)(k >> 5);

@@ -197,7 +197,7 @@ struct PackArgs {
   const uint16_t* x;       // [T][K] bf16
   const int32_t* perm;     // [T*k] (input unless topk_idx is set)
   const int32_t* offsets;  // [E+1] (input unless topk_idx is set)
-  uint16_t* out;           // [packed_rows_max(T*k, E)][K] packed
+  uint16_t* out;           // [packed_rows_alloc(T*k, E)][K] packed
   const int32_t* topk_idx; // [T*k] or null: derive the dispatch here (T*k <= kFusedDispatchMax)
   int32_t* d_counts;       // with topk_idx: dispatch outputs published by workgroup 0
   int32_t* d_offsets;
@@ -219,8 +219,8 @@ struct PackA8Args {
   const float* scale;      // [T] per-token power-of-two scales
   const int32_t* perm;     // [T*k]
   const int32_t* offsets;  // [E+1]
-  uint8_t* out;            // [packed_rows_max(T*k, E)][K] packed units
-  float* row_scale;        // [packed_rows_max(T*k, E)]
+  uint8_t* out;            // [packed_rows_alloc(T*k, E)][K] packed units
+  float* row_scale;        // [packed_rows_alloc(T*k, E)]
   int T, K, E, topk;
   int rows;                // > 0: bound on the dispatched rows to pack (else T*topk)
 };

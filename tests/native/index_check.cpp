@@ -201,12 +201,13 @@ static void check_gemm(int K, int N, int G, int T, int topk, const std::vector<i
   const int NBL = (NB + tiles - 1) / tiles;
   const long long work = (long long)NBL * W * S;
   const int nblk = (int)((work + 7) / 8 * 8);
-  const long long prows = moe::packed_rows_max(n, E);
+  const long long prows = moe::packed_rows_alloc(n, E);
   const unsigned long long act_bytes = (unsigned long long)prows * K * 2;
   const unsigned long long h_elems = (unsigned long long)prows * N;
   const unsigned long long w_bytes = (unsigned long long)E * NB * U * G * 1024;
   const int pend = moe::padded_offset(offsets.data(), E);
-  CHECK(pend % 16 == 0 && pend <= prows, "padded rows %d of %lld", pend, prows);
+  CHECK(pend % 16 == 0 && pend + 16 <= prows, "padded rows %d and the zero block of %lld", pend, prows);
+  const int zrb = pend / 16;  // the zero row block
   std::vector<unsigned char> seen(cover ? (size_t)n * NB : 0, 0);
   std::vector<unsigned char> hwritten(cover ? (size_t)h_elems : 0, 0);
   for (int b = 0; b < nblk; ++b) {
@@ -239,9 +240,10 @@ static void check_gemm(int K, int N, int G, int T, int topk, const std::vector<i
       for (int j = 0; j < CPW; ++j) {
         const int f = CPW * wave + j;
         CHECK(16 + f < 32, "lds slot %d", 16 + f);
-        const long long rb = (prow0 >> 4) + std::min(f, nfrag - 1);
-        CHECK(rb * 16 >= pe && rb * 16 + 16 <= pe_end, "A fragment %lld outside expert %d rows [%d,%d)", rb, e, pe,
-              pe_end);
+        // fragments past the expert's last row read the zero row block
+        const long long rb = f < nfrag ? (prow0 >> 4) + f : zrb;
+        CHECK(rb == zrb || (rb * 16 >= pe && rb * 16 + 16 <= pe_end), "A fragment %lld outside expert %d rows [%d,%d)",
+              rb, e, pe, pe_end);
         for (int lane = 0; lane < 64; ++lane) {
           const unsigned long long a = moe::gemm_a_offset(rb, K, lane);
           CHECK(a < (1ull << 32) && a + (U - 1) * 1024ull + 16 <= act_bytes, "A offset %llu of %llu", a, act_bytes);
@@ -261,6 +263,17 @@ static void check_gemm(int K, int N, int G, int T, int topk, const std::vector<i
         if (nb0 >= NB) continue;
         CHECK(nb0 + TPW <= NB && (nb0 * 16) % 32 == 0, "wave columns %d..+%d of %d", nb0 * 16, TPW * 16, N);
         const int KF = TPW / 2;
+        // the first row block of the first expert served also zeroes H's
+        // zero row block (wave row 0, the wave's own fragments)
+        if (mb == 0 && offsets[e] == 0 && wm == 0)
+          for (int kf = 0; kf < KF; ++kf) {
+            const unsigned long long frag = (unsigned long long)zrb * (N >> 5) + (nb0 >> 1) + kf;
+            for (int x = 0; x < 512; ++x) {
+              const unsigned long long hi = frag * 512 + x;
+              CHECK(hi < h_elems, "zero H index %llu of %llu", hi, h_elems);
+              if (cover && hi < h_elems) CHECK(hwritten[hi]++ == 0, "zero H element %llu written twice", hi);
+            }
+          }
         for (int i = 0; i < 8; ++i) {
           if (wm * 128 + 16 * i >= nrows) break;
           const int fprow = prow0 + wm * 128 + 16 * i;
@@ -299,6 +312,9 @@ static void check_gemm(int K, int N, int G, int T, int topk, const std::vector<i
         }
       }
   }
+  if (cover && n > 0 && min_rows == 1)  // H's zero row block: every fragment written once
+    for (unsigned long long hi = (unsigned long long)zrb * 16 * N; hi < (unsigned long long)(zrb + 1) * 16 * N; ++hi)
+      CHECK(hwritten[hi] == 1, "zero H element %llu written %d times", hi, (int)hwritten[hi]);
   long long nitems = 0;
   for (int i = 0; i < E; ++i)
     if (offsets[i + 1] - offsets[i] >= min_rows) nitems += (long long)((offsets[i + 1] - offsets[i] + BM - 1) / BM) * NBL;
@@ -317,7 +333,7 @@ static void check_gemm(int K, int N, int G, int T, int topk, const std::vector<i
   for (int i = 0; i < n; ++i) perm[i] = (int)(rng() % std::max(1, T * topk));
   const long long frags = prows / 16 * U;
   const long long pblocks = (frags + 3) / 4;
-  std::vector<unsigned char> filled((size_t)(pend / 16) * U, 0);
+  std::vector<unsigned char> filled((size_t)(pend / 16 + 1) * U, 0);  // the zero row block included
   std::vector<int> poffs(E + 1);
   for (int i = 0; i <= E; ++i) poffs[i] = moe::padded_offset(offsets.data(), i);
   for (long long blk = 0; blk < pblocks; ++blk)
@@ -327,12 +343,13 @@ static void check_gemm(int K, int N, int G, int T, int topk, const std::vector<i
         const long long rb = frag / U;
         const int u = (int)(frag - rb * U);
         const long long prow = rb * 16 + (lane & 15);
-        if (prow >= pend) continue;
+        if (prow >= pend + 16) continue;
         int e = 0;
-        while (poffs[e + 1] <= prow) ++e;
+        if (prow < pend)
+          while (poffs[e + 1] <= prow) ++e;
         CHECK(e < E, "pack: row %lld has no expert", prow);
         const int local = (int)(prow - poffs[e]);
-        if (local < offsets[e + 1] - offsets[e]) {
+        if (prow < pend && local < offsets[e + 1] - offsets[e]) {
           const int token = perm[offsets[e] + local] / topk;
           const unsigned long long src = (unsigned long long)token * K + u * 32 + 8 * (lane >> 4);
           CHECK(token < T && src + 8 <= (unsigned long long)T * K, "pack read %llu", src);
@@ -356,13 +373,14 @@ static void check_gemm(int K, int N, int G, int T, int topk, const std::vector<i
         const int u0 = (int)(frag0 - rb * U);
         CHECK(u0 + 3 < U, "pack4: fragments %lld..+3 cross a row block", frag0);
         const long long prow = rb * 16 + (lane & 15);
-        if (prow >= pend) continue;
+        if (prow >= pend + 16) continue;
         int e = 0;
-        while (poffs[e + 1] <= prow) ++e;
+        if (prow < pend)
+          while (poffs[e + 1] <= prow) ++e;
         CHECK(e < E, "pack4: row %lld has no expert", prow);
         const int local = (int)(prow - poffs[e]);
         for (int f = 0; f < 4; ++f) {
-          if (local < offsets[e + 1] - offsets[e]) {
+          if (prow < pend && local < offsets[e + 1] - offsets[e]) {
             const int token = perm[offsets[e] + local] / topk;
             const unsigned long long src = (unsigned long long)token * K + u0 * 32 + 8 * (lane >> 4) + 32 * f;
             CHECK(token < T && src + 8 <= (unsigned long long)T * K, "pack4 read %llu", src);
