@@ -102,6 +102,13 @@ MOE_HD inline void unit_range(int part, int parts, int U, int* u0, int* u1) {
 // experts with fewer than min_rows rows get no work (another kernel serves
 // them).  Returns false for logical indices past the last item (grid
 // padding).
+// The number of (expert, row block, column block) items of that work order.
+MOE_HD inline int gemm_items(const int* offsets, int E, int BM, int NBL) {
+  int w = 0;
+  for (int i = 0; i < E; ++i) w += (offsets[i + 1] - offsets[i] + BM - 1) / BM * NBL;
+  return w;
+}
+
 MOE_HD inline bool gemm_item(const int* offsets, int E, int BM, int NBL, int CG, int L, int* e, int* mb,
                              int* nblock, int min_rows = 1) {
   int base = 0;

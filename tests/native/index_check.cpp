@@ -188,8 +188,11 @@ static void check_split(int N, const std::vector<int>& offsets, int hot, int ct)
 // stores stay in the buffer and (when `cover`) write every output element
 // exactly once; and that the row-packing kernel's reads and writes stay in
 // bounds and fill every packed fragment of every expert.
+// up = true: the up projections' placement, each XCD dealt an equal share
+// of the real items (xcd_item over gemm_items), then padding; otherwise the
+// grid cut into eight equal parts (xcd_logical).
 static void check_gemm(int K, int N, int G, int T, int topk, const std::vector<int>& offsets, bool cover,
-                       std::mt19937& rng, int min_rows = 1, int S = 1) {
+                       std::mt19937& rng, int min_rows = 1, int S = 1, bool up = false) {
   const int BM = 256, NF = 4, WR = 2, WC = 4, WAVES = WR * WC, CPW = 16 / WAVES, TPW = NF / G, CG = 4;
   std::set<std::tuple<int, int, int, int>> items;
   const int E = (int)offsets.size() - 1;
@@ -210,9 +213,13 @@ static void check_gemm(int K, int N, int G, int T, int topk, const std::vector<i
   const int zrb = pend / 16;  // the zero row block
   std::vector<unsigned char> seen(cover ? (size_t)n * NB : 0, 0);
   std::vector<unsigned char> hwritten(cover ? (size_t)h_elems : 0, 0);
+  CHECK(!up || (S == 1 && min_rows == 1), "up placement with S=%d min_rows=%d", S, min_rows);
+  const int nreal = moe::gemm_items(offsets.data(), E, BM, NBL);
+  CHECK(min_rows > 1 || nreal <= work, "gemm real items %d > grid work %lld", nreal, work);
   for (int b = 0; b < nblk; ++b) {
     int e, mb, nblock;
-    const int Lg = moe::xcd_logical(b, nblk);
+    const int Lg = up ? moe::xcd_item(b, nreal, 0) : moe::xcd_logical(b, nblk);
+    if (Lg < 0) continue;  // padding (up placement)
     const int kslice = Lg / (NBL * W);
     if (kslice >= S) continue;
     if (!moe::gemm_item(offsets.data(), E, BM, NBL, CG, Lg - kslice * NBL * W, &e, &mb, &nblock, min_rows))
@@ -482,7 +489,7 @@ int main() {
   {
     std::vector<int> counts = {2110, 1980, 2051, 2003, 2090, 2046, 2049, 2055};
     const std::vector<int> off = offsets_from(counts);
-    check_gemm(4096, 14336, 2, 8192, 2, off, false, rng);
+    check_gemm(4096, 14336, 2, 8192, 2, off, false, rng, 1, 1, true);
     check_gemm(14336, 4096, 1, 8192, 2, off, false, rng);
   }
   for (int it = 0; it < 120; ++it) {
@@ -494,8 +501,8 @@ int main() {
     std::vector<int> counts(E, 0);
     for (int a = 0; a < T * topk; ++a) counts[it % 2 ? (int)(rng() % E) : (int)(rng() % (1 + E / 3))]++;
     const std::vector<int> off = offsets_from(counts);
-    check_gemm(K, N, 2, T, topk, off, true, rng);
-    check_gemm(K, N, 1, T, topk, off, true, rng);
+    check_gemm(K, N, 2, T, topk, off, true, rng, 1, 1, true);
+    check_gemm(K, N, 1, T, topk, off, true, rng, 1, 1, true);
     check_gemm(N, K, 1, T, topk, off, true, rng);
     const int hot = 1 + (int)(rng() % 130);  // the hybrid split: experts with >= hot rows
     check_gemm(K, N, 2, T, topk, off, true, rng, hot);
