@@ -201,7 +201,9 @@ def test_act8_grouped_gemm(wd, kind, T, m, p, E, k, tune):
 
 @pytest.mark.parametrize("wd", ["fp8a8", "i8a8"])
 @pytest.mark.parametrize("path", ["skinny", "gemm"])
-@pytest.mark.parametrize("T,m,p,E,k", [(40, 256, 384, 8, 2), (300, 512, 256, 16, 2), (3, 128, 128, 64, 4)])
+@pytest.mark.parametrize("T,m,p,E,k", [(40, 256, 384, 8, 2), (300, 512, 256, 16, 2), (3, 128, 128, 64, 4),
+                                       # past 1024 tokens: eight tokens per routing block, a ragged last one
+                                       (1100, 256, 256, 8, 2), (1030, 512, 256, 16, 2)])
 def test_act8_quantised_in_routing_pass(wd, path, T, m, p, E, k, tune):
     """The layer quantises its experts' input rows inside the routing pass
     (route_quant on, the default); the same layer with the quantisation

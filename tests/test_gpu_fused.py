@@ -38,12 +38,14 @@ PATHS = [
     ("decode_int8", (64, 512, 1024, 8, 2, "swiglu", "i8", None), ""),
     ("skewed_split", (256, 256, 640, 16, 2, "swiglu", "bf16", 1.2), ""),
     ("relu_e12", (40, 256, 512, 12, 3, "relu", "bf16", None), ""),  # E=12: the unfused norm kernel
-    ("prefill_gemm", (2048, 512, 768, 8, 2, "swiglu", "bf16", None), "g"),
+    # past 1024 tokens the staged router takes eight tokens per block: a
+    # ragged last block of four
+    ("prefill_gemm", (2052, 512, 768, 8, 2, "swiglu", "bf16", None), "g"),
     ("tiny_f32", (32, 256, 512, 8, 2, "relu", "f32", None), ""),
     # 8-bit activations: the normalised rows quantised in the routing pass
     # (E = 8), or by the quantisation kernel after the norm kernel (E = 12)
     ("decode_fp8a8", (64, 512, 1024, 8, 2, "swiglu", "fp8a8", None), ""),
-    ("prefill_i8a8", (1024, 512, 768, 8, 2, "swiglu", "i8a8", None), "g"),
+    ("prefill_i8a8", (1100, 512, 768, 8, 2, "swiglu", "i8a8", None), "g"),
     ("relu_e12_fp8a8", (40, 256, 512, 12, 3, "relu", "fp8a8", None), ""),
 ]
 FUSIONS = [("layer", True), ("rms", False), ("none", True)]
