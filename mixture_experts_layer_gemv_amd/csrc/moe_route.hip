@@ -287,6 +287,24 @@ __global__ __launch_bounds__(64 * NW) void k_route_fast(const void* __restrict__
     const int n4 = nt * ym / 4;
     for (int i = tid; i < n4; i += NT) yr[i] = make_float4(0.f, 0.f, 0.f, 0.f);
   }
+  // The router weights: the wave's chunks are c = wave, wave + NW, ...; each
+  // group of WU of them is loaded whole (a chunk past the end reloads the
+  // group's first) while the group before it is multiplied, and the first
+  // group while the rows are staged.
+  const int q = lane & (S::Q - 1);
+  const int rr = lane >> S::LQ;
+  const int nchunks = m / S::RPC;
+  constexpr int WU = 8;
+  auto load_group = [&](int c0, float4(&wv)[WU]) {
+#pragma unroll
+    for (int u = 0; u < WU; ++u) {
+      const int c = c0 + NW * u < nchunks ? c0 + NW * u : c0;
+      wv[u] = *reinterpret_cast<const float4*>(wg + (size_t)(c * S::RPC + rr) * E + 4 * q);
+    }
+  };
+  float4 wv[WU];
+  if (wave < nchunks) load_group(wave, wv);
+
   // stage x rows [t0, t0 + nt) (rows past T are zero), eight loads in flight
   // per thread before the first LDS write
   {
@@ -400,20 +418,11 @@ __global__ __launch_bounds__(64 * NW) void k_route_fast(const void* __restrict__
   float acc[S::NV];
 #pragma unroll
   for (int i = 0; i < S::NV; ++i) acc[i] = 0.0f;
-  const int q = lane & (S::Q - 1);
-  const int rr = lane >> S::LQ;
-  const int nchunks = m / S::RPC;
-  // The wave's chunks are c = wave, wave + 16, ...; each group of WU of them
-  // issues all its weight loads before the first product (a chunk past the
-  // end reloads the group's first), and the products keep increasing c.
-  constexpr int WU = 8;
+  // the products keep increasing c
   for (int c0 = wave; c0 < nchunks; c0 += NW * WU) {
-    float4 wv[WU];
-#pragma unroll
-    for (int u = 0; u < WU; ++u) {
-      const int c = c0 + NW * u < nchunks ? c0 + NW * u : c0;
-      wv[u] = *reinterpret_cast<const float4*>(wg + (size_t)(c * S::RPC + rr) * E + 4 * q);
-    }
+    float4 wn[WU];
+    const bool more = c0 + NW * WU < nchunks;
+    if (more) load_group(c0 + NW * WU, wn);
 #pragma unroll
     for (int u = 0; u < WU; ++u) {
       const int c = c0 + NW * u;
@@ -432,6 +441,10 @@ __global__ __launch_bounds__(64 * NW) void k_route_fast(const void* __restrict__
           acc[t * 4 + 3] = fmaf(xv, wv[u].w, acc[t * 4 + 3]);
         }
       }
+    }
+    if (more) {
+#pragma unroll
+      for (int u = 0; u < WU; ++u) wv[u] = wn[u];
     }
   }
   // sum over the row lanes (lane bits LQ..5)
