@@ -37,10 +37,11 @@
 // keeps the equal parts of the grid (xcd_logical): dealing its real items
 // evenly measured ~1 % slower.
 //
-// Measured on the Mixtral-shaped prefill layer (T = 8192), the kernel runs
-// the matrix cores about half the time: the global -> LDS copies alone take
-// three quarters of its time, and with copies, LDS reads and products all
-// running the clock drops from ~2.4 to ~2.0 GHz.
+// Measured on the Mixtral-shaped prefill layer (T = 8192), the up
+// projection keeps the matrix pipe busy ~75 % of its active cycles, at
+// ~1.75 GHz: with copies, LDS reads and products all running, the clock
+// drops from 2.4 GHz, and a variant that only copies took three quarters of
+// the kernel's time.
 #include <type_traits>
 
 #include "moe_convert.hpp"
@@ -135,6 +136,15 @@ __device__ __forceinline__ void mfma_fence_out(floatx4_t (&acc)[MF][NF], floatx4
   acc_tie(accx);
 }
 
+// H's zero row block (row block zrb of the packed H, N columns), 32-column
+// fragments f0 .. f0 + nf - 1, written by the first row block of the first
+// expert served, so that the down projection can read it in place of the
+// row fragments past an expert's last row.
+__device__ __forceinline__ void zero_h_block(uint16_t* h, int zrb, int N, int f0, int nf, int lane) {
+  for (int f = 0; f < nf; ++f)
+    reinterpret_cast<u32x4_t*>(h)[((long long)zrb * (N >> 5) + f0 + f) * 64 + lane] = u32x4_t{0u, 0u, 0u, 0u};
+}
+
 // One expert projection tile: BM rows x 256 weight columns over the whole
 // reduction.  QB: weight bits (0 bf16, 8 int8, 4 int4); integer weights are
 // converted exactly to bf16 after their LDS read (the decode kernels'
@@ -146,15 +156,6 @@ __device__ __forceinline__ void mfma_fence_out(floatx4_t (&acc)[MF][NF], floatx4
 // SKIP: row fragments past the row block's last real row skip their
 // products (the fragment reads still run, so the steady state keeps no branch
 // around a load); for layers whose experts hold few rows.
-// H's zero row block (row block zrb of the packed H, N columns), 32-column
-// fragments f0 .. f0 + nf - 1, written by the first row block of the first
-// expert served, so that the down projection can read it in place of the
-// row fragments past an expert's last row.
-__device__ __forceinline__ void zero_h_block(uint16_t* h, int zrb, int N, int f0, int nf, int lane) {
-  for (int f = 0; f < nf; ++f)
-    reinterpret_cast<u32x4_t*>(h)[((long long)zrb * (N >> 5) + f0 + f) * 64 + lane] = u32x4_t{0u, 0u, 0u, 0u};
-}
-
 template <int EPI, bool SKIP, int QB>
 __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_ffn_gemm(
     const GemmArgs A) {

@@ -225,12 +225,12 @@ constexpr int route_lds_bytes(int tb) { return tb * 65536 < kRouteLdsX ? tb * 65
 
 // Router for E in {8, 16, 32, 64}: one block of NW waves per TB tokens
 // (TB * E <= 128, NW >= TB), staging at most LX bytes of activation rows.
-// 16 waves and up to 128 KiB by default; large batches of rows up to 8 KiB
-// take 8 tokens on 8 waves in 64 KiB, so that two blocks share a CU and one
-// stages its rows while the other multiplies.  The tokens' activation rows
-// are staged in LDS; each wave
-// streams 1 KiB chunks of the router weights with one coalesced 16-byte load
-// per lane (lane = row-in-chunk x expert quad) and keeps TB x 4 partial sums.
+// 16 waves and up to 128 KiB by default; large batches of rows of at most
+// 8 KiB take 8 tokens on 8 waves in 64 KiB, so that two blocks share a CU
+// and one stages its rows while the other multiplies.  The tokens'
+// activation rows are staged in LDS; each wave streams 1 KiB chunks of the
+// router weights with one coalesced 16-byte load per lane (lane =
+// row-in-chunk x expert quad) and keeps TB x 4 partial sums.
 // Sums over rows: across the lanes of a wave (reduce-scatter when there are
 // enough partials, butterfly otherwise), then a fixed-order sum over the NW
 // waves in LDS.  One wave per token then takes the top-k.  The block also
