@@ -335,7 +335,7 @@ moe_status moe_layer_forward(const moe_weights* w, const float* w_router, const 
  *            gamma).  The norm is computed in fp32 inside the routing pass
  *            and rounded to x's dtype; routing and experts use x'.
  *  gamma     device fp32 [m] (required with a norm); beta device fp32 [m] or
- *            NULL (layer norm only).  eps in [0, 1].
+ *            NULL (layer norm only); both 16-byte aligned.  eps in [0, 1].
  *  residual  device [T][m] in y_dtype, or NULL; added to the fp32 sum before
  *            y is rounded.
  *  x_norm    optional device [T][m] in x_dtype, 16-byte aligned: receives x'

@@ -1412,6 +1412,8 @@ moe_status moe_layer_forward_fused(const moe_weights* w, const float* w_router, 
   if (T > 0 && norm != MOE_NORM_NONE && !gamma) return fail(MOE_ERR_INVALID_ARG, "gamma is NULL");
   if (residual && !aligned16(residual)) return fail(MOE_ERR_INVALID_ARG, "residual must be 16-byte aligned");
   if (x_norm && !aligned16(x_norm)) return fail(MOE_ERR_INVALID_ARG, "x_norm must be 16-byte aligned");
+  if ((gamma && !aligned16(gamma)) || (beta && !aligned16(beta)))
+    return fail(MOE_ERR_INVALID_ARG, "gamma/beta must be 16-byte aligned");
   Fusion f;
   f.norm = norm;
   f.gamma = gamma;

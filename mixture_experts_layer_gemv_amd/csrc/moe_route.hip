@@ -331,24 +331,45 @@ __global__ __launch_bounds__(64 * NW) void k_route_fast(const void* __restrict__
     // Norm of the staged rows (the reductions along the row inside this
     // block, one wave per token), in place, so the router and the experts
     // both see the normalised rows; they also go to F.xn for the experts.
+    // Rows are read and written 16 bytes at a time (EV elements; m is a
+    // multiple of 64), gamma and beta likewise.
     __shared__ float mu_s[TB], r_s[TB];
-    auto xat = [&](int t, int c) {
-      if constexpr (XBF16)
-        return bf16_to_f32(reinterpret_cast<const uint16_t*>(xs_raw)[t * m + c]);
-      else
-        return reinterpret_cast<const float*>(xs_raw)[t * m + c];
+    constexpr int EV = XBF16 ? 8 : 4;
+    const int mv = m / EV;  // 16-byte vectors per row
+    uint4* const xv4 = reinterpret_cast<uint4*>(xs_raw);
+    auto unpack = [](const uint4& v, float (&f)[EV]) {
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if constexpr (XBF16) {
+          f[2 * j] = __uint_as_float(w[j] << 16);
+          f[2 * j + 1] = __uint_as_float(w[j] & 0xFFFF0000u);
+        } else {
+          f[j] = __uint_as_float(w[j]);
+        }
+      }
     };
     if (wave < nt) {
       float mu = 0.0f;
       if (F.norm == 1) {
         float sum = 0.0f;
-        for (int c = lane; c < m; c += 64) sum += xat(wave, c);
+        for (int i = lane; i < mv; i += 64) {
+          float f[EV];
+          unpack(xv4[wave * mv + i], f);
+#pragma unroll
+          for (int j = 0; j < EV; ++j) sum += f[j];
+        }
         mu = wave_sum64(sum) / (float)m;
       }
       float ss = 0.0f;
-      for (int c = lane; c < m; c += 64) {
-        const float d = xat(wave, c) - mu;
-        ss = fmaf(d, d, ss);
+      for (int i = lane; i < mv; i += 64) {
+        float f[EV];
+        unpack(xv4[wave * mv + i], f);
+#pragma unroll
+        for (int j = 0; j < EV; ++j) {
+          const float d = f[j] - mu;
+          ss = fmaf(d, d, ss);
+        }
       }
       ss = wave_sum64(ss);
       if (lane == 0) {
@@ -357,17 +378,37 @@ __global__ __launch_bounds__(64 * NW) void k_route_fast(const void* __restrict__
       }
     }
     __syncthreads();
-    for (int i = tid; i < nt * m; i += NT) {
-      const int t = i / m, c = i - t * m;
-      const float v = norm_value<XBF16>(F, xat(t, c), mu_s[t], r_s[t], c);
-      if constexpr (XBF16) {
-        const uint16_t b = f32_to_bf16(v);
-        reinterpret_cast<uint16_t*>(xs_raw)[i] = b;
-        static_cast<uint16_t*>(F.xn)[(size_t)t0 * m + i] = b;
-      } else {
-        reinterpret_cast<float*>(xs_raw)[i] = v;
-        static_cast<float*>(F.xn)[(size_t)t0 * m + i] = v;
+    uint4* const xn4 = reinterpret_cast<uint4*>(static_cast<char*>(F.xn) + (size_t)t0 * m * XB);
+    const bool with_beta = F.norm == 1 && F.beta;
+    for (int i = tid; i < nt * mv; i += NT) {
+      const int t = i / mv, c0 = (i - t * mv) * EV;
+      float f[EV], g[EV], b[EV];
+      unpack(xv4[i], f);
+#pragma unroll
+      for (int j = 0; j < EV; j += 4) {
+        const float4 g4 = *reinterpret_cast<const float4*>(F.gamma + c0 + j);
+        g[j] = g4.x, g[j + 1] = g4.y, g[j + 2] = g4.z, g[j + 3] = g4.w;
+        const float4 b4 = with_beta ? *reinterpret_cast<const float4*>(F.beta + c0 + j) : make_float4(0.f, 0.f, 0.f, 0.f);
+        b[j] = b4.x, b[j + 1] = b4.y, b[j + 2] = b4.z, b[j + 3] = b4.w;
       }
+      uint32_t w[4];
+#pragma unroll
+      for (int j = 0; j < EV; ++j) {
+        float v = (f[j] - mu_s[t]) * r_s[t] * g[j];
+        if (with_beta) v += b[j];
+        if constexpr (XBF16) {
+          const uint32_t h = f32_to_bf16(v);
+          if (j & 1)
+            w[j >> 1] |= h << 16;
+          else
+            w[j >> 1] = h;
+        } else {
+          w[j] = __float_as_uint(v);
+        }
+      }
+      const uint4 o = make_uint4(w[0], w[1], w[2], w[3]);
+      xv4[i] = o;
+      xn4[i] = o;
     }
     __syncthreads();
   }

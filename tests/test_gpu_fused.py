@@ -120,11 +120,13 @@ def test_fused_argument_errors():
     y = layer.new_output()
     ws = layer.ensure_workspace(8)
     g = to_device(np.ones(256, np.float32))
+    g_mis = to_device(np.ones(257, np.float32))[1:]  # 4 bytes past a 16-byte boundary
     args = lambda norm, gamma, beta, eps: (layer.handle, layer.wg, layer.bias, layer.x, layer.x_dtype, norm, gamma,
                                            beta, eps, None, 8, 256, 512, 8, 2, y, layer.y_dtype, ws, layer.ws_bytes)
     for bad in [(7, g, None, 1e-5), (M.MOE_NORM_LAYER, None, None, 1e-5), (M.MOE_NORM_RMS, g, g, 1e-5),
                 (M.MOE_NORM_NONE, g, None, 1e-5), (M.MOE_NORM_LAYER, g, None, -1.0),
-                (M.MOE_NORM_LAYER, g, None, float("nan"))]:
+                (M.MOE_NORM_LAYER, g, None, float("nan")), (M.MOE_NORM_LAYER, g_mis, None, 1e-5),
+                (M.MOE_NORM_LAYER, g, g_mis, 1e-5)]:
         with pytest.raises(M.MoeError) as ei:
             M.moe_layer_forward_fused(*args(*bad))
         assert ei.value.status == M.MOE_ERR_INVALID_ARG, bad
