@@ -252,16 +252,6 @@ __device__ __forceinline__ float residual_at(const RouteFuse& F, size_t i) {
                     : static_cast<const float*>(F.residual)[i];
 }
 
-// The normalised value of x (a row element at column c) given the row's mean
-// mu and reciprocal deviation r, rounded to the activation dtype's precision.
-template <bool XBF16>
-__device__ __forceinline__ float norm_value(const RouteFuse& F, float xv, float mu, float r, int c) {
-  float v = (xv - mu) * r * F.gamma[c];
-  if (F.norm == 1 && F.beta) v += F.beta[c];
-  if constexpr (XBF16) v = bf16_to_f32(f32_to_bf16(v));
-  return v;
-}
-
 template <int E, int TB, bool XBF16, int NW = 16, int LX = route_lds_bytes(TB)>
 __global__ __launch_bounds__(64 * NW) void k_route_fast(const void* __restrict__ x, const float* __restrict__ wg,
                                                      const float* __restrict__ bias, int T, int m, int k,
@@ -601,14 +591,25 @@ __global__ __launch_bounds__(1024) void k_dispatch(const int32_t* __restrict__ i
 // One block per row: the row's norm written to F.xn (the unfused form).
 template <bool XBF16>
 __global__ __launch_bounds__(256) void k_norm_rows(const void* __restrict__ x, int m, const RouteFuse F) {
+  // 16 bytes (EV elements) of the row per thread and step; m is a multiple
+  // of 64, gamma, beta and the rows 16-byte aligned
+  constexpr int EV = XBF16 ? 8 : 4;
   __shared__ float part[4];
   const int t = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const size_t base = (size_t)t * m;
-  auto xat = [&](int c) {
-    if constexpr (XBF16)
-      return bf16_to_f32(static_cast<const uint16_t*>(x)[base + c]);
-    else
-      return static_cast<const float*>(x)[base + c];
+  const int mv = m / EV;
+  const uint4* const row = reinterpret_cast<const uint4*>(static_cast<const char*>(x) + (size_t)t * m * (XBF16 ? 2 : 4));
+  uint4* const out = reinterpret_cast<uint4*>(static_cast<char*>(F.xn) + (size_t)t * m * (XBF16 ? 2 : 4));
+  auto unpack = [](const uint4& v, float (&f)[EV]) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if constexpr (XBF16) {
+        f[2 * j] = __uint_as_float(w[j] << 16);
+        f[2 * j + 1] = __uint_as_float(w[j] & 0xFFFF0000u);
+      } else {
+        f[j] = __uint_as_float(w[j]);
+      }
+    }
   };
   auto block_sum = [&](float v) {
     v = wave_sum64(v);
@@ -621,21 +622,52 @@ __global__ __launch_bounds__(256) void k_norm_rows(const void* __restrict__ x, i
   float mu = 0.0f;
   if (F.norm == 1) {
     float sum = 0.0f;
-    for (int c = tid; c < m; c += 256) sum += xat(c);
+    for (int i = tid; i < mv; i += 256) {
+      float f[EV];
+      unpack(row[i], f);
+#pragma unroll
+      for (int j = 0; j < EV; ++j) sum += f[j];
+    }
     mu = block_sum(sum) / (float)m;
   }
   float ss = 0.0f;
-  for (int c = tid; c < m; c += 256) {
-    const float d = xat(c) - mu;
-    ss = fmaf(d, d, ss);
+  for (int i = tid; i < mv; i += 256) {
+    float f[EV];
+    unpack(row[i], f);
+#pragma unroll
+    for (int j = 0; j < EV; ++j) {
+      const float d = f[j] - mu;
+      ss = fmaf(d, d, ss);
+    }
   }
   const float r = 1.0f / sqrtf(block_sum(ss) / (float)m + F.eps);
-  for (int c = tid; c < m; c += 256) {
-    const float v = norm_value<XBF16>(F, xat(c), mu, r, c);
-    if constexpr (XBF16)
-      static_cast<uint16_t*>(F.xn)[base + c] = f32_to_bf16(v);
-    else
-      static_cast<float*>(F.xn)[base + c] = v;
+  const bool with_beta = F.norm == 1 && F.beta;
+  for (int i = tid; i < mv; i += 256) {
+    const int c0 = i * EV;
+    float f[EV];
+    unpack(row[i], f);
+    uint32_t w[4];
+#pragma unroll
+    for (int j = 0; j < EV; j += 4) {
+      const float4 g4 = *reinterpret_cast<const float4*>(F.gamma + c0 + j);
+      const float4 b4 = with_beta ? *reinterpret_cast<const float4*>(F.beta + c0 + j) : make_float4(0.f, 0.f, 0.f, 0.f);
+      const float g[4] = {g4.x, g4.y, g4.z, g4.w}, bb[4] = {b4.x, b4.y, b4.z, b4.w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        float v = (f[j + q] - mu) * r * g[q];
+        if (with_beta) v += bb[q];
+        if constexpr (XBF16) {
+          const uint32_t h = f32_to_bf16(v);
+          if ((j + q) & 1)
+            w[(j + q) >> 1] |= h << 16;
+          else
+            w[(j + q) >> 1] = h;
+        } else {
+          w[j + q] = __float_as_uint(v);
+        }
+      }
+    }
+    out[i] = make_uint4(w[0], w[1], w[2], w[3]);
   }
 }
 
