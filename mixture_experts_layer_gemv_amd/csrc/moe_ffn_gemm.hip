@@ -38,8 +38,8 @@
 // evenly measured ~1 % slower.
 //
 // Measured on the Mixtral-shaped prefill layer (T = 8192), the up
-// projection keeps the matrix pipe busy ~75 % of its active cycles, at
-// ~1.75 GHz: with copies, LDS reads and products all running, the clock
+// projection keeps the matrix pipe busy ~80 % of its active cycles, at
+// ~1.67 GHz: with copies, LDS reads and products all running, the clock
 // drops from 2.4 GHz, and a variant that only copies took three quarters of
 // the kernel's time.
 #include <type_traits>
