@@ -366,13 +366,13 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
       else
         __builtin_amdgcn_s_waitcnt(vmcnt_imm(CPS * (STAGES - 2)));
       ring_barrier();  // group 0: B1(ks); group 1: B2(ks)
-      // bf16 weights: the products at normal wave priority and the next
-      // stage's activation fragments read before its weight fragments
-      // (Mixtral prefill: up 2.84 -> 2.73 ms, down 1.55 -> 1.50 ms); the
-      // converted kinds keep weights first (int8: 3-4 % slower with
-      // activations first, fp8 and int4 unchanged), fp8 at normal priority
-      // too (1-1.5 % faster), int8 and int4 at the raised one
-      if constexpr (QB == 0 || QB == 9) {
+      // bf16 and int4 weights: the products at normal wave priority and the
+      // next stage's activation fragments read before its weight fragments
+      // (Mixtral prefill, bf16: up 2.84 -> 2.73 ms, down 1.55 -> 1.50 ms;
+      // int4: up 2.5 % faster); int8 and fp8 read weights first (int8: 3-4 %
+      // slower with activations first, fp8 unchanged), fp8 at normal
+      // priority (1-1.5 % faster), int8 at the raised one
+      if constexpr (QB == 0 || QB == 4 || QB == 9) {
         MOE_MMA(f);
       } else {
         asm volatile("s_setprio 1");
@@ -381,7 +381,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
       }
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(CPS * (STAGES - 2)));
       ring_barrier();  // group 0: B2(ks); group 1: B1(ks+1)
-      if constexpr (QB == 0) {
+      if constexpr (QB == 0 || QB == 4) {
         MOE_LOAD_A(f, ks + 1);
         MOE_LOAD_B(f, ks + 1);
       } else {
